@@ -1,0 +1,360 @@
+"""Pins of the fp64 CPU oracle against things other than itself: a dense
+brute force with an independent selection, closed forms, textbook
+reductions, invariants, metamorphic relations and the workload's stated
+distributions.  A final group plants plausible mistakes in the oracle and
+checks that these pins catch each one.  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as O
+from mixture_experts_layer_top_amd.inputs import CONFIGS, ROUTER_PARTS, make_layer, to_f64
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+SMALL = {
+    "tiny": CONFIGS["tiny"],
+    "mixtral": CONFIGS["mixtral"].shrink(T=48, d=24, f=40),
+    "qwen2moe": CONFIGS["qwen2moe"].shrink(T=48, d=24, f=40, f_shared=56),
+    "mixtral_skew": CONFIGS["mixtral_skew"].shrink(T=64, d=24, f=40),
+    "deepseek": CONFIGS["deepseek"].shrink(T=48, d=24, f=40, f_shared=32),
+}
+
+
+def small_layer(name, seed=0):
+    cfg = SMALL[name]
+    return cfg, to_f64(make_layer(cfg, seed=seed))
+
+
+def rms(a):
+    return float(np.sqrt(np.mean(np.square(a))))
+
+
+def o1_vs_o2(layer, cfg, tol=1e-12):
+    """Oracle forward against the dense brute force: same selection, same y."""
+    ref = O.forward(layer, cfg.k, cfg.renorm)
+    bf = O.brute_force(layer, cfg.k, cfg.renorm)
+    assert np.array_equal(ref["idx"], bf["idx"]), "selection differs from brute-force sort"
+    err = np.max(np.abs(ref["y"] - bf["y"]))
+    assert err <= tol * rms(bf["y"]), f"y differs from brute force: {err} vs rms {rms(bf['y'])}"
+    return ref, bf
+
+
+def permutation_pins(idx, counts, offsets, perm_token, inv, E):
+    T, k = idx.shape
+    R = T * k
+    assert counts.sum() == R
+    assert offsets[0] == 0 and offsets[-1] == R
+    assert np.all(np.diff(offsets) == counts)
+    # bijection (t, j) <-> r
+    assert sorted(inv.ravel().tolist()) == list(range(R))
+    assert np.all(perm_token[inv] == np.arange(T)[:, None])
+    # the expert of row inv[t, j] is idx[t, j]
+    row_expert = np.repeat(np.arange(E), counts)
+    assert np.all(row_expert[inv] == idx)
+    # stable: strictly ascending tokens inside each segment
+    for e in range(E):
+        seg = perm_token[offsets[e]:offsets[e + 1]]
+        assert np.all(np.diff(seg) > 0)
+    # library cross-check: a stable argsort of the flattened pairs by expert
+    order = np.argsort(idx.ravel(), kind="stable")
+    assert np.array_equal(order // k, perm_token)
+    assert np.array_equal(np.argsort(order), inv.ravel())
+
+
+# ---------------------------------------------------------------- selection
+
+
+def test_selection_equals_python_sort_with_ties():
+    rng = np.random.default_rng(7)
+    L = rng.integers(-3, 4, size=(500, 16)).astype(np.float64)  # many exact ties
+    for k in (1, 2, 5, 16):
+        idx = O.select_topk(L, k)
+        ref = [sorted(range(16), key=lambda e: (-L[t, e], e))[:k] for t in range(500)]
+        assert np.array_equal(idx, np.array(ref))
+
+
+def test_duplicated_router_columns_tie_to_lower_index():
+    cfg, layer = small_layer("mixtral")
+    W = layer["W_r"].copy()
+    W[:, 5] = W[:, 2]  # experts 2 and 5 tie on every token
+    L = O.router_logits(layer["x"], W)
+    idx = O.select_topk(L, cfg.k)
+    for t in range(L.shape[0]):
+        row = list(idx[t])
+        if 5 in row:
+            assert 2 in row and row.index(2) < row.index(5)
+    # where only one of the tied pair fits, it is the lower one
+    assert np.any([(2 in r) and (5 not in r) for r in idx])
+    assert not np.any([(5 in r) and (2 not in r) for r in idx])
+
+
+def test_zero_token_closed_forms():
+    gold = {c["name"]: c for c in json.load(open(GOLDEN))["cases"]}
+    for name in ("mixtral", "qwen2moe", "deepseek", "tiny"):
+        cfg, layer = small_layer(name)
+        layer["x"][3] = 0.0
+        L, idx, w = O.route(layer, cfg.k, cfg.renorm)
+        assert list(idx[3]) == list(range(cfg.k))
+        expect = 1.0 / cfg.k if cfg.renorm else 1.0 / cfg.E
+        np.testing.assert_allclose(w[3], expect, rtol=1e-15)
+    assert "1/k" in gold["zero_token_unbiased_renorm"]["expected_w"]
+    g = gold["zero_token_skew_bias"]
+    cfg, layer = small_layer("mixtral_skew")
+    layer["x"][0] = 0.0
+    L, idx, w = O.route(layer, cfg.k, cfg.renorm)
+    assert list(idx[0]) == g["expected_idx"]
+    q = 2.0 ** -g["r"]
+    # the bias is stored as float32, so exp(b1 - b0) is 2^-1.8 to ~1e-7
+    np.testing.assert_allclose(w[0], [1 / (1 + q), q / (1 + q)], rtol=1e-6)
+
+
+def test_hand_example():
+    layer = dict(x=np.array([[1.0, 0.0]]), W_r=np.array([[1.0, 0.0], [0.0, 0.0]]), b=None,
+                 W_gate=np.array([[[2.0], [5.0]], [[1.0], [1.0]]]),
+                 W_up=np.array([[[3.0], [7.0]], [[1.0], [1.0]]]),
+                 W_down=np.array([[[0.5, -1.0]], [[9.0, 9.0]]]))
+    r = O.forward(layer, 1, True)
+    assert r["idx"].tolist() == [[0]]
+    a = 3.0 * 2.0 / (1.0 + math.exp(-2.0))
+    np.testing.assert_allclose(r["y"][0], [0.5 * a, -a], rtol=1e-15)
+    r2 = O.forward(layer, 1, False)
+    np.testing.assert_allclose(r2["w"][0, 0], math.e / (math.e + 1.0), rtol=1e-15)
+    np.testing.assert_allclose(r2["y"][0], r2["w"][0, 0] * np.array([0.5 * a, -a]), rtol=1e-15)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_weight_properties(name):
+    cfg, layer = small_layer(name)
+    L, idx, w = O.route(layer, cfg.k, cfg.renorm)
+    assert np.all(np.diff(w, axis=1) <= 0)  # rank order => non-increasing weights
+    assert np.all(w > 0)
+    if cfg.renorm:
+        np.testing.assert_allclose(w.sum(1), 1.0, atol=1e-15)
+    else:
+        assert np.all(w.sum(1) < 1.0)
+        # full softmax over E sums to 1; the k selected are the largest probabilities
+        np.testing.assert_allclose(O.topk_weights(L, O.select_topk(L, cfg.E), False).sum(1),
+                                   1.0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- dispatch
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_permutation_invariants(name):
+    cfg, layer = small_layer(name)
+    L, idx, w = O.route(layer, cfg.k, cfg.renorm)
+    counts, offsets, perm_token, inv, perm_w = O.dispatch(idx, w, cfg.E)
+    permutation_pins(idx, counts, offsets, perm_token, inv, cfg.E)
+    np.testing.assert_array_equal(perm_w[inv], w)
+
+
+def test_permutation_handmade():
+    idx = np.array([[2, 0], [0, 1], [2, 1], [1, 2]])
+    counts = O.expert_counts(idx, 3)
+    assert counts.tolist() == [2, 3, 3]
+    pt, inv, slot = O.permutation(idx, 3)
+    # expert 0: tokens 0,1; expert 1: tokens 1,2,3; expert 2: tokens 0,2,3
+    assert pt.tolist() == [0, 1, 1, 2, 3, 0, 2, 3]
+    assert inv.tolist() == [[5, 0], [1, 2], [6, 3], [4, 7]]
+    assert slot.tolist() == [1, 0, 1, 1, 0, 0, 0, 1]
+
+
+# ---------------------------------------------------------------- expert FFN
+
+
+def test_single_expert_is_textbook_swiglu():
+    cfg = CONFIGS["tiny"]
+    lay = to_f64(make_layer(cfg.shrink(T=32, d=16, f=24), seed=3))
+    one = dict(x=lay["x"], W_r=lay["W_r"][:, :1], b=None, W_gate=lay["W_gate"][:1],
+               W_up=lay["W_up"][:1], W_down=lay["W_down"][:1])
+    r = O.forward(one, 1, True)
+    x = torch.from_numpy(lay["x"])
+    ref = (torch.nn.functional.silu(x @ torch.from_numpy(lay["W_gate"][0]))
+           * (x @ torch.from_numpy(lay["W_up"][0]))) @ torch.from_numpy(lay["W_down"][0])
+    np.testing.assert_allclose(r["y"], ref.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.all(r["w"] == 1.0)
+
+
+@pytest.mark.parametrize("which", ["W_gate", "W_up"])
+def test_zero_projection_gives_exact_zero(which):
+    cfg, layer = small_layer("mixtral")
+    layer[which] = np.zeros_like(layer[which])
+    r = O.forward(layer, cfg.k, cfg.renorm)
+    assert np.all(r["y"] == 0.0)
+
+
+def test_down_projection_homogeneity():
+    cfg, layer = small_layer("deepseek")
+    r1 = O.forward(layer, cfg.k, cfg.renorm)
+    layer2 = dict(layer, W_down=2.0 * layer["W_down"], Ws_down=2.0 * layer["Ws_down"])
+    r2 = O.forward(layer2, cfg.k, cfg.renorm)
+    assert np.array_equal(r2["y"], 2.0 * r1["y"])
+
+
+def test_k_equals_E_is_dense_soft_mixture():
+    cfg = CONFIGS["mixtral"].shrink(T=40, d=16, f=24)
+    layer = to_f64(make_layer(cfg, seed=5))
+    r = O.forward(layer, cfg.E, True)
+    x = torch.from_numpy(layer["x"])
+    P = torch.softmax(torch.from_numpy(O.router_logits(layer["x"], layer["W_r"])), dim=1)
+    y = torch.zeros(40, 16, dtype=torch.float64)
+    for e in range(cfg.E):
+        F = (torch.nn.functional.silu(x @ torch.from_numpy(layer["W_gate"][e]))
+             * (x @ torch.from_numpy(layer["W_up"][e]))) @ torch.from_numpy(layer["W_down"][e])
+        y += P[:, e:e + 1] * F
+    np.testing.assert_allclose(r["y"], y.numpy(), rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- whole layer
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_oracle_matches_dense_brute_force(name):
+    cfg, layer = small_layer(name)
+    o1_vs_o2(layer, cfg)
+
+
+def test_token_output_matches_forward():
+    cfg, layer = small_layer("qwen2moe")
+    r = O.forward(layer, cfg.k, cfg.renorm)
+    for t in (0, 7, 47):
+        yt = O.token_output(layer, t, r["idx"][t], r["w"][t])
+        np.testing.assert_allclose(yt, r["y"][t], rtol=1e-12, atol=1e-14)
+
+
+def test_token_permutation_metamorphic():
+    cfg, layer = small_layer("deepseek")
+    r = O.forward(layer, cfg.k, cfg.renorm)
+    p = np.random.default_rng(1).permutation(cfg.T)
+    r2 = O.forward(dict(layer, x=layer["x"][p]), cfg.k, cfg.renorm)
+    np.testing.assert_allclose(r2["y"], r["y"][p], rtol=1e-13, atol=1e-14)
+    assert np.array_equal(r2["counts"], r["counts"])
+
+
+def test_expert_relabelling_metamorphic():
+    cfg, layer = small_layer("mixtral_skew")
+    r = O.forward(layer, cfg.k, cfg.renorm)
+    q = np.random.default_rng(2).permutation(cfg.E)
+    lay2 = dict(layer, W_r=layer["W_r"][:, q], b=layer["b"][q], W_gate=layer["W_gate"][q],
+                W_up=layer["W_up"][q], W_down=layer["W_down"][q])
+    r2 = O.forward(lay2, cfg.k, cfg.renorm)
+    np.testing.assert_allclose(r2["y"], r["y"], rtol=1e-12, atol=1e-14)
+    assert np.array_equal(r2["counts"], r["counts"][q])
+
+
+def test_duplicated_tokens_identical_rows():
+    cfg, layer = small_layer("qwen2moe")
+    layer["x"][10] = layer["x"][20]
+    r = O.forward(layer, cfg.k, cfg.renorm)
+    assert np.array_equal(r["y"][10], r["y"][20])
+
+
+def test_fp32_logit_bound_holds():
+    cfg = CONFIGS["deepseek"]
+    lay = make_layer(cfg, seed=0, T=512, parts=ROUTER_PARTS)
+    x, W = lay["x"].float(), lay["W_r"].float()
+    L32 = (x @ W).double().numpy()  # float32 accumulation in some order
+    L64 = O.router_logits(to_f64(lay)["x"], to_f64(lay)["W_r"])
+    bound = O.fp32_logit_error_bound(to_f64(lay)["x"], to_f64(lay)["W_r"], safety=1.0)
+    assert np.all(np.abs(L32 - L64) <= bound[:, None])
+
+
+# ---------------------------------------------------------------- stated distributions
+
+
+def shares(name, seed=0):
+    cfg = CONFIGS[name]
+    lay = to_f64(make_layer(cfg, seed=seed, parts=ROUTER_PARTS))
+    L = O.router_logits(lay["x"], lay["W_r"], lay.get("b"))
+    idx = O.select_topk(L, cfg.k)
+    return O.expert_counts(idx, cfg.E) / idx.size
+
+
+def test_tiny_routing_near_uniform():
+    s = shares("tiny")
+    assert np.all((s >= 0.15) & (s <= 0.35)), s
+
+
+def test_skew_routing_matches_stated_band():
+    s = shares("mixtral_skew")
+    assert 0.35 <= s[0] <= 0.55, s
+    assert s[7] < 0.05, s
+    assert np.all(np.diff(s) < 0), s
+
+
+def test_mixtral_routing_unbiased_band():
+    s = shares("mixtral")
+    assert np.all(np.abs(s - 0.125) <= 0.02), s
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+
+def _tie_layer():
+    cfg, layer = small_layer("mixtral")
+    layer["W_r"] = layer["W_r"].copy()
+    layer["W_r"][:, 5] = layer["W_r"][:, 2]
+    return cfg, layer
+
+
+MUTATIONS = {
+    "ties_to_higher_index": ("select_topk",
+                             lambda L, k: np.lexsort((-np.broadcast_to(np.arange(L.shape[1]), L.shape), -L),
+                                                     axis=1)[:, :k]),
+    "no_renormalisation": ("topk_weights",
+                           lambda L, idx, renorm, _f=O.topk_weights: _f(L, idx, False)),
+    "silu_on_up_projection": ("swiglu_ffn",
+                              lambda z, Wg, Wu, Wd, chunk=4096: (z @ Wg * O.silu(z @ Wu)) @ Wd),
+    "combine_wrong_slot_weight": ("combine",
+                                  lambda Y, inv, w, _f=O.combine: _f(Y, inv, w[:, ::-1])),
+    "bias_dropped": ("router_logits", lambda x, W_r, b=None: np.asarray(x) @ np.asarray(W_r)),
+    "transposed_down_operand": ("swiglu_ffn",
+                                lambda z, Wg, Wu, Wd, chunk=4096: (O.silu(z @ Wg) * (z @ Wu)) @ Wd.T.reshape(Wd.shape)),
+    "inclusive_scan": ("exclusive_offsets",
+                       lambda c: np.concatenate([np.cumsum(c), [np.sum(c)]])),
+    "shared_gate_dropped": ("sigmoid", lambda z: np.ones_like(z)),
+    "unstable_permutation": ("permutation", None),
+}
+
+
+def _unstable_permutation(idx, E, _f=O.permutation):
+    pt, inv, slot = _f(idx, E)
+    # reverse the token order inside each expert segment
+    counts = O.expert_counts(idx, E)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    pt2, slot2 = pt.copy(), slot.copy()
+    for e in range(E):
+        pt2[off[e]:off[e + 1]] = pt[off[e]:off[e + 1]][::-1]
+        slot2[off[e]:off[e + 1]] = slot[off[e]:off[e + 1]][::-1]
+    inv2 = np.empty_like(inv)
+    inv2[pt2, slot2] = np.arange(len(pt2))
+    return pt2, inv2, slot2
+
+
+def _run_pins(name):
+    """The pins a mutation is expected to trip, for the config it matters in."""
+    cfg, layer = _tie_layer() if name == "ties_to_higher_index" else small_layer(
+        {"bias_dropped": "mixtral_skew", "shared_gate_dropped": "qwen2moe",
+         "no_renormalisation": "mixtral"}.get(name, "deepseek"))
+    if name == "transposed_down_operand":
+        cfg = SMALL["tiny"].shrink(T=32, d=24, f=24)
+        layer = to_f64(make_layer(cfg, seed=0))
+    ref, _ = o1_vs_o2(layer, cfg)
+    permutation_pins(ref["idx"], ref["counts"], ref["offsets"], ref["perm_token"], ref["inv"], cfg.E)
+
+
+@pytest.mark.parametrize("name", list(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    if name == "unstable_permutation":
+        fn = _unstable_permutation
+    _run_pins(name)  # unmutated oracle passes
+    monkeypatch.setattr(O, attr, fn)
+    with pytest.raises(AssertionError):
+        _run_pins(name)

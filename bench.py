@@ -1,0 +1,194 @@
+"""Benchmark: one MoE expert-layer forward per step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
+
+A step is the whole hot path on one batch of synthetic tokens that is
+already resident in HBM: route -> permute -> (shared experts) -> grouped
+GEMM0 + SwiGLU -> grouped GEMM1 + fused weighted combine.  The default
+workload is the Mixtral-8x7B-shape layer (T=4096, d=4096, f=14336, E=8,
+top-2, bf16).  Prints one JSON line with the layer's throughput in TFLOP/s
+(algorithmic flops, no padding), tokens/s, the per-stage times from HIP
+events recorded on the launch stream, the roofline of the dominant kernel
+(the layer-0 grouped GEMM) and the fp64 CPU oracle timed on a bounded token
+sample of the same layer on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "MoE layer fwd TFLOP/s (% bf16 MFMA peak) + tokens/s, 1×MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral")
+    ap.add_argument("--unfused", action="store_true", help="time the deterministic unfused path")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-target-s", type=float, default=10.0,
+                    help="approximate seconds of oracle work for the CPU baseline sample")
+    return ap.parse_args()
+
+
+def stage_bytes(cfg):
+    """Algorithmic HBM bytes of the memory-bound stages (fused path)."""
+    s = 2 if cfg.dtype == "bf16" else 4
+    T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
+    R = T * k
+    return {
+        "route": T * d * s + d * E * s + T * k * 8,
+        "permute": T * k * 4 + R * 16,
+    }
+
+
+def cpu_baseline(cfg, layer, target_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload's
+    tokens with the full expert weights (the same tensors the GPU ran on;
+    the bf16 -> fp64 conversion is excluded from the time)."""
+    from threadpoolctl import threadpool_info
+    import oracle.moe_oracle as O
+    from mixture_experts_layer_top_amd.inputs import to_f64
+
+    host = to_f64(layer)
+    n = 64
+    best = None
+    while True:
+        sub = dict(host, x=host["x"][:n])
+        t0 = time.perf_counter()
+        O.forward(sub, cfg.k, cfg.renorm)
+        dt = time.perf_counter() - t0
+        best = (n, dt)
+        if dt >= target_s / 4 or n >= cfg.T:
+            break
+        n = min(cfg.T, n * 4)
+    n, dt = best
+    sub_cfg = cfg.shrink(T=n, d=cfg.d, f=cfg.f, f_shared=cfg.f_shared)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    del host
+    return {
+        "value": sub_cfg.flops() / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"first {n} of {cfg.T} tokens, full expert weights, fp64 numpy; "
+                  f"{dt:.2f} s; bf16->fp64 input conversion excluded",
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the expert layer is timed on one GPU's share "
+              "of tokens, and no multi-GPU path exists in this build (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mixture_experts_layer_top_amd.inputs import CONFIGS, make_layer
+    from mixture_experts_layer_top_amd.layer import MoeLayer
+    from mixture_experts_layer_top_amd import _lib
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    _lib.load()
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    layer = make_layer(cfg, seed=0, device=dev)
+    m = MoeLayer(cfg, layer, fused=not args.unfused, keep_logits=False)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        m.forward()
+    torch.cuda.synchronize()
+
+    stages = MoeLayer.STAGES
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        pos = [1]
+
+        def mark(_name, s=s, pos=pos):
+            ev[s][pos[0]].record(stream)
+            pos[0] += 1
+
+        m.forward(marks=mark)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    step_ms = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps)) / args.steps
+    stage_ms = {}
+    for i, name in enumerate(stages):
+        stage_ms[name] = sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    flops = cfg.flops()
+    T, d, f, k = cfg.T, cfg.d, cfg.f, cfg.k
+    R = T * k
+    g0_flops = 4 * R * d * f
+    g1_flops = 2 * R * f * d
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    g0 = g0_flops / (stage_ms["expert_up"] * 1e-3) / 1e12
+    g1 = g1_flops / (stage_ms["expert_down"] * 1e-3) / 1e12
+    by = stage_bytes(cfg)
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded Gaussian inputs and random-init weights of the layer's shapes)",
+        "config": {"workload": f"{cfg.name}: MoE expert layer T={T} d={d} f={f} E={cfg.E} "
+                               f"top-{k}" + (f" + {cfg.n_shared} shared f={cfg.f_shared}"
+                                             if cfg.n_shared else ""),
+                   "T": T, "d": d, "f": f, "E": cfg.E, "k": k,
+                   "path": "unfused" if args.unfused else "fused gather + fused combine"},
+        "pct_of_bf16_peak": round(100 * tflops / peak, 2),
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "event_ms_per_step": round(step_ms, 4),
+        "stages_ms": {kk: round(v, 4) for kk, v in stage_ms.items()},
+        "stage_rates": {
+            "expert_up_TFLOPs": round(g0, 1),
+            "expert_down_TFLOPs": round(g1, 1),
+            "route_GBs": round(by["route"] / (stage_ms["route"] * 1e-3) / 1e9, 1),
+        },
+        "roofline": {
+            "kernel": "grouped_gemm_bf16_kernel<true> (layer 0 + SwiGLU)",
+            "bound": "mfma",
+            "achieved": round(g0, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(g0 / peak, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, layer, args.cpu_target_s)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the forward pass of a Mixture-of-Experts
+ * expert layer on one MI355X (gfx950), on one GPU's share of tokens.
+ *
+ * The layer (what each call computes, and where the pages state it):
+ *   - each token activates a sparse subset of E experts
+ *       (DisagMoE technical summary, "1. Declaracao do Problema");
+ *   - the subset is the router's top-k; tokens are dispatched to their
+ *     experts and the expert outputs combined back
+ *       (DisagMoE technical summary, "2.2 AF-Pipe", stage alignment);
+ *   - experts are FFN layers ("2.1 Posicionamento de Componentes
+ *     Desagregados") made of two GEMMs, "layer 0" over the token dimension
+ *     M and "layer 1" over the hidden dimension N
+ *       (COMET page, "COMET's Technical Principles", tensor decomposition).
+ * The pages fix no score function or activation.  This library implements
+ * a softmax router with optional renormalisation of the k selected weights,
+ * and SwiGLU experts F_e(z) = (SiLU(z W_gate[e]) * (z W_up[e])) W_down[e],
+ * SiLU(h) = h / (1 + exp(-h)), without biases.
+ *
+ * Conventions shared by every call:
+ *   - every tensor pointer is a DEVICE pointer owned by the caller; tensors
+ *     are dense and row-major; no call allocates, frees or keeps device
+ *     memory between calls;
+ *   - every call is asynchronous on the given stream (NULL = the null
+ *     stream); arguments are validated on the host before anything is
+ *     launched, and a rejected call launches nothing; a device fault
+ *     surfaces at the caller's next synchronisation;
+ *   - return value: MOE_OK, or an error code (see moe_status_string);
+ *   - dtype MOE_BF16: x and weights bf16, accumulation fp32; MOE_F32: all
+ *     fp32 (the small-layer path, plain FMA, not tuned for size);
+ *   - limits: 1 <= k <= E <= 256; d, f > 0 and multiples of 8; T >= 0
+ *     (T = 0 or rows = 0 is valid: nothing to compute, and moe_permute
+ *     still writes zero counts and offsets); T*k < 2^31; pointers 16-byte
+ *     aligned;
+ *   - scratch memory comes from a caller-owned workspace whose size the
+ *     matching *_workspace_size call returns.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,     /* null required pointer, bad size, k > E, ... */
+  MOE_ERR_UNSUPPORTED = 2, /* misaligned pointer, d or f not a multiple of 8, unknown enum */
+  MOE_ERR_WORKSPACE = 3,   /* workspace smaller than *_workspace_size */
+  MOE_ERR_HIP = 4          /* a HIP launch failed */
+};
+
+enum { MOE_F32 = 0, MOE_BF16 = 1 };                          /* storage dtype */
+enum { MOE_SOFTMAX_TOPK_RENORM = 0, MOE_SOFTMAX_TOPK = 1 };  /* router weights */
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* moe_status_string(int status);
+
+/*
+ * moe_route -- router logits, top-k selection and weights.
+ * Passage: top-k expert selection per token (DisagMoE technical summary,
+ * "2.2 AF-Pipe"); sparse activation ("1. Declaracao do Problema").
+ *   logits L[t,e] = sum_i x[t,i] W_r[i,e] + bias[e], fp32 accumulation;
+ *   topk_idx[t, j]: the j-th expert of token t in the order (descending L,
+ *     ascending expert index) -- exactly equal logits go to the lower index;
+ *   topk_w[t, j] = p_sel / sum over the k picks of p (score RENORM) or p_sel
+ *     (score TOPK), p = softmax over all E logits.
+ * Arguments:
+ *   x [T, d] (dtype), W_r [d, E] (dtype), bias [E] fp32 or NULL;
+ *   topk_idx [T, k] int32 out; topk_w [T, k] fp32 out;
+ *   logits_out [T, E] fp32 out or NULL: the exact logits the selection used.
+ */
+int moe_route(const void* x, const void* W_r, const float* bias, int T, int d, int E, int k,
+              int score, int dtype, int32_t* topk_idx, float* topk_w, float* logits_out,
+              hipStream_t stream);
+
+/* Workspace bytes moe_permute needs for T tokens, E experts, top-k. */
+size_t moe_permute_workspace_size(int T, int E, int k);
+
+/*
+ * moe_permute -- dispatch: per-expert histogram, exclusive prefix scan and a
+ * stable token permutation (the dispatch of DisagMoE technical summary,
+ * "2.2 AF-Pipe"; the token fetch of COMET page, "COMET's Technical
+ * Principles", computation rescheduling).
+ *   counts[e]  = #{(t, j) : topk_idx[t, j] = e};
+ *   offsets[0] = 0, offsets[e+1] = offsets[e] + counts[e]  (offsets[E] = T*k);
+ *   the pairs of expert e take rows offsets[e] .. offsets[e+1]-1 in
+ *   ascending token order: perm_token[r] = t, inv[t, j] = r,
+ *   perm_w[r] = topk_w[t, j];
+ *   x_perm[r, :] = x[perm_token[r], :] when x_perm is not NULL (NULL: the
+ *   gather is left to moe_expert_up, which reads x through perm_token).
+ * Arguments: topk_idx [T, k] int32 with values in [0, E) (values outside are
+ *   undefined behaviour); topk_w [T, k] fp32 or NULL (then perm_w must be
+ *   NULL); x [T, d] (dtype) required only with x_perm; counts [E],
+ *   offsets [E+1], perm_token [T*k], inv [T, k] int32 out; perm_w [T*k]
+ *   fp32 out or NULL; x_perm [T*k, d] (dtype) out or NULL.
+ * The result is deterministic (no atomics decide any order).
+ */
+int moe_permute(const int32_t* topk_idx, const float* topk_w, const void* x, int T, int d, int E,
+                int k, int dtype, int32_t* counts, int32_t* offsets, int32_t* perm_token,
+                int32_t* inv, float* perm_w, void* x_perm, void* workspace, size_t ws_bytes,
+                hipStream_t stream);
+
+/* Workspace bytes moe_expert_up / moe_expert_down / moe_ffn_forward need. */
+size_t moe_ffn_workspace_size(int E, int rows, int d, int f);
+
+/*
+ * moe_expert_up -- grouped GEMM "layer 0" with fused SwiGLU (COMET page,
+ * "COMET's Technical Principles": layer 0 decomposed along the token
+ * dimension M; here its tiles are walked M-first for each weight panel).
+ * For every expert e and row r in [offsets[e], offsets[e+1]):
+ *   z = x[gather_idx[r], :] (or x[r, :] when gather_idx is NULL),
+ *   a_out[r, :] = SiLU(z W_gate[e]) * (z W_up[e]), stored in dtype (bf16
+ *   rounds to nearest even).
+ * Arguments: x [n_x, d]; gather_idx [rows] int32 or NULL; offsets [E+1]
+ *   int32 device (offsets[0] = 0, non-decreasing, offsets[E] = rows);
+ *   W_gate, W_up [E, d, f]; a_out [rows, f] out.
+ */
+int moe_expert_up(const void* x, const int32_t* gather_idx, const int32_t* offsets, int E,
+                  int rows, int d, int f, int dtype, const void* W_gate, const void* W_up,
+                  void* a_out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_expert_down -- grouped GEMM "layer 1" (COMET page, "COMET's Technical
+ * Principles": layer 1 decomposed along the hidden dimension N; tiles are
+ * walked N-first) with an optional fused top-k weighted combine
+ * (DisagMoE technical summary, "2.2 AF-Pipe", combine).
+ *   out[r, :] = a[r, :] W_down[e] for rows r of expert e;
+ *   y_perm != NULL: y_perm[r, :] = out[r, :]  (fp32, deterministic);
+ *   y != NULL:      y[scatter_idx[r], :] += row_w[r] * out[r, :]
+ *                   (fp32 atomic adds: the summation order of the k
+ *                   contributions of a token is not fixed; row_w NULL
+ *                   means weight 1, scatter_idx NULL means row r -> r).
+ * At least one of y_perm and y must be given.  y must be initialised by the
+ * caller (zero, or a shared-expert output).
+ * Arguments: a [rows, f] (dtype); offsets as in moe_expert_up;
+ *   W_down [E, f, d]; y_perm [rows, d] fp32 or NULL; scatter_idx [rows]
+ *   int32 or NULL; row_w [rows] fp32 or NULL; y [n_y, d] fp32 or NULL.
+ */
+int moe_expert_down(const void* a, const int32_t* offsets, int E, int rows, int f, int d,
+                    int dtype, const void* W_down, float* y_perm, const int32_t* scatter_idx,
+                    const float* row_w, float* y, void* workspace, size_t ws_bytes,
+                    hipStream_t stream);
+
+/*
+ * moe_ffn_forward -- moe_expert_up followed by moe_expert_down on the same
+ * stream (the expert FFN of DisagMoE technical summary, "2.1"; both GEMMs
+ * of COMET page, "COMET's Technical Principles").  a_buf [rows, f] (dtype)
+ * is the caller's buffer for the intermediate activation.
+ */
+int moe_ffn_forward(const void* x, const int32_t* gather_idx, const int32_t* offsets, int E,
+                    int rows, int d, int f, int dtype, const void* W_gate, const void* W_up,
+                    const void* W_down, void* a_buf, float* y_perm, const int32_t* scatter_idx,
+                    const float* row_w, float* y, void* workspace, size_t ws_bytes,
+                    hipStream_t stream);
+
+/*
+ * moe_combine -- top-k weighted combine / unpermute (DisagMoE technical
+ * summary, "2.2 AF-Pipe", combine), plus an optional shared-expert term:
+ *   v[t, :] = sum_j topk_w[t, j] * y_perm[inv[t, j], :]   (if inv != NULL)
+ *             + g_t * y_shared[t, :]                      (if y_shared != NULL)
+ *   g_t = 1 / (1 + exp(-shared_gate_logit[t])) (or 1 when the logit is NULL)
+ *   y = v (accumulate = 0) or y += v (accumulate = 1).
+ * With neither term, v = 0 (accumulate = 0 then clears y, e.g. before the
+ * fused combine of moe_expert_down adds into it).
+ * The k terms are summed in slot order: deterministic.
+ * Arguments: y_perm [T*k, d] fp32, inv [T, k] int32 and topk_w [T, k] fp32,
+ *   all three given or inv NULL; y_shared [T, d] fp32 or NULL;
+ *   shared_gate_logit [T] fp32 or NULL; y [T, d] fp32 out.
+ */
+int moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w, int T, int d, int k,
+                const float* y_shared, const float* shared_gate_logit, int accumulate, float* y,
+                hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,167 @@
+// C ABI of libmoe.so: argument validation on the host, then the launches.
+// Every check happens before anything is enqueued, so a rejected call has
+// no effect on the stream.  See include/moe.h for the contract of each call.
+#include "../../include/moe.h"
+
+#include "moe_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+bool dims_ok(int v) { return v > 0 && (v % 8) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument (null pointer, size out of range, or k > E)";
+    case MOE_ERR_UNSUPPORTED:
+      return "unsupported argument (misaligned pointer, dimension not a multiple of 8, or unknown enum)";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_route(const void* x, const void* W_r, const float* bias, int T, int d, int E, int k,
+              int score, int dtype, int32_t* topk_idx, float* topk_w, float* logits_out,
+              hipStream_t stream) {
+  if (T < 0 || E < 1 || E > 256 || k < 1 || k > E || d <= 0) return MOE_ERR_INVALID;
+  if ((long long)T * k >= (1ll << 31) || (long long)T * E >= (1ll << 31)) return MOE_ERR_INVALID;
+  if (!dtype_ok(dtype) || (score != MOE_SOFTMAX_TOPK_RENORM && score != MOE_SOFTMAX_TOPK))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !W_r || !topk_idx || !topk_w) return MOE_ERR_INVALID;
+  if (d % 8) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(W_r) || !aligned16(topk_idx) || !aligned16(topk_w) ||
+      (bias && !aligned16(bias)) || (logits_out && !aligned16(logits_out)))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_route(x, W_r, bias, T, d, E, k, score == MOE_SOFTMAX_TOPK_RENORM,
+                                      dtype == MOE_BF16, topk_idx, topk_w, logits_out, stream));
+}
+
+size_t moe_permute_workspace_size(int T, int E, int k) {
+  if (T < 0 || E < 1 || E > 256 || k < 1) return 0;
+  return moe::permute_workspace_bytes(T, E, k);
+}
+
+int moe_permute(const int32_t* topk_idx, const float* topk_w, const void* x, int T, int d, int E,
+                int k, int dtype, int32_t* counts, int32_t* offsets, int32_t* perm_token,
+                int32_t* inv, float* perm_w, void* x_perm, void* workspace, size_t ws_bytes,
+                hipStream_t stream) {
+  if (T < 0 || E < 1 || E > 256 || k < 1 || k > E) return MOE_ERR_INVALID;
+  if ((long long)T * k >= (1ll << 31)) return MOE_ERR_INVALID;
+  if (!dtype_ok(dtype)) return MOE_ERR_UNSUPPORTED;
+  if (!counts || !offsets) return MOE_ERR_INVALID;
+  if (T > 0 && (!topk_idx || !perm_token || !inv)) return MOE_ERR_INVALID;
+  if (perm_w && !topk_w) return MOE_ERR_INVALID;
+  if (x_perm) {
+    if (!x) return MOE_ERR_INVALID;
+    if (!dims_ok(d)) return d <= 0 ? MOE_ERR_INVALID : MOE_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_UNSUPPORTED;
+  }
+  const size_t need = moe::permute_workspace_bytes(T, E, k);
+  if (need > 0 && (!workspace || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  if (!aligned16(workspace) || !aligned16(counts) || !aligned16(offsets) ||
+      !aligned16(perm_token) || !aligned16(inv) || (perm_w && !aligned16(perm_w)))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_permute(topk_idx, topk_w, x, T, d, E, k, dtype == MOE_BF16, counts,
+                                        offsets, perm_token, inv, perm_w, x_perm, workspace,
+                                        stream));
+}
+
+size_t moe_ffn_workspace_size(int E, int rows, int d, int f) {
+  return moe::ffn_workspace_bytes(E, rows, d, f);
+}
+
+static int check_ffn_common(const int32_t* offsets, int E, int rows, int d, int f, int dtype,
+                            void* workspace, size_t ws_bytes) {
+  if (E < 1 || E > 256 || rows < 0 || d <= 0 || f <= 0) return MOE_ERR_INVALID;
+  if ((long long)rows * (d > f ? d : f) >= (1ll << 40)) return MOE_ERR_INVALID;
+  if (!dtype_ok(dtype)) return MOE_ERR_UNSUPPORTED;
+  if (!dims_ok(d) || !dims_ok(f)) return MOE_ERR_UNSUPPORTED;
+  if (rows > 0 && !offsets) return MOE_ERR_INVALID;
+  const size_t need = moe::ffn_workspace_bytes(E, rows, d, f);
+  if (need > 0 && (!workspace || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  (void)ws_bytes;
+  return MOE_OK;
+}
+
+int moe_expert_up(const void* x, const int32_t* gather_idx, const int32_t* offsets, int E,
+                  int rows, int d, int f, int dtype, const void* W_gate, const void* W_up,
+                  void* a_out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  int st = check_ffn_common(offsets, E, rows, d, f, dtype, workspace, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (rows == 0) return MOE_OK;
+  if (!x || !W_gate || !W_up || !a_out) return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(a_out) ||
+      (gather_idx && !aligned16(gather_idx)) || !aligned16(offsets))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_expert_up(x, gather_idx, offsets, E, rows, d, f,
+                                          dtype == MOE_BF16, W_gate, W_up, a_out, workspace,
+                                          stream));
+}
+
+int moe_expert_down(const void* a, const int32_t* offsets, int E, int rows, int f, int d,
+                    int dtype, const void* W_down, float* y_perm, const int32_t* scatter_idx,
+                    const float* row_w, float* y, void* workspace, size_t ws_bytes,
+                    hipStream_t stream) {
+  int st = check_ffn_common(offsets, E, rows, d, f, dtype, workspace, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (rows == 0) return MOE_OK;
+  if (!a || !W_down || (!y_perm && !y)) return MOE_ERR_INVALID;
+  if (!aligned16(a) || !aligned16(W_down) || !aligned16(offsets) ||
+      (y_perm && !aligned16(y_perm)) || (y && !aligned16(y)) ||
+      (scatter_idx && !aligned16(scatter_idx)) || (row_w && !aligned16(row_w)))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_expert_down(a, offsets, E, rows, f, d, dtype == MOE_BF16, W_down,
+                                            y_perm, scatter_idx, row_w, y, workspace, stream));
+}
+
+int moe_ffn_forward(const void* x, const int32_t* gather_idx, const int32_t* offsets, int E,
+                    int rows, int d, int f, int dtype, const void* W_gate, const void* W_up,
+                    const void* W_down, void* a_buf, float* y_perm, const int32_t* scatter_idx,
+                    const float* row_w, float* y, void* workspace, size_t ws_bytes,
+                    hipStream_t stream) {
+  int st = check_ffn_common(offsets, E, rows, d, f, dtype, workspace, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (rows == 0) return MOE_OK;
+  if (!x || !W_gate || !W_up || !W_down || !a_buf || (!y_perm && !y)) return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_down) ||
+      !aligned16(a_buf) || !aligned16(offsets) || (gather_idx && !aligned16(gather_idx)) ||
+      (y_perm && !aligned16(y_perm)) || (y && !aligned16(y)) ||
+      (scatter_idx && !aligned16(scatter_idx)) || (row_w && !aligned16(row_w)))
+    return MOE_ERR_UNSUPPORTED;
+  const bool bf = dtype == MOE_BF16;
+  hipError_t e = moe::launch_expert_up(x, gather_idx, offsets, E, rows, d, f, bf, W_gate, W_up,
+                                       a_buf, workspace, stream);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_expert_down(a_buf, offsets, E, rows, f, d, bf, W_down, y_perm,
+                                            scatter_idx, row_w, y, workspace, stream));
+}
+
+int moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w, int T, int d, int k,
+                const float* y_shared, const float* shared_gate_logit, int accumulate, float* y,
+                hipStream_t stream) {
+  if (T < 0 || k < 1 || k > 256 || d <= 0) return MOE_ERR_INVALID;
+  if ((long long)T * k >= (1ll << 31)) return MOE_ERR_INVALID;
+  if (accumulate != 0 && accumulate != 1) return MOE_ERR_INVALID;
+  if (T == 0) return MOE_OK;
+  if (!y) return MOE_ERR_INVALID;
+  if (inv && (!y_perm || !topk_w)) return MOE_ERR_INVALID;
+  if (shared_gate_logit && !y_shared) return MOE_ERR_INVALID;
+  if (d % 8) return MOE_ERR_UNSUPPORTED;
+  if ((inv && (!aligned16(y_perm) || !aligned16(inv) || !aligned16(topk_w))) || !aligned16(y) ||
+      (y_shared && !aligned16(y_shared)))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_combine(y_perm, inv, topk_w, T, d, k, y_shared, shared_gate_logit,
+                                        accumulate == 1, y, stream));
+}
+
+}  // extern "C"

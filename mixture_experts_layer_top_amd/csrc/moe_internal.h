@@ -1,0 +1,68 @@
+// Internal declarations shared by the HIP translation units of libmoe.so:
+// device helpers (bf16 conversion, wave reductions) and the host-side
+// launchers each kernel file exports to the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// float -> bfloat16 with round-to-nearest-even (inputs are finite).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float silu(float h) { return h / (1.0f + __expf(-h)); }
+
+// Round up a / b.
+__host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ __forceinline__ size_t align_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
+
+// ------------------------------------------------------------------------
+// host launchers (each returns a hipError_t of the launch)
+// ------------------------------------------------------------------------
+
+hipError_t launch_route(const void* x, const void* W_r, const float* bias, int T, int d, int E,
+                        int k, bool renorm, bool bf16, int32_t* idx, float* w, float* logits_out,
+                        hipStream_t s);
+
+size_t permute_workspace_bytes(int T, int E, int k);
+hipError_t launch_permute(const int32_t* idx, const float* topk_w, const void* x, int T, int d,
+                          int E, int k, bool bf16, int32_t* counts, int32_t* offsets,
+                          int32_t* perm_token, int32_t* inv, float* perm_w, void* x_perm,
+                          void* ws, hipStream_t s);
+
+size_t ffn_workspace_bytes(int E, int rows, int d, int f);
+hipError_t launch_expert_up(const void* x, const int32_t* gather_idx, const int32_t* offsets,
+                            int E, int rows, int d, int f, bool bf16, const void* W_gate,
+                            const void* W_up, void* a_out, void* ws, hipStream_t s);
+hipError_t launch_expert_down(const void* a, const int32_t* offsets, int E, int rows, int f,
+                              int d, bool bf16, const void* W_down, float* y_perm,
+                              const int32_t* scatter_idx, const float* row_w, float* y, void* ws,
+                              hipStream_t s);
+
+hipError_t launch_combine(const float* y_perm, const int32_t* inv, const float* topk_w, int T,
+                          int d, int k, const float* y_shared, const float* gate_logit,
+                          bool accumulate, float* y, hipStream_t s);
+
+}  // namespace moe

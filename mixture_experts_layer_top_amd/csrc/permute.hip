@@ -1,0 +1,192 @@
+// Dispatch: per-expert histogram, exclusive prefix scan, stable permutation
+// and (optionally) the gather of token rows into expert-major order.
+//
+// Dispatch of each token to its k experts: DisagMoE technical summary,
+// "2.2 AF-Pipe"; fetching the tokens an expert needs: COMET page, "COMET's
+// Technical Principles" (computation rescheduling).
+//
+// The row order is fixed (stable counting sort): expert-major, tokens
+// ascending inside an expert.  No atomic decides an order, so the result is
+// deterministic:
+//   1. hist:  each block of 256 tokens counts its (t, j) pairs per expert
+//             in LDS, writes its block histogram, and adds it into the
+//             global counts (integer adds commute);
+//   2. scan:  one workgroup turns counts into offsets and the block
+//             histograms into each block's first row per expert;
+//   3. rank:  each block walks its pairs in (t, j) order, 256 at a time;
+//             inside a wave, lanes with the same expert are found with a
+//             ballot loop and ranked by popcount of lower lanes; across
+//             waves, by a prefix over per-wave counts in LDS;
+//   4. gather (optional): x_perm[r] = x[perm_token[r]], 16-byte vectors.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kPT = 256;       // tokens per block in hist / rank
+constexpr int kThreads = 256;
+
+__global__ void zero_i32_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+__global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restrict__ idx, int T,
+                                                        int E, int k, int32_t* __restrict__ blk_cnt,
+                                                        int32_t* __restrict__ counts) {
+  __shared__ int cnt[256];
+  for (int e = threadIdx.x; e < E; e += kThreads) cnt[e] = 0;
+  __syncthreads();
+  const size_t p0 = (size_t)blockIdx.x * kPT * k;
+  const size_t p1 = min((size_t)(blockIdx.x + 1) * kPT, (size_t)T) * k;
+  for (size_t p = p0 + threadIdx.x; p < p1; p += kThreads) atomicAdd(&cnt[idx[p]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    const int c = cnt[e];
+    blk_cnt[(size_t)blockIdx.x * E + e] = c;
+    if (c) atomicAdd(&counts[e], c);
+  }
+}
+
+// One workgroup of 1024 threads.  Thread (part, e) owns a contiguous range
+// of blocks for expert e; part totals are scanned in LDS.
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts, int E,
+                                                    int nb, const int32_t* __restrict__ blk_cnt,
+                                                    int32_t* __restrict__ blk_base,
+                                                    int32_t* __restrict__ offsets) {
+  __shared__ int off[257];
+  __shared__ int part_sum[1024];
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      off[e] = run;
+      run += counts[e];
+    }
+    off[E] = run;
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += 1024) offsets[e] = off[e];
+
+  const int P = max(1, 1024 / E);  // parts per expert
+  const int e = tid % E, part = tid / E;
+  const bool active = part < P;
+  const int b_lo = active ? (int)((long long)nb * part / P) : 0;
+  const int b_hi = active ? (int)((long long)nb * (part + 1) / P) : 0;
+  int sum = 0;
+  for (int b = b_lo; b < b_hi; ++b) sum += blk_cnt[(size_t)b * E + e];
+  part_sum[tid] = sum;
+  __syncthreads();
+  if (active) {
+    int run = off[e];
+    for (int p2 = 0; p2 < part; ++p2) run += part_sum[p2 * E + e];
+    for (int b = b_lo; b < b_hi; ++b) {
+      blk_base[(size_t)b * E + e] = run;
+      run += blk_cnt[(size_t)b * E + e];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void rank_kernel(
+    const int32_t* __restrict__ idx, const float* __restrict__ topk_w, int T, int E, int k,
+    const int32_t* __restrict__ blk_base, int32_t* __restrict__ perm_token,
+    int32_t* __restrict__ inv, float* __restrict__ perm_w) {
+  __shared__ int run[256];        // rows already taken by earlier chunks, per expert
+  __shared__ int wcnt[4][256];    // per-wave counts of the current chunk
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += kThreads) {
+    run[e] = 0;
+    wcnt[0][e] = wcnt[1][e] = wcnt[2][e] = wcnt[3][e] = 0;
+  }
+  __syncthreads();
+  const int t0 = blockIdx.x * kPT;
+  const int npairs = (min(t0 + kPT, T) - t0) * k;
+  const size_t pbase = (size_t)t0 * k;
+  const int32_t* base = blk_base + (size_t)blockIdx.x * E;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+  for (int c0 = 0; c0 < npairs; c0 += kThreads) {
+    const int p = c0 + tid;
+    const bool valid = p < npairs;
+    const int e = valid ? idx[pbase + p] : -1;
+    // lanes holding the same expert
+    uint64_t todo = __ballot(valid);
+    uint64_t mine = 0;
+    while (todo) {
+      const int leader = __ffsll((unsigned long long)todo) - 1;
+      const int ve = __shfl(e, leader);
+      const uint64_t m = __ballot(valid && e == ve);
+      if (valid && e == ve) mine = m;
+      todo &= ~m;
+    }
+    const int rank_w = __popcll(mine & lt_mask);
+    if (valid && rank_w == 0) wcnt[wave][e] = __popcll(mine);
+    __syncthreads();
+    if (valid) {
+      int r = base[e] + run[e] + rank_w;
+      for (int w2 = 0; w2 < wave; ++w2) r += wcnt[w2][e];
+      const size_t pg = pbase + p;
+      perm_token[r] = (int)(pg / k);
+      inv[pg] = r;
+      if (perm_w) perm_w[r] = topk_w[pg];
+    }
+    __syncthreads();
+    for (int e2 = tid; e2 < E; e2 += kThreads) {
+      run[e2] += wcnt[0][e2] + wcnt[1][e2] + wcnt[2][e2] + wcnt[3][e2];
+      wcnt[0][e2] = wcnt[1][e2] = wcnt[2][e2] = wcnt[3][e2] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+// x_perm[r, :] = x[perm_token[r], :]; rows of `vecs` 16-byte vectors.
+constexpr int kGatherRows = 8;
+__global__ __launch_bounds__(kThreads) void gather_kernel(const u32x4* __restrict__ x,
+                                                          const int32_t* __restrict__ perm_token,
+                                                          int R, int vecs,
+                                                          u32x4* __restrict__ x_perm) {
+  const int r0 = blockIdx.x * kGatherRows;
+  const int n = min(kGatherRows, R - r0) * vecs;
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const int rr = i / vecs, c = i - rr * vecs;
+    const int r = r0 + rr;
+    const int t = perm_token[r];
+    x_perm[(size_t)r * vecs + c] = x[(size_t)t * vecs + c];
+  }
+}
+
+}  // namespace
+
+size_t permute_workspace_bytes(int T, int E, int k) {
+  (void)k;
+  const size_t nb = (size_t)cdiv(T, kPT);
+  return 2 * align_up(nb * E * sizeof(int32_t), 256);
+}
+
+hipError_t launch_permute(const int32_t* idx, const float* topk_w, const void* x, int T, int d,
+                          int E, int k, bool bf16, int32_t* counts, int32_t* offsets,
+                          int32_t* perm_token, int32_t* inv, float* perm_w, void* x_perm,
+                          void* ws, hipStream_t s) {
+  const int nb = cdiv(T, kPT);
+  int32_t* blk_cnt = static_cast<int32_t*>(ws);
+  int32_t* blk_base = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                                 align_up((size_t)nb * E * sizeof(int32_t), 256));
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(cdiv(E, 256)), dim3(256), 0, s, counts, E);
+  if (nb > 0)
+    hipLaunchKernelGGL(hist_kernel, dim3(nb), dim3(kThreads), 0, s, idx, T, E, k, blk_cnt, counts);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, counts, E, nb, blk_cnt, blk_base,
+                     offsets);
+  if (nb > 0)
+    hipLaunchKernelGGL(rank_kernel, dim3(nb), dim3(kThreads), 0, s, idx, topk_w, T, E, k,
+                       blk_base, perm_token, inv, perm_w);
+  const int R = T * k;
+  if (x_perm && R > 0) {
+    const int vecs = d * (bf16 ? 2 : 4) / 16;
+    hipLaunchKernelGGL(gather_kernel, dim3(cdiv(R, kGatherRows)), dim3(kThreads), 0, s,
+                       static_cast<const u32x4*>(x), perm_token, R, vecs,
+                       static_cast<u32x4*>(x_perm));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

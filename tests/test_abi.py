@@ -1,0 +1,146 @@
+"""The C-ABI library loads, exports every symbol include/moe.h declares, and
+rejects bad arguments on the host with the documented status codes, before
+anything is launched (so these run without a GPU).  Fake device addresses
+are safe here because a rejected call never dereferences them."""
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_top_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+A = 0x7F0000000000  # 16-byte aligned fake address
+MIS = A + 4         # misaligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\*]+\s+\*?(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libmoe.so is not built (python -m mixture_experts_layer_top_amd.build)")
+    return L.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    assert set(names) == set(L.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for st in range(5):
+        assert L.status_string(st)
+    assert "unknown" in L.status_string(99)
+
+
+def route(**kw):
+    args = dict(x=A, W_r=A, bias=None, T=16, d=64, E=8, k=2, score=0, dtype=1, topk_idx=A,
+                topk_w=A, logits_out=None)
+    args.update(kw)
+    return L.moe_route(**args, stream=0, check=False)
+
+
+def test_route_validation(lib):
+    assert route(k=9) == L.MOE_ERR_INVALID            # k > E
+    assert route(k=0) == L.MOE_ERR_INVALID
+    assert route(E=0) == L.MOE_ERR_INVALID
+    assert route(E=257, k=2) == L.MOE_ERR_INVALID
+    assert route(T=-1) == L.MOE_ERR_INVALID
+    assert route(x=None) == L.MOE_ERR_INVALID
+    assert route(topk_w=None) == L.MOE_ERR_INVALID
+    assert route(d=60) == L.MOE_ERR_UNSUPPORTED       # not a multiple of 8
+    assert route(x=MIS) == L.MOE_ERR_UNSUPPORTED
+    assert route(dtype=7) == L.MOE_ERR_UNSUPPORTED
+    assert route(score=5) == L.MOE_ERR_UNSUPPORTED
+    assert route(T=0) == L.MOE_OK                     # no-op, nothing launched
+    assert route(T=1 << 30, k=4) == L.MOE_ERR_INVALID  # T*k overflows int32 rows
+
+
+def permute(**kw):
+    args = dict(topk_idx=A, topk_w=A, x=None, T=64, d=64, E=8, k=2, dtype=1, counts=A,
+                offsets=A, perm_token=A, inv=A, perm_w=A, x_perm=None, workspace=A,
+                ws_bytes=1 << 20)
+    args.update(kw)
+    return L.moe_permute(**args, stream=0, check=False)
+
+
+def test_permute_validation(lib):
+    need = L.moe_permute_workspace_size(64, 8, 2)
+    assert need > 0
+    assert permute(ws_bytes=need - 1) == L.MOE_ERR_WORKSPACE
+    assert permute(workspace=None) == L.MOE_ERR_WORKSPACE
+    assert permute(k=9) == L.MOE_ERR_INVALID
+    assert permute(counts=None) == L.MOE_ERR_INVALID
+    assert permute(inv=None) == L.MOE_ERR_INVALID
+    assert permute(topk_w=None) == L.MOE_ERR_INVALID   # perm_w requested without weights
+    assert permute(x_perm=A) == L.MOE_ERR_INVALID      # gather requested without x
+    assert permute(x_perm=A, x=A, d=12) == L.MOE_ERR_UNSUPPORTED
+    assert permute(perm_token=MIS) == L.MOE_ERR_UNSUPPORTED
+
+
+def up(**kw):
+    args = dict(x=A, gather_idx=None, offsets=A, E=8, rows=128, d=64, f=128, dtype=1, W_gate=A,
+                W_up=A, a_out=A, workspace=A, ws_bytes=1 << 20)
+    args.update(kw)
+    return L.moe_expert_up(**args, stream=0, check=False)
+
+
+def down(**kw):
+    args = dict(a=A, offsets=A, E=8, rows=128, f=128, d=64, dtype=1, W_down=A, y_perm=A,
+                scatter_idx=None, row_w=None, y=None, workspace=A, ws_bytes=1 << 20)
+    args.update(kw)
+    return L.moe_expert_down(**args, stream=0, check=False)
+
+
+def test_ffn_validation(lib):
+    assert up(W_up=None) == L.MOE_ERR_INVALID
+    assert up(offsets=None) == L.MOE_ERR_INVALID
+    assert up(f=100) == L.MOE_ERR_UNSUPPORTED
+    assert up(d=-8) == L.MOE_ERR_INVALID
+    assert up(E=0) == L.MOE_ERR_INVALID
+    assert up(a_out=MIS) == L.MOE_ERR_UNSUPPORTED
+    assert up(rows=0) == L.MOE_OK
+    assert down(y_perm=None, y=None) == L.MOE_ERR_INVALID  # no output requested
+    assert down(y=MIS, y_perm=None) == L.MOE_ERR_UNSUPPORTED
+    assert down(dtype=3) == L.MOE_ERR_UNSUPPORTED
+    assert down(rows=0) == L.MOE_OK
+    st = L.moe_ffn_forward(A, None, A, 8, 128, 64, 128, 1, A, A, None, A, A, None, None, None, A,
+                           1 << 20, stream=0, check=False)
+    assert st == L.MOE_ERR_INVALID  # W_down missing
+
+
+def test_combine_validation(lib):
+    c = lambda **kw: L.moe_combine(**dict(dict(y_perm=A, inv=A, topk_w=A, T=16, d=64, k=2,  # noqa
+                                               y_shared=None, shared_gate_logit=None,
+                                               accumulate=0, y=A), **kw), stream=0, check=False)
+    assert c(y=None) == L.MOE_ERR_INVALID
+    assert c(topk_w=None) == L.MOE_ERR_INVALID
+    assert c(shared_gate_logit=A) == L.MOE_ERR_INVALID  # gate without a shared term
+    assert c(accumulate=2) == L.MOE_ERR_INVALID
+    assert c(d=20) == L.MOE_ERR_UNSUPPORTED
+    assert c(T=0) == L.MOE_OK
+
+
+def test_binding_raises_on_error(lib):
+    with pytest.raises(L.MoeError):
+        L.moe_route(A, A, None, 16, 64, 8, 9, 0, 1, A, A, None, stream=0)
+
+
+def test_product_path_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "mixture_experts_layer_top_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".h")):
+                src = open(os.path.join(dirpath, fn)).read()
+                assert "import oracle" not in src and "from oracle" not in src, fn
+                assert "moe_oracle" not in src, fn

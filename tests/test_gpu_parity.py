@@ -1,0 +1,310 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Bars (the design notes derive each):
+* routing: the oracle's selection run on the GPU's own fp32 logits equals
+  the GPU's top-k indices bit for bit; the GPU's fp32 logits are within the
+  certified fp32 error bound of the fp64 logits, and every token whose fp64
+  selection differs from the GPU's is a certified near-tie;
+* weights: within a relative bound derived from fp32 exp/sum/divide;
+* dispatch: counts, offsets, perm_token, inv, perm_w (and x_perm) equal the
+  oracle's on the GPU's selection, bit for bit;
+* output: max |y_gpu - y_ref| <= tau * rms(y_ref), tau = 2e-2 for bf16
+  inputs with fp32 accumulation and 1e-4 for the fp32 layer, y_ref the fp64
+  oracle at the GPU's selection.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as O
+from mixture_experts_layer_top_amd.inputs import CONFIGS, make_layer, to_f64
+
+pytestmark = pytest.mark.gpu
+
+TAU = {"bf16": 2e-2, "f32": 1e-4}
+U32 = 2.0 ** -24
+
+MID = {
+    "tiny": CONFIGS["tiny"],
+    "mixtral": CONFIGS["mixtral"].shrink(T=2000, d=520, f=392),
+    "qwen2moe": CONFIGS["qwen2moe"].shrink(T=1024, d=264, f=200, f_shared=256),
+    "mixtral_skew": CONFIGS["mixtral_skew"].shrink(T=3000, d=256, f=256),
+    "deepseek": CONFIGS["deepseek"].shrink(T=1500, d=256, f=136, f_shared=136),
+}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def L():
+    from mixture_experts_layer_top_amd import _lib
+    _lib.load()
+    return _lib
+
+
+def run_layer(cfg, layer, fused):
+    from mixture_experts_layer_top_amd.layer import MoeLayer
+    m = MoeLayer(cfg, layer, fused=fused)
+    m.forward()
+    torch.cuda.synchronize()
+    return m
+
+
+def rms(a):
+    return float(np.sqrt(np.mean(np.square(a))))
+
+
+class LazyExperts:
+    """fp64 view of a [E, a, b] device tensor, converted one expert at a time."""
+
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, e):
+        return self.t[e].to("cpu", torch.float64).numpy()
+
+
+def host_layer(layer, lazy=False):
+    out = {}
+    for k_, v in layer.items():
+        if v is None:
+            out[k_] = None
+        elif lazy and v.dim() == 3:
+            out[k_] = LazyExperts(v)
+        else:
+            out[k_] = v.to("cpu", torch.float64).numpy()
+    return out
+
+
+def check_routing(cfg, m, h):
+    """Checks (i) and (ii) of the routing bar; returns the GPU selection and
+    the near-tie tokens."""
+    k, E = cfg.k, cfg.E
+    L32 = m.logits.to("cpu", torch.float64).numpy()
+    idx_g = m.idx.cpu().numpy().astype(np.int64)
+    w_g = m.w.cpu().numpy().astype(np.float64)
+    # (i) the decision on the GPU's own logits is exact
+    idx_o = O.select_topk(L32, k)
+    bad = np.nonzero(np.any(idx_o != idx_g, axis=1))[0]
+    assert len(bad) == 0, f"selection differs on GPU logits at tokens {bad[:10]}"
+    w_o = O.topk_weights(L32, idx_o, cfg.renorm)
+    span = float(np.max(L32.max(1) - L32.min(1)))
+    w_rtol = (2 * E + 16 + 4 * span) * U32
+    np.testing.assert_allclose(w_g, w_o, rtol=w_rtol, atol=0)
+    # (ii) against fp64 logits
+    L64 = O.router_logits(h["x"], h["W_r"], h.get("b"))
+    bound = O.fp32_logit_error_bound(h["x"], h["W_r"], h.get("b"))
+    assert np.all(np.abs(L32 - L64) <= bound[:, None]), "fp32 logits outside the certified bound"
+    idx64 = O.select_topk(L64, k)
+    diff = np.nonzero(np.any(idx64 != idx_g, axis=1))[0]
+    margin = O.selection_margin(L64, k)
+    assert np.all(margin[diff] <= 2 * bound[diff]), "a routing difference is not a near-tie"
+    if len(diff):
+        log(f"  near-tie tokens (fp64 selection differs, certified): {diff.tolist()}")
+    return idx_g, w_g, diff
+
+
+def check_dispatch(cfg, m, idx_g, w_g):
+    counts, offsets, perm_token, inv, perm_w = O.dispatch(idx_g, w_g, cfg.E)
+    assert np.array_equal(m.counts.cpu().numpy(), counts)
+    assert np.array_equal(m.offsets.cpu().numpy(), offsets)
+    assert np.array_equal(m.perm_token.cpu().numpy(), perm_token)
+    assert np.array_equal(m.inv.cpu().numpy(), inv)
+    assert np.array_equal(m.perm_w.cpu().numpy().astype(np.float64), perm_w)
+    return perm_token
+
+
+def check_y(cfg, y_g, y_ref, what=""):
+    err = float(np.max(np.abs(y_g - y_ref)))
+    r = rms(y_ref)
+    tau = TAU[cfg.dtype]
+    log(f"  {cfg.name} {what}: max|dy| / rms = {err / r:.3e} (bar {tau:g})")
+    assert err <= tau * r
+
+
+# ---------------------------------------------------------------- mid sizes
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
+@pytest.mark.parametrize("name", list(MID))
+def test_layer_parity_mid(L, name, fused):
+    cfg = MID[name]
+    log(f"[parity-mid] {name} fused={fused} T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k}")
+    layer = make_layer(cfg, seed=11, device="cuda")
+    m = run_layer(cfg, layer, fused)
+    h = host_layer(layer)
+    idx_g, w_g, _ = check_routing(cfg, m, h)
+    perm_token = check_dispatch(cfg, m, idx_g, w_g)
+    if not fused:
+        assert torch.equal(m.x_perm.cpu(), layer["x"].cpu()[torch.from_numpy(perm_token)])
+    ref = O.forward(h, cfg.k, cfg.renorm, idx=idx_g)
+    check_y(cfg, m.y.cpu().double().numpy(), ref["y"], "fused" if fused else "unfused")
+
+
+def test_unfused_path_is_deterministic(L):
+    cfg = MID["deepseek"]
+    layer = make_layer(cfg, seed=3, device="cuda")
+    m1 = run_layer(cfg, layer, False)
+    y1, p1 = m1.y.clone(), m1.perm_token.clone()
+    m2 = run_layer(cfg, layer, False)
+    assert torch.equal(m2.perm_token, p1)
+    assert torch.equal(m2.y, y1)
+
+
+def test_fused_and_unfused_agree(L):
+    cfg = MID["qwen2moe"]
+    layer = make_layer(cfg, seed=5, device="cuda")
+    a = run_layer(cfg, layer, True).y.cpu().double().numpy()
+    b = run_layer(cfg, layer, False).y.cpu().double().numpy()
+    assert np.max(np.abs(a - b)) <= 1e-5 * rms(b)  # same products, only the fp32 add order differs
+
+
+# ---------------------------------------------------------------- edge cases
+
+
+def small_cfg(**kw):
+    base = dict(name="edge", cfg_id=9, T=130, d=72, f=40, E=8, k=2, renorm=True, dtype="bf16")
+    base.update(kw)
+    return CONFIGS["mixtral"].__class__(**base)
+
+
+@pytest.mark.parametrize("T", [1, 63, 65, 257])
+def test_ragged_token_counts(L, T):
+    cfg = small_cfg(T=T)
+    log(f"[edge] ragged T={T}")
+    layer = make_layer(cfg, seed=T, device="cuda")
+    m = run_layer(cfg, layer, True)
+    h = host_layer(layer)
+    idx_g, w_g, _ = check_routing(cfg, m, h)
+    check_dispatch(cfg, m, idx_g, w_g)
+    check_y(cfg, m.y.cpu().double().numpy(), O.forward(h, cfg.k, cfg.renorm, idx=idx_g)["y"])
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (4, 4), (256, 8), (3, 2)])
+def test_expert_count_extremes(L, E, k):
+    cfg = small_cfg(E=E, k=k, T=300, d=64, f=48)
+    log(f"[edge] E={E} k={k}")
+    layer = make_layer(cfg, seed=E, device="cuda")
+    m = run_layer(cfg, layer, True)
+    h = host_layer(layer)
+    idx_g, w_g, _ = check_routing(cfg, m, h)
+    check_dispatch(cfg, m, idx_g, w_g)
+    check_y(cfg, m.y.cpu().double().numpy(), O.forward(h, cfg.k, cfg.renorm, idx=idx_g)["y"])
+    if k == 1 and cfg.renorm:
+        assert np.all(w_g == 1.0)
+
+
+def test_empty_experts(L):
+    cfg = small_cfg(E=8, k=2, T=500, biased=True)
+    layer = make_layer(cfg, seed=1, device="cuda")
+    layer["b"] = torch.tensor([0, -1e4, 0, -1e4, 0, 0, -1e4, 0], dtype=torch.float32,
+                              device="cuda")
+    m = run_layer(cfg, layer, True)
+    counts = m.counts.cpu().numpy()
+    assert counts[1] == counts[3] == counts[6] == 0
+    h = host_layer(layer)
+    idx_g, w_g, _ = check_routing(cfg, m, h)
+    check_dispatch(cfg, m, idx_g, w_g)
+    check_y(cfg, m.y.cpu().double().numpy(), O.forward(h, cfg.k, cfg.renorm, idx=idx_g)["y"])
+
+
+def test_exact_ties_go_to_lower_index(L):
+    cfg = small_cfg(E=8, k=3, T=256)
+    layer = make_layer(cfg, seed=2, device="cuda")
+    layer["W_r"][:, 6] = layer["W_r"][:, 1]
+    layer["W_r"][:, 7] = layer["W_r"][:, 1]
+    m = run_layer(cfg, layer, True)
+    L32 = m.logits.cpu().numpy()
+    assert np.array_equal(L32[:, 6], L32[:, 1]) and np.array_equal(L32[:, 7], L32[:, 1])
+    idx = m.idx.cpu().numpy()
+    for row in idx:
+        r = list(row)
+        for hi in (6, 7):
+            if hi in r:
+                assert 1 in r and r.index(1) < r.index(hi)
+        if 7 in r:
+            assert 6 in r and r.index(6) < r.index(7)
+
+
+@pytest.mark.parametrize("name", ["mixtral", "deepseek", "mixtral_skew"])
+def test_zero_token_closed_form(L, name):
+    cfg = MID[name]
+    layer = make_layer(cfg, seed=4, device="cuda")
+    layer["x"][5].zero_()
+    m = run_layer(cfg, layer, True)
+    idx = m.idx[5].cpu().numpy()
+    w = m.w[5].cpu().double().numpy()
+    if cfg.biased:
+        q = 2.0 ** -1.8
+        assert idx.tolist() == [0, 1]
+        np.testing.assert_allclose(w, [1 / (1 + q), q / (1 + q)], rtol=1e-6)
+    else:
+        assert idx.tolist() == list(range(cfg.k))
+        np.testing.assert_allclose(w, 1.0 / (cfg.k if cfg.renorm else cfg.E), rtol=1e-6)
+
+
+def test_zero_tokens_is_noop(L):
+    cfg = small_cfg(T=0)
+    layer = make_layer(cfg, seed=0, device="cuda")
+    from mixture_experts_layer_top_amd.layer import MoeLayer
+    m = MoeLayer(cfg, layer, fused=True)
+    m.counts.fill_(7)
+    m.offsets.fill_(7)
+    m.forward()
+    torch.cuda.synchronize()
+    assert m.counts.cpu().tolist() == [0] * cfg.E
+    assert m.offsets.cpu().tolist() == [0] * (cfg.E + 1)
+
+
+def test_zero_projection_exact_zero(L):
+    cfg = MID["mixtral"]
+    layer = make_layer(cfg, seed=6, device="cuda")
+    layer["W_up"].zero_()
+    m = run_layer(cfg, layer, True)
+    assert torch.count_nonzero(m.y).item() == 0
+
+
+def test_down_projection_homogeneity(L):
+    cfg = MID["deepseek"]
+    layer = make_layer(cfg, seed=7, device="cuda")
+    y1 = run_layer(cfg, layer, False).y.clone()
+    layer["W_down"].mul_(2)
+    layer["Ws_down"].mul_(2)
+    y2 = run_layer(cfg, layer, False).y
+    assert torch.equal(y2, 2 * y1)
+
+
+# ---------------------------------------------------------------- full sizes
+
+
+@pytest.mark.parametrize("name", ["mixtral", "qwen2moe", "mixtral_skew", "deepseek"])
+def test_full_size_sampled(L, name):
+    """The workload at full size, in the launch configuration the benchmark
+    times (fused path): routing and dispatch checked on every token, y on a
+    sample of tokens the oracle computes one expert group at a time."""
+    cfg = CONFIGS[name]
+    log(f"[full] {name} T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k}")
+    layer = make_layer(cfg, seed=0, device="cuda")
+    m = run_layer(cfg, layer, True)
+    h = host_layer(layer, lazy=True)
+    idx_g, w_g, near = check_routing(cfg, m, h)
+    log("  routing ok")
+    check_dispatch(cfg, m, idx_g, w_g)
+    log("  dispatch ok")
+    counts = m.counts.cpu().numpy()
+    rng = np.random.default_rng(123)
+    ts = set([0, cfg.T - 1]) | set(rng.choice(cfg.T, 24, replace=False).tolist())
+    small_e = int(np.argmin(counts))
+    ts |= set(np.nonzero(np.any(idx_g == small_e, axis=1))[0][:4].tolist())
+    ts |= set(near.tolist())
+    ts = np.array(sorted(ts))
+    sub = dict(h, x=h["x"][ts])
+    ref = O.forward(sub, cfg.k, cfg.renorm, idx=idx_g[ts])
+    check_y(cfg, m.y.cpu().double().numpy()[ts], ref["y"], f"{len(ts)} sampled tokens")

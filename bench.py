@@ -39,7 +39,21 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-target-s", type=float, default=10.0,
                     help="approximate seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="instead of the layer, run a plain device copy of BYTES bytes three "
+                         "times (the reference reading for HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes):
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 3}), flush=True)
 
 
 def stage_bytes(cfg):
@@ -51,6 +65,23 @@ def stage_bytes(cfg):
         "route": T * d * s + d * E * s + T * k * 8,
         "permute": T * k * 4 + R * 16,
     }
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the layer-0 GEMM from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, or None when gemm.hip has changed since the
+    counters were taken (or they were taken on another workload)."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(HERE, "profiles", "gemm_up_traffic.json")))
+        src = open(os.path.join(HERE, rec["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest()[:16] != rec["source_sha256_16"]:
+        return None
+    if not rec["workload"].startswith(workload + " "):
+        return None
+    return rec["traffic_bytes"]
 
 
 def cpu_baseline(cfg, layer, target_s):
@@ -95,6 +126,10 @@ def main():
               "of tokens, and no multi-GPU path exists in this build (use --gpus 1).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
     from mixture_experts_layer_top_amd.inputs import CONFIGS, make_layer
@@ -182,7 +217,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(g0 / peak, 4),
-            "traffic": None,
+            "traffic": measured_traffic(cfg.name),
         },
     }
     if not args.no_cpu_baseline:

@@ -72,11 +72,15 @@ const char* moe_status_string(int status);
  * Arguments:
  *   x [T, d] (dtype), W_r [d, E] (dtype), bias [E] fp32 or NULL;
  *   topk_idx [T, k] int32 out; topk_w [T, k] fp32 out;
- *   logits_out [T, E] fp32 out or NULL: the exact logits the selection used.
+ *   logits_out [T, E] fp32 out or NULL: the exact logits the selection used;
+ *   workspace of at least moe_route_workspace_size(d, E, dtype) bytes (the
+ *   bf16 path keeps a transposed copy of W_r there during the call).
+ * The logits are summed in a fixed order: the call is deterministic.
  */
+size_t moe_route_workspace_size(int d, int E, int dtype);
 int moe_route(const void* x, const void* W_r, const float* bias, int T, int d, int E, int k,
               int score, int dtype, int32_t* topk_idx, float* topk_w, float* logits_out,
-              hipStream_t stream);
+              void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes moe_permute needs for T tokens, E experts, top-k. */
 size_t moe_permute_workspace_size(int T, int E, int k);

@@ -16,8 +16,11 @@
 //   * layer 0: the 256 columns are 128 columns of W_gate and the same 128
 //     columns of W_up, so SiLU(h) * u is formed in registers (the two
 //     accumulators of an output element sit in the same lane);
-//   * K steps of 64, double-buffered in LDS (2 x 64 KiB), one barrier per
-//     step; global loads of step i+1 are in flight while step i computes;
+//   * K stages of 32, four LDS buffers (4 x 32 KiB): three stages are in
+//     flight while one computes; one barrier per stage;
+//   * operands move HBM -> LDS with global_load_lds_dwordx4 (no register
+//     staging); one load fills 1 KiB of consecutive LDS, so each layout's
+//     swizzle is applied to the global addresses instead;
 //   * A (tokens, K contiguous) is stored row-major with the 16-byte chunk
 //     index XOR-swizzled by the row, read with ds_read_b128;
 //   * B (weights [K, N], N contiguous) is stored as is, swizzled by 32-byte
@@ -36,12 +39,29 @@ namespace moe {
 namespace {
 
 constexpr int BM = 256;        // rows per tile
-constexpr int BNA = 256;       // accumulator columns per tile
-constexpr int BK = 64;         // K per pipeline step
-constexpr int kThreads = 256;  // 4 waves
-constexpr int A_ELEMS = BM * BK;    // 16384 bf16 = 32 KiB
-constexpr int B_ELEMS = BK * BNA;   // 16384 bf16 = 32 KiB
-constexpr int STAGE = A_ELEMS + B_ELEMS;
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#endif
+constexpr int BK = MOE_GEMM_BK;  // K per pipeline stage (32 or 64)
+constexpr int A_CPR = BK / 8;    // 16-byte chunks per A row in a stage
+constexpr int A_RPL = 1024 / (BK * 2);  // A rows per 1 KiB load
+constexpr int A_LOADS = BM * BK * 2 / 1024;
+#ifndef MOE_GEMM_NST
+#define MOE_GEMM_NST (BK == 32 ? 4 : 2)
+#endif
+constexpr int NST = MOE_GEMM_NST;  // LDS stages (NST - 1 in flight while one computes)
+constexpr int A_BYTES = BM * BK * 2;  // 16 KiB per stage
+
+// Per tile-width constants.  BNA = accumulator columns per tile.
+template <int BNA>
+struct TileCfg {
+  static constexpr int B_BYTES = BK * BNA * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int CPR = BNA / 8;                     // 16-byte chunks per B row
+  static constexpr int ROWS_PER_LOAD = 1024 / (BNA * 2);  // B rows per 1 KiB load
+  static constexpr int B_LOADS = B_BYTES / 1024;
+};
+static_assert(BK == 32 || BK == 64, "stage depth");
 
 struct GemmArgs {
   const bf16_t* A;          // [n_a, K] rows (x for layer 0, activations for layer 1)
@@ -55,12 +75,14 @@ struct GemmArgs {
   const int32_t* scatter;   // layer 1 fused combine target row, or NULL (identity)
   const float* row_w;       // layer 1 fused combine weight, or NULL (1)
   float* y;                 // layer 1 fused combine target, or NULL
-  int tiles_n;              // column tiles per expert
+  int tiles_n;              // column tiles per expert, times ksplit
+  int ksplit;               // K ranges per output tile (layer 1 with fused combine only)
+  int k_per_split;          // K per range, a multiple of BK
   int grid_per_xcd;         // padded grid / 8
 };
 
 struct TileInfo {
-  int e, row0, row_end, n_t, m_t;
+  int e, row0, row_end, n_t, m_t, ks;
   bool ok;
 };
 
@@ -120,143 +142,286 @@ __device__ __forceinline__ TileInfo locate_tile(const GemmArgs& p, int tile) {
     ti.m_t = local / p.tiles_n;
     ti.n_t = local - ti.m_t * p.tiles_n;
   }
+  // the column index runs over (n-tile, K range) pairs, K range innermost
+  ti.ks = ti.n_t % p.ksplit;
+  ti.n_t = ti.n_t / p.ksplit;
   ti.row0 = toff + ti.m_t * BM;
   ti.row_end = min(ti.row0 + BM, p.offsets[ti.e + 1]);
   return ti;
 }
 
-// LDS element offsets (bf16 units) of the swizzled layouts
-__device__ __forceinline__ int a_lds_off(int row, int chunk) {  // chunk: 16 B, 0..7
-  return row * BK + ((chunk ^ (row & 7)) << 3);
+// Byte offsets inside one stage.
+// A: [BM rows][BK] bf16, 64 B per row.  A fragment read touches 16
+// consecutive rows at one 16-byte chunk.  The chunk index is XOR-ed with
+// ((row >> 1) ^ (row >> 3)) & 3, which gives distinct banks both for any 8
+// consecutive rows in a 128-byte bank window and for any 16 consecutive rows
+// in a 256-byte window.
+// B: [BK rows][BNA] bf16.  One transpose read touches 4 rows x 32 bytes per
+// 16 lanes (rows 8 apart for the next 16 lanes).  The chunk index is XOR-ed
+// with 2 * (row % 8) + (row & 8): even values keep the 32-byte pairs whole,
+// the low part spreads 4 rows over a 128-byte window and bit 3 moves rows
+// 8..15 to the other half of a 256-byte window.
+__device__ __forceinline__ int a_swz(int row) {
+  // BK = 32: 4 chunks per row; BK = 64: 8 chunks per row (then (row ^ row >> 3) & 7
+  // is distinct over any 8 consecutive rows and over the rows of one parity
+  // among 16 consecutive rows)
+  return BK == 32 ? (((row >> 1) ^ (row >> 3)) & 3) : ((row ^ (row >> 3)) & 7);
 }
-__device__ __forceinline__ int b_lds_off(int krow, int col) {  // col: bf16 index, 0..255
-  const int chunk = col >> 3;
-  return krow * BNA + ((chunk ^ ((krow & 15) << 1)) << 3) + (col & 7);
+__device__ __forceinline__ int a_off(int row, int chunk) {
+  return row * (BK * 2) + ((chunk ^ a_swz(row)) << 4);
+}
+template <int BNA>
+__device__ __forceinline__ int b_swz(int krow) {
+  constexpr int CPR = BNA / 8;  // 16 or 32 chunks per row
+  return (((krow & 7) << 1) + (krow & 8)) & (CPR - 1);
+}
+template <int BNA>
+__device__ __forceinline__ int b_off(int krow, int col) {
+  return krow * (BNA * 2) + (((col >> 3) ^ b_swz<BNA>(krow)) << 4) + ((col & 7) << 1);
 }
 
-template <bool UP>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * STAGE];
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// 16 zero bytes in device memory: A chunks past K load from here, so the
+// K tail of the last stage arrives as zeros (no clearing pass needed).
+__device__ __attribute__((aligned(16))) const bf16_t kZeroChunk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+
+#ifndef MOE_GEMM_PP
+#define MOE_GEMM_PP 0
+#endif
+
+// One direct-to-LDS load: 64 lanes x 16 bytes from their global addresses to
+// the 1 KiB of LDS starting at lds_addr (wave-uniform).  Written as inline
+// assembly so that the compiler's wait-count pass does not model it: these
+// loads are waited for explicitly with wait_vmcnt (the main loop issues no
+// other vector-memory operation, and its last stage waits for zero).
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
+  // no "memory" clobber: the compiler would then wait for all vector-memory
+  // operations before every later LDS read.  Ordering against the LDS reads
+  // of the same buffer comes from s_barrier, which the compiler does not
+  // move volatile statements across.
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gptr), "s"(lds_addr)
+      : "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// wait until at most `later` stages of LPS loads each are still in flight
+template <int LPS>
+__device__ __forceinline__ void wait_stages(int later) {
+  if (later >= 3) wait_vmcnt<3 * LPS>();
+  else if (later == 2) wait_vmcnt<2 * LPS>();
+  else if (later == 1) wait_vmcnt<LPS>();
+  else wait_vmcnt<0>();
+}
+
+// WM x WN waves; each owns (BM / WM) x (BNA / WN) accumulators.
+template <bool UP, int WM, int WN, int BNA>
+__global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(GemmArgs p) {
+  using C = TileCfg<BNA>;
+  constexpr int NW = WM * WN;
+  constexpr int NT = 64 * NW;
+  constexpr int MI = BM / WM / 16;     // 16-row blocks per wave
+  constexpr int NJ = BNA / WN / 16;    // 16-column blocks per wave
+  constexpr int A_LD = A_LOADS / NW;   // A loads per wave per stage
+  constexpr int B_LD = C::B_LOADS / NW;
+  constexpr int LPS = A_LD + B_LD;
+  static_assert(A_LD >= 1 && B_LD >= 1 && A_LOADS % NW == 0 && C::B_LOADS % NW == 0,
+                "loader split");
+  static_assert(!UP || NJ % 2 == 0, "gate/up pairs");
+  __shared__ __attribute__((aligned(1024))) char lds[NST * C::STAGE];
 
   const int b = blockIdx.x;
   const int tile = (b & 7) * p.grid_per_xcd + (b >> 3);
   const TileInfo ti = locate_tile<UP>(p, tile);
   if (!ti.ok) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
   const int K = p.K, N = p.N;
   const int n0 = ti.n_t * (UP ? BNA / 2 : BNA);
+  const uint32_t lds0 = lds_addr_of(lds);
+  const int k_begin = ti.ks * p.k_per_split;
+  const int k_end = min(K, k_begin + p.k_per_split);
 
-  // ---- global -> LDS loader setup
-  // A: thread owns chunk (tid & 7) of rows (tid >> 3) + 32 i
-  const int a_chunk = tid & 7;
-  const bf16_t* a_src[8];
-  bool a_ok[8];
+  // ---- direct-to-LDS loader.  One load moves 64 lanes x 16 B = 1 KiB into
+  // consecutive LDS bytes, so each layout's swizzle is applied on the global
+  // side: lane i fills slot i.  A load j: rows A_RPL j .. A_RPL (j + 1) - 1.
+  const bf16_t* a_src[A_LD];
+  int a_k[A_LD];  // this lane's K offset inside a stage
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = ti.row0 + (tid >> 3) + 32 * i;
-    a_ok[i] = r < ti.row_end;
-    const int src_row = a_ok[i] ? (p.gather ? p.gather[r] : r) : 0;
-    a_src[i] = p.A + (size_t)src_row * K + a_chunk * 8;
+  for (int q = 0; q < A_LD; ++q) {
+    const int row = (wave * A_LD + q) * A_RPL + lane / A_CPR;
+    a_k[q] = ((lane % A_CPR) ^ a_swz(row)) * 8;
+    int r = ti.row0 + row;
+    if (r >= ti.row_end) r = ti.row0;  // padding rows read a valid row; results are discarded
+    const int src_row = p.gather ? p.gather[r] : r;
+    a_src[q] = p.A + (size_t)src_row * K;
   }
-  // B: thread owns chunk (tid & 31) of K rows (tid >> 5) + 8 i
-  const int b_chunk = tid & 31;
-  const int b_row = tid >> 5;
-  int b_col;
-  const bf16_t* bmat;
-  if (UP) {
-    bmat = (b_chunk < 16) ? p.B0 : p.B1;
-    b_col = n0 + (b_chunk & 15) * 8;
-  } else {
-    bmat = p.B0;
-    b_col = n0 + b_chunk * 8;
-  }
-  const bool b_col_ok = b_col < N;
-  const bf16_t* b_src = bmat + (size_t)ti.e * K * N + (size_t)b_row * N + (b_col_ok ? b_col : 0);
-
-  u32x4 ra[8], rb[8];
-  auto load_global = [&](int k0) {
+  // B load j: K rows j * ROWS_PER_LOAD ..
+  const bf16_t* b_src[B_LD];
+  int b_krow[B_LD];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool ok = a_ok[i] && (k0 + a_chunk * 8 < K);
-      ra[i] = ok ? *reinterpret_cast<const u32x4*>(a_src[i] + k0) : u32x4{0u, 0u, 0u, 0u};
+  for (int q = 0; q < B_LD; ++q) {
+    const int krow = (wave * B_LD + q) * C::ROWS_PER_LOAD + lane / C::CPR;
+    const int chunk = (lane % C::CPR) ^ b_swz<BNA>(krow);
+    const bf16_t* mat;
+    int col;
+    if (UP) {
+      mat = (chunk < C::CPR / 2) ? p.B0 : p.B1;
+      col = n0 + (chunk % (C::CPR / 2)) * 8;
+    } else {
+      mat = p.B0;
+      col = n0 + chunk * 8;
+    }
+    if (col >= N) col = N - 8;  // padding columns read valid data; results are discarded
+    b_krow[q] = krow;
+    b_src[q] = mat + (size_t)ti.e * K * N + col;
+  }
+  auto issue_stage = [&](int kt) {
+    const int k0 = k_begin + kt * BK;
+    const uint32_t sb = lds0 + (uint32_t)((kt % NST) * C::STAGE);
+#pragma unroll
+    for (int q = 0; q < A_LD; ++q) {
+      const int kk = k0 + a_k[q];
+      const bf16_t* src = kk < k_end ? a_src[q] + kk : kZeroChunk;  // K tail -> zeros
+      lds_dma16(src, sb + (uint32_t)((wave * A_LD + q) * 1024));
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool ok = b_col_ok && (k0 + b_row + 8 * i < K);
-      rb[i] = ok ? *reinterpret_cast<const u32x4*>(b_src + (size_t)(k0 + 8 * i) * N)
-                 : u32x4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < B_LD; ++q) {
+      const int kr = min(k0 + b_krow[q], K - 1);
+      lds_dma16(b_src[q] + (size_t)kr * N, sb + (uint32_t)(A_BYTES + (wave * B_LD + q) * 1024));
     }
   };
-  auto store_lds = [&](int stage) {
-    bf16_t* As = lds + stage * STAGE;
-    bf16_t* Bs = As + A_ELEMS;
+
+  // ---- per-lane LDS read offsets (within a stage)
+  const int wrow0 = wm * (BM / WM);
+  constexpr int KS = BK / 32;  // MFMA K steps per stage
+  int a_rd[KS][MI];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(As + a_lds_off((tid >> 3) + 32 * i, a_chunk)) = ra[i];
+  for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(Bs + b_lds_off(b_row + 8 * i, b_chunk * 8)) = rb[i];
+    for (int mi = 0; mi < MI; ++mi)
+      a_rd[ks][mi] = a_off(wrow0 + mi * 16 + (lane & 15), ks * 4 + (lane >> 4));
+  auto col_block = [&](int nj) {
+    if (UP)
+      return (nj < NJ / 2) ? (wn * (NJ / 2) * 16 + nj * 16)
+                           : (BNA / 2 + wn * (NJ / 2) * 16 + (nj - NJ / 2) * 16);
+    return wn * NJ * 16 + nj * 16;
+  };
+  int b_rd[KS][NJ], b_rd4[KS][NJ];
+  const int b_kr = (lane >> 4) * 8 + ((lane & 15) >> 2);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int nj = 0; nj < NJ; ++nj) {
+      // rows b_kr and b_kr + 4 differ in their swizzle: separate offsets
+      b_rd[ks][nj] = b_off<BNA>(ks * 32 + b_kr, col_block(nj) + (lane & 3) * 4);
+      b_rd4[ks][nj] = b_off<BNA>(ks * 32 + b_kr + 4, col_block(nj) + (lane & 3) * 4);
+    }
+
+  f32x4 acc[MI][NJ];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < NJ; ++nj) acc[mi][nj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = cdiv(k_end - k_begin, BK);
+  auto read_frags = [&](int kt, int ks, bf16x8 (&af)[MI], bf16x8 (&bfr)[NJ]) {
+    const char* As = lds + (kt % NST) * C::STAGE;
+    const char* Bs = As + A_BYTES;
+#pragma unroll
+    for (int nj = 0; nj < NJ; ++nj) {
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Bs + b_rd[ks][nj]));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Bs + b_rd4[ks][nj]));
+      bfr[nj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) af[mi] = *reinterpret_cast<const bf16x8*>(As + a_rd[ks][mi]);
+  };
+  auto mfmas = [&](const bf16x8 (&af)[MI], const bf16x8 (&bfr)[NJ]) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < NJ; ++nj)
+        acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[nj], acc[mi][nj], 0, 0, 0);
   };
 
-  // ---- per-lane LDS read offsets
-  int a_rd[8][2];
 #pragma unroll
-  for (int mi = 0; mi < 8; ++mi)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      a_rd[mi][ks] = a_lds_off(wm * 128 + mi * 16 + (lane & 15), ks * 4 + (lane >> 4));
-  int b_col_l[8];
-#pragma unroll
-  for (int nj = 0; nj < 8; ++nj) {
-    int c0;
-    if (UP) c0 = (nj < 4) ? (wn * 64 + nj * 16) : (128 + wn * 64 + (nj - 4) * 16);
-    else c0 = wn * 128 + nj * 16;
-    b_col_l[nj] = c0 + (lane & 3) * 4;
-  }
-  const int b_krow = (lane >> 4) * 8 + ((lane & 15) >> 2);
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nk) issue_stage(s);
+  // a wave whose rows all lie past the expert's last row (the tail tile of
+  // an expert) still loads its share of the operands but skips the MFMAs
+#ifndef MOE_GEMM_NO_WAVE_SKIP
+  const bool wave_active = wrow0 < ti.row_end - ti.row0;
+#else
+  constexpr bool wave_active = true;
+#endif
 
-  f32x4 acc[8][8];
-#pragma unroll
-  for (int mi = 0; mi < 8; ++mi)
-#pragma unroll
-    for (int nj = 0; nj < 8; ++nj) acc[mi][nj] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nk = cdiv(K, BK);
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+#if MOE_GEMM_PP
+  // Ping-pong: the two halves of the waves (one wave of each per SIMD) run
+  // one barrier apart, so while one half reads its fragments from LDS the
+  // other half keeps the SIMD's matrix core busy.  Per stage kt each wave
+  // runs a memory phase (refill the buffer of stage kt - 1, read stage kt's
+  // fragments) and a compute phase, each closed by a barrier.  Visibility:
+  // before the barrier that precedes any read of stage kt + 1, every wave
+  // has waited for its own loads of that stage (half 1 at the end of its
+  // memory phase, half 0 at the end of its compute phase).  Reuse: a buffer
+  // is refilled only after the barrier that closes the last memory phase
+  // reading it, and every wave drains its LDS reads before that barrier.
+  static_assert(NW == 8 && WM == 2 && KS == 1, "ping-pong pairs the two row halves");
+  const int half = wm;
+  wait_stages<LPS>(min(NST - 2, nk - 1));
+  __builtin_amdgcn_s_barrier();
+  if (half == 1) __builtin_amdgcn_s_barrier();
   for (int kt = 0; kt < nk; ++kt) {
-    const int stage = kt & 1;
-    if (kt + 1 < nk) load_global((kt + 1) * BK);
-    const bf16_t* As = lds + stage * STAGE;
-    const bf16_t* Bs = As + A_ELEMS;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 af[8], bfr[8];
-#pragma unroll
-      for (int mi = 0; mi < 8; ++mi) af[mi] = *reinterpret_cast<const bf16x8*>(As + a_rd[mi][ks]);
-#pragma unroll
-      for (int nj = 0; nj < 8; ++nj) {
-        const int kr = ks * 32 + b_krow;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4*)(Bs + b_lds_off(kr, b_col_l[nj])));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4*)(Bs + b_lds_off(kr + 4, b_col_l[nj])));
-        bfr[nj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-#pragma unroll
-      for (int mi = 0; mi < 8; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < 8; ++nj)
-          acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[nj], acc[mi][nj], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_lds(stage ^ 1);
-    __syncthreads();
+    if (kt + NST - 1 < nk) issue_stage(kt + NST - 1);
+    bf16x8 af[MI], bfr[NJ];
+    read_frags(kt, 0, af, bfr);
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    if (half == 1 && kt + 1 < nk) wait_stages<LPS>(min(NST - 2, nk - 2 - kt));
+    __builtin_amdgcn_s_barrier();
+    mfmas(af, bfr);
+    if (half == 0 && kt + 1 < nk) wait_stages<LPS>(min(NST - 2, nk - 2 - kt));
+    __builtin_amdgcn_s_barrier();
   }
+  if (half == 0) __builtin_amdgcn_s_barrier();
+  wait_vmcnt<0>();
+#else
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt has landed once at most the loads of the later stages issued
+    // so far are outstanding; then every wave's share is visible after the
+    // barrier, and every wave is done with the buffer of stage kt - 1
+    wait_stages<LPS>(min(NST - 2, nk - 1 - kt));
+    __builtin_amdgcn_s_barrier();
+    bf16x8 af[MI], bfr[NJ];
+    if (wave_active) read_frags(kt, 0, af, bfr);
+    // refill the buffer of stage kt - 1 (issued after this stage's first
+    // reads so that no read waits for the new loads)
+    if (kt + NST - 1 < nk) issue_stage(kt + NST - 1);
+    if (wave_active) mfmas(af, bfr);
+#pragma unroll
+    for (int ks = 1; ks < KS; ++ks) {
+      if (wave_active) {
+        read_frags(kt, ks, af, bfr);
+        mfmas(af, bfr);
+      }
+    }
+  }
+#endif
 
   // ---- epilogue.  Accumulator layout of a 16 x 16 block: column lane % 16,
   // rows 4 * (lane / 16) + i.
@@ -264,25 +429,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(GemmArgs
   const int row_l = (lane >> 4) * 4;
   if (UP) {
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi) {
+    for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = ti.row0 + wm * 128 + mi * 16 + row_l + i;
+        const int row = ti.row0 + wrow0 + mi * 16 + row_l + i;
         if (row >= ti.row_end) continue;
         bf16_t* orow = p.a_out + (size_t)row * N;
 #pragma unroll
-        for (int nj = 0; nj < 4; ++nj) {
-          const int col = n0 + wn * 64 + nj * 16 + col_l;
-          if (col < N) orow[col] = f32_to_bf16(silu(acc[mi][nj][i]) * acc[mi][nj + 4][i]);
+        for (int nj = 0; nj < NJ / 2; ++nj) {
+          const int col = n0 + col_block(nj) + col_l;
+          if (col < N) orow[col] = f32_to_bf16(silu(acc[mi][nj][i]) * acc[mi][nj + NJ / 2][i]);
         }
       }
     }
   } else {
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi) {
+    for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = ti.row0 + wm * 128 + mi * 16 + row_l + i;
+        const int row = ti.row0 + wrow0 + mi * 16 + row_l + i;
         if (row >= ti.row_end) continue;
         float* prow = p.y_perm ? p.y_perm + (size_t)row * N : nullptr;
         float* yrow = nullptr;
@@ -293,8 +458,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(GemmArgs
           if (p.row_w) wgt = p.row_w[row];
         }
 #pragma unroll
-        for (int nj = 0; nj < 8; ++nj) {
-          const int col = n0 + wn * 128 + nj * 16 + col_l;
+        for (int nj = 0; nj < NJ; ++nj) {
+          const int col = n0 + col_block(nj) + col_l;
           if (col >= N) continue;
           const float v = acc[mi][nj][i];
           if (prow) prow[col] = v;
@@ -361,6 +526,74 @@ int max_tiles_m(int rows, int E) {
   return (int)(((long long)rows + (long long)E * (BM - 1)) / BM);
 }
 
+#ifndef MOE_UP_WN
+#define MOE_UP_WN 4
+#endif
+#ifndef MOE_UP_BNA
+#define MOE_UP_BNA 256
+#endif
+#ifndef MOE_DN_WN
+#define MOE_DN_WN 4
+#endif
+#ifndef MOE_DN_BNA
+#define MOE_DN_BNA 256
+#endif
+constexpr int UP_WN = MOE_UP_WN, UP_BNA = MOE_UP_BNA, DN_WN = MOE_DN_WN, DN_BNA = MOE_DN_BNA;
+
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// K ranges per layer-1 tile.  Only with the fused combine (its atomic adds
+// take partial sums for free): pick the smallest split that fills the last
+// round of tiles on the CUs to >= 90%, else the best of 1..4.
+int choose_ksplit(long long tiles, int K, int cus) {
+  int best = 1;
+  double best_eff = 0.0;
+  for (int sp = 1; sp <= 4; ++sp) {
+    if ((long long)sp * BK > K) break;
+    const double work = (double)tiles * sp / cus;
+    const double eff = work / (double)((long long)((tiles * sp + cus - 1) / cus));
+    if (eff >= 0.9) return sp;
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = sp;
+    }
+  }
+  return best;
+}
+
+template <bool UP, int WM, int WN, int BNA>
+hipError_t launch_gemm(GemmArgs& p, int rows, int E, int ncols, hipStream_t s) {
+  const int tiles_n = cdiv(ncols, UP ? BNA / 2 : BNA);
+  const long long tiles_mn = (long long)max_tiles_m(rows, E) * tiles_n;
+  int ksplit = 1;
+  (void)tiles_mn;
+#ifdef MOE_GEMM_KSPLIT
+  // measured slower on the Mixtral-shape layer (the extra atomic traffic
+  // outweighs the fuller last round of tiles), so off unless asked for
+  if (!UP && p.y != nullptr && p.y_perm == nullptr) ksplit = choose_ksplit(tiles_mn, p.K, num_cus());
+#endif
+  p.k_per_split = cdiv(cdiv(p.K, ksplit), BK) * BK;
+  p.ksplit = cdiv(p.K, p.k_per_split);
+  p.tiles_n = tiles_n * p.ksplit;
+  const long long tiles = (long long)max_tiles_m(rows, E) * p.tiles_n;
+  const long long grid = (tiles + 7) / 8 * 8;
+  p.grid_per_xcd = (int)(grid / 8);
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<UP, WM, WN, BNA>), dim3((unsigned)grid),
+                     dim3(64 * WM * WN), 0, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t ffn_workspace_bytes(int E, int rows, int d, int f) {
@@ -389,12 +622,7 @@ hipError_t launch_expert_up(const void* x, const int32_t* gather_idx, const int3
   p.B0 = static_cast<const bf16_t*>(W_gate);
   p.B1 = static_cast<const bf16_t*>(W_up);
   p.a_out = static_cast<bf16_t*>(a_out);
-  p.tiles_n = cdiv(f, BNA / 2);
-  const long long tiles = (long long)max_tiles_m(rows, E) * p.tiles_n;
-  const long long grid = (tiles + 7) / 8 * 8;
-  p.grid_per_xcd = (int)(grid / 8);
-  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+  return launch_gemm<true, 2, UP_WN, UP_BNA>(p, rows, E, f, s);
 }
 
 hipError_t launch_expert_down(const void* a, const int32_t* offsets, int E, int rows, int f,
@@ -421,12 +649,7 @@ hipError_t launch_expert_down(const void* a, const int32_t* offsets, int E, int 
   p.scatter = scatter_idx;
   p.row_w = row_w;
   p.y = y;
-  p.tiles_n = cdiv(d, BNA);
-  const long long tiles = (long long)max_tiles_m(rows, E) * p.tiles_n;
-  const long long grid = (tiles + 7) / 8 * 8;
-  p.grid_per_xcd = (int)(grid / 8);
-  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+  return launch_gemm<false, 2, DN_WN, DN_BNA>(p, rows, E, d, s);
 }
 
 }  // namespace moe

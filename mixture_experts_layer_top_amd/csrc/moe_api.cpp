@@ -29,9 +29,14 @@ const char* moe_status_string(int status) {
   }
 }
 
+size_t moe_route_workspace_size(int d, int E, int dtype) {
+  if (d <= 0 || E < 1 || E > 256 || !dtype_ok(dtype)) return 0;
+  return moe::route_workspace_bytes(d, E, dtype == MOE_BF16);
+}
+
 int moe_route(const void* x, const void* W_r, const float* bias, int T, int d, int E, int k,
               int score, int dtype, int32_t* topk_idx, float* topk_w, float* logits_out,
-              hipStream_t stream) {
+              void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (T < 0 || E < 1 || E > 256 || k < 1 || k > E || d <= 0) return MOE_ERR_INVALID;
   if ((long long)T * k >= (1ll << 31) || (long long)T * E >= (1ll << 31)) return MOE_ERR_INVALID;
   if (!dtype_ok(dtype) || (score != MOE_SOFTMAX_TOPK_RENORM && score != MOE_SOFTMAX_TOPK))
@@ -39,11 +44,15 @@ int moe_route(const void* x, const void* W_r, const float* bias, int T, int d, i
   if (T == 0) return MOE_OK;
   if (!x || !W_r || !topk_idx || !topk_w) return MOE_ERR_INVALID;
   if (d % 8) return MOE_ERR_UNSUPPORTED;
+  const size_t need = moe::route_workspace_bytes(d, E, dtype == MOE_BF16);
+  if (need > 0 && (!workspace || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(W_r) || !aligned16(topk_idx) || !aligned16(topk_w) ||
-      (bias && !aligned16(bias)) || (logits_out && !aligned16(logits_out)))
+      (bias && !aligned16(bias)) || (logits_out && !aligned16(logits_out)) ||
+      (workspace && !aligned16(workspace)))
     return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_route(x, W_r, bias, T, d, E, k, score == MOE_SOFTMAX_TOPK_RENORM,
-                                      dtype == MOE_BF16, topk_idx, topk_w, logits_out, stream));
+                                      dtype == MOE_BF16, topk_idx, topk_w, logits_out, workspace,
+                                      stream));
 }
 
 size_t moe_permute_workspace_size(int T, int E, int k) {

@@ -32,7 +32,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
-__device__ __forceinline__ float silu(float h) { return h / (1.0f + __expf(-h)); }
+// SiLU(h) = h / (1 + exp(-h)), with the hardware reciprocal (about 1 ulp)
+__device__ __forceinline__ float silu(float h) {
+  return h * __builtin_amdgcn_rcpf(1.0f + __expf(-h));
+}
 
 // Round up a / b.
 __host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
@@ -42,9 +45,10 @@ __host__ __device__ __forceinline__ size_t align_up(size_t a, size_t b) { return
 // host launchers (each returns a hipError_t of the launch)
 // ------------------------------------------------------------------------
 
+size_t route_workspace_bytes(int d, int E, bool bf16);
 hipError_t launch_route(const void* x, const void* W_r, const float* bias, int T, int d, int E,
                         int k, bool renorm, bool bf16, int32_t* idx, float* w, float* logits_out,
-                        hipStream_t s);
+                        void* ws, hipStream_t s);
 
 size_t permute_workspace_bytes(int T, int E, int k);
 hipError_t launch_permute(const int32_t* idx, const float* topk_w, const void* x, int T, int d,

@@ -2,27 +2,29 @@
 //
 // Top-k expert choice per token: DisagMoE technical summary, "2.2 AF-Pipe".
 //
-// bf16 path: a workgroup of 4 wave64s takes 64 tokens (16 per wave).  The
-// logits L = x W_r are a skinny contraction (E <= 256 columns); each wave
-// runs v_mfma_f32_16x16x32_bf16 with its 16 token rows as the A operand,
-// read straight from HBM (16 contiguous bytes of K per lane), and W_r as the
-// B operand.  W_r is row-major [d, E] (E contiguous), so a 64-row chunk of
-// it is staged in LDS as is and read back with ds_read_b64_tr_b16, which
-// hands each lane 4 consecutive K values of one column.  Products of bf16
-// are exact in fp32; the sum is fp32.  The kernel is bound by reading x
-// from HBM once.
+// bf16 path.  The logits L = x W_r are a skinny contraction (E <= 256
+// columns) bound by reading x from HBM once:
+//   1. a small pre-pass writes W_r transposed (K contiguous, [E_pad, d], zero
+//      rows past E) into the caller's workspace; it is at most d * 256 * 2
+//      bytes and stays in L2 for the main pass;
+//   2. a workgroup of 4 wave64s takes 16 * MB tokens; the 4 waves split K
+//      four ways, and each wave streams its token rows (A operand, 16
+//      contiguous K-bytes per lane) and the transposed W_r rows (B operand,
+//      likewise) straight from memory into v_mfma_f32_16x16x32_bf16 -- no LDS
+//      staging, no barrier in the loop.  bf16 products are exact in fp32;
+//      sums are fp32;
+//   3. the four partial logits are added in wave order (deterministic), the
+//      bias added, and the result kept in LDS for the selection.
 //
-// Selection and weights: the logits go to LDS; 4 lanes serve one token and
-// each scans every 4th expert.  The j-th pick is the best (value desc,
-// index asc) among experts strictly below the (j-1)-th pick in that order,
-// so no pick is ever marked; equal logits go to the lower index.
+// Selection and weights: 4 lanes serve one token and each scans every 4th
+// expert.  The j-th pick is the best (value desc, index asc) among experts
+// strictly below the (j-1)-th pick in that order, so no pick is ever marked;
+// exactly equal logits go to the lower index.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kTok = 64;   // tokens per workgroup
-constexpr int kKC = 64;    // rows of W_r staged per chunk
 constexpr int kThreads = 256;
 
 struct RouteArgs {
@@ -35,12 +37,14 @@ struct RouteArgs {
   float* logits_out;
 };
 
-// Softmax top-k over the logits rows of this workgroup (in LDS), one wave
-// per 16 tokens, 4 lanes per token.
+// Softmax top-k over `ntok` logits rows in LDS, one wave per 16 tokens, 4
+// lanes per token.  Waves past the last 16-token group return (whole waves,
+// so the 4-lane shuffles stay uniform).
 __device__ __forceinline__ void select_and_weigh(const float* ll, int lstride, const RouteArgs& a,
-                                                 int t_base) {
+                                                 int t_base, int ntok) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  if (wave * 16 >= ntok) return;
   const int tt = wave * 16 + (lane >> 2);
   const int q = lane & 3;
   const int t = t_base + tt;
@@ -99,9 +103,9 @@ __device__ __forceinline__ void select_and_weigh(const float* ll, int lstride, c
 }
 
 __device__ __forceinline__ void write_logits(const float* ll, int lstride, const RouteArgs& a,
-                                             int t_base) {
+                                             int t_base, int ntok) {
   if (a.logits_out == nullptr) return;
-  const int n = kTok * a.E;
+  const int n = ntok * a.E;
   for (int i = threadIdx.x; i < n; i += kThreads) {
     const int tt = i / a.E, e = i - tt * a.E;
     const int t = t_base + tt;
@@ -109,84 +113,117 @@ __device__ __forceinline__ void write_logits(const float* ll, int lstride, const
   }
 }
 
-// NB = ceil(E / 16) column blocks of 16 experts.
-template <int NB>
-__global__ __launch_bounds__(kThreads) void route_bf16_kernel(RouteArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int Ep = NB * 16;
-  constexpr int ws = Ep + 8;  // LDS row stride of the W_r chunk, in bf16 (16 B pad)
-  constexpr int ls = Ep + 1;  // LDS row stride of the logits, in floats
-  bf16_t* wl = reinterpret_cast<bf16_t*>(smem);
-  float* ll = reinterpret_cast<float*>(smem + kKC * ws * 2);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t_base = blockIdx.x * kTok;
-  const int my_t = t_base + wave * 16 + (lane & 15);
-  const bool t_ok = my_t < a.T;
-  const bf16_t* W = static_cast<const bf16_t*>(a.W);
-  const bf16_t* xrow = static_cast<const bf16_t*>(a.x) + (size_t)(t_ok ? my_t : 0) * a.d;
-  const int d = a.d, E = a.E;
-
-  f32x4 acc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = 0; k0 < d; k0 += kKC) {
-    __syncthreads();  // the previous chunk has been consumed
-    for (int i = tid; i < kKC * Ep; i += kThreads) {
-      const int r = i / Ep, c = i - r * Ep;
-      bf16_t v = 0;
-      if (k0 + r < d && c < E) v = W[(size_t)(k0 + r) * E + c];
-      wl[r * ws + c] = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < kKC; ks += 32) {
-      const int kk = k0 + ks + (lane >> 4) * 8;
-      bf16x8 av;
-      if (t_ok && kk < d) {
-        av = *reinterpret_cast<const bf16x8*>(xrow + kk);
-      } else {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) av[u] = (__bf16)0.0f;
-      }
-      const int rr = ks + (lane >> 4) * 8 + ((lane & 15) >> 2);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int cc = nb * 16 + (lane & 3) * 4;
-        typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-        const bf16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4*)(wl + rr * ws + cc));
-        const bf16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4*)(wl + (rr + 4) * ws + cc));
-        const bf16x8 bv = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[nb], 0, 0, 0);
-      }
-    }
-  }
-
-  // accumulator lane layout of a 16x16 block: column = lane % 16, rows =
-  // 4 * (lane / 16) + i
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int e = nb * 16 + (lane & 15);
-    if (e < E) {
-      const float b = a.bias ? a.bias[e] : 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tt = wave * 16 + (lane >> 4) * 4 + i;
-        ll[tt * ls + e] = acc[nb][i] + b;
-      }
-    }
+// W_t[e, k] = W_r[k, e] for e < E, 0 for E <= e < Ep.  One block per 64 rows of W_r.
+__global__ __launch_bounds__(kThreads) void transpose_router_kernel(const bf16_t* __restrict__ W,
+                                                                   int d, int E, int Ep,
+                                                                   bf16_t* __restrict__ Wt) {
+  __shared__ bf16_t tile[64][257];
+  const int k0 = blockIdx.x * 64;
+  for (int i = threadIdx.x; i < 64 * E; i += kThreads) {
+    const int r = i / E, e = i - r * E;
+    tile[r][e] = (k0 + r < d) ? W[(size_t)(k0 + r) * E + e] : (bf16_t)0;
   }
   __syncthreads();
-  write_logits(ll, ls, a, t_base);
-  select_and_weigh(ll, ls, a, t_base);
+  for (int i = threadIdx.x; i < Ep * 64; i += kThreads) {
+    const int e = i / 64, r = i - e * 64;
+    if (k0 + r < d) Wt[(size_t)e * d + k0 + r] = (e < E) ? tile[r][e] : (bf16_t)0;
+  }
 }
 
-// fp32 path (small layers): plain sequential FMA dot products.
+// NB = ceil(E / 16) column blocks of 16 experts; MB = token blocks of 16 per workgroup.
+template <int NB, int MB>
+__global__ __launch_bounds__(kThreads) void route_bf16_kernel(RouteArgs a, const bf16_t* __restrict__ Wt) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int Ep = NB * 16;
+  constexpr int TW = MB * 16;   // tokens per workgroup
+  constexpr int ls = Ep + 1;    // LDS row stride of the logits, in floats
+  float* part = reinterpret_cast<float*>(smem);  // [4][TW][Ep] partial logits
+  float* ll = part;                               // [TW][ls] logits (reuses part)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t_base = blockIdx.x * TW;
+  const int d = a.d, E = a.E;
+  const int kq = cdiv(cdiv(d, 4), 32) * 32;  // K per wave, a multiple of 32
+  const int kb = wave * kq, ke = min(d, kb + kq);
+
+  const bf16_t* xr[MB];
+  bool t_ok[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int t = t_base + mb * 16 + (lane & 15);
+    t_ok[mb] = t < a.T;
+    xr[mb] = static_cast<const bf16_t*>(a.x) + (size_t)(t_ok[mb] ? t : 0) * d;
+  }
+  const bf16_t* wr[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) wr[nb] = Wt + (size_t)(nb * 16 + (lane & 15)) * d;
+
+  f32x4 acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bf16x8 zero8 = {};
+#pragma unroll 4
+  for (int k0 = kb; k0 < ke; k0 += 32) {
+    const int kk = k0 + (lane >> 4) * 8;
+    const bool kin = kk < ke;  // d % 8 == 0: a lane's 8 values are all in or all out
+    bf16x8 av[MB], bv[NB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      av[mb] = (kin && t_ok[mb]) ? *reinterpret_cast<const bf16x8*>(xr[mb] + kk) : zero8;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      bv[nb] = kin ? *reinterpret_cast<const bf16x8*>(wr[nb] + kk) : zero8;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mb], bv[nb], acc[mb][nb], 0, 0, 0);
+  }
+
+  // accumulator lane layout of a 16x16 block: column lane % 16, rows
+  // 4 * (lane / 16) + i
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tt = mb * 16 + (lane >> 4) * 4 + i;
+        part[(wave * TW + tt) * Ep + nb * 16 + (lane & 15)] = acc[mb][nb][i];
+      }
+  __syncthreads();
+  // sum the four K quarters in wave order, add the bias
+  float lv[(TW * Ep + kThreads - 1) / kThreads];
+#pragma unroll
+  for (int u = 0; u < (TW * Ep + kThreads - 1) / kThreads; ++u) {
+    const int i = tid + u * kThreads;
+    float v = 0.f;
+    if (i < TW * Ep) {
+      const int e = i % Ep;
+      v = part[i] + part[TW * Ep + i] + part[2 * TW * Ep + i] + part[3 * TW * Ep + i];
+      if (a.bias && e < E) v += a.bias[e];
+    }
+    lv[u] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < (TW * Ep + kThreads - 1) / kThreads; ++u) {
+    const int i = tid + u * kThreads;
+    if (i < TW * Ep) ll[(i / Ep) * ls + (i % Ep)] = lv[u];
+  }
+  __syncthreads();
+  write_logits(ll, ls, a, t_base, TW);
+  select_and_weigh(ll, ls, a, t_base, TW);
+}
+
+// fp32 path (small layers): plain sequential FMA dot products, 64 tokens
+// per workgroup.
 __global__ __launch_bounds__(kThreads) void route_f32_kernel(RouteArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int kTok = 64;
   float* ll = reinterpret_cast<float*>(smem);
   const int ls = a.E + 1;
   const int t_base = blockIdx.x * kTok;
@@ -203,57 +240,75 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(RouteArgs a) {
     ll[tt * ls + e] = acc + (a.bias ? a.bias[e] : 0.f);
   }
   __syncthreads();
-  write_logits(ll, ls, a, t_base);
-  select_and_weigh(ll, ls, a, t_base);
+  write_logits(ll, ls, a, t_base, kTok);
+  select_and_weigh(ll, ls, a, t_base, kTok);
 }
 
-template <int NB>
-hipError_t launch_nb(const RouteArgs& a, int grid, hipStream_t s) {
-  constexpr int Ep = NB * 16;
-  const size_t lds = (size_t)kKC * (Ep + 8) * 2 + (size_t)kTok * (Ep + 1) * 4;
+template <int NB, int MB>
+hipError_t launch_nb_mb(const RouteArgs& a, const bf16_t* Wt, hipStream_t s) {
+  constexpr int Ep = NB * 16, TW = MB * 16;
+  const size_t lds = (size_t)4 * TW * Ep * 4;  // >= TW * (Ep + 1) * 4, the logits reuse it
   if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)route_bf16_kernel<NB>,
+    hipError_t e = hipFuncSetAttribute((const void*)route_bf16_kernel<NB, MB>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(route_bf16_kernel<NB>, dim3(grid), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((route_bf16_kernel<NB, MB>), dim3(cdiv(a.T, TW)), dim3(kThreads), lds, s, a, Wt);
   return hipGetLastError();
+}
+
+// Token blocks per workgroup: as many as keep >= 256 workgroups in flight
+// and the partial-logit buffer at <= 32 KiB.
+template <int NB>
+hipError_t launch_nb(const RouteArgs& a, const bf16_t* Wt, hipStream_t s) {
+  constexpr int Ep = NB * 16;
+  if (a.T >= 256 * 64 && 64 * Ep <= 2048) return launch_nb_mb<NB, 4>(a, Wt, s);
+  if (a.T >= 256 * 32 && 32 * Ep <= 2048) return launch_nb_mb<NB, 2>(a, Wt, s);
+  return launch_nb_mb<NB, 1>(a, Wt, s);
 }
 
 }  // namespace
 
+size_t route_workspace_bytes(int d, int E, bool bf16) {
+  if (!bf16) return 0;
+  return align_up((size_t)cdiv(E, 16) * 16 * d * sizeof(bf16_t), 256);
+}
+
 hipError_t launch_route(const void* x, const void* W_r, const float* bias, int T, int d, int E,
                         int k, bool renorm, bool bf16, int32_t* idx, float* w, float* logits_out,
-                        hipStream_t s) {
+                        void* ws, hipStream_t s) {
   RouteArgs a{x, W_r, bias, T, d, E, k, renorm ? 1 : 0, idx, w, logits_out};
-  const int grid = cdiv(T, kTok);
   if (!bf16) {
-    const size_t lds = (size_t)kTok * (E + 1) * 4;
+    const size_t lds = (size_t)64 * (E + 1) * 4;
     if (lds > 65536) {
       hipError_t e = hipFuncSetAttribute((const void*)route_f32_kernel,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(route_f32_kernel, dim3(grid), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL(route_f32_kernel, dim3(cdiv(T, 64)), dim3(kThreads), lds, s, a);
     return hipGetLastError();
   }
-  switch (cdiv(E, 16)) {
-    case 1: return launch_nb<1>(a, grid, s);
-    case 2: return launch_nb<2>(a, grid, s);
-    case 3: return launch_nb<3>(a, grid, s);
-    case 4: return launch_nb<4>(a, grid, s);
-    case 5: return launch_nb<5>(a, grid, s);
-    case 6: return launch_nb<6>(a, grid, s);
-    case 7: return launch_nb<7>(a, grid, s);
-    case 8: return launch_nb<8>(a, grid, s);
-    case 9: return launch_nb<9>(a, grid, s);
-    case 10: return launch_nb<10>(a, grid, s);
-    case 11: return launch_nb<11>(a, grid, s);
-    case 12: return launch_nb<12>(a, grid, s);
-    case 13: return launch_nb<13>(a, grid, s);
-    case 14: return launch_nb<14>(a, grid, s);
-    case 15: return launch_nb<15>(a, grid, s);
-    default: return launch_nb<16>(a, grid, s);
+  const int Ep = cdiv(E, 16) * 16;
+  bf16_t* Wt = static_cast<bf16_t*>(ws);
+  hipLaunchKernelGGL(transpose_router_kernel, dim3(cdiv(d, 64)), dim3(kThreads), 0, s,
+                     static_cast<const bf16_t*>(W_r), d, E, Ep, Wt);
+  switch (Ep / 16) {
+    case 1: return launch_nb<1>(a, Wt, s);
+    case 2: return launch_nb<2>(a, Wt, s);
+    case 3: return launch_nb<3>(a, Wt, s);
+    case 4: return launch_nb<4>(a, Wt, s);
+    case 5: return launch_nb<5>(a, Wt, s);
+    case 6: return launch_nb<6>(a, Wt, s);
+    case 7: return launch_nb<7>(a, Wt, s);
+    case 8: return launch_nb<8>(a, Wt, s);
+    case 9: return launch_nb<9>(a, Wt, s);
+    case 10: return launch_nb<10>(a, Wt, s);
+    case 11: return launch_nb<11>(a, Wt, s);
+    case 12: return launch_nb<12>(a, Wt, s);
+    case 13: return launch_nb<13>(a, Wt, s);
+    case 14: return launch_nb<14>(a, Wt, s);
+    case 15: return launch_nb<15>(a, Wt, s);
+    default: return launch_nb<16>(a, Wt, s);
   }
 }
 

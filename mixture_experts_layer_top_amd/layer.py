@@ -16,10 +16,11 @@ Two variants of the same layer:
   writes y_perm, and moe_combine sums the k slots in order.
 
 Shared experts: the ungated ones run as one grouped FFN with E = n_shared
-whose rows all read x (row r of shared expert s reads token r - s*T) and
-add straight into y; the gated one writes its output to a buffer, scaled per
-token by sigmoid(x . w_s) inside moe_combine, the gate logit coming from
-moe_route with E = 1.
+whose rows all read x (row r of shared expert s reads token r - s*T); on the
+fused path they add straight into y, on the deterministic path their outputs
+are summed into y in expert order by moe_combine.  The gated one writes its
+output to a buffer, scaled per token by sigmoid(x . w_s) inside moe_combine,
+the gate logit coming from moe_route with E = 1.
 """
 from __future__ import annotations
 
@@ -53,6 +54,8 @@ class MoeLayer:
         self.a = e(R, f, dt=act)
         self.y_perm = None if fused else e(R, d)
         self.y = e(T, d)
+        self.ws_route_bytes = L.moe_route_workspace_size(d, E, self.dtype)
+        self.ws_route = e(max(self.ws_route_bytes, 16), dt=torch.uint8)
         self.ws_perm_bytes = L.moe_permute_workspace_size(T, E, k)
         self.ws_perm = e(max(self.ws_perm_bytes, 16), dt=torch.uint8)
         self.ws_ffn_bytes = L.moe_ffn_workspace_size(E, R, d, f)
@@ -67,19 +70,24 @@ class MoeLayer:
             self.s_offsets = (torch.arange(self.ns + 1, dtype=i32, device=dev) * T).contiguous()
             self.s_ws_bytes = L.moe_ffn_workspace_size(self.ns, self.ns * T, d, fs)
             self.s_ws = e(max(self.s_ws_bytes, 16), dt=torch.uint8)
+            if not cfg.shared_gated and not fused:
+                self.ys_all = e(self.ns * T, d)
             if cfg.shared_gated:
                 self.ys = e(T, d)
                 self.g_idx = e(T, 1, dt=i32)
                 self.g_w = e(T, 1)
                 self.g_logit = e(T, 1)
                 self.w_s_col = layer["w_s"].reshape(d, 1).contiguous()
+                self.g_ws_bytes = L.moe_route_workspace_size(d, 1, self.dtype)
+                self.g_ws = e(max(self.g_ws_bytes, 16), dt=torch.uint8)
 
     # -- stages ------------------------------------------------------------
     def route(self, stream=None):
         c, t = self.cfg, self.t
         score = L.MOE_SOFTMAX_TOPK_RENORM if c.renorm else L.MOE_SOFTMAX_TOPK
         L.moe_route(t["x"], t["W_r"], t.get("b"), c.T, c.d, c.E, c.k, score, self.dtype,
-                    self.idx, self.w, self.logits, stream=stream)
+                    self.idx, self.w, self.logits, self.ws_route, self.ws_route_bytes,
+                    stream=stream)
 
     def permute(self, stream=None):
         c, t = self.cfg, self.t
@@ -101,7 +109,8 @@ class MoeLayer:
         if c.shared_gated:
             # gate logit x . w_s (a one-column router), then y = g * S(x) (+ routed later)
             L.moe_route(t["x"], self.w_s_col, None, T, d, 1, 1, L.MOE_SOFTMAX_TOPK, self.dtype,
-                        self.g_idx, self.g_w, self.g_logit, stream=stream)
+                        self.g_idx, self.g_w, self.g_logit, self.g_ws, self.g_ws_bytes,
+                        stream=stream)
             L.moe_expert_up(t["x"], self.s_rows, self.s_offsets, self.ns, rows, d, fs, self.dtype,
                             t["Ws_gate"], t["Ws_up"], self.s_a, self.s_ws, self.s_ws_bytes,
                             stream=stream)
@@ -112,13 +121,23 @@ class MoeLayer:
                 L.moe_combine(None, None, None, T, d, c.k, self.ys, self.g_logit, 0, self.y,
                               stream=stream)
         else:
-            L.moe_combine(None, None, None, T, d, c.k, None, None, 0, self.y, stream=stream)
             L.moe_expert_up(t["x"], self.s_rows, self.s_offsets, self.ns, rows, d, fs, self.dtype,
                             t["Ws_gate"], t["Ws_up"], self.s_a, self.s_ws, self.s_ws_bytes,
                             stream=stream)
-            L.moe_expert_down(self.s_a, self.s_offsets, self.ns, rows, fs, d, self.dtype,
-                              t["Ws_down"], None, self.s_rows, None, self.y, self.s_ws,
-                              self.s_ws_bytes, stream=stream)
+            if self.fused:
+                # y = 0, then every shared expert adds into it (atomic adds)
+                L.moe_combine(None, None, None, T, d, c.k, None, None, 0, self.y, stream=stream)
+                L.moe_expert_down(self.s_a, self.s_offsets, self.ns, rows, fs, d, self.dtype,
+                                  t["Ws_down"], None, self.s_rows, None, self.y, self.s_ws,
+                                  self.s_ws_bytes, stream=stream)
+            else:
+                # deterministic: per-expert outputs, summed into y in expert order
+                L.moe_expert_down(self.s_a, self.s_offsets, self.ns, rows, fs, d, self.dtype,
+                                  t["Ws_down"], self.ys_all, None, None, None, self.s_ws,
+                                  self.s_ws_bytes, stream=stream)
+                for s_ in range(self.ns):
+                    L.moe_combine(None, None, None, T, d, c.k, self.ys_all[s_ * T:(s_ + 1) * T],
+                                  None, 1 if s_ else 0, self.y, stream=stream)
 
     def expert_up(self, stream=None):
         c, t = self.cfg, self.t

@@ -45,7 +45,7 @@ def test_status_strings(lib):
 
 def route(**kw):
     args = dict(x=A, W_r=A, bias=None, T=16, d=64, E=8, k=2, score=0, dtype=1, topk_idx=A,
-                topk_w=A, logits_out=None)
+                topk_w=A, logits_out=None, workspace=A, ws_bytes=1 << 20)
     args.update(kw)
     return L.moe_route(**args, stream=0, check=False)
 
@@ -64,6 +64,11 @@ def test_route_validation(lib):
     assert route(score=5) == L.MOE_ERR_UNSUPPORTED
     assert route(T=0) == L.MOE_OK                     # no-op, nothing launched
     assert route(T=1 << 30, k=4) == L.MOE_ERR_INVALID  # T*k overflows int32 rows
+    need = L.moe_route_workspace_size(64, 8, 1)
+    assert need >= 16 * 64 * 2
+    assert route(ws_bytes=need - 1) == L.MOE_ERR_WORKSPACE
+    assert route(workspace=None) == L.MOE_ERR_WORKSPACE
+    assert L.moe_route_workspace_size(64, 8, 0) == 0          # fp32 path needs none
 
 
 def permute(**kw):
@@ -133,7 +138,7 @@ def test_combine_validation(lib):
 
 def test_binding_raises_on_error(lib):
     with pytest.raises(L.MoeError):
-        L.moe_route(A, A, None, 16, 64, 8, 9, 0, 1, A, A, None, stream=0)
+        L.moe_route(A, A, None, 16, 64, 8, 9, 0, 1, A, A, None, A, 1 << 20, stream=0)
 
 
 def test_product_path_does_not_import_oracle():

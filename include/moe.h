@@ -114,8 +114,8 @@ size_t moe_ffn_workspace_size(int E, int rows, int d, int f);
 
 /*
  * moe_expert_up -- grouped GEMM "layer 0" with fused SwiGLU (COMET page,
- * "COMET's Technical Principles": layer 0 decomposed along the token
- * dimension M; here its tiles are walked M-first for each weight panel).
+ * "COMET's Technical Principles": the expert's first GEMM, over the token
+ * dimension M; its tiles are walked M-first for each weight panel).
  * For every expert e and row r in [offsets[e], offsets[e+1]):
  *   z = x[gather_idx[r], :] (or x[r, :] when gather_idx is NULL),
  *   a_out[r, :] = SiLU(z W_gate[e]) * (z W_up[e]), stored in dtype (bf16
@@ -130,8 +130,9 @@ int moe_expert_up(const void* x, const int32_t* gather_idx, const int32_t* offse
 
 /*
  * moe_expert_down -- grouped GEMM "layer 1" (COMET page, "COMET's Technical
- * Principles": layer 1 decomposed along the hidden dimension N; tiles are
- * walked N-first) with an optional fused top-k weighted combine
+ * Principles": the expert's second GEMM, producing the hidden dimension N;
+ * tiles are walked M-first for each weight panel) with an optional fused
+ * top-k weighted combine
  * (DisagMoE technical summary, "2.2 AF-Pipe", combine).
  *   out[r, :] = a[r, :] W_down[e] for rows r of expert e;
  *   y_perm != NULL: y_perm[r, :] = out[r, :]  (fp32, deterministic);

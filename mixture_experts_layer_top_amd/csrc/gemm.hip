@@ -3,24 +3,27 @@
 //
 // The two GEMMs of an expert and their decomposition: COMET page, "COMET's
 // Technical Principles" -- layer 0 split along the token dimension M,
-// layer 1 along the hidden dimension N.  On one GPU that survives as the
-// tile walk: layer-0 tiles of one (expert, weight panel) are consecutive
-// along M, so the panel is fetched once and reused from L2; layer-1 tiles
-// of one (expert, row block) are consecutive along N, so its row block is
-// reused and each finished output tile goes straight to the combine.
+// layer 1 along the hidden dimension N, chosen there so that communication
+// and computation units line up across GPUs.  On one GPU there is nothing
+// to line up, and the tile walk is chosen for the caches instead: both
+// layers walk M fastest inside an (expert, weight panel), so the tiles that
+// run together share the panel.
 //
 // bf16 kernel (gfx950):
-//   * workgroup = 4 wave64s (2 x 2), macro tile 256 rows x 256 accumulator
-//     columns; each wave owns 128 x 128 = 8 x 8 blocks of 16 x 16 computed
-//     with v_mfma_f32_16x16x32_bf16 (fp32 accumulation);
+//   * workgroup = 8 wave64s (two per SIMD, 2 x 4), macro tile 256 rows x
+//     256 accumulator columns; each wave owns 128 x 64 = 8 x 4 blocks of
+//     16 x 16 computed with v_mfma_f32_16x16x32_bf16 (fp32 accumulation,
+//     128 accumulator registers per lane);
 //   * layer 0: the 256 columns are 128 columns of W_gate and the same 128
 //     columns of W_up, so SiLU(h) * u is formed in registers (the two
 //     accumulators of an output element sit in the same lane);
-//   * K stages of 32, four LDS buffers (4 x 32 KiB): three stages are in
-//     flight while one computes; one barrier per stage;
+//   * K stages of 64 (every gathered token row is one full 128-byte line
+//     per stage), two LDS buffers of 64 KiB: one stage loads while the other
+//     computes; one barrier per stage;
 //   * operands move HBM -> LDS with global_load_lds_dwordx4 (no register
-//     staging); one load fills 1 KiB of consecutive LDS, so each layout's
-//     swizzle is applied to the global addresses instead;
+//     staging), their issues spread between the MFMA rows; one load fills
+//     1 KiB of consecutive LDS, so each layout's swizzle is applied to the
+//     global addresses instead;
 //   * A (tokens, K contiguous) is stored row-major with the 16-byte chunk
 //     index XOR-swizzled by the row, read with ds_read_b128;
 //   * B (weights [K, N], N contiguous) is stored as is, swizzled by 32-byte
@@ -32,7 +35,8 @@
 //   * tiles never straddle experts; each workgroup derives its (expert,
 //     tile) from the device-side offsets with a wave prefix sum, so the
 //     host never reads the per-expert counts; the workgroup id is remapped
-//     so that consecutive tiles land on the same XCD (and its L2).
+//     so that consecutive tiles land on the same XCD (and its L2); waves of
+//     an expert's tail tile whose rows are all empty skip their MFMAs.
 #include "moe_internal.h"
 
 namespace moe {
@@ -208,6 +212,24 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
       : "m0");
 }
 
+// One 4-byte-per-lane direct-to-LDS load, used only to pull lines into L2
+// ahead of their real load (the LDS bytes it writes are never read).
+__device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(gptr), "s"(lds_addr)
+      : "m0");
+}
+
+#ifndef MOE_GEMM_L2PF
+#define MOE_GEMM_L2PF 0
+#endif
+#ifndef MOE_GEMM_SPREAD
+#define MOE_GEMM_SPREAD 1
+#endif
+
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
@@ -218,13 +240,14 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-// wait until at most `later` stages of LPS loads each are still in flight
-template <int LPS>
+// Wait until a stage's loads have landed, given that after them were issued
+// TAIL more loads of the same issue group and `later` groups of LPS loads.
+template <int LPS, int TAIL = 0>
 __device__ __forceinline__ void wait_stages(int later) {
-  if (later >= 3) wait_vmcnt<3 * LPS>();
-  else if (later == 2) wait_vmcnt<2 * LPS>();
-  else if (later == 1) wait_vmcnt<LPS>();
-  else wait_vmcnt<0>();
+  if (later >= 3) wait_vmcnt<3 * LPS + TAIL>();
+  else if (later == 2) wait_vmcnt<2 * LPS + TAIL>();
+  else if (later == 1) wait_vmcnt<LPS + TAIL>();
+  else wait_vmcnt<TAIL>();
 }
 
 // WM x WN waves; each owns (BM / WM) x (BNA / WN) accumulators.
@@ -237,15 +260,21 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
   constexpr int NJ = BNA / WN / 16;    // 16-column blocks per wave
   constexpr int A_LD = A_LOADS / NW;   // A loads per wave per stage
   constexpr int B_LD = C::B_LOADS / NW;
-  constexpr int LPS = A_LD + B_LD;
+  // L2 warm-up loads per wave per stage (issued right after each stage's loads)
+  constexpr int PF = (MOE_GEMM_L2PF > 0 && NW == 8 && !MOE_GEMM_PP) ? 1 : 0;
+  constexpr int LPS = A_LD + B_LD + PF;
   static_assert(A_LD >= 1 && B_LD >= 1 && A_LOADS % NW == 0 && C::B_LOADS % NW == 0,
                 "loader split");
   static_assert(!UP || NJ % 2 == 0, "gate/up pairs");
-  __shared__ __attribute__((aligned(1024))) char lds[NST * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[NST * C::STAGE + (MOE_GEMM_L2PF ? 256 : 0)];
 
   const int b = blockIdx.x;
   const int tile = (b & 7) * p.grid_per_xcd + (b >> 3);
-  const TileInfo ti = locate_tile<UP>(p, tile);
+  // both layers walk M fastest inside an (expert, N panel): the tiles that
+  // run together on an XCD then share their weight panel (read once from
+  // HBM) and a handful of token-row blocks (measured: higher L2 hit rate and
+  // faster than walking N fastest for layer 1 too)
+  const TileInfo ti = locate_tile<true>(p, tile);
   if (!ti.ok) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -291,20 +320,60 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
     b_krow[q] = krow;
     b_src[q] = mat + (size_t)ti.e * K * N + col;
   }
-  auto issue_stage = [&](int kt) {
+  // load i (0 <= i < A_LD + B_LD) of this wave's share of stage kt
+  auto issue_load = [&](int kt, int i) {
     const int k0 = k_begin + kt * BK;
     const uint32_t sb = lds0 + (uint32_t)((kt % NST) * C::STAGE);
-#pragma unroll
-    for (int q = 0; q < A_LD; ++q) {
-      const int kk = k0 + a_k[q];
-      const bf16_t* src = kk < k_end ? a_src[q] + kk : kZeroChunk;  // K tail -> zeros
-      lds_dma16(src, sb + (uint32_t)((wave * A_LD + q) * 1024));
-    }
-#pragma unroll
-    for (int q = 0; q < B_LD; ++q) {
+    if (i < A_LD) {
+      const int kk = k0 + a_k[i];
+      const bf16_t* src = kk < k_end ? a_src[i] + kk : kZeroChunk;  // K tail -> zeros
+      lds_dma16(src, sb + (uint32_t)((wave * A_LD + i) * 1024));
+    } else {
+      const int q = i - A_LD;
       const int kr = min(k0 + b_krow[q], K - 1);
       lds_dma16(b_src[q] + (size_t)kr * N, sb + (uint32_t)(A_BYTES + (wave * B_LD + q) * 1024));
     }
+  };
+  auto issue_stage = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < A_LD + B_LD; ++i) issue_load(kt, i);
+  };
+
+  // ---- L2 warm-up of a later stage: one lane per 128-byte line.  Waves 0-3
+  // cover the 256 A rows (one line each when BK = 64), waves 4-7 the B rows
+  // (4 lines per K row of 256 columns).
+  const bf16_t* pf_src = nullptr;
+  int pf_kstride = 0;  // elements per K step of the line this lane warms
+  if (PF) {
+    if (wave < 4) {
+      int r = ti.row0 + wave * 64 + lane;
+      if (r >= ti.row_end) r = ti.row0;
+      pf_src = p.A + (size_t)(p.gather ? p.gather[r] : r) * K;
+      pf_kstride = 1;
+    } else {
+      const int krow = (wave - 4) * 16 + (lane >> 2);
+      const int line = lane & 3;
+      const bf16_t* mat;
+      int col;
+      if (UP) {
+        mat = line < 2 ? p.B0 : p.B1;
+        col = n0 + (line & 1) * 64;
+      } else {
+        mat = p.B0;
+        col = n0 + line * 64;
+      }
+      if (col >= N) col = N - 8;
+      pf_src = mat + (size_t)ti.e * K * N + (size_t)krow * N + col;
+      pf_kstride = N;
+    }
+  }
+  const uint32_t pf_lds = lds0 + (uint32_t)(NST * C::STAGE);
+  auto prefetch_stage = [&](int kt) {
+    const int k0 = k_begin + kt * BK;
+    int koff = k0;
+    if (wave >= 4) koff = min(k0 + (wave - 4) * 16 + (lane >> 2), K - 1) - ((wave - 4) * 16 + (lane >> 2));
+    else koff = min(k0, K - 8);
+    lds_dma4(pf_src + (size_t)koff * pf_kstride, pf_lds);
   };
 
   // ---- per-lane LDS read offsets (within a stage)
@@ -359,10 +428,32 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
       for (int nj = 0; nj < NJ; ++nj)
         acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[nj], acc[mi][nj], 0, 0, 0);
   };
+  // the same MFMAs with the loads of stage `ld_kt` (if < nk) spread between
+  // their rows, so that no wave stalls on a burst of load issues while its
+  // matrix core idles
+  auto mfmas_with_loads = [&](const bf16x8 (&af)[MI], const bf16x8 (&bfr)[NJ], int ld_kt) {
+    constexpr int NL = A_LD + B_LD;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+      for (int nj = 0; nj < NJ; ++nj)
+        acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[nj], acc[mi][nj], 0, 0, 0);
+      // loads i with i * MI / NL == mi go after row mi
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+        if ((i * MI) / NL == mi && ld_kt < nk) issue_load(ld_kt, i);
+    }
+  };
 
+  // every stage's loads are followed by the warm-up of stage + MOE_GEMM_L2PF
+  // (clamped to the last stage, so each issue group has LPS loads)
+  auto issue_group = [&](int kt) {
+    issue_stage(kt);
+    if (PF) prefetch_stage(min(kt + MOE_GEMM_L2PF, nk - 1));
+  };
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
-    if (s < nk) issue_stage(s);
+    if (s < nk) issue_group(s);
   // a wave whose rows all lie past the expert's last row (the tail tile of
   // an expert) still loads its share of the operands but skips the MFMAs
 #ifndef MOE_GEMM_NO_WAVE_SKIP
@@ -405,14 +496,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
     // stage kt has landed once at most the loads of the later stages issued
     // so far are outstanding; then every wave's share is visible after the
     // barrier, and every wave is done with the buffer of stage kt - 1
-    wait_stages<LPS>(min(NST - 2, nk - 1 - kt));
+    wait_stages<LPS, PF>(min(NST - 2, nk - 1 - kt));
     __builtin_amdgcn_s_barrier();
     bf16x8 af[MI], bfr[NJ];
     if (wave_active) read_frags(kt, 0, af, bfr);
     // refill the buffer of stage kt - 1 (issued after this stage's first
     // reads so that no read waits for the new loads)
-    if (kt + NST - 1 < nk) issue_stage(kt + NST - 1);
+#if MOE_GEMM_SPREAD
+    if (wave_active) {
+      mfmas_with_loads(af, bfr, kt + NST - 1);
+    } else if (kt + NST - 1 < nk) {
+      issue_stage(kt + NST - 1);
+    }
+    if (PF && kt + NST - 1 < nk) prefetch_stage(min(kt + NST - 1 + MOE_GEMM_L2PF, nk - 1));
+#else
+    if (kt + NST - 1 < nk) issue_group(kt + NST - 1);
     if (wave_active) mfmas(af, bfr);
+#endif
 #pragma unroll
     for (int ks = 1; ks < KS; ++ks) {
       if (wave_active) {
@@ -421,6 +521,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
       }
     }
   }
+  wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
 #endif
 
   // ---- epilogue.  Accumulator layout of a 16 x 16 block: column lane % 16,

@@ -4,7 +4,8 @@
 
 A step is the whole hot path on one batch of synthetic tokens that is
 already resident in HBM: route -> permute -> (shared experts) -> grouped
-GEMM0 + SwiGLU -> grouped GEMM1 + fused weighted combine.  The default
+GEMM0 + SwiGLU (token rows gathered on load) -> grouped GEMM1 -> weighted
+combine.  The default
 workload is the Mixtral-8x7B-shape layer (T=4096, d=4096, f=14336, E=8,
 top-2, bf16).  Prints one JSON line with the layer's throughput in TFLOP/s
 (algorithmic flops, no padding), tokens/s, the per-stage times from HIP
@@ -35,7 +36,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral")
-    ap.add_argument("--unfused", action="store_true", help="time the deterministic unfused path")
+    ap.add_argument("--path", default="fast", choices=["fast", "atomic", "reference"],
+                    help="fast: gather fused into layer 0, separate deterministic combine; "
+                         "atomic: combine fused into layer 1 with atomic adds; "
+                         "reference: permuted copy of x and separate combine")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-target-s", type=float, default=10.0,
                     help="approximate seconds of oracle work for the CPU baseline sample")
@@ -143,7 +147,7 @@ def main():
     cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     layer = make_layer(cfg, seed=0, device=dev)
-    m = MoeLayer(cfg, layer, fused=not args.unfused, keep_logits=False)
+    m = MoeLayer(cfg, layer, keep_logits=False, path=args.path)
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
@@ -200,7 +204,9 @@ def main():
                                f"top-{k}" + (f" + {cfg.n_shared} shared f={cfg.f_shared}"
                                              if cfg.n_shared else ""),
                    "T": T, "d": d, "f": f, "E": cfg.E, "k": k,
-                   "path": "unfused" if args.unfused else "fused gather + fused combine"},
+                   "path": {"fast": "gather fused into layer 0, separate combine",
+                            "atomic": "gather fused into layer 0, combine fused into layer 1",
+                            "reference": "permuted copy of x, separate combine"}[args.path]},
         "pct_of_bf16_peak": round(100 * tflops / peak, 2),
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "event_ms_per_step": round(step_ms, 4),

@@ -4,23 +4,26 @@ Allocates the buffers of the path once (torch is used for device memory and
 the stream only) and issues the C-ABI calls in order:
 
     moe_route -> moe_permute -> [shared experts] -> moe_expert_up
-              -> moe_expert_down (+ fused combine, or moe_combine)
+              -> moe_expert_down -> [moe_combine]
 
-Two variants of the same layer:
+Two independent choices shape the path:
 
-* ``fused=True`` (the fast path): the gather of token rows happens inside
-  the layer-0 GEMM's loads (no permuted copy of x), and the combine happens
-  inside the layer-1 GEMM's epilogue with fp32 atomic adds into y, which is
-  first set to the shared-expert term (or cleared).
-* ``fused=False`` (deterministic): x_perm is materialised, the layer-1 GEMM
-  writes y_perm, and moe_combine sums the k slots in order.
+* gather: "fused" -- the layer-0 GEMM reads token rows of x through the
+  permutation (no permuted copy of x); "copy" -- moe_permute writes x_perm.
+* combine: "separate" -- the layer-1 GEMM writes y_perm (fp32) and
+  moe_combine sums each token's k rows in slot order (deterministic);
+  "atomic" -- the layer-1 epilogue adds w * out straight into y with fp32
+  atomic adds (no y_perm; the order of a token's k adds is not fixed).
 
-Shared experts: the ungated ones run as one grouped FFN with E = n_shared
-whose rows all read x (row r of shared expert s reads token r - s*T); on the
-fused path they add straight into y, on the deterministic path their outputs
-are summed into y in expert order by moe_combine.  The gated one writes its
-output to a buffer, scaled per token by sigmoid(x . w_s) inside moe_combine,
-the gate logit coming from moe_route with E = 1.
+Paths: "fast" = fused gather + separate combine (the benchmarked default,
+deterministic); "atomic" = fused gather + atomic combine; "reference" =
+copy gather + separate combine.
+
+Shared experts run as one grouped FFN with E = n_shared whose rows all read
+x (row r of shared expert s reads token r - s*T).  With the separate combine
+their outputs go to a buffer and moe_combine adds them (the gated one scaled
+per token by sigmoid(x . w_s), its gate logit from moe_route with E = 1);
+with the atomic combine they are added into y first.
 """
 from __future__ import annotations
 
@@ -29,12 +32,19 @@ import torch
 from . import _lib as L
 from .inputs import LayerConfig
 
+PATHS = {"fast": ("fused", "separate"), "atomic": ("fused", "atomic"),
+         "reference": ("copy", "separate")}
+
 
 class MoeLayer:
-    def __init__(self, cfg: LayerConfig, layer: dict, fused: bool = True, keep_logits: bool = True):
+    def __init__(self, cfg: LayerConfig, layer: dict, fused=None, keep_logits: bool = True,
+                 path: str = "fast"):
+        if fused is not None:  # shorthand kept for callers of the two original paths
+            path = "atomic" if fused else "reference"
+        self.path = path
+        self.gather, self.comb = PATHS[path]
         self.cfg = cfg
         self.t = layer
-        self.fused = fused
         dev = layer["x"].device
         T, d, f, E, k = cfg.T, cfg.d, cfg.f, cfg.E, cfg.k
         R = T * k
@@ -50,9 +60,9 @@ class MoeLayer:
         self.perm_token = e(R, dt=i32)
         self.inv = e(T, k, dt=i32)
         self.perm_w = e(R)
-        self.x_perm = None if fused else e(R, d, dt=act)
+        self.x_perm = e(R, d, dt=act) if self.gather == "copy" else None
         self.a = e(R, f, dt=act)
-        self.y_perm = None if fused else e(R, d)
+        self.y_perm = e(R, d) if self.comb == "separate" else None
         self.y = e(T, d)
         self.ws_route_bytes = L.moe_route_workspace_size(d, E, self.dtype)
         self.ws_route = e(max(self.ws_route_bytes, 16), dt=torch.uint8)
@@ -70,10 +80,9 @@ class MoeLayer:
             self.s_offsets = (torch.arange(self.ns + 1, dtype=i32, device=dev) * T).contiguous()
             self.s_ws_bytes = L.moe_ffn_workspace_size(self.ns, self.ns * T, d, fs)
             self.s_ws = e(max(self.s_ws_bytes, 16), dt=torch.uint8)
-            if not cfg.shared_gated and not fused:
-                self.ys_all = e(self.ns * T, d)
+            if not (self.comb == "atomic" and not cfg.shared_gated):
+                self.ys_all = e(self.ns * T, d)   # per-expert shared outputs
             if cfg.shared_gated:
-                self.ys = e(T, d)
                 self.g_idx = e(T, 1, dt=i32)
                 self.g_w = e(T, 1)
                 self.g_logit = e(T, 1)
@@ -96,65 +105,52 @@ class MoeLayer:
                       self.ws_perm, self.ws_perm_bytes, stream=stream)
 
     def shared(self, stream=None):
-        """Initialise y with the shared-expert term (or clear it when there is
-        none and the combine is fused)."""
+        """Shared-expert outputs (and, with the atomic combine, y initialised
+        with them, or cleared when there are none)."""
         c, t = self.cfg, self.t
+        T, d = c.T, c.d
         if not self.ns:
-            if self.fused:
-                L.moe_combine(None, None, None, c.T, c.d, c.k, None, None, 0, self.y,
-                              stream=stream)
+            if self.comb == "atomic":
+                L.moe_combine(None, None, None, T, d, c.k, None, None, 0, self.y, stream=stream)
             return
-        T, d, fs = c.T, c.d, c.f_shared
+        fs = c.f_shared
         rows = self.ns * T
         if c.shared_gated:
-            # gate logit x . w_s (a one-column router), then y = g * S(x) (+ routed later)
+            # gate logit x . w_s (a one-column router)
             L.moe_route(t["x"], self.w_s_col, None, T, d, 1, 1, L.MOE_SOFTMAX_TOPK, self.dtype,
                         self.g_idx, self.g_w, self.g_logit, self.g_ws, self.g_ws_bytes,
                         stream=stream)
-            L.moe_expert_up(t["x"], self.s_rows, self.s_offsets, self.ns, rows, d, fs, self.dtype,
-                            t["Ws_gate"], t["Ws_up"], self.s_a, self.s_ws, self.s_ws_bytes,
-                            stream=stream)
+        L.moe_expert_up(t["x"], self.s_rows, self.s_offsets, self.ns, rows, d, fs, self.dtype,
+                        t["Ws_gate"], t["Ws_up"], self.s_a, self.s_ws, self.s_ws_bytes,
+                        stream=stream)
+        if self.comb == "atomic" and not c.shared_gated:
+            # y = 0, then every shared expert adds into it
+            L.moe_combine(None, None, None, T, d, c.k, None, None, 0, self.y, stream=stream)
             L.moe_expert_down(self.s_a, self.s_offsets, self.ns, rows, fs, d, self.dtype,
-                              t["Ws_down"], self.ys, None, None, None, self.s_ws, self.s_ws_bytes,
-                              stream=stream)
-            if self.fused:
-                L.moe_combine(None, None, None, T, d, c.k, self.ys, self.g_logit, 0, self.y,
-                              stream=stream)
-        else:
-            L.moe_expert_up(t["x"], self.s_rows, self.s_offsets, self.ns, rows, d, fs, self.dtype,
-                            t["Ws_gate"], t["Ws_up"], self.s_a, self.s_ws, self.s_ws_bytes,
-                            stream=stream)
-            if self.fused:
-                # y = 0, then every shared expert adds into it (atomic adds)
-                L.moe_combine(None, None, None, T, d, c.k, None, None, 0, self.y, stream=stream)
-                L.moe_expert_down(self.s_a, self.s_offsets, self.ns, rows, fs, d, self.dtype,
-                                  t["Ws_down"], None, self.s_rows, None, self.y, self.s_ws,
-                                  self.s_ws_bytes, stream=stream)
-            else:
-                # deterministic: per-expert outputs, summed into y in expert order
-                L.moe_expert_down(self.s_a, self.s_offsets, self.ns, rows, fs, d, self.dtype,
-                                  t["Ws_down"], self.ys_all, None, None, None, self.s_ws,
-                                  self.s_ws_bytes, stream=stream)
-                for s_ in range(self.ns):
-                    L.moe_combine(None, None, None, T, d, c.k, self.ys_all[s_ * T:(s_ + 1) * T],
-                                  None, 1 if s_ else 0, self.y, stream=stream)
+                              t["Ws_down"], None, self.s_rows, None, self.y, self.s_ws,
+                              self.s_ws_bytes, stream=stream)
+            return
+        L.moe_expert_down(self.s_a, self.s_offsets, self.ns, rows, fs, d, self.dtype,
+                          t["Ws_down"], self.ys_all, None, None, None, self.s_ws,
+                          self.s_ws_bytes, stream=stream)
+        if self.comb == "atomic":  # gated: y = g * S(x); the routed part adds in later
+            L.moe_combine(None, None, None, T, d, c.k, self.ys_all, self.g_logit, 0, self.y,
+                          stream=stream)
 
     def expert_up(self, stream=None):
         c, t = self.cfg, self.t
         R = c.T * c.k
-        if self.fused:
-            L.moe_expert_up(t["x"], self.perm_token, self.offsets, c.E, R, c.d, c.f, self.dtype,
-                            t["W_gate"], t["W_up"], self.a, self.ws_ffn, self.ws_ffn_bytes,
-                            stream=stream)
+        if self.gather == "fused":
+            src, gidx = t["x"], self.perm_token
         else:
-            L.moe_expert_up(self.x_perm, None, self.offsets, c.E, R, c.d, c.f, self.dtype,
-                            t["W_gate"], t["W_up"], self.a, self.ws_ffn, self.ws_ffn_bytes,
-                            stream=stream)
+            src, gidx = self.x_perm, None
+        L.moe_expert_up(src, gidx, self.offsets, c.E, R, c.d, c.f, self.dtype, t["W_gate"],
+                        t["W_up"], self.a, self.ws_ffn, self.ws_ffn_bytes, stream=stream)
 
     def expert_down(self, stream=None):
         c, t = self.cfg, self.t
         R = c.T * c.k
-        if self.fused:
+        if self.comb == "atomic":
             L.moe_expert_down(self.a, self.offsets, c.E, R, c.f, c.d, self.dtype, t["W_down"],
                               None, self.perm_token, self.perm_w, self.y, self.ws_ffn,
                               self.ws_ffn_bytes, stream=stream)
@@ -164,14 +160,17 @@ class MoeLayer:
                               stream=stream)
 
     def combine(self, stream=None):
-        if self.fused:
+        if self.comb == "atomic":
             return
         c = self.cfg
-        ys = self.ys if (self.ns and c.shared_gated) else None
+        T = c.T
+        ys = self.ys_all[:T] if self.ns else None
         gl = self.g_logit if (self.ns and c.shared_gated) else None
-        acc = 1 if (self.ns and not c.shared_gated) else 0
-        L.moe_combine(self.y_perm, self.inv, self.w, c.T, c.d, c.k, ys, gl, acc, self.y,
+        L.moe_combine(self.y_perm, self.inv, self.w, T, c.d, c.k, ys, gl, 0, self.y,
                       stream=stream)
+        for s_ in range(1, self.ns):  # further ungated shared experts, in expert order
+            L.moe_combine(None, None, None, T, c.d, c.k, self.ys_all[s_ * T:(s_ + 1) * T],
+                          None, 1, self.y, stream=stream)
 
     STAGES = ("route", "permute", "shared", "expert_up", "expert_down", "combine")
 

@@ -48,9 +48,11 @@ def L():
     return _lib
 
 
-def run_layer(cfg, layer, fused):
+def run_layer(cfg, layer, path="fast"):
     from mixture_experts_layer_top_amd.layer import MoeLayer
-    m = MoeLayer(cfg, layer, fused=fused)
+    if path is True or path is False:
+        path = "atomic" if path else "reference"
+    m = MoeLayer(cfg, layer, path=path)
     m.forward()
     torch.cuda.synchronize()
     return m
@@ -132,38 +134,46 @@ def check_y(cfg, y_g, y_ref, what=""):
 # ---------------------------------------------------------------- mid sizes
 
 
-@pytest.mark.parametrize("fused", [True, False], ids=["fused", "unfused"])
+PATH_IDS = ["fast", "atomic", "reference"]
+
+
+@pytest.mark.parametrize("path", PATH_IDS)
 @pytest.mark.parametrize("name", list(MID))
-def test_layer_parity_mid(L, name, fused):
+def test_layer_parity_mid(L, name, path):
     cfg = MID[name]
-    log(f"[parity-mid] {name} fused={fused} T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k}")
+    log(f"[parity-mid] {name} path={path} T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k}")
     layer = make_layer(cfg, seed=11, device="cuda")
-    m = run_layer(cfg, layer, fused)
+    m = run_layer(cfg, layer, path)
     h = host_layer(layer)
     idx_g, w_g, _ = check_routing(cfg, m, h)
     perm_token = check_dispatch(cfg, m, idx_g, w_g)
-    if not fused:
+    if path == "reference":
         assert torch.equal(m.x_perm.cpu(), layer["x"].cpu()[torch.from_numpy(perm_token)])
     ref = O.forward(h, cfg.k, cfg.renorm, idx=idx_g)
-    check_y(cfg, m.y.cpu().double().numpy(), ref["y"], "fused" if fused else "unfused")
+    check_y(cfg, m.y.cpu().double().numpy(), ref["y"], path)
 
 
-def test_unfused_path_is_deterministic(L):
-    cfg = MID["deepseek"]
+@pytest.mark.parametrize("path", ["fast", "reference"])
+@pytest.mark.parametrize("name", ["deepseek", "qwen2moe"])
+def test_deterministic_paths_are_bitwise_repeatable(L, name, path):
+    cfg = MID[name]
     layer = make_layer(cfg, seed=3, device="cuda")
-    m1 = run_layer(cfg, layer, False)
+    m1 = run_layer(cfg, layer, path)
     y1, p1 = m1.y.clone(), m1.perm_token.clone()
-    m2 = run_layer(cfg, layer, False)
+    m2 = run_layer(cfg, layer, path)
     assert torch.equal(m2.perm_token, p1)
     assert torch.equal(m2.y, y1)
 
 
-def test_fused_and_unfused_agree(L):
+def test_paths_agree(L):
     cfg = MID["qwen2moe"]
     layer = make_layer(cfg, seed=5, device="cuda")
-    a = run_layer(cfg, layer, True).y.cpu().double().numpy()
-    b = run_layer(cfg, layer, False).y.cpu().double().numpy()
-    assert np.max(np.abs(a - b)) <= 1e-5 * rms(b)  # same products, only the fp32 add order differs
+    ys = {p: run_layer(cfg, layer, p).y.cpu().double().numpy() for p in PATH_IDS}
+    b = ys["reference"]
+    for p in ("fast", "atomic"):
+        # same products; only the order of the fp32 adds may differ
+        assert np.max(np.abs(ys[p] - b)) <= 1e-5 * rms(b), p
+    assert np.array_equal(ys["fast"], ys["reference"])  # identical sums in identical order
 
 
 # ---------------------------------------------------------------- edge cases
@@ -180,7 +190,7 @@ def test_ragged_token_counts(L, T):
     cfg = small_cfg(T=T)
     log(f"[edge] ragged T={T}")
     layer = make_layer(cfg, seed=T, device="cuda")
-    m = run_layer(cfg, layer, True)
+    m = run_layer(cfg, layer, "fast")
     h = host_layer(layer)
     idx_g, w_g, _ = check_routing(cfg, m, h)
     check_dispatch(cfg, m, idx_g, w_g)
@@ -192,7 +202,7 @@ def test_expert_count_extremes(L, E, k):
     cfg = small_cfg(E=E, k=k, T=300, d=64, f=48)
     log(f"[edge] E={E} k={k}")
     layer = make_layer(cfg, seed=E, device="cuda")
-    m = run_layer(cfg, layer, True)
+    m = run_layer(cfg, layer, "fast")
     h = host_layer(layer)
     idx_g, w_g, _ = check_routing(cfg, m, h)
     check_dispatch(cfg, m, idx_g, w_g)
@@ -206,7 +216,7 @@ def test_empty_experts(L):
     layer = make_layer(cfg, seed=1, device="cuda")
     layer["b"] = torch.tensor([0, -1e4, 0, -1e4, 0, 0, -1e4, 0], dtype=torch.float32,
                               device="cuda")
-    m = run_layer(cfg, layer, True)
+    m = run_layer(cfg, layer, "fast")
     counts = m.counts.cpu().numpy()
     assert counts[1] == counts[3] == counts[6] == 0
     h = host_layer(layer)
@@ -220,7 +230,7 @@ def test_exact_ties_go_to_lower_index(L):
     layer = make_layer(cfg, seed=2, device="cuda")
     layer["W_r"][:, 6] = layer["W_r"][:, 1]
     layer["W_r"][:, 7] = layer["W_r"][:, 1]
-    m = run_layer(cfg, layer, True)
+    m = run_layer(cfg, layer, "fast")
     L32 = m.logits.cpu().numpy()
     assert np.array_equal(L32[:, 6], L32[:, 1]) and np.array_equal(L32[:, 7], L32[:, 1])
     idx = m.idx.cpu().numpy()
@@ -238,7 +248,7 @@ def test_zero_token_closed_form(L, name):
     cfg = MID[name]
     layer = make_layer(cfg, seed=4, device="cuda")
     layer["x"][5].zero_()
-    m = run_layer(cfg, layer, True)
+    m = run_layer(cfg, layer, "fast")
     idx = m.idx[5].cpu().numpy()
     w = m.w[5].cpu().double().numpy()
     if cfg.biased:
@@ -254,7 +264,7 @@ def test_zero_tokens_is_noop(L):
     cfg = small_cfg(T=0)
     layer = make_layer(cfg, seed=0, device="cuda")
     from mixture_experts_layer_top_amd.layer import MoeLayer
-    m = MoeLayer(cfg, layer, fused=True)
+    m = MoeLayer(cfg, layer, path="fast")
     m.counts.fill_(7)
     m.offsets.fill_(7)
     m.forward()
@@ -267,17 +277,17 @@ def test_zero_projection_exact_zero(L):
     cfg = MID["mixtral"]
     layer = make_layer(cfg, seed=6, device="cuda")
     layer["W_up"].zero_()
-    m = run_layer(cfg, layer, True)
+    m = run_layer(cfg, layer, "fast")
     assert torch.count_nonzero(m.y).item() == 0
 
 
 def test_down_projection_homogeneity(L):
     cfg = MID["deepseek"]
     layer = make_layer(cfg, seed=7, device="cuda")
-    y1 = run_layer(cfg, layer, False).y.clone()
+    y1 = run_layer(cfg, layer, "reference").y.clone()
     layer["W_down"].mul_(2)
     layer["Ws_down"].mul_(2)
-    y2 = run_layer(cfg, layer, False).y
+    y2 = run_layer(cfg, layer, "reference").y
     assert torch.equal(y2, 2 * y1)
 
 
@@ -287,12 +297,12 @@ def test_down_projection_homogeneity(L):
 @pytest.mark.parametrize("name", ["mixtral", "qwen2moe", "mixtral_skew", "deepseek"])
 def test_full_size_sampled(L, name):
     """The workload at full size, in the launch configuration the benchmark
-    times (fused path): routing and dispatch checked on every token, y on a
+    times (the "fast" path): routing and dispatch checked on every token, y on a
     sample of tokens the oracle computes one expert group at a time."""
     cfg = CONFIGS[name]
     log(f"[full] {name} T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k}")
     layer = make_layer(cfg, seed=0, device="cuda")
-    m = run_layer(cfg, layer, True)
+    m = run_layer(cfg, layer, "fast")
     h = host_layer(layer, lazy=True)
     idx_g, w_g, near = check_routing(cfg, m, h)
     log("  routing ok")

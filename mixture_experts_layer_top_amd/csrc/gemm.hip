@@ -525,46 +525,88 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
 #endif
 
   // ---- epilogue.  Accumulator layout of a 16 x 16 block: column lane % 16,
-  // rows 4 * (lane / 16) + i.
+  // rows 4 * (lane / 16) + i.  Outputs go through a per-wave LDS staging
+  // area (16 rows at a time) so that global stores are 16-byte vectors
+  // covering whole row segments.
+  __syncthreads();  // every wave is done reading the operand stages
   const int col_l = lane & 15;
   const int row_l = (lane >> 4) * 4;
+  // per-wave staging area: 16 rows of the wave's output columns, padded
+  constexpr int STG = UP ? 16 * (NJ / 2 * 16 + 8) * 2 : 16 * (NJ * 16 + 4) * 4;
+  static_assert(STG % 16 == 0 && NW * STG <= NST * C::STAGE, "staging fits the operand LDS");
+  char* stg = lds + wave * STG;
   if (UP) {
+    // 16 rows x (NJ / 2 * 16) bf16 outputs per block row; the wave's output
+    // columns are contiguous: n0 + wn * (NJ / 2) * 16 + [0, NJ / 2 * 16)
+    constexpr int OC = NJ / 2 * 16;          // output columns per wave
+    constexpr int SS = OC + 8;               // staging stride in bf16 (16-byte aligned)
+    bf16_t* sb = reinterpret_cast<bf16_t*>(stg);
+    const int ocol0 = n0 + wn * OC;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = ti.row0 + wrow0 + mi * 16 + row_l + i;
-        if (row >= ti.row_end) continue;
-        bf16_t* orow = p.a_out + (size_t)row * N;
+      for (int nj = 0; nj < NJ / 2; ++nj)
 #pragma unroll
-        for (int nj = 0; nj < NJ / 2; ++nj) {
-          const int col = n0 + col_block(nj) + col_l;
-          if (col < N) orow[col] = f32_to_bf16(silu(acc[mi][nj][i]) * acc[mi][nj + NJ / 2][i]);
+        for (int i = 0; i < 4; ++i)
+          sb[(row_l + i) * SS + nj * 16 + col_l] =
+              f32_to_bf16(silu(acc[mi][nj][i]) * acc[mi][nj + NJ / 2][i]);
+      // each lane stores 16 bytes (8 columns) of one row
+      constexpr int CH = OC / 8;              // 16-byte chunks per row
+#pragma unroll
+      for (int q = 0; q < (16 * CH + 63) / 64; ++q) {
+        const int idx = q * 64 + lane;
+        if (idx < 16 * CH) {
+          const int r = idx / CH, c = idx % CH;
+          const int row = ti.row0 + wrow0 + mi * 16 + r;
+          const int col = ocol0 + c * 8;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(sb + r * SS + c * 8);
+          if (row < ti.row_end && col < N)
+            *reinterpret_cast<u32x4*>(p.a_out + (size_t)row * N + col) = v;
         }
       }
     }
   } else {
+    if (p.y_perm) {
+      constexpr int OC = NJ * 16;   // output columns per wave, contiguous
+      constexpr int SS = OC + 4;    // staging stride in floats (16-byte aligned, padded)
+      float* sf = reinterpret_cast<float*>(stg);
+      const int ocol0 = n0 + wn * OC;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
+      for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = ti.row0 + wrow0 + mi * 16 + row_l + i;
-        if (row >= ti.row_end) continue;
-        float* prow = p.y_perm ? p.y_perm + (size_t)row * N : nullptr;
-        float* yrow = nullptr;
-        float wgt = 1.f;
-        if (p.y) {
-          const int tgt = p.scatter ? p.scatter[row] : row;
-          yrow = p.y + (size_t)tgt * N;
-          if (p.row_w) wgt = p.row_w[row];
+        for (int nj = 0; nj < NJ; ++nj)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sf[(row_l + i) * SS + nj * 16 + col_l] = acc[mi][nj][i];
+        constexpr int CH = OC / 4;  // 16-byte chunks per row
+#pragma unroll
+        for (int q = 0; q < (16 * CH + 63) / 64; ++q) {
+          const int idx = q * 64 + lane;
+          if (idx < 16 * CH) {
+            const int r = idx / CH, c = idx % CH;
+            const int row = ti.row0 + wrow0 + mi * 16 + r;
+            const int col = ocol0 + c * 4;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(sf + r * SS + c * 4);
+            if (row < ti.row_end && col < N)
+              *reinterpret_cast<f32x4*>(p.y_perm + (size_t)row * N + col) = v;
+          }
         }
+      }
+    }
+    if (p.y) {
 #pragma unroll
-        for (int nj = 0; nj < NJ; ++nj) {
-          const int col = n0 + col_block(nj) + col_l;
-          if (col >= N) continue;
-          const float v = acc[mi][nj][i];
-          if (prow) prow[col] = v;
-          if (yrow) unsafeAtomicAdd(yrow + col, wgt * v);
+      for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = ti.row0 + wrow0 + mi * 16 + row_l + i;
+          if (row >= ti.row_end) continue;
+          const int tgt = p.scatter ? p.scatter[row] : row;
+          float* yrow = p.y + (size_t)tgt * N;
+          const float wgt = p.row_w ? p.row_w[row] : 1.f;
+#pragma unroll
+          for (int nj = 0; nj < NJ; ++nj) {
+            const int col = n0 + col_block(nj) + col_l;
+            if (col < N) unsafeAtomicAdd(yrow + col, wgt * acc[mi][nj][i]);
+          }
         }
       }
     }

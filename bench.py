@@ -217,7 +217,7 @@ def main():
             "route_GBs": round(by["route"] / (stage_ms["route"] * 1e-3) / 1e9, 1),
         },
         "roofline": {
-            "kernel": "grouped_gemm_bf16_kernel<true> (layer 0 + SwiGLU)",
+            "kernel": "grouped_gemm_bf16_kernel<true, 2, 4, 256> (layer 0 + SwiGLU)",
             "bound": "mfma",
             "achieved": round(g0, 2),
             "peak": peak,

@@ -35,8 +35,8 @@
 //   * tiles never straddle experts; each workgroup derives its (expert,
 //     tile) from the device-side offsets with a wave prefix sum, so the
 //     host never reads the per-expert counts; the workgroup id is remapped
-//     so that consecutive tiles land on the same XCD (and its L2); waves of
-//     an expert's tail tile whose rows are all empty skip their MFMAs.
+//     so that consecutive tiles land on the same XCD (and its L2), where
+//     they run in near lockstep and share their panels' lines.
 #include "moe_internal.h"
 
 namespace moe {
@@ -52,6 +52,12 @@ constexpr int A_RPL = 1024 / (BK * 2);  // A rows per 1 KiB load
 constexpr int A_LOADS = BM * BK * 2 / 1024;
 #ifndef MOE_GEMM_NST
 #define MOE_GEMM_NST (BK == 32 ? 4 : 2)
+#endif
+// MOE_GEMM_BRING3: with BK = 64, give the weight operand (B) three LDS
+// stage buffers and the token operand (A) two (64 + 96 = 160 KiB): weight
+// loads are issued two stages ahead, token rows one stage ahead.
+#ifndef MOE_GEMM_BRING3
+#define MOE_GEMM_BRING3 0
 #endif
 constexpr int NST = MOE_GEMM_NST;  // LDS stages (NST - 1 in flight while one computes)
 constexpr int A_BYTES = BM * BK * 2;  // 16 KiB per stage
@@ -266,7 +272,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
   static_assert(A_LD >= 1 && B_LD >= 1 && A_LOADS % NW == 0 && C::B_LOADS % NW == 0,
                 "loader split");
   static_assert(!UP || NJ % 2 == 0, "gate/up pairs");
-  __shared__ __attribute__((aligned(1024))) char lds[NST * C::STAGE + (MOE_GEMM_L2PF ? 256 : 0)];
+  constexpr bool RING3 = MOE_GEMM_BRING3 && BK == 64 && !MOE_GEMM_PP;
+  constexpr int A_SLOTS = RING3 ? 2 : NST;
+  constexpr int B_SLOTS = RING3 ? 3 : NST;
+  constexpr int LDS_OPS = A_SLOTS * A_BYTES + B_SLOTS * C::B_BYTES;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_OPS + (MOE_GEMM_L2PF ? 256 : 0)];
+  // operand buffers: A slots first, then B slots
+  auto a_base = [&](int kt) { return (kt % A_SLOTS) * A_BYTES; };
+  auto b_base = [&](int kt) { return A_SLOTS * A_BYTES + (kt % B_SLOTS) * C::B_BYTES; };
 
   const int b = blockIdx.x;
   const int tile = (b & 7) * p.grid_per_xcd + (b >> 3);
@@ -285,6 +298,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
   const uint32_t lds0 = lds_addr_of(lds);
   const int k_begin = ti.ks * p.k_per_split;
   const int k_end = min(K, k_begin + p.k_per_split);
+  const int nk_ = cdiv(k_end - k_begin, BK);  // K stages of this tile
 
   // ---- direct-to-LDS loader.  One load moves 64 lanes x 16 B = 1 KiB into
   // consecutive LDS bytes, so each layout's swizzle is applied on the global
@@ -320,20 +334,24 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
     b_krow[q] = krow;
     b_src[q] = mat + (size_t)ti.e * K * N + col;
   }
-  // load i (0 <= i < A_LD + B_LD) of this wave's share of stage kt
-  auto issue_load = [&](int kt, int i) {
-    const int k0 = k_begin + kt * BK;
-    const uint32_t sb = lds0 + (uint32_t)((kt % NST) * C::STAGE);
+  // load i (0 <= i < A_LD + B_LD) of this wave's share of a stage: the A
+  // loads (i < A_LD) of stage kt_a, the B loads of stage kt_b; stages past
+  // the last are skipped
+  auto issue_load2 = [&](int kt_a, int kt_b, int i) {
     if (i < A_LD) {
-      const int kk = k0 + a_k[i];
+      if (kt_a >= nk_) return;
+      const int kk = k_begin + kt_a * BK + a_k[i];
       const bf16_t* src = kk < k_end ? a_src[i] + kk : kZeroChunk;  // K tail -> zeros
-      lds_dma16(src, sb + (uint32_t)((wave * A_LD + i) * 1024));
+      lds_dma16(src, lds0 + (uint32_t)(a_base(kt_a) + (wave * A_LD + i) * 1024));
     } else {
+      if (kt_b >= nk_) return;
       const int q = i - A_LD;
-      const int kr = min(k0 + b_krow[q], K - 1);
-      lds_dma16(b_src[q] + (size_t)kr * N, sb + (uint32_t)(A_BYTES + (wave * B_LD + q) * 1024));
+      const int kr = min(k_begin + kt_b * BK + b_krow[q], K - 1);
+      lds_dma16(b_src[q] + (size_t)kr * N,
+                lds0 + (uint32_t)(b_base(kt_b) + (wave * B_LD + q) * 1024));
     }
   };
+  auto issue_load = [&](int kt, int i) { issue_load2(kt, kt, i); };
   auto issue_stage = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < A_LD + B_LD; ++i) issue_load(kt, i);
@@ -367,7 +385,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
       pf_kstride = N;
     }
   }
-  const uint32_t pf_lds = lds0 + (uint32_t)(NST * C::STAGE);
+  const uint32_t pf_lds = lds0 + (uint32_t)LDS_OPS;
   auto prefetch_stage = [&](int kt) {
     const int k0 = k_begin + kt * BK;
     int koff = k0;
@@ -408,10 +426,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj) acc[mi][nj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = cdiv(k_end - k_begin, BK);
+  const int nk = nk_;
   auto read_frags = [&](int kt, int ks, bf16x8 (&af)[MI], bf16x8 (&bfr)[NJ]) {
-    const char* As = lds + (kt % NST) * C::STAGE;
-    const char* Bs = As + A_BYTES;
+    const char* As = lds + a_base(kt);
+    const char* Bs = lds + b_base(kt);
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj) {
       const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Bs + b_rd[ks][nj]));
@@ -431,17 +449,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
   // the same MFMAs with the loads of stage `ld_kt` (if < nk) spread between
   // their rows, so that no wave stalls on a burst of load issues while its
   // matrix core idles
-  auto mfmas_with_loads = [&](const bf16x8 (&af)[MI], const bf16x8 (&bfr)[NJ], int ld_kt) {
+  auto mfmas_with_loads = [&](const bf16x8 (&af)[MI], const bf16x8 (&bfr)[NJ], int ld_a,
+                              int ld_b) {
     constexpr int NL = A_LD + B_LD;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
       for (int nj = 0; nj < NJ; ++nj)
         acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[nj], acc[mi][nj], 0, 0, 0);
-      // loads i with i * MI / NL == mi go after row mi
+      // loads i with i * MI / NL == mi go after row mi (A loads first)
 #pragma unroll
       for (int i = 0; i < NL; ++i)
-        if ((i * MI) / NL == mi && ld_kt < nk) issue_load(ld_kt, i);
+        if ((i * MI) / NL == mi) issue_load2(ld_a, ld_b, i);
     }
   };
 
@@ -451,14 +470,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
     issue_stage(kt);
     if (PF) prefetch_stage(min(kt + MOE_GEMM_L2PF, nk - 1));
   };
+  if (RING3) {
+    // B(0), then the steady-state group [A(0), B(1)]
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
-    if (s < nk) issue_group(s);
-  // a wave whose rows all lie past the expert's last row (the tail tile of
-  // an expert) still loads its share of the operands but skips the MFMAs
-#ifndef MOE_GEMM_NO_WAVE_SKIP
+    for (int i = A_LD; i < A_LD + B_LD; ++i) issue_load2(0, 0, i);
+#pragma unroll
+    for (int i = 0; i < A_LD + B_LD; ++i) issue_load2(0, 1, i);
+  } else {
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+      if (s < nk) issue_group(s);
+  }
+#ifdef MOE_GEMM_WAVE_SKIP
   const bool wave_active = wrow0 < ti.row_end - ti.row0;
 #else
+  // measured: letting a tail tile's empty waves skip their MFMAs makes that
+  // tile finish early and breaks the lockstep of the tiles that share its
+  // operand panels in L2 (layer-0 L2 hit rate 59% with the skip, 79% without)
   constexpr bool wave_active = true;
 #endif
 
@@ -496,15 +524,25 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
     // stage kt has landed once at most the loads of the later stages issued
     // so far are outstanding; then every wave's share is visible after the
     // barrier, and every wave is done with the buffer of stage kt - 1
-    wait_stages<LPS, PF>(min(NST - 2, nk - 1 - kt));
+    if (RING3) {
+      // A(kt) and B(kt) have landed once at most B(kt + 1) is outstanding
+      if (kt + 1 < nk) wait_vmcnt<B_LD>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_stages<LPS, PF>(min(NST - 2, nk - 1 - kt));
+    }
     __builtin_amdgcn_s_barrier();
     bf16x8 af[MI], bfr[NJ];
     if (wave_active) read_frags(kt, 0, af, bfr);
     // refill the buffer of stage kt - 1 (issued after this stage's first
     // reads so that no read waits for the new loads)
 #if MOE_GEMM_SPREAD
-    if (wave_active) {
-      mfmas_with_loads(af, bfr, kt + NST - 1);
+    if (RING3) {
+      // A(kt + 1) into the A slot of stage kt - 1, B(kt + 2) into the B slot
+      // of stage kt - 1: both were last read before this stage's barrier
+      mfmas_with_loads(af, bfr, kt + 1, kt + 2);
+    } else if (wave_active) {
+      mfmas_with_loads(af, bfr, kt + NST - 1, kt + NST - 1);
     } else if (kt + NST - 1 < nk) {
       issue_stage(kt + NST - 1);
     }
@@ -533,7 +571,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
   const int row_l = (lane >> 4) * 4;
   // per-wave staging area: 16 rows of the wave's output columns, padded
   constexpr int STG = UP ? 16 * (NJ / 2 * 16 + 8) * 2 : 16 * (NJ * 16 + 4) * 4;
-  static_assert(STG % 16 == 0 && NW * STG <= NST * C::STAGE, "staging fits the operand LDS");
+  static_assert(STG % 16 == 0 && NW * STG <= LDS_OPS, "staging fits the operand LDS");
   char* stg = lds + wave * STG;
   if (UP) {
     // 16 rows x (NJ / 2 * 16) bf16 outputs per block row; the wave's output

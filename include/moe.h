@@ -120,7 +120,8 @@ size_t moe_ffn_workspace_size(int E, int rows, int d, int f);
  *   z = x[gather_idx[r], :] (or x[r, :] when gather_idx is NULL),
  *   a_out[r, :] = SiLU(z W_gate[e]) * (z W_up[e]), stored in dtype (bf16
  *   rounds to nearest even).
- * Arguments: x [n_x, d]; gather_idx [rows] int32 or NULL; offsets [E+1]
+ * Arguments: x [n_x, d]; gather_idx [rows] int32 or NULL, entries in
+ *   [0, min(n_x, rows)) (others are undefined behaviour); offsets [E+1]
  *   int32 device (offsets[0] = 0, non-decreasing, offsets[E] = rows);
  *   W_gate, W_up [E, d, f]; a_out [rows, f] out.
  */

@@ -57,7 +57,7 @@ constexpr int A_LOADS = BM * BK * 2 / 1024;
 // stage buffers and the token operand (A) two (64 + 96 = 160 KiB): weight
 // loads are issued two stages ahead, token rows one stage ahead.
 #ifndef MOE_GEMM_BRING3
-#define MOE_GEMM_BRING3 0
+#define MOE_GEMM_BRING3 1
 #endif
 constexpr int NST = MOE_GEMM_NST;  // LDS stages (NST - 1 in flight while one computes)
 constexpr int A_BYTES = BM * BK * 2;  // 16 KiB per stage
@@ -161,21 +161,18 @@ __device__ __forceinline__ TileInfo locate_tile(const GemmArgs& p, int tile) {
 }
 
 // Byte offsets inside one stage.
-// A: [BM rows][BK] bf16, 64 B per row.  A fragment read touches 16
+// A: [BM rows][BK] bf16, 2 BK bytes per row.  A fragment read touches 16
 // consecutive rows at one 16-byte chunk.  The chunk index is XOR-ed with
-// ((row >> 1) ^ (row >> 3)) & 3, which gives distinct banks both for any 8
-// consecutive rows in a 128-byte bank window and for any 16 consecutive rows
-// in a 256-byte window.
+// ((row >> 1) ^ (row >> 3)) & 3 (BK = 32) or (row >> 1) & 7 (BK = 64); the
+// latter measured free of bank conflicts on gfx950.
 // B: [BK rows][BNA] bf16.  One transpose read touches 4 rows x 32 bytes per
 // 16 lanes (rows 8 apart for the next 16 lanes).  The chunk index is XOR-ed
 // with 2 * (row % 8) + (row & 8): even values keep the 32-byte pairs whole,
 // the low part spreads 4 rows over a 128-byte window and bit 3 moves rows
 // 8..15 to the other half of a 256-byte window.
 __device__ __forceinline__ int a_swz(int row) {
-  // BK = 32: 4 chunks per row; BK = 64: 8 chunks per row (then (row ^ row >> 3) & 7
-  // is distinct over any 8 consecutive rows and over the rows of one parity
-  // among 16 consecutive rows)
-  return BK == 32 ? (((row >> 1) ^ (row >> 3)) & 3) : ((row ^ (row >> 3)) & 7);
+  // BK = 32: 4 chunks per row; BK = 64: 8 chunks per row
+  return BK == 32 ? (((row >> 1) ^ (row >> 3)) & 3) : ((row >> 1) & 7);
 }
 __device__ __forceinline__ int a_off(int row, int chunk) {
   return row * (BK * 2) + ((chunk ^ a_swz(row)) << 4);
@@ -652,6 +649,318 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
 }
 
 // ------------------------------------------------------------------------
+// Ping-pong kernel: 8 wave64s, two per SIMD, in two groups that take turns
+// on the SIMD's matrix core.  Group X (waves 0-3) owns rows 0-127 of the
+// 256 x 256 macro tile, group Y (waves 4-7) rows 128-255; wave w of a group
+// owns columns w * 32 + [0, 32) of both 128-column B halves (128 x 64 =
+// 8 x 4 accumulator blocks).  Phases, separated by workgroup barriers:
+//
+//   phase 2s    : X memory(s)  | Y compute(s - 1)
+//   phase 2s + 1: X compute(s) | Y memory(s)
+//
+// memory(s) = read the wave's fragments of the whole stage s (both K steps)
+// from LDS and issue the wave's loads of a later stage; compute(s) = its 64
+// MFMAs.  So on every SIMD one wave keeps the matrix core busy while the
+// other waits on LDS reads and load issue.  X issues all A loads (stage s+1
+// during memory(s): two phases to land), Y all B loads (stage s+2 during
+// memory(s): three phases).  LDS: A ring of 2 stages, B ring of 3 (5 x 32
+// KiB).  A stage's slot is refilled only after both groups' memory phases
+// for it (each ends with its reads waited for, before the barrier).
+//
+// B stage layout: two halves of 64 K rows x 128 columns (256 B per row),
+// each 1 KiB load filling 4 rows of one half.  Layer 0: half 0 = W_gate,
+// half 1 = W_up (the same 128 columns); layer 1: the two 128-column halves
+// of a 256-column panel.
+//
+// Loads use the scalar-base form of global_load_lds_dwordx4 (uniform 64-bit
+// base + per-lane 32-bit byte offset): one register per load slot; stages
+// advance the scalar base.  K must be a multiple of the stage depth (64)
+// and the token matrix smaller than 4 GiB; other shapes take the kernel
+// above.
+// ------------------------------------------------------------------------
+namespace pp {
+constexpr int NW = 8, MI = 8, NJ = 4;
+constexpr int LD = 8;                       // 1 KiB loads per wave per stage (A for X, B for Y)
+constexpr int SLOT = 32768;                 // one operand stage
+constexpr int HALF = 16384;                 // one B half (64 rows x 256 B)
+constexpr int B_RING = 2 * SLOT;            // B slots start after the two A slots
+constexpr int LDS_BYTES = 5 * SLOT;
+static_assert(BM * BK * 2 == SLOT, "stage sizes");
+static_assert(BK == 64, "two MFMA K steps per stage");
+
+// A swizzle from the row's position inside its 16-row block only, so that
+// every 16-row fragment block of a wave has the same lane offsets: the
+// fragment addresses of one K step are one register plus immediates.
+// XOR-ing the chunk with row / 2 (mod 8) makes the fragment read (16 rows
+// at one chunk per 16 lanes) free of LDS bank conflicts on gfx950
+// (measured with SQ_LDS_BANK_CONFLICT: 0, against ~1 conflict cycle per
+// busy cycle for XOR with row % 8, row % 8 ^ row / 8 or 2 (row / 4 % 4)).
+__device__ __forceinline__ int a_swz16(int row) { return (row >> 1) & 7; }
+
+// One direct-to-LDS load with a scalar base: lane i reads 16 bytes at
+// base + voff_i and writes LDS bytes lds_addr + 16 i.
+__device__ __forceinline__ void lds_dma16_s(uint32_t voff, const void* base, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(lds_addr)
+      : "m0");
+}
+
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+}  // namespace pp
+
+template <bool UP>
+__global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p) {
+  using namespace pp;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+
+  const int b = blockIdx.x;
+  const int tile = (b & 7) * p.grid_per_xcd + (b >> 3);
+  const TileInfo ti0 = locate_tile<true>(p, tile);
+  if (!ti0.ok) return;
+  // the tile is the same for every lane: keep it in scalar registers
+  const int t_e = __builtin_amdgcn_readfirstlane(ti0.e);
+  const int t_row0 = __builtin_amdgcn_readfirstlane(ti0.row0);
+  const int t_row_end = __builtin_amdgcn_readfirstlane(ti0.row_end);
+  const int t_n = __builtin_amdgcn_readfirstlane(ti0.n_t);
+  const int t_ks = __builtin_amdgcn_readfirstlane(ti0.ks);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool X = wave < 4;       // leading group: rows 0-127, issues the A loads
+  const int wg = wave & 3;       // wave inside its group
+  const int K = p.K, N = p.N;
+  const int n0 = t_n * (UP ? 128 : 256);
+  const uint32_t lds0 = lds_addr_of(lds);
+  const int k_begin = t_ks * p.k_per_split;
+  const int k_end = min(K, k_begin + p.k_per_split);
+  const int nk = (k_end - k_begin) / BK;
+
+  // ---- loads.  X: load j = 8 wg + q fills A rows 8 j .. 8 j + 7; lane l
+  // reads 16 B of row 8 j + l / 8 (chunk swizzled by the row).  Y: load
+  // j = 8 wg + q fills K rows 4 (j % 16) .. + 3 of B half j / 16; lane l reads
+  // 16 B of row 4 (j % 16) + l / 16; the lane part depends on q % 4 only.
+  uint32_t ld_off[LD];  // X: A byte offsets at k_begin; Y: B byte offsets (first 4 used)
+  const char* ld_base0; // stage-0 scalar base (Y: of row group 2 (wg & 1))
+  const int b_half = wg >> 1;
+  if (X) {
+#pragma unroll
+    for (int q = 0; q < LD; ++q) {
+      const int row = (wg * LD + q) * 8 + (lane >> 3);
+      const int chunk = (lane & 7) ^ a_swz16(row);
+      int r = t_row0 + row;
+      if (r >= t_row_end) r = t_row0;  // padding rows read a valid row; results are discarded
+      const int src_row = p.gather ? p.gather[r] : r;
+      ld_off[q] = ((uint32_t)src_row * (uint32_t)K + (uint32_t)(k_begin + chunk * 8)) * 2u;
+    }
+    ld_base0 = uniform_ptr(p.A);
+  } else {
+    const bf16_t* b_mat = UP ? (b_half ? p.B1 : p.B0) : p.B0;
+    const int n0h = UP ? n0 : n0 + b_half * 128;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int krow = 4 * u + (lane >> 4);  // row inside its 16-row group
+      const int chunk = (lane & 15) ^ b_swz<128>(krow);
+      int col = n0h + chunk * 8;
+      if (col >= N) col = N - 8;  // padding columns read valid data; results are discarded
+      ld_off[u] = ((uint32_t)krow * (uint32_t)N + (uint32_t)col) * 2u;
+      ld_off[u + 4] = 0;
+    }
+    ld_base0 = uniform_ptr(b_mat + (size_t)t_e * K * N +
+                           (size_t)(k_begin + 16 * (2 * (wg & 1))) * N);
+  }
+  // (K is a multiple of BK here: the host sends other shapes elsewhere)
+  auto issue_a = [&](int kt, int q) {
+    const uint32_t dst = lds0 + (uint32_t)((kt & 1) * SLOT + (wg * LD + q) * 1024);
+    lds_dma16_s(ld_off[q], ld_base0 + (size_t)kt * BK * 2, dst);
+  };
+  auto issue_b = [&](int kt, int slot, int q) {
+    const uint32_t dst = lds0 + (uint32_t)(B_RING + slot * SLOT + (wg * LD + q) * 1024);
+    const char* base = ld_base0 + ((size_t)kt * BK + (size_t)(16 * (q >> 2))) * N * 2;
+    lds_dma16_s(ld_off[q & 3], uniform_ptr(base), dst);
+  };
+
+  // ---- fragment read offsets (bytes inside a stage slot)
+  const int l15 = lane & 15, g = lane >> 4;
+  const int wrow0 = X ? 0 : 128;
+  const int a_s = a_swz16(l15);
+  const int a_rd0 = (wrow0 + l15) * 128 + ((g ^ a_s) << 4);        // K step 0
+  const int a_rd1 = (wrow0 + l15) * 128 + (((g + 4) ^ a_s) << 4);  // K step 1
+  // B: blocks nj = 0, 1 in half 0, nj = 2, 3 the same columns of half 1; K
+  // step 1 adds 32 rows (8 KiB, same swizzle)
+  int b_rd[2], b_rd4[2];
+  const int b_kr = g * 8 + (l15 >> 2);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    b_rd[c] = b_off<128>(b_kr, wg * 32 + c * 16 + (lane & 3) * 4);
+    b_rd4[c] = b_off<128>(b_kr + 4, wg * 32 + c * 16 + (lane & 3) * 4);
+  }
+
+  f32x4 acc[MI][NJ];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < NJ; ++nj) acc[mi][nj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  bf16x8 fa[2][MI], fb[2][NJ];  // fragments of one stage: [K step][block]
+  // memory phase: issue this wave's loads (A(ld_kt) for X, B(ld_kt) for Y),
+  // read the stage's fragments, wait for the reads
+  auto memory = [&](int s, int ld_kt, int ld_bslot) {
+    const char* As = lds + (s & 1) * SLOT;
+    const char* Bs = lds + B_RING + (s % 3) * SLOT;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int nj = 0; nj < NJ; ++nj) {
+        const char* Bh = Bs + (nj >> 1) * HALF + ks * 8192;
+        const bf16x4 lo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Bh + b_rd[nj & 1]));
+        const bf16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Bh + b_rd4[nj & 1]));
+        fb[ks][nj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      const char* Ak = As + (ks ? a_rd1 : a_rd0);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        fa[ks][mi] = *reinterpret_cast<const bf16x8*>(Ak + mi * 2048);
+      // half of the loads after each K step's reads
+      if (ld_kt < nk) {
+#pragma unroll
+        for (int q = ks * 4; q < ks * 4 + 4; ++q) {
+          if (X) issue_a(ld_kt, q);
+          else issue_b(ld_kt, ld_bslot, q);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  };
+  auto compute = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj)
+          acc[mi][nj] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ks][mi], fb[ks][nj], acc[mi][nj], 0, 0, 0);
+  };
+
+  // The two groups run separate loops with the same barrier count: one
+  // after the prologue and two per stage.
+  if (X) {
+    // prologue: A(0)
+#pragma unroll
+    for (int q = 0; q < LD; ++q) issue_a(0, q);
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    for (int s = 0; s < nk; ++s) {
+      memory(s, s + 1, 0);   // phase 2s: read stage s, load A(s + 1)
+      __builtin_amdgcn_s_barrier();
+      compute();             // phase 2s + 1
+      wait_vmcnt<0>();       // A(s + 1) has landed
+      __builtin_amdgcn_s_barrier();
+    }
+  } else {
+    // prologue: B(0), B(1)
+#pragma unroll
+    for (int q = 0; q < LD; ++q) issue_b(0, 0, q);
+    if (nk > 1) {
+#pragma unroll
+      for (int q = 0; q < LD; ++q) issue_b(1, 1, q);
+      wait_vmcnt<LD>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    for (int s = 0; s < nk; ++s) {
+      if (s > 0) compute();  // phase 2s: stage s - 1
+      __builtin_amdgcn_s_barrier();
+      // phase 2s + 1: read stage s, load B(s + 2) into the slot of stage s - 1;
+      // then B(s + 1) must have landed
+      memory(s, s + 2, (s + 2) % 3);
+      if (s + 2 < nk) wait_vmcnt<LD>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+    }
+    compute();  // phase 2 nk: stage nk - 1 (LDS is free: all reads and loads waited for)
+  }
+
+  // ---- epilogue (accumulator layout of a 16 x 16 block: column lane % 16,
+  // rows 4 * (lane / 16) + i), staged through the wave's own LDS area
+  const int col_l = lane & 15;
+  const int row_l = (lane >> 4) * 4;
+  if (UP) {
+    constexpr int OC = 32, SS = OC + 8;  // output columns per wave; staging stride (bf16)
+    bf16_t* sb = reinterpret_cast<bf16_t*>(lds + wave * 16 * SS * 2);
+    const int ocol0 = n0 + wg * OC;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+      for (int nj = 0; nj < 2; ++nj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sb[(row_l + i) * SS + nj * 16 + col_l] =
+              f32_to_bf16(silu(acc[mi][nj][i]) * acc[mi][nj + 2][i]);
+      // 16 rows x 4 chunks of 16 B: one per lane
+      const int r = lane >> 2, c = lane & 3;
+      const int row = t_row0 + wrow0 + mi * 16 + r;
+      const int col = ocol0 + c * 8;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sb + r * SS + c * 8);
+      if (row < t_row_end && col < N)
+        *reinterpret_cast<u32x4*>(p.a_out + (size_t)row * N + col) = v;
+    }
+  } else {
+    // the wave's columns: n0 + h * 128 + wg * 32 + [0, 32) for halves h = 0, 1
+    if (p.y_perm) {
+      constexpr int SS = 64 + 4;  // staging stride in floats
+      float* sf = reinterpret_cast<float*>(lds + wave * 16 * SS * 4);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sf[(row_l + i) * SS + nj * 16 + col_l] = acc[mi][nj][i];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // 16 rows x 16 chunks of 16 B
+          const int idx = q * 64 + lane;
+          const int r = idx >> 4, c = idx & 15;
+          const int row = t_row0 + wrow0 + mi * 16 + r;
+          const int col = n0 + (c >> 3) * 128 + wg * 32 + (c & 7) * 4;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(sf + r * SS + c * 4);
+          if (row < t_row_end && col < N)
+            *reinterpret_cast<f32x4*>(p.y_perm + (size_t)row * N + col) = v;
+        }
+      }
+    }
+    if (p.y) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = t_row0 + wrow0 + mi * 16 + row_l + i;
+          if (row >= t_row_end) continue;
+          const int tgt = p.scatter ? p.scatter[row] : row;
+          float* yrow = p.y + (size_t)tgt * N;
+          const float wgt = p.row_w ? p.row_w[row] : 1.f;
+#pragma unroll
+          for (int nj = 0; nj < NJ; ++nj) {
+            const int col = n0 + (nj >> 1) * 128 + wg * 32 + (nj & 1) * 16 + col_l;
+            if (col < N) unsafeAtomicAdd(yrow + col, wgt * acc[mi][nj][i]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
 // fp32 path (small layers): one thread per output element, sequential FMA.
 // ------------------------------------------------------------------------
 
@@ -719,6 +1028,9 @@ int max_tiles_m(int rows, int E) {
 #ifndef MOE_DN_BNA
 #define MOE_DN_BNA 256
 #endif
+#ifndef MOE_GEMM_PPK
+#define MOE_GEMM_PPK 1
+#endif
 constexpr int UP_WN = MOE_UP_WN, UP_BNA = MOE_UP_BNA, DN_WN = MOE_DN_WN, DN_BNA = MOE_DN_BNA;
 
 int num_cus() {
@@ -753,8 +1065,11 @@ int choose_ksplit(long long tiles, int K, int cus) {
   return best;
 }
 
+// a_rows_bytes: size of the A matrix the kernel may read (rows that can be
+// addressed times K times 2 bytes)
 template <bool UP, int WM, int WN, int BNA>
-hipError_t launch_gemm(GemmArgs& p, int rows, int E, int ncols, hipStream_t s) {
+hipError_t launch_gemm(GemmArgs& p, int rows, int E, int ncols, unsigned long long a_rows_bytes,
+                       hipStream_t s) {
   const int tiles_n = cdiv(ncols, UP ? BNA / 2 : BNA);
   const long long tiles_mn = (long long)max_tiles_m(rows, E) * tiles_n;
   int ksplit = 1;
@@ -770,6 +1085,14 @@ hipError_t launch_gemm(GemmArgs& p, int rows, int E, int ncols, hipStream_t s) {
   const long long tiles = (long long)max_tiles_m(rows, E) * p.tiles_n;
   const long long grid = (tiles + 7) / 8 * 8;
   p.grid_per_xcd = (int)(grid / 8);
+#if MOE_GEMM_PPK
+  static_assert(BNA == 256, "ping-pong kernel tile width");
+  if (p.K % BK == 0 && p.k_per_split % BK == 0 && a_rows_bytes < (1ull << 32)) {
+    hipLaunchKernelGGL((grouped_gemm_bf16_pp_kernel<UP>), dim3((unsigned)grid),
+                       dim3(64 * pp::NW), 0, s, p);
+    return hipGetLastError();
+  }
+#endif
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<UP, WM, WN, BNA>), dim3((unsigned)grid),
                      dim3(64 * WM * WN), 0, s, p);
   return hipGetLastError();
@@ -803,7 +1126,8 @@ hipError_t launch_expert_up(const void* x, const int32_t* gather_idx, const int3
   p.B0 = static_cast<const bf16_t*>(W_gate);
   p.B1 = static_cast<const bf16_t*>(W_up);
   p.a_out = static_cast<bf16_t*>(a_out);
-  return launch_gemm<true, 2, UP_WN, UP_BNA>(p, rows, E, f, s);
+  // gather entries are < rows (documented), so A spans at most rows x d
+  return launch_gemm<true, 2, UP_WN, UP_BNA>(p, rows, E, f, (unsigned long long)rows * d * 2, s);
 }
 
 hipError_t launch_expert_down(const void* a, const int32_t* offsets, int E, int rows, int f,
@@ -830,7 +1154,7 @@ hipError_t launch_expert_down(const void* a, const int32_t* offsets, int E, int 
   p.scatter = scatter_idx;
   p.row_w = row_w;
   p.y = y;
-  return launch_gemm<false, 2, DN_WN, DN_BNA>(p, rows, E, d, s);
+  return launch_gemm<false, 2, DN_WN, DN_BNA>(p, rows, E, d, (unsigned long long)rows * f * 2, s);
 }
 
 }  // namespace moe

@@ -33,6 +33,9 @@ MID = {
     "qwen2moe": CONFIGS["qwen2moe"].shrink(T=1024, d=264, f=200, f_shared=256),
     "mixtral_skew": CONFIGS["mixtral_skew"].shrink(T=3000, d=256, f=256),
     "deepseek": CONFIGS["deepseek"].shrink(T=1500, d=256, f=136, f_shared=136),
+    # K a multiple of 64 (the ping-pong GEMM), N ragged against its tiles
+    "mixtral_k64": CONFIGS["mixtral"].shrink(T=2000, d=512, f=320),
+    "qwen2moe_k64": CONFIGS["qwen2moe"].shrink(T=1024, d=320, f=192, f_shared=448),
 }
 
 
@@ -209,6 +212,22 @@ def test_expert_count_extremes(L, E, k):
     check_y(cfg, m.y.cpu().double().numpy(), O.forward(h, cfg.k, cfg.renorm, idx=idx_g)["y"])
     if k == 1 and cfg.renorm:
         assert np.all(w_g == 1.0)
+
+
+@pytest.mark.parametrize("nk", [1, 2, 3, 5])
+def test_gemm_stage_counts(L, nk):
+    """d = f = 64 nk: the ping-pong GEMM with 1, 2, 3 and 5 K stages (its
+    prologue and ring take different branches for nk < 3)."""
+    cfg = small_cfg(E=16, k=4, T=700, d=64 * nk, f=64 * nk)
+    log(f"[edge] GEMM stages nk={nk}")
+    layer = make_layer(cfg, seed=40 + nk, device="cuda")
+    for path in PATH_IDS:
+        m = run_layer(cfg, layer, path)
+        h = host_layer(layer)
+        idx_g, w_g, _ = check_routing(cfg, m, h)
+        check_dispatch(cfg, m, idx_g, w_g)
+        check_y(cfg, m.y.cpu().double().numpy(), O.forward(h, cfg.k, cfg.renorm, idx=idx_g)["y"],
+                path)
 
 
 def test_empty_experts(L):

@@ -37,51 +37,61 @@ struct RouteArgs {
   float* logits_out;
 };
 
-// Softmax top-k over `ntok` logits rows in LDS, one wave per 16 tokens, 4
-// lanes per token.  Waves past the last 16-token group return (whole waves,
-// so the 4-lane shuffles stay uniform).
+// Softmax top-k over `ntok` logits rows in LDS: 16 lanes per token, each
+// holding NV = Ep / 16 of the row's logits in registers (expert q + 16 u for
+// lane q; padded experts hold -inf).  Waves take groups of 4 tokens in turn.
+// The j-th pick is the best (value desc, index asc) strictly below the
+// (j-1)-th pick in that order, found by a per-lane scan and a 16-lane
+// reduction, so no pick is ever marked and exactly equal logits go to the
+// lower index.  With renormalisation the unnormalised weights are written
+// first and divided by their sum afterwards (by the same lane).
+template <int NV>
 __device__ __forceinline__ void select_and_weigh(const float* ll, int lstride, const RouteArgs& a,
                                                  int t_base, int ntok) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  if (wave * 16 >= ntok) return;
-  const int tt = wave * 16 + (lane >> 2);
-  const int q = lane & 3;
-  const int t = t_base + tt;
-  const float* row = ll + tt * lstride;
+  const int nwaves = blockDim.x >> 6;
+  const int q = lane & 15;
   const int E = a.E, k = a.k;
+  for (int g0 = (threadIdx.x >> 6) * 4; g0 < ntok; g0 += nwaves * 4) {
+    const int tt = g0 + (lane >> 4);
+    const int t = t_base + tt;
+    const bool live = tt < ntok;
+    const float* row = ll + (live ? tt : 0) * lstride;
+    float v[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int e = q + 16 * u;
+      v[u] = (e < E) ? row[e] : -INFINITY;
+    }
+    // softmax denominator relative to the row max
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) m = fmaxf(m, v[u]);
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float sum = 0.f;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) sum += (q + 16 * u < E) ? __expf(v[u] - m) : 0.f;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off);
 
-  // full softmax denominator, relative to the row max
-  float m = -INFINITY;
-  for (int e = q; e < E; e += 4) m = fmaxf(m, row[e]);
-  m = fmaxf(m, __shfl_xor(m, 1));
-  m = fmaxf(m, __shfl_xor(m, 2));
-  float s = 0.f;
-  for (int e = q; e < E; e += 4) s += __expf(row[e] - m);
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
-
-  // two passes of the same deterministic selection: first the sum over the
-  // picks (renormalisation), then the outputs
-  float sel_sum = 0.f;
-  for (int pass = 0; pass < 2; ++pass) {
-    float pv = INFINITY;
+    float pv = INFINITY, sel = 0.f;
     int pe = -1;
-    const float denom = a.renorm ? sel_sum : s;
     for (int j = 0; j < k; ++j) {
       float bv = -INFINITY;
       int be = 0x7fffffff;
-      for (int e = q; e < E; e += 4) {
-        const float v = row[e];
-        const bool below = (v < pv) || (v == pv && e > pe);
-        const bool better = (v > bv) || (v == bv && e < be);
-        if (below && better) {
-          bv = v;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int e = q + 16 * u;
+        const bool below = (v[u] < pv) || (v[u] == pv && e > pe);
+        const bool better = (v[u] > bv) || (v[u] == bv && e < be);
+        if (e < E && below && better) {
+          bv = v[u];
           be = e;
         }
       }
 #pragma unroll
-      for (int off = 1; off <= 2; off <<= 1) {
+      for (int off = 1; off < 16; off <<= 1) {
         const float ov = __shfl_xor(bv, off);
         const int oe = __shfl_xor(be, off);
         if (ov > bv || (ov == bv && oe < be)) {
@@ -92,12 +102,14 @@ __device__ __forceinline__ void select_and_weigh(const float* ll, int lstride, c
       pv = bv;
       pe = be;
       const float ex = __expf(bv - m);
-      if (pass == 0) {
-        sel_sum += ex;
-      } else if (q == 0 && t < a.T) {
+      sel += ex;
+      if (q == 0 && live && t < a.T) {
         a.idx[(size_t)t * k + j] = be;
-        a.w[(size_t)t * k + j] = ex / denom;
+        a.w[(size_t)t * k + j] = a.renorm ? ex : ex / sum;
       }
+    }
+    if (a.renorm && q == 0 && live && t < a.T) {
+      for (int j = 0; j < k; ++j) a.w[(size_t)t * k + j] = a.w[(size_t)t * k + j] / sel;
     }
   }
 }
@@ -106,7 +118,7 @@ __device__ __forceinline__ void write_logits(const float* ll, int lstride, const
                                              int t_base, int ntok) {
   if (a.logits_out == nullptr) return;
   const int n = ntok * a.E;
-  for (int i = threadIdx.x; i < n; i += kThreads) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
     const int tt = i / a.E, e = i - tt * a.E;
     const int t = t_base + tt;
     if (t < a.T) a.logits_out[(size_t)t * a.E + e] = ll[tt * lstride + e];
@@ -130,20 +142,23 @@ __global__ __launch_bounds__(kThreads) void transpose_router_kernel(const bf16_t
   }
 }
 
-// NB = ceil(E / 16) column blocks of 16 experts; MB = token blocks of 16 per workgroup.
-template <int NB, int MB>
-__global__ __launch_bounds__(kThreads) void route_bf16_kernel(RouteArgs a, const bf16_t* __restrict__ Wt) {
+// NB = ceil(E / 16) column blocks of 16 experts; MB = token blocks of 16 per
+// workgroup; NWV waves split K (more waves = more loads in flight per CU: the
+// kernel is bound by streaming x once from HBM).
+template <int NB, int MB, int NWV>
+__global__ __launch_bounds__(NWV * 64) void route_bf16_kernel(RouteArgs a, const bf16_t* __restrict__ Wt) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int Ep = NB * 16;
   constexpr int TW = MB * 16;   // tokens per workgroup
   constexpr int ls = Ep + 1;    // LDS row stride of the logits, in floats
-  float* part = reinterpret_cast<float*>(smem);  // [4][TW][Ep] partial logits
+  constexpr int NT = NWV * 64;
+  float* part = reinterpret_cast<float*>(smem);  // [NWV][TW][Ep] partial logits
   float* ll = part;                               // [TW][ls] logits (reuses part)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t_base = blockIdx.x * TW;
   const int d = a.d, E = a.E;
-  const int kq = cdiv(cdiv(d, 4), 32) * 32;  // K per wave, a multiple of 32
+  const int kq = cdiv(cdiv(d, NWV), 32) * 32;  // K per wave, a multiple of 32
   const int kb = wave * kq, ke = min(d, kb + kq);
 
   const bf16_t* xr[MB];
@@ -164,23 +179,31 @@ __global__ __launch_bounds__(kThreads) void route_bf16_kernel(RouteArgs a, const
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // K in chunks of ST steps of 32: all loads of a chunk are issued before its
+  // MFMAs, so each wave keeps ST (MB + NB) 1 KiB loads in flight
+  constexpr int ST = (MB + NB) <= 2 ? 8 : (MB + NB) <= 4 ? 4 : 2;
   const bf16x8 zero8 = {};
-#pragma unroll 4
-  for (int k0 = kb; k0 < ke; k0 += 32) {
-    const int kk = k0 + (lane >> 4) * 8;
-    const bool kin = kk < ke;  // d % 8 == 0: a lane's 8 values are all in or all out
-    bf16x8 av[MB], bv[NB];
+  for (int k0 = kb; k0 < ke; k0 += 32 * ST) {
+    bf16x8 av[ST][MB], bv[ST][NB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      av[mb] = (kin && t_ok[mb]) ? *reinterpret_cast<const bf16x8*>(xr[mb] + kk) : zero8;
+    for (int st = 0; st < ST; ++st) {
+      const int kk = k0 + st * 32 + (lane >> 4) * 8;
+      const bool kin = kk < ke;  // d % 8 == 0: a lane's 8 values are all in or all out
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      bv[nb] = kin ? *reinterpret_cast<const bf16x8*>(wr[nb] + kk) : zero8;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
+        av[st][mb] = (kin && t_ok[mb]) ? *reinterpret_cast<const bf16x8*>(xr[mb] + kk) : zero8;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mb], bv[nb], acc[mb][nb], 0, 0, 0);
+        bv[st][nb] = kin ? *reinterpret_cast<const bf16x8*>(wr[nb] + kk) : zero8;
+    }
+#pragma unroll
+    for (int st = 0; st < ST; ++st)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[mb][nb] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[st][mb], bv[st][nb], acc[mb][nb], 0, 0, 0);
   }
 
   // accumulator lane layout of a 16x16 block: column lane % 16, rows
@@ -195,28 +218,30 @@ __global__ __launch_bounds__(kThreads) void route_bf16_kernel(RouteArgs a, const
         part[(wave * TW + tt) * Ep + nb * 16 + (lane & 15)] = acc[mb][nb][i];
       }
   __syncthreads();
-  // sum the four K quarters in wave order, add the bias
-  float lv[(TW * Ep + kThreads - 1) / kThreads];
+  // sum the K parts in wave order, add the bias
+  constexpr int PER = (TW * Ep + NT - 1) / NT;
+  float lv[PER];
 #pragma unroll
-  for (int u = 0; u < (TW * Ep + kThreads - 1) / kThreads; ++u) {
-    const int i = tid + u * kThreads;
+  for (int u = 0; u < PER; ++u) {
+    const int i = tid + u * NT;
     float v = 0.f;
     if (i < TW * Ep) {
       const int e = i % Ep;
-      v = part[i] + part[TW * Ep + i] + part[2 * TW * Ep + i] + part[3 * TW * Ep + i];
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) v += part[w * TW * Ep + i];
       if (a.bias && e < E) v += a.bias[e];
     }
     lv[u] = v;
   }
   __syncthreads();
 #pragma unroll
-  for (int u = 0; u < (TW * Ep + kThreads - 1) / kThreads; ++u) {
-    const int i = tid + u * kThreads;
+  for (int u = 0; u < PER; ++u) {
+    const int i = tid + u * NT;
     if (i < TW * Ep) ll[(i / Ep) * ls + (i % Ep)] = lv[u];
   }
   __syncthreads();
   write_logits(ll, ls, a, t_base, TW);
-  select_and_weigh(ll, ls, a, t_base, TW);
+  select_and_weigh<NB>(ll, ls, a, t_base, TW);
 }
 
 // fp32 path (small layers): plain sequential FMA dot products, 64 tokens
@@ -241,30 +266,41 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(RouteArgs a) {
   }
   __syncthreads();
   write_logits(ll, ls, a, t_base, kTok);
-  select_and_weigh(ll, ls, a, t_base, kTok);
+  select_and_weigh<16>(ll, ls, a, t_base, kTok);
 }
 
-template <int NB, int MB>
+template <int NB, int MB, int NWV>
 hipError_t launch_nb_mb(const RouteArgs& a, const bf16_t* Wt, hipStream_t s) {
   constexpr int Ep = NB * 16, TW = MB * 16;
-  const size_t lds = (size_t)4 * TW * Ep * 4;  // >= TW * (Ep + 1) * 4, the logits reuse it
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)route_bf16_kernel<NB, MB>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((route_bf16_kernel<NB, MB>), dim3(cdiv(a.T, TW)), dim3(kThreads), lds, s, a, Wt);
+  const size_t lds = (size_t)NWV * TW * Ep * 4;  // >= TW * (Ep + 1) * 4, the logits reuse it
+  static_assert((size_t)NWV * TW * Ep * 4 <= 65536, "partial logits fit 64 KiB");
+  hipLaunchKernelGGL((route_bf16_kernel<NB, MB, NWV>), dim3(cdiv(a.T, TW)), dim3(NWV * 64), lds, s,
+                     a, Wt);
   return hipGetLastError();
 }
 
-// Token blocks per workgroup: as many as keep >= 256 workgroups in flight
-// and the partial-logit buffer at <= 32 KiB.
+// Token blocks per workgroup (MB) and K-splitting waves (NWV): the kernel
+// streams x once, so it wants many loads in flight -- about 16 waves per
+// CU -- while the partial logits [NWV][16 MB][Ep] stay within 64 KiB and
+// each workgroup reads the transposed W_r (from L2) once per 16 MB tokens.
 template <int NB>
 hipError_t launch_nb(const RouteArgs& a, const bf16_t* Wt, hipStream_t s) {
   constexpr int Ep = NB * 16;
-  if (a.T >= 256 * 64 && 64 * Ep <= 2048) return launch_nb_mb<NB, 4>(a, Wt, s);
-  if (a.T >= 256 * 32 && 32 * Ep <= 2048) return launch_nb_mb<NB, 2>(a, Wt, s);
-  return launch_nb_mb<NB, 1>(a, Wt, s);
+  constexpr int NW16 = (16 * 16 * Ep * 4 <= 65536) ? 16 : (8 * 16 * Ep * 4 <= 65536) ? 8 : 4;
+  constexpr int NW32 = (16 * 32 * Ep * 4 <= 65536) ? 16 : (8 * 32 * Ep * 4 <= 65536) ? 8 : 4;
+  if constexpr (4 * 64 * Ep * 4 <= 65536) {
+    // 4 token blocks for long batches: a quarter of the W_r reads per token
+    if (a.T >= 256 * 64) return launch_nb_mb<NB, 4, 4>(a, Wt, s);
+  }
+  if constexpr (4 * 32 * Ep * 4 <= 65536) {
+    if (a.T >= 256 * 32) {
+      // 2 token blocks: fewer reads of W_r per token
+      if (a.T >= 256 * 32 * 4) return launch_nb_mb<NB, 2, (NW32 > 4 ? 4 : NW32)>(a, Wt, s);
+      return launch_nb_mb<NB, 2, (NW32 > 8 ? 8 : NW32)>(a, Wt, s);
+    }
+  }
+  if (a.T >= 256 * 16 * 2) return launch_nb_mb<NB, 1, (NW16 > 8 ? 8 : NW16)>(a, Wt, s);
+  return launch_nb_mb<NB, 1, NW16>(a, Wt, s);
 }
 
 }  // namespace

@@ -658,44 +658,60 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
 //   phase 2s    : X memory(s)  | Y compute(s - 1)
 //   phase 2s + 1: X compute(s) | Y memory(s)
 //
-// memory(s) = read the wave's fragments of the whole stage s (both K steps)
-// from LDS and issue the wave's loads of a later stage; compute(s) = its 64
-// MFMAs.  So on every SIMD one wave keeps the matrix core busy while the
-// other waits on LDS reads and load issue.  X issues all A loads (stage s+1
-// during memory(s): two phases to land), Y all B loads (stage s+2 during
-// memory(s): three phases).  LDS: A ring of 2 stages, B ring of 3 (5 x 32
-// KiB).  A stage's slot is refilled only after both groups' memory phases
-// for it (each ends with its reads waited for, before the barrier).
+// memory(s) = read the wave's fragments of stage s from LDS and issue the
+// wave's loads of a later stage; compute(s) = its MFMAs on stage s.  So on
+// every SIMD one wave keeps the matrix core busy while the other waits on
+// LDS reads and load issue.  X issues all A loads, Y all B loads.  With
+// rings of RA (A) and RB (B) stages, memory(s) loads stage s + RA - 1 (X)
+// or s + RB - 1 (Y) into the slot of stage s - 1, whose readers finished
+// before phase 2s (each memory phase ends with its reads waited for); a
+// wave waits for its part of stage s + 1 at the end of phase 2s + 1, and
+// the barrier after it makes the stage visible to all.
 //
-// B stage layout: two halves of 64 K rows x 128 columns (256 B per row),
+// Stage depth PBK = 64 (two MFMA K steps per stage; rings 2 + 3) or 32 (one
+// K step; rings 5 + 5): the same 160 KiB of LDS, but with 32-deep stages
+// every load is issued 3 stages (6 phases) ahead instead of 1 (A) or 2 (B).
+//
+// B stage layout: two halves of PBK K rows x 128 columns (256 B per row),
 // each 1 KiB load filling 4 rows of one half.  Layer 0: half 0 = W_gate,
 // half 1 = W_up (the same 128 columns); layer 1: the two 128-column halves
 // of a 256-column panel.
 //
 // Loads use the scalar-base form of global_load_lds_dwordx4 (uniform 64-bit
 // base + per-lane 32-bit byte offset): one register per load slot; stages
-// advance the scalar base.  K must be a multiple of the stage depth (64)
-// and the token matrix smaller than 4 GiB; other shapes take the kernel
-// above.
+// advance the scalar base.  K must be a multiple of PBK and the A operand
+// smaller than 4 GiB; other shapes take the kernel above.
 // ------------------------------------------------------------------------
+#ifndef MOE_PP_PRIO
+#define MOE_PP_PRIO 1
+#endif
 namespace pp {
 constexpr int NW = 8, MI = 8, NJ = 4;
-constexpr int LD = 8;                       // 1 KiB loads per wave per stage (A for X, B for Y)
-constexpr int SLOT = 32768;                 // one operand stage
-constexpr int HALF = 16384;                 // one B half (64 rows x 256 B)
-constexpr int B_RING = 2 * SLOT;            // B slots start after the two A slots
-constexpr int LDS_BYTES = 5 * SLOT;
-static_assert(BM * BK * 2 == SLOT, "stage sizes");
-static_assert(BK == 64, "two MFMA K steps per stage");
 
-// A swizzle from the row's position inside its 16-row block only, so that
-// every 16-row fragment block of a wave has the same lane offsets: the
-// fragment addresses of one K step are one register plus immediates.
-// XOR-ing the chunk with row / 2 (mod 8) makes the fragment read (16 rows
-// at one chunk per 16 lanes) free of LDS bank conflicts on gfx950
-// (measured with SQ_LDS_BANK_CONFLICT: 0, against ~1 conflict cycle per
-// busy cycle for XOR with row % 8, row % 8 ^ row / 8 or 2 (row / 4 % 4)).
-__device__ __forceinline__ int a_swz16(int row) { return (row >> 1) & 7; }
+template <int PBK>
+struct Cfg {
+  static constexpr int SLOT = BM * PBK * 2;            // one operand stage (A or B)
+  static constexpr int HALF = PBK * 128 * 2;           // one B half
+  static constexpr int RA = PBK == 64 ? 2 : 5;         // A ring
+  static constexpr int RB = PBK == 64 ? 3 : 5;         // B ring
+  static constexpr int LDS_BYTES = (RA + RB) * SLOT;
+  static constexpr int KS = PBK / 32;                  // MFMA K steps per stage
+  static constexpr int LD = SLOT / 1024 / 4;           // 1 KiB loads per wave per stage
+  static constexpr int CPR = PBK / 8;                  // 16-byte chunks per A row
+  static constexpr int RPL = 1024 / (PBK * 2);         // A rows per load
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+};
+
+// A swizzle: the 16-byte chunk index XOR-ed with row / 2 (mod chunks per
+// row).  It depends on the row's position inside its 16-row block only,
+// so every fragment block of a wave has the same lane offsets (one
+// register plus immediates), and it makes the fragment read (16 rows at
+// one chunk per 16 lanes) free of LDS bank conflicts on gfx950: measured
+// with SQ_LDS_BANK_CONFLICT, 0 for 128-byte and 64-byte rows, against ~1
+// conflict cycle per busy cycle for XOR with row % 8, row % 8 ^ row / 8,
+// 2 (row / 4 % 4) (128-byte rows) or row / 4 % 4 (64-byte rows).
+template <int PBK>
+__device__ __forceinline__ int a_swz16(int row) { return (row >> 1) & (PBK / 8 - 1); }
 
 // One direct-to-LDS load with a scalar base: lane i reads 16 bytes at
 // base + voff_i and writes LDS bytes lds_addr + 16 i.
@@ -714,12 +730,24 @@ __device__ __forceinline__ const char* uniform_ptr(const void* p) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
+
+// s_waitcnt vmcnt(n * LD) for a run-time n in 0..3
+template <int LD>
+__device__ __forceinline__ void wait_groups(int n) {
+  if (n >= 3) wait_vmcnt<3 * LD>();
+  else if (n == 2) wait_vmcnt<2 * LD>();
+  else if (n == 1) wait_vmcnt<LD>();
+  else wait_vmcnt<0>();
+}
 }  // namespace pp
 
-template <bool UP>
+template <bool UP, int PBK>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p) {
   using namespace pp;
-  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+  using C = Cfg<PBK>;
+  constexpr int SLOT = C::SLOT, HALF = C::HALF, RA = C::RA, RB = C::RB, KS = C::KS, LD = C::LD;
+  constexpr int B_RING = RA * SLOT;  // B slots start after the A slots
+  __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
   const int b = blockIdx.x;
   const int tile = (b & 7) * p.grid_per_xcd + (b >> 3);
@@ -741,20 +769,21 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
   const uint32_t lds0 = lds_addr_of(lds);
   const int k_begin = t_ks * p.k_per_split;
   const int k_end = min(K, k_begin + p.k_per_split);
-  const int nk = (k_end - k_begin) / BK;
+  const int nk = (k_end - k_begin) / PBK;
 
-  // ---- loads.  X: load j = 8 wg + q fills A rows 8 j .. 8 j + 7; lane l
-  // reads 16 B of row 8 j + l / 8 (chunk swizzled by the row).  Y: load
-  // j = 8 wg + q fills K rows 4 (j % 16) .. + 3 of B half j / 16; lane l reads
-  // 16 B of row 4 (j % 16) + l / 16; the lane part depends on q % 4 only.
-  uint32_t ld_off[LD];  // X: A byte offsets at k_begin; Y: B byte offsets (first 4 used)
-  const char* ld_base0; // stage-0 scalar base (Y: of row group 2 (wg & 1))
+  // ---- loads.  X: load j = LD wg + q fills A rows RPL j .. RPL (j + 1) - 1;
+  // lane l reads 16 B of row RPL j + l / CPR (chunk swizzled by the row).
+  // Y: load j = LD wg + q fills K rows 4 (j % (PBK / 4)) .. + 3 of B half
+  // j / (PBK / 4) = wg / 2; lane l reads 16 B of row 4 (j % (PBK / 4)) + l / 16.
+  // Its lane part depends on q % 4 only (q / 4 adds 16 rows).
+  uint32_t ld_off[LD];  // X: A byte offsets at k_begin; Y: B byte offsets (q < 4)
+  const char* ld_base0; // stage-0 scalar base
   const int b_half = wg >> 1;
   if (X) {
 #pragma unroll
     for (int q = 0; q < LD; ++q) {
-      const int row = (wg * LD + q) * 8 + (lane >> 3);
-      const int chunk = (lane & 7) ^ a_swz16(row);
+      const int row = (wg * LD + q) * C::RPL + lane / C::CPR;
+      const int chunk = (lane % C::CPR) ^ a_swz16<PBK>(row);
       int r = t_row0 + row;
       if (r >= t_row_end) r = t_row0;  // padding rows read a valid row; results are discarded
       const int src_row = p.gather ? p.gather[r] : r;
@@ -765,34 +794,32 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
     const bf16_t* b_mat = UP ? (b_half ? p.B1 : p.B0) : p.B0;
     const int n0h = UP ? n0 : n0 + b_half * 128;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int krow = 4 * u + (lane >> 4);  // row inside its 16-row group
+    for (int u = 0; u < LD; ++u) {
+      const int krow = 4 * (u & 3) + (lane >> 4);  // row inside its 16-row group
       const int chunk = (lane & 15) ^ b_swz<128>(krow);
       int col = n0h + chunk * 8;
       if (col >= N) col = N - 8;  // padding columns read valid data; results are discarded
       ld_off[u] = ((uint32_t)krow * (uint32_t)N + (uint32_t)col) * 2u;
-      ld_off[u + 4] = 0;
     }
     ld_base0 = uniform_ptr(b_mat + (size_t)t_e * K * N +
-                           (size_t)(k_begin + 16 * (2 * (wg & 1))) * N);
+                           (size_t)(k_begin + (PBK / 2) * (wg & 1)) * N);
   }
-  // (K is a multiple of BK here: the host sends other shapes elsewhere)
-  auto issue_a = [&](int kt, int q) {
-    const uint32_t dst = lds0 + (uint32_t)((kt & 1) * SLOT + (wg * LD + q) * 1024);
-    lds_dma16_s(ld_off[q], ld_base0 + (size_t)kt * BK * 2, dst);
+  auto issue_a = [&](int kt, int slot, int q) {
+    const uint32_t dst = lds0 + (uint32_t)(slot * SLOT + (wg * LD + q) * 1024);
+    lds_dma16_s(ld_off[q], ld_base0 + (size_t)kt * PBK * 2, dst);
   };
   auto issue_b = [&](int kt, int slot, int q) {
     const uint32_t dst = lds0 + (uint32_t)(B_RING + slot * SLOT + (wg * LD + q) * 1024);
-    const char* base = ld_base0 + ((size_t)kt * BK + (size_t)(16 * (q >> 2))) * N * 2;
-    lds_dma16_s(ld_off[q & 3], uniform_ptr(base), dst);
+    const char* base = ld_base0 + ((size_t)kt * PBK + (size_t)(16 * (q >> 2))) * N * 2;
+    lds_dma16_s(ld_off[q], uniform_ptr(base), dst);
   };
 
   // ---- fragment read offsets (bytes inside a stage slot)
   const int l15 = lane & 15, g = lane >> 4;
   const int wrow0 = X ? 0 : 128;
-  const int a_s = a_swz16(l15);
-  const int a_rd0 = (wrow0 + l15) * 128 + ((g ^ a_s) << 4);        // K step 0
-  const int a_rd1 = (wrow0 + l15) * 128 + (((g + 4) ^ a_s) << 4);  // K step 1
+  const int a_s = a_swz16<PBK>(l15);
+  const int a_rd0 = (wrow0 + l15) * (PBK * 2) + ((g ^ a_s) << 4);        // K step 0
+  const int a_rd1 = (wrow0 + l15) * (PBK * 2) + (((g + 4) ^ a_s) << 4);  // K step 1 (PBK = 64)
   // B: blocks nj = 0, 1 in half 0, nj = 2, 3 the same columns of half 1; K
   // step 1 adds 32 rows (8 KiB, same swizzle)
   int b_rd[2], b_rd4[2];
@@ -809,14 +836,14 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj) acc[mi][nj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  bf16x8 fa[2][MI], fb[2][NJ];  // fragments of one stage: [K step][block]
-  // memory phase: issue this wave's loads (A(ld_kt) for X, B(ld_kt) for Y),
-  // read the stage's fragments, wait for the reads
-  auto memory = [&](int s, int ld_kt, int ld_bslot) {
-    const char* As = lds + (s & 1) * SLOT;
-    const char* Bs = lds + B_RING + (s % 3) * SLOT;
+  bf16x8 fa[KS][MI], fb[KS][NJ];  // fragments of one stage: [K step][block]
+  // memory phase: read the stage's fragments (A slot sa, B slot sb), issue
+  // this wave's loads of stage ld_kt into slot ld_slot, wait for the reads
+  auto memory = [&](int sa, int sb, int ld_kt, int ld_slot) {
+    const char* As = lds + sa * SLOT;
+    const char* Bs = lds + B_RING + sb * SLOT;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int nj = 0; nj < NJ; ++nj) {
         const char* Bh = Bs + (nj >> 1) * HALF + ks * 8192;
@@ -829,65 +856,73 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
       const char* Ak = As + (ks ? a_rd1 : a_rd0);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
-        fa[ks][mi] = *reinterpret_cast<const bf16x8*>(Ak + mi * 2048);
-      // half of the loads after each K step's reads
+        fa[ks][mi] = *reinterpret_cast<const bf16x8*>(Ak + mi * 16 * PBK * 2);
+      // the loads after the reads of each K step (half of them each when
+      // there are two)
       if (ld_kt < nk) {
 #pragma unroll
-        for (int q = ks * 4; q < ks * 4 + 4; ++q) {
-          if (X) issue_a(ld_kt, q);
-          else issue_b(ld_kt, ld_bslot, q);
+        for (int q = ks * (LD / KS); q < (ks + 1) * (LD / KS); ++q) {
+          if (X) issue_a(ld_kt, ld_slot, q);
+          else issue_b(ld_kt, ld_slot, q);
         }
       }
     }
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
   };
   auto compute = [&]() {
+    if (MOE_PP_PRIO) __builtin_amdgcn_s_setprio(MOE_PP_PRIO);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int nj = 0; nj < NJ; ++nj)
           acc[mi][nj] =
               __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ks][mi], fb[ks][nj], acc[mi][nj], 0, 0, 0);
+    if (MOE_PP_PRIO) __builtin_amdgcn_s_setprio(0);
   };
 
   // The two groups run separate loops with the same barrier count: one
-  // after the prologue and two per stage.
+  // after the prologue and two per stage.  Slots rotate: stage s sits in A
+  // slot s % RA and B slot s % RB.
   if (X) {
-    // prologue: A(0)
+    // prologue: A(0) .. A(RA - 2); wait for A(0)
+    for (int s = 0; s < RA - 1 && s < nk; ++s)
 #pragma unroll
-    for (int q = 0; q < LD; ++q) issue_a(0, q);
-    wait_vmcnt<0>();
+      for (int q = 0; q < LD; ++q) issue_a(s, s, q);
+    wait_groups<LD>(min(RA - 2, nk - 1));
     __builtin_amdgcn_s_barrier();
+    int sa = 0, sb = 0;
     for (int s = 0; s < nk; ++s) {
-      memory(s, s + 1, 0);   // phase 2s: read stage s, load A(s + 1)
+      const int la = sa == 0 ? RA - 1 : sa - 1;  // slot of stage s - 1 = of s + RA - 1
+      memory(sa, sb, s + RA - 1, la);            // phase 2s
       __builtin_amdgcn_s_barrier();
-      compute();             // phase 2s + 1
-      wait_vmcnt<0>();       // A(s + 1) has landed
+      compute();                                  // phase 2s + 1
+      // A(s + 1) has landed once the later stages' loads are all that remain
+      wait_groups<LD>(min(RA - 2, nk - 2 - s));
       __builtin_amdgcn_s_barrier();
+      sa = sa == RA - 1 ? 0 : sa + 1;
+      sb = sb == RB - 1 ? 0 : sb + 1;
     }
   } else {
-    // prologue: B(0), B(1)
+    // prologue: B(0) .. B(RB - 2); wait for B(0)
+    for (int s = 0; s < RB - 1 && s < nk; ++s)
 #pragma unroll
-    for (int q = 0; q < LD; ++q) issue_b(0, 0, q);
-    if (nk > 1) {
-#pragma unroll
-      for (int q = 0; q < LD; ++q) issue_b(1, 1, q);
-      wait_vmcnt<LD>();
-    } else {
-      wait_vmcnt<0>();
-    }
+      for (int q = 0; q < LD; ++q) issue_b(s, s, q);
+    wait_groups<LD>(min(RB - 2, nk - 1));
     __builtin_amdgcn_s_barrier();
+    int sa = 0, sb = 0;
     for (int s = 0; s < nk; ++s) {
       if (s > 0) compute();  // phase 2s: stage s - 1
       __builtin_amdgcn_s_barrier();
-      // phase 2s + 1: read stage s, load B(s + 2) into the slot of stage s - 1;
-      // then B(s + 1) must have landed
-      memory(s, s + 2, (s + 2) % 3);
-      if (s + 2 < nk) wait_vmcnt<LD>();
-      else wait_vmcnt<0>();
+      // phase 2s + 1: read stage s, load B(s + RB - 1) into the slot of stage
+      // s - 1; then B(s + 1) must have landed
+      const int lb = sb == 0 ? RB - 1 : sb - 1;
+      memory(sa, sb, s + RB - 1, lb);
+      wait_groups<LD>(min(RB - 2, nk - 2 - s));
       __builtin_amdgcn_s_barrier();
+      sa = sa == RA - 1 ? 0 : sa + 1;
+      sb = sb == RB - 1 ? 0 : sb + 1;
     }
     compute();  // phase 2 nk: stage nk - 1 (LDS is free: all reads and loads waited for)
   }
@@ -1031,6 +1066,9 @@ int max_tiles_m(int rows, int E) {
 #ifndef MOE_GEMM_PPK
 #define MOE_GEMM_PPK 1
 #endif
+#ifndef MOE_PP_BK
+#define MOE_PP_BK 64  // stage depth of the ping-pong kernel (64 or 32)
+#endif
 constexpr int UP_WN = MOE_UP_WN, UP_BNA = MOE_UP_BNA, DN_WN = MOE_DN_WN, DN_BNA = MOE_DN_BNA;
 
 int num_cus() {
@@ -1087,8 +1125,8 @@ hipError_t launch_gemm(GemmArgs& p, int rows, int E, int ncols, unsigned long lo
   p.grid_per_xcd = (int)(grid / 8);
 #if MOE_GEMM_PPK
   static_assert(BNA == 256, "ping-pong kernel tile width");
-  if (p.K % BK == 0 && p.k_per_split % BK == 0 && a_rows_bytes < (1ull << 32)) {
-    hipLaunchKernelGGL((grouped_gemm_bf16_pp_kernel<UP>), dim3((unsigned)grid),
+  if (p.K % MOE_PP_BK == 0 && p.k_per_split % MOE_PP_BK == 0 && a_rows_bytes < (1ull << 32)) {
+    hipLaunchKernelGGL((grouped_gemm_bf16_pp_kernel<UP, MOE_PP_BK>), dim3((unsigned)grid),
                        dim3(64 * pp::NW), 0, s, p);
     return hipGetLastError();
   }

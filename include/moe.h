@@ -109,7 +109,14 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, const void* x, int
                 int32_t* inv, float* perm_w, void* x_perm, void* workspace, size_t ws_bytes,
                 hipStream_t stream);
 
-/* Workspace bytes moe_expert_up / moe_expert_down / moe_ffn_forward need. */
+/*
+ * Workspace bytes that let moe_expert_up / moe_expert_down / moe_ffn_forward
+ * split the K loop of the tiles of a mostly idle last round of tiles (the
+ * partial sums of the split tiles are kept there and added in a fixed
+ * order by a second pass, so results stay deterministic).  The workspace is
+ * optional: with NULL or fewer bytes the GEMMs run unsplit.  One call's
+ * workspace must not be used by another call running at the same time.
+ */
 size_t moe_ffn_workspace_size(int E, int rows, int d, int f);
 
 /*

@@ -89,6 +89,10 @@ struct GemmArgs {
   int ksplit;               // K ranges per output tile (layer 1 with fused combine only)
   int k_per_split;          // K per range, a multiple of BK
   int grid_per_xcd;         // padded grid / 8
+  // ping-pong kernel only: tail split (see assign_work)
+  float* part;              // partial accumulators of split tiles, or NULL (no split)
+  int n_cu;                 // compute units the tiles are spread over
+  int fixup;                // 0: main pass; 1: sum the split tiles' partials
 };
 
 struct TileInfo {
@@ -741,7 +745,128 @@ __device__ __forceinline__ void wait_groups(int n) {
 }
 }  // namespace pp
 
-template <bool UP, int PBK>
+// Tail split.  With N_t output tiles on C compute units the last round
+// holds N_t mod C tiles; when that is at most C / 2 (and N_t <= 8 C), each
+// of those tail tiles is split along K into S = min(C / tail, stages) parts that run
+// side by side, their fp32 partial accumulators go to p.part, and a second
+// launch (fixup) adds the parts in part order and runs the tile's normal
+// epilogue.  Every workgroup derives N_t, the split and its own work item
+// from the device offsets, so the host never reads the routing.
+//   main pass, block b: b < G (the first F = N_t - tail tiles, padded to a
+//     multiple of 8 and walked XCD-aware as usual) -> full tile; b >= G ->
+//     split item j = b - G: tail tile F + j / S, part j % S;
+//   fixup pass, block b < tail: tail tile F + b.
+struct Work {
+  int tile, ks, S, item;  // item: index of the split item (-1: a whole tile)
+  int k_begin, k_end;
+  bool ok;
+  TileInfo ti;
+};
+
+// One pass over the offsets (4 experts per lane, as in locate_tile): the
+// per-expert tile counts, their wave prefix sum (the total and each
+// expert's first tile), the split, this block's work item and its tile.
+__device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
+  const int lane = threadIdx.x & 63;
+  int cnt_tiles[4], mt[4], offe[4];
+  int lane_sum = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = lane * 4 + u;
+    int m = 0, o = 0;
+    if (e < p.E) {
+      o = p.offsets[e];
+      m = cdiv(p.offsets[e + 1] - o, BM);
+    }
+    mt[u] = m;
+    offe[u] = o;
+    cnt_tiles[u] = m * p.tiles_n;
+    lane_sum += cnt_tiles[u];
+  }
+  int incl = lane_sum;
+#pragma unroll
+  for (int sft = 1; sft < 64; sft <<= 1) {
+    const int v = __shfl_up(incl, sft);
+    if (lane >= sft) incl += v;
+  }
+  const int n_tiles = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+  const int C = p.n_cu;
+  int tail = n_tiles % C;
+  const int nk_all = p.K / pbk;
+  int S = 1, kps = p.K;
+  // split only where the last round is a large share of the launch (at
+  // most 8 rounds) and mostly idle (at most half full); otherwise the fixup
+  // pass costs more than the idle compute units
+  if (p.part != nullptr && tail > 0 && 2 * tail <= C && n_tiles <= 8 * C && nk_all >= 2) {
+    S = min(C / tail, nk_all);
+    kps = cdiv(nk_all, S) * pbk;
+    S = cdiv(p.K, kps);  // parts that are not empty
+  }
+  if (S == 1) tail = 0;
+  const int F = n_tiles - tail;
+  Work w{};
+  w.S = S;
+  w.ok = false;
+  w.item = -1;
+  w.ks = 0;
+  w.k_begin = 0;
+  w.k_end = p.K;
+  w.tile = -1;
+  if (p.fixup) {
+    if (b < tail) {
+      w.tile = F + b;
+      w.item = b * S;
+    }
+  } else {
+    const int G = cdiv(F, 8) * 8;
+    if (b < G) {
+      const int t = (b & 7) * (G / 8) + (b >> 3);
+      if (t < F) w.tile = t;
+    } else if (b - G < tail * S) {
+      const int j = b - G;
+      w.tile = F + j / S;
+      w.ks = j % S;
+      w.item = j;
+      w.k_begin = w.ks * kps;
+      w.k_end = min(p.K, w.k_begin + kps);
+    }
+  }
+  if (w.tile < 0) return w;
+  // the expert holding tile w.tile, from the same prefix sums
+  int start = incl - lane_sum;
+  int hit_e = -1, hit_start = 0, hit_mt = 0, hit_off = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (w.tile >= start && w.tile < start + cnt_tiles[u]) {
+      hit_e = lane * 4 + u;
+      hit_start = start;
+      hit_mt = mt[u];
+      hit_off = offe[u];
+    }
+    start += cnt_tiles[u];
+  }
+  const uint64_t hit = __ballot(hit_e >= 0);
+  if (hit == 0) return w;
+  const int src = __ffsll((unsigned long long)hit) - 1;
+  TileInfo& ti = w.ti;
+  ti.e = __shfl(hit_e, src);
+  const int tstart = __shfl(hit_start, src);
+  const int tmt = __shfl(hit_mt, src);
+  const int toff = __shfl(hit_off, src);
+  const int local = w.tile - tstart;
+  ti.n_t = local / tmt;  // M fastest inside an (expert, N panel)
+  ti.m_t = local - ti.n_t * tmt;
+  ti.ks = 0;
+  ti.row0 = toff + ti.m_t * BM;
+  ti.row_end = min(ti.row0 + BM, p.offsets[ti.e + 1]);
+  ti.ok = true;
+  w.ok = true;
+  return w;
+}
+
+// FIX = false: the main pass; FIX = true: the fixup pass of the tail split
+// (no K loop: the accumulators are the sum of the split items' partials).
+template <bool UP, int PBK, bool FIX>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p) {
   using namespace pp;
   using C = Cfg<PBK>;
@@ -749,16 +874,14 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
   constexpr int B_RING = RA * SLOT;  // B slots start after the A slots
   __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
-  const int b = blockIdx.x;
-  const int tile = (b & 7) * p.grid_per_xcd + (b >> 3);
-  const TileInfo ti0 = locate_tile<true>(p, tile);
-  if (!ti0.ok) return;
+  const Work wk = assign_work(p, blockIdx.x, PBK);
+  if (!wk.ok) return;
+  const TileInfo& ti0 = wk.ti;
   // the tile is the same for every lane: keep it in scalar registers
   const int t_e = __builtin_amdgcn_readfirstlane(ti0.e);
   const int t_row0 = __builtin_amdgcn_readfirstlane(ti0.row0);
   const int t_row_end = __builtin_amdgcn_readfirstlane(ti0.row_end);
   const int t_n = __builtin_amdgcn_readfirstlane(ti0.n_t);
-  const int t_ks = __builtin_amdgcn_readfirstlane(ti0.ks);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -767,9 +890,11 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
   const int K = p.K, N = p.N;
   const int n0 = t_n * (UP ? 128 : 256);
   const uint32_t lds0 = lds_addr_of(lds);
-  const int k_begin = t_ks * p.k_per_split;
-  const int k_end = min(K, k_begin + p.k_per_split);
-  const int nk = (k_end - k_begin) / PBK;
+  const int k_begin = __builtin_amdgcn_readfirstlane(wk.k_begin);
+  const int k_end = __builtin_amdgcn_readfirstlane(wk.k_end);
+  const int nk = FIX ? 0 : (k_end - k_begin) / PBK;
+  const int w_item = __builtin_amdgcn_readfirstlane(wk.item);
+  const int w_S = __builtin_amdgcn_readfirstlane(wk.S);
 
   // ---- loads.  X: load j = LD wg + q fills A rows RPL j .. RPL (j + 1) - 1;
   // lane l reads 16 B of row RPL j + l / CPR (chunk swizzled by the row).
@@ -885,7 +1010,9 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
   // The two groups run separate loops with the same barrier count: one
   // after the prologue and two per stage.  Slots rotate: stage s sits in A
   // slot s % RA and B slot s % RB.
-  if (X) {
+  if (FIX) {
+    // no K loop
+  } else if (X) {
     // prologue: A(0) .. A(RA - 2); wait for A(0)
     for (int s = 0; s < RA - 1 && s < nk; ++s)
 #pragma unroll
@@ -924,7 +1051,30 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
       sa = sa == RA - 1 ? 0 : sa + 1;
       sb = sb == RB - 1 ? 0 : sb + 1;
     }
-    compute();  // phase 2 nk: stage nk - 1 (LDS is free: all reads and loads waited for)
+    if (nk > 0) compute();  // phase 2 nk: stage nk - 1 (LDS is free: all reads and loads waited for)
+  }
+
+  // partial accumulators of split item i: [i][wave][mi * NJ + nj][lane] x 4 floats
+  f32x4* part_base = reinterpret_cast<f32x4*>(p.part) + (size_t)(w_item < 0 ? 0 : w_item) * 512 * MI * NJ;
+  if (FIX) {
+    // sum the S partials of this tail tile in part order
+    const int S = w_S;
+    for (int sp = 0; sp < S; ++sp) {
+      const f32x4* src = part_base + (size_t)sp * 512 * MI * NJ;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj)
+          acc[mi][nj] += src[((size_t)wave * MI * NJ + mi * NJ + nj) * 64 + lane];
+    }
+  } else if (w_item >= 0) {
+    // a split item: store the partial accumulators; the fixup pass finishes the tile
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < NJ; ++nj)
+        part_base[((size_t)wave * MI * NJ + mi * NJ + nj) * 64 + lane] = acc[mi][nj];
+    return;
   }
 
   // ---- epilogue (accumulator layout of a 16 x 16 block: column lane % 16,
@@ -1105,9 +1255,14 @@ int choose_ksplit(long long tiles, int K, int cus) {
 
 // a_rows_bytes: size of the A matrix the kernel may read (rows that can be
 // addressed times K times 2 bytes)
+// Workspace of the ping-pong kernel's tail split: one 256 x 256 fp32
+// partial tile per split item, at most one item per compute unit.
+size_t pp_part_bytes(int n_cu) { return (size_t)n_cu * BM * 256 * sizeof(float); }
+
+// p.part: the caller's workspace (ws_bytes); used when large enough
 template <bool UP, int WM, int WN, int BNA>
 hipError_t launch_gemm(GemmArgs& p, int rows, int E, int ncols, unsigned long long a_rows_bytes,
-                       hipStream_t s) {
+                       size_t ws_bytes, hipStream_t s) {
   const int tiles_n = cdiv(ncols, UP ? BNA / 2 : BNA);
   const long long tiles_mn = (long long)max_tiles_m(rows, E) * tiles_n;
   int ksplit = 1;
@@ -1125,9 +1280,21 @@ hipError_t launch_gemm(GemmArgs& p, int rows, int E, int ncols, unsigned long lo
   p.grid_per_xcd = (int)(grid / 8);
 #if MOE_GEMM_PPK
   static_assert(BNA == 256, "ping-pong kernel tile width");
-  if (p.K % MOE_PP_BK == 0 && p.k_per_split % MOE_PP_BK == 0 && a_rows_bytes < (1ull << 32)) {
-    hipLaunchKernelGGL((grouped_gemm_bf16_pp_kernel<UP, MOE_PP_BK>), dim3((unsigned)grid),
-                       dim3(64 * pp::NW), 0, s, p);
+  if (ksplit == 1 && p.K % MOE_PP_BK == 0 && a_rows_bytes < (1ull << 32)) {
+    // main pass: the whole tiles plus at most n_cu split items; then the
+    // fixup pass over at most n_cu / 2 tail tiles (both derive the split
+    // from the device offsets; without a workspace there is none)
+    p.n_cu = num_cus();
+    p.fixup = 0;
+    if (ws_bytes < pp_part_bytes(p.n_cu)) p.part = nullptr;
+    const long long grid_pp = grid + (p.part ? p.n_cu : 0);
+    hipLaunchKernelGGL((grouped_gemm_bf16_pp_kernel<UP, MOE_PP_BK, false>),
+                       dim3((unsigned)grid_pp), dim3(64 * pp::NW), 0, s, p);
+    if (p.part) {
+      p.fixup = 1;
+      hipLaunchKernelGGL((grouped_gemm_bf16_pp_kernel<UP, MOE_PP_BK, true>),
+                         dim3((unsigned)(p.n_cu / 2)), dim3(64 * pp::NW), 0, s, p);
+    }
     return hipGetLastError();
   }
 #endif
@@ -1140,13 +1307,13 @@ hipError_t launch_gemm(GemmArgs& p, int rows, int E, int ncols, unsigned long lo
 
 size_t ffn_workspace_bytes(int E, int rows, int d, int f) {
   (void)E; (void)rows; (void)d; (void)f;
-  return 0;
+  return pp_part_bytes(num_cus());
 }
 
 hipError_t launch_expert_up(const void* x, const int32_t* gather_idx, const int32_t* offsets,
                             int E, int rows, int d, int f, bool bf16, const void* W_gate,
-                            const void* W_up, void* a_out, void* ws, hipStream_t s) {
-  (void)ws;
+                            const void* W_up, void* a_out, void* ws, size_t ws_bytes,
+                            hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (!bf16) {
     const size_t n = (size_t)rows * f;
@@ -1164,15 +1331,16 @@ hipError_t launch_expert_up(const void* x, const int32_t* gather_idx, const int3
   p.B0 = static_cast<const bf16_t*>(W_gate);
   p.B1 = static_cast<const bf16_t*>(W_up);
   p.a_out = static_cast<bf16_t*>(a_out);
+  p.part = static_cast<float*>(ws);
   // gather entries are < rows (documented), so A spans at most rows x d
-  return launch_gemm<true, 2, UP_WN, UP_BNA>(p, rows, E, f, (unsigned long long)rows * d * 2, s);
+  return launch_gemm<true, 2, UP_WN, UP_BNA>(p, rows, E, f, (unsigned long long)rows * d * 2,
+                                             ws ? ws_bytes : 0, s);
 }
 
 hipError_t launch_expert_down(const void* a, const int32_t* offsets, int E, int rows, int f,
                               int d, bool bf16, const void* W_down, float* y_perm,
                               const int32_t* scatter_idx, const float* row_w, float* y, void* ws,
-                              hipStream_t s) {
-  (void)ws;
+                              size_t ws_bytes, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (!bf16) {
     const size_t n = (size_t)rows * d;
@@ -1192,7 +1360,9 @@ hipError_t launch_expert_down(const void* a, const int32_t* offsets, int E, int 
   p.scatter = scatter_idx;
   p.row_w = row_w;
   p.y = y;
-  return launch_gemm<false, 2, DN_WN, DN_BNA>(p, rows, E, d, (unsigned long long)rows * f * 2, s);
+  p.part = static_cast<float*>(ws);
+  return launch_gemm<false, 2, DN_WN, DN_BNA>(p, rows, E, d, (unsigned long long)rows * f * 2,
+                                              ws ? ws_bytes : 0, s);
 }
 
 }  // namespace moe

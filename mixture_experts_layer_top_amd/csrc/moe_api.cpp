@@ -96,8 +96,8 @@ static int check_ffn_common(const int32_t* offsets, int E, int rows, int d, int 
   if (!dtype_ok(dtype)) return MOE_ERR_UNSUPPORTED;
   if (!dims_ok(d) || !dims_ok(f)) return MOE_ERR_UNSUPPORTED;
   if (rows > 0 && !offsets) return MOE_ERR_INVALID;
-  const size_t need = moe::ffn_workspace_bytes(E, rows, d, f);
-  if (need > 0 && (!workspace || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  // the workspace is optional (it enables the GEMMs' tail split)
+  if (workspace && !aligned16(workspace)) return MOE_ERR_UNSUPPORTED;
   (void)ws_bytes;
   return MOE_OK;
 }
@@ -114,7 +114,7 @@ int moe_expert_up(const void* x, const int32_t* gather_idx, const int32_t* offse
     return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_expert_up(x, gather_idx, offsets, E, rows, d, f,
                                           dtype == MOE_BF16, W_gate, W_up, a_out, workspace,
-                                          stream));
+                                          ws_bytes, stream));
 }
 
 int moe_expert_down(const void* a, const int32_t* offsets, int E, int rows, int f, int d,
@@ -130,7 +130,8 @@ int moe_expert_down(const void* a, const int32_t* offsets, int E, int rows, int 
       (scatter_idx && !aligned16(scatter_idx)) || (row_w && !aligned16(row_w)))
     return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_expert_down(a, offsets, E, rows, f, d, dtype == MOE_BF16, W_down,
-                                            y_perm, scatter_idx, row_w, y, workspace, stream));
+                                            y_perm, scatter_idx, row_w, y, workspace, ws_bytes,
+                                            stream));
 }
 
 int moe_ffn_forward(const void* x, const int32_t* gather_idx, const int32_t* offsets, int E,
@@ -149,10 +150,10 @@ int moe_ffn_forward(const void* x, const int32_t* gather_idx, const int32_t* off
     return MOE_ERR_UNSUPPORTED;
   const bool bf = dtype == MOE_BF16;
   hipError_t e = moe::launch_expert_up(x, gather_idx, offsets, E, rows, d, f, bf, W_gate, W_up,
-                                       a_buf, workspace, stream);
+                                       a_buf, workspace, ws_bytes, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(moe::launch_expert_down(a_buf, offsets, E, rows, f, d, bf, W_down, y_perm,
-                                            scatter_idx, row_w, y, workspace, stream));
+                                            scatter_idx, row_w, y, workspace, ws_bytes, stream));
 }
 
 int moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w, int T, int d, int k,

@@ -59,11 +59,12 @@ hipError_t launch_permute(const int32_t* idx, const float* topk_w, const void* x
 size_t ffn_workspace_bytes(int E, int rows, int d, int f);
 hipError_t launch_expert_up(const void* x, const int32_t* gather_idx, const int32_t* offsets,
                             int E, int rows, int d, int f, bool bf16, const void* W_gate,
-                            const void* W_up, void* a_out, void* ws, hipStream_t s);
+                            const void* W_up, void* a_out, void* ws, size_t ws_bytes,
+                            hipStream_t s);
 hipError_t launch_expert_down(const void* a, const int32_t* offsets, int E, int rows, int f,
                               int d, bool bf16, const void* W_down, float* y_perm,
                               const int32_t* scatter_idx, const float* row_w, float* y, void* ws,
-                              hipStream_t s);
+                              size_t ws_bytes, hipStream_t s);
 
 hipError_t launch_combine(const float* y_perm, const int32_t* inv, const float* topk_w, int T,
                           int d, int k, const float* y_shared, const float* gate_logit,

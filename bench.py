@@ -73,13 +73,13 @@ def stage_bytes(cfg):
 
 def gemm_kernel_name(cfg, up):
     """The bf16 grouped-GEMM kernel the library launches for this layer: the
-    ping-pong kernel when K is a multiple of its 64-deep stages and the A
-    operand is below 4 GiB, else the general kernel."""
+    ping-pong kernel (main pass) when K is a multiple of its 64-deep stages
+    and the A operand is below 4 GiB, else the general kernel."""
     K = cfg.d if up else cfg.f
     a_bytes = cfg.T * cfg.k * K * 2
     u = "true" if up else "false"
     if K % 64 == 0 and a_bytes < (1 << 32):
-        return f"grouped_gemm_bf16_pp_kernel<{u}>"
+        return f"grouped_gemm_bf16_pp_kernel<{u}, 64, false>"
     return f"grouped_gemm_bf16_kernel<{u}, 2, 4, 256>"
 
 

@@ -246,6 +246,7 @@ __global__ __launch_bounds__(NWV * 64) void route_bf16_kernel(RouteArgs a, const
 
 // fp32 path (small layers): plain sequential FMA dot products, 64 tokens
 // per workgroup.
+template <int NV>
 __global__ __launch_bounds__(kThreads) void route_f32_kernel(RouteArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int kTok = 64;
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(RouteArgs a) {
   }
   __syncthreads();
   write_logits(ll, ls, a, t_base, kTok);
-  select_and_weigh<16>(ll, ls, a, t_base, kTok);
+  select_and_weigh<NV>(ll, ls, a, t_base, kTok);
 }
 
 template <int NB, int MB, int NWV>
@@ -315,14 +316,21 @@ hipError_t launch_route(const void* x, const void* W_r, const float* bias, int T
                         void* ws, hipStream_t s) {
   RouteArgs a{x, W_r, bias, T, d, E, k, renorm ? 1 : 0, idx, w, logits_out};
   if (!bf16) {
-    const size_t lds = (size_t)64 * (E + 1) * 4;
-    if (lds > 65536) {
-      hipError_t e = hipFuncSetAttribute((const void*)route_f32_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(route_f32_kernel, dim3(cdiv(T, 64)), dim3(kThreads), lds, s, a);
-    return hipGetLastError();
+    const size_t lds = (size_t)64 * (E + 1) * 4;  // <= 64 * 257 * 4 = 65792 bytes
+    auto launch = [&](auto kern) -> hipError_t {
+      if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL(kern, dim3(cdiv(T, 64)), dim3(kThreads), lds, s, a);
+      return hipGetLastError();
+    };
+    // logits per lane in the selection: E / 16 rounded up
+    if (E <= 16) return launch(route_f32_kernel<1>);
+    if (E <= 32) return launch(route_f32_kernel<2>);
+    if (E <= 64) return launch(route_f32_kernel<4>);
+    return launch(route_f32_kernel<16>);
   }
   const int Ep = cdiv(E, 16) * 16;
   bf16_t* Wt = static_cast<bf16_t*>(ws);

@@ -126,8 +126,10 @@ def make_layer(cfg: LayerConfig, seed: int = 0, device=None, T: Optional[int] = 
 
     Returns a dict of torch tensors on ``device`` (host when None):
     x[T,d], W_r[d,E], b[E] (float32, or None), W_gate/W_up[E,d,f], W_down[E,f,d],
-    and, for shared experts, Ws_gate/Ws_up[n_shared,d,f_s], Ws_down[n_shared,f_s,d],
-    w_s[d] (gated config only).  ``T`` overrides the token count (a
+    and, for shared experts, Ws_gate/Ws_up[d, n_shared*f_s] (shared expert s
+    in columns s*f_s .. (s+1)*f_s - 1: the experts side by side, as one FFN
+    of width n_shared*f_s), Ws_down[n_shared,f_s,d], w_s[d] (gated config
+    only).  ``T`` overrides the token count (a
     differently sized x, used for bounded samples; on the host back-end its
     rows are the first rows of the full draw).  ``parts``
     restricts the draw to the named tensors (e.g. ``ROUTER_PARTS``); every
@@ -160,8 +162,8 @@ def make_layer(cfg: LayerConfig, seed: int = 0, device=None, T: Optional[int] = 
             gs.append(_draw(cfg, "Ws_gate", _shared_tid(s, "gate"), seed, (d, fs), 1.0 / math.sqrt(d), device))
             us.append(_draw(cfg, "Ws_up", _shared_tid(s, "up"), seed, (d, fs), 1.0 / math.sqrt(d), device))
             ds.append(_draw(cfg, "Ws_down", _shared_tid(s, "down"), seed, (fs, d), 1.0 / math.sqrt(fs), device))
-        out["Ws_gate"] = torch.stack(gs)
-        out["Ws_up"] = torch.stack(us)
+        out["Ws_gate"] = torch.cat(gs, dim=1)
+        out["Ws_up"] = torch.cat(us, dim=1)
         out["Ws_down"] = torch.stack(ds)
     if want("w_s"):
         out["w_s"] = None

@@ -19,11 +19,12 @@ Paths: "fast" = fused gather + separate combine (the benchmarked default,
 deterministic); "atomic" = fused gather + atomic combine; "reference" =
 copy gather + separate combine.
 
-Shared experts run as one grouped FFN with E = n_shared whose rows all read
-x (row r of shared expert s reads token r - s*T).  With the separate combine
-their outputs go to a buffer and moe_combine adds them (the gated one scaled
-per token by sigmoid(x . w_s), its gate logit from moe_route with E = 1);
-with the atomic combine they are added into y first.
+Shared experts: the n_s experts are stored side by side (gate/up projections
+[d, n_s*f_s], down projections [n_s*f_s, d]), so their sum is one SwiGLU FFN
+of width n_s*f_s, run as a single-expert FFN over x (offsets {0, T}).  With
+the separate combine its output goes to a [T, d] buffer that moe_combine adds
+(scaled per token by sigmoid(x . w_s) in the gated variant, its gate logit
+from moe_route with E = 1); with the atomic combine it initialises y.
 """
 from __future__ import annotations
 
@@ -73,15 +74,13 @@ class MoeLayer:
         # shared experts
         self.ns = cfg.n_shared
         if self.ns:
-            fs = cfg.f_shared
-            self.s_a = e(self.ns * T, fs, dt=act)
-            ar = torch.arange(T, dtype=i32, device=dev)
-            self.s_rows = ar.repeat(self.ns).contiguous()
-            self.s_offsets = (torch.arange(self.ns + 1, dtype=i32, device=dev) * T).contiguous()
-            self.s_ws_bytes = L.moe_ffn_workspace_size(self.ns, self.ns * T, d, fs)
+            self.fs_all = self.ns * cfg.f_shared   # width of the side-by-side FFN
+            self.s_a = e(T, self.fs_all, dt=act)
+            self.s_offsets = torch.tensor([0, T], dtype=i32, device=dev)
+            self.s_ws_bytes = L.moe_ffn_workspace_size(1, T, d, self.fs_all)
             self.s_ws = e(max(self.s_ws_bytes, 16), dt=torch.uint8)
             if not (self.comb == "atomic" and not cfg.shared_gated):
-                self.ys_all = e(self.ns * T, d)   # per-expert shared outputs
+                self.ys = e(T, d)   # shared-expert output
             if cfg.shared_gated:
                 self.g_idx = e(T, 1, dt=i32)
                 self.g_w = e(T, 1)
@@ -105,36 +104,28 @@ class MoeLayer:
                       self.ws_perm, self.ws_perm_bytes, stream=stream)
 
     def shared(self, stream=None):
-        """Shared-expert outputs (and, with the atomic combine, y initialised
-        with them, or cleared when there are none)."""
+        """Shared-expert output (and, with the atomic combine, y initialised
+        with it, or cleared when there are none)."""
         c, t = self.cfg, self.t
         T, d = c.T, c.d
         if not self.ns:
             if self.comb == "atomic":
                 L.moe_combine(None, None, None, T, d, c.k, None, None, 0, self.y, stream=stream)
             return
-        fs = c.f_shared
-        rows = self.ns * T
+        fs = self.fs_all
         if c.shared_gated:
             # gate logit x . w_s (a one-column router)
             L.moe_route(t["x"], self.w_s_col, None, T, d, 1, 1, L.MOE_SOFTMAX_TOPK, self.dtype,
                         self.g_idx, self.g_w, self.g_logit, self.g_ws, self.g_ws_bytes,
                         stream=stream)
-        L.moe_expert_up(t["x"], self.s_rows, self.s_offsets, self.ns, rows, d, fs, self.dtype,
-                        t["Ws_gate"], t["Ws_up"], self.s_a, self.s_ws, self.s_ws_bytes,
-                        stream=stream)
-        if self.comb == "atomic" and not c.shared_gated:
-            # y = 0, then every shared expert adds into it
-            L.moe_combine(None, None, None, T, d, c.k, None, None, 0, self.y, stream=stream)
-            L.moe_expert_down(self.s_a, self.s_offsets, self.ns, rows, fs, d, self.dtype,
-                              t["Ws_down"], None, self.s_rows, None, self.y, self.s_ws,
-                              self.s_ws_bytes, stream=stream)
-            return
-        L.moe_expert_down(self.s_a, self.s_offsets, self.ns, rows, fs, d, self.dtype,
-                          t["Ws_down"], self.ys_all, None, None, None, self.s_ws,
-                          self.s_ws_bytes, stream=stream)
-        if self.comb == "atomic":  # gated: y = g * S(x); the routed part adds in later
-            L.moe_combine(None, None, None, T, d, c.k, self.ys_all, self.g_logit, 0, self.y,
+        L.moe_expert_up(t["x"], None, self.s_offsets, 1, T, d, fs, self.dtype, t["Ws_gate"],
+                        t["Ws_up"], self.s_a, self.s_ws, self.s_ws_bytes, stream=stream)
+        # ungated with the atomic combine: the output initialises y directly
+        out = self.y if (self.comb == "atomic" and not c.shared_gated) else self.ys
+        L.moe_expert_down(self.s_a, self.s_offsets, 1, T, fs, d, self.dtype, t["Ws_down"],
+                          out, None, None, None, self.s_ws, self.s_ws_bytes, stream=stream)
+        if self.comb == "atomic" and c.shared_gated:  # y = g * S(x); the routed part adds in later
+            L.moe_combine(None, None, None, T, d, c.k, self.ys, self.g_logit, 0, self.y,
                           stream=stream)
 
     def expert_up(self, stream=None):
@@ -164,13 +155,10 @@ class MoeLayer:
             return
         c = self.cfg
         T = c.T
-        ys = self.ys_all[:T] if self.ns else None
+        ys = self.ys if self.ns else None
         gl = self.g_logit if (self.ns and c.shared_gated) else None
         L.moe_combine(self.y_perm, self.inv, self.w, T, c.d, c.k, ys, gl, 0, self.y,
                       stream=stream)
-        for s_ in range(1, self.ns):  # further ungated shared experts, in expert order
-            L.moe_combine(None, None, None, T, c.d, c.k, self.ys_all[s_ * T:(s_ + 1) * T],
-                          None, 1, self.y, stream=stream)
 
     STAGES = ("route", "permute", "shared", "expert_up", "expert_down", "combine")
 

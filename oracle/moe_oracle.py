@@ -181,11 +181,15 @@ def combine(Y: np.ndarray, inv: np.ndarray, w: np.ndarray) -> np.ndarray:
 
 
 def shared_output(x, Ws_gate, Ws_up, Ws_down, w_s=None) -> np.ndarray:
-    """sum_s F_s(x), scaled per token by sigmoid(x . w_s) when w_s is given."""
+    """sum_s F_s(x), scaled per token by sigmoid(x . w_s) when w_s is given.
+    Ws_down is [n_s, f_s, d]; shared expert s's gate/up projections are
+    columns s*f_s .. (s+1)*f_s - 1 of Ws_gate/Ws_up [d, n_s*f_s]."""
     x = np.asarray(x, np.float64)
-    ys = np.zeros((x.shape[0], Ws_down.shape[2]), np.float64)
-    for s in range(Ws_gate.shape[0]):
-        ys += swiglu_ffn(x, Ws_gate[s], Ws_up[s], Ws_down[s])
+    n_s, f_s, d = Ws_down.shape
+    ys = np.zeros((x.shape[0], d), np.float64)
+    for s in range(n_s):
+        cols = slice(s * f_s, (s + 1) * f_s)
+        ys += swiglu_ffn(x, Ws_gate[:, cols], Ws_up[:, cols], Ws_down[s])
     if w_s is not None:
         g = sigmoid(x @ np.asarray(w_s, np.float64))
         ys = g[:, None] * ys
@@ -303,9 +307,10 @@ def brute_force(layer: dict, k: int, renorm: bool) -> dict:
         y += G[:, e:e + 1] * (a @ layer["W_down"][e])
     if layer.get("Ws_gate") is not None:
         ys = np.zeros_like(y)
-        for s in range(layer["Ws_gate"].shape[0]):
-            h = x @ layer["Ws_gate"][s]
-            u = x @ layer["Ws_up"][s]
+        n_s, f_s, _ = layer["Ws_down"].shape
+        for s in range(n_s):
+            h = x @ layer["Ws_gate"][:, s * f_s:(s + 1) * f_s]
+            u = x @ layer["Ws_up"][:, s * f_s:(s + 1) * f_s]
             ys += (h * (1.0 / (1.0 + np.exp(-h))) * u) @ layer["Ws_down"][s]
         if layer.get("w_s") is not None:
             g = 1.0 / (1.0 + np.exp(-(x @ layer["w_s"])))

@@ -97,6 +97,7 @@ struct GemmArgs {
 
 struct TileInfo {
   int e, row0, row_end, n_t, m_t, ks;
+  int nb;  // ping-pong kernel: 16-row blocks in the tile (<= BM / 16)
   bool ok;
 };
 
@@ -857,8 +858,19 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   ti.n_t = local / tmt;  // M fastest inside an (expert, N panel)
   ti.m_t = local - ti.n_t * tmt;
   ti.ks = 0;
-  ti.row0 = toff + ti.m_t * BM;
-  ti.row_end = min(ti.row0 + BM, p.offsets[ti.e + 1]);
+  // Balanced M tiles: the expert's c rows form nbe = ceil(c / 16) blocks of
+  // 16, dealt to its tmt = ceil(c / BM) tiles as evenly as possible (tile m
+  // takes blocks [m nbe / tmt, (m + 1) nbe / tmt), between 1 and BM / 16 of
+  // them).  Against full tiles plus one ragged last tile, this removes all
+  // padding but the last block's, and the tiles of an (expert, N panel),
+  // which run side by side and share the panel, take equal time.
+  const int c_e = p.offsets[ti.e + 1] - toff;
+  const int nbe = cdiv(c_e, 16);
+  const int b0 = (int)((long long)ti.m_t * nbe / tmt);
+  const int b1 = (int)((long long)(ti.m_t + 1) * nbe / tmt);
+  ti.nb = b1 - b0;
+  ti.row0 = toff + 16 * b0;
+  ti.row_end = min(toff + 16 * b1, toff + c_e);
   ti.ok = true;
   w.ok = true;
   return w;
@@ -882,11 +894,18 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
   const int t_row0 = __builtin_amdgcn_readfirstlane(ti0.row0);
   const int t_row_end = __builtin_amdgcn_readfirstlane(ti0.row_end);
   const int t_n = __builtin_amdgcn_readfirstlane(ti0.n_t);
+  // the tile's nb 16-row blocks: the first ceil(nb / 2) go to group X, the
+  // rest to group Y; each wave computes only its group's blocks
+  const int t_nb = __builtin_amdgcn_readfirstlane(ti0.nb);
+  const int t_bx = (t_nb + 1) >> 1;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool X = wave < 4;       // leading group: rows 0-127, issues the A loads
+  const bool X = wave < 4;       // leading group: LDS rows 0-127, issues the A loads
   const int wg = wave & 3;       // wave inside its group
+  const int my_nb = X ? t_bx : t_nb - t_bx;    // blocks this wave computes (0..MI)
+  const int grow0 = X ? 0 : 16 * t_bx;         // the group's first row inside the tile
+  const int grow_end = min(t_row_end, t_row0 + grow0 + 16 * my_nb);  // its row bound
   const int K = p.K, N = p.N;
   const int n0 = t_n * (UP ? 128 : 256);
   const uint32_t lds0 = lds_addr_of(lds);
@@ -907,10 +926,15 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
   if (X) {
 #pragma unroll
     for (int q = 0; q < LD; ++q) {
-      const int row = (wg * LD + q) * C::RPL + lane / C::CPR;
+      const int row = (wg * LD + q) * C::RPL + lane / C::CPR;  // LDS row
       const int chunk = (lane % C::CPR) ^ a_swz16<PBK>(row);
-      int r = t_row0 + row;
-      if (r >= t_row_end) r = t_row0;  // padding rows read a valid row; results are discarded
+      // LDS rows 0-127 hold group X's blocks, 128-255 group Y's
+      const int j = row & 127;
+      const int gnb = row < 128 ? t_bx : t_nb - t_bx;
+      int r = t_row0 + (row < 128 ? 0 : 16 * t_bx) + j;
+      // rows past the group's blocks or the expert's rows read a valid row;
+      // their results are never stored
+      if (j >= 16 * gnb || r >= t_row_end) r = t_row0;
       const int src_row = p.gather ? p.gather[r] : r;
       ld_off[q] = ((uint32_t)src_row * (uint32_t)K + (uint32_t)(k_begin + chunk * 8)) * 2u;
     }
@@ -981,7 +1005,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
       const char* Ak = As + (ks ? a_rd1 : a_rd0);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
-        fa[ks][mi] = *reinterpret_cast<const bf16x8*>(Ak + mi * 16 * PBK * 2);
+        if (mi < my_nb) fa[ks][mi] = *reinterpret_cast<const bf16x8*>(Ak + mi * 16 * PBK * 2);
       // the loads after the reads of each K step (half of them each when
       // there are two)
       if (ld_kt < nk) {
@@ -996,14 +1020,18 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
   };
   auto compute = [&]() {
     if (MOE_PP_PRIO) __builtin_amdgcn_s_setprio(MOE_PP_PRIO);
+    // blocks in (16-row block, K step) order: one test per block of a
+    // partial tile
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int mi = 0; mi < MI; ++mi) {
+      if (mi >= my_nb) break;
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int nj = 0; nj < NJ; ++nj)
-          acc[mi][nj] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ks][mi], fb[ks][nj], acc[mi][nj], 0, 0, 0);
+          acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ks][mi], fb[ks][nj],
+                                                               acc[mi][nj], 0, 0, 0);
+    }
     if (MOE_PP_PRIO) __builtin_amdgcn_s_setprio(0);
   };
 
@@ -1087,6 +1115,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
     const int ocol0 = n0 + wg * OC;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
+      if (mi >= my_nb) break;
 #pragma unroll
       for (int nj = 0; nj < 2; ++nj)
 #pragma unroll
@@ -1095,10 +1124,10 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
               f32_to_bf16(silu(acc[mi][nj][i]) * acc[mi][nj + 2][i]);
       // 16 rows x 4 chunks of 16 B: one per lane
       const int r = lane >> 2, c = lane & 3;
-      const int row = t_row0 + wrow0 + mi * 16 + r;
+      const int row = t_row0 + grow0 + mi * 16 + r;
       const int col = ocol0 + c * 8;
       const u32x4 v = *reinterpret_cast<const u32x4*>(sb + r * SS + c * 8);
-      if (row < t_row_end && col < N)
+      if (row < grow_end && col < N)
         *reinterpret_cast<u32x4*>(p.a_out + (size_t)row * N + col) = v;
     }
   } else {
@@ -1108,6 +1137,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
       float* sf = reinterpret_cast<float*>(lds + wave * 16 * SS * 4);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
+        if (mi >= my_nb) break;
 #pragma unroll
         for (int nj = 0; nj < NJ; ++nj)
 #pragma unroll
@@ -1116,10 +1146,10 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
         for (int q = 0; q < 4; ++q) {  // 16 rows x 16 chunks of 16 B
           const int idx = q * 64 + lane;
           const int r = idx >> 4, c = idx & 15;
-          const int row = t_row0 + wrow0 + mi * 16 + r;
+          const int row = t_row0 + grow0 + mi * 16 + r;
           const int col = n0 + (c >> 3) * 128 + wg * 32 + (c & 7) * 4;
           const f32x4 v = *reinterpret_cast<const f32x4*>(sf + r * SS + c * 4);
-          if (row < t_row_end && col < N)
+          if (row < grow_end && col < N)
             *reinterpret_cast<f32x4*>(p.y_perm + (size_t)row * N + col) = v;
         }
       }
@@ -1129,8 +1159,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
       for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = t_row0 + wrow0 + mi * 16 + row_l + i;
-          if (row >= t_row_end) continue;
+          const int row = t_row0 + grow0 + mi * 16 + row_l + i;
+          if (row >= grow_end) continue;
           const int tgt = p.scatter ? p.scatter[row] : row;
           float* yrow = p.y + (size_t)tgt * N;
           const float wgt = p.row_w ? p.row_w[row] : 1.f;

@@ -9,15 +9,18 @@
 // ascending inside an expert.  No atomic decides an order, so the result is
 // deterministic:
 //   1. hist:  each block of 256 tokens counts its (t, j) pairs per expert
-//             in LDS, writes its block histogram, and adds it into the
-//             global counts (integer adds commute);
-//   2. scan:  one workgroup turns counts into offsets and the block
-//             histograms into each block's first row per expert;
+//             in LDS and writes its block histogram;
+//   2. scan:  the per-expert totals become the offsets, and the block
+//             histograms each block's first row per expert;
 //   3. rank:  each block walks its pairs in (t, j) order, 256 at a time;
 //             inside a wave, lanes with the same expert are found with a
 //             ballot loop and ranked by popcount of lower lanes; across
 //             waves, by a prefix over per-wave counts in LDS;
 //   4. gather (optional): x_perm[r] = x[perm_token[r]], 16-byte vectors.
+// When the block histograms are small (blocks x experts <= 32768), every
+// rank block does the scan itself (its own column prefixes, and the
+// totals): two launches, hist and scan+rank.  Otherwise hist also adds into
+// the global counts (integer adds commute) and one workgroup scans.
 #include "moe_internal.h"
 
 namespace moe {
@@ -44,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restric
   for (int e = threadIdx.x; e < E; e += kThreads) {
     const int c = cnt[e];
     blk_cnt[(size_t)blockIdx.x * E + e] = c;
-    if (c) atomicAdd(&counts[e], c);
+    if (counts && c) atomicAdd(&counts[e], c);
   }
 }
 
@@ -87,22 +90,78 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   }
 }
 
+// This block's first row per expert (sbase, LDS) from the block histograms
+// blk_cnt [nb, E]: offsets (exclusive scan of the per-expert totals) plus
+// the counts of the earlier blocks.  Block 0 also writes counts and offsets.
+__device__ __forceinline__ void block_bases(const int32_t* __restrict__ blk_cnt, int nb, int E,
+                                            int32_t* __restrict__ counts,
+                                            int32_t* __restrict__ offsets, int* sbase) {
+  __shared__ int psum[kThreads], ppre[kThreads], wsum[kThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int P = max(1, kThreads / E);  // parts per expert column (E <= 256)
+  const int e = tid % E, part = tid / E;
+  int s_all = 0, s_pre = 0;
+  if (part < P) {
+    const int b_lo = (int)((long long)nb * part / P), b_hi = (int)((long long)nb * (part + 1) / P);
+    for (int b = b_lo; b < b_hi; ++b) {
+      const int c = blk_cnt[(size_t)b * E + e];
+      s_all += c;
+      if (b < (int)blockIdx.x) s_pre += c;
+    }
+  }
+  psum[tid] = s_all;
+  ppre[tid] = s_pre;
+  __syncthreads();
+  int tot = 0, pre = 0;
+  if (tid < E) {
+    for (int q = 0; q < P; ++q) {
+      tot += psum[q * E + tid];
+      pre += ppre[q * E + tid];
+    }
+  }
+  // exclusive scan of the totals over experts: wave prefix, then wave sums
+  int incl = tot;
+#pragma unroll
+  for (int sft = 1; sft < 64; sft <<= 1) {
+    const int v = __shfl_up(incl, sft);
+    if (lane >= sft) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  for (int w2 = 0; w2 < wave; ++w2) incl += wsum[w2];
+  const int excl = incl - tot;
+  if (tid < E) {
+    sbase[tid] = excl + pre;
+    if (blockIdx.x == 0) {
+      counts[tid] = tot;
+      offsets[tid] = excl;
+      if (tid == E - 1) offsets[E] = incl;
+    }
+  }
+}
+
+// FUSED: derive the block bases here (block_bases) instead of reading them
+// from the scan kernel's blk_base
+template <bool FUSED>
 __global__ __launch_bounds__(kThreads) void rank_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ topk_w, int T, int E, int k,
     const int32_t* __restrict__ blk_base, int32_t* __restrict__ perm_token,
-    int32_t* __restrict__ inv, float* __restrict__ perm_w) {
+    int32_t* __restrict__ inv, float* __restrict__ perm_w, const int32_t* __restrict__ blk_cnt,
+    int nb, int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
   __shared__ int run[256];        // rows already taken by earlier chunks, per expert
   __shared__ int wcnt[4][256];    // per-wave counts of the current chunk
+  __shared__ int sbase[256];      // FUSED: this block's first row per expert
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < E; e += kThreads) {
     run[e] = 0;
     wcnt[0][e] = wcnt[1][e] = wcnt[2][e] = wcnt[3][e] = 0;
   }
+  if (FUSED) block_bases(blk_cnt, nb, E, counts, offsets, sbase);
   __syncthreads();
   const int t0 = blockIdx.x * kPT;
   const int npairs = (min(t0 + kPT, T) - t0) * k;
   const size_t pbase = (size_t)t0 * k;
-  const int32_t* base = blk_base + (size_t)blockIdx.x * E;
+  const int* base = FUSED ? sbase : blk_base + (size_t)blockIdx.x * E;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
   for (int c0 = 0; c0 < npairs; c0 += kThreads) {
@@ -171,14 +230,25 @@ hipError_t launch_permute(const int32_t* idx, const float* topk_w, const void* x
   int32_t* blk_cnt = static_cast<int32_t*>(ws);
   int32_t* blk_base = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
                                                  align_up((size_t)nb * E * sizeof(int32_t), 256));
-  hipLaunchKernelGGL(zero_i32_kernel, dim3(cdiv(E, 256)), dim3(256), 0, s, counts, E);
-  if (nb > 0)
-    hipLaunchKernelGGL(hist_kernel, dim3(nb), dim3(kThreads), 0, s, idx, T, E, k, blk_cnt, counts);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, counts, E, nb, blk_cnt, blk_base,
-                     offsets);
-  if (nb > 0)
-    hipLaunchKernelGGL(rank_kernel, dim3(nb), dim3(kThreads), 0, s, idx, topk_w, T, E, k,
-                       blk_base, perm_token, inv, perm_w);
+  if (nb > 0 && (long long)nb * E <= 32768) {
+    // two launches: block histograms, then scan + rank in every block
+    hipLaunchKernelGGL(hist_kernel, dim3(nb), dim3(kThreads), 0, s, idx, T, E, k, blk_cnt,
+                       (int32_t*)nullptr);
+    hipLaunchKernelGGL(rank_kernel<true>, dim3(nb), dim3(kThreads), 0, s, idx, topk_w, T, E, k,
+                       (const int32_t*)nullptr, perm_token, inv, perm_w, blk_cnt, nb, counts,
+                       offsets);
+  } else {
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(cdiv(E, 256)), dim3(256), 0, s, counts, E);
+    if (nb > 0)
+      hipLaunchKernelGGL(hist_kernel, dim3(nb), dim3(kThreads), 0, s, idx, T, E, k, blk_cnt,
+                         counts);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, counts, E, nb, blk_cnt, blk_base,
+                       offsets);
+    if (nb > 0)
+      hipLaunchKernelGGL(rank_kernel<false>, dim3(nb), dim3(kThreads), 0, s, idx, topk_w, T, E,
+                         k, blk_base, perm_token, inv, perm_w, (const int32_t*)nullptr, 0,
+                         (int32_t*)nullptr, (int32_t*)nullptr);
+  }
   const int R = T * k;
   if (x_perm && R > 0) {
     const int vecs = d * (bf16 ? 2 : 4) / 16;

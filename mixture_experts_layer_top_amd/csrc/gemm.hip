@@ -747,9 +747,9 @@ __device__ __forceinline__ void wait_groups(int n) {
 }  // namespace pp
 
 // Tail split.  With N_t output tiles on C compute units the last round
-// holds N_t mod C tiles; when that is at most C / 2 (and N_t <= 8 C), each
-// of those tail tiles is split along K into S = min(C / tail, stages) parts that run
-// side by side, their fp32 partial accumulators go to p.part, and a second
+// holds N_t mod C tiles; when that is at most C / 2 (and N_t <= 64 C), each
+// of those tail tiles is split along K into S = min(C / tail, stages) parts
+// that run side by side, their fp32 partial accumulators go to p.part, and a second
 // launch (fixup) adds the parts in part order and runs the tile's normal
 // epilogue.  Every workgroup derives N_t, the split and its own work item
 // from the device offsets, so the host never reads the routing.
@@ -757,6 +757,9 @@ __device__ __forceinline__ void wait_groups(int n) {
 //     multiple of 8 and walked XCD-aware as usual) -> full tile; b >= G ->
 //     split item j = b - G: tail tile F + j / S, part j % S;
 //   fixup pass, block b < tail: tail tile F + b.
+#ifndef MOE_PP_SPLIT_MAX_ROUNDS
+#define MOE_PP_SPLIT_MAX_ROUNDS 64
+#endif
 struct Work {
   int tile, ks, S, item;  // item: index of the split item (-1: a whole tile)
   int k_begin, k_end;
@@ -795,10 +798,11 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   int tail = n_tiles % C;
   const int nk_all = p.K / pbk;
   int S = 1, kps = p.K;
-  // split only where the last round is a large share of the launch (at
-  // most 8 rounds) and mostly idle (at most half full); otherwise the fixup
-  // pass costs more than the idle compute units
-  if (p.part != nullptr && tail > 0 && 2 * tail <= C && n_tiles <= 8 * C && nk_all >= 2) {
+  // split only where the last round is mostly idle (at most half full) and
+  // the launch has at most MOE_PP_SPLIT_MAX_ROUNDS rounds; otherwise the
+  // fixup pass costs more than the idle compute units
+  if (p.part != nullptr && tail > 0 && 2 * tail <= C &&
+      n_tiles <= MOE_PP_SPLIT_MAX_ROUNDS * C && nk_all >= 2) {
     S = min(C / tail, nk_all);
     kps = cdiv(nk_all, S) * pbk;
     S = cdiv(p.K, kps);  // parts that are not empty

@@ -98,7 +98,10 @@ size_t moe_permute_workspace_size(int T, int E, int k);
  *   x_perm[r, :] = x[perm_token[r], :] when x_perm is not NULL (NULL: the
  *   gather is left to moe_expert_up, which reads x through perm_token).
  * Arguments: topk_idx [T, k] int32 with values in [0, E) (values outside are
- *   undefined behaviour); topk_w [T, k] fp32 or NULL (then perm_w must be
+ *   undefined behaviour) and the k experts of a token distinct, as
+ *   moe_route produces them (an expert repeated in one token's list is
+ *   counted once: both slots get the same row, offsets[E] < T*k, and every
+ *   row below offsets[E] is still written); topk_w [T, k] fp32 or NULL (then perm_w must be
  *   NULL); x [T, d] (dtype) required only with x_perm; counts [E],
  *   offsets [E+1], perm_token [T*k], inv [T, k] int32 out; perm_w [T*k]
  *   fp32 out or NULL; x_perm [T*k, d] (dtype) out or NULL.

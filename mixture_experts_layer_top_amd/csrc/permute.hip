@@ -12,10 +12,8 @@
 //             in LDS and writes its block histogram;
 //   2. scan:  the per-expert totals become the offsets, and the block
 //             histograms each block's first row per expert;
-//   3. rank:  each block walks its pairs in (t, j) order, 256 at a time;
-//             inside a wave, lanes with the same expert are found with a
-//             ballot loop and ranked by popcount of lower lanes; across
-//             waves, by a prefix over per-wave counts in LDS;
+//   3. rank:  each block marks its tokens in per-expert bit columns (LDS
+//             OR) and ranks each pair by popcounts of the bits below it;
 //   4. gather (optional): x_perm[r] = x[perm_token[r]], 16-byte vectors.
 // When the block histograms are small (blocks x experts <= 32768), every
 // rank block does the scan itself (its own column prefixes, and the
@@ -34,18 +32,28 @@ __global__ void zero_i32_kernel(int32_t* p, int n) {
   if (i < n) p[i] = 0;
 }
 
+// Block histogram over kPT = 256 tokens (thread i = token t0 + i): the same
+// per-expert token bit columns as the rank kernel, so counts and ranks
+// agree by construction (an expert repeated in one token's list counts
+// once there and in the ranks).
 __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restrict__ idx, int T,
                                                         int E, int k, int32_t* __restrict__ blk_cnt,
                                                         int32_t* __restrict__ counts) {
-  __shared__ int cnt[256];
-  for (int e = threadIdx.x; e < E; e += kThreads) cnt[e] = 0;
+  constexpr int NWD = kPT / 64;
+  __shared__ unsigned long long bits[256 * NWD];  // [E][NWD]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < E * NWD; i += kThreads) bits[i] = 0ull;
   __syncthreads();
-  const size_t p0 = (size_t)blockIdx.x * kPT * k;
-  const size_t p1 = min((size_t)(blockIdx.x + 1) * kPT, (size_t)T) * k;
-  for (size_t p = p0 + threadIdx.x; p < p1; p += kThreads) atomicAdd(&cnt[idx[p]], 1);
+  const int t = blockIdx.x * kPT + tid;
+  if (t < T) {
+    const int32_t* it = idx + (size_t)t * k;
+    for (int j = 0; j < k; ++j) atomicOr(&bits[it[j] * NWD + wave], 1ull << lane);
+  }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    const int c = cnt[e];
+  for (int e = tid; e < E; e += kThreads) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < NWD; ++w) c += __popcll(bits[e * NWD + w]);
     blk_cnt[(size_t)blockIdx.x * E + e] = c;
     if (counts && c) atomicAdd(&counts[e], c);
   }
@@ -140,61 +148,55 @@ __device__ __forceinline__ void block_bases(const int32_t* __restrict__ blk_cnt,
   }
 }
 
+// Stable ranks of one block of kPT = 256 tokens (thread i = token t0 + i).
+// Each token sets its bit in the bit column of every expert it picked
+// (LDS OR: the result does not depend on the order of the ORs); a pair's
+// row is then base[e] + (rows of e among the block's earlier 64-token
+// words) + (bits of e below the token in its own word).  No two pairs of
+// one token share an expert, so token order is a total order per expert.
 // FUSED: derive the block bases here (block_bases) instead of reading them
-// from the scan kernel's blk_base
+// from the scan kernel's blk_base.
 template <bool FUSED>
 __global__ __launch_bounds__(kThreads) void rank_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ topk_w, int T, int E, int k,
     const int32_t* __restrict__ blk_base, int32_t* __restrict__ perm_token,
     int32_t* __restrict__ inv, float* __restrict__ perm_w, const int32_t* __restrict__ blk_cnt,
     int nb, int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-  __shared__ int run[256];        // rows already taken by earlier chunks, per expert
-  __shared__ int wcnt[4][256];    // per-wave counts of the current chunk
-  __shared__ int sbase[256];      // FUSED: this block's first row per expert
+  static_assert(kPT == kThreads && kPT % 64 == 0, "one token per thread");
+  constexpr int NWD = kPT / 64;                    // 64-token words per expert column
+  __shared__ unsigned long long bits[256 * NWD];   // [E][NWD]
+  __shared__ int wbase[256 * NWD];                 // [E][NWD]
+  __shared__ int sbase[256];                       // FUSED: this block's first row per expert
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < E; e += kThreads) {
-    run[e] = 0;
-    wcnt[0][e] = wcnt[1][e] = wcnt[2][e] = wcnt[3][e] = 0;
-  }
+  for (int i = tid; i < E * NWD; i += kThreads) bits[i] = 0ull;
   if (FUSED) block_bases(blk_cnt, nb, E, counts, offsets, sbase);
   __syncthreads();
-  const int t0 = blockIdx.x * kPT;
-  const int npairs = (min(t0 + kPT, T) - t0) * k;
-  const size_t pbase = (size_t)t0 * k;
+  const int t = blockIdx.x * kPT + tid;
+  const bool valid = t < T;
+  const int32_t* it = idx + (size_t)(valid ? t : 0) * k;
+  const unsigned long long me = 1ull << lane;
+  if (valid)
+    for (int j = 0; j < k; ++j) atomicOr(&bits[it[j] * NWD + wave], me);
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < NWD; ++w) {
+      wbase[e * NWD + w] = run;
+      run += __popcll(bits[e * NWD + w]);
+    }
+  }
+  __syncthreads();
+  if (!valid) return;
   const int* base = FUSED ? sbase : blk_base + (size_t)blockIdx.x * E;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-
-  for (int c0 = 0; c0 < npairs; c0 += kThreads) {
-    const int p = c0 + tid;
-    const bool valid = p < npairs;
-    const int e = valid ? idx[pbase + p] : -1;
-    // lanes holding the same expert
-    uint64_t todo = __ballot(valid);
-    uint64_t mine = 0;
-    while (todo) {
-      const int leader = __ffsll((unsigned long long)todo) - 1;
-      const int ve = __shfl(e, leader);
-      const uint64_t m = __ballot(valid && e == ve);
-      if (valid && e == ve) mine = m;
-      todo &= ~m;
-    }
-    const int rank_w = __popcll(mine & lt_mask);
-    if (valid && rank_w == 0) wcnt[wave][e] = __popcll(mine);
-    __syncthreads();
-    if (valid) {
-      int r = base[e] + run[e] + rank_w;
-      for (int w2 = 0; w2 < wave; ++w2) r += wcnt[w2][e];
-      const size_t pg = pbase + p;
-      perm_token[r] = (int)(pg / k);
-      inv[pg] = r;
-      if (perm_w) perm_w[r] = topk_w[pg];
-    }
-    __syncthreads();
-    for (int e2 = tid; e2 < E; e2 += kThreads) {
-      run[e2] += wcnt[0][e2] + wcnt[1][e2] + wcnt[2][e2] + wcnt[3][e2];
-      wcnt[0][e2] = wcnt[1][e2] = wcnt[2][e2] = wcnt[3][e2] = 0;
-    }
-    __syncthreads();
+  const unsigned long long below = me - 1ull;
+  for (int j = 0; j < k; ++j) {
+    const int e = it[j];
+    const int r = base[e] + wbase[e * NWD + wave] + __popcll(bits[e * NWD + wave] & below);
+    const size_t pg = (size_t)t * k + j;
+    perm_token[r] = t;
+    inv[pg] = r;
+    if (perm_w) perm_w[r] = topk_w[pg];
   }
 }
 

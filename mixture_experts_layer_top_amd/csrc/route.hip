@@ -125,21 +125,23 @@ __device__ __forceinline__ void write_logits(const float* ll, int lstride, const
   }
 }
 
-// W_t[e, k] = W_r[k, e] for e < E, 0 for E <= e < Ep.  One block per 64 rows of W_r.
+// W_t[e, k] = W_r[k, e] for e < E, 0 for E <= e < Ep (d % 8 == 0).  Thread
+// (kc, e) gathers rows 8 kc .. 8 kc + 7 of column e and writes them as one
+// 16-byte vector; consecutive threads take consecutive experts, so each row
+// read of a wave is contiguous.
 __global__ __launch_bounds__(kThreads) void transpose_router_kernel(const bf16_t* __restrict__ W,
                                                                    int d, int E, int Ep,
                                                                    bf16_t* __restrict__ Wt) {
-  __shared__ bf16_t tile[64][257];
-  const int k0 = blockIdx.x * 64;
-  for (int i = threadIdx.x; i < 64 * E; i += kThreads) {
-    const int r = i / E, e = i - r * E;
-    tile[r][e] = (k0 + r < d) ? W[(size_t)(k0 + r) * E + e] : (bf16_t)0;
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (d / 8) * Ep) return;
+  const int e = i % Ep, kc = i / Ep;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (e < E) {
+    const bf16_t* src = W + (size_t)kc * 8 * E + e;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) v[r >> 1] |= (uint32_t)src[(size_t)r * E] << (16 * (r & 1));
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < Ep * 64; i += kThreads) {
-    const int e = i / 64, r = i - e * 64;
-    if (k0 + r < d) Wt[(size_t)e * d + k0 + r] = (e < E) ? tile[r][e] : (bf16_t)0;
-  }
+  *reinterpret_cast<u32x4*>(Wt + (size_t)e * d + (size_t)kc * 8) = v;
 }
 
 // NB = ceil(E / 16) column blocks of 16 experts; MB = token blocks of 16 per
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(NWV * 64) void route_bf16_kernel(RouteArgs a, const
 
   // K in chunks of ST steps of 32: all loads of a chunk are issued before its
   // MFMAs, so each wave keeps ST (MB + NB) 1 KiB loads in flight
-  constexpr int ST = (MB + NB) <= 2 ? 8 : (MB + NB) <= 4 ? 4 : 2;
+  constexpr int ST = (MB + NB) <= 2 ? 8 : (MB + NB) <= 8 ? 4 : 2;
   const bf16x8 zero8 = {};
   for (int k0 = kb; k0 < ke; k0 += 32 * ST) {
     bf16x8 av[ST][MB], bv[ST][NB];
@@ -334,8 +336,8 @@ hipError_t launch_route(const void* x, const void* W_r, const float* bias, int T
   }
   const int Ep = cdiv(E, 16) * 16;
   bf16_t* Wt = static_cast<bf16_t*>(ws);
-  hipLaunchKernelGGL(transpose_router_kernel, dim3(cdiv(d, 64)), dim3(kThreads), 0, s,
-                     static_cast<const bf16_t*>(W_r), d, E, Ep, Wt);
+  hipLaunchKernelGGL(transpose_router_kernel, dim3(cdiv((d / 8) * Ep, kThreads)), dim3(kThreads),
+                     0, s, static_cast<const bf16_t*>(W_r), d, E, Ep, Wt);
   switch (Ep / 16) {
     case 1: return launch_nb<1>(a, Wt, s);
     case 2: return launch_nb<2>(a, Wt, s);

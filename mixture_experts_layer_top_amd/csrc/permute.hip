@@ -26,6 +26,14 @@ namespace {
 
 constexpr int kPT = 256;       // tokens per block in hist / rank
 constexpr int kThreads = 256;
+constexpr int kKR = 8;         // picks of a token held in registers
+
+// The first min(k, kKR) picks of one token, all loads issued before any is
+// used (addresses clamped to the token's row, so no predicates).
+__device__ __forceinline__ void load_picks(const int32_t* __restrict__ it, int k, int (&er)[kKR]) {
+#pragma unroll
+  for (int j = 0; j < kKR; ++j) er[j] = it[min(j, k - 1)];
+}
 
 __global__ void zero_i32_kernel(int32_t* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -47,7 +55,12 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restric
   const int t = blockIdx.x * kPT + tid;
   if (t < T) {
     const int32_t* it = idx + (size_t)t * k;
-    for (int j = 0; j < k; ++j) atomicOr(&bits[it[j] * NWD + wave], 1ull << lane);
+    int er[kKR];
+    load_picks(it, k, er);
+#pragma unroll
+    for (int j = 0; j < kKR; ++j)
+      if (j < k) atomicOr(&bits[er[j] * NWD + wave], 1ull << lane);
+    for (int j = kKR; j < k; ++j) atomicOr(&bits[it[j] * NWD + wave], 1ull << lane);
   }
   __syncthreads();
   for (int e = tid; e < E; e += kThreads) {
@@ -111,10 +124,18 @@ __device__ __forceinline__ void block_bases(const int32_t* __restrict__ blk_cnt,
   int s_all = 0, s_pre = 0;
   if (part < P) {
     const int b_lo = (int)((long long)nb * part / P), b_hi = (int)((long long)nb * (part + 1) / P);
-    for (int b = b_lo; b < b_hi; ++b) {
-      const int c = blk_cnt[(size_t)b * E + e];
-      s_all += c;
-      if (b < (int)blockIdx.x) s_pre += c;
+    // 8 loads in flight at a time (clamped addresses; entries past b_hi count 0)
+    for (int b0 = b_lo; b0 < b_hi; b0 += 8) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = blk_cnt[(size_t)min(b0 + u, b_hi - 1) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int b = b0 + u;
+        const int v = b < b_hi ? c[u] : 0;
+        s_all += v;
+        if (b < (int)blockIdx.x) s_pre += v;
+      }
     }
   }
   psum[tid] = s_all;
@@ -175,8 +196,14 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
   const bool valid = t < T;
   const int32_t* it = idx + (size_t)(valid ? t : 0) * k;
   const unsigned long long me = 1ull << lane;
-  if (valid)
-    for (int j = 0; j < k; ++j) atomicOr(&bits[it[j] * NWD + wave], me);
+  int er[kKR];
+  if (valid) {
+    load_picks(it, k, er);
+#pragma unroll
+    for (int j = 0; j < kKR; ++j)
+      if (j < k) atomicOr(&bits[er[j] * NWD + wave], me);
+    for (int j = kKR; j < k; ++j) atomicOr(&bits[it[j] * NWD + wave], me);
+  }
   __syncthreads();
   for (int e = tid; e < E; e += kThreads) {
     int run = 0;
@@ -190,14 +217,17 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
   if (!valid) return;
   const int* base = FUSED ? sbase : blk_base + (size_t)blockIdx.x * E;
   const unsigned long long below = me - 1ull;
-  for (int j = 0; j < k; ++j) {
-    const int e = it[j];
+  auto place = [&](int j, int e) {
     const int r = base[e] + wbase[e * NWD + wave] + __popcll(bits[e * NWD + wave] & below);
     const size_t pg = (size_t)t * k + j;
     perm_token[r] = t;
     inv[pg] = r;
     if (perm_w) perm_w[r] = topk_w[pg];
-  }
+  };
+#pragma unroll
+  for (int j = 0; j < kKR; ++j)
+    if (j < k) place(j, er[j]);
+  for (int j = kKR; j < k; ++j) place(j, it[j]);
 }
 
 // x_perm[r, :] = x[perm_token[r], :]; rows of `vecs` 16-byte vectors.

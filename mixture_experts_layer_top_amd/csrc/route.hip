@@ -157,7 +157,8 @@ __global__ __launch_bounds__(NWV * 64) void route_bf16_kernel(RouteArgs a, const
   float* part = reinterpret_cast<float*>(smem);  // [NWV][TW][Ep] partial logits
   float* ll = part;                               // [TW][ls] logits (reuses part)
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: K bounds in SGPRs
   const int t_base = blockIdx.x * TW;
   const int d = a.d, E = a.E;
   const int kq = cdiv(cdiv(d, NWV), 32) * 32;  // K per wave, a multiple of 32
@@ -185,18 +186,31 @@ __global__ __launch_bounds__(NWV * 64) void route_bf16_kernel(RouteArgs a, const
   // MFMAs, so each wave keeps ST (MB + NB) 1 KiB loads in flight
   constexpr int ST = (MB + NB) <= 2 ? 8 : (MB + NB) <= 8 ? 4 : 2;
   const bf16x8 zero8 = {};
+  // rows of tokens past T read token 0 (xr); their logits are never stored
   for (int k0 = kb; k0 < ke; k0 += 32 * ST) {
     bf16x8 av[ST][MB], bv[ST][NB];
+    if (k0 + 32 * ST <= ke) {
+      // the whole chunk lies inside K: no predicates
 #pragma unroll
-    for (int st = 0; st < ST; ++st) {
-      const int kk = k0 + st * 32 + (lane >> 4) * 8;
-      const bool kin = kk < ke;  // d % 8 == 0: a lane's 8 values are all in or all out
+      for (int st = 0; st < ST; ++st) {
+        const int kk = k0 + st * 32 + (lane >> 4) * 8;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        av[st][mb] = (kin && t_ok[mb]) ? *reinterpret_cast<const bf16x8*>(xr[mb] + kk) : zero8;
+        for (int mb = 0; mb < MB; ++mb) av[st][mb] = *reinterpret_cast<const bf16x8*>(xr[mb] + kk);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        bv[st][nb] = kin ? *reinterpret_cast<const bf16x8*>(wr[nb] + kk) : zero8;
+        for (int nb = 0; nb < NB; ++nb) bv[st][nb] = *reinterpret_cast<const bf16x8*>(wr[nb] + kk);
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < ST; ++st) {
+        const int kk = k0 + st * 32 + (lane >> 4) * 8;
+        const bool kin = kk < ke;  // d % 8 == 0: a lane's 8 values are all in or all out
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          av[st][mb] = kin ? *reinterpret_cast<const bf16x8*>(xr[mb] + kk) : zero8;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          bv[st][nb] = kin ? *reinterpret_cast<const bf16x8*>(wr[nb] + kk) : zero8;
+      }
     }
 #pragma unroll
     for (int st = 0; st < ST; ++st)

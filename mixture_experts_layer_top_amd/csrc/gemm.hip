@@ -756,12 +756,16 @@ __device__ __forceinline__ void wait_groups(int n) {
 //   main pass, block b: b < G (the first F = N_t - tail tiles, padded to a
 //     multiple of 8 and walked XCD-aware as usual) -> full tile; b >= G ->
 //     split item j = b - G: tail tile F + j / S, part j % S;
-//   fixup pass, block b < tail: tail tile F + b.
+//   fixup pass, block b < tail * FIXQ: tail tile F + b / FIXQ, 16-row
+//     block b % FIXQ of each wave (the partials are read by FIXQ times more
+//     workgroups than there are tail tiles).
 #ifndef MOE_PP_SPLIT_MAX_ROUNDS
 #define MOE_PP_SPLIT_MAX_ROUNDS 64
 #endif
+constexpr int FIXQ = 8;  // fixup workgroups per tail tile (one 16-row block of each wave)
 struct Work {
   int tile, ks, S, item;  // item: index of the split item (-1: a whole tile)
+  int fix_mi;             // fixup pass: the 16-row block this workgroup finishes
   int k_begin, k_end;
   bool ok;
   TileInfo ti;
@@ -817,10 +821,12 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   w.k_begin = 0;
   w.k_end = p.K;
   w.tile = -1;
+  w.fix_mi = 0;
   if (p.fixup) {
-    if (b < tail) {
-      w.tile = F + b;
-      w.item = b * S;
+    if (b < tail * FIXQ) {
+      w.tile = F + b / FIXQ;
+      w.item = (b / FIXQ) * S;
+      w.fix_mi = b % FIXQ;
     }
   } else {
     const int G = cdiv(F, 8) * 8;
@@ -888,7 +894,11 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
   using C = Cfg<PBK>;
   constexpr int SLOT = C::SLOT, HALF = C::HALF, RA = C::RA, RB = C::RB, KS = C::KS, LD = C::LD;
   constexpr int B_RING = RA * SLOT;  // B slots start after the A slots
-  __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
+  // the fixup pass uses LDS only for the epilogue's per-wave staging (at
+  // most 16 rows x 68 floats per wave): sized so that several of its short
+  // workgroups share a compute unit
+  constexpr int FIX_LDS = NW * 16 * 68 * 4;
+  __shared__ __attribute__((aligned(1024))) char lds[FIX ? FIX_LDS : C::LDS_BYTES];
 
   const Work wk = assign_work(p, blockIdx.x, PBK);
   if (!wk.ok) return;
@@ -918,6 +928,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
   const int nk = FIX ? 0 : (k_end - k_begin) / PBK;
   const int w_item = __builtin_amdgcn_readfirstlane(wk.item);
   const int w_S = __builtin_amdgcn_readfirstlane(wk.S);
+  const int w_fix_mi = __builtin_amdgcn_readfirstlane(wk.fix_mi);
 
   // ---- loads.  X: load j = LD wg + q fills A rows RPL j .. RPL (j + 1) - 1;
   // lane l reads 16 B of row RPL j + l / CPR (chunk swizzled by the row).
@@ -1090,14 +1101,14 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
   f32x4* part_base = reinterpret_cast<f32x4*>(p.part) + (size_t)(w_item < 0 ? 0 : w_item) * 512 * MI * NJ;
   if (FIX) {
     // sum the S partials of this tail tile in part order
+    // (this workgroup's 16-row block fix_mi of every wave only, held in
+    // acc[0]; the epilogue places it at block fix_mi)
     const int S = w_S;
     for (int sp = 0; sp < S; ++sp) {
       const f32x4* src = part_base + (size_t)sp * 512 * MI * NJ;
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < NJ; ++nj)
-          acc[mi][nj] += src[((size_t)wave * MI * NJ + mi * NJ + nj) * 64 + lane];
+      for (int nj = 0; nj < NJ; ++nj)
+        acc[0][nj] += src[((size_t)wave * MI * NJ + w_fix_mi * NJ + nj) * 64 + lane];
     }
   } else if (w_item >= 0) {
     // a split item: store the partial accumulators; the fixup pass finishes the tile
@@ -1113,13 +1124,16 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
   // rows 4 * (lane / 16) + i), staged through the wave's own LDS area
   const int col_l = lane & 15;
   const int row_l = (lane >> 4) * 4;
+  // the fixup pass finishes one block per wave (acc[0] = block fix_mi)
+  constexpr int EMI = FIX ? 1 : MI;
+  const int mi_off = FIX ? w_fix_mi : 0;
   if (UP) {
     constexpr int OC = 32, SS = OC + 8;  // output columns per wave; staging stride (bf16)
     bf16_t* sb = reinterpret_cast<bf16_t*>(lds + wave * 16 * SS * 2);
     const int ocol0 = n0 + wg * OC;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      if (mi >= my_nb) break;
+    for (int mi = 0; mi < EMI; ++mi) {
+      if (mi + mi_off >= my_nb) break;
 #pragma unroll
       for (int nj = 0; nj < 2; ++nj)
 #pragma unroll
@@ -1128,7 +1142,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
               f32_to_bf16(silu(acc[mi][nj][i]) * acc[mi][nj + 2][i]);
       // 16 rows x 4 chunks of 16 B: one per lane
       const int r = lane >> 2, c = lane & 3;
-      const int row = t_row0 + grow0 + mi * 16 + r;
+      const int row = t_row0 + grow0 + (mi + mi_off) * 16 + r;
       const int col = ocol0 + c * 8;
       const u32x4 v = *reinterpret_cast<const u32x4*>(sb + r * SS + c * 8);
       if (row < grow_end && col < N)
@@ -1140,8 +1154,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
       constexpr int SS = 64 + 4;  // staging stride in floats
       float* sf = reinterpret_cast<float*>(lds + wave * 16 * SS * 4);
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        if (mi >= my_nb) break;
+      for (int mi = 0; mi < EMI; ++mi) {
+        if (mi + mi_off >= my_nb) break;
 #pragma unroll
         for (int nj = 0; nj < NJ; ++nj)
 #pragma unroll
@@ -1150,7 +1164,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
         for (int q = 0; q < 4; ++q) {  // 16 rows x 16 chunks of 16 B
           const int idx = q * 64 + lane;
           const int r = idx >> 4, c = idx & 15;
-          const int row = t_row0 + grow0 + mi * 16 + r;
+          const int row = t_row0 + grow0 + (mi + mi_off) * 16 + r;
           const int col = n0 + (c >> 3) * 128 + wg * 32 + (c & 7) * 4;
           const f32x4 v = *reinterpret_cast<const f32x4*>(sf + r * SS + c * 4);
           if (row < grow_end && col < N)
@@ -1160,10 +1174,10 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
     }
     if (p.y) {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
+      for (int mi = 0; mi < EMI; ++mi) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = t_row0 + grow0 + mi * 16 + row_l + i;
+          const int row = t_row0 + grow0 + (mi + mi_off) * 16 + row_l + i;
           if (row >= grow_end) continue;
           const int tgt = p.scatter ? p.scatter[row] : row;
           float* yrow = p.y + (size_t)tgt * N;
@@ -1327,7 +1341,7 @@ hipError_t launch_gemm(GemmArgs& p, int rows, int E, int ncols, unsigned long lo
     if (p.part) {
       p.fixup = 1;
       hipLaunchKernelGGL((grouped_gemm_bf16_pp_kernel<UP, MOE_PP_BK, true>),
-                         dim3((unsigned)(p.n_cu / 2)), dim3(64 * pp::NW), 0, s, p);
+                         dim3((unsigned)(p.n_cu / 2 * FIXQ)), dim3(64 * pp::NW), 0, s, p);
     }
     return hipGetLastError();
   }

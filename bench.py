@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-target-s", type=float, default=10.0,
                     help="approximate seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--sweep", choices=["tokens", "skew"], default=None,
+                    help="instead of one workload, time the Mixtral-shape layer over the "
+                         "token-count sweep (T = 128 .. 32768) or the router-bias-strength "
+                         "sweep (0 .. 2x the skewed workload's bias); one JSON line per point")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the layer, run a plain device copy of BYTES bytes three "
                          "times (the reference reading for HBM byte counters)")
@@ -144,28 +148,15 @@ def cpu_baseline(cfg, layer, target_s):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the expert layer is timed on one GPU's share "
-              "of tokens, and no multi-GPU path exists in this build (use --gpus 1).",
-              file=sys.stderr)
-        sys.exit(2)
-
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-
+def time_layer(cfg, args):
+    """Draw the layer on the GPU, run the warmup steps, then time exactly
+    args.steps steps (host sync on both sides), with HIP events recorded on
+    the launch stream between stages.  Returns the layer, the MoeLayer, the
+    wall-clock ms per step, the event ms per step and the per-stage ms."""
     import torch
-    from mixture_experts_layer_top_amd.inputs import CONFIGS, make_layer
+    from mixture_experts_layer_top_amd.inputs import make_layer
     from mixture_experts_layer_top_amd.layer import MoeLayer
-    from mixture_experts_layer_top_amd import _lib
 
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    _lib.load()
-    cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     layer = make_layer(cfg, seed=0, device=dev)
     m = MoeLayer(cfg, layer, keep_logits=False, path=args.path)
@@ -196,7 +187,69 @@ def main():
     stage_ms = {}
     for i, name in enumerate(stages):
         stage_ms[name] = sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
+    return layer, m, wall * 1e3 / args.steps, step_ms, stage_ms
+
+
+def run_sweep(args):
+    """One JSON line per point of the token-count or router-bias sweep of the
+    Mixtral-shape layer (the robustness axes of the COMET page, "COMET's
+    Performance": input token length and imbalanced expert loads)."""
+    import torch
+    from mixture_experts_layer_top_amd.inputs import sweep_configs
+
+    for cfg in sweep_configs(args.sweep):
+        layer, m, ms_per_step, step_ms, stage_ms = time_layer(cfg, args)
+        counts = m.counts.cpu().numpy()
+        share = counts / max(1, counts.sum())
+        T, d, f, k = cfg.T, cfg.d, cfg.f, cfg.k
+        R = T * k
+        out = {
+            "metric": METRIC,
+            "sweep": args.sweep,
+            "workload": cfg.name,
+            "T": T, "d": d, "f": f, "E": cfg.E, "k": k,
+            "bias_scale": cfg.bias_scale if cfg.biased else 0.0,
+            "value": round(cfg.flops() / (ms_per_step * 1e-3) / 1e12, 2),
+            "unit": "TFLOP/s",
+            "ms_per_step": round(ms_per_step, 4),
+            "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+            "steps": args.steps, "warmup": args.warmup,
+            "expert_share_max": round(float(share.max()), 4),
+            "expert_share_min": round(float(share.min()), 4),
+            "stages_ms": {kk: round(v, 4) for kk, v in stage_ms.items()},
+            "expert_up_TFLOPs": round(4 * R * d * f / (stage_ms["expert_up"] * 1e-3) / 1e12, 1),
+            "expert_down_TFLOPs": round(2 * R * f * d / (stage_ms["expert_down"] * 1e-3) / 1e12, 1),
+        }
+        print(json.dumps(out), flush=True)
+        del layer, m
+        torch.cuda.empty_cache()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the expert layer is timed on one GPU's share "
+              "of tokens, and no multi-GPU path exists in this build (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    import torch
+    from mixture_experts_layer_top_amd.inputs import CONFIGS
+    from mixture_experts_layer_top_amd import _lib
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    _lib.load()
+    if args.sweep:
+        run_sweep(args)
+        return
+    cfg = CONFIGS[args.workload]
+    layer, m, ms_per_step, step_ms, stage_ms = time_layer(cfg, args)
 
     flops = cfg.flops()
     T, d, f, k = cfg.T, cfg.d, cfg.f, cfg.k

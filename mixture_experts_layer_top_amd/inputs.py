@@ -49,6 +49,7 @@ class LayerConfig:
     renorm: bool    # renormalise the k selected softmax weights
     dtype: str      # "bf16" or "f32" storage of x and weights
     biased: bool = False       # per-expert logit bias (skewed load)
+    bias_scale: float = 1.0    # strength of that bias (the skew sweep's axis)
     n_shared: int = 0          # always-on shared SwiGLU experts
     f_shared: int = 0          # their FFN dim
     shared_gated: bool = False # shared output scaled by sigmoid(x . w_s)
@@ -84,6 +85,26 @@ CONFIGS = {
                             dtype="bf16", n_shared=2, f_shared=1408),
 }
 
+# The two robustness axes the COMET page reports on ("COMET's Performance":
+# speedups across input token lengths, and behaviour under imbalanced expert
+# loads), as sweeps of the Mixtral-shape layer: the token count from 128 to
+# 32768, and the strength of the skewed workload's router bias from 0 (no
+# skew) to twice the stated bias.
+SWEEP_TOKENS = (128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768)
+SWEEP_BIAS_SCALES = (0.0, 0.5, 1.0, 1.5, 2.0)
+
+
+def sweep_configs(kind: str):
+    """The layers of one sweep: kind "tokens" or "skew"."""
+    if kind == "tokens":
+        return [dataclasses.replace(CONFIGS["mixtral"], name=f"mixtral_T{T}", T=T)
+                for T in SWEEP_TOKENS]
+    if kind == "skew":
+        return [dataclasses.replace(CONFIGS["mixtral_skew"], name=f"mixtral_skew_b{s:g}",
+                                    bias_scale=s) for s in SWEEP_BIAS_SCALES]
+    raise ValueError(f"unknown sweep {kind!r} (tokens or skew)")
+
+
 # tensor ids inside one config's seed space
 _TID = {"x": 0, "W_r": 1, "W_gate": 2, "W_up": 3, "W_down": 4, "w_s": 5}
 
@@ -92,9 +113,10 @@ def _shared_tid(s: int, which: str) -> int:
     return 16 + 3 * s + {"gate": 0, "up": 1, "down": 2}[which]
 
 
-def skew_bias(E: int) -> np.ndarray:
-    """Per-expert router bias of the skewed-load workload, float32."""
-    return np.array([1.5 * math.log((e + 1) ** -1.2) for e in range(E)], dtype=np.float32)
+def skew_bias(E: int, scale: float = 1.0) -> np.ndarray:
+    """Per-expert router bias of the skewed-load workload (times ``scale``), float32."""
+    return np.array([scale * 1.5 * math.log((e + 1) ** -1.2) for e in range(E)],
+                    dtype=np.float32)
 
 
 def _draw_numpy(cfg_id: int, tid: int, seed: int, shape, std: float) -> np.ndarray:
@@ -153,7 +175,7 @@ def make_layer(cfg: LayerConfig, seed: int = 0, device=None, T: Optional[int] = 
     if want("b"):
         out["b"] = None
         if cfg.biased:
-            b = torch.from_numpy(skew_bias(E))
+            b = torch.from_numpy(skew_bias(E, cfg.bias_scale))
             out["b"] = b if device is None else b.to(device)
     if cfg.n_shared and want("Ws"):
         fs = cfg.f_shared

@@ -345,13 +345,12 @@ def test_down_projection_homogeneity(L):
 # ---------------------------------------------------------------- full sizes
 
 
-@pytest.mark.parametrize("name", ["mixtral", "qwen2moe", "mixtral_skew", "deepseek"])
-def test_full_size_sampled(L, name):
-    """The workload at full size, in the launch configuration the benchmark
-    times (the "fast" path): routing and dispatch checked on every token, y on a
-    sample of tokens the oracle computes one expert group at a time."""
-    cfg = CONFIGS[name]
-    log(f"[full] {name} T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k}")
+def check_full_sampled(cfg, n_sample=24):
+    """The layer at full size, in the launch configuration the benchmark
+    times (the "fast" path): routing and dispatch checked on every token, y on
+    a sample of tokens the oracle computes one expert group at a time.
+    Returns the GPU's per-expert counts."""
+    log(f"[full] {cfg.name} T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k}")
     layer = make_layer(cfg, seed=0, device="cuda")
     m = run_layer(cfg, layer, "fast")
     h = host_layer(layer, lazy=True)
@@ -361,7 +360,7 @@ def test_full_size_sampled(L, name):
     log("  dispatch ok")
     counts = m.counts.cpu().numpy()
     rng = np.random.default_rng(123)
-    ts = set([0, cfg.T - 1]) | set(rng.choice(cfg.T, 24, replace=False).tolist())
+    ts = set([0, cfg.T - 1]) | set(rng.choice(cfg.T, min(n_sample, cfg.T), replace=False).tolist())
     small_e = int(np.argmin(counts))
     ts |= set(np.nonzero(np.any(idx_g == small_e, axis=1))[0][:4].tolist())
     ts |= set(near.tolist())
@@ -369,3 +368,36 @@ def test_full_size_sampled(L, name):
     sub = dict(h, x=h["x"][ts])
     ref = O.forward(sub, cfg.k, cfg.renorm, idx=idx_g[ts])
     check_y(cfg, m.y.cpu().double().numpy()[ts], ref["y"], f"{len(ts)} sampled tokens")
+    return counts
+
+
+@pytest.mark.parametrize("name", ["mixtral", "qwen2moe", "mixtral_skew", "deepseek"])
+def test_full_size_sampled(L, name):
+    check_full_sampled(CONFIGS[name])
+
+
+# ---------------------------------------------------------------- sweeps
+
+
+@pytest.mark.parametrize("T", [128, 512, 32768])
+def test_token_sweep_sampled(L, T):
+    """Points of the token-count sweep of the Mixtral-shape layer at full d, f."""
+    from mixture_experts_layer_top_amd.inputs import sweep_configs
+    cfg = {c.T: c for c in sweep_configs("tokens")}[T]
+    counts = check_full_sampled(cfg, n_sample=16)
+    assert counts.sum() == cfg.T * cfg.k
+
+
+@pytest.mark.parametrize("scale", [0.0, 2.0])
+def test_skew_sweep_sampled(L, scale):
+    """Ends of the router-bias-strength sweep: no skew, and twice the skewed
+    workload's bias (expert 0 then sits at the top-2 ceiling of one half of
+    the assignments, and the last experts get almost none or none)."""
+    from mixture_experts_layer_top_amd.inputs import sweep_configs
+    cfg = {c.bias_scale: c for c in sweep_configs("skew")}[scale]
+    counts = check_full_sampled(cfg, n_sample=16)
+    share = counts / counts.sum()
+    if scale == 0.0:
+        assert np.all(np.abs(share - 0.125) <= 0.02), share
+    else:
+        assert 0.48 <= share[0] <= 0.5 and share[7] < 0.01, share

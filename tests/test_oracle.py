@@ -288,6 +288,27 @@ def test_skew_routing_matches_stated_band():
     assert np.all(np.diff(s) < 0), s
 
 
+def test_skew_sweep_routing_shares():
+    """The bias-strength sweep of the skewed workload: scale 0 is the unbiased
+    band, scale 1 the stated band, and expert 0's share grows with the
+    strength while expert 7's shrinks."""
+    from mixture_experts_layer_top_amd.inputs import sweep_configs
+    cfgs = sweep_configs("skew")
+    lay = to_f64(make_layer(cfgs[0], seed=0, parts=ROUTER_PARTS))
+    L0 = O.router_logits(lay["x"], lay["W_r"], None)
+    sh = []
+    for c in cfgs:
+        b = to_f64(make_layer(c, seed=0, parts=("b",)))["b"]
+        idx = O.select_topk(L0 + b[None, :], c.k)
+        sh.append(O.expert_counts(idx, c.E) / idx.size)
+    sh = np.array(sh)
+    assert np.all(np.abs(sh[0] - 0.125) <= 0.02), sh[0]
+    i1 = [c.bias_scale for c in cfgs].index(1.0)
+    assert 0.35 <= sh[i1][0] <= 0.55 and sh[i1][7] < 0.05, sh[i1]
+    assert np.all(np.diff(sh[:, 0]) > 0), sh[:, 0]
+    assert np.all(np.diff(sh[:, 7]) < 0), sh[:, 7]
+
+
 def test_mixtral_routing_unbiased_band():
     s = shares("mixtral")
     assert np.all(np.abs(s - 0.125) <= 0.02), s

@@ -37,6 +37,8 @@
 //     host never reads the per-expert counts; the workgroup id is remapped
 //     so that consecutive tiles land on the same XCD (and its L2), where
 //     they run in near lockstep and share their panels' lines.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -89,6 +91,7 @@ struct GemmArgs {
   int ksplit;               // K ranges per output tile (layer 1 with fused combine only)
   int k_per_split;          // K per range, a multiple of BK
   int grid_per_xcd;         // padded grid / 8
+  int m_group;              // ping-pong kernel: M tiles walked per pass over the N panels
   // ping-pong kernel only: tail split (see assign_work)
   float* part;              // partial accumulators of split tiles, or NULL (no split)
   int n_cu;                 // compute units the tiles are spread over
@@ -865,8 +868,16 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   const int tmt = __shfl(hit_mt, src);
   const int toff = __shfl(hit_off, src);
   const int local = w.tile - tstart;
-  ti.n_t = local / tmt;  // M fastest inside an (expert, N panel)
-  ti.m_t = local - ti.n_t * tmt;
+  // An expert's M tiles are walked in groups of at most m_group: group q
+  // covers all N panels, M fastest inside each panel, before group q + 1,
+  // so a group's token rows (the A operand) are reused by every panel while
+  // they still sit in the last-level cache.
+  const int G = min(p.m_group, tmt);  // (all M tiles of a small expert: M fastest per panel)
+  const int q = local / (G * p.tiles_n);
+  const int mq = min(G, tmt - q * G);  // M tiles in group q
+  const int r = local - q * G * p.tiles_n;
+  ti.n_t = r / mq;
+  ti.m_t = q * G + (r - ti.n_t * mq);
   ti.ks = 0;
   // Balanced M tiles: the expert's c rows form nbe = ceil(c / 16) blocks of
   // 16, dealt to its tmt = ceil(c / BM) tiles as evenly as possible (tile m
@@ -1267,6 +1278,9 @@ int max_tiles_m(int rows, int E) {
 #ifndef MOE_PP_BK
 #define MOE_PP_BK 64  // stage depth of the ping-pong kernel (64 or 32)
 #endif
+#ifndef MOE_PP_MGROUP_MB
+#define MOE_PP_MGROUP_MB 64
+#endif
 constexpr int UP_WN = MOE_UP_WN, UP_BNA = MOE_UP_BNA, DN_WN = MOE_DN_WN, DN_BNA = MOE_DN_BNA;
 
 int num_cus() {
@@ -1323,6 +1337,13 @@ hipError_t launch_gemm(GemmArgs& p, int rows, int E, int ncols, unsigned long lo
   p.k_per_split = cdiv(cdiv(p.K, ksplit), BK) * BK;
   p.ksplit = cdiv(p.K, p.k_per_split);
   p.tiles_n = tiles_n * p.ksplit;
+  // M tiles per pass over an expert's N panels: about MOE_PP_MGROUP_MB of A
+  // rows (0: all of the expert's M tiles in one pass)
+  {
+    const long long a_tile = (long long)BM * p.K * 2;
+    const long long lim = (long long)MOE_PP_MGROUP_MB << 20;
+    p.m_group = lim > 0 ? (int)std::max(1LL, lim / a_tile) : (1 << 30);
+  }
   const long long tiles = (long long)max_tiles_m(rows, E) * p.tiles_n;
   const long long grid = (tiles + 7) / 8 * 8;
   p.grid_per_xcd = (int)(grid / 8);

@@ -91,7 +91,8 @@ struct GemmArgs {
   int ksplit;               // K ranges per output tile (layer 1 with fused combine only)
   int k_per_split;          // K per range, a multiple of BK
   int grid_per_xcd;         // padded grid / 8
-  int m_group;              // ping-pong kernel: M tiles walked per pass over the N panels
+  int m_group;              // ping-pong kernel: most M tiles walked per pass over the N panels
+  int m_group_min;          // experts with at most this many M tiles are walked in one pass
   // ping-pong kernel only: tail split (see assign_work)
   float* part;              // partial accumulators of split tiles, or NULL (no split)
   int n_cu;                 // compute units the tiles are spread over
@@ -868,27 +869,40 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   const int tmt = __shfl(hit_mt, src);
   const int toff = __shfl(hit_off, src);
   const int local = w.tile - tstart;
-  // An expert's M tiles are walked in groups of at most m_group: group q
-  // covers all N panels, M fastest inside each panel, before group q + 1,
-  // so a group's token rows (the A operand) are reused by every panel while
-  // they still sit in the last-level cache.
-  const int G = min(p.m_group, tmt);  // (all M tiles of a small expert: M fastest per panel)
-  const int q = local / (G * p.tiles_n);
-  const int mq = min(G, tmt - q * G);  // M tiles in group q
-  const int r = local - q * G * p.tiles_n;
+  // A large expert's M tiles are walked in ng balanced groups of at most
+  // m_group tiles (the first tmt % ng groups hold one tile more); a group
+  // covers all N panels, M fastest inside each panel, before the next, so
+  // its token rows (the A operand) are reused by every panel while they
+  // still sit in the last-level cache.  A small expert is one group.
+  const int ng = tmt <= p.m_group_min ? 1 : cdiv(tmt, p.m_group);
+  const int tn = p.tiles_n;
+  const int g_lo = tmt / ng, g_rem = tmt - g_lo * ng;  // group sizes g_lo + 1 (g_rem of them), g_lo
+  const int big = g_rem * (g_lo + 1) * tn;            // tiles in the larger groups
+  int q, m0, mq;
+  if (local < big) {
+    q = local / ((g_lo + 1) * tn);
+    m0 = q * (g_lo + 1);
+    mq = g_lo + 1;
+  } else {
+    q = g_rem + (local - big) / (g_lo * tn);
+    m0 = g_rem * (g_lo + 1) + (q - g_rem) * g_lo;
+    mq = g_lo;
+  }
+  const int r = local - m0 * tn;
   ti.n_t = r / mq;
-  ti.m_t = q * G + (r - ti.n_t * mq);
+  ti.m_t = m0 + (r - ti.n_t * mq);
   ti.ks = 0;
   // Balanced M tiles: the expert's c rows form nbe = ceil(c / 16) blocks of
-  // 16, dealt to its tmt = ceil(c / BM) tiles as evenly as possible (tile m
-  // takes blocks [m nbe / tmt, (m + 1) nbe / tmt), between 1 and BM / 16 of
-  // them).  Against full tiles plus one ragged last tile, this removes all
-  // padding but the last block's, and the tiles of an (expert, N panel),
-  // which run side by side and share the panel, take equal time.
+  // 16, dealt to its tmt = ceil(c / BM) tiles as evenly as possible (the
+  // first nbe % tmt tiles take one block more; every tile takes between 1
+  // and BM / 16).  Against full tiles plus one ragged last tile, this
+  // removes all padding but the last block's, and the tiles of an (expert,
+  // N panel), which run side by side and share the panel, take equal time.
   const int c_e = p.offsets[ti.e + 1] - toff;
   const int nbe = cdiv(c_e, 16);
-  const int b0 = (int)((long long)ti.m_t * nbe / tmt);
-  const int b1 = (int)((long long)(ti.m_t + 1) * nbe / tmt);
+  const int b_lo = nbe / tmt, b_rem = nbe - b_lo * tmt;
+  const int b0 = ti.m_t * b_lo + min(ti.m_t, b_rem);
+  const int b1 = b0 + b_lo + (ti.m_t < b_rem ? 1 : 0);
   ti.nb = b1 - b0;
   ti.row0 = toff + 16 * b0;
   ti.row_end = min(toff + 16 * b1, toff + c_e);
@@ -1279,7 +1293,10 @@ int max_tiles_m(int rows, int E) {
 #define MOE_PP_BK 64  // stage depth of the ping-pong kernel (64 or 32)
 #endif
 #ifndef MOE_PP_MGROUP_MB
-#define MOE_PP_MGROUP_MB 64
+#define MOE_PP_MGROUP_MB 32
+#endif
+#ifndef MOE_PP_MGROUP_MIN_MB
+#define MOE_PP_MGROUP_MIN_MB 64
 #endif
 constexpr int UP_WN = MOE_UP_WN, UP_BNA = MOE_UP_BNA, DN_WN = MOE_DN_WN, DN_BNA = MOE_DN_BNA;
 
@@ -1337,12 +1354,15 @@ hipError_t launch_gemm(GemmArgs& p, int rows, int E, int ncols, unsigned long lo
   p.k_per_split = cdiv(cdiv(p.K, ksplit), BK) * BK;
   p.ksplit = cdiv(p.K, p.k_per_split);
   p.tiles_n = tiles_n * p.ksplit;
-  // M tiles per pass over an expert's N panels: about MOE_PP_MGROUP_MB of A
-  // rows (0: all of the expert's M tiles in one pass)
+  // M tiles per pass over an expert's N panels: experts whose A rows exceed
+  // MOE_PP_MGROUP_MIN_MB are walked in passes of at most MOE_PP_MGROUP_MB of
+  // A rows (0: every expert in one pass)
   {
     const long long a_tile = (long long)BM * p.K * 2;
     const long long lim = (long long)MOE_PP_MGROUP_MB << 20;
     p.m_group = lim > 0 ? (int)std::max(1LL, lim / a_tile) : (1 << 30);
+    p.m_group_min = lim > 0 ? (int)std::max(1LL, ((long long)MOE_PP_MGROUP_MIN_MB << 20) / a_tile)
+                            : (1 << 30);
   }
   const long long tiles = (long long)max_tiles_m(rows, E) * p.tiles_n;
   const long long grid = (tiles + 7) / 8 * 8;

@@ -291,7 +291,8 @@ def main():
             "route_GBs": round(by["route"] / (stage_ms["route"] * 1e-3) / 1e9, 1),
         },
         "roofline": {
-            "kernel": gemm_kernel_name(cfg, up=True) + " (layer 0 + SwiGLU)",
+            "kernel": gemm_kernel_name(cfg, up=True) + " (layer 0 + SwiGLU; main pass and "
+                      "tail-split fixup, the launches the expert_up events bracket)",
             "bound": "mfma",
             "achieved": round(g0, 2),
             "peak": peak,

@@ -140,6 +140,17 @@ int moe_expert_up(const void* x, const int32_t* gather_idx, const int32_t* offse
                   void* a_out, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_expert_up_save -- moe_expert_up that also keeps the two projections
+ * for the backward pass (training: COMET page, "What Is COMET"):
+ *   h_out[r, :] = z W_gate[e],  u_out[r, :] = z W_up[e]   (dtype, bf16 RNE),
+ * with a_out as in moe_expert_up.  h_out, u_out [rows, f] out, both required.
+ */
+int moe_expert_up_save(const void* x, const int32_t* gather_idx, const int32_t* offsets, int E,
+                       int rows, int d, int f, int dtype, const void* W_gate, const void* W_up,
+                       void* a_out, void* h_out, void* u_out, void* workspace, size_t ws_bytes,
+                       hipStream_t stream);
+
+/*
  * moe_expert_down -- grouped GEMM "layer 1" (COMET page, "COMET's Technical
  * Principles": the expert's second GEMM, producing the hidden dimension N;
  * tiles are walked M-first for each weight panel) with an optional fused
@@ -191,6 +202,105 @@ int moe_ffn_forward(const void* x, const int32_t* gather_idx, const int32_t* off
 int moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w, int T, int d, int k,
                 const float* y_shared, const float* shared_gate_logit, int accumulate, float* y,
                 hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Backward pass (training).  The pages train MoE models (COMET page, "What
+ * Is COMET"; DisagMoE technical summary, "2.2 AF-Pipe", whose pipeline has
+ * a backward stream); the calls below give the exact gradients of the
+ * forward calls above for an upstream gradient dy of y, in reverse order:
+ *   moe_combine_backward -> moe_expert_down_backward -> moe_expert_up_backward
+ *   -> moe_unpermute; moe_topk_weights_backward -> moe_linear_backward
+ *   (router: G = dL, W = W_r; gated shared expert: G = dgate, W = w_s).
+ * Conventions as above (device pointers owned by the caller, asynchronous,
+ * host validation first, no allocation); bf16 storage for the GEMM calls
+ * (MOE_ERR_UNSUPPORTED for fp32); every sum in a fixed order
+ * (deterministic).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * moe_combine_backward -- gradient of moe_combine (DisagMoE technical
+ * summary, "2.2 AF-Pipe", combine):
+ *   dw[t, j] = <dy[t, :], y_perm[inv[t, j], :]>,
+ *   dy_perm[inv[t, j], :] = topk_w[t, j] * dy[t, :]              (bf16 RNE);
+ *   shared term (dy_shared != NULL): dy_shared[t, :] = g_t * dy[t, :] (bf16),
+ *     g_t = sigmoid(shared_gate_logit[t]) or 1 when the logit is NULL;
+ *     with the logit and y_shared: dgate_logit[t] = <dy[t], y_shared[t]> g_t (1 - g_t).
+ * Arguments: dy [T, d] fp32; y_perm [T*k, d] fp32 (the forward's);
+ *   inv, topk_w [T, k]; y_shared [T, d] fp32 (ungated shared output of the
+ *   forward) or NULL; shared_gate_logit [T] or NULL; dy_perm [T*k, d] bf16
+ *   out; dw [T, k] fp32 out; dy_shared [T, d] bf16 out or NULL;
+ *   dgate_logit [T] fp32 out (required with the logit) or NULL.  1 <= k <= 8.
+ */
+int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* inv,
+                         const float* topk_w, int T, int d, int k, const float* y_shared,
+                         const float* shared_gate_logit, void* dy_perm, float* dw,
+                         void* dy_shared, float* dgate_logit, hipStream_t stream);
+
+/*
+ * moe_expert_down_backward -- gradients of moe_expert_down (layer 1) and of
+ * the SwiGLU of moe_expert_up, per expert e and row r of e:
+ *   dA = dy_perm[r] W_down[e]^T,  s = sigmoid(h[r]),
+ *   dhu[r, 0:f]  = dA * u[r] * s (1 + h[r] (1 - s))     (dH, bf16),
+ *   dhu[r, f:2f] = dA * h[r] * s                        (dU, bf16),
+ *   dW_down[e]   = sum_{r of e} act[r]^T dy_perm[r]     (fp32; 0 for empty experts).
+ * Arguments: dy_perm [rows, d] bf16; offsets as in moe_expert_up; W_down
+ *   [E, f, d]; h, u [rows, f] (moe_expert_up_save); act [rows, f] (its
+ *   a_out); dhu [rows, 2f] bf16 out; dW_down [E, f, d] fp32 out.
+ */
+int moe_expert_down_backward(const void* dy_perm, const int32_t* offsets, int E, int rows, int f,
+                             int d, int dtype, const void* W_down, const void* h, const void* u,
+                             const void* act, void* dhu, float* dW_down, hipStream_t stream);
+
+/*
+ * moe_expert_up_backward -- gradients of moe_expert_up (layer 0) given dhu:
+ *   dx_perm[r] (+)= dhu[r, 0:f] W_gate[e]^T + dhu[r, f:2f] W_up[e]^T   (fp32),
+ *   dW_gate[e] = sum_{r of e} z_r^T dhu[r, 0:f],  dW_up[e] = sum z_r^T dhu[r, f:2f]
+ *   (fp32; 0 for empty experts), z_r = x[gather_idx[r]] (or x[r]).
+ * Arguments: x, gather_idx, offsets, W_gate, W_up as in moe_expert_up; dhu
+ *   [rows, 2f] bf16; dx_perm [rows, d] fp32 out (added to when accumulate =
+ *   1); dW_gate, dW_up [E, d, f] fp32 out.
+ */
+int moe_expert_up_backward(const void* x, const int32_t* gather_idx, const int32_t* offsets,
+                           int E, int rows, int d, int f, int dtype, const void* W_gate,
+                           const void* W_up, const void* dhu, float* dx_perm, int accumulate,
+                           float* dW_gate, float* dW_up, hipStream_t stream);
+
+/*
+ * moe_unpermute -- gradient of the dispatch (DisagMoE technical summary,
+ * "2.2 AF-Pipe", dispatch): dx[t, :] (+)= sum_j dx_perm[inv[t, j], :] in slot
+ * order.  dx_perm [T*k, d] fp32, inv [T, k], dx [T, d] fp32 out (added to
+ * when accumulate = 1); 1 <= k <= 8.
+ */
+int moe_unpermute(const float* dx_perm, const int32_t* inv, int T, int d, int k, int accumulate,
+                  float* dx, hipStream_t stream);
+
+/*
+ * moe_topk_weights_backward -- gradient of the top-k weights of moe_route
+ * with respect to the logits, at the forward's selection (the selection
+ * itself is piecewise constant):
+ *   score RENORM: dL[t, e_j] = w_j (dw_j - sum_i w_i dw_i), 0 elsewhere;
+ *   score TOPK:   dL[t, e] = p_e ([e = e_j] dw_j - sum_i p_{e_i} dw_i).
+ * The weights are recomputed in fp32 from logits (moe_route's logits_out).
+ * Arguments: logits [T, E] fp32, topk_idx [T, k], dw [T, k] fp32, dL [T, E] fp32 out.
+ */
+int moe_topk_weights_backward(const float* logits, const int32_t* topk_idx, const float* dw, int T,
+                              int E, int k, int score, float* dL, hipStream_t stream);
+
+/*
+ * moe_linear_backward -- gradients of the skinny map L = x W (+ b) of the
+ * router (DisagMoE technical summary, "2.2 AF-Pipe": top-k router) or of
+ * the shared expert's gate, given G = dL [T, E]:
+ *   dW = x^T G (fp32, summed over token chunks in order),
+ *   db = sum_t G[t]   (if db != NULL),
+ *   dx += G W^T       (if dx != NULL; fp32, added to).
+ * Arguments: x [T, d] (dtype), W [d, E] (dtype), G [T, E] fp32, dW [d, E]
+ *   fp32 out or NULL, db [E] fp32 out or NULL, dx [T, d] fp32 in/out or NULL;
+ *   workspace of moe_linear_backward_workspace_size(T, d, E) bytes (when dW).
+ */
+size_t moe_linear_backward_workspace_size(int T, int d, int E);
+int moe_linear_backward(const void* x, const void* W, const float* G, int T, int d, int E,
+                        int dtype, float* dW, float* db, float* dx, void* workspace,
+                        size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

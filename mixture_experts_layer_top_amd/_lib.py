@@ -23,7 +23,10 @@ EXPORTS = (
     "moe_status_string", "moe_route_workspace_size", "moe_route", "moe_permute_workspace_size",
     "moe_permute",
     "moe_ffn_workspace_size", "moe_expert_up", "moe_expert_down", "moe_ffn_forward",
-    "moe_combine",
+    "moe_combine", "moe_expert_up_save",
+    "moe_combine_backward", "moe_expert_down_backward", "moe_expert_up_backward",
+    "moe_unpermute", "moe_topk_weights_backward", "moe_linear_backward_workspace_size",
+    "moe_linear_backward",
 )
 
 _lib = None
@@ -59,6 +62,18 @@ def load():
         "moe_ffn_forward": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                   vp, vp, vp, sz, vp]),
         "moe_combine": (i32, [vp, vp, vp, i32, i32, i32, vp, vp, i32, vp, vp]),
+        "moe_expert_up_save": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                     vp, sz, vp]),
+        "moe_combine_backward": (i32, [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                       vp]),
+        "moe_expert_down_backward": (i32, [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                           vp, vp]),
+        "moe_expert_up_backward": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                         i32, vp, vp, vp]),
+        "moe_unpermute": (i32, [vp, vp, i32, i32, i32, i32, vp, vp]),
+        "moe_topk_weights_backward": (i32, [vp, vp, vp, i32, i32, i32, i32, vp, vp]),
+        "moe_linear_backward_workspace_size": (sz, [i32, i32, i32]),
+        "moe_linear_backward": (i32, [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -168,4 +183,75 @@ def moe_combine(y_perm, inv, topk_w, T, d, k, y_shared, shared_gate_logit, accum
                             _p(shared_gate_logit), accumulate, _p(y), _stream(stream))
     if check:
         _check("moe_combine", st)
+    return st
+
+
+# ---------------------------------------------------------------- training
+
+
+def moe_expert_up_save(x, gather_idx, offsets, E, rows, d, f, dtype, W_gate, W_up, a_out, h_out,
+                       u_out, workspace, ws_bytes, stream=None, check=True):
+    st = load().moe_expert_up_save(_p(x), _p(gather_idx), _p(offsets), E, rows, d, f, dtype,
+                                   _p(W_gate), _p(W_up), _p(a_out), _p(h_out), _p(u_out),
+                                   _p(workspace), ws_bytes, _stream(stream))
+    if check:
+        _check("moe_expert_up_save", st)
+    return st
+
+
+def moe_combine_backward(dy, y_perm, inv, topk_w, T, d, k, y_shared, shared_gate_logit, dy_perm,
+                         dw, dy_shared, dgate_logit, stream=None, check=True):
+    st = load().moe_combine_backward(_p(dy), _p(y_perm), _p(inv), _p(topk_w), T, d, k,
+                                     _p(y_shared), _p(shared_gate_logit), _p(dy_perm), _p(dw),
+                                     _p(dy_shared), _p(dgate_logit), _stream(stream))
+    if check:
+        _check("moe_combine_backward", st)
+    return st
+
+
+def moe_expert_down_backward(dy_perm, offsets, E, rows, f, d, dtype, W_down, h, u, act, dhu,
+                             dW_down, stream=None, check=True):
+    st = load().moe_expert_down_backward(_p(dy_perm), _p(offsets), E, rows, f, d, dtype,
+                                         _p(W_down), _p(h), _p(u), _p(act), _p(dhu), _p(dW_down),
+                                         _stream(stream))
+    if check:
+        _check("moe_expert_down_backward", st)
+    return st
+
+
+def moe_expert_up_backward(x, gather_idx, offsets, E, rows, d, f, dtype, W_gate, W_up, dhu,
+                           dx_perm, accumulate, dW_gate, dW_up, stream=None, check=True):
+    st = load().moe_expert_up_backward(_p(x), _p(gather_idx), _p(offsets), E, rows, d, f, dtype,
+                                       _p(W_gate), _p(W_up), _p(dhu), _p(dx_perm), accumulate,
+                                       _p(dW_gate), _p(dW_up), _stream(stream))
+    if check:
+        _check("moe_expert_up_backward", st)
+    return st
+
+
+def moe_unpermute(dx_perm, inv, T, d, k, accumulate, dx, stream=None, check=True):
+    st = load().moe_unpermute(_p(dx_perm), _p(inv), T, d, k, accumulate, _p(dx), _stream(stream))
+    if check:
+        _check("moe_unpermute", st)
+    return st
+
+
+def moe_topk_weights_backward(logits, topk_idx, dw, T, E, k, score, dL, stream=None, check=True):
+    st = load().moe_topk_weights_backward(_p(logits), _p(topk_idx), _p(dw), T, E, k, score,
+                                          _p(dL), _stream(stream))
+    if check:
+        _check("moe_topk_weights_backward", st)
+    return st
+
+
+def moe_linear_backward_workspace_size(T, d, E):
+    return load().moe_linear_backward_workspace_size(T, d, E)
+
+
+def moe_linear_backward(x, W, G, T, d, E, dtype, dW, db, dx, workspace, ws_bytes, stream=None,
+                        check=True):
+    st = load().moe_linear_backward(_p(x), _p(W), _p(G), T, d, E, dtype, _p(dW), _p(db), _p(dx),
+                                    _p(workspace), ws_bytes, _stream(stream))
+    if check:
+        _check("moe_linear_backward", st)
     return st

@@ -20,7 +20,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["moe_api.cpp", "route.hip", "permute.hip", "gemm.hip", "combine.hip"]
+SOURCES = ["moe_api.cpp", "route.hip", "permute.hip", "gemm.hip", "combine.hip",
+           "gemm_bwd.hip", "backward.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

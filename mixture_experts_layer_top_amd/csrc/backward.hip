@@ -1,0 +1,348 @@
+// Memory-bound backward kernels of the MoE layer: combine, unpermute, top-k
+// weights and the router's (or shared gate's) skinny linear map.
+//
+// The layer is trained (COMET page, "What Is COMET"; DisagMoE page, "2.2
+// AF-Pipe", backward stream); these are the gradients of its combine
+// (DisagMoE page, "2.2 AF-Pipe": top-k weighted combine), of the dispatch
+// (unpermute: each token sums the gradients of its k permuted rows) and of
+// the top-k router:
+//   combine:  dw[t,j] = <dy[t], y_perm[inv[t,j]]>,  dy_perm[inv[t,j]] = w[t,j] dy[t];
+//             shared term g S: dy_shared = g dy, dgate[t] = <dy[t], S[t]> g (1 - g);
+//   weights:  renormalised: dL[e_j] = w_j (dw_j - sum_i w_i dw_i), 0 elsewhere;
+//             otherwise:    dL[e] = p_e ([e = e_j] dw_j - sum_i p_{e_i} dw_i);
+//   linear:   dW = x^T G, db = sum_t G[t], dx += G W^T  (G = dL, or the gate's dz).
+// Every sum runs in a fixed order (block reductions in wave order, partial
+// sums over token chunks added in chunk order): results are deterministic.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// one workgroup per token; KS = k (1..8)
+template <int KS>
+__global__ __launch_bounds__(kThreads) void combine_backward_kernel(
+    const f32x4* __restrict__ dy, const f32x4* __restrict__ y_perm, const int32_t* __restrict__ inv,
+    const float* __restrict__ topk_w, int vecs, const f32x4* __restrict__ y_shared,
+    const float* __restrict__ gate_logit, bf16_t* __restrict__ dy_perm, float* __restrict__ dw,
+    bf16_t* __restrict__ dy_shared, float* __restrict__ dgate) {
+  __shared__ float red[kThreads / 64][KS + 1];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int r[KS];
+  float w[KS], dot[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    r[j] = inv[(size_t)t * KS + j];
+    w[j] = topk_w[(size_t)t * KS + j];
+    dot[j] = 0.f;
+  }
+  float g = 1.f, dot_s = 0.f;
+  if (gate_logit) g = 1.f / (1.f + __expf(-gate_logit[t]));
+  for (int c = threadIdx.x; c < vecs; c += kThreads) {
+    const f32x4 v = dy[(size_t)t * vecs + c];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      const f32x4 yp = y_perm[(size_t)r[j] * vecs + c];
+      dot[j] += v[0] * yp[0] + v[1] * yp[1] + v[2] * yp[2] + v[3] * yp[3];
+      const f32x4 s = w[j] * v;
+      uint2 o;
+      o.x = pack_bf16x2(s[0], s[1]);
+      o.y = pack_bf16x2(s[2], s[3]);
+      *reinterpret_cast<uint2*>(dy_perm + ((size_t)r[j] * vecs + c) * 4) = o;
+    }
+    if (dy_shared) {
+      const f32x4 s = g * v;
+      uint2 o;
+      o.x = pack_bf16x2(s[0], s[1]);
+      o.y = pack_bf16x2(s[2], s[3]);
+      *reinterpret_cast<uint2*>(dy_shared + ((size_t)t * vecs + c) * 4) = o;
+      if (dgate) {
+        const f32x4 ys = y_shared[(size_t)t * vecs + c];
+        dot_s += v[0] * ys[0] + v[1] * ys[1] + v[2] * ys[2] + v[3] * ys[3];
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < KS; ++j) {
+    const float s = wave_sum(dot[j]);
+    if (lane == 0) red[wave][j] = s;
+  }
+  {
+    const float s = wave_sum(dot_s);
+    if (lane == 0) red[wave][KS] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x <= KS) {
+    const int j = threadIdx.x;
+    float s = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kThreads / 64; ++w2) s += red[w2][j];
+    if (j < KS) dw[(size_t)t * KS + j] = s;
+    else if (dgate) dgate[t] = s * g * (1.f - g);
+  }
+}
+
+// dx[t] (+)= sum_j dx_perm[inv[t, j]] (slot order); one workgroup per token
+template <int KS>
+__global__ __launch_bounds__(kThreads) void unpermute_kernel(const f32x4* __restrict__ dx_perm,
+                                                             const int32_t* __restrict__ inv,
+                                                             int vecs, int accumulate,
+                                                             f32x4* __restrict__ dx) {
+  const int t = blockIdx.x;
+  int r[KS];
+#pragma unroll
+  for (int j = 0; j < KS; ++j) r[j] = inv[(size_t)t * KS + j];
+  for (int c = threadIdx.x; c < vecs; c += kThreads) {
+    f32x4 v = accumulate ? dx[(size_t)t * vecs + c] : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KS; ++j) s += dx_perm[(size_t)r[j] * vecs + c];
+    dx[(size_t)t * vecs + c] = v + s;
+  }
+}
+
+// dL [T, E] from the fp32 logits, the selection and dw; one thread per token
+__global__ __launch_bounds__(kThreads) void topk_weights_backward_kernel(
+    const float* __restrict__ L, const int32_t* __restrict__ idx, const float* __restrict__ dw,
+    int T, int E, int k, int renorm, float* __restrict__ dL) {
+  const int t = blockIdx.x * kThreads + threadIdx.x;
+  if (t >= T) return;
+  const float* Lt = L + (size_t)t * E;
+  const int32_t* it = idx + (size_t)t * k;
+  const float* dwt = dw + (size_t)t * k;
+  float* out = dL + (size_t)t * E;
+  if (renorm) {
+    // softmax over the k selected logits
+    float m = -INFINITY;
+    for (int j = 0; j < k; ++j) m = fmaxf(m, Lt[it[j]]);
+    float z = 0.f;
+    for (int j = 0; j < k; ++j) z += __expf(Lt[it[j]] - m);
+    float s = 0.f;
+    for (int j = 0; j < k; ++j) s += __expf(Lt[it[j]] - m) / z * dwt[j];
+    for (int e = 0; e < E; ++e) out[e] = 0.f;
+    for (int j = 0; j < k; ++j) out[it[j]] = __expf(Lt[it[j]] - m) / z * (dwt[j] - s);
+  } else {
+    float m = -INFINITY;
+    for (int e = 0; e < E; ++e) m = fmaxf(m, Lt[e]);
+    float z = 0.f;
+    for (int e = 0; e < E; ++e) z += __expf(Lt[e] - m);
+    float s = 0.f;
+    for (int j = 0; j < k; ++j) s += __expf(Lt[it[j]] - m) / z * dwt[j];
+    for (int e = 0; e < E; ++e) out[e] = -__expf(Lt[e] - m) / z * s;
+    for (int j = 0; j < k; ++j) out[it[j]] += __expf(Lt[it[j]] - m) / z * dwt[j];
+  }
+}
+
+template <typename XT>
+__device__ __forceinline__ float ldx(const XT* p, size_t i);
+template <>
+__device__ __forceinline__ float ldx<bf16_t>(const bf16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+template <>
+__device__ __forceinline__ float ldx<float>(const float* p, size_t i) { return p[i]; }
+
+// dW partials: block (column chunk cb of 256 columns, token chunk tc of TC
+// tokens) writes part[tc][i][e] = sum_{t in chunk} x[t, i] G[t, e] for its
+// columns i and every e, 64 experts at a time; G rows are staged in LDS.
+constexpr int TC = 512;    // tokens per chunk
+constexpr int GR = 32;     // G rows per LDS stage
+template <typename XT>
+__global__ __launch_bounds__(kThreads) void xtg_partial_kernel(const XT* __restrict__ x,
+                                                               const float* __restrict__ G, int T,
+                                                               int d, int E,
+                                                               float* __restrict__ part) {
+  __shared__ float gs[GR][64];
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  const int tc = blockIdx.y;
+  const int t0 = tc * TC, t1 = min(T, t0 + TC);
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int ne = min(64, E - e0);
+    float acc[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) acc[e] = 0.f;
+    for (int tb = t0; tb < t1; tb += GR) {
+      const int nt = min(GR, t1 - tb);
+      __syncthreads();
+      for (int q = threadIdx.x; q < GR * 64; q += kThreads) {
+        const int rr = q >> 6, e = q & 63;
+        gs[rr][e] = (rr < nt && e < ne) ? G[(size_t)(tb + rr) * E + e0 + e] : 0.f;
+      }
+      __syncthreads();
+      if (i < d) {
+        for (int rr = 0; rr < nt; ++rr) {
+          const float xv = ldx<XT>(x, (size_t)(tb + rr) * d + i);
+#pragma unroll
+          for (int e = 0; e < 64; ++e) acc[e] = fmaf(xv, gs[rr][e], acc[e]);
+        }
+      }
+    }
+    if (i < d) {
+#pragma unroll
+      for (int e = 0; e < 64; ++e)
+        if (e < ne) part[((size_t)tc * d + i) * E + e0 + e] = acc[e];
+    }
+  }
+}
+
+// dW[i, e] = sum over chunks (in order) of part[c][i][e]
+__global__ __launch_bounds__(kThreads) void sum_chunks_kernel(const float* __restrict__ part,
+                                                              int nc, size_t n,
+                                                              float* __restrict__ out) {
+  const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int c = 0; c < nc; ++c) s += part[(size_t)c * n + i];
+  out[i] = s;
+}
+
+// db[e] = sum_t G[t, e] (one workgroup per expert, wave-order reduction)
+__global__ __launch_bounds__(kThreads) void colsum_kernel(const float* __restrict__ G, int T,
+                                                          int E, float* __restrict__ db) {
+  __shared__ float red[kThreads / 64];
+  const int e = blockIdx.x;
+  float s = 0.f;
+  for (int t = threadIdx.x; t < T; t += kThreads) s += G[(size_t)t * E + e];
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float v = 0.f;
+    for (int w2 = 0; w2 < kThreads / 64; ++w2) v += red[w2];
+    db[e] = v;
+  }
+}
+
+// dx[t, i] += sum_e G[t, e] W[i, e]: block = 16 tokens x 256 columns; each
+// thread keeps its column's W row (64 experts at a time) in registers.
+constexpr int DXT = 16;
+template <typename WT>
+__global__ __launch_bounds__(kThreads) void dx_linear_kernel(const float* __restrict__ G,
+                                                             const WT* __restrict__ W, int T,
+                                                             int d, int E,
+                                                             float* __restrict__ dx) {
+  __shared__ float gs[DXT][64];
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  const int t0 = blockIdx.y * DXT;
+  const int nt = min(DXT, T - t0);
+  float acc[DXT];
+#pragma unroll
+  for (int q = 0; q < DXT; ++q) acc[q] = 0.f;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int ne = min(64, E - e0);
+    float wr[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) wr[e] = (i < d && e < ne) ? ldx<WT>(W, (size_t)i * E + e0 + e) : 0.f;
+    __syncthreads();
+    for (int q = threadIdx.x; q < DXT * 64; q += kThreads) {
+      const int rr = q >> 6, e = q & 63;
+      gs[rr][e] = (rr < nt && e < ne) ? G[(size_t)(t0 + rr) * E + e0 + e] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < DXT; ++q)
+#pragma unroll
+      for (int e = 0; e < 64; ++e) acc[q] = fmaf(gs[q][e], wr[e], acc[q]);
+  }
+  if (i < d)
+    for (int q = 0; q < nt; ++q) dx[(size_t)(t0 + q) * d + i] += acc[q];
+}
+
+template <int KS>
+void launch_cb(const float* dy, const float* y_perm, const int32_t* inv, const float* topk_w,
+               int T, int d, const float* y_shared, const float* gate_logit, void* dy_perm,
+               float* dw, void* dy_shared, float* dgate, hipStream_t s) {
+  hipLaunchKernelGGL((combine_backward_kernel<KS>), dim3(T), dim3(kThreads), 0, s,
+                     reinterpret_cast<const f32x4*>(dy), reinterpret_cast<const f32x4*>(y_perm),
+                     inv, topk_w, d / 4, reinterpret_cast<const f32x4*>(y_shared), gate_logit,
+                     static_cast<bf16_t*>(dy_perm), dw, static_cast<bf16_t*>(dy_shared), dgate);
+}
+
+template <int KS>
+void launch_up(const float* dx_perm, const int32_t* inv, int T, int d, bool accumulate, float* dx,
+               hipStream_t s) {
+  hipLaunchKernelGGL((unpermute_kernel<KS>), dim3(T), dim3(kThreads), 0, s,
+                     reinterpret_cast<const f32x4*>(dx_perm), inv, d / 4, accumulate ? 1 : 0,
+                     reinterpret_cast<f32x4*>(dx));
+}
+
+}  // namespace
+
+hipError_t launch_combine_backward(const float* dy, const float* y_perm, const int32_t* inv,
+                                   const float* topk_w, int T, int d, int k,
+                                   const float* y_shared, const float* gate_logit, void* dy_perm,
+                                   float* dw, void* dy_shared, float* dgate, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  switch (k) {
+#define MOE_CB(K) case K: launch_cb<K>(dy, y_perm, inv, topk_w, T, d, y_shared, gate_logit, dy_perm, dw, dy_shared, dgate, s); break;
+    MOE_CB(1) MOE_CB(2) MOE_CB(3) MOE_CB(4) MOE_CB(5) MOE_CB(6) MOE_CB(7) MOE_CB(8)
+#undef MOE_CB
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_unpermute(const float* dx_perm, const int32_t* inv, int T, int d, int k,
+                            bool accumulate, float* dx, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  switch (k) {
+#define MOE_UP(K) case K: launch_up<K>(dx_perm, inv, T, d, accumulate, dx, s); break;
+    MOE_UP(1) MOE_UP(2) MOE_UP(3) MOE_UP(4) MOE_UP(5) MOE_UP(6) MOE_UP(7) MOE_UP(8)
+#undef MOE_UP
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_weights_backward(const float* logits, const int32_t* idx, const float* dw,
+                                        int T, int E, int k, bool renorm, float* dL,
+                                        hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_weights_backward_kernel, dim3(cdiv(T, kThreads)), dim3(kThreads), 0, s,
+                     logits, idx, dw, T, E, k, renorm ? 1 : 0, dL);
+  return hipGetLastError();
+}
+
+size_t linear_backward_workspace_bytes(int T, int d, int E) {
+  const size_t nc = (size_t)cdiv(T, TC);
+  return align_up(nc * (size_t)d * E * sizeof(float), 256);
+}
+
+hipError_t launch_linear_backward(const void* x, const void* W, const float* G, int T, int d,
+                                  int E, bool bf16, float* dW, float* db, float* dx, void* ws,
+                                  hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int nc = cdiv(T, TC);
+  float* part = static_cast<float*>(ws);
+  if (dW) {
+    const dim3 grid(cdiv(d, kThreads), nc);
+    if (bf16)
+      hipLaunchKernelGGL(xtg_partial_kernel<bf16_t>, grid, dim3(kThreads), 0, s,
+                         static_cast<const bf16_t*>(x), G, T, d, E, part);
+    else
+      hipLaunchKernelGGL(xtg_partial_kernel<float>, grid, dim3(kThreads), 0, s,
+                         static_cast<const float*>(x), G, T, d, E, part);
+    const size_t n = (size_t)d * E;
+    hipLaunchKernelGGL(sum_chunks_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, s, part, nc, n, dW);
+  }
+  if (db) hipLaunchKernelGGL(colsum_kernel, dim3(E), dim3(kThreads), 0, s, G, T, E, db);
+  if (dx) {
+    const dim3 grid(cdiv(d, kThreads), cdiv(T, DXT));
+    if (bf16)
+      hipLaunchKernelGGL(dx_linear_kernel<bf16_t>, grid, dim3(kThreads), 0, s, G,
+                         static_cast<const bf16_t*>(W), T, d, E, dx);
+    else
+      hipLaunchKernelGGL(dx_linear_kernel<float>, grid, dim3(kThreads), 0, s, G,
+                         static_cast<const float*>(W), T, d, E, dx);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -83,6 +83,8 @@ struct GemmArgs {
   const bf16_t* B0;         // [E, K, N]: W_gate (layer 0) or W_down (layer 1)
   const bf16_t* B1;         // [E, K, N]: W_up (layer 0) or NULL
   bf16_t* a_out;            // layer 0 output [rows, N]
+  bf16_t* h_out;            // layer 0: x W_gate [rows, N] saved for the backward, or NULL
+  bf16_t* u_out;            // layer 0: x W_up [rows, N] (given with h_out)
   float* y_perm;            // layer 1 output [rows, N] or NULL
   const int32_t* scatter;   // layer 1 fused combine target row, or NULL (identity)
   const float* row_w;       // layer 1 fused combine weight, or NULL (1)
@@ -586,26 +588,31 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
     constexpr int SS = OC + 8;               // staging stride in bf16 (16-byte aligned)
     bf16_t* sb = reinterpret_cast<bf16_t*>(stg);
     const int ocol0 = n0 + wn * OC;
+    const int nout = p.h_out ? 3 : 1;  // SiLU(h) u, then (training) h and u
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
+      for (int o = 0; o < nout; ++o) {
+        bf16_t* dst = o == 0 ? p.a_out : (o == 1 ? p.h_out : p.u_out);
 #pragma unroll
-      for (int nj = 0; nj < NJ / 2; ++nj)
+        for (int nj = 0; nj < NJ / 2; ++nj)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sb[(row_l + i) * SS + nj * 16 + col_l] =
-              f32_to_bf16(silu(acc[mi][nj][i]) * acc[mi][nj + NJ / 2][i]);
-      // each lane stores 16 bytes (8 columns) of one row
-      constexpr int CH = OC / 8;              // 16-byte chunks per row
+          for (int i = 0; i < 4; ++i) {
+            const float h = acc[mi][nj][i], u = acc[mi][nj + NJ / 2][i];
+            sb[(row_l + i) * SS + nj * 16 + col_l] = f32_to_bf16(o == 0 ? silu(h) * u : (o == 1 ? h : u));
+          }
+        // each lane stores 16 bytes (8 columns) of one row
+        constexpr int CH = OC / 8;              // 16-byte chunks per row
 #pragma unroll
-      for (int q = 0; q < (16 * CH + 63) / 64; ++q) {
-        const int idx = q * 64 + lane;
-        if (idx < 16 * CH) {
-          const int r = idx / CH, c = idx % CH;
-          const int row = ti.row0 + wrow0 + mi * 16 + r;
-          const int col = ocol0 + c * 8;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(sb + r * SS + c * 8);
-          if (row < ti.row_end && col < N)
-            *reinterpret_cast<u32x4*>(p.a_out + (size_t)row * N + col) = v;
+        for (int q = 0; q < (16 * CH + 63) / 64; ++q) {
+          const int idx = q * 64 + lane;
+          if (idx < 16 * CH) {
+            const int r = idx / CH, c = idx % CH;
+            const int row = ti.row0 + wrow0 + mi * 16 + r;
+            const int col = ocol0 + c * 8;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(sb + r * SS + c * 8);
+            if (row < ti.row_end && col < N)
+              *reinterpret_cast<u32x4*>(dst + (size_t)row * N + col) = v;
+          }
         }
       }
     }
@@ -1156,22 +1163,27 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
     constexpr int OC = 32, SS = OC + 8;  // output columns per wave; staging stride (bf16)
     bf16_t* sb = reinterpret_cast<bf16_t*>(lds + wave * 16 * SS * 2);
     const int ocol0 = n0 + wg * OC;
+    const int nout = p.h_out ? 3 : 1;  // SiLU(h) u, then (training) h and u
 #pragma unroll
     for (int mi = 0; mi < EMI; ++mi) {
       if (mi + mi_off >= my_nb) break;
+      for (int o = 0; o < nout; ++o) {
+        bf16_t* dst = o == 0 ? p.a_out : (o == 1 ? p.h_out : p.u_out);
 #pragma unroll
-      for (int nj = 0; nj < 2; ++nj)
+        for (int nj = 0; nj < 2; ++nj)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sb[(row_l + i) * SS + nj * 16 + col_l] =
-              f32_to_bf16(silu(acc[mi][nj][i]) * acc[mi][nj + 2][i]);
-      // 16 rows x 4 chunks of 16 B: one per lane
-      const int r = lane >> 2, c = lane & 3;
-      const int row = t_row0 + grow0 + (mi + mi_off) * 16 + r;
-      const int col = ocol0 + c * 8;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(sb + r * SS + c * 8);
-      if (row < grow_end && col < N)
-        *reinterpret_cast<u32x4*>(p.a_out + (size_t)row * N + col) = v;
+          for (int i = 0; i < 4; ++i) {
+            const float h = acc[mi][nj][i], u = acc[mi][nj + 2][i];
+            sb[(row_l + i) * SS + nj * 16 + col_l] = f32_to_bf16(o == 0 ? silu(h) * u : (o == 1 ? h : u));
+          }
+        // 16 rows x 4 chunks of 16 B: one per lane
+        const int r = lane >> 2, c = lane & 3;
+        const int row = t_row0 + grow0 + (mi + mi_off) * 16 + r;
+        const int col = ocol0 + c * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sb + r * SS + c * 8);
+        if (row < grow_end && col < N)
+          *reinterpret_cast<u32x4*>(dst + (size_t)row * N + col) = v;
+      }
     }
   } else {
     // the wave's columns: n0 + h * 128 + wg * 32 + [0, 32) for halves h = 0, 1
@@ -1234,7 +1246,8 @@ __device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int 
 __global__ void up_f32_kernel(const float* __restrict__ x, const int32_t* __restrict__ gather,
                               const int32_t* __restrict__ offsets, int E, int rows, int d, int f,
                               const float* __restrict__ Wg, const float* __restrict__ Wu,
-                              float* __restrict__ a_out) {
+                              float* __restrict__ a_out, float* __restrict__ h_out,
+                              float* __restrict__ u_out) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (size_t)rows * f) return;
   const int r = (int)(i / f), c = (int)(i - (size_t)r * f);
@@ -1248,6 +1261,10 @@ __global__ void up_f32_kernel(const float* __restrict__ x, const int32_t* __rest
     v = fmaf(z[kk], u[(size_t)kk * f], v);
   }
   a_out[i] = silu(h) * v;
+  if (h_out) {
+    h_out[i] = h;
+    u_out[i] = v;
+  }
 }
 
 __global__ void down_f32_kernel(const float* __restrict__ a, const int32_t* __restrict__ offsets,
@@ -1401,19 +1418,22 @@ size_t ffn_workspace_bytes(int E, int rows, int d, int f) {
 
 hipError_t launch_expert_up(const void* x, const int32_t* gather_idx, const int32_t* offsets,
                             int E, int rows, int d, int f, bool bf16, const void* W_gate,
-                            const void* W_up, void* a_out, void* ws, size_t ws_bytes,
-                            hipStream_t s) {
+                            const void* W_up, void* a_out, void* h_out, void* u_out, void* ws,
+                            size_t ws_bytes, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (!bf16) {
     const size_t n = (size_t)rows * f;
     hipLaunchKernelGGL(up_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        static_cast<const float*>(x), gather_idx, offsets, E, rows, d, f,
                        static_cast<const float*>(W_gate), static_cast<const float*>(W_up),
-                       static_cast<float*>(a_out));
+                       static_cast<float*>(a_out), static_cast<float*>(h_out),
+                       static_cast<float*>(u_out));
     return hipGetLastError();
   }
   GemmArgs p{};
   p.A = static_cast<const bf16_t*>(x);
+  p.h_out = static_cast<bf16_t*>(h_out);
+  p.u_out = static_cast<bf16_t*>(u_out);
   p.gather = gather_idx;
   p.offsets = offsets;
   p.E = E; p.rows = rows; p.K = d; p.N = f;

@@ -113,8 +113,25 @@ int moe_expert_up(const void* x, const int32_t* gather_idx, const int32_t* offse
       (gather_idx && !aligned16(gather_idx)) || !aligned16(offsets))
     return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_expert_up(x, gather_idx, offsets, E, rows, d, f,
-                                          dtype == MOE_BF16, W_gate, W_up, a_out, workspace,
-                                          ws_bytes, stream));
+                                          dtype == MOE_BF16, W_gate, W_up, a_out, nullptr,
+                                          nullptr, workspace, ws_bytes, stream));
+}
+
+int moe_expert_up_save(const void* x, const int32_t* gather_idx, const int32_t* offsets, int E,
+                       int rows, int d, int f, int dtype, const void* W_gate, const void* W_up,
+                       void* a_out, void* h_out, void* u_out, void* workspace, size_t ws_bytes,
+                       hipStream_t stream) {
+  int st = check_ffn_common(offsets, E, rows, d, f, dtype, workspace, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (rows == 0) return MOE_OK;
+  if (!x || !W_gate || !W_up || !a_out || !h_out || !u_out) return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(a_out) ||
+      !aligned16(h_out) || !aligned16(u_out) || (gather_idx && !aligned16(gather_idx)) ||
+      !aligned16(offsets))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_expert_up(x, gather_idx, offsets, E, rows, d, f,
+                                          dtype == MOE_BF16, W_gate, W_up, a_out, h_out, u_out,
+                                          workspace, ws_bytes, stream));
 }
 
 int moe_expert_down(const void* a, const int32_t* offsets, int E, int rows, int f, int d,
@@ -150,7 +167,7 @@ int moe_ffn_forward(const void* x, const int32_t* gather_idx, const int32_t* off
     return MOE_ERR_UNSUPPORTED;
   const bool bf = dtype == MOE_BF16;
   hipError_t e = moe::launch_expert_up(x, gather_idx, offsets, E, rows, d, f, bf, W_gate, W_up,
-                                       a_buf, workspace, ws_bytes, stream);
+                                       a_buf, nullptr, nullptr, workspace, ws_bytes, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(moe::launch_expert_down(a_buf, offsets, E, rows, f, d, bf, W_down, y_perm,
                                             scatter_idx, row_w, y, workspace, ws_bytes, stream));
@@ -172,6 +189,120 @@ int moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w, in
     return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_combine(y_perm, inv, topk_w, T, d, k, y_shared, shared_gate_logit,
                                         accumulate == 1, y, stream));
+}
+
+// ---------------------------------------------------------------- backward
+
+int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* inv,
+                         const float* topk_w, int T, int d, int k, const float* y_shared,
+                         const float* shared_gate_logit, void* dy_perm, float* dw,
+                         void* dy_shared, float* dgate_logit, hipStream_t stream) {
+  if (T < 0 || k < 1 || d <= 0) return MOE_ERR_INVALID;
+  if (k > 8) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * k >= (1ll << 31)) return MOE_ERR_INVALID;
+  if (T == 0) return MOE_OK;
+  if (!dy || !y_perm || !inv || !topk_w || !dy_perm || !dw) return MOE_ERR_INVALID;
+  if (shared_gate_logit && (!dy_shared || !y_shared || !dgate_logit)) return MOE_ERR_INVALID;
+  if (dgate_logit && !shared_gate_logit) return MOE_ERR_INVALID;
+  if (d % 8) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(dy) || !aligned16(y_perm) || !aligned16(inv) || !aligned16(topk_w) ||
+      !aligned16(dy_perm) || !aligned16(dw) || (y_shared && !aligned16(y_shared)) ||
+      (dy_shared && !aligned16(dy_shared)))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_combine_backward(dy, y_perm, inv, topk_w, T, d, k, y_shared,
+                                                 shared_gate_logit, dy_perm, dw, dy_shared,
+                                                 dgate_logit, stream));
+}
+
+static int check_bwd_common(const int32_t* offsets, int E, int rows, int d, int f, int dtype) {
+  if (E < 1 || E > 256 || rows < 0 || d <= 0 || f <= 0) return MOE_ERR_INVALID;
+  if ((long long)rows * 2 * (d > f ? d : f) >= (1ll << 40)) return MOE_ERR_INVALID;
+  if ((long long)E * d * 2 * f >= (1ll << 40)) return MOE_ERR_INVALID;
+  if (!dtype_ok(dtype)) return MOE_ERR_UNSUPPORTED;
+  if (dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;  // the backward GEMMs are bf16 MFMA
+  if (!dims_ok(d) || !dims_ok(f)) return MOE_ERR_UNSUPPORTED;
+  if (!offsets) return MOE_ERR_INVALID;
+  if (!aligned16(offsets)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int moe_expert_down_backward(const void* dy_perm, const int32_t* offsets, int E, int rows, int f,
+                             int d, int dtype, const void* W_down, const void* h, const void* u,
+                             const void* act, void* dhu, float* dW_down, hipStream_t stream) {
+  int st = check_bwd_common(offsets, E, rows, d, f, dtype);
+  if (st != MOE_OK) return st;
+  if (!W_down || !dW_down) return MOE_ERR_INVALID;
+  if (rows > 0 && (!dy_perm || !h || !u || !act || !dhu)) return MOE_ERR_INVALID;
+  if (!aligned16(W_down) || !aligned16(dW_down) || (dy_perm && !aligned16(dy_perm)) ||
+      (h && !aligned16(h)) || (u && !aligned16(u)) || (act && !aligned16(act)) ||
+      (dhu && !aligned16(dhu)))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_expert_down_backward(dy_perm, offsets, E, rows, f, d, W_down, h,
+                                                     u, act, dhu, dW_down, stream));
+}
+
+int moe_expert_up_backward(const void* x, const int32_t* gather_idx, const int32_t* offsets,
+                           int E, int rows, int d, int f, int dtype, const void* W_gate,
+                           const void* W_up, const void* dhu, float* dx_perm, int accumulate,
+                           float* dW_gate, float* dW_up, hipStream_t stream) {
+  int st = check_bwd_common(offsets, E, rows, d, f, dtype);
+  if (st != MOE_OK) return st;
+  if (accumulate != 0 && accumulate != 1) return MOE_ERR_INVALID;
+  if (!W_gate || !W_up || !dW_gate || !dW_up) return MOE_ERR_INVALID;
+  if (rows > 0 && (!x || !dhu || !dx_perm)) return MOE_ERR_INVALID;
+  if (!aligned16(W_gate) || !aligned16(W_up) || !aligned16(dW_gate) || !aligned16(dW_up) ||
+      (x && !aligned16(x)) || (dhu && !aligned16(dhu)) || (dx_perm && !aligned16(dx_perm)) ||
+      (gather_idx && !aligned16(gather_idx)))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_expert_up_backward(x, gather_idx, offsets, E, rows, d, f, W_gate,
+                                                   W_up, dhu, dx_perm, accumulate, dW_gate,
+                                                   dW_up, stream));
+}
+
+int moe_unpermute(const float* dx_perm, const int32_t* inv, int T, int d, int k, int accumulate,
+                  float* dx, hipStream_t stream) {
+  if (T < 0 || k < 1 || d <= 0) return MOE_ERR_INVALID;
+  if (k > 8) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * k >= (1ll << 31)) return MOE_ERR_INVALID;
+  if (accumulate != 0 && accumulate != 1) return MOE_ERR_INVALID;
+  if (T == 0) return MOE_OK;
+  if (!dx_perm || !inv || !dx) return MOE_ERR_INVALID;
+  if (d % 8) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(dx_perm) || !aligned16(inv) || !aligned16(dx)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_unpermute(dx_perm, inv, T, d, k, accumulate == 1, dx, stream));
+}
+
+int moe_topk_weights_backward(const float* logits, const int32_t* topk_idx, const float* dw, int T,
+                              int E, int k, int score, float* dL, hipStream_t stream) {
+  if (T < 0 || E < 1 || E > 256 || k < 1 || k > E) return MOE_ERR_INVALID;
+  if ((long long)T * E >= (1ll << 31)) return MOE_ERR_INVALID;
+  if (score != MOE_SOFTMAX_TOPK_RENORM && score != MOE_SOFTMAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !dw || !dL) return MOE_ERR_INVALID;
+  return hip_status(moe::launch_topk_weights_backward(logits, topk_idx, dw, T, E, k,
+                                                      score == MOE_SOFTMAX_TOPK_RENORM, dL,
+                                                      stream));
+}
+
+size_t moe_linear_backward_workspace_size(int T, int d, int E) {
+  if (T < 0 || d <= 0 || E < 1 || E > 256) return 0;
+  return moe::linear_backward_workspace_bytes(T, d, E);
+}
+
+int moe_linear_backward(const void* x, const void* W, const float* G, int T, int d, int E,
+                        int dtype, float* dW, float* db, float* dx, void* workspace,
+                        size_t ws_bytes, hipStream_t stream) {
+  if (T < 0 || d <= 0 || E < 1 || E > 256) return MOE_ERR_INVALID;
+  if ((long long)T * (d > E ? d : E) >= (1ll << 31)) return MOE_ERR_INVALID;
+  if (!dtype_ok(dtype)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!G || (dW && !x) || (dx && !W)) return MOE_ERR_INVALID;
+  if (dW) {
+    const size_t need = moe::linear_backward_workspace_bytes(T, d, E);
+    if (!workspace || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  }
+  return hip_status(moe::launch_linear_backward(x, W, G, T, d, E, dtype == MOE_BF16, dW, db, dx,
+                                                workspace, stream));
 }
 
 }  // extern "C"

@@ -59,8 +59,8 @@ hipError_t launch_permute(const int32_t* idx, const float* topk_w, const void* x
 size_t ffn_workspace_bytes(int E, int rows, int d, int f);
 hipError_t launch_expert_up(const void* x, const int32_t* gather_idx, const int32_t* offsets,
                             int E, int rows, int d, int f, bool bf16, const void* W_gate,
-                            const void* W_up, void* a_out, void* ws, size_t ws_bytes,
-                            hipStream_t s);
+                            const void* W_up, void* a_out, void* h_out, void* u_out, void* ws,
+                            size_t ws_bytes, hipStream_t s);
 hipError_t launch_expert_down(const void* a, const int32_t* offsets, int E, int rows, int f,
                               int d, bool bf16, const void* W_down, float* y_perm,
                               const int32_t* scatter_idx, const float* row_w, float* y, void* ws,
@@ -69,5 +69,29 @@ hipError_t launch_expert_down(const void* a, const int32_t* offsets, int E, int 
 hipError_t launch_combine(const float* y_perm, const int32_t* inv, const float* topk_w, int T,
                           int d, int k, const float* y_shared, const float* gate_logit,
                           bool accumulate, float* y, hipStream_t s);
+
+// backward
+hipError_t launch_combine_backward(const float* dy, const float* y_perm, const int32_t* inv,
+                                   const float* topk_w, int T, int d, int k,
+                                   const float* y_shared, const float* gate_logit, void* dy_perm,
+                                   float* dw, void* dy_shared, float* dgate, hipStream_t s);
+hipError_t launch_expert_down_backward(const void* dy_perm, const int32_t* offsets, int E,
+                                       int rows, int f, int d, const void* W_down,
+                                       const void* h, const void* u, const void* act,
+                                       void* dhu, float* dW_down, hipStream_t s);
+hipError_t launch_expert_up_backward(const void* x, const int32_t* gather_idx,
+                                     const int32_t* offsets, int E, int rows, int d, int f,
+                                     const void* W_gate, const void* W_up, const void* dhu,
+                                     float* dx_perm, int accumulate, float* dW_gate,
+                                     float* dW_up, hipStream_t s);
+hipError_t launch_unpermute(const float* dx_perm, const int32_t* inv, int T, int d, int k,
+                            bool accumulate, float* dx, hipStream_t s);
+hipError_t launch_topk_weights_backward(const float* logits, const int32_t* idx, const float* dw,
+                                        int T, int E, int k, bool renorm, float* dL,
+                                        hipStream_t s);
+size_t linear_backward_workspace_bytes(int T, int d, int E);
+hipError_t launch_linear_backward(const void* x, const void* W, const float* G, int T, int d,
+                                  int E, bool bf16, float* dW, float* db, float* dx, void* ws,
+                                  hipStream_t s);
 
 }  // namespace moe

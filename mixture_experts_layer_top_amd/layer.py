@@ -19,6 +19,18 @@ Paths: "fast" = fused gather + separate combine (the benchmarked default,
 deterministic); "atomic" = fused gather + atomic combine; "reference" =
 copy gather + separate combine.
 
+Training (``train=True``): the forward also keeps the layer-0 projections
+h = x W_gate and u = x W_up (routed and shared) and the router logits, and
+``backward(dy)`` issues the backward C-ABI calls in reverse order:
+
+    moe_combine_backward -> moe_expert_down_backward -> moe_expert_up_backward
+    -> moe_unpermute -> moe_topk_weights_backward -> moe_linear_backward
+    [-> shared experts: moe_expert_down_backward, moe_expert_up_backward,
+        moe_linear_backward for the gate]
+
+leaving the gradients in ``self.grads`` (fp32 device tensors).  Training
+needs the deterministic separate combine (y_perm) and bf16 storage.
+
 Shared experts: the n_s experts are stored side by side (gate/up projections
 [d, n_s*f_s], down projections [n_s*f_s, d]), so their sum is one SwiGLU FFN
 of width n_s*f_s, run as a single-expert FFN over x (offsets {0, T}).  With
@@ -39,11 +51,16 @@ PATHS = {"fast": ("fused", "separate"), "atomic": ("fused", "atomic"),
 
 class MoeLayer:
     def __init__(self, cfg: LayerConfig, layer: dict, fused=None, keep_logits: bool = True,
-                 path: str = "fast"):
+                 path: str = "fast", train: bool = False):
         if fused is not None:  # shorthand kept for callers of the two original paths
             path = "atomic" if fused else "reference"
         self.path = path
         self.gather, self.comb = PATHS[path]
+        self.train = train
+        if train:
+            if self.comb != "separate" or cfg.dtype != "bf16":
+                raise ValueError("training needs the separate combine and bf16 storage")
+            keep_logits = True
         self.cfg = cfg
         self.t = layer
         dev = layer["x"].device
@@ -71,6 +88,9 @@ class MoeLayer:
         self.ws_perm = e(max(self.ws_perm_bytes, 16), dt=torch.uint8)
         self.ws_ffn_bytes = L.moe_ffn_workspace_size(E, R, d, f)
         self.ws_ffn = e(max(self.ws_ffn_bytes, 16), dt=torch.uint8)
+        if train:
+            self.h = e(R, f, dt=act)
+            self.u = e(R, f, dt=act)
         # shared experts
         self.ns = cfg.n_shared
         if self.ns:
@@ -79,6 +99,9 @@ class MoeLayer:
             self.s_offsets = torch.tensor([0, T], dtype=i32, device=dev)
             self.s_ws_bytes = L.moe_ffn_workspace_size(1, T, d, self.fs_all)
             self.s_ws = e(max(self.s_ws_bytes, 16), dt=torch.uint8)
+            if train:
+                self.s_h = e(T, self.fs_all, dt=act)
+                self.s_u = e(T, self.fs_all, dt=act)
             if not (self.comb == "atomic" and not cfg.shared_gated):
                 self.ys = e(T, d)   # shared-expert output
             if cfg.shared_gated:
@@ -118,8 +141,13 @@ class MoeLayer:
             L.moe_route(t["x"], self.w_s_col, None, T, d, 1, 1, L.MOE_SOFTMAX_TOPK, self.dtype,
                         self.g_idx, self.g_w, self.g_logit, self.g_ws, self.g_ws_bytes,
                         stream=stream)
-        L.moe_expert_up(t["x"], None, self.s_offsets, 1, T, d, fs, self.dtype, t["Ws_gate"],
-                        t["Ws_up"], self.s_a, self.s_ws, self.s_ws_bytes, stream=stream)
+        if self.train:
+            L.moe_expert_up_save(t["x"], None, self.s_offsets, 1, T, d, fs, self.dtype,
+                                 t["Ws_gate"], t["Ws_up"], self.s_a, self.s_h, self.s_u, self.s_ws,
+                                 self.s_ws_bytes, stream=stream)
+        else:
+            L.moe_expert_up(t["x"], None, self.s_offsets, 1, T, d, fs, self.dtype, t["Ws_gate"],
+                            t["Ws_up"], self.s_a, self.s_ws, self.s_ws_bytes, stream=stream)
         # ungated with the atomic combine: the output initialises y directly
         out = self.y if (self.comb == "atomic" and not c.shared_gated) else self.ys
         L.moe_expert_down(self.s_a, self.s_offsets, 1, T, fs, d, self.dtype, t["Ws_down"],
@@ -135,8 +163,13 @@ class MoeLayer:
             src, gidx = t["x"], self.perm_token
         else:
             src, gidx = self.x_perm, None
-        L.moe_expert_up(src, gidx, self.offsets, c.E, R, c.d, c.f, self.dtype, t["W_gate"],
-                        t["W_up"], self.a, self.ws_ffn, self.ws_ffn_bytes, stream=stream)
+        if self.train:
+            L.moe_expert_up_save(src, gidx, self.offsets, c.E, R, c.d, c.f, self.dtype,
+                                 t["W_gate"], t["W_up"], self.a, self.h, self.u, self.ws_ffn,
+                                 self.ws_ffn_bytes, stream=stream)
+        else:
+            L.moe_expert_up(src, gidx, self.offsets, c.E, R, c.d, c.f, self.dtype, t["W_gate"],
+                            t["W_up"], self.a, self.ws_ffn, self.ws_ffn_bytes, stream=stream)
 
     def expert_down(self, stream=None):
         c, t = self.cfg, self.t
@@ -170,3 +203,85 @@ class MoeLayer:
             if marks is not None:
                 marks(name)
         return self.y
+
+    # -- backward ----------------------------------------------------------
+    BSTAGES = ("combine_bwd", "expert_down_bwd", "expert_up_bwd", "unpermute", "router_bwd",
+               "shared_bwd")
+
+    def _alloc_backward(self):
+        if getattr(self, "_bwd_ready", False):
+            return
+        c, t = self.cfg, self.t
+        dev = t["x"].device
+        T, d, f, E, k = c.T, c.d, c.f, c.E, c.k
+        R = T * k
+        f32, bf = torch.float32, torch.bfloat16
+        e = lambda *sh, dt=f32: torch.empty(*sh, dtype=dt, device=dev)  # noqa: E731
+        self.dy_perm = e(R, d, dt=bf)
+        self.dw = e(T, k)
+        self.dhu = e(R, 2 * f, dt=bf)
+        self.dx_perm = e(R, d)
+        self.dL = e(T, E)
+        g = dict(dx=e(T, d), dW_r=e(d, E), dW_gate=e(E, d, f), dW_up=e(E, d, f),
+                 dW_down=e(E, f, d), db=e(E) if t.get("b") is not None else None)
+        self.ws_lin_bytes = L.moe_linear_backward_workspace_size(T, d, E)
+        self.ws_lin = e(max(self.ws_lin_bytes, 16), dt=torch.uint8)
+        if self.ns:
+            fs = self.fs_all
+            self.dys = e(T, d, dt=bf)
+            self.s_dhu = e(T, 2 * fs, dt=bf)
+            g.update(dWs_gate=e(d, fs), dWs_up=e(d, fs), dWs_down=e(fs, d))
+            if c.shared_gated:
+                self.dgl = e(T, 1)
+                g["dw_s"] = e(d, 1)
+                self.ws_lin1_bytes = L.moe_linear_backward_workspace_size(T, d, 1)
+                self.ws_lin1 = e(max(self.ws_lin1_bytes, 16), dt=torch.uint8)
+        self.grads = g
+        self._bwd_ready = True
+
+    def backward(self, dy, stream=None, marks=None):
+        """Gradients of <dy, y> for the last forward (``train=True``); ``marks``
+        as in ``forward``, after each backward stage."""
+        if not self.train:
+            raise RuntimeError("construct the layer with train=True to run the backward")
+        self._alloc_backward()
+        c, t, g = self.cfg, self.t, self.grads
+        T, d, f, E, k = c.T, c.d, c.f, c.E, c.k
+        R = T * k
+        mk = (lambda n: marks(n)) if marks is not None else (lambda n: None)
+        gated = bool(self.ns and c.shared_gated)
+        L.moe_combine_backward(dy, self.y_perm, self.inv, self.w, T, d, k,
+                               self.ys if gated else None, self.g_logit if gated else None,
+                               self.dy_perm, self.dw, self.dys if self.ns else None,
+                               self.dgl if gated else None, stream=stream)
+        mk("combine_bwd")
+        L.moe_expert_down_backward(self.dy_perm, self.offsets, E, R, f, d, self.dtype,
+                                   t["W_down"], self.h, self.u, self.a, self.dhu, g["dW_down"],
+                                   stream=stream)
+        mk("expert_down_bwd")
+        L.moe_expert_up_backward(t["x"], self.perm_token, self.offsets, E, R, d, f, self.dtype,
+                                 t["W_gate"], t["W_up"], self.dhu, self.dx_perm, 0, g["dW_gate"],
+                                 g["dW_up"], stream=stream)
+        mk("expert_up_bwd")
+        L.moe_unpermute(self.dx_perm, self.inv, T, d, k, 0, g["dx"], stream=stream)
+        mk("unpermute")
+        score = L.MOE_SOFTMAX_TOPK_RENORM if c.renorm else L.MOE_SOFTMAX_TOPK
+        L.moe_topk_weights_backward(self.logits, self.idx, self.dw, T, E, k, score, self.dL,
+                                    stream=stream)
+        L.moe_linear_backward(t["x"], t["W_r"], self.dL, T, d, E, self.dtype, g["dW_r"],
+                              g["db"], g["dx"], self.ws_lin, self.ws_lin_bytes, stream=stream)
+        mk("router_bwd")
+        if self.ns:
+            fs = self.fs_all
+            L.moe_expert_down_backward(self.dys, self.s_offsets, 1, T, fs, d, self.dtype,
+                                       t["Ws_down"], self.s_h, self.s_u, self.s_a, self.s_dhu,
+                                       g["dWs_down"], stream=stream)
+            L.moe_expert_up_backward(t["x"], None, self.s_offsets, 1, T, d, fs, self.dtype,
+                                     t["Ws_gate"], t["Ws_up"], self.s_dhu, g["dx"], 1,
+                                     g["dWs_gate"], g["dWs_up"], stream=stream)
+            if gated:
+                L.moe_linear_backward(t["x"], self.w_s_col, self.dgl, T, d, 1, self.dtype,
+                                      g["dw_s"], None, g["dx"], self.ws_lin1, self.ws_lin1_bytes,
+                                      stream=stream)
+        mk("shared_bwd")
+        return g

@@ -1,0 +1,187 @@
+"""Parity of the HIP backward pass (through the C ABI) with the fp64 CPU
+backward oracle.
+
+Every gradient the layer returns (x, router W_r and bias, expert gate/up/down
+weights, shared experts and their gate vector) and the slot-weight gradient
+dw are compared with the oracle evaluated at the GPU's selection, on seeded
+upstream gradients dy.  Bars, per tensor (per expert for the experts'
+weight gradients, whose scale differs between experts with many and few
+tokens; an empty expert's gradients must be exactly zero):
+  * normwise: ||g_gpu - g_ref||_F <= NORM_TAU * ||g_ref||_F, NORM_TAU = 1e-2;
+  * elementwise: |g_gpu - g_ref| <= EL_TAU * (|g_ref| + rms(g_ref)),
+    EL_TAU = 5e-2 (a gradient entry's error scales with the entry: a few
+    tokens can dominate an expert's weight-gradient entry, so a bar against
+    the rms alone would be set by the tensor's tails);
+  * the router bias gradient db[e] = sum_t dL[t, e] is a sum with heavy
+    cancellation, bounded against its terms' magnitudes:
+    |db_gpu - db_ref| <= NORM_TAU * sum_t |dL_ref[t, e]|.
+Where they come from: the forward's bar for bf16 storage is 2e-2 * rms for
+one bf16 intermediate (the activation a); the backward chains three bf16
+roundings (dy_perm = w dy, then dH and dU, with the saved h, u and a as
+operands; 2^-9 relative each), with fp32 accumulation everywhere else.
+Measured on the mid-size workloads: normwise 0.16-0.36%, elementwise
+constant <= 3.4%, db <= 0.1%.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_backward as B
+from mixture_experts_layer_top_amd.inputs import CONFIGS, make_layer
+
+pytestmark = pytest.mark.gpu
+
+NORM_TAU = 1e-2
+EL_TAU = 5e-2
+
+MID = {
+    "mixtral": CONFIGS["mixtral"].shrink(T=2000, d=520, f=392),
+    "qwen2moe": CONFIGS["qwen2moe"].shrink(T=1024, d=264, f=200, f_shared=256),
+    "mixtral_skew": CONFIGS["mixtral_skew"].shrink(T=3000, d=256, f=256),
+    "deepseek": CONFIGS["deepseek"].shrink(T=1500, d=256, f=136, f_shared=136),
+    "mixtral_k64": CONFIGS["mixtral"].shrink(T=2000, d=512, f=320),
+}
+
+# oracle gradient key -> (GPU gradient key, reshape of the GPU tensor to the oracle's)
+KEYS = {"dx": "dx", "dW_r": "dW_r", "db": "db", "dW_gate": "dW_gate", "dW_up": "dW_up",
+        "dW_down": "dW_down", "dWs_gate": "dWs_gate", "dWs_up": "dWs_up",
+        "dWs_down": "dWs_down", "dw_s": "dw_s"}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def L():
+    from mixture_experts_layer_top_amd import _lib
+    _lib.load()
+    return _lib
+
+
+def rms(a):
+    return float(np.sqrt(np.mean(np.square(a))))
+
+
+def host(layer):
+    return {k: (None if v is None else v.to("cpu", torch.float64).numpy()) for k, v in layer.items()}
+
+
+def run_train(cfg, layer, dy):
+    from mixture_experts_layer_top_amd.layer import MoeLayer
+    m = MoeLayer(cfg, layer, path="fast", train=True)
+    m.forward()
+    g = m.backward(dy)
+    torch.cuda.synchronize()
+    return m, g
+
+
+def errors(got, ref):
+    """normwise relative error, max error over rms, and the smallest c with
+    |got - ref| <= c (|ref| + rms(ref)) everywhere"""
+    diff = np.abs(got - ref)
+    r = rms(ref)
+    nrm = float(np.linalg.norm(diff) / np.linalg.norm(ref))
+    mx = float(np.max(diff)) / r
+    c = float(np.max(diff / (np.abs(ref) + r)))
+    return nrm, mx, c
+
+
+PER_EXPERT = ("dW_gate", "dW_up", "dW_down")
+
+
+def check_grads(cfg, m, g, h, dy_h):
+    """Log every statistic first, then assert the bars of the module
+    docstring (per expert for the experts' weight gradients)."""
+    idx = m.idx.cpu().numpy().astype(np.int64)
+    ref = B.backward(h, dy_h, cfg.k, cfg.renorm, idx=idx)
+    fails = []
+    got_dw = m.dw.cpu().double().numpy()
+    items = [("dw", got_dw, ref["dw"])]
+    for rk, gk in KEYS.items():
+        if ref.get(rk) is None:
+            assert g.get(gk) is None, gk
+            continue
+        items.append((rk, g[gk].cpu().double().numpy().reshape(ref[rk].shape), ref[rk]))
+    for rk, got, rf in items:
+        if rk in PER_EXPERT:
+            worst = [0.0, 0.0, 0.0]
+            for e in range(cfg.E):
+                if not np.any(rf[e]):
+                    if np.any(got[e]):
+                        fails.append(f"{rk}[{e}] must be exactly zero (empty expert)")
+                    continue
+                st = errors(got[e], rf[e])
+                worst = [max(a, b) for a, b in zip(worst, st)]
+                if st[0] > NORM_TAU or st[2] > EL_TAU:
+                    fails.append(f"{rk}[{e}]: normwise {st[0]:.3e}, c {st[2]:.3e}")
+            log(f"  {cfg.name} {rk} (worst expert): normwise {worst[0]:.3e}, max/rms {worst[1]:.3e}, "
+                f"c {worst[2]:.3e}")
+        elif rk == "db":
+            scale = np.sum(np.abs(ref["dL"]), axis=0)
+            ratio = float(np.max(np.abs(got - rf) / np.maximum(scale, 1e-300)))
+            log(f"  {cfg.name} db: max |d| / sum_t |dL| = {ratio:.3e}")
+            if ratio > NORM_TAU:
+                fails.append(f"db: {ratio:.3e}")
+        else:
+            st = errors(got, rf)
+            log(f"  {cfg.name} {rk}: normwise {st[0]:.3e}, max/rms {st[1]:.3e}, c {st[2]:.3e}")
+            if st[0] > NORM_TAU or st[2] > EL_TAU:
+                fails.append(f"{rk}: normwise {st[0]:.3e}, c {st[2]:.3e}")
+    assert not fails, fails
+
+
+@pytest.mark.parametrize("name", list(MID))
+def test_backward_parity_mid(L, name):
+    cfg = MID[name]
+    log(f"[bwd] {name} T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k}")
+    layer = make_layer(cfg, seed=0, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    dy = torch.randn(cfg.T, cfg.d, generator=gen, device="cuda", dtype=torch.float32)
+    m, g = run_train(cfg, layer, dy)
+    check_grads(cfg, m, g, host(layer), dy.cpu().double().numpy())
+
+
+def test_backward_is_deterministic(L):
+    cfg = MID["deepseek"]
+    layer = make_layer(cfg, seed=2, device="cuda")
+    dy = torch.randn(cfg.T, cfg.d, generator=torch.Generator(device="cuda").manual_seed(3),
+                     device="cuda", dtype=torch.float32)
+    _, g1 = run_train(cfg, layer, dy)
+    g1 = {k: (None if v is None else v.clone()) for k, v in g1.items()}
+    _, g2 = run_train(cfg, layer, dy)
+    for k, v in g1.items():
+        if v is not None:
+            assert torch.equal(v, g2[k]), k
+
+
+def test_backward_zero_upstream(L):
+    cfg = MID["qwen2moe"]
+    layer = make_layer(cfg, seed=4, device="cuda")
+    m, g = run_train(cfg, layer, torch.zeros(cfg.T, cfg.d, device="cuda"))
+    for k, v in g.items():
+        if v is not None:
+            assert torch.count_nonzero(v).item() == 0, k
+
+
+def test_backward_empty_expert_gets_zero_weight_gradients(L):
+    """A skewed router at twice the stated bias leaves the last expert empty:
+    its weight gradients are exactly zero, the others are not."""
+    from mixture_experts_layer_top_amd.inputs import sweep_configs
+    base = {c.bias_scale: c for c in sweep_configs("skew")}[2.0]
+    cfg = base.shrink(T=512, d=128, f=128)
+    layer = make_layer(cfg, seed=0, device="cuda")
+    dy = torch.randn(cfg.T, cfg.d, generator=torch.Generator(device="cuda").manual_seed(5),
+                     device="cuda", dtype=torch.float32)
+    m, g = run_train(cfg, layer, dy)
+    counts = m.counts.cpu().numpy()
+    empty = np.nonzero(counts == 0)[0]
+    assert len(empty) > 0, counts
+    for e in range(cfg.E):
+        for k in ("dW_gate", "dW_up", "dW_down"):
+            nz = torch.count_nonzero(g[k][e]).item()
+            assert (nz == 0) == (counts[e] == 0), (k, e, counts[e], nz)
+    check_grads(cfg, m, g, host(layer), dy.cpu().double().numpy())

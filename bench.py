@@ -47,6 +47,10 @@ def parse():
                     help="instead of one workload, time the Mixtral-shape layer over the "
                          "token-count sweep (T = 128 .. 32768) or the router-bias-strength "
                          "sweep (0 .. 2x the skewed workload's bias); one JSON line per point")
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step instead: the forward that keeps h = x W_gate and "
+                         "u = x W_up, then the backward of a seeded upstream gradient; one JSON "
+                         "line with the backward's rate and per-stage times")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the layer, run a plain device copy of BYTES bytes three "
                          "times (the reference reading for HBM byte counters)")
@@ -225,6 +229,78 @@ def run_sweep(args):
         torch.cuda.empty_cache()
 
 
+def backward_flops(cfg):
+    """Algorithmic flops of the layer's backward: each GEMM's data and weight
+    gradients (twice the forward's GEMM flops), the router's dW_r and dx
+    (2 * 2 T d E) and the shared gate's (2 * 2 T d)."""
+    T, d, f, E, k = cfg.T, cfg.d, cfg.f, cfg.E, cfg.k
+    fl = 12 * T * k * d * f + 4 * T * d * E
+    fl += cfg.n_shared * 12 * T * d * cfg.f_shared
+    if cfg.shared_gated:
+        fl += 4 * T * d
+    return fl
+
+
+def run_backward(args):
+    """Training step of the workload: forward (train=True) then backward, the
+    backward's stages bracketed by HIP events on the launch stream."""
+    import torch
+    from mixture_experts_layer_top_amd.inputs import CONFIGS, make_layer
+    from mixture_experts_layer_top_amd.layer import MoeLayer
+
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    layer = make_layer(cfg, seed=0, device=dev)
+    m = MoeLayer(cfg, layer, path="fast", train=True)
+    dy = torch.randn(cfg.T, cfg.d, generator=torch.Generator(device=dev).manual_seed(1),
+                     device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        m.forward()
+        m.backward(dy)
+    torch.cuda.synchronize()
+    bst = MoeLayer.BSTAGES
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(bst) + 2)]
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        m.forward()
+        ev[s][1].record(stream)
+        pos = [2]
+
+        def mark(_name, s=s, pos=pos):
+            ev[s][pos[0]].record(stream)
+            pos[0] += 1
+
+        m.backward(dy, marks=mark)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg = lambda i, j: sum(ev[s][i].elapsed_time(ev[s][j]) for s in range(args.steps)) / args.steps  # noqa: E731
+    fwd_ms = avg(0, 1)
+    bwd_ms = avg(1, len(bst) + 1)
+    stage_ms = {name: avg(i + 1, i + 2) for i, name in enumerate(bst)}
+    T, d, f, k = cfg.T, cfg.d, cfg.f, cfg.k
+    R = T * k
+    out = {
+        "metric": "MoE layer bwd TFLOP/s + training-step tokens/s, 1xMI355X",
+        "workload": cfg.name, "T": T, "d": d, "f": f, "E": cfg.E, "k": k,
+        "value": round(backward_flops(cfg) / (bwd_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "steps": args.steps, "warmup": args.warmup,
+        "train_step_ms": round(wall * 1e3 / args.steps, 4),
+        "train_tokens_per_s": round(T / (wall / args.steps), 1),
+        "forward_ms": round(fwd_ms, 4), "backward_ms": round(bwd_ms, 4),
+        "backward_stages_ms": {kk: round(v, 4) for kk, v in stage_ms.items()},
+        "stage_rates": {
+            "expert_down_bwd_TFLOPs": round(4 * R * d * f / (stage_ms["expert_down_bwd"] * 1e-3) / 1e12, 1),
+            "expert_up_bwd_TFLOPs": round(8 * R * d * f / (stage_ms["expert_up_bwd"] * 1e-3) / 1e12, 1),
+        },
+        "dtype": "bf16", "data": "synthetic",
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -247,6 +323,9 @@ def main():
     _lib.load()
     if args.sweep:
         run_sweep(args)
+        return
+    if args.backward:
+        run_backward(args)
         return
     cfg = CONFIGS[args.workload]
     layer, m, ms_per_step, step_ms, stage_ms = time_layer(cfg, args)

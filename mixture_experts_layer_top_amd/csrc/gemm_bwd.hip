@@ -18,9 +18,10 @@
 //              rows of x gathered through the permutation).
 //
 // Kernel: 4 wave64s (2 x 2) per 128 x 128 tile, each wave 64 x 64 = 4 x 4
-// blocks of v_mfma_f32_16x16x32_bf16; K stages of 32; operands staged
-// global -> registers -> LDS in a two-stage ring (the next stage's loads are
-// in flight during the current stage's MFMAs; one barrier per stage).
+// blocks of v_mfma_f32_16x16x32_bf16; K stages of 32; operands move HBM ->
+// LDS with direct-to-LDS loads (global_load_lds_dwordx4, no register
+// staging) into a ring of 4 stages, issued 3 stages ahead; one barrier per
+// stage.
 //   K-contiguous operands (DGRAD): LDS [128 rows][32 K], the 16-byte chunk
 //     index XOR-ed with (row / 4) % 4 so that a fragment read (16 rows at one
 //     chunk per 16 lanes) touches every bank once; read with ds_read_b128.
@@ -133,12 +134,45 @@ __device__ __forceinline__ Loc locate_dgrad(const BwdArgs& p, int tile) {
   return L;
 }
 
+// 16 zero bytes: chunks outside the operand (rows, columns or K past the
+// end) are loaded from here, so they arrive in LDS as zeros
+__device__ __attribute__((aligned(16))) const bf16_t kZeroBwd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+
+// One direct-to-LDS load: 64 lanes x 16 bytes from their global addresses to
+// the 1 KiB of LDS at lds_addr (wave-uniform).  Inline assembly, so the
+// compiler's wait-count pass does not model it: the ring's waits are explicit
+// (wait_loads) and ordering against the LDS reads comes from s_barrier.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gptr), "s"(lds_addr)
+      : "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+constexpr int NS = 4;              // LDS ring: stages in flight
+constexpr int LPW = 4;             // loads per wave per stage (2 of A, 2 of B)
+
+// wait until at most `later` stages of this wave's loads are outstanding
+__device__ __forceinline__ void wait_loads(int later) {
+  if (later >= 2) wait_vm<2 * LPW>();
+  else if (later == 1) wait_vm<LPW>();
+  else wait_vm<0>();
+}
+
 template <int MODE, int EPI>
 __global__ __launch_bounds__(NT) void grouped_gemm_bwd_kernel(BwdArgs p) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds;
 
   // ---- the tile
   int e, m0, n0, row_end = 0, k_beg = 0, nk;
@@ -157,61 +191,89 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bwd_kernel(BwdArgs p) {
     const int n_t = local / p.tiles_m;
     m0 = (local - n_t * p.tiles_m) * BM;
     n0 = n_t * BN;
-    k_beg = p.offsets[e];
-    row_end = p.offsets[e + 1];  // end of the K range (rows of expert e)
-    k_beg = __builtin_amdgcn_readfirstlane(k_beg);
-    row_end = __builtin_amdgcn_readfirstlane(row_end);
+    k_beg = __builtin_amdgcn_readfirstlane(p.offsets[e]);
+    row_end = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);  // end of the K range
     nk = cdiv(row_end - k_beg, BK);
   }
 
-  // ---- loads of one stage into registers: 2 chunks of 16 B per operand per thread
-  u32x4 ra[2], rb[2];
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  auto load = [&](int s) {
+  // ---- this wave's loads: A and B loads j = 2 wave + q (q = 0, 1), each
+  // filling 1 KiB of its operand's stage.  K-contiguous: rows 16 j .. 16 j + 15
+  // x 4 chunks; K-outer: K rows 4 j .. 4 j + 3 x 16 chunks.  The LDS swizzle
+  // is applied on the global side: lane i fills physical chunk i of the 1 KiB
+  // and reads the logical chunk that belongs there.
+  int a_row[2], a_col[2], b_row[2], b_col[2];  // per load: row / column of the lane's chunk
+  const bf16_t* a_ptr[2];                       // DGRAD: the lane's A row
+  const bf16_t* b0_ptr[2];                      // DGRAD: the lane's B0 / B1 rows
+  const bf16_t* b1_ptr[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int j = 2 * wave + q;
+    if (MODE == DGRAD) {
+      const int row = 16 * j + (lane >> 2);
+      const int lc = (lane & 3) ^ ((row >> 2) & 3);
+      const int r = m0 + row, n = n0 + row;
+      a_col[q] = b_col[q] = lc * 8;           // K offset inside the stage
+      a_row[q] = r < row_end ? r : -1;
+      b_row[q] = n < p.N ? n : -1;
+      a_ptr[q] = p.A + (size_t)(r < row_end ? r : 0) * p.lda;
+      const size_t bn = (size_t)e * p.N + (n < p.N ? n : 0);
+      b0_ptr[q] = p.B0 + bn * p.K0;
+      b1_ptr[q] = p.B1 ? p.B1 + bn * p.K1 - p.K0 : nullptr;  // indexed by k >= K0
+    } else {
+      const int krow = 4 * j + (lane >> 4);
+      const int lc = (lane & 15) ^ ko_swz(krow);
+      a_row[q] = b_row[q] = krow;             // K row inside the stage
+      a_col[q] = m0 + lc * 8;
+      b_col[q] = n0 + lc * 8;
+      a_ptr[q] = b0_ptr[q] = b1_ptr[q] = nullptr;
+    }
+  }
+
+  // WGRAD with a row gather: this wave's 8 K rows of a stage (8 wave .. 8
+  // wave + 7) read A rows a_gather[r].  The indices are fetched with scalar
+  // loads (a uniform address through the constant address space) one stage
+  // before they are needed, so the vector-memory counter the ring waits on
+  // counts only the ring's own loads.
+  typedef __attribute__((address_space(4))) const int32_t* cidx_t;
+  const cidx_t gidx = (cidx_t)p.a_gather;
+  const bool gather = MODE == WGRAD && p.a_gather != nullptr;
+  int gi[8];
+  auto fetch_gather = [&](int st) {
+    const int base = k_beg + st * BK + 8 * wave, last = row_end - 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gi[i] = gidx[min(base + i, last)];
+  };
+
+  auto issue_stage = [&](int s) {
+    const uint32_t base = lds0 + (uint32_t)((s % NS) * STAGE);
     const int kk = s * BK;
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      const int c = tid + c2 * NT;
+    for (int q = 0; q < 2; ++q) {
+      const int j = 2 * wave + q;
+      const void* ga = kZeroBwd;
+      const void* gb = kZeroBwd;
       if (MODE == DGRAD) {
-        const int row = c >> 2, ch = c & 3;
-        const int k = kk + ch * 8;
-        // A: permuted row m0 + row
-        const int r = m0 + row;
-        ra[c2] = (r < row_end && k < p.K)
-                     ? *reinterpret_cast<const u32x4*>(p.A + (size_t)r * p.lda + k)
-                     : zero;
-        // B: weight row n0 + row of expert e; K range split over B0 / B1
-        const int n = n0 + row;
-        const bf16_t* src = nullptr;
-        if (n < p.N && k < p.K) {
-          src = k < p.K0 ? p.B0 + ((size_t)e * p.N + n) * p.K0 + k
-                         : p.B1 + ((size_t)e * p.N + n) * p.K1 + (k - p.K0);
-        }
-        rb[c2] = src ? *reinterpret_cast<const u32x4*>(src) : zero;
+        const int k = kk + a_col[q];
+        if (a_row[q] >= 0 && k < p.K) ga = a_ptr[q] + k;
+        if (b_row[q] >= 0 && k < p.K) gb = k < p.K0 ? b0_ptr[q] + k : b1_ptr[q] + k;
       } else {
-        const int krow = c >> 4, ch = c & 15;
-        const int r = k_beg + kk + krow;
-        const bool rin = r < row_end;
-        const int ca = m0 + ch * 8, cb = n0 + ch * 8;
-        const int src_row = rin ? (p.a_gather ? p.a_gather[r] : r) : 0;
-        ra[c2] = (rin && ca < p.M)
-                     ? *reinterpret_cast<const u32x4*>(p.A + (size_t)src_row * p.lda + ca)
-                     : zero;
-        rb[c2] = (rin && cb < p.N) ? *reinterpret_cast<const u32x4*>(p.B0 + (size_t)r * p.ldb + cb)
-                                   : zero;
+        const int r = k_beg + kk + a_row[q];
+        if (r < row_end) {
+          if (a_col[q] < p.M) {
+            int src = r;
+            if (gather) {
+              const int g = lane >> 4;  // K row 8 wave + 4 q + g
+              const int lo = g & 1 ? gi[4 * q + 1] : gi[4 * q];
+              const int hi = g & 1 ? gi[4 * q + 3] : gi[4 * q + 2];
+              src = g & 2 ? hi : lo;
+            }
+            ga = p.A + (size_t)src * p.lda + a_col[q];
+          }
+          if (b_col[q] < p.N) gb = p.B0 + (size_t)r * p.ldb + b_col[q];
+        }
       }
-    }
-  };
-  auto store = [&](int buf) {
-    char* base = lds + buf * STAGE;
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      const int c = tid + c2 * NT;
-      int off;
-      if (MODE == DGRAD) off = kc_off(c >> 2, c & 3);
-      else off = (c >> 4) * (BN * 2) + (((c & 15) ^ ko_swz(c >> 4)) << 4);
-      *reinterpret_cast<u32x4*>(base + off) = ra[c2];
-      *reinterpret_cast<u32x4*>(base + OP_BYTES + off) = rb[c2];
+      dma16(ga, base + (uint32_t)(j * 1024));
+      dma16(gb, base + (uint32_t)(OP_BYTES + j * 1024));
     }
   };
 
@@ -243,15 +305,23 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bwd_kernel(BwdArgs p) {
     }
   }
 
-  if (nk > 0) {
-    load(0);
-    store(0);
-    __syncthreads();
+  // prologue: stages 0 .. NS - 2
+  for (int s0 = 0; s0 < NS - 1 && s0 < nk; ++s0) {
+    if (gather) fetch_gather(s0);
+    issue_stage(s0);
   }
+  if (gather && NS - 1 < nk) fetch_gather(NS - 1);
   for (int s = 0; s < nk; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nk) load(s + 1);
-    const char* As = lds + buf * STAGE;
+    // stage s has landed once only stages s + 1 .. s + NS - 2 (if they exist)
+    // remain; the barrier makes every wave's loads of stage s visible and
+    // ends every wave's reads of slot (s - 1) % NS, which stage s + NS - 1 refills
+    wait_loads(min(NS - 2, nk - 1 - s));
+    __syncthreads();
+    if (s + NS - 1 < nk) {
+      issue_stage(s + NS - 1);
+      if (gather && s + NS < nk) fetch_gather(s + NS);
+    }
+    const char* As = lds + (s % NS) * STAGE;
     const char* Bs = As + OP_BYTES;
     bf16x8 fa[4], fb[4];
 #pragma unroll
@@ -273,8 +343,6 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bwd_kernel(BwdArgs p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    if (s + 1 < nk) store(buf ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue (accumulator layout: column lane % 16, rows 4 (lane / 16) + q)

@@ -380,6 +380,464 @@ __global__ __launch_bounds__(NT) void grouped_gemm_bwd_kernel(BwdArgs p) {
       }
 }
 
+// ------------------------------------------------------------------------
+// 256 x 256 tiles in ping-pong (the large-tile kernel).  8 waves in two
+// groups of 4: group X computes the tile's first 128 rows and issues the A
+// loads, group Y the last 128 rows and issues the B loads; each wave owns
+// 128 x 64 (8 x 4 blocks of 16 x 16).  The groups alternate between a
+// memory phase (fragment reads from LDS and the next stage's loads) and a
+// compute phase (64 MFMAs per K stage of 64), so one group's MFMAs overlap
+// the other's LDS traffic on every SIMD; MFMAs run at raised wave priority.
+// Against the 128 x 128 tile, a wave issues 4 MFMAs per 16-byte fragment
+// read instead of 2.  LDS: A ring of 2 stages, B ring of 3 (160 KiB).
+// ------------------------------------------------------------------------
+namespace bpp {
+constexpr int PBK = 64, RA = 2, RB = 3, MI = 8, NJ = 4, KS = PBK / 32, LD = 8;
+constexpr int SLOT = 256 * PBK * 2;          // one operand stage: 32 KiB
+constexpr int HALF = PBK * 128 * 2;          // K-outer: one 128-column half of a stage
+constexpr int B_RING = RA * SLOT;            // B slots follow the A slots
+constexpr int LDS_BYTES = (RA + RB) * SLOT;  // 160 KiB
+static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+
+// K-contiguous stage [256 rows][64 K]: 16-byte chunk index XOR-ed with
+// (row / 2) % 8 (a fragment read, 16 rows at one chunk, touches every bank
+// once); K-outer stage: two halves [64 K rows][128 columns] with the 32-byte
+// pair swizzle of the 128 x 128 kernel above.
+__device__ __forceinline__ lds_bf16x4* lds_at(uint32_t a) { return (lds_bf16x4*)(uintptr_t)a; }
+__device__ __forceinline__ int kc2_off(int row, int chunk) {
+  return row * (PBK * 2) + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_groups(int n) {
+  if (n >= 2) wait_vm<2 * N>();
+  else if (n == 1) wait_vm<N>();
+  else wait_vm<0>();
+}
+
+// The DGRAD tile: (expert, 256-row M tile, N panel), M fastest inside an
+// (expert, N panel).  An expert's c rows form ceil(c / 16) blocks of 16
+// dealt evenly to its ceil(c / 256) M tiles (the first ones take one more),
+// so the tiles sharing a panel take equal time and only the expert's last
+// block is padded.
+struct PTile {
+  int e, row0, row_end, nb, n_t;
+  bool ok;
+};
+__device__ __forceinline__ PTile locate_dgrad256(const BwdArgs& p, int tile) {
+  const int lane = threadIdx.x & 63;
+  int cnt[4], mt[4], off[4];
+  int lane_sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane * 4 + q;
+    int m = 0, o = 0;
+    if (e < p.E) {
+      o = p.offsets[e];
+      m = cdiv(p.offsets[e + 1] - o, 256);
+    }
+    mt[q] = m;
+    off[q] = o;
+    cnt[q] = m * p.tiles_n;
+    lane_sum += cnt[q];
+  }
+  int incl = lane_sum;
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) {
+    const int v = __shfl_up(incl, s);
+    if (lane >= s) incl += v;
+  }
+  int start = incl - lane_sum;
+  int he = -1, hs = 0, hm = 0, ho = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (tile >= start && tile < start + cnt[q]) {
+      he = lane * 4 + q;
+      hs = start;
+      hm = mt[q];
+      ho = off[q];
+    }
+    start += cnt[q];
+  }
+  const uint64_t hit = __ballot(he >= 0);
+  PTile L{};
+  L.ok = hit != 0;
+  if (!L.ok) return L;
+  const int src = __ffsll((unsigned long long)hit) - 1;
+  L.e = __shfl(he, src);
+  const int local = tile - __shfl(hs, src);
+  const int tmt = __shfl(hm, src);
+  const int toff = __shfl(ho, src);
+  L.n_t = local / tmt;
+  const int m_t = local - L.n_t * tmt;
+  const int c_e = p.offsets[L.e + 1] - toff;
+  const int nbe = cdiv(c_e, 16);
+  const int b_lo = nbe / tmt, b_rem = nbe - b_lo * tmt;
+  const int b0 = m_t * b_lo + min(m_t, b_rem);
+  const int b1 = b0 + b_lo + (m_t < b_rem ? 1 : 0);
+  L.nb = b1 - b0;
+  L.row0 = toff + 16 * b0;
+  L.row_end = min(toff + 16 * b1, toff + c_e);
+  return L;
+}
+}  // namespace bpp
+
+template <int MODE, int EPI>
+__global__ __launch_bounds__(512, 1) void grouped_gemm_bwd256_kernel(BwdArgs p) {
+  using namespace bpp;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool X = wave < 4;  // X: tile rows 0-127, issues the A loads; Y: rows 128-255, B loads
+  const int wg = wave & 3;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds;
+
+  // ---- the tile.  DGRAD tiles cost the same (K is fixed): XCD-aware, the
+  // grid a multiple of 8 and consecutive tiles, which share a weight panel,
+  // on the same XCD's L2.  WGRAD tiles cost their expert's rows: dealt
+  // round-robin (block order), so every XCD gets a share of every expert.
+  const int G = gridDim.x;
+  const int tile = MODE == DGRAD ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  int e, n0, m0 = 0, row0 = 0, row_end = 0, k_beg = 0, nk, my_nb, grow0, nb = 8, nbx = 4;
+  if (MODE == DGRAD) {
+    const PTile L = locate_dgrad256(p, tile);
+    if (!L.ok) return;
+    e = __builtin_amdgcn_readfirstlane(L.e);
+    row0 = __builtin_amdgcn_readfirstlane(L.row0);
+    row_end = __builtin_amdgcn_readfirstlane(L.row_end);
+    n0 = __builtin_amdgcn_readfirstlane(L.n_t) * 256;
+    nb = __builtin_amdgcn_readfirstlane(L.nb);
+    nbx = (nb + 1) >> 1;              // X takes the first ceil(nb / 2) blocks, Y the rest
+    my_nb = X ? nbx : nb - nbx;
+    grow0 = X ? 0 : 16 * nbx;
+    nk = cdiv(p.K, PBK);
+  } else {
+    const int per_e = p.tiles_m * p.tiles_n;
+    e = tile / per_e;
+    if (e >= p.E) return;
+    const int local = tile - e * per_e;
+    // the side with fewer panels runs fastest, so the tiles running side by
+    // side read the operand with more panels once
+    int m_t, n_t;
+    if (p.tiles_n <= p.tiles_m) {
+      m_t = local / p.tiles_n;
+      n_t = local - m_t * p.tiles_n;
+    } else {
+      n_t = local / p.tiles_m;
+      m_t = local - n_t * p.tiles_m;
+    }
+    m0 = m_t * 256;
+    n0 = n_t * 256;
+    grow0 = X ? 0 : 128;
+    my_nb = min(MI, max(0, cdiv(p.M - (m0 + grow0), 16)));
+    k_beg = __builtin_amdgcn_readfirstlane(p.offsets[e]);
+    row_end = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
+    nk = cdiv(row_end - k_beg, PBK);
+  }
+
+  // ---- this wave's 8 loads per stage (1 KiB each), q = 0..7
+  //   K-contiguous (DGRAD): LDS rows 64 wg + 8 q + lane / 8, chunk lane % 8;
+  //     A: LDS rows 0-127 are group X's blocks, 128-255 group Y's; B: LDS row
+  //     = column n0 + row of the output;
+  //   K-outer (WGRAD): half wg / 2, K rows 32 (wg % 2) + 4 q + lane / 16,
+  //     chunk lane % 16 (A half = 128 M columns, B half = 128 N columns).
+  // The swizzle is applied on the global side: lane i fills physical chunk
+  // i.  DGRAD: load q of a wave covers operand rows rb + 8 q + lane / 8
+  // (rb: the wave's first row; those with lane / 8 + 8 q < ld_lim exist),
+  // at element offset ld_lane + q ld_step from the tile's base.  Addresses
+  // are formed at issue.
+  const bf16_t* base0 = p.A;
+  const bf16_t* base1 = p.A;
+  int k_split = p.K;  // k < k_split reads base0, the rest base1
+  int ld_lane = 0, ld_lim = 0, ld_step = 0;
+  int ko_col = 0;  // WGRAD: the wave's first column
+  if (MODE == DGRAD) {
+    int rb, stride;
+    if (X) {
+      // LDS rows 0-127 (waves 0, 1): group X's blocks; 128-255: group Y's
+      base0 = base1 = p.A + (size_t)row0 * p.lda;
+      const int j0 = 64 * (wg & 1);
+      const int gnb = wg < 2 ? nbx : nb - nbx;
+      rb = (wg < 2 ? 0 : 16 * nbx) + j0;  // row inside the tile
+      ld_lim = min(16 * gnb - j0, row_end - row0 - rb);
+      stride = p.lda;
+    } else {
+      const size_t bn = (size_t)e * p.N + n0;
+      base0 = p.B0 + bn * p.K0;
+      base1 = p.B1 ? p.B1 + bn * p.K0 - p.K0 : base0;  // K1 = K0; indexed by k >= K0
+      k_split = p.K0;
+      rb = 64 * wg;
+      ld_lim = p.N - n0 - rb;
+      stride = p.K0;
+    }
+    ld_lane = (rb + (lane >> 3)) * stride;
+    ld_step = 8 * stride;
+  } else {
+    base0 = X ? p.A : p.B0;
+    ko_col = (X ? m0 : n0) + 128 * (wg >> 1);
+  }
+
+  // issue this wave's loads of stage kt into slot `slot` of its ring
+  auto issue = [&](int kt, int slot) {
+    const uint32_t dst0 = lds0 + (uint32_t)((X ? 0 : B_RING) + slot * SLOT + wg * LD * 1024);
+    const int kk = kt * PBK;
+#pragma unroll
+    for (int q = 0; q < LD; ++q) {
+      const void* ga = kZeroBwd;
+      if (MODE == DGRAD) {
+        // logical chunk of physical chunk lane % 8 in LDS row 64 wg + 8 q + lane / 8
+        const int k = kk + (((lane & 7) ^ (4 * (q & 1) + (lane >> 4))) << 3);
+        // B of layer 0 spans W_gate (k < K0) then W_up; A is one operand
+        if ((lane >> 3) + 8 * q < ld_lim && k < p.K)
+          ga = (k < k_split ? base0 : base1) + (ld_lane + q * ld_step) + k;
+      } else {
+        const int krow = 32 * (wg & 1) + 4 * q + (lane >> 4);
+        const int col = ko_col + (((lane & 15) ^ ko_swz(krow)) << 3);
+        const int r = k_beg + kk + krow;
+        if (r < row_end && col < (X ? p.M : p.N))
+          ga = base0 + (size_t)r * (X ? p.lda : p.ldb) + col;
+      }
+      dma16(ga, dst0 + (uint32_t)(q * 1024));
+    }
+  };
+
+  // ---- fragment read offsets (bytes inside a stage slot).  K step 1 is
+  // chunk + 4 (K-contiguous: the swizzle XORs it, so it has its own
+  // offset) or 32 K rows further (K-outer: + 8 KiB).  Blocks: K-contiguous
+  // + 16 rows = + 2 KiB; K-outer + 16 columns = the offset XOR 32 bytes
+  // (the swizzle XORs into the same bits).
+  const int l15 = lane & 15, g = lane >> 4;
+  int fa_off[2], fb_off[2];
+  if (MODE == DGRAD) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      fa_off[ks] = kc2_off((X ? 0 : 128) + l15, ks * 4 + g);
+      fb_off[ks] = kc2_off(wg * 64 + l15, ks * 4 + g);
+    }
+  } else {
+    const int kr = g * 8 + (l15 >> 2), c = (lane & 3) * 4;
+    // [0]: K rows kr, [1]: kr + 4 (the two halves of a transposed read)
+    fa_off[0] = (X ? 0 : HALF) + ko_off(kr, c);
+    fa_off[1] = (X ? 0 : HALF) + ko_off(kr + 4, c);
+    fb_off[0] = (wg >> 1) * HALF + ko_off(kr, (wg & 1) * 64 + c);
+    fb_off[1] = (wg >> 1) * HALF + ko_off(kr + 4, (wg & 1) * 64 + c);
+  }
+
+  f32x4 acc[MI][NJ];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < NJ; ++nj) acc[mi][nj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  bf16x8 fa[KS][MI], fb[KS][NJ];
+  // memory phase: issue this wave's loads of stage ld_kt into slot ld_slot
+  // (the slot of the stage before, which no wave reads any more), read the
+  // stage's fragments (A slot sa, B slot sb), wait for the reads.  Issuing
+  // first keeps the load addresses and the fragments from being live together.
+  auto memory = [&](int sa, int sb, int ld_kt, int ld_slot) {
+    if (ld_kt < nk) issue(ld_kt, ld_slot);
+    const char* As = lds + sa * SLOT;
+    const char* Bs = lds + B_RING + sb * SLOT;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int nj = 0; nj < NJ; ++nj) {
+        if (MODE == DGRAD) {
+          fb[ks][nj] = *reinterpret_cast<const bf16x8*>(Bs + fb_off[ks] + nj * 16 * PBK * 2);
+        } else {
+          // the slot base has no bits below 1 KiB: XOR-ing the sum equals
+          // XOR-ing the offset, and keeps the per-block addresses inside the
+          // loop (transient) instead of 24 hoisted registers
+          const uint32_t bk = lds0 + (uint32_t)(B_RING + sb * SLOT + ks * 8192);
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lds_at(((bk + fb_off[0]) ^ (32 * nj))));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lds_at(((bk + fb_off[1]) ^ (32 * nj))));
+          fb[ks][nj] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      }
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        if (mi < my_nb) {
+          if (MODE == DGRAD) {
+            fa[ks][mi] = *reinterpret_cast<const bf16x8*>(As + fa_off[ks] + mi * 16 * PBK * 2);
+          } else {
+            const uint32_t ak = lds0 + (uint32_t)(sa * SLOT + ks * 8192);
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lds_at(((ak + fa_off[0]) ^ (32 * mi))));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lds_at(((ak + fa_off[1]) ^ (32 * mi))));
+            fa[ks][mi] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  };
+  auto compute = [&]() {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      if (mi >= my_nb) break;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj)
+          acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ks][mi], fb[ks][nj],
+                                                               acc[mi][nj], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Both groups pass the same barriers: one after the prologue, two per stage.
+  if (X) {
+    // prologue: A(0) .. A(RA - 2); wait for A(0)
+    for (int s = 0; s < RA - 1 && s < nk; ++s) issue(s, s);
+    wait_groups<LD>(min(RA - 2, nk - 1));
+    __builtin_amdgcn_s_barrier();
+    int sa = 0, sb = 0;
+    for (int s = 0; s < nk; ++s) {
+      const int la = sa == 0 ? RA - 1 : sa - 1;  // slot of stage s - 1 = of stage s + RA - 1
+      memory(sa, sb, s + RA - 1, la);
+      __builtin_amdgcn_s_barrier();
+      compute();
+      wait_groups<LD>(min(RA - 2, nk - 2 - s));  // A(s + 1) has landed
+      __builtin_amdgcn_s_barrier();
+      sa = sa == RA - 1 ? 0 : sa + 1;
+      sb = sb == RB - 1 ? 0 : sb + 1;
+    }
+  } else {
+    for (int s = 0; s < RB - 1 && s < nk; ++s) issue(s, s);
+    wait_groups<LD>(min(RB - 2, nk - 1));
+    __builtin_amdgcn_s_barrier();
+    int sa = 0, sb = 0;
+    for (int s = 0; s < nk; ++s) {
+      if (s > 0) compute();  // stage s - 1
+      __builtin_amdgcn_s_barrier();
+      const int lb = sb == 0 ? RB - 1 : sb - 1;
+      memory(sa, sb, s + RB - 1, lb);
+      wait_groups<LD>(min(RB - 2, nk - 2 - s));  // B(s + 1) has landed
+      __builtin_amdgcn_s_barrier();
+      sa = sa == RA - 1 ? 0 : sa + 1;
+      sb = sb == RB - 1 ? 0 : sb + 1;
+    }
+    if (nk > 0) compute();
+  }
+
+  // ---- epilogue.  Both groups have passed their last barrier after their
+  // last LDS read, so the ring is free: each wave stages one 16-row block of
+  // its 16 x 64 outputs at a time in its own LDS area (accumulator layout:
+  // column lane % 16, rows 4 (lane / 16) + i) and reads it back by rows, so
+  // that every global access is 16 bytes per lane.
+  constexpr int SS = 64 + 4;  // staging row stride in floats
+  float* st = reinterpret_cast<float*>(lds + wave * 16 * SS * 4);
+  // an opaque copy of the lane index: the epilogue's lane-dependent
+  // offsets cannot be hoisted above the K loop, where every register counts
+  int lane_e = lane;
+  asm volatile("" : "+v"(lane_e));
+  const int col_l = lane_e & 15, row_l = (lane_e >> 4) * 4;
+  const int ncol0 = n0 + wg * 64;  // the wave's first output column
+  int rbase, rlim;                 // the wave's first row, its row bound
+  if (MODE == DGRAD) {
+    rbase = row0 + grow0;
+    rlim = min(row_end, row0 + grow0 + 16 * my_nb);
+  } else {
+    rbase = m0 + grow0;
+    rlim = p.M;
+  }
+  const bool add = EPI == EPI_F32 && p.accumulate;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    if (mi >= my_nb) break;
+    // the block's accumulators into the staging area
+#pragma unroll
+    for (int nj = 0; nj < NJ; ++nj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[(row_l + i) * SS + nj * 16 + col_l] = acc[mi][nj][i];
+    __builtin_amdgcn_wave_barrier();
+    if (EPI == EPI_SWIGLU_BWD) {
+      // 16 rows x 8 chunks of 8 columns: 2 per lane
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int idx = c2 * 64 + lane_e, r = idx >> 3, c = (idx & 7) * 8;
+        const int m = rbase + mi * 16 + r, n = ncol0 + c;
+        if (m < rlim && n < p.N) {
+          const size_t at = (size_t)m * p.N + n;
+          const u32x4 hv = *reinterpret_cast<const u32x4*>(p.h + at);
+          const u32x4 uv = *reinterpret_cast<const u32x4*>(p.u + at);
+          const f32x4 g0 = *reinterpret_cast<const f32x4*>(st + r * SS + c);
+          const f32x4 g1 = *reinterpret_cast<const f32x4*>(st + r * SS + c + 4);
+          u32x4 dh, du;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float dhj[2], duj[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const int el = 2 * j + t;
+              const float gv = el < 4 ? g0[el] : g1[el - 4];
+              const float h = __uint_as_float(t ? (hv[j] & 0xffff0000u) : (hv[j] << 16));
+              const float u = __uint_as_float(t ? (uv[j] & 0xffff0000u) : (uv[j] << 16));
+              const float sg = 1.f / (1.f + __expf(-h));
+              dhj[t] = gv * u * sg * (1.f + h * (1.f - sg));
+              duj[t] = gv * h * sg;
+            }
+            dh[j] = pack_bf16x2(dhj[0], dhj[1]);
+            du[j] = pack_bf16x2(duj[0], duj[1]);
+          }
+          bf16_t* d = p.dhu + (size_t)m * 2 * p.N + n;
+          *reinterpret_cast<u32x4*>(d) = dh;
+          *reinterpret_cast<u32x4*>(d + p.N) = du;
+        }
+      }
+    } else {
+      // 16 rows x 16 chunks of 4 floats: 4 per lane
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int idx = c4 * 64 + lane_e, r = idx >> 4, c = (idx & 15) * 4;
+        const int m = rbase + mi * 16 + r, n = ncol0 + c;
+        if (m < rlim && n < p.N) {
+          f32x4 v = *reinterpret_cast<const f32x4*>(st + r * SS + c);
+          float* o;
+          if (MODE == DGRAD)
+            o = p.out + (size_t)m * p.N + n;
+          else if (n < p.n_split)
+            o = p.w0 + ((size_t)e * p.M + m) * p.n_split + n;
+          else
+            o = p.w1 + ((size_t)e * p.M + m) * (p.N - p.n_split) + (n - p.n_split);
+          if (add) v += *reinterpret_cast<const f32x4*>(o);
+          *reinterpret_cast<f32x4*>(o) = v;
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+#ifndef MOE_BWD_PP
+#define MOE_BWD_PP 1
+#endif
+
+int pad8(long long g) { return (int)((g + 7) / 8 * 8); }
+
+// DGRAD / WGRAD launches of the ping-pong kernel (tile 256 x 256)
+// the ping-pong DGRAD keeps 32-bit element offsets of a tile's rows
+bool dgrad256_ok(const BwdArgs& p) {
+  return MOE_BWD_PP && 256ll * (p.lda > p.K0 ? p.lda : p.K0) < (1ll << 31) &&
+         (p.B1 == nullptr || p.K1 == p.K0);
+}
+
+template <int EPI>
+void launch_dgrad256(BwdArgs p, int rows, hipStream_t s) {
+  p.tiles_n = cdiv(p.N, 256);
+  // sum_e ceil(c_e / 256) <= floor((rows + E (256 - 1)) / 256)
+  const long long mt = ((long long)rows + (long long)p.E * 255) / 256;
+  const int grid = pad8(mt * p.tiles_n);
+  if (grid > 0)
+    hipLaunchKernelGGL((grouped_gemm_bwd256_kernel<DGRAD, EPI>), dim3(grid), dim3(512), 0, s, p);
+}
+void launch_wgrad256(BwdArgs q, hipStream_t s) {
+  q.tiles_m = cdiv(q.M, 256);
+  q.tiles_n = cdiv(q.N, 256);
+  const int grid = pad8((long long)q.E * q.tiles_m * q.tiles_n);
+  hipLaunchKernelGGL((grouped_gemm_bwd256_kernel<WGRAD, EPI_WGRAD>), dim3(grid), dim3(512), 0, s, q);
+}
+
 int dgrad_grid(int rows, int E, int tiles_n) {
   // sum_e ceil(c_e / BM) <= floor((rows + E (BM - 1)) / BM)
   const long long mt = ((long long)rows + (long long)E * (BM - 1)) / BM;
@@ -409,10 +867,14 @@ hipError_t launch_expert_down_backward(const void* dy_perm, const int32_t* offse
     p.h = static_cast<const bf16_t*>(h);
     p.u = static_cast<const bf16_t*>(u);
     p.dhu = static_cast<bf16_t*>(dhu);
-    const int grid = dgrad_grid(rows, E, p.tiles_n);
-    if (grid > 0)
-      hipLaunchKernelGGL((grouped_gemm_bwd_kernel<DGRAD, EPI_SWIGLU_BWD>), dim3(grid), dim3(NT), 0,
-                         s, p);
+    if (dgrad256_ok(p)) {
+      launch_dgrad256<EPI_SWIGLU_BWD>(p, rows, s);
+    } else {
+      const int grid = dgrad_grid(rows, E, p.tiles_n);
+      if (grid > 0)
+        hipLaunchKernelGGL((grouped_gemm_bwd_kernel<DGRAD, EPI_SWIGLU_BWD>), dim3(grid), dim3(NT),
+                           0, s, p);
+    }
   }
   // dW_down[e] = act_e^T dY_e (every expert, empty ones get zeros)
   BwdArgs q{};
@@ -428,8 +890,11 @@ hipError_t launch_expert_down_backward(const void* dy_perm, const int32_t* offse
   q.tiles_n = cdiv(d, BN);
   q.w0 = dW_down;
   q.n_split = d;
-  hipLaunchKernelGGL((grouped_gemm_bwd_kernel<WGRAD, EPI_WGRAD>),
-                     dim3((unsigned)(E * q.tiles_m * q.tiles_n)), dim3(NT), 0, s, q);
+  if (MOE_BWD_PP)
+    launch_wgrad256(q, s);
+  else
+    hipLaunchKernelGGL((grouped_gemm_bwd_kernel<WGRAD, EPI_WGRAD>),
+                       dim3((unsigned)(E * q.tiles_m * q.tiles_n)), dim3(NT), 0, s, q);
   return hipGetLastError();
 }
 
@@ -455,9 +920,14 @@ hipError_t launch_expert_up_backward(const void* x, const int32_t* gather_idx,
     p.tiles_n = cdiv(d, BN);
     p.out = dx_perm;
     p.accumulate = accumulate;
-    const int grid = dgrad_grid(rows, E, p.tiles_n);
-    if (grid > 0)
-      hipLaunchKernelGGL((grouped_gemm_bwd_kernel<DGRAD, EPI_F32>), dim3(grid), dim3(NT), 0, s, p);
+    if (dgrad256_ok(p)) {
+      launch_dgrad256<EPI_F32>(p, rows, s);
+    } else {
+      const int grid = dgrad_grid(rows, E, p.tiles_n);
+      if (grid > 0)
+        hipLaunchKernelGGL((grouped_gemm_bwd_kernel<DGRAD, EPI_F32>), dim3(grid), dim3(NT), 0, s,
+                           p);
+    }
   }
   // [dW_gate[e] | dW_up[e]] = x_perm_e^T [dH_e | dU_e]
   BwdArgs q{};
@@ -475,8 +945,11 @@ hipError_t launch_expert_up_backward(const void* x, const int32_t* gather_idx,
   q.w0 = dW_gate;
   q.w1 = dW_up;
   q.n_split = f;
-  hipLaunchKernelGGL((grouped_gemm_bwd_kernel<WGRAD, EPI_WGRAD>),
-                     dim3((unsigned)(E * q.tiles_m * q.tiles_n)), dim3(NT), 0, s, q);
+  if (MOE_BWD_PP && gather_idx == nullptr)  // the ping-pong WGRAD reads A rows in order
+    launch_wgrad256(q, s);
+  else
+    hipLaunchKernelGGL((grouped_gemm_bwd_kernel<WGRAD, EPI_WGRAD>),
+                       dim3((unsigned)(E * q.tiles_m * q.tiles_n)), dim3(NT), 0, s, q);
   return hipGetLastError();
 }
 

@@ -29,7 +29,11 @@ h = x W_gate and u = x W_up (routed and shared) and the router logits, and
         moe_linear_backward for the gate]
 
 leaving the gradients in ``self.grads`` (fp32 device tensors).  Training
-needs the deterministic separate combine (y_perm) and bf16 storage.
+needs the deterministic separate combine (y_perm) and bf16 storage, and
+always has moe_permute write x_perm: the layer-0 weight gradient reads the
+expert's token rows in order from it (the forward GEMMs still read x
+through the permutation on the "fast" path: x, T rows, stays in the
+last-level cache where x_perm, T k rows, may not).
 
 Shared experts: the n_s experts are stored side by side (gate/up projections
 [d, n_s*f_s], down projections [n_s*f_s, d]), so their sum is one SwiGLU FFN
@@ -78,7 +82,7 @@ class MoeLayer:
         self.perm_token = e(R, dt=i32)
         self.inv = e(T, k, dt=i32)
         self.perm_w = e(R)
-        self.x_perm = e(R, d, dt=act) if self.gather == "copy" else None
+        self.x_perm = e(R, d, dt=act) if (self.gather == "copy" or train) else None
         self.a = e(R, f, dt=act)
         self.y_perm = e(R, d) if self.comb == "separate" else None
         self.y = e(T, d)
@@ -259,7 +263,7 @@ class MoeLayer:
                                    t["W_down"], self.h, self.u, self.a, self.dhu, g["dW_down"],
                                    stream=stream)
         mk("expert_down_bwd")
-        L.moe_expert_up_backward(t["x"], self.perm_token, self.offsets, E, R, d, f, self.dtype,
+        L.moe_expert_up_backward(self.x_perm, None, self.offsets, E, R, d, f, self.dtype,
                                  t["W_gate"], t["W_up"], self.dhu, self.dx_perm, 0, g["dW_gate"],
                                  g["dW_up"], stream=stream)
         mk("expert_up_bwd")

@@ -185,3 +185,29 @@ def test_backward_empty_expert_gets_zero_weight_gradients(L):
             nz = torch.count_nonzero(g[k][e]).item()
             assert (nz == 0) == (counts[e] == 0), (k, e, counts[e], nz)
     check_grads(cfg, m, g, host(layer), dy.cpu().double().numpy())
+
+
+def test_expert_up_backward_gather_matches_permuted_copy(L):
+    """moe_expert_up_backward reading x through the permutation (the
+    128 x 128 kernel's row gather) and reading the permuted copy x_perm (the
+    256 x 256 ping-pong kernel) give the same gradients: the data gradient
+    bit for bit (the same kernel), the weight gradients to fp32 rounding
+    (both sum each expert's rows in row order, 64 at a time)."""
+    cfg = MID["mixtral"]
+    layer = make_layer(cfg, seed=6, device="cuda")
+    dy = torch.randn(cfg.T, cfg.d, generator=torch.Generator(device="cuda").manual_seed(8),
+                     device="cuda", dtype=torch.float32)
+    m, g = run_train(cfg, layer, dy)
+    R = cfg.T * cfg.k
+    dx_perm = torch.empty_like(m.dx_perm)
+    dWg = torch.empty_like(g["dW_gate"])
+    dWu = torch.empty_like(g["dW_up"])
+    L.moe_expert_up_backward(layer["x"], m.perm_token, m.offsets, cfg.E, R, cfg.d, cfg.f,
+                             L.MOE_BF16, layer["W_gate"], layer["W_up"], m.dhu, dx_perm, 0, dWg,
+                             dWu)
+    torch.cuda.synchronize()
+    assert torch.equal(dx_perm, m.dx_perm)
+    for got, ref in ((dWg, g["dW_gate"]), (dWu, g["dW_up"])):
+        err = (got - ref).abs().max().item() / ref.abs().max().item()
+        log(f"  gather vs copy weight gradient: max rel {err:.3e}")
+        assert err <= 1e-6

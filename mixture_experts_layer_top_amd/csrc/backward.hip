@@ -15,6 +15,8 @@
 // sums over token chunks added in chunk order): results are deterministic.
 #include "moe_internal.h"
 
+#include <algorithm>
+
 namespace moe {
 namespace {
 
@@ -148,30 +150,31 @@ __device__ __forceinline__ float ldx<bf16_t>(const bf16_t* p, size_t i) { return
 template <>
 __device__ __forceinline__ float ldx<float>(const float* p, size_t i) { return p[i]; }
 
-// dW partials: block (column chunk cb of 256 columns, token chunk tc of TC
+// dW partials: block (column chunk of 256 columns, token chunk tc of tc_len
 // tokens) writes part[tc][i][e] = sum_{t in chunk} x[t, i] G[t, e] for its
-// columns i and every e, 64 experts at a time; G rows are staged in LDS.
-constexpr int TC = 512;    // tokens per chunk
-constexpr int GR = 32;     // G rows per LDS stage
-template <typename XT>
+// columns i and every e, EB experts at a time (EB = the smallest of 8, 16,
+// 32, 64 covering E, so no lane of the accumulator is padding for E <= 64);
+// G rows are staged in LDS.
+constexpr int GR = 32;  // G rows per LDS stage
+template <typename XT, int EB>
 __global__ __launch_bounds__(kThreads) void xtg_partial_kernel(const XT* __restrict__ x,
                                                                const float* __restrict__ G, int T,
-                                                               int d, int E,
+                                                               int d, int E, int tc_len,
                                                                float* __restrict__ part) {
-  __shared__ float gs[GR][64];
+  __shared__ float gs[GR][EB];
   const int i = blockIdx.x * kThreads + threadIdx.x;
   const int tc = blockIdx.y;
-  const int t0 = tc * TC, t1 = min(T, t0 + TC);
-  for (int e0 = 0; e0 < E; e0 += 64) {
-    const int ne = min(64, E - e0);
-    float acc[64];
+  const int t0 = tc * tc_len, t1 = min(T, t0 + tc_len);
+  for (int e0 = 0; e0 < E; e0 += EB) {
+    const int ne = min(EB, E - e0);
+    float acc[EB];
 #pragma unroll
-    for (int e = 0; e < 64; ++e) acc[e] = 0.f;
+    for (int e = 0; e < EB; ++e) acc[e] = 0.f;
     for (int tb = t0; tb < t1; tb += GR) {
       const int nt = min(GR, t1 - tb);
       __syncthreads();
-      for (int q = threadIdx.x; q < GR * 64; q += kThreads) {
-        const int rr = q >> 6, e = q & 63;
+      for (int q = threadIdx.x; q < GR * EB; q += kThreads) {
+        const int rr = q / EB, e = q % EB;
         gs[rr][e] = (rr < nt && e < ne) ? G[(size_t)(tb + rr) * E + e0 + e] : 0.f;
       }
       __syncthreads();
@@ -179,16 +182,24 @@ __global__ __launch_bounds__(kThreads) void xtg_partial_kernel(const XT* __restr
         for (int rr = 0; rr < nt; ++rr) {
           const float xv = ldx<XT>(x, (size_t)(tb + rr) * d + i);
 #pragma unroll
-          for (int e = 0; e < 64; ++e) acc[e] = fmaf(xv, gs[rr][e], acc[e]);
+          for (int e = 0; e < EB; ++e) acc[e] = fmaf(xv, gs[rr][e], acc[e]);
         }
       }
     }
     if (i < d) {
 #pragma unroll
-      for (int e = 0; e < 64; ++e)
+      for (int e = 0; e < EB; ++e)
         if (e < ne) part[((size_t)tc * d + i) * E + e0 + e] = acc[e];
     }
   }
+}
+
+// tokens per partial chunk: about 1024 blocks over (column chunks x token
+// chunks), a multiple of GR between GR and 512
+int xtg_chunk(int T, int d) {
+  const long long want = (long long)T * cdiv(d, kThreads) / 1024;
+  const int tc = (int)std::min<long long>(512, std::max<long long>(GR, (want + GR - 1) / GR * GR));
+  return tc;
 }
 
 // dW[i, e] = sum over chunks (in order) of part[c][i][e]
@@ -219,39 +230,41 @@ __global__ __launch_bounds__(kThreads) void colsum_kernel(const float* __restric
   }
 }
 
-// dx[t, i] += sum_e G[t, e] W[i, e]: block = 16 tokens x 256 columns; each
-// thread keeps its column's W row (64 experts at a time) in registers.
-constexpr int DXT = 16;
-template <typename WT>
+// dx[t, i] += sum_e G[t, e] W[i, e]: block = DXT tokens x 256 columns; each
+// thread keeps its column's W row (EB experts at a time) in registers.
+constexpr int DXT = 64;
+template <typename WT, int EB>
 __global__ __launch_bounds__(kThreads) void dx_linear_kernel(const float* __restrict__ G,
                                                              const WT* __restrict__ W, int T,
                                                              int d, int E,
                                                              float* __restrict__ dx) {
-  __shared__ float gs[DXT][64];
+  __shared__ float gs[DXT][EB];
   const int i = blockIdx.x * kThreads + threadIdx.x;
   const int t0 = blockIdx.y * DXT;
   const int nt = min(DXT, T - t0);
   float acc[DXT];
 #pragma unroll
   for (int q = 0; q < DXT; ++q) acc[q] = 0.f;
-  for (int e0 = 0; e0 < E; e0 += 64) {
-    const int ne = min(64, E - e0);
-    float wr[64];
+  for (int e0 = 0; e0 < E; e0 += EB) {
+    const int ne = min(EB, E - e0);
+    float wr[EB];
 #pragma unroll
-    for (int e = 0; e < 64; ++e) wr[e] = (i < d && e < ne) ? ldx<WT>(W, (size_t)i * E + e0 + e) : 0.f;
+    for (int e = 0; e < EB; ++e) wr[e] = (i < d && e < ne) ? ldx<WT>(W, (size_t)i * E + e0 + e) : 0.f;
     __syncthreads();
-    for (int q = threadIdx.x; q < DXT * 64; q += kThreads) {
-      const int rr = q >> 6, e = q & 63;
+    for (int q = threadIdx.x; q < DXT * EB; q += kThreads) {
+      const int rr = q / EB, e = q % EB;
       gs[rr][e] = (rr < nt && e < ne) ? G[(size_t)(t0 + rr) * E + e0 + e] : 0.f;
     }
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < DXT; ++q)
 #pragma unroll
-      for (int e = 0; e < 64; ++e) acc[q] = fmaf(gs[q][e], wr[e], acc[q]);
+      for (int e = 0; e < EB; ++e) acc[q] = fmaf(gs[q][e], wr[e], acc[q]);
   }
   if (i < d)
-    for (int q = 0; q < nt; ++q) dx[(size_t)(t0 + q) * d + i] += acc[q];
+#pragma unroll
+    for (int q = 0; q < DXT; ++q)
+      if (q < nt) dx[(size_t)(t0 + q) * d + i] += acc[q];
 }
 
 template <int KS>
@@ -310,38 +323,46 @@ hipError_t launch_topk_weights_backward(const float* logits, const int32_t* idx,
 }
 
 size_t linear_backward_workspace_bytes(int T, int d, int E) {
-  const size_t nc = (size_t)cdiv(T, TC);
+  const size_t nc = (size_t)cdiv(T, xtg_chunk(T, d));
   return align_up(nc * (size_t)d * E * sizeof(float), 256);
+}
+
+template <typename XT, int EB>
+void launch_linear_bwd(const void* x, const void* W, const float* G, int T, int d, int E,
+                       float* dW, float* dx, void* ws, hipStream_t s) {
+  if (dW) {
+    const int tc = xtg_chunk(T, d);
+    const int nc = cdiv(T, tc);
+    float* part = static_cast<float*>(ws);
+    hipLaunchKernelGGL((xtg_partial_kernel<XT, EB>), dim3(cdiv(d, kThreads), nc), dim3(kThreads),
+                       0, s, static_cast<const XT*>(x), G, T, d, E, tc, part);
+    const size_t n = (size_t)d * E;
+    hipLaunchKernelGGL(sum_chunks_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, s, part, nc, n, dW);
+  }
+  if (dx)
+    hipLaunchKernelGGL((dx_linear_kernel<XT, EB>), dim3(cdiv(d, kThreads), cdiv(T, DXT)),
+                       dim3(kThreads), 0, s, G, static_cast<const XT*>(W), T, d, E, dx);
+}
+
+template <typename XT>
+void launch_linear_bwd_e(const void* x, const void* W, const float* G, int T, int d, int E,
+                         float* dW, float* dx, void* ws, hipStream_t s) {
+  if (E <= 8) launch_linear_bwd<XT, 8>(x, W, G, T, d, E, dW, dx, ws, s);
+  else if (E <= 16) launch_linear_bwd<XT, 16>(x, W, G, T, d, E, dW, dx, ws, s);
+  else if (E <= 32) launch_linear_bwd<XT, 32>(x, W, G, T, d, E, dW, dx, ws, s);
+  else launch_linear_bwd<XT, 64>(x, W, G, T, d, E, dW, dx, ws, s);
 }
 
 hipError_t launch_linear_backward(const void* x, const void* W, const float* G, int T, int d,
                                   int E, bool bf16, float* dW, float* db, float* dx, void* ws,
                                   hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int nc = cdiv(T, TC);
-  float* part = static_cast<float*>(ws);
-  if (dW) {
-    const dim3 grid(cdiv(d, kThreads), nc);
-    if (bf16)
-      hipLaunchKernelGGL(xtg_partial_kernel<bf16_t>, grid, dim3(kThreads), 0, s,
-                         static_cast<const bf16_t*>(x), G, T, d, E, part);
-    else
-      hipLaunchKernelGGL(xtg_partial_kernel<float>, grid, dim3(kThreads), 0, s,
-                         static_cast<const float*>(x), G, T, d, E, part);
-    const size_t n = (size_t)d * E;
-    hipLaunchKernelGGL(sum_chunks_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, s, part, nc, n, dW);
-  }
+  if (bf16)
+    launch_linear_bwd_e<bf16_t>(x, W, G, T, d, E, dW, dx, ws, s);
+  else
+    launch_linear_bwd_e<float>(x, W, G, T, d, E, dW, dx, ws, s);
   if (db) hipLaunchKernelGGL(colsum_kernel, dim3(E), dim3(kThreads), 0, s, G, T, E, db);
-  if (dx) {
-    const dim3 grid(cdiv(d, kThreads), cdiv(T, DXT));
-    if (bf16)
-      hipLaunchKernelGGL(dx_linear_kernel<bf16_t>, grid, dim3(kThreads), 0, s, G,
-                         static_cast<const bf16_t*>(W), T, d, E, dx);
-    else
-      hipLaunchKernelGGL(dx_linear_kernel<float>, grid, dim3(kThreads), 0, s, G,
-                         static_cast<const float*>(W), T, d, E, dx);
-  }
   return hipGetLastError();
 }
 

@@ -172,3 +172,143 @@ def backward(layer: dict, dy: np.ndarray, k: int, renorm: bool,
         out.update(dWs_gate=dWs_gate, dWs_up=dWs_up, dWs_down=dWs_down)
     out["dx"] = dx
     return out
+
+
+# --------------------------------------------------------------------------
+# selected gradient entries of a full-size layer, one by one
+# --------------------------------------------------------------------------
+
+
+def sampled_backward(layer: dict, dy: np.ndarray, k: int, renorm: bool, idx: np.ndarray,
+                     tokens, expert_cols=(), expert_rows=(), shared_cols=(), shared_rows=()):
+    """The same gradients as ``backward``, but only the entries asked for,
+    each computed from its own definition so that full-size layers stay
+    within reach of the CPU:
+
+    * per token t of ``tokens``: dx[t] (routed, router and shared parts),
+      dw[t], dL[t] and, for a gated shared expert, dz[t] = d<dy, y>/d(x_t . w_s);
+    * per (e, j) of ``expert_cols``: column j of dW_gate[e] and of dW_up[e]
+      (sums over expert e's rows of x^T dh[:, j], x^T du[:, j]);
+    * per (e, i) of ``expert_rows``: row i of dW_down[e] (a[:, i]^T dY);
+    * per column j of ``shared_cols`` / row i of ``shared_rows``: the same
+      for the side-by-side shared experts (every token is a row).
+
+    ``layer["W_gate"][e]`` etc. may be any per-expert accessor returning a
+    [d, f] / [f, d] array (one expert converted at a time); ``idx`` fixes
+    the selection (the weights are recomputed from the fp64 logits at it).
+    The formulas are those of the module docstring, steps 1-5.
+    """
+    x = layer["x"]
+    W_r = np.asarray(layer["W_r"], np.float64)
+    b = layer.get("b")
+    E = W_r.shape[1]
+    T, d = x.shape
+    tokens = np.asarray(tokens, np.int64)
+    nt = len(tokens)
+    f64 = lambda a: np.asarray(a, np.float64)  # noqa: E731
+
+    def weights_of(rows_t):
+        L = f64(x[rows_t]) @ W_r + (0.0 if b is None else f64(b))
+        return L, F.topk_weights(L, idx[rows_t], renorm)
+
+    out = {}
+    # -- tokens: routed experts, one expert's weights at a time
+    Lt, wt = weights_of(tokens)
+    xt = f64(x[tokens])
+    dyt = f64(dy[tokens])
+    dx = np.zeros((nt, d), np.float64)
+    dw = np.zeros((nt, k), np.float64)
+    for e in np.unique(idx[tokens]):
+        Wg, Wu, Wd = f64(layer["W_gate"][e]), f64(layer["W_up"][e]), f64(layer["W_down"][e])
+        for a_, j in zip(*np.nonzero(idx[tokens] == e)):
+            h = xt[a_] @ Wg
+            u = xt[a_] @ Wu
+            Y = (F.silu(h) * u) @ Wd
+            dw[a_, j] = dyt[a_] @ Y
+            da = (wt[a_, j] * dyt[a_]) @ Wd.T
+            dh = da * u * dsilu(h)
+            du = da * F.silu(h)
+            dx[a_] += Wg @ dh + Wu @ du
+    dL = topk_weights_backward(Lt, idx[tokens], renorm, dw)
+    dx += dL @ W_r.T
+    out.update(dw=dw, dL=dL)
+    # -- tokens: shared experts
+    shared = layer.get("Ws_gate") is not None
+    if shared:
+        Wsg, Wsu = f64(layer["Ws_gate"]), f64(layer["Ws_up"])
+        n_s, f_s, _ = layer["Ws_down"].shape
+        gated = layer.get("w_s") is not None
+        S = np.zeros((nt, d), np.float64)
+        parts = []
+        for s in range(n_s):
+            cols = slice(s * f_s, (s + 1) * f_s)
+            Wsd = f64(layer["Ws_down"][s])
+            h = xt @ Wsg[:, cols]
+            u = xt @ Wsu[:, cols]
+            S += (F.silu(h) * u) @ Wsd
+            parts.append((cols, Wsd, h, u))
+        if gated:
+            w_s = f64(layer["w_s"])
+            g = F.sigmoid(xt @ w_s)
+            dS = g[:, None] * dyt
+            dz = np.sum(dyt * S, axis=1) * g * (1.0 - g)
+            dx += dz[:, None] * w_s[None, :]
+            out["dz"] = dz
+        else:
+            dS = dyt
+        for cols, Wsd, h, u in parts:
+            da = dS @ Wsd.T
+            dx += (da * u * dsilu(h)) @ Wsg[:, cols].T + (da * F.silu(h)) @ Wsu[:, cols].T
+    out["dx"] = dx
+
+    # -- expert weight gradients: the expert's rows, then the asked columns / rows
+    want = sorted({e for e, _ in expert_cols} | {e for e, _ in expert_rows})
+    cols_out, rows_out = {}, {}
+    for e in want:
+        toks, slots = np.nonzero(idx == e)
+        if len(toks) == 0:
+            for (e2, j) in expert_cols:
+                if e2 == e:
+                    cols_out[(e, j)] = (np.zeros(d), np.zeros(d))
+            for (e2, i) in expert_rows:
+                if e2 == e:
+                    rows_out[(e, i)] = np.zeros(d)
+            continue
+        _, w_rows = weights_of(toks)
+        Xe = f64(x[toks])
+        dYe = w_rows[np.arange(len(toks)), slots][:, None] * f64(dy[toks])
+        Wg, Wu, Wd = layer["W_gate"][e], layer["W_up"][e], layer["W_down"][e]
+        for (e2, j) in expert_cols:
+            if e2 != e:
+                continue
+            h = Xe @ f64(Wg[:, j])
+            u = Xe @ f64(Wu[:, j])
+            da = dYe @ f64(Wd[j, :])
+            cols_out[(e, j)] = (Xe.T @ (da * u * dsilu(h)), Xe.T @ (da * F.silu(h)))
+        for (e2, i) in expert_rows:
+            if e2 != e:
+                continue
+            a = F.silu(Xe @ f64(Wg[:, i])) * (Xe @ f64(Wu[:, i]))
+            rows_out[(e, i)] = a @ dYe
+    out.update(expert_cols=cols_out, expert_rows=rows_out)
+
+    # -- shared weight gradients: every token is a row
+    if shared and (shared_cols or shared_rows):
+        X = f64(x)
+        DY = f64(dy)
+        if layer.get("w_s") is not None:
+            DY = F.sigmoid(X @ f64(layer["w_s"]))[:, None] * DY
+        Wsg, Wsu = f64(layer["Ws_gate"]), f64(layer["Ws_up"])
+        n_s, f_s, _ = layer["Ws_down"].shape
+        scol, srow = {}, {}
+        for j in shared_cols:
+            s, jj = divmod(j, f_s)
+            h = X @ Wsg[:, j]
+            u = X @ Wsu[:, j]
+            da = DY @ f64(layer["Ws_down"][s][jj, :])
+            scol[j] = (X.T @ (da * u * dsilu(h)), X.T @ (da * F.silu(h)))
+        for i in shared_rows:
+            a = F.silu(X @ Wsg[:, i]) * (X @ Wsu[:, i])
+            srow[i] = a @ DY
+        out.update(shared_cols=scol, shared_rows=srow)
+    return out

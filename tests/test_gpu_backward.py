@@ -240,3 +240,120 @@ def test_linear_backward_any_expert_count(L, E):
         log(f"  linear backward E={E} {name}: normwise {nrm:.2e}, c {c:.2e}")
         # fp32 sums of at most T bf16 x fp32 products: far inside 1e-5
         assert nrm <= 1e-5 and c <= 1e-4, (name, nrm, c)
+
+
+# ---------------------------------------------------------------- full size
+
+
+class _PerExpert:
+    """fp64 view of a [E, a, b] device tensor, converted one expert at a time."""
+
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, e):
+        return self.t[e].to("cpu", torch.float64).numpy()
+
+
+def _host_lazy(layer):
+    return {k_: (None if v is None else (_PerExpert(v) if v.dim() == 3 else
+                                         v.to("cpu", torch.float64).numpy()))
+            for k_, v in layer.items()}
+
+
+def _bars(name, got, ref, fails):
+    nrm, mx, c = errors(got, ref)
+    log(f"  {name}: normwise {nrm:.3e}, max/rms {mx:.3e}, c {c:.3e}")
+    if nrm > NORM_TAU or c > EL_TAU:
+        fails.append(f"{name}: normwise {nrm:.3e}, c {c:.3e}")
+
+
+@pytest.mark.parametrize("name", ["mixtral", "qwen2moe", "mixtral_skew", "deepseek"])
+def test_backward_full_size_sampled(L, name):
+    """The training step at full size, in the launch configuration the
+    benchmark times, checked on entries the oracle computes one by one: dx,
+    dw, dL and the shared gate's dz of sampled tokens; columns of dW_gate and
+    dW_up and rows of dW_down of the most- and least-loaded experts and a
+    random one; columns and rows of the shared experts' weight gradients.
+    The whole-tensor reductions over every token (dW_r = x^T dL, db, dw_s =
+    x^T dz) and the top-k weights backward on every token are checked
+    against their fp64 definitions applied to the GPU's own dL, dz and dw
+    (which the samples tie to the oracle)."""
+    cfg = CONFIGS[name]
+    log(f"[bwd full] {name} T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k}")
+    layer = make_layer(cfg, seed=0, device="cuda")
+    dy = torch.randn(cfg.T, cfg.d, generator=torch.Generator(device="cuda").manual_seed(11),
+                     device="cuda", dtype=torch.float32)
+    m, g = run_train(cfg, layer, dy)
+    h = _host_lazy(layer)
+    dyh = dy.cpu().double().numpy()
+    idx = m.idx.cpu().numpy().astype(np.int64)
+    counts = m.counts.cpu().numpy()
+    rng = np.random.default_rng(7)
+    nonempty = np.nonzero(counts > 0)[0]
+    e_big = int(np.argmax(counts))
+    e_small = int(nonempty[np.argmin(counts[nonempty])])
+    experts = sorted({e_big, e_small, int(rng.choice(nonempty))})
+    toks = {0, cfg.T - 1} | set(rng.choice(cfg.T, 6, replace=False).tolist())
+    toks |= set(np.nonzero(np.any(idx == e_small, axis=1))[0][:2].tolist())
+    toks = np.array(sorted(toks))
+    js = [0, cfg.f - 1, int(rng.integers(cfg.f))]
+    ec = [(e, j) for e in experts for j in js]
+    fs_all = cfg.n_shared * cfg.f_shared if cfg.n_shared else 0
+    sj = [0, fs_all - 1, int(rng.integers(fs_all))] if fs_all else []
+    ref = B.sampled_backward(h, dyh, cfg.k, cfg.renorm, idx, toks, ec, ec, sj, sj)
+    log(f"  oracle done: {len(toks)} tokens, experts {experts} (counts {counts[experts].tolist()})")
+    fails = []
+    _bars("dx[sampled tokens]", g["dx"].cpu().double().numpy()[toks], ref["dx"], fails)
+    dw_g = m.dw.cpu().double().numpy()
+    _bars("dw[sampled tokens]", dw_g[toks], ref["dw"], fails)
+    dL_g = m.dL.cpu().double().numpy()
+    # dL = w (dw - <w, dw>) (or the full-softmax form): an error eps in dw
+    # moves an entry by at most 2 eps max|dw| (w, p <= 1)
+    lim = 2 * NORM_TAU * np.max(np.abs(ref["dw"]), axis=1)
+    worst = float(np.max(np.max(np.abs(dL_g[toks] - ref["dL"]), axis=1) / lim))
+    log(f"  dL[sampled tokens]: max |d| / (2 tau max|dw|) = {worst:.3e}")
+    if worst > 1.0:
+        fails.append(f"dL: {worst:.3e}")
+    for e, j in ec:
+        _bars(f"dW_gate[{e}][:, {j}]", g["dW_gate"][e][:, j].cpu().double().numpy(),
+              ref["expert_cols"][(e, j)][0], fails)
+        _bars(f"dW_up[{e}][:, {j}]", g["dW_up"][e][:, j].cpu().double().numpy(),
+              ref["expert_cols"][(e, j)][1], fails)
+        _bars(f"dW_down[{e}][{j}, :]", g["dW_down"][e][j, :].cpu().double().numpy(),
+              ref["expert_rows"][(e, j)], fails)
+    for j in sj:
+        _bars(f"dWs_gate[:, {j}]", g["dWs_gate"][:, j].cpu().double().numpy(),
+              ref["shared_cols"][j][0], fails)
+        _bars(f"dWs_up[:, {j}]", g["dWs_up"][:, j].cpu().double().numpy(),
+              ref["shared_cols"][j][1], fails)
+        _bars(f"dWs_down[{j}, :]", g["dWs_down"][j, :].cpu().double().numpy(),
+              ref["shared_rows"][j], fails)
+    # reductions over every token, on the GPU's own inputs (exact operands)
+    x = h["x"]
+    L32 = m.logits.cpu().double().numpy()
+    dL_def = B.topk_weights_backward(L32, idx, cfg.renorm, dw_g)
+    scale = np.max(np.abs(dw_g), axis=1, keepdims=True) + 1e-30
+    tk = float(np.max(np.abs(dL_g - dL_def) / scale))
+    log(f"  top-k weights backward, every token: max |d| / max|dw| = {tk:.3e}")
+    if tk > 1e-5:
+        fails.append(f"top-k weights backward: {tk:.3e}")
+    nrm, _, c = errors(g["dW_r"].cpu().double().numpy(), x.T @ dL_g)
+    log(f"  dW_r vs x^T dL: normwise {nrm:.3e}, c {c:.3e}")
+    if nrm > 1e-5 or c > 1e-4:
+        fails.append(f"dW_r: {nrm:.3e} {c:.3e}")
+    if g.get("db") is not None:
+        r = float(np.max(np.abs(g["db"].cpu().double().numpy() - dL_g.sum(0)) /
+                         (np.abs(dL_g).sum(0) + 1e-30)))
+        log(f"  db vs sum_t dL: {r:.3e}")
+        if r > 1e-5:
+            fails.append(f"db: {r:.3e}")
+    if "dz" in ref:
+        dz_g = m.dgl.cpu().double().numpy().reshape(-1)
+        _bars("dz[sampled tokens]", dz_g[toks], ref["dz"], fails)
+        nrm, _, c = errors(g["dw_s"].cpu().double().numpy().reshape(-1), x.T @ dz_g)
+        log(f"  dw_s vs x^T dz: normwise {nrm:.3e}, c {c:.3e}")
+        if nrm > 1e-5 or c > 1e-4:
+            fails.append(f"dw_s: {nrm:.3e} {c:.3e}")
+    assert not fails, fails

@@ -190,3 +190,38 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     monkeypatch.setattr(B, attr, fn)
     with pytest.raises(AssertionError):
         check()
+
+
+@pytest.mark.parametrize("name", ["mixtral", "qwen2moe", "deepseek"])
+def test_sampled_entries_equal_the_full_backward(name):
+    """The one-by-one entries used to check full-size layers (dx, dw, dL of
+    chosen tokens, columns of dW_gate/dW_up and rows of dW_down of chosen
+    experts, the shared experts' columns and rows) equal the full backward's."""
+    base = CONFIGS[name]
+    kw = {"f_shared": 16} if base.n_shared else {}
+    cfg = base.shrink(T=64, d=32, f=24, **kw)
+    lay = to_f64(make_layer(cfg, seed=1))
+    dy = np.random.default_rng(0).standard_normal((cfg.T, cfg.d))
+    ref = B.backward(lay, dy, cfg.k, cfg.renorm)
+    idx = O.forward(lay, cfg.k, cfg.renorm)["idx"]
+    toks = [0, 7, cfg.T - 1]
+    ec = [(e, j) for e in range(cfg.E) for j in (0, cfg.f - 1)]
+    er = [(e, i) for e in range(cfg.E) for i in (0, 5)]
+    fs_all = cfg.n_shared * cfg.f_shared if cfg.n_shared else 0
+    sc = [0, fs_all - 1] if fs_all else []
+    got = B.sampled_backward(lay, dy, cfg.k, cfg.renorm, idx, toks, ec, er, sc, sc)
+    tol = dict(rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got["dx"], ref["dx"][toks], **tol)
+    np.testing.assert_allclose(got["dw"], ref["dw"][toks], **tol)
+    np.testing.assert_allclose(got["dL"], ref["dL"][toks], **tol)
+    for (e, j), (g1, g2) in got["expert_cols"].items():
+        np.testing.assert_allclose(g1, ref["dW_gate"][e][:, j], **tol)
+        np.testing.assert_allclose(g2, ref["dW_up"][e][:, j], **tol)
+    for (e, i), r in got["expert_rows"].items():
+        np.testing.assert_allclose(r, ref["dW_down"][e][i, :], **tol)
+    for j, (g1, g2) in got.get("shared_cols", {}).items():
+        np.testing.assert_allclose(g1, ref["dWs_gate"][:, j], **tol)
+        np.testing.assert_allclose(g2, ref["dWs_up"][:, j], **tol)
+    for i, r in got.get("shared_rows", {}).items():
+        s, ii = divmod(i, cfg.f_shared)
+        np.testing.assert_allclose(r, ref["dWs_down"][s][ii, :], **tol)

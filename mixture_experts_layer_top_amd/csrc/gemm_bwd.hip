@@ -482,7 +482,29 @@ __device__ __forceinline__ PTile locate_dgrad256(const BwdArgs& p, int tile) {
 }
 }  // namespace bpp
 
-template <int MODE, int EPI>
+// One direct-to-LDS load with a scalar base: lane i reads 16 bytes at
+// base + voff_i and writes LDS bytes lds_addr + 16 i.
+__device__ __forceinline__ void dma16_s(uint32_t voff, const void* base, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(lds_addr)
+      : "m0");
+}
+
+__device__ __forceinline__ const char* uniform_ptr(const void* q) {
+  const uint64_t v = (uint64_t)(uintptr_t)q;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// FASTK (DGRAD with K and K0 multiples of 64): no stage straddles the end of
+// K or the W_gate / W_up boundary, so every load of a stage shares one scalar
+// base and each lane keeps one 32-bit byte offset per load (rows past the
+// operand read the tile's first row; their results are never stored).
+template <int MODE, int EPI, bool FASTK = false>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_bwd256_kernel(BwdArgs p) {
   using namespace bpp;
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
@@ -577,10 +599,26 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bwd256_kernel(BwdArgs p) 
     ko_col = (X ? m0 : n0) + 128 * (wg >> 1);
   }
 
+  uint32_t fk_off[FASTK ? LD : 1];  // FASTK: byte offsets from the stage's base
+  if (FASTK) {
+#pragma unroll
+    for (int q = 0; q < LD; ++q) {
+      const bool ok = (lane >> 3) + 8 * q < ld_lim;
+      const int kc = ((lane & 7) ^ (4 * (q & 1) + (lane >> 4))) << 3;
+      fk_off[q] = (uint32_t)((ok ? ld_lane + q * ld_step : 0) + kc) * 2u;
+    }
+  }
+
   // issue this wave's loads of stage kt into slot `slot` of its ring
   auto issue = [&](int kt, int slot) {
     const uint32_t dst0 = lds0 + (uint32_t)((X ? 0 : B_RING) + slot * SLOT + wg * LD * 1024);
     const int kk = kt * PBK;
+    if (FASTK) {
+      const char* sb = uniform_ptr(kk < k_split ? (const void*)(base0 + kk) : (const void*)(base1 + kk));
+#pragma unroll
+      for (int q = 0; q < LD; ++q) dma16_s(fk_off[q], sb, dst0 + (uint32_t)(q * 1024));
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < LD; ++q) {
       const void* ga = kZeroBwd;
@@ -822,13 +860,21 @@ bool dgrad256_ok(const BwdArgs& p) {
          (p.B1 == nullptr || p.K1 == p.K0);
 }
 
+#ifndef MOE_BWD_FASTK
+#define MOE_BWD_FASTK 1
+#endif
+
 template <int EPI>
 void launch_dgrad256(BwdArgs p, int rows, hipStream_t s) {
   p.tiles_n = cdiv(p.N, 256);
   // sum_e ceil(c_e / 256) <= floor((rows + E (256 - 1)) / 256)
   const long long mt = ((long long)rows + (long long)p.E * 255) / 256;
   const int grid = pad8(mt * p.tiles_n);
-  if (grid > 0)
+  if (grid <= 0) return;
+  if (MOE_BWD_FASTK && p.K % 64 == 0 && p.K0 % 64 == 0)
+    hipLaunchKernelGGL((grouped_gemm_bwd256_kernel<DGRAD, EPI, true>), dim3(grid), dim3(512), 0, s,
+                       p);
+  else
     hipLaunchKernelGGL((grouped_gemm_bwd256_kernel<DGRAD, EPI>), dim3(grid), dim3(512), 0, s, p);
 }
 void launch_wgrad256(BwdArgs q, hipStream_t s) {

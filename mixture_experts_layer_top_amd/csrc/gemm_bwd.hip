@@ -600,12 +600,23 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bwd256_kernel(BwdArgs p) 
   }
 
   uint32_t fk_off[FASTK ? LD : 1];  // FASTK: byte offsets from the stage's base
-  if (FASTK) {
+  if (FASTK && MODE == DGRAD) {
 #pragma unroll
     for (int q = 0; q < LD; ++q) {
       const bool ok = (lane >> 3) + 8 * q < ld_lim;
       const int kc = ((lane & 7) ^ (4 * (q & 1) + (lane >> 4))) << 3;
       fk_off[q] = (uint32_t)((ok ? ld_lane + q * ld_step : 0) + kc) * 2u;
+    }
+  } else if (FASTK) {
+    // WGRAD: K row 32 (wg % 2) + 4 q + lane / 16 of a full stage, from the
+    // stage's base row; columns past the operand read column 0 (unstored)
+    const int ld = X ? p.lda : p.ldb, lim = X ? p.M : p.N;
+#pragma unroll
+    for (int q = 0; q < LD; ++q) {
+      const int kr = 4 * q + (lane >> 4);
+      int col = ko_col + (((lane & 15) ^ ko_swz(kr)) << 3);
+      if (col >= lim) col = 0;
+      fk_off[q] = (uint32_t)(kr * ld + col) * 2u;
     }
   }
 
@@ -613,8 +624,14 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bwd256_kernel(BwdArgs p) 
   auto issue = [&](int kt, int slot) {
     const uint32_t dst0 = lds0 + (uint32_t)((X ? 0 : B_RING) + slot * SLOT + wg * LD * 1024);
     const int kk = kt * PBK;
-    if (FASTK) {
+    if (FASTK && MODE == DGRAD) {
       const char* sb = uniform_ptr(kk < k_split ? (const void*)(base0 + kk) : (const void*)(base1 + kk));
+#pragma unroll
+      for (int q = 0; q < LD; ++q) dma16_s(fk_off[q], sb, dst0 + (uint32_t)(q * 1024));
+      return;
+    }
+    if (FASTK && k_beg + kk + PBK <= row_end) {  // WGRAD, a stage of the expert's rows only
+      const char* sb = uniform_ptr(base0 + (size_t)(k_beg + kk + 32 * (wg & 1)) * (X ? p.lda : p.ldb));
 #pragma unroll
       for (int q = 0; q < LD; ++q) dma16_s(fk_off[q], sb, dst0 + (uint32_t)(q * 1024));
       return;
@@ -881,7 +898,13 @@ void launch_wgrad256(BwdArgs q, hipStream_t s) {
   q.tiles_m = cdiv(q.M, 256);
   q.tiles_n = cdiv(q.N, 256);
   const int grid = pad8((long long)q.E * q.tiles_m * q.tiles_n);
-  hipLaunchKernelGGL((grouped_gemm_bwd256_kernel<WGRAD, EPI_WGRAD>), dim3(grid), dim3(512), 0, s, q);
+  // the scalar-base form keeps 32-bit offsets within 32 rows of A and B
+  if (MOE_BWD_FASTK && 32ll * (q.lda > q.ldb ? q.lda : q.ldb) * 2 < (1ll << 32))
+    hipLaunchKernelGGL((grouped_gemm_bwd256_kernel<WGRAD, EPI_WGRAD, true>), dim3(grid), dim3(512), 0,
+                       s, q);
+  else
+    hipLaunchKernelGGL((grouped_gemm_bwd256_kernel<WGRAD, EPI_WGRAD>), dim3(grid), dim3(512), 0, s,
+                       q);
 }
 
 int dgrad_grid(int rows, int E, int tiles_n) {

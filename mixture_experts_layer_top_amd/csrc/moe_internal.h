@@ -45,6 +45,8 @@ __host__ __device__ __forceinline__ size_t align_up(size_t a, size_t b) { return
 // host launchers (each returns a hipError_t of the launch)
 // ------------------------------------------------------------------------
 
+int device_cu_count();  // compute units of the current device
+
 size_t route_workspace_bytes(int d, int E, bool bf16);
 hipError_t launch_route(const void* x, const void* W_r, const float* bias, int T, int d, int E,
                         int k, bool renorm, bool bf16, int32_t* idx, float* w, float* logits_out,

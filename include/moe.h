@@ -296,6 +296,9 @@ int moe_topk_weights_backward(const float* logits, const int32_t* topk_idx, cons
  * Arguments: x [T, d] (dtype), W [d, E] (dtype), G [T, E] fp32, dW [d, E]
  *   fp32 out or NULL, db [E] fp32 out or NULL, dx [T, d] fp32 in/out or NULL;
  *   workspace of moe_linear_backward_workspace_size(T, d, E) bytes (when dW).
+ * Requirements: 1 <= E <= 256; d a multiple of 8 and x, dx 16-byte aligned
+ * (MOE_ERR_UNSUPPORTED otherwise: x rows and dx rows move as 16-byte vectors).
+ * Every sum runs in a fixed order: the results are deterministic.
  */
 size_t moe_linear_backward_workspace_size(int T, int d, int E);
 int moe_linear_backward(const void* x, const void* W, const float* G, int T, int d, int E,

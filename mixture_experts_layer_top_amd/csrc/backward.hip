@@ -150,26 +150,46 @@ __device__ __forceinline__ float ldx<bf16_t>(const bf16_t* p, size_t i) { return
 template <>
 __device__ __forceinline__ float ldx<float>(const float* p, size_t i) { return p[i]; }
 
-// dW partials: block (column chunk of 256 columns, token chunk tc of tc_len
-// tokens) writes part[tc][i][e] = sum_{t in chunk} x[t, i] G[t, e] for its
-// columns i and every e, EB experts at a time (EB = the smallest of 8, 16,
-// 32, 64 covering E, so no lane of the accumulator is padding for E <= 64);
-// G rows are staged in LDS.
+// dW partials (register-blocked fp32): a block takes EB experts, XCB
+// columns (512, or 256 for EB = 64) and token chunk tc of tc_len tokens.
+// Thread (token slice ts, expert group eg, column group cg) accumulates an
+// 8 x 8 block over the rows ts, ts + TS, ... of each staged group of rows,
+//   acc[c][j] += x[t, c0 + 8 cg + c] G[t, e0 + 8 eg + j],
+// and the TS slices are then added in slice order through LDS (TS = 4, 2
+// for EB = 8, 16: the same partial sums with more threads in flight), and
+// written to part[tc][column][expert].  x row segments (16 bytes, coalesced
+// over the column groups) come from global memory, 8 rows in flight; G rows
+// are staged in LDS 32 at a time and read as broadcasts.  EB: the smallest
+// of 8, 16, 32, 64 covering E (E > 64 loops over 64-expert chunks).
 constexpr int GR = 32;  // G rows per LDS stage
+template <int EB>
+struct XtgShape {
+  static constexpr int EG = EB / 8;                   // expert groups
+  static constexpr int TS = EB == 8 ? 4 : EB == 16 ? 2 : 1;  // token slices
+  static constexpr int CG = kThreads / (EG * TS);     // column groups
+  static constexpr int CB = 8 * CG;                   // columns per block
+};
 template <typename XT, int EB>
 __global__ __launch_bounds__(kThreads) void xtg_partial_kernel(const XT* __restrict__ x,
                                                                const float* __restrict__ G, int T,
                                                                int d, int E, int tc_len,
                                                                float* __restrict__ part) {
-  __shared__ float gs[GR][EB];
-  const int i = blockIdx.x * kThreads + threadIdx.x;
+  using S = XtgShape<EB>;
+  constexpr int EG = S::EG, TS = S::TS, CG = S::CG, CB = S::CB;
+  __shared__ __attribute__((aligned(16))) float gs[GR][EB];
+  __shared__ __attribute__((aligned(16))) float red[TS > 1 ? (TS - 1) * CG * EG * 64 : 1];
+  const int cg = threadIdx.x % CG, eg = (threadIdx.x / CG) % EG, ts = threadIdx.x / (CG * EG);
+  const int col = blockIdx.x * CB + 8 * cg;
+  const bool col_ok = col < d;  // d is a multiple of 8: a column group is whole or absent
   const int tc = blockIdx.y;
   const int t0 = tc * tc_len, t1 = min(T, t0 + tc_len);
   for (int e0 = 0; e0 < E; e0 += EB) {
     const int ne = min(EB, E - e0);
-    float acc[EB];
+    float acc[8][8];
 #pragma unroll
-    for (int e = 0; e < EB; ++e) acc[e] = 0.f;
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[c][j] = 0.f;
     for (int tb = t0; tb < t1; tb += GR) {
       const int nt = min(GR, t1 - tb);
       __syncthreads();
@@ -178,28 +198,89 @@ __global__ __launch_bounds__(kThreads) void xtg_partial_kernel(const XT* __restr
         gs[rr][e] = (rr < nt && e < ne) ? G[(size_t)(tb + rr) * E + e0 + e] : 0.f;
       }
       __syncthreads();
-      if (i < d) {
-        for (int rr = 0; rr < nt; ++rr) {
-          const float xv = ldx<XT>(x, (size_t)(tb + rr) * d + i);
+      if (col_ok) {
+        // this slice's rows ts, ts + TS, ...: 8 of them loaded before their
+        // arithmetic (rows past the stage read row tb, and are not used)
+        for (int rb = ts; rb < nt; rb += 8 * TS) {
+          u32x4 xr[8][sizeof(XT) == 2 ? 1 : 2];
 #pragma unroll
-          for (int e = 0; e < EB; ++e) acc[e] = fmaf(xv, gs[rr][e], acc[e]);
+          for (int u = 0; u < 8; ++u) {
+            const int rr = rb + u * TS < nt ? rb + u * TS : 0;
+            const XT* xp = x + (size_t)(tb + rr) * d + col;
+            xr[u][0] = *reinterpret_cast<const u32x4*>(xp);
+            if (sizeof(XT) == 4) xr[u][sizeof(XT) == 2 ? 0 : 1] = *reinterpret_cast<const u32x4*>(xp + 4);
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int rr = rb + u * TS;
+            if (rr >= nt) break;
+            float xv[8];
+            if (sizeof(XT) == 2) {
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                xv[2 * c] = __uint_as_float(xr[u][0][c] << 16);
+                xv[2 * c + 1] = __uint_as_float(xr[u][0][c] & 0xffff0000u);
+              }
+            } else {
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                xv[c] = __uint_as_float(xr[u][0][c]);
+                xv[4 + c] = __uint_as_float(xr[u][sizeof(XT) == 2 ? 0 : 1][c]);
+              }
+            }
+            const f32x4 g0 = *reinterpret_cast<const f32x4*>(&gs[rr][8 * eg]);
+            const f32x4 g1 = *reinterpret_cast<const f32x4*>(&gs[rr][8 * eg + 4]);
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+              for (int j = 0; j < 8; ++j)
+                acc[c][j] = fmaf(xv[c], j < 4 ? g0[j] : g1[j - 4], acc[c][j]);
+          }
         }
       }
     }
-    if (i < d) {
+    if (TS > 1) {
+      // slices 1 .. TS - 1 hand their sums to slice 0, which adds them in order
+      const int slot = threadIdx.x % (CG * EG);
+      __syncthreads();
+      if (ts > 0) {
 #pragma unroll
-      for (int e = 0; e < EB; ++e)
-        if (e < ne) part[((size_t)tc * d + i) * E + e0 + e] = acc[e];
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) red[((ts - 1) * CG * EG + slot) * 64 + c * 8 + j] = acc[c][j];
+      }
+      __syncthreads();
+      if (ts == 0) {
+        for (int s2 = 1; s2 < TS; ++s2)
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[c][j] += red[((s2 - 1) * CG * EG + slot) * 64 + c * 8 + j];
+      }
+    }
+    if (col_ok && ts == 0) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (8 * eg + j < ne) part[((size_t)tc * d + col + c) * E + e0 + 8 * eg + j] = acc[c][j];
     }
   }
 }
 
-// tokens per partial chunk: about 1024 blocks over (column chunks x token
+// expert block of the dW partials for E experts, and its columns per block
+int xtg_eb(int E) { return E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : 64; }
+int xtg_cols(int E) {
+  const int eb = xtg_eb(E);
+  return eb == 8 ? XtgShape<8>::CB : eb == 16 ? XtgShape<16>::CB : eb == 32 ? XtgShape<32>::CB
+                                                                           : XtgShape<64>::CB;
+}
+
+// tokens per partial chunk: about 1024 blocks over (column blocks x token
 // chunks), a multiple of GR between GR and 512
-int xtg_chunk(int T, int d) {
-  const long long want = (long long)T * cdiv(d, kThreads) / 1024;
-  const int tc = (int)std::min<long long>(512, std::max<long long>(GR, (want + GR - 1) / GR * GR));
-  return tc;
+int xtg_chunk(int T, int d, int E) {
+  const long long want = (long long)T * cdiv(d, xtg_cols(E)) / 1024;
+  return (int)std::min<long long>(512, std::max<long long>(GR, (want + GR - 1) / GR * GR));
 }
 
 // dW[i, e] = sum over chunks (in order) of part[c][i][e]
@@ -209,7 +290,15 @@ __global__ __launch_bounds__(kThreads) void sum_chunks_kernel(const float* __res
   const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= n) return;
   float s = 0.f;
-  for (int c = 0; c < nc; ++c) s += part[(size_t)c * n + i];
+  int c = 0;
+  for (; c + 8 <= nc; c += 8) {  // 8 loads in flight, added in chunk order
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(c + u) * n + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; c < nc; ++c) s += part[(size_t)c * n + i];
   out[i] = s;
 }
 
@@ -230,41 +319,112 @@ __global__ __launch_bounds__(kThreads) void colsum_kernel(const float* __restric
   }
 }
 
-// dx[t, i] += sum_e G[t, e] W[i, e]: block = DXT tokens x 256 columns; each
-// thread keeps its column's W row (EB experts at a time) in registers.
-constexpr int DXT = 64;
+// dx[t, i] += sum_e G[t, e] W[i, e] (register-blocked fp32): a block takes
+// 64 tokens x 256 columns; thread (token group ty, column group tx) keeps an
+// 8 x 8 block, summing over the experts in order.  Per chunk of EB experts
+// (EB as for the dW partials), G is staged transposed (gs[e][t]) and W as
+// its rows' chunk, transposed (ws[e][i]); a thread reads 8 tokens and 8
+// columns per expert as 16-byte LDS reads (the token reads are broadcasts
+// across the wave, the column reads 512 contiguous bytes).  Staging loads
+// are 16 bytes wide where E and the pointers allow (rows then start
+// 16-byte aligned).
+constexpr int DXT = 64, DXC = 256;
 template <typename WT, int EB>
 __global__ __launch_bounds__(kThreads) void dx_linear_kernel(const float* __restrict__ G,
                                                              const WT* __restrict__ W, int T,
                                                              int d, int E,
                                                              float* __restrict__ dx) {
-  __shared__ float gs[DXT][EB];
-  const int i = blockIdx.x * kThreads + threadIdx.x;
-  const int t0 = blockIdx.y * DXT;
-  const int nt = min(DXT, T - t0);
-  float acc[DXT];
+  constexpr int WV = 16 / sizeof(WT);  // W elements per 16-byte load
+  __shared__ __attribute__((aligned(16))) float gs[EB][DXT + 4];
+  __shared__ __attribute__((aligned(16))) WT ws[EB][DXC + 8];
+  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;
+  const int t0 = blockIdx.y * DXT, c0 = blockIdx.x * DXC;
+  const bool gvec = (E % 4) == 0 && ((uintptr_t)G & 15) == 0;
+  const bool wvec = (E % WV) == 0 && ((uintptr_t)W & 15) == 0;
+  float acc[8][8];
 #pragma unroll
-  for (int q = 0; q < DXT; ++q) acc[q] = 0.f;
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[a][c] = 0.f;
   for (int e0 = 0; e0 < E; e0 += EB) {
     const int ne = min(EB, E - e0);
-    float wr[EB];
-#pragma unroll
-    for (int e = 0; e < EB; ++e) wr[e] = (i < d && e < ne) ? ldx<WT>(W, (size_t)i * E + e0 + e) : 0.f;
     __syncthreads();
-    for (int q = threadIdx.x; q < DXT * EB; q += kThreads) {
-      const int rr = q / EB, e = q % EB;
-      gs[rr][e] = (rr < nt && e < ne) ? G[(size_t)(t0 + rr) * E + e0 + e] : 0.f;
+    if (gvec) {
+      for (int q = threadIdx.x; q < DXT * (EB / 4); q += kThreads) {
+        const int rr = q / (EB / 4), e = (q % (EB / 4)) * 4;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (t0 + rr < T && e < ne) v = *reinterpret_cast<const f32x4*>(G + (size_t)(t0 + rr) * E + e0 + e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) gs[e + j][rr] = v[j];
+      }
+    } else {
+      for (int q = threadIdx.x; q < DXT * EB; q += kThreads) {
+        const int rr = q / EB, e = q % EB;
+        gs[e][rr] = (t0 + rr < T && e < ne) ? G[(size_t)(t0 + rr) * E + e0 + e] : 0.f;
+      }
+    }
+    if (wvec) {
+      for (int q = threadIdx.x; q < DXC * (EB / WV); q += kThreads) {
+        const int i = q / (EB / WV), e = (q % (EB / WV)) * WV;
+        WT v[WV];
+#pragma unroll
+        for (int j = 0; j < WV; ++j) v[j] = WT(0);
+        if (c0 + i < d && e < ne) {
+          const u32x4 raw = *reinterpret_cast<const u32x4*>(W + (size_t)(c0 + i) * E + e0 + e);
+          __builtin_memcpy(v, &raw, 16);
+        }
+#pragma unroll
+        for (int j = 0; j < WV; ++j) ws[e + j][i] = v[j];
+      }
+    } else {
+      for (int q = threadIdx.x; q < DXC * EB; q += kThreads) {
+        const int i = q / EB, e = q % EB;
+        ws[e][i] = (c0 + i < d && e < ne) ? W[(size_t)(c0 + i) * E + e0 + e] : WT(0);
+      }
     }
     __syncthreads();
+    for (int e = 0; e < ne; ++e) {
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(&gs[e][8 * ty]);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(&gs[e][8 * ty + 4]);
+      float wv[8];
+      if (sizeof(WT) == 2) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&ws[e][8 * tx]);
 #pragma unroll
-    for (int q = 0; q < DXT; ++q)
+        for (int c = 0; c < 4; ++c) {
+          wv[2 * c] = __uint_as_float(v[c] << 16);
+          wv[2 * c + 1] = __uint_as_float(v[c] & 0xffff0000u);
+        }
+      } else {
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(&ws[e][8 * tx]);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(&ws[e][8 * tx + 4]);
 #pragma unroll
-      for (int e = 0; e < EB; ++e) acc[q] = fmaf(gs[q][e], wr[e], acc[q]);
+        for (int c = 0; c < 4; ++c) {
+          wv[c] = v0[c];
+          wv[4 + c] = v1[c];
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[a][c] = fmaf(a < 4 ? g0[a] : g1[a - 4], wv[c], acc[a][c]);
+    }
   }
-  if (i < d)
+  const int col = c0 + 8 * tx;
+  if (col >= d) return;
 #pragma unroll
-    for (int q = 0; q < DXT; ++q)
-      if (q < nt) dx[(size_t)(t0 + q) * d + i] += acc[q];
+  for (int a = 0; a < 8; ++a) {
+    const int t = t0 + 8 * ty + a;
+    if (t >= T) continue;
+    f32x4* o = reinterpret_cast<f32x4*>(dx + (size_t)t * d + col);
+    f32x4 v0 = o[0], v1 = o[1];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v0[c] += acc[a][c];
+      v1[c] += acc[a][4 + c];
+    }
+    o[0] = v0;
+    o[1] = v1;
+  }
 }
 
 template <int KS>
@@ -323,7 +483,7 @@ hipError_t launch_topk_weights_backward(const float* logits, const int32_t* idx,
 }
 
 size_t linear_backward_workspace_bytes(int T, int d, int E) {
-  const size_t nc = (size_t)cdiv(T, xtg_chunk(T, d));
+  const size_t nc = (size_t)cdiv(T, xtg_chunk(T, d, E));
   return align_up(nc * (size_t)d * E * sizeof(float), 256);
 }
 
@@ -331,18 +491,19 @@ template <typename XT, int EB>
 void launch_linear_bwd(const void* x, const void* W, const float* G, int T, int d, int E,
                        float* dW, float* dx, void* ws, hipStream_t s) {
   if (dW) {
-    const int tc = xtg_chunk(T, d);
+    const int tc = xtg_chunk(T, d, E);
     const int nc = cdiv(T, tc);
+    constexpr int CB = XtgShape<EB>::CB;  // columns per block (= xtg_cols(E))
     float* part = static_cast<float*>(ws);
-    hipLaunchKernelGGL((xtg_partial_kernel<XT, EB>), dim3(cdiv(d, kThreads), nc), dim3(kThreads),
-                       0, s, static_cast<const XT*>(x), G, T, d, E, tc, part);
+    hipLaunchKernelGGL((xtg_partial_kernel<XT, EB>), dim3(cdiv(d, CB), nc), dim3(kThreads), 0, s,
+                       static_cast<const XT*>(x), G, T, d, E, tc, part);
     const size_t n = (size_t)d * E;
     hipLaunchKernelGGL(sum_chunks_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
                        dim3(kThreads), 0, s, part, nc, n, dW);
   }
   if (dx)
-    hipLaunchKernelGGL((dx_linear_kernel<XT, EB>), dim3(cdiv(d, kThreads), cdiv(T, DXT)),
-                       dim3(kThreads), 0, s, G, static_cast<const XT*>(W), T, d, E, dx);
+    hipLaunchKernelGGL((dx_linear_kernel<XT, EB>), dim3(cdiv(d, DXC), cdiv(T, DXT)), dim3(kThreads),
+                       0, s, G, static_cast<const XT*>(W), T, d, E, dx);
 }
 
 template <typename XT>

@@ -297,6 +297,8 @@ int moe_linear_backward(const void* x, const void* W, const float* G, int T, int
   if (!dtype_ok(dtype)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!G || (dW && !x) || (dx && !W)) return MOE_ERR_INVALID;
+  if (!dims_ok(d)) return MOE_ERR_UNSUPPORTED;
+  if ((dW && !aligned16(x)) || (dx && !aligned16(dx))) return MOE_ERR_UNSUPPORTED;
   if (dW) {
     const size_t need = moe::linear_backward_workspace_bytes(T, d, E);
     if (!workspace || ws_bytes < need) return MOE_ERR_WORKSPACE;

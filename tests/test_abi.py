@@ -136,6 +136,64 @@ def test_combine_validation(lib):
     assert c(T=0) == L.MOE_OK
 
 
+def test_backward_validation(lib):
+    """The training entry points reject bad arguments on the host."""
+    cb = dict(dy=A, y_perm=A, inv=A, topk_w=A, T=16, d=64, k=2, y_shared=None,
+              shared_gate_logit=None, dy_perm=A, dw=A, dy_shared=None, dgate_logit=None)
+    def combine_bwd(**kw):
+        return L.moe_combine_backward(**{**cb, **kw}, stream=0, check=False)
+    assert combine_bwd(k=9) == L.MOE_ERR_UNSUPPORTED
+    assert combine_bwd(k=0) == L.MOE_ERR_INVALID
+    assert combine_bwd(dy=None) == L.MOE_ERR_INVALID
+    assert combine_bwd(d=60) == L.MOE_ERR_UNSUPPORTED
+    assert combine_bwd(dw=MIS) == L.MOE_ERR_UNSUPPORTED
+    assert combine_bwd(shared_gate_logit=A) == L.MOE_ERR_INVALID  # gate without its outputs
+    assert combine_bwd(T=0) == L.MOE_OK
+    db = dict(dy_perm=A, offsets=A, E=8, rows=32, f=64, d=64, dtype=L.MOE_BF16, W_down=A, h=A,
+              u=A, act=A, dhu=A, dW_down=A)
+    def down_bwd(**kw):
+        return L.moe_expert_down_backward(**{**db, **kw}, stream=0, check=False)
+    assert down_bwd(dtype=L.MOE_F32) == L.MOE_ERR_UNSUPPORTED  # bf16 MFMA only
+    assert down_bwd(f=60) == L.MOE_ERR_UNSUPPORTED
+    assert down_bwd(E=0) == L.MOE_ERR_INVALID
+    assert down_bwd(offsets=None) == L.MOE_ERR_INVALID
+    assert down_bwd(h=None) == L.MOE_ERR_INVALID
+    assert down_bwd(dhu=MIS) == L.MOE_ERR_UNSUPPORTED
+    ub = dict(x=A, gather_idx=None, offsets=A, E=8, rows=32, d=64, f=64, dtype=L.MOE_BF16,
+              W_gate=A, W_up=A, dhu=A, dx_perm=A, accumulate=0, dW_gate=A, dW_up=A)
+    def up_bwd(**kw):
+        return L.moe_expert_up_backward(**{**ub, **kw}, stream=0, check=False)
+    assert up_bwd(accumulate=2) == L.MOE_ERR_INVALID
+    assert up_bwd(dW_up=None) == L.MOE_ERR_INVALID
+    assert up_bwd(x=MIS) == L.MOE_ERR_UNSUPPORTED
+    assert up_bwd(d=12) == L.MOE_ERR_UNSUPPORTED
+    unp = dict(dx_perm=A, inv=A, T=16, d=64, k=2, accumulate=0, dx=A)
+    def unpermute(**kw):
+        return L.moe_unpermute(**{**unp, **kw}, stream=0, check=False)
+    assert unpermute(k=9) == L.MOE_ERR_UNSUPPORTED
+    assert unpermute(inv=None) == L.MOE_ERR_INVALID
+    assert unpermute(d=20) == L.MOE_ERR_UNSUPPORTED
+    assert unpermute(T=0) == L.MOE_OK
+    tk = dict(logits=A, topk_idx=A, dw=A, T=16, E=8, k=2, score=0, dL=A)
+    def topk_bwd(**kw):
+        return L.moe_topk_weights_backward(**{**tk, **kw}, stream=0, check=False)
+    assert topk_bwd(k=9) == L.MOE_ERR_INVALID
+    assert topk_bwd(score=5) == L.MOE_ERR_UNSUPPORTED
+    assert topk_bwd(dL=None) == L.MOE_ERR_INVALID
+    lb = dict(x=A, W=A, G=A, T=16, d=64, E=8, dtype=L.MOE_BF16, dW=A, db=None, dx=A,
+              workspace=A, ws_bytes=1 << 24)
+    def lin_bwd(**kw):
+        return L.moe_linear_backward(**{**lb, **kw}, stream=0, check=False)
+    assert lin_bwd(E=257) == L.MOE_ERR_INVALID
+    assert lin_bwd(G=None) == L.MOE_ERR_INVALID
+    assert lin_bwd(d=12) == L.MOE_ERR_UNSUPPORTED        # rows move as 16-byte vectors
+    assert lin_bwd(x=MIS) == L.MOE_ERR_UNSUPPORTED
+    assert lin_bwd(dx=MIS) == L.MOE_ERR_UNSUPPORTED
+    assert lin_bwd(ws_bytes=16) == L.MOE_ERR_WORKSPACE
+    assert lin_bwd(T=0) == L.MOE_OK
+    assert L.moe_linear_backward_workspace_size(16, 64, 8) > 0
+
+
 def test_binding_raises_on_error(lib):
     with pytest.raises(L.MoeError):
         L.moe_route(A, A, None, 16, 64, 8, 9, 0, 1, A, A, None, A, 1 << 20, stream=0)

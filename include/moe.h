@@ -212,27 +212,29 @@ int moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w, in
  *   -> moe_unpermute; moe_topk_weights_backward -> moe_linear_backward
  *   (router: G = dL, W = W_r; gated shared expert: G = dgate, W = w_s).
  * Conventions as above (device pointers owned by the caller, asynchronous,
- * host validation first, no allocation); bf16 storage for the GEMM calls
- * (MOE_ERR_UNSUPPORTED for fp32); every sum in a fixed order
- * (deterministic).
+ * host validation first, no allocation); bf16 or fp32 storage as in the
+ * forward (fp32: plain FMA kernels for small layers, as the forward's fp32
+ * path); every sum in a fixed order (deterministic).
  * ------------------------------------------------------------------------ */
 
 /*
  * moe_combine_backward -- gradient of moe_combine (DisagMoE technical
  * summary, "2.2 AF-Pipe", combine):
  *   dw[t, j] = <dy[t, :], y_perm[inv[t, j], :]>,
- *   dy_perm[inv[t, j], :] = topk_w[t, j] * dy[t, :]              (bf16 RNE);
- *   shared term (dy_shared != NULL): dy_shared[t, :] = g_t * dy[t, :] (bf16),
+ *   dy_perm[inv[t, j], :] = topk_w[t, j] * dy[t, :]              (dtype; bf16 RNE);
+ *   shared term (dy_shared != NULL): dy_shared[t, :] = g_t * dy[t, :] (dtype),
  *     g_t = sigmoid(shared_gate_logit[t]) or 1 when the logit is NULL;
  *     with the logit and y_shared: dgate_logit[t] = <dy[t], y_shared[t]> g_t (1 - g_t).
  * Arguments: dy [T, d] fp32; y_perm [T*k, d] fp32 (the forward's);
  *   inv, topk_w [T, k]; y_shared [T, d] fp32 (ungated shared output of the
- *   forward) or NULL; shared_gate_logit [T] or NULL; dy_perm [T*k, d] bf16
- *   out; dw [T, k] fp32 out; dy_shared [T, d] bf16 out or NULL;
- *   dgate_logit [T] fp32 out (required with the logit) or NULL.  1 <= k <= 8.
+ *   forward) or NULL; shared_gate_logit [T] or NULL; dy_perm [T*k, d] out in
+ *   dtype (the storage dtype of the layer); dw [T, k] fp32 out; dy_shared
+ *   [T, d] out in dtype or NULL; dgate_logit [T] fp32 out (required with the
+ *   logit) or NULL.  1 <= k <= 8.
  */
 int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* inv,
-                         const float* topk_w, int T, int d, int k, const float* y_shared,
+                         const float* topk_w, int T, int d, int k, int dtype,
+                         const float* y_shared,
                          const float* shared_gate_logit, void* dy_perm, float* dw,
                          void* dy_shared, float* dgate_logit, hipStream_t stream);
 
@@ -240,12 +242,12 @@ int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* in
  * moe_expert_down_backward -- gradients of moe_expert_down (layer 1) and of
  * the SwiGLU of moe_expert_up, per expert e and row r of e:
  *   dA = dy_perm[r] W_down[e]^T,  s = sigmoid(h[r]),
- *   dhu[r, 0:f]  = dA * u[r] * s (1 + h[r] (1 - s))     (dH, bf16),
- *   dhu[r, f:2f] = dA * h[r] * s                        (dU, bf16),
+ *   dhu[r, 0:f]  = dA * u[r] * s (1 + h[r] (1 - s))     (dH, dtype),
+ *   dhu[r, f:2f] = dA * h[r] * s                        (dU, dtype),
  *   dW_down[e]   = sum_{r of e} act[r]^T dy_perm[r]     (fp32; 0 for empty experts).
- * Arguments: dy_perm [rows, d] bf16; offsets as in moe_expert_up; W_down
+ * Arguments: dy_perm [rows, d] (dtype); offsets as in moe_expert_up; W_down
  *   [E, f, d]; h, u [rows, f] (moe_expert_up_save); act [rows, f] (its
- *   a_out); dhu [rows, 2f] bf16 out; dW_down [E, f, d] fp32 out.
+ *   a_out); dhu [rows, 2f] out (dtype); dW_down [E, f, d] fp32 out.
  */
 int moe_expert_down_backward(const void* dy_perm, const int32_t* offsets, int E, int rows, int f,
                              int d, int dtype, const void* W_down, const void* h, const void* u,
@@ -257,8 +259,8 @@ int moe_expert_down_backward(const void* dy_perm, const int32_t* offsets, int E,
  *   dW_gate[e] = sum_{r of e} z_r^T dhu[r, 0:f],  dW_up[e] = sum z_r^T dhu[r, f:2f]
  *   (fp32; 0 for empty experts), z_r = x[gather_idx[r]] (or x[r]).
  * Arguments: x, gather_idx, offsets, W_gate, W_up as in moe_expert_up; dhu
- *   [rows, 2f] bf16; dx_perm [rows, d] fp32 out (added to when accumulate =
- *   1); dW_gate, dW_up [E, d, f] fp32 out.
+ *   [rows, 2f] (dtype); dx_perm [rows, d] fp32 out (added to when
+ *   accumulate = 1); dW_gate, dW_up [E, d, f] fp32 out.
  */
 int moe_expert_up_backward(const void* x, const int32_t* gather_idx, const int32_t* offsets,
                            int E, int rows, int d, int f, int dtype, const void* W_gate,

@@ -64,8 +64,8 @@ def load():
         "moe_combine": (i32, [vp, vp, vp, i32, i32, i32, vp, vp, i32, vp, vp]),
         "moe_expert_up_save": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                      vp, sz, vp]),
-        "moe_combine_backward": (i32, [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp,
-                                       vp]),
+        "moe_combine_backward": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                       vp, vp]),
         "moe_expert_down_backward": (i32, [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                            vp, vp]),
         "moe_expert_up_backward": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp,
@@ -199,9 +199,9 @@ def moe_expert_up_save(x, gather_idx, offsets, E, rows, d, f, dtype, W_gate, W_u
     return st
 
 
-def moe_combine_backward(dy, y_perm, inv, topk_w, T, d, k, y_shared, shared_gate_logit, dy_perm,
-                         dw, dy_shared, dgate_logit, stream=None, check=True):
-    st = load().moe_combine_backward(_p(dy), _p(y_perm), _p(inv), _p(topk_w), T, d, k,
+def moe_combine_backward(dy, y_perm, inv, topk_w, T, d, k, dtype, y_shared, shared_gate_logit,
+                         dy_perm, dw, dy_shared, dgate_logit, stream=None, check=True):
+    st = load().moe_combine_backward(_p(dy), _p(y_perm), _p(inv), _p(topk_w), T, d, k, dtype,
                                      _p(y_shared), _p(shared_gate_logit), _p(dy_perm), _p(dw),
                                      _p(dy_shared), _p(dgate_logit), _stream(stream))
     if check:

@@ -28,13 +28,26 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// one workgroup per token; KS = k (1..8)
-template <int KS>
+// 4 scaled values to the row-major output (bf16 RNE or fp32), vector index c
+template <typename OT>
+__device__ __forceinline__ void store4(OT* out, size_t c, const f32x4 s) {
+  if (sizeof(OT) == 2) {
+    uint2 o;
+    o.x = pack_bf16x2(s[0], s[1]);
+    o.y = pack_bf16x2(s[2], s[3]);
+    *reinterpret_cast<uint2*>(out + c * 4) = o;
+  } else {
+    *reinterpret_cast<f32x4*>(out + c * 4) = s;
+  }
+}
+
+// one workgroup per token; KS = k (1..8); OT: storage type of dy_perm, dy_shared
+template <int KS, typename OT>
 __global__ __launch_bounds__(kThreads) void combine_backward_kernel(
     const f32x4* __restrict__ dy, const f32x4* __restrict__ y_perm, const int32_t* __restrict__ inv,
     const float* __restrict__ topk_w, int vecs, const f32x4* __restrict__ y_shared,
-    const float* __restrict__ gate_logit, bf16_t* __restrict__ dy_perm, float* __restrict__ dw,
-    bf16_t* __restrict__ dy_shared, float* __restrict__ dgate) {
+    const float* __restrict__ gate_logit, OT* __restrict__ dy_perm, float* __restrict__ dw,
+    OT* __restrict__ dy_shared, float* __restrict__ dgate) {
   __shared__ float red[kThreads / 64][KS + 1];
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -54,18 +67,10 @@ __global__ __launch_bounds__(kThreads) void combine_backward_kernel(
     for (int j = 0; j < KS; ++j) {
       const f32x4 yp = y_perm[(size_t)r[j] * vecs + c];
       dot[j] += v[0] * yp[0] + v[1] * yp[1] + v[2] * yp[2] + v[3] * yp[3];
-      const f32x4 s = w[j] * v;
-      uint2 o;
-      o.x = pack_bf16x2(s[0], s[1]);
-      o.y = pack_bf16x2(s[2], s[3]);
-      *reinterpret_cast<uint2*>(dy_perm + ((size_t)r[j] * vecs + c) * 4) = o;
+      store4(dy_perm, (size_t)r[j] * vecs + c, w[j] * v);
     }
     if (dy_shared) {
-      const f32x4 s = g * v;
-      uint2 o;
-      o.x = pack_bf16x2(s[0], s[1]);
-      o.y = pack_bf16x2(s[2], s[3]);
-      *reinterpret_cast<uint2*>(dy_shared + ((size_t)t * vecs + c) * 4) = o;
+      store4(dy_shared, (size_t)t * vecs + c, g * v);
       if (dgate) {
         const f32x4 ys = y_shared[(size_t)t * vecs + c];
         dot_s += v[0] * ys[0] + v[1] * ys[1] + v[2] * ys[2] + v[3] * ys[3];
@@ -429,12 +434,19 @@ __global__ __launch_bounds__(kThreads) void dx_linear_kernel(const float* __rest
 
 template <int KS>
 void launch_cb(const float* dy, const float* y_perm, const int32_t* inv, const float* topk_w,
-               int T, int d, const float* y_shared, const float* gate_logit, void* dy_perm,
-               float* dw, void* dy_shared, float* dgate, hipStream_t s) {
-  hipLaunchKernelGGL((combine_backward_kernel<KS>), dim3(T), dim3(kThreads), 0, s,
-                     reinterpret_cast<const f32x4*>(dy), reinterpret_cast<const f32x4*>(y_perm),
-                     inv, topk_w, d / 4, reinterpret_cast<const f32x4*>(y_shared), gate_logit,
-                     static_cast<bf16_t*>(dy_perm), dw, static_cast<bf16_t*>(dy_shared), dgate);
+               int T, int d, bool bf16, const float* y_shared, const float* gate_logit,
+               void* dy_perm, float* dw, void* dy_shared, float* dgate, hipStream_t s) {
+  const f32x4* dyv = reinterpret_cast<const f32x4*>(dy);
+  const f32x4* ypv = reinterpret_cast<const f32x4*>(y_perm);
+  const f32x4* ysv = reinterpret_cast<const f32x4*>(y_shared);
+  if (bf16)
+    hipLaunchKernelGGL((combine_backward_kernel<KS, bf16_t>), dim3(T), dim3(kThreads), 0, s, dyv,
+                       ypv, inv, topk_w, d / 4, ysv, gate_logit, static_cast<bf16_t*>(dy_perm),
+                       dw, static_cast<bf16_t*>(dy_shared), dgate);
+  else
+    hipLaunchKernelGGL((combine_backward_kernel<KS, float>), dim3(T), dim3(kThreads), 0, s, dyv,
+                       ypv, inv, topk_w, d / 4, ysv, gate_logit, static_cast<float*>(dy_perm), dw,
+                       static_cast<float*>(dy_shared), dgate);
 }
 
 template <int KS>
@@ -448,12 +460,12 @@ void launch_up(const float* dx_perm, const int32_t* inv, int T, int d, bool accu
 }  // namespace
 
 hipError_t launch_combine_backward(const float* dy, const float* y_perm, const int32_t* inv,
-                                   const float* topk_w, int T, int d, int k,
+                                   const float* topk_w, int T, int d, int k, bool bf16,
                                    const float* y_shared, const float* gate_logit, void* dy_perm,
                                    float* dw, void* dy_shared, float* dgate, hipStream_t s) {
   if (T == 0) return hipSuccess;
   switch (k) {
-#define MOE_CB(K) case K: launch_cb<K>(dy, y_perm, inv, topk_w, T, d, y_shared, gate_logit, dy_perm, dw, dy_shared, dgate, s); break;
+#define MOE_CB(K) case K: launch_cb<K>(dy, y_perm, inv, topk_w, T, d, bf16, y_shared, gate_logit, dy_perm, dw, dy_shared, dgate, s); break;
     MOE_CB(1) MOE_CB(2) MOE_CB(3) MOE_CB(4) MOE_CB(5) MOE_CB(6) MOE_CB(7) MOE_CB(8)
 #undef MOE_CB
     default: return hipErrorInvalidValue;

@@ -903,6 +903,81 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bwd256_pair_kernel(BwdArg
     bwd256_body<WGRAD, EPI_WGRAD, true>(pw, lds, blockIdx.x - gd, gridDim.x - gd);
 }
 
+// ------------------------------------------------------------------------
+// fp32 layers (small): one thread per output element, a plain FMA loop over
+// K in order, as the forward's fp32 path.
+// ------------------------------------------------------------------------
+__device__ __forceinline__ int expert_of_row_b(const int32_t* offsets, int E, int r) {
+  int lo = 0, hi = E;  // e with offsets[e] <= r < offsets[e + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (offsets[mid] <= r) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// dA[r, n] = sum_k dY[r, k] W_down[e][n, k]; dhu[r, n] = dA u s (1 + h (1 - s)),
+// dhu[r, f + n] = dA h s, s = sigmoid(h)
+__global__ void down_bwd_dgrad_f32_kernel(const float* __restrict__ dy, const int32_t* __restrict__ offsets,
+                                          int E, int rows, int f, int d,
+                                          const float* __restrict__ Wd, const float* __restrict__ h,
+                                          const float* __restrict__ u, float* __restrict__ dhu) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)rows * f) return;
+  const int r = (int)(i / f), n = (int)(i - (size_t)r * f);
+  const int e = expert_of_row_b(offsets, E, r);
+  const float* a = dy + (size_t)r * d;
+  const float* w = Wd + ((size_t)e * f + n) * d;
+  float acc = 0.f;
+  for (int k = 0; k < d; ++k) acc = fmaf(a[k], w[k], acc);
+  const float hv = h[i], uv = u[i];
+  const float sg = 1.f / (1.f + __expf(-hv));
+  dhu[(size_t)r * 2 * f + n] = acc * uv * sg * (1.f + hv * (1.f - sg));
+  dhu[(size_t)r * 2 * f + f + n] = acc * hv * sg;
+}
+
+// dX[r, n] (+)= sum_{k < f} dhu[r, k] W_gate[e][n, k] + sum_{k < f} dhu[r, f + k] W_up[e][n, k]
+__global__ void up_bwd_dgrad_f32_kernel(const float* __restrict__ dhu, const int32_t* __restrict__ offsets,
+                                        int E, int rows, int d, int f,
+                                        const float* __restrict__ Wg, const float* __restrict__ Wu,
+                                        float* __restrict__ dx, int accumulate) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)rows * d) return;
+  const int r = (int)(i / d), n = (int)(i - (size_t)r * d);
+  const int e = expert_of_row_b(offsets, E, r);
+  const float* g = dhu + (size_t)r * 2 * f;
+  const float* wg = Wg + ((size_t)e * d + n) * f;
+  const float* wu = Wu + ((size_t)e * d + n) * f;
+  float acc = 0.f;
+  for (int k = 0; k < f; ++k) acc = fmaf(g[k], wg[k], acc);
+  for (int k = 0; k < f; ++k) acc = fmaf(g[f + k], wu[k], acc);
+  dx[i] = accumulate ? dx[i] + acc : acc;
+}
+
+// C_e[m, n] = sum_{r in e} A[src(r), m] B[r, n] (rows of e in order); columns
+// n < n_split go to w0 [E, M, n_split], the rest to w1 [E, M, N - n_split]
+__global__ void wgrad_f32_kernel(const float* __restrict__ A, int lda, const int32_t* __restrict__ gather,
+                                 const float* __restrict__ B, int ldb,
+                                 const int32_t* __restrict__ offsets, int E, int M, int N,
+                                 int n_split, float* __restrict__ w0, float* __restrict__ w1) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)E * M * N) return;
+  const int e = (int)(i / ((size_t)M * N));
+  const size_t mn = i - (size_t)e * M * N;
+  const int m = (int)(mn / N), n = (int)(mn - (size_t)m * N);
+  float acc = 0.f;
+  for (int r = offsets[e]; r < offsets[e + 1]; ++r) {
+    const int src = gather ? gather[r] : r;
+    acc = fmaf(A[(size_t)src * lda + m], B[(size_t)r * ldb + n], acc);
+  }
+  if (n < n_split)
+    w0[((size_t)e * M + m) * n_split + n] = acc;
+  else
+    w1[((size_t)e * M + m) * (N - n_split) + (n - n_split)] = acc;
+}
+
+unsigned blocks_of(size_t n) { return (unsigned)((n + 255) / 256); }
+
 #ifndef MOE_BWD_PP
 #define MOE_BWD_PP 1
 #endif
@@ -995,9 +1070,21 @@ int dgrad_grid(int rows, int E, int tiles_n) {
 }  // namespace
 
 hipError_t launch_expert_down_backward(const void* dy_perm, const int32_t* offsets, int E,
-                                       int rows, int f, int d, const void* W_down,
+                                       int rows, int f, int d, bool bf16, const void* W_down,
                                        const void* h, const void* u, const void* act,
                                        void* dhu, float* dW_down, hipStream_t s) {
+  if (!bf16) {
+    if (rows > 0)
+      hipLaunchKernelGGL(down_bwd_dgrad_f32_kernel, dim3(blocks_of((size_t)rows * f)), dim3(256),
+                         0, s, static_cast<const float*>(dy_perm), offsets, E, rows, f, d,
+                         static_cast<const float*>(W_down), static_cast<const float*>(h),
+                         static_cast<const float*>(u), static_cast<float*>(dhu));
+    hipLaunchKernelGGL(wgrad_f32_kernel, dim3(blocks_of((size_t)E * f * d)), dim3(256), 0, s,
+                       static_cast<const float*>(act), f, nullptr,
+                       static_cast<const float*>(dy_perm), d, offsets, E, f, d, d, dW_down,
+                       nullptr);
+    return hipGetLastError();
+  }
   // dA = dY W_down[e]^T with the SwiGLU backward in the epilogue
   BwdArgs p{};
   p.A = static_cast<const bf16_t*>(dy_perm);
@@ -1049,9 +1136,21 @@ hipError_t launch_expert_down_backward(const void* dy_perm, const int32_t* offse
 
 hipError_t launch_expert_up_backward(const void* x, const int32_t* gather_idx,
                                      const int32_t* offsets, int E, int rows, int d, int f,
-                                     const void* W_gate, const void* W_up, const void* dhu,
-                                     float* dx_perm, int accumulate, float* dW_gate,
-                                     float* dW_up, hipStream_t s) {
+                                     bool bf16, const void* W_gate, const void* W_up,
+                                     const void* dhu, float* dx_perm, int accumulate,
+                                     float* dW_gate, float* dW_up, hipStream_t s) {
+  if (!bf16) {
+    if (rows > 0)
+      hipLaunchKernelGGL(up_bwd_dgrad_f32_kernel, dim3(blocks_of((size_t)rows * d)), dim3(256), 0,
+                         s, static_cast<const float*>(dhu), offsets, E, rows, d, f,
+                         static_cast<const float*>(W_gate), static_cast<const float*>(W_up),
+                         dx_perm, accumulate);
+    hipLaunchKernelGGL(wgrad_f32_kernel, dim3(blocks_of((size_t)E * d * 2 * f)), dim3(256), 0, s,
+                       static_cast<const float*>(x), d, gather_idx,
+                       static_cast<const float*>(dhu), 2 * f, offsets, E, d, 2 * f, f, dW_gate,
+                       dW_up);
+    return hipGetLastError();
+  }
   // dX = dH W_gate[e]^T + dU W_up[e]^T: K runs over W_gate's f columns, then W_up's
   BwdArgs p{};
   p.A = static_cast<const bf16_t*>(dhu);

@@ -194,11 +194,11 @@ int moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w, in
 // ---------------------------------------------------------------- backward
 
 int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* inv,
-                         const float* topk_w, int T, int d, int k, const float* y_shared,
-                         const float* shared_gate_logit, void* dy_perm, float* dw,
-                         void* dy_shared, float* dgate_logit, hipStream_t stream) {
+                         const float* topk_w, int T, int d, int k, int dtype,
+                         const float* y_shared, const float* shared_gate_logit, void* dy_perm,
+                         float* dw, void* dy_shared, float* dgate_logit, hipStream_t stream) {
   if (T < 0 || k < 1 || d <= 0) return MOE_ERR_INVALID;
-  if (k > 8) return MOE_ERR_UNSUPPORTED;
+  if (k > 8 || !dtype_ok(dtype)) return MOE_ERR_UNSUPPORTED;
   if ((long long)T * k >= (1ll << 31)) return MOE_ERR_INVALID;
   if (T == 0) return MOE_OK;
   if (!dy || !y_perm || !inv || !topk_w || !dy_perm || !dw) return MOE_ERR_INVALID;
@@ -209,9 +209,9 @@ int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* in
       !aligned16(dy_perm) || !aligned16(dw) || (y_shared && !aligned16(y_shared)) ||
       (dy_shared && !aligned16(dy_shared)))
     return MOE_ERR_UNSUPPORTED;
-  return hip_status(moe::launch_combine_backward(dy, y_perm, inv, topk_w, T, d, k, y_shared,
-                                                 shared_gate_logit, dy_perm, dw, dy_shared,
-                                                 dgate_logit, stream));
+  return hip_status(moe::launch_combine_backward(dy, y_perm, inv, topk_w, T, d, k,
+                                                 dtype == MOE_BF16, y_shared, shared_gate_logit,
+                                                 dy_perm, dw, dy_shared, dgate_logit, stream));
 }
 
 static int check_bwd_common(const int32_t* offsets, int E, int rows, int d, int f, int dtype) {
@@ -219,7 +219,6 @@ static int check_bwd_common(const int32_t* offsets, int E, int rows, int d, int 
   if ((long long)rows * 2 * (d > f ? d : f) >= (1ll << 40)) return MOE_ERR_INVALID;
   if ((long long)E * d * 2 * f >= (1ll << 40)) return MOE_ERR_INVALID;
   if (!dtype_ok(dtype)) return MOE_ERR_UNSUPPORTED;
-  if (dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;  // the backward GEMMs are bf16 MFMA
   if (!dims_ok(d) || !dims_ok(f)) return MOE_ERR_UNSUPPORTED;
   if (!offsets) return MOE_ERR_INVALID;
   if (!aligned16(offsets)) return MOE_ERR_UNSUPPORTED;
@@ -237,8 +236,9 @@ int moe_expert_down_backward(const void* dy_perm, const int32_t* offsets, int E,
       (h && !aligned16(h)) || (u && !aligned16(u)) || (act && !aligned16(act)) ||
       (dhu && !aligned16(dhu)))
     return MOE_ERR_UNSUPPORTED;
-  return hip_status(moe::launch_expert_down_backward(dy_perm, offsets, E, rows, f, d, W_down, h,
-                                                     u, act, dhu, dW_down, stream));
+  return hip_status(moe::launch_expert_down_backward(dy_perm, offsets, E, rows, f, d,
+                                                     dtype == MOE_BF16, W_down, h, u, act, dhu,
+                                                     dW_down, stream));
 }
 
 int moe_expert_up_backward(const void* x, const int32_t* gather_idx, const int32_t* offsets,
@@ -254,9 +254,9 @@ int moe_expert_up_backward(const void* x, const int32_t* gather_idx, const int32
       (x && !aligned16(x)) || (dhu && !aligned16(dhu)) || (dx_perm && !aligned16(dx_perm)) ||
       (gather_idx && !aligned16(gather_idx)))
     return MOE_ERR_UNSUPPORTED;
-  return hip_status(moe::launch_expert_up_backward(x, gather_idx, offsets, E, rows, d, f, W_gate,
-                                                   W_up, dhu, dx_perm, accumulate, dW_gate,
-                                                   dW_up, stream));
+  return hip_status(moe::launch_expert_up_backward(x, gather_idx, offsets, E, rows, d, f,
+                                                   dtype == MOE_BF16, W_gate, W_up, dhu, dx_perm,
+                                                   accumulate, dW_gate, dW_up, stream));
 }
 
 int moe_unpermute(const float* dx_perm, const int32_t* inv, int T, int d, int k, int accumulate,

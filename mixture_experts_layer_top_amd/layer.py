@@ -29,7 +29,8 @@ h = x W_gate and u = x W_up (routed and shared) and the router logits, and
         moe_linear_backward for the gate]
 
 leaving the gradients in ``self.grads`` (fp32 device tensors).  Training
-needs the deterministic separate combine (y_perm) and bf16 storage, and
+needs the deterministic separate combine (y_perm), keeps the backward's
+intermediates in the layer's storage dtype (bf16 or fp32), and
 always has moe_permute write x_perm: the layer-0 weight gradient reads the
 expert's token rows in order from it (the forward GEMMs still read x
 through the permutation on the "fast" path: x, T rows, stays in the
@@ -62,8 +63,8 @@ class MoeLayer:
         self.gather, self.comb = PATHS[path]
         self.train = train
         if train:
-            if self.comb != "separate" or cfg.dtype != "bf16":
-                raise ValueError("training needs the separate combine and bf16 storage")
+            if self.comb != "separate":
+                raise ValueError("training needs the separate combine")
             keep_logits = True
         self.cfg = cfg
         self.t = layer
@@ -219,11 +220,12 @@ class MoeLayer:
         dev = t["x"].device
         T, d, f, E, k = c.T, c.d, c.f, c.E, c.k
         R = T * k
-        f32, bf = torch.float32, torch.bfloat16
+        f32 = torch.float32
+        act = torch.bfloat16 if c.dtype == "bf16" else f32
         e = lambda *sh, dt=f32: torch.empty(*sh, dtype=dt, device=dev)  # noqa: E731
-        self.dy_perm = e(R, d, dt=bf)
+        self.dy_perm = e(R, d, dt=act)
         self.dw = e(T, k)
-        self.dhu = e(R, 2 * f, dt=bf)
+        self.dhu = e(R, 2 * f, dt=act)
         self.dx_perm = e(R, d)
         self.dL = e(T, E)
         g = dict(dx=e(T, d), dW_r=e(d, E), dW_gate=e(E, d, f), dW_up=e(E, d, f),
@@ -232,8 +234,8 @@ class MoeLayer:
         self.ws_lin = e(max(self.ws_lin_bytes, 16), dt=torch.uint8)
         if self.ns:
             fs = self.fs_all
-            self.dys = e(T, d, dt=bf)
-            self.s_dhu = e(T, 2 * fs, dt=bf)
+            self.dys = e(T, d, dt=act)
+            self.s_dhu = e(T, 2 * fs, dt=act)
             g.update(dWs_gate=e(d, fs), dWs_up=e(d, fs), dWs_down=e(fs, d))
             if c.shared_gated:
                 self.dgl = e(T, 1)
@@ -254,7 +256,7 @@ class MoeLayer:
         R = T * k
         mk = (lambda n: marks(n)) if marks is not None else (lambda n: None)
         gated = bool(self.ns and c.shared_gated)
-        L.moe_combine_backward(dy, self.y_perm, self.inv, self.w, T, d, k,
+        L.moe_combine_backward(dy, self.y_perm, self.inv, self.w, T, d, k, self.dtype,
                                self.ys if gated else None, self.g_logit if gated else None,
                                self.dy_perm, self.dw, self.dys if self.ns else None,
                                self.dgl if gated else None, stream=stream)

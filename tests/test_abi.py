@@ -138,7 +138,7 @@ def test_combine_validation(lib):
 
 def test_backward_validation(lib):
     """The training entry points reject bad arguments on the host."""
-    cb = dict(dy=A, y_perm=A, inv=A, topk_w=A, T=16, d=64, k=2, y_shared=None,
+    cb = dict(dy=A, y_perm=A, inv=A, topk_w=A, T=16, d=64, k=2, dtype=L.MOE_BF16, y_shared=None,
               shared_gate_logit=None, dy_perm=A, dw=A, dy_shared=None, dgate_logit=None)
     def combine_bwd(**kw):
         return L.moe_combine_backward(**{**cb, **kw}, stream=0, check=False)
@@ -148,12 +148,13 @@ def test_backward_validation(lib):
     assert combine_bwd(d=60) == L.MOE_ERR_UNSUPPORTED
     assert combine_bwd(dw=MIS) == L.MOE_ERR_UNSUPPORTED
     assert combine_bwd(shared_gate_logit=A) == L.MOE_ERR_INVALID  # gate without its outputs
+    assert combine_bwd(dtype=7) == L.MOE_ERR_UNSUPPORTED
     assert combine_bwd(T=0) == L.MOE_OK
     db = dict(dy_perm=A, offsets=A, E=8, rows=32, f=64, d=64, dtype=L.MOE_BF16, W_down=A, h=A,
               u=A, act=A, dhu=A, dW_down=A)
     def down_bwd(**kw):
         return L.moe_expert_down_backward(**{**db, **kw}, stream=0, check=False)
-    assert down_bwd(dtype=L.MOE_F32) == L.MOE_ERR_UNSUPPORTED  # bf16 MFMA only
+    assert down_bwd(dtype=5) == L.MOE_ERR_UNSUPPORTED
     assert down_bwd(f=60) == L.MOE_ERR_UNSUPPORTED
     assert down_bwd(E=0) == L.MOE_ERR_INVALID
     assert down_bwd(offsets=None) == L.MOE_ERR_INVALID

@@ -874,7 +874,13 @@ __device__ __forceinline__ void bwd256_body(const BwdArgs& p, char* lds, const i
           else
             o = p.w1 + ((size_t)e * p.M + m) * (p.N - p.n_split) + (n - p.n_split);
           if (add) v += *reinterpret_cast<const f32x4*>(o);
-          *reinterpret_cast<f32x4*>(o) = v;
+          // weight gradients are not read again soon: non-temporal stores
+          // keep them from evicting the operand panels of running tiles
+          // from the caches (+1-2%)
+          if (MODE == WGRAD)
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(o));
+          else
+            *reinterpret_cast<f32x4*>(o) = v;
         }
       }
     }

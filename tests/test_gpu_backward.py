@@ -127,6 +127,12 @@ def check_grads(cfg, m, g, h, dy_h, norm_tau=NORM_TAU, el_tau=EL_TAU):
             log(f"  {cfg.name} db: max |d| / sum_t |dL| = {ratio:.3e}")
             if ratio > norm_tau:
                 fails.append(f"db: {ratio:.3e}")
+        elif not np.any(rf):
+            # e.g. one expert with renormalised weights: w = 1 exactly, so the
+            # router gets no gradient at all
+            log(f"  {cfg.name} {rk}: reference exactly zero, GPU max |g| {np.max(np.abs(got)):.3e}")
+            if np.any(got):
+                fails.append(f"{rk} must be exactly zero")
         else:
             st = errors(got, rf)
             log(f"  {cfg.name} {rk}: normwise {st[0]:.3e}, max/rms {st[1]:.3e}, c {st[2]:.3e}")
@@ -170,6 +176,38 @@ def test_backward_parity_f32(L, name):
     dy = torch.randn(cfg.T, cfg.d, generator=gen, device="cuda", dtype=torch.float32)
     m, g = run_train(cfg, layer, dy)
     check_grads(cfg, m, g, host(layer), dy.cpu().double().numpy(), F32_NORM_TAU, F32_EL_TAU)
+
+
+def _edge_cfg(**kw):
+    base = dict(name="edge", cfg_id=9, T=130, d=72, f=40, E=8, k=2, renorm=True, dtype="bf16")
+    base.update(kw)
+    return CONFIGS["mixtral"].__class__(**base)
+
+
+def _edge_run(cfg, seed):
+    layer = make_layer(cfg, seed=seed, device="cuda")
+    dy = torch.randn(cfg.T, cfg.d, generator=torch.Generator(device="cuda").manual_seed(seed),
+                     device="cuda", dtype=torch.float32)
+    m, g = run_train(cfg, layer, dy)
+    check_grads(cfg, m, g, host(layer), dy.cpu().double().numpy())
+
+
+@pytest.mark.parametrize("E,k,T", [(1, 1, 300), (4, 4, 300), (256, 8, 300), (3, 2, 300),
+                                   (4, 2, 1), (8, 2, 63)])
+def test_backward_expert_and_token_extremes(L, E, k, T):
+    """One expert; k = E; 256 experts of about nine rows each; an odd E; a
+    single token; a ragged T: the backward against the oracle."""
+    log(f"[bwd edge] E={E} k={k} T={T}")
+    _edge_run(_edge_cfg(E=E, k=k, T=T, d=64, f=48), seed=100 + E + T)
+
+
+@pytest.mark.parametrize("nk", [1, 2, 3, 5])
+def test_backward_stage_counts(L, nk):
+    """d = f = 64 nk: the scalar-base backward GEMMs with 1, 2, 3 and 5 K
+    stages of the data gradients (their prologues take other branches for
+    nk < 3) and weight-gradient K ranges of about 175 rows."""
+    log(f"[bwd edge] stages nk={nk}")
+    _edge_run(_edge_cfg(E=16, k=4, T=700, d=64 * nk, f=64 * nk), seed=200 + nk)
 
 
 def test_backward_is_deterministic(L):

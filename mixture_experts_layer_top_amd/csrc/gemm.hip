@@ -99,6 +99,7 @@ struct GemmArgs {
   float* part;              // partial accumulators of split tiles, or NULL (no split)
   int n_cu;                 // compute units the tiles are spread over
   int fixup;                // 0: main pass; 1: sum the split tiles' partials
+  int nt_y;                 // y_perm stores non-temporal (y_perm larger than the last-level cache)
 };
 
 struct TileInfo {
@@ -1197,15 +1198,30 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
         for (int nj = 0; nj < NJ; ++nj)
 #pragma unroll
           for (int i = 0; i < 4; ++i) sf[(row_l + i) * SS + nj * 16 + col_l] = acc[mi][nj][i];
+        // 16 rows x 16 chunks of 16 B; two separate loops, so that the
+        // compiler keeps the non-temporal hint (merging the two stores drops it)
+        if (p.nt_y) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {  // 16 rows x 16 chunks of 16 B
-          const int idx = q * 64 + lane;
-          const int r = idx >> 4, c = idx & 15;
-          const int row = t_row0 + grow0 + (mi + mi_off) * 16 + r;
-          const int col = n0 + (c >> 3) * 128 + wg * 32 + (c & 7) * 4;
-          const f32x4 v = *reinterpret_cast<const f32x4*>(sf + r * SS + c * 4);
-          if (row < grow_end && col < N)
-            *reinterpret_cast<f32x4*>(p.y_perm + (size_t)row * N + col) = v;
+          for (int q = 0; q < 4; ++q) {
+            const int idx = q * 64 + lane;
+            const int r = idx >> 4, c = idx & 15;
+            const int row = t_row0 + grow0 + (mi + mi_off) * 16 + r;
+            const int col = n0 + (c >> 3) * 128 + wg * 32 + (c & 7) * 4;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(sf + r * SS + c * 4);
+            if (row < grow_end && col < N)
+              __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p.y_perm + (size_t)row * N + col));
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int idx = q * 64 + lane;
+            const int r = idx >> 4, c = idx & 15;
+            const int row = t_row0 + grow0 + (mi + mi_off) * 16 + r;
+            const int col = n0 + (c >> 3) * 128 + wg * 32 + (c & 7) * 4;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(sf + r * SS + c * 4);
+            if (row < grow_end && col < N)
+              *reinterpret_cast<f32x4*>(p.y_perm + (size_t)row * N + col) = v;
+          }
         }
       }
     }
@@ -1392,6 +1408,10 @@ hipError_t launch_gemm(GemmArgs& p, int rows, int E, int ncols, unsigned long lo
     // from the device offsets; without a workspace there is none)
     p.n_cu = num_cus();
     p.fixup = 0;
+    // a y_perm beyond the 256 MB last-level cache is streamed past it (the
+    // combine re-reads it from HBM either way); a smaller one stays cached
+    // for the combine (DeepSeek shape, 1.6 GB: +2%; Mixtral, 134 MB: cached)
+    p.nt_y = p.y_perm && (unsigned long long)rows * ncols * 4 > (256ull << 20);
     if (ws_bytes < pp_part_bytes(p.n_cu)) p.part = nullptr;
     const long long grid_pp = grid + (p.part ? p.n_cu : 0);
     hipLaunchKernelGGL((grouped_gemm_bf16_pp_kernel<UP, MOE_PP_BK, false>),

@@ -832,8 +832,10 @@ __device__ __forceinline__ void bwd256_body(const BwdArgs& p, char* lds, const i
         const int m = rbase + mi * 16 + r, n = ncol0 + c;
         if (m < rlim && n < p.N) {
           const size_t at = (size_t)m * p.N + n;
-          const u32x4 hv = *reinterpret_cast<const u32x4*>(p.h + at);
-          const u32x4 uv = *reinterpret_cast<const u32x4*>(p.u + at);
+          // h, u are read once and dH, dU are re-read only by the next launch,
+          // past the last-level cache at these sizes: non-temporal (+0.2-0.5%)
+          const u32x4 hv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.h + at));
+          const u32x4 uv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.u + at));
           const f32x4 g0 = *reinterpret_cast<const f32x4*>(st + r * SS + c);
           const f32x4 g1 = *reinterpret_cast<const f32x4*>(st + r * SS + c + 4);
           u32x4 dh, du;
@@ -854,8 +856,8 @@ __device__ __forceinline__ void bwd256_body(const BwdArgs& p, char* lds, const i
             du[j] = pack_bf16x2(duj[0], duj[1]);
           }
           bf16_t* d = p.dhu + (size_t)m * 2 * p.N + n;
-          *reinterpret_cast<u32x4*>(d) = dh;
-          *reinterpret_cast<u32x4*>(d + p.N) = du;
+          __builtin_nontemporal_store(dh, reinterpret_cast<u32x4*>(d));
+          __builtin_nontemporal_store(du, reinterpret_cast<u32x4*>(d + p.N));
         }
       }
     } else {

@@ -247,11 +247,21 @@ int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* in
  *   dW_down[e]   = sum_{r of e} act[r]^T dy_perm[r]     (fp32; 0 for empty experts).
  * Arguments: dy_perm [rows, d] (dtype); offsets as in moe_expert_up; W_down
  *   [E, f, d]; h, u [rows, f] (moe_expert_up_save); act [rows, f] (its
- *   a_out); dhu [rows, 2f] out (dtype); dW_down [E, f, d] fp32 out.
+ *   a_out); dhu [rows, 2f] out (dtype); dW_down [E, f, d] fp32 out;
+ *   workspace of moe_ffn_backward_workspace_size(E, rows, d, f) bytes or
+ *   NULL (optional: with it, a launch with fewer weight-gradient tiles than
+ *   about two per compute unit, such as the shared experts run as one
+ *   expert, cuts each expert's rows into chunks whose fp32 partials are
+ *   added in chunk order; the results stay deterministic either way).
  */
 int moe_expert_down_backward(const void* dy_perm, const int32_t* offsets, int E, int rows, int f,
                              int d, int dtype, const void* W_down, const void* h, const void* u,
-                             const void* act, void* dhu, float* dW_down, hipStream_t stream);
+                             const void* act, void* dhu, float* dW_down, void* workspace,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of the optional workspace of moe_expert_down_backward and
+ * moe_expert_up_backward (0 when no split would be used). */
+size_t moe_ffn_backward_workspace_size(int E, int rows, int d, int f);
 
 /*
  * moe_expert_up_backward -- gradients of moe_expert_up (layer 0) given dhu:
@@ -260,12 +270,14 @@ int moe_expert_down_backward(const void* dy_perm, const int32_t* offsets, int E,
  *   (fp32; 0 for empty experts), z_r = x[gather_idx[r]] (or x[r]).
  * Arguments: x, gather_idx, offsets, W_gate, W_up as in moe_expert_up; dhu
  *   [rows, 2f] (dtype); dx_perm [rows, d] fp32 out (added to when
- *   accumulate = 1); dW_gate, dW_up [E, d, f] fp32 out.
+ *   accumulate = 1); dW_gate, dW_up [E, d, f] fp32 out; workspace as in
+ *   moe_expert_down_backward (not used with a row gather).
  */
 int moe_expert_up_backward(const void* x, const int32_t* gather_idx, const int32_t* offsets,
                            int E, int rows, int d, int f, int dtype, const void* W_gate,
                            const void* W_up, const void* dhu, float* dx_perm, int accumulate,
-                           float* dW_gate, float* dW_up, hipStream_t stream);
+                           float* dW_gate, float* dW_up, void* workspace, size_t ws_bytes,
+                           hipStream_t stream);
 
 /*
  * moe_unpermute -- gradient of the dispatch (DisagMoE technical summary,

@@ -26,7 +26,7 @@ EXPORTS = (
     "moe_combine", "moe_expert_up_save",
     "moe_combine_backward", "moe_expert_down_backward", "moe_expert_up_backward",
     "moe_unpermute", "moe_topk_weights_backward", "moe_linear_backward_workspace_size",
-    "moe_linear_backward",
+    "moe_linear_backward", "moe_ffn_backward_workspace_size",
 )
 
 _lib = None
@@ -67,9 +67,10 @@ def load():
         "moe_combine_backward": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                        vp, vp]),
         "moe_expert_down_backward": (i32, [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
-                                           vp, vp]),
+                                           vp, vp, sz, vp]),
         "moe_expert_up_backward": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp,
-                                         i32, vp, vp, vp]),
+                                         i32, vp, vp, vp, sz, vp]),
+        "moe_ffn_backward_workspace_size": (sz, [i32, i32, i32, i32]),
         "moe_unpermute": (i32, [vp, vp, i32, i32, i32, i32, vp, vp]),
         "moe_topk_weights_backward": (i32, [vp, vp, vp, i32, i32, i32, i32, vp, vp]),
         "moe_linear_backward_workspace_size": (sz, [i32, i32, i32]),
@@ -209,21 +210,27 @@ def moe_combine_backward(dy, y_perm, inv, topk_w, T, d, k, dtype, y_shared, shar
     return st
 
 
+def moe_ffn_backward_workspace_size(E, rows, d, f):
+    return load().moe_ffn_backward_workspace_size(E, rows, d, f)
+
+
 def moe_expert_down_backward(dy_perm, offsets, E, rows, f, d, dtype, W_down, h, u, act, dhu,
-                             dW_down, stream=None, check=True):
+                             dW_down, workspace=None, ws_bytes=0, stream=None, check=True):
     st = load().moe_expert_down_backward(_p(dy_perm), _p(offsets), E, rows, f, d, dtype,
                                          _p(W_down), _p(h), _p(u), _p(act), _p(dhu), _p(dW_down),
-                                         _stream(stream))
+                                         _p(workspace), ws_bytes, _stream(stream))
     if check:
         _check("moe_expert_down_backward", st)
     return st
 
 
 def moe_expert_up_backward(x, gather_idx, offsets, E, rows, d, f, dtype, W_gate, W_up, dhu,
-                           dx_perm, accumulate, dW_gate, dW_up, stream=None, check=True):
+                           dx_perm, accumulate, dW_gate, dW_up, workspace=None, ws_bytes=0,
+                           stream=None, check=True):
     st = load().moe_expert_up_backward(_p(x), _p(gather_idx), _p(offsets), E, rows, d, f, dtype,
                                        _p(W_gate), _p(W_up), _p(dhu), _p(dx_perm), accumulate,
-                                       _p(dW_gate), _p(dW_up), _stream(stream))
+                                       _p(dW_gate), _p(dW_up), _p(workspace), ws_bytes,
+                                       _stream(stream))
     if check:
         _check("moe_expert_up_backward", st)
     return st

@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -41,12 +42,33 @@ def hipcc() -> str:
     return h
 
 
+def scratch_kernels(remarks: str) -> list[tuple[str, int]]:
+    """Kernels with a scratch (private) segment, from hipcc's
+    kernel-resource-usage remarks: (mangled name, bytes per lane)."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name is not None and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # every kernel keeps its state in registers and LDS: a kernel that spills
+    # (accumulators demoted to scratch run several times slower) is a build error
+    spilled = scratch_kernels(r.stderr)
+    if spilled:
+        raise RuntimeError(f"{src}: kernels with scratch memory: {spilled}")
     return obj
 
 

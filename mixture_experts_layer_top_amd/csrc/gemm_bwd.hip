@@ -32,6 +32,8 @@
 // Every sum runs in a fixed order: the results are deterministic.
 #include "moe_internal.h"
 
+#include <algorithm>
+
 namespace moe {
 // compute units of the current device (cached per device; 256 if unknown)
 int device_cu_count() {
@@ -79,6 +81,12 @@ struct BwdArgs {
   float* w0;
   float* w1;
   int n_split;
+  // WGRAD K split: each expert's rows are cut in ksplit chunks; chunk c of
+  // expert e writes its partial C_e as slab e * ksplit + c of w0 (the host
+  // points w0 at the workspace, n_split = N) and wgrad_sum_kernel adds the
+  // chunks in order into the weight gradients (ksplit = 1: straight to w0 / w1)
+  int ksplit;
+  float* part;  // host side only: the workspace, before w0 is pointed at it
 };
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -536,6 +544,7 @@ __device__ __forceinline__ void bwd256_body(const BwdArgs& p, char* lds, const i
   // round-robin (block order), so every XCD gets a share of every expert.
   const int tile = MODE == DGRAD ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
   int e, n0, m0 = 0, row0 = 0, row_end = 0, k_beg = 0, nk, my_nb, grow0, nb = 8, nbx = 4;
+  int kchunk = 0;  // WGRAD: the K chunk of a split expert
   if (MODE == DGRAD) {
     const PTile L = locate_dgrad256(p, tile);
     if (!L.ok) return;
@@ -549,10 +558,13 @@ __device__ __forceinline__ void bwd256_body(const BwdArgs& p, char* lds, const i
     grow0 = X ? 0 : 16 * nbx;
     nk = cdiv(p.K, PBK);
   } else {
-    const int per_e = p.tiles_m * p.tiles_n;
+    const int per_c = p.tiles_m * p.tiles_n;
+    const int per_e = per_c * p.ksplit;
     e = tile / per_e;
     if (e >= p.E) return;
-    const int local = tile - e * per_e;
+    const int lc = tile - e * per_e;
+    kchunk = lc / per_c;
+    const int local = lc - kchunk * per_c;
     // the side with fewer panels runs fastest, so the tiles running side by
     // side read the operand with more panels once
     int m_t, n_t;
@@ -569,6 +581,12 @@ __device__ __forceinline__ void bwd256_body(const BwdArgs& p, char* lds, const i
     my_nb = min(MI, max(0, cdiv(p.M - (m0 + grow0), 16)));
     k_beg = __builtin_amdgcn_readfirstlane(p.offsets[e]);
     row_end = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
+    if (p.ksplit > 1) {  // chunk kchunk of the expert's rows (stages of PBK; may be empty)
+      const int kc = cdiv(cdiv(row_end - k_beg, p.ksplit), PBK) * PBK;
+      k_beg = min(row_end, k_beg + kchunk * kc);
+      row_end = min(row_end, k_beg + kc);
+      e = e * p.ksplit + kchunk;  // output slab of the partial (w0 = part, n_split = N)
+    }
     nk = cdiv(row_end - k_beg, PBK);
   }
 
@@ -817,7 +835,9 @@ __device__ __forceinline__ void bwd256_body(const BwdArgs& p, char* lds, const i
   const bool add = EPI == EPI_F32 && p.accumulate;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
-    if (mi >= my_nb) break;
+    // a skipped block, not an early exit: with a second exit the loop may
+    // stay rolled, and acc[mi] then lives in scratch memory (3x slower)
+    if (mi >= my_nb) continue;
     // the block's accumulators into the staging area
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj)
@@ -986,6 +1006,25 @@ __global__ void wgrad_f32_kernel(const float* __restrict__ A, int lda, const int
 
 unsigned blocks_of(size_t n) { return (unsigned)((n + 255) / 256); }
 
+// dW_e = sum over the K chunks c (in order) of part[e][c] (M x N each), to
+// w0 (columns < n_split) / w1; 4 columns per thread (N, n_split multiples of 8)
+__global__ void wgrad_sum_kernel(const float* __restrict__ part, int E, int S, int M, int N,
+                                 int n_split, float* __restrict__ w0, float* __restrict__ w1) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;  // 4-column group
+  const size_t nv = (size_t)E * M * (N / 4);
+  if (i >= nv) return;
+  const int e = (int)(i / ((size_t)M * (N / 4)));
+  const size_t rem = i - (size_t)e * M * (N / 4);
+  const int m = (int)(rem / (N / 4)), n = (int)(rem - (size_t)m * (N / 4)) * 4;
+  const size_t mn = (size_t)M * N;
+  const float* src = part + (size_t)e * S * mn + (size_t)m * N + n;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+  for (int c = 1; c < S; ++c) acc += *reinterpret_cast<const f32x4*>(src + (size_t)c * mn);
+  float* dst = n < n_split ? w0 + ((size_t)e * M + m) * n_split + n
+                           : w1 + ((size_t)e * M + m) * (N - n_split) + (n - n_split);
+  __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(dst));
+}
+
 #ifndef MOE_BWD_PP
 #define MOE_BWD_PP 1
 #endif
@@ -1021,12 +1060,35 @@ int dgrad256_grid(BwdArgs& p, int rows) {
 int wgrad256_grid(BwdArgs& q) {
   q.tiles_m = cdiv(q.M, 256);
   q.tiles_n = cdiv(q.N, 256);
-  return pad8((long long)q.E * q.tiles_m * q.tiles_n);
+  return pad8((long long)q.E * q.ksplit * q.tiles_m * q.tiles_n);
 }
 bool dgrad_fast(const BwdArgs& p) { return MOE_BWD_FASTK && p.K % 64 == 0 && p.K0 % 64 == 0; }
 // the scalar-base form keeps 32-bit offsets within 32 rows of A and B
 bool wgrad_fast(const BwdArgs& q) {
   return MOE_BWD_FASTK && 32ll * (q.lda > q.ldb ? q.lda : q.ldb) * 2 < (1ll << 32);
+}
+
+// K chunks per expert for the weight gradients: when the launch has fewer
+// than two tiles per compute unit (few experts: the shared experts run as one
+// expert over every token), each expert's rows are cut into chunks of at least
+// 512 rows so that about two tiles per compute unit run; the partials need
+// E * S * M * N fp32 of workspace (with less, fewer chunks or none).
+int wgrad_chunks(int E, int rows, int M, int N, size_t ws_bytes) {
+  const long long tiles = (long long)E * cdiv(M, 256) * cdiv(N, 256);
+  const long long want = 2ll * device_cu_count();
+  if (tiles >= want || E <= 0) return 1;
+  long long S = (want + tiles - 1) / tiles;
+  S = std::min<long long>(S, std::max<long long>(1, (long long)rows / E / 512));
+  S = std::min<long long>(S, 16);
+  const long long per = (long long)E * M * N * 4;
+  if (per > 0) S = std::min<long long>(S, (long long)(ws_bytes / per));
+  return S >= 2 ? (int)S : 1;
+}
+
+void launch_wgrad_sum(const BwdArgs& q, hipStream_t s) {
+  const size_t nv = (size_t)q.E * q.M * (q.N / 4);
+  hipLaunchKernelGGL(wgrad_sum_kernel, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, s, q.part,
+                     q.E, q.ksplit, q.M, q.N, q.n_split, q.w0, q.w1);
 }
 
 template <int EPI>
@@ -1039,14 +1101,27 @@ void launch_dgrad256(BwdArgs p, int rows, hipStream_t s) {
   else
     hipLaunchKernelGGL((grouped_gemm_bwd256_kernel<DGRAD, EPI>), dim3(grid), dim3(512), 0, s, p);
 }
+// the kernel's view of a WGRAD launch: with a K split, the partials go to
+// slabs of the workspace (one M x N slab per expert and chunk)
+BwdArgs wgrad_kernel_args(const BwdArgs& q) {
+  BwdArgs g = q;
+  if (q.ksplit > 1) {
+    g.w0 = q.part;
+    g.w1 = nullptr;
+    g.n_split = q.N;
+  }
+  return g;
+}
 void launch_wgrad256(BwdArgs q, hipStream_t s) {
   const int grid = wgrad256_grid(q);
+  const BwdArgs g = wgrad_kernel_args(q);
   if (wgrad_fast(q))
     hipLaunchKernelGGL((grouped_gemm_bwd256_kernel<WGRAD, EPI_WGRAD, true>), dim3(grid), dim3(512), 0,
-                       s, q);
+                       s, g);
   else
     hipLaunchKernelGGL((grouped_gemm_bwd256_kernel<WGRAD, EPI_WGRAD>), dim3(grid), dim3(512), 0, s,
-                       q);
+                       g);
+  if (q.ksplit > 1) launch_wgrad_sum(q, s);
 }
 
 // DGRAD and WGRAD of one layer in one launch when both take the scalar-base
@@ -1064,8 +1139,9 @@ bool launch_pair256(BwdArgs p, BwdArgs q, int rows, hipStream_t s) {
   const long long typ = ((long long)rows / 256 + p.E / 2) * p.tiles_n;
   if (typ > (long long)MOE_BWD_PAIR_ROUNDS * device_cu_count()) return false;
   const int gw = wgrad256_grid(q);
-  hipLaunchKernelGGL((grouped_gemm_bwd256_pair_kernel<EPI>), dim3(gd + gw), dim3(512), 0, s, p, q,
-                     gd);
+  hipLaunchKernelGGL((grouped_gemm_bwd256_pair_kernel<EPI>), dim3(gd + gw), dim3(512), 0, s, p,
+                     wgrad_kernel_args(q), gd);
+  if (q.ksplit > 1) launch_wgrad_sum(q, s);
   return true;
 }
 
@@ -1077,10 +1153,20 @@ int dgrad_grid(int rows, int E, int tiles_n) {
 
 }  // namespace
 
+size_t ffn_backward_workspace_bytes(int E, int rows, int d, int f) {
+  const size_t huge = (size_t)1 << 62;
+  const int s1 = wgrad_chunks(E, rows, f, d, huge);      // dW_down: M = f, N = d
+  const int s0 = wgrad_chunks(E, rows, d, 2 * f, huge);  // dW_gate | dW_up: M = d, N = 2f
+  const size_t b1 = s1 > 1 ? (size_t)E * s1 * f * d * 4 : 0;
+  const size_t b0 = s0 > 1 ? (size_t)E * s0 * d * 2 * f * 4 : 0;
+  return align_up(b1 > b0 ? b1 : b0, 256);
+}
+
 hipError_t launch_expert_down_backward(const void* dy_perm, const int32_t* offsets, int E,
                                        int rows, int f, int d, bool bf16, const void* W_down,
                                        const void* h, const void* u, const void* act,
-                                       void* dhu, float* dW_down, hipStream_t s) {
+                                       void* dhu, float* dW_down, void* ws, size_t ws_bytes,
+                                       hipStream_t s) {
   if (!bf16) {
     if (rows > 0)
       hipLaunchKernelGGL(down_bwd_dgrad_f32_kernel, dim3(blocks_of((size_t)rows * f)), dim3(256),
@@ -1123,6 +1209,8 @@ hipError_t launch_expert_down_backward(const void* dy_perm, const int32_t* offse
   q.tiles_n = cdiv(d, BN);
   q.w0 = dW_down;
   q.n_split = d;
+  q.ksplit = MOE_BWD_PP ? wgrad_chunks(E, rows, f, d, ws_bytes) : 1;
+  q.part = static_cast<float*>(ws);
   if (launch_pair256<EPI_SWIGLU_BWD>(p, q, rows, s)) return hipGetLastError();
   if (rows > 0) {
     if (dgrad256_ok(p)) {
@@ -1146,7 +1234,8 @@ hipError_t launch_expert_up_backward(const void* x, const int32_t* gather_idx,
                                      const int32_t* offsets, int E, int rows, int d, int f,
                                      bool bf16, const void* W_gate, const void* W_up,
                                      const void* dhu, float* dx_perm, int accumulate,
-                                     float* dW_gate, float* dW_up, hipStream_t s) {
+                                     float* dW_gate, float* dW_up, void* ws, size_t ws_bytes,
+                                     hipStream_t s) {
   if (!bf16) {
     if (rows > 0)
       hipLaunchKernelGGL(up_bwd_dgrad_f32_kernel, dim3(blocks_of((size_t)rows * d)), dim3(256), 0,
@@ -1191,6 +1280,9 @@ hipError_t launch_expert_up_backward(const void* x, const int32_t* gather_idx,
   q.w0 = dW_gate;
   q.w1 = dW_up;
   q.n_split = f;
+  // the K split needs the 256 x 256 kernel (rows in order, no gather)
+  q.ksplit = (MOE_BWD_PP && gather_idx == nullptr) ? wgrad_chunks(E, rows, d, 2 * f, ws_bytes) : 1;
+  q.part = static_cast<float*>(ws);
   if (launch_pair256<EPI_F32>(p, q, rows, s)) return hipGetLastError();
   if (rows > 0) {
     if (dgrad256_ok(p)) {

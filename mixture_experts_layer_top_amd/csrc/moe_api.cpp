@@ -225,11 +225,19 @@ static int check_bwd_common(const int32_t* offsets, int E, int rows, int d, int 
   return MOE_OK;
 }
 
+size_t moe_ffn_backward_workspace_size(int E, int rows, int d, int f) {
+  if (E < 1 || E > 256 || rows < 0 || d <= 0 || f <= 0) return 0;
+  return moe::ffn_backward_workspace_bytes(E, rows, d, f);
+}
+
 int moe_expert_down_backward(const void* dy_perm, const int32_t* offsets, int E, int rows, int f,
                              int d, int dtype, const void* W_down, const void* h, const void* u,
-                             const void* act, void* dhu, float* dW_down, hipStream_t stream) {
+                             const void* act, void* dhu, float* dW_down, void* workspace,
+                             size_t ws_bytes, hipStream_t stream) {
   int st = check_bwd_common(offsets, E, rows, d, f, dtype);
   if (st != MOE_OK) return st;
+  if (workspace && !aligned16(workspace)) return MOE_ERR_UNSUPPORTED;
+  if (!workspace) ws_bytes = 0;
   if (!W_down || !dW_down) return MOE_ERR_INVALID;
   if (rows > 0 && (!dy_perm || !h || !u || !act || !dhu)) return MOE_ERR_INVALID;
   if (!aligned16(W_down) || !aligned16(dW_down) || (dy_perm && !aligned16(dy_perm)) ||
@@ -238,15 +246,18 @@ int moe_expert_down_backward(const void* dy_perm, const int32_t* offsets, int E,
     return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_expert_down_backward(dy_perm, offsets, E, rows, f, d,
                                                      dtype == MOE_BF16, W_down, h, u, act, dhu,
-                                                     dW_down, stream));
+                                                     dW_down, workspace, ws_bytes, stream));
 }
 
 int moe_expert_up_backward(const void* x, const int32_t* gather_idx, const int32_t* offsets,
                            int E, int rows, int d, int f, int dtype, const void* W_gate,
                            const void* W_up, const void* dhu, float* dx_perm, int accumulate,
-                           float* dW_gate, float* dW_up, hipStream_t stream) {
+                           float* dW_gate, float* dW_up, void* workspace, size_t ws_bytes,
+                           hipStream_t stream) {
   int st = check_bwd_common(offsets, E, rows, d, f, dtype);
   if (st != MOE_OK) return st;
+  if (workspace && !aligned16(workspace)) return MOE_ERR_UNSUPPORTED;
+  if (!workspace) ws_bytes = 0;
   if (accumulate != 0 && accumulate != 1) return MOE_ERR_INVALID;
   if (!W_gate || !W_up || !dW_gate || !dW_up) return MOE_ERR_INVALID;
   if (rows > 0 && (!x || !dhu || !dx_perm)) return MOE_ERR_INVALID;
@@ -256,7 +267,8 @@ int moe_expert_up_backward(const void* x, const int32_t* gather_idx, const int32
     return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_expert_up_backward(x, gather_idx, offsets, E, rows, d, f,
                                                    dtype == MOE_BF16, W_gate, W_up, dhu, dx_perm,
-                                                   accumulate, dW_gate, dW_up, stream));
+                                                   accumulate, dW_gate, dW_up, workspace, ws_bytes,
+                                                   stream));
 }
 
 int moe_unpermute(const float* dx_perm, const int32_t* inv, int T, int d, int k, int accumulate,

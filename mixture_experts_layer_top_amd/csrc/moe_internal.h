@@ -77,15 +77,18 @@ hipError_t launch_combine_backward(const float* dy, const float* y_perm, const i
                                    const float* topk_w, int T, int d, int k, bool bf16,
                                    const float* y_shared, const float* gate_logit, void* dy_perm,
                                    float* dw, void* dy_shared, float* dgate, hipStream_t s);
+size_t ffn_backward_workspace_bytes(int E, int rows, int d, int f);
 hipError_t launch_expert_down_backward(const void* dy_perm, const int32_t* offsets, int E,
                                        int rows, int f, int d, bool bf16, const void* W_down,
                                        const void* h, const void* u, const void* act,
-                                       void* dhu, float* dW_down, hipStream_t s);
+                                       void* dhu, float* dW_down, void* ws, size_t ws_bytes,
+                                       hipStream_t s);
 hipError_t launch_expert_up_backward(const void* x, const int32_t* gather_idx,
                                      const int32_t* offsets, int E, int rows, int d, int f,
                                      bool bf16, const void* W_gate, const void* W_up,
                                      const void* dhu, float* dx_perm, int accumulate,
-                                     float* dW_gate, float* dW_up, hipStream_t s);
+                                     float* dW_gate, float* dW_up, void* ws, size_t ws_bytes,
+                                     hipStream_t s);
 hipError_t launch_unpermute(const float* dx_perm, const int32_t* inv, int T, int d, int k,
                             bool accumulate, float* dx, hipStream_t s);
 hipError_t launch_topk_weights_backward(const float* logits, const int32_t* idx, const float* dw,

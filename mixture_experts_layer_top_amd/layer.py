@@ -230,6 +230,13 @@ class MoeLayer:
         self.dL = e(T, E)
         g = dict(dx=e(T, d), dW_r=e(d, E), dW_gate=e(E, d, f), dW_up=e(E, d, f),
                  dW_down=e(E, f, d), db=e(E) if t.get("b") is not None else None)
+        # the backward GEMMs' optional workspace (K-split partials of weight
+        # gradients with few tiles: here the shared experts, one expert over T rows)
+        need = L.moe_ffn_backward_workspace_size(E, R, d, f)
+        if self.ns:
+            need = max(need, L.moe_ffn_backward_workspace_size(1, T, d, self.fs_all))
+        self.ws_bwd_bytes = need
+        self.ws_bwd = e(max(need, 16), dt=torch.uint8)
         self.ws_lin_bytes = L.moe_linear_backward_workspace_size(T, d, E)
         self.ws_lin = e(max(self.ws_lin_bytes, 16), dt=torch.uint8)
         if self.ns:
@@ -263,11 +270,11 @@ class MoeLayer:
         mk("combine_bwd")
         L.moe_expert_down_backward(self.dy_perm, self.offsets, E, R, f, d, self.dtype,
                                    t["W_down"], self.h, self.u, self.a, self.dhu, g["dW_down"],
-                                   stream=stream)
+                                   self.ws_bwd, self.ws_bwd_bytes, stream=stream)
         mk("expert_down_bwd")
         L.moe_expert_up_backward(self.x_perm, None, self.offsets, E, R, d, f, self.dtype,
                                  t["W_gate"], t["W_up"], self.dhu, self.dx_perm, 0, g["dW_gate"],
-                                 g["dW_up"], stream=stream)
+                                 g["dW_up"], self.ws_bwd, self.ws_bwd_bytes, stream=stream)
         mk("expert_up_bwd")
         L.moe_unpermute(self.dx_perm, self.inv, T, d, k, 0, g["dx"], stream=stream)
         mk("unpermute")
@@ -281,10 +288,12 @@ class MoeLayer:
             fs = self.fs_all
             L.moe_expert_down_backward(self.dys, self.s_offsets, 1, T, fs, d, self.dtype,
                                        t["Ws_down"], self.s_h, self.s_u, self.s_a, self.s_dhu,
-                                       g["dWs_down"], stream=stream)
+                                       g["dWs_down"], self.ws_bwd, self.ws_bwd_bytes,
+                                       stream=stream)
             L.moe_expert_up_backward(t["x"], None, self.s_offsets, 1, T, d, fs, self.dtype,
                                      t["Ws_gate"], t["Ws_up"], self.s_dhu, g["dx"], 1,
-                                     g["dWs_gate"], g["dWs_up"], stream=stream)
+                                     g["dWs_gate"], g["dWs_up"], self.ws_bwd, self.ws_bwd_bytes,
+                                     stream=stream)
             if gated:
                 L.moe_linear_backward(t["x"], self.w_s_col, self.dgl, T, d, 1, self.dtype,
                                       g["dw_s"], None, g["dx"], self.ws_lin1, self.ws_lin1_bytes,

@@ -151,7 +151,7 @@ def test_backward_validation(lib):
     assert combine_bwd(dtype=7) == L.MOE_ERR_UNSUPPORTED
     assert combine_bwd(T=0) == L.MOE_OK
     db = dict(dy_perm=A, offsets=A, E=8, rows=32, f=64, d=64, dtype=L.MOE_BF16, W_down=A, h=A,
-              u=A, act=A, dhu=A, dW_down=A)
+              u=A, act=A, dhu=A, dW_down=A, workspace=None, ws_bytes=0)
     def down_bwd(**kw):
         return L.moe_expert_down_backward(**{**db, **kw}, stream=0, check=False)
     assert down_bwd(dtype=5) == L.MOE_ERR_UNSUPPORTED
@@ -160,8 +160,10 @@ def test_backward_validation(lib):
     assert down_bwd(offsets=None) == L.MOE_ERR_INVALID
     assert down_bwd(h=None) == L.MOE_ERR_INVALID
     assert down_bwd(dhu=MIS) == L.MOE_ERR_UNSUPPORTED
+    assert down_bwd(workspace=MIS, ws_bytes=1 << 20) == L.MOE_ERR_UNSUPPORTED
     ub = dict(x=A, gather_idx=None, offsets=A, E=8, rows=32, d=64, f=64, dtype=L.MOE_BF16,
-              W_gate=A, W_up=A, dhu=A, dx_perm=A, accumulate=0, dW_gate=A, dW_up=A)
+              W_gate=A, W_up=A, dhu=A, dx_perm=A, accumulate=0, dW_gate=A, dW_up=A,
+              workspace=None, ws_bytes=0)
     def up_bwd(**kw):
         return L.moe_expert_up_backward(**{**ub, **kw}, stream=0, check=False)
     assert up_bwd(accumulate=2) == L.MOE_ERR_INVALID

@@ -269,13 +269,70 @@ def test_expert_up_backward_gather_matches_permuted_copy(L):
     dWu = torch.empty_like(g["dW_up"])
     L.moe_expert_up_backward(layer["x"], m.perm_token, m.offsets, cfg.E, R, cfg.d, cfg.f,
                              L.MOE_BF16, layer["W_gate"], layer["W_up"], m.dhu, dx_perm, 0, dWg,
-                             dWu)
+                             dWu, None, 0)
     torch.cuda.synchronize()
     assert torch.equal(dx_perm, m.dx_perm)
     for got, ref in ((dWg, g["dW_gate"]), (dWu, g["dW_up"])):
         err = (got - ref).abs().max().item() / ref.abs().max().item()
         log(f"  gather vs copy weight gradient: max rel {err:.3e}")
         assert err <= 1e-6
+
+
+@pytest.mark.parametrize("counts", [[4173], [3100, 1073], [0, 4173]])
+def test_weight_gradient_k_split(L, counts):
+    """With the workspace, launches with few weight-gradient tiles cut each
+    expert's rows into K chunks and add the fp32 partials in chunk order.
+    The data gradients (dhu, dx_perm) are unchanged bit for bit; the weight
+    gradients equal their fp64 definition on the same bf16 operands
+    (dW_down[e] = act_e^T dy_e, dW_gate[e] = x_e^T dH_e, dW_up[e] = x_e^T dU_e)
+    to fp32 summation error, split or not; an empty expert's are zero."""
+    d, f = 512, 384
+    E, rows = len(counts), sum(counts)
+    ws_bytes = L.moe_ffn_backward_workspace_size(E, rows, d, f)
+    assert ws_bytes > 0  # 4-6 tiles per expert: the split is taken
+    gen = torch.Generator(device="cuda").manual_seed(rows + E)
+
+    def rnd(*shape, scale=1.0):
+        return (torch.randn(*shape, generator=gen, device="cuda") * scale).to(torch.bfloat16)
+
+    offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32,
+                           device="cuda")
+    dy, x = rnd(rows, d), rnd(rows, d)
+    h, u, act = rnd(rows, f), rnd(rows, f), rnd(rows, f)
+    W_down, W_gate, W_up = rnd(E, f, d, scale=f ** -0.5), rnd(E, d, f, scale=d ** -0.5), \
+        rnd(E, d, f, scale=d ** -0.5)
+    out = {}
+    for split in (False, True):
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if split else None
+        dhu = torch.empty(rows, 2 * f, dtype=torch.bfloat16, device="cuda")
+        dWd = torch.full((E, f, d), float("nan"), device="cuda")
+        dxp = torch.empty(rows, d, device="cuda")
+        dWg = torch.full((E, d, f), float("nan"), device="cuda")
+        dWu = torch.full((E, d, f), float("nan"), device="cuda")
+        L.moe_expert_down_backward(dy, offsets, E, rows, f, d, L.MOE_BF16, W_down, h, u, act, dhu,
+                                   dWd, ws, ws_bytes if split else 0)
+        L.moe_expert_up_backward(x, None, offsets, E, rows, d, f, L.MOE_BF16, W_gate, W_up, dhu,
+                                 dxp, 0, dWg, dWu, ws, ws_bytes if split else 0)
+        torch.cuda.synchronize()
+        out[split] = dict(dhu=dhu, dx=dxp, dW_down=dWd, dW_gate=dWg, dW_up=dWu)
+    assert torch.equal(out[False]["dhu"], out[True]["dhu"])
+    assert torch.equal(out[False]["dx"], out[True]["dx"])
+    dhu = out[True]["dhu"].cpu().double()
+    ops = {"dW_down": (act, dy), "dW_gate": (x, dhu[:, :f]), "dW_up": (x, dhu[:, f:])}
+    off = offsets.cpu().tolist()
+    for key, (a, b) in ops.items():
+        a = a.cpu().double() if torch.is_tensor(a) and a.is_cuda else a
+        b = b.cpu().double() if torch.is_tensor(b) and b.is_cuda else b
+        for e in range(E):
+            ref = (a[off[e]:off[e + 1]].T @ b[off[e]:off[e + 1]]).numpy()
+            for split in (False, True):
+                got = out[split][key][e].cpu().double().numpy()
+                if counts[e] == 0:
+                    assert np.count_nonzero(got) == 0, (key, e, split)
+                    continue
+                err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+                log(f"  {key}[{e}] split={split}: normwise {err:.2e}")
+                assert err <= 1e-5, (key, e, split, err)
 
 
 @pytest.mark.parametrize("E", [1, 3, 8, 16, 32, 100])

@@ -57,7 +57,9 @@ constexpr int OP_BYTES = BM * BK * 2;    // one operand stage: 8 KiB (both layou
 constexpr int STAGE = 2 * OP_BYTES;      // A then B
 
 enum { DGRAD = 0, WGRAD = 1 };
-enum { EPI_SWIGLU_BWD = 0, EPI_F32 = 1, EPI_WGRAD = 2 };
+// EPI_F32_ADD: EPI_F32 adding to out (accumulate = 1), a variant of its own so
+// that the common, store-only epilogue carries none of the loads' waits
+enum { EPI_SWIGLU_BWD = 0, EPI_F32 = 1, EPI_WGRAD = 2, EPI_F32_ADD = 3 };
 
 struct BwdArgs {
   const bf16_t* A;          // DGRAD: [rows, K], K contiguous; WGRAD: [*, M], M contiguous
@@ -832,9 +834,57 @@ __device__ __forceinline__ void bwd256_body(const BwdArgs& p, char* lds, const i
     rbase = m0 + grow0;
     rlim = p.M;
   }
-  const bool add = EPI == EPI_F32 && p.accumulate;
+  constexpr bool add = EPI == EPI_F32_ADD;
+  // The epilogue's loads (h and u for the SwiGLU backward; the old dX_perm
+  // when accumulating) are issued one 16-row block ahead, before the
+  // previous block's stores.  vmcnt counts loads and stores together and
+  // retires them in order: issued per block, every chunk's wait also drained
+  // the stores before it, one memory round trip per chunk; issued ahead, the
+  // wait for block mi + 1's loads leaves block mi's stores in flight and the
+  // loads' latency overlaps block mi's math and stores.
+  u32x4 hu[2][4];   // SwiGLU: [block parity][h, u of chunk 0, h, u of chunk 1]
+  f32x4 old[2][4];  // accumulate: [block parity][chunk]
+  // The loads are branch-free (a lane outside the output reads element 0,
+  // in bounds whenever the tile has a row, and discards it): loads inside
+  // branches make the compiler's wait counts fall back to waiting for all.
+  auto prefetch = [&](int mi, int b) {
+    if (EPI == EPI_SWIGLU_BWD) {
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int idx = c2 * 64 + lane_e, r = idx >> 3, c = (idx & 7) * 8;
+        const int m = rbase + mi * 16 + r, n = ncol0 + c;
+        const size_t at = m < rlim && n < p.N ? (size_t)m * p.N + n : 0;
+        // h, u are read once and dH, dU are re-read only by the next
+        // launch, past the last-level cache at these sizes: non-temporal
+        hu[b][2 * c2] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.h + at));
+        hu[b][2 * c2 + 1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.u + at));
+      }
+    } else if (MODE == DGRAD && add) {
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const int idx = c4 * 64 + lane_e, r = idx >> 4, c = (idx & 15) * 4;
+        const int m = rbase + mi * 16 + r, n = ncol0 + c;
+        const size_t at = m < rlim && n < p.N ? (size_t)m * p.N + n : 0;
+        old[b][c4] = *reinterpret_cast<const f32x4*>(p.out + at);
+      }
+    }
+  };
+  // Every prefetch is issued, before any branch (a block past the tile's
+  // rows reads element 0): a load issued on one path only would make the
+  // waits after the join count as if it were not in flight, and wait for it.
+  // The scheduling barriers keep the compiler from sinking the loads back to
+  // their use.
+  constexpr bool loads = EPI == EPI_SWIGLU_BWD || (MODE == DGRAD && add);
+  if (loads) {
+    prefetch(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
+    if (loads) {
+      if (mi + 1 < MI) prefetch(mi + 1, (mi + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // a skipped block, not an early exit: with a second exit the loop may
     // stay rolled, and acc[mi] then lives in scratch memory (3x slower)
     if (mi >= my_nb) continue;
@@ -851,11 +901,7 @@ __device__ __forceinline__ void bwd256_body(const BwdArgs& p, char* lds, const i
         const int idx = c2 * 64 + lane_e, r = idx >> 3, c = (idx & 7) * 8;
         const int m = rbase + mi * 16 + r, n = ncol0 + c;
         if (m < rlim && n < p.N) {
-          const size_t at = (size_t)m * p.N + n;
-          // h, u are read once and dH, dU are re-read only by the next launch,
-          // past the last-level cache at these sizes: non-temporal (+0.2-0.5%)
-          const u32x4 hv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.h + at));
-          const u32x4 uv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.u + at));
+          const u32x4 hv = hu[mi & 1][2 * c2], uv = hu[mi & 1][2 * c2 + 1];
           const f32x4 g0 = *reinterpret_cast<const f32x4*>(st + r * SS + c);
           const f32x4 g1 = *reinterpret_cast<const f32x4*>(st + r * SS + c + 4);
           u32x4 dh, du;
@@ -895,7 +941,7 @@ __device__ __forceinline__ void bwd256_body(const BwdArgs& p, char* lds, const i
             o = p.w0 + ((size_t)e * p.M + m) * p.n_split + n;
           else
             o = p.w1 + ((size_t)e * p.M + m) * (p.N - p.n_split) + (n - p.n_split);
-          if (add) v += *reinterpret_cast<const f32x4*>(o);
+          if (MODE == DGRAD && add) v += old[mi & 1][c4];
           // weight gradients are not read again soon: non-temporal stores
           // keep them from evicting the operand panels of running tiles
           // from the caches (+1-2%)
@@ -1283,10 +1329,15 @@ hipError_t launch_expert_up_backward(const void* x, const int32_t* gather_idx,
   // the K split needs the 256 x 256 kernel (rows in order, no gather)
   q.ksplit = (MOE_BWD_PP && gather_idx == nullptr) ? wgrad_chunks(E, rows, d, 2 * f, ws_bytes) : 1;
   q.part = static_cast<float*>(ws);
-  if (launch_pair256<EPI_F32>(p, q, rows, s)) return hipGetLastError();
+  const bool add = accumulate != 0;
+  if (add ? launch_pair256<EPI_F32_ADD>(p, q, rows, s) : launch_pair256<EPI_F32>(p, q, rows, s))
+    return hipGetLastError();
   if (rows > 0) {
     if (dgrad256_ok(p)) {
-      launch_dgrad256<EPI_F32>(p, rows, s);
+      if (add)
+        launch_dgrad256<EPI_F32_ADD>(p, rows, s);
+      else
+        launch_dgrad256<EPI_F32>(p, rows, s);
     } else {
       const int grid = dgrad_grid(rows, E, p.tiles_n);
       if (grid > 0)

@@ -432,6 +432,181 @@ __global__ __launch_bounds__(kThreads) void dx_linear_kernel(const float* __rest
   }
 }
 
+// ---- bf16 x and W: the same two products on the matrix cores
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  G is fp32: it enters as
+// hi + lo with hi = bf16(G), lo = bf16(G - hi).  G - hi is exact in fp32, so
+// |G - hi - lo| <= 2^-18 |G|, and every product with a bf16 x or W value is
+// exact in the fp32 accumulator: the result is an fp32 sum as above, in a
+// different but fixed order.
+typedef __attribute__((address_space(3))) bf16x4 lds_b16x4;
+
+__device__ __forceinline__ void split_bf16(float g, bf16_t& hi, bf16_t& lo) {
+  hi = f32_to_bf16(g);
+  lo = f32_to_bf16(g - bf16_to_f32(hi));
+}
+
+// 8 consecutive K values of one column for an MFMA operand, from a K-outer
+// LDS tile (row stride ld elements): the gfx950 LDS transpose read gives
+// lane l (g = l / 16) column l % 16 of rows kr .. kr + 3 (kr = 8 g + l % 16
+// / 4 addressed, 4 columns per lane); two reads cover rows 8 g .. 8 g + 7.
+__device__ __forceinline__ bf16x8 tr_frag(const bf16_t* tile, int ld, int kr, int col) {
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b16x4*)(tile + kr * ld + col));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b16x4*)(tile + (kr + 4) * ld + col));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// dW partials: part[c][i][e] = sum over the tokens t of chunk c of
+// x[t, i] G[t, e].  A workgroup takes 128 columns of x, NB * 16 experts
+// (blockIdx.z selects the group) and one token chunk, 32 tokens a step:
+// x and G (as hi, lo) are staged K-outer in LDS (rows 32 bytes longer than
+// the data, against bank conflicts) and both operands are read with the
+// transpose read; wave w owns columns 32 w .. 32 w + 31 (2 x NB blocks).
+constexpr int XM_COLS = 128, XM_K = 32, XM_LD = XM_COLS + 16;
+template <int NB>
+__global__ __launch_bounds__(kThreads) void xtg_mfma_kernel(const bf16_t* __restrict__ x,
+                                                            const float* __restrict__ G, int T,
+                                                            int d, int E, int tc_len,
+                                                            float* __restrict__ part) {
+  constexpr int EP = 16 * NB, GL = EP + 16;
+  __shared__ __attribute__((aligned(16))) bf16_t xs[XM_K * XM_LD];
+  __shared__ __attribute__((aligned(16))) bf16_t gh[XM_K * GL];
+  __shared__ __attribute__((aligned(16))) bf16_t gl[XM_K * GL];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c0 = blockIdx.x * XM_COLS, e0 = blockIdx.z * EP;
+  const int t0 = blockIdx.y * tc_len, t1 = min(T, t0 + tc_len);
+  const int kr = (lane >> 4) * 8 + ((lane & 15) >> 2), cq = (lane & 3) * 4;
+  f32x4 acc[2][NB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int tb = t0; tb < t1; tb += XM_K) {
+    const int nt = min(XM_K, t1 - tb);
+    __syncthreads();
+    // x: 32 rows x 16 chunks of 8 columns (d is a multiple of 8: a chunk is
+    // whole or past the end); zeros past the chunk's tokens
+    for (int q = threadIdx.x; q < XM_K * 16; q += kThreads) {
+      const int r = q >> 4, cc = (q & 15) * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (r < nt && c0 + cc < d) v = *reinterpret_cast<const u32x4*>(x + (size_t)(tb + r) * d + c0 + cc);
+      *reinterpret_cast<u32x4*>(xs + r * XM_LD + cc) = v;
+    }
+    for (int q = threadIdx.x; q < XM_K * EP; q += kThreads) {
+      const int r = q / EP, e = q % EP;
+      const float v = r < nt && e0 + e < E ? G[(size_t)(tb + r) * E + e0 + e] : 0.f;
+      split_bf16(v, gh[r * GL + e], gl[r * GL + e]);
+    }
+    __syncthreads();
+    bf16x8 a[2], bh[NB], bl[NB];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) a[mb] = tr_frag(xs, XM_LD, kr, 32 * w + 16 * mb + cq);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      bh[nb] = tr_frag(gh, GL, kr, 16 * nb + cq);
+      bl[nb] = tr_frag(gl, GL, kr, 16 * nb + cq);
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], bh[nb], acc[mb][nb], 0, 0, 0);
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], bl[nb], acc[mb][nb], 0, 0, 0);
+      }
+  }
+  // lane l holds columns c0 + 32 w + 16 mb + 4 (l / 16) + i, expert e0 + 16 nb + l % 16
+  const int e = e0 + (lane & 15);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = c0 + 32 * w + 16 * mb + 4 * (lane >> 4) + i;
+        if (col < d && e + 16 * nb < E)
+          part[((size_t)blockIdx.y * d + col) * E + e + 16 * nb] = acc[mb][nb][i];
+      }
+}
+
+// dx[t, i] += sum_e G[t, e] W[i, e], as C^T = W G^T: A = W (rows i, K = e),
+// B = G^T (K = e, columns t), both K-contiguous, so the fragments are
+// 16-byte LDS reads.  A workgroup takes 64 tokens x 256 columns, experts in
+// stages of 32 KS; wave w owns columns 64 w .. 64 w + 63 of all 64 tokens
+// (4 x 4 blocks).  The accumulators start from dx (lane l: token l % 16 of a
+// block, 4 consecutive columns), so dx is read and written once, 16 bytes
+// per lane, and the sum order is fixed.
+constexpr int DM_T = 64, DM_C = 256;
+template <int KS>
+__global__ __launch_bounds__(kThreads) void dx_mfma_kernel(const float* __restrict__ G,
+                                                           const bf16_t* __restrict__ W, int T,
+                                                           int d, int E, float* __restrict__ dx) {
+  constexpr int EK = 32 * KS, LD = EK + 8;  // experts per stage; LDS row stride (+16 bytes)
+  __shared__ __attribute__((aligned(16))) bf16_t ws[DM_C * LD];
+  __shared__ __attribute__((aligned(16))) bf16_t gh[DM_T * LD];
+  __shared__ __attribute__((aligned(16))) bf16_t gl[DM_T * LD];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, l15 = lane & 15;
+  const int t0 = blockIdx.y * DM_T, c0 = blockIdx.x * DM_C;
+  const bool wvec = (E % 8) == 0 && ((uintptr_t)W & 15) == 0;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int t = t0 + 16 * nb + l15, col = c0 + 64 * w + 16 * mb + 4 * g;
+      acc[mb][nb] = t < T && col < d ? *reinterpret_cast<const f32x4*>(dx + (size_t)t * d + col)
+                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  for (int e0 = 0; e0 < E; e0 += EK) {
+    __syncthreads();
+    // W rows c0 .. c0 + 255, experts e0 .. e0 + EK - 1 (zeros past d and E)
+    for (int q = threadIdx.x; q < DM_C * (EK / 8); q += kThreads) {
+      const int r = q / (EK / 8), ec = (q % (EK / 8)) * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (c0 + r < d) {
+        const bf16_t* src = W + (size_t)(c0 + r) * E + e0 + ec;
+        if (wvec) {
+          if (e0 + ec < E) v = *reinterpret_cast<const u32x4*>(src);
+        } else {
+          bf16_t b[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) b[j] = e0 + ec + j < E ? src[j] : bf16_t(0);
+          __builtin_memcpy(&v, b, 16);
+        }
+      }
+      *reinterpret_cast<u32x4*>(ws + r * LD + ec) = v;
+    }
+    for (int q = threadIdx.x; q < DM_T * EK; q += kThreads) {
+      const int r = q / EK, e = q % EK;
+      const float v = t0 + r < T && e0 + e < E ? G[(size_t)(t0 + r) * E + e0 + e] : 0.f;
+      split_bf16(v, gh[r * LD + e], gl[r * LD + e]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 a[4], bh[4], bl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a[j] = *reinterpret_cast<const bf16x8*>(ws + (64 * w + 16 * j + l15) * LD + 32 * ks + 8 * g);
+        bh[j] = *reinterpret_cast<const bf16x8*>(gh + (16 * j + l15) * LD + 32 * ks + 8 * g);
+        bl[j] = *reinterpret_cast<const bf16x8*>(gl + (16 * j + l15) * LD + 32 * ks + 8 * g);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], bh[nb], acc[mb][nb], 0, 0, 0);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], bl[nb], acc[mb][nb], 0, 0, 0);
+        }
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int t = t0 + 16 * nb + l15, col = c0 + 64 * w + 16 * mb + 4 * g;
+      if (t < T && col < d) *reinterpret_cast<f32x4*>(dx + (size_t)t * d + col) = acc[mb][nb];
+    }
+}
+
 template <int KS>
 void launch_cb(const float* dy, const float* y_perm, const int32_t* inv, const float* topk_w,
                int T, int d, bool bf16, const float* y_shared, const float* gate_logit,
@@ -494,9 +669,52 @@ hipError_t launch_topk_weights_backward(const float* logits, const int32_t* idx,
   return hipGetLastError();
 }
 
+// MFMA form (bf16 x): experts per workgroup group (16 NB), and tokens per
+// partial chunk: about 1024 workgroups over (column blocks x expert groups x
+// token chunks), a multiple of 32 between 32 and 1024
+int xtg_mfma_nb(int E) { return E <= 16 ? 1 : E <= 32 ? 2 : 4; }
+int xtg_mfma_chunk(int T, int d, int E) {
+  const long long blocks = (long long)cdiv(d, XM_COLS) * cdiv(E, 16 * xtg_mfma_nb(E));
+  const long long want = (long long)T * blocks / 1024;
+  return (int)std::min<long long>(1024, std::max<long long>(XM_K, (want + XM_K - 1) / XM_K * XM_K));
+}
+
 size_t linear_backward_workspace_bytes(int T, int d, int E) {
-  const size_t nc = (size_t)cdiv(T, xtg_chunk(T, d, E));
+  // partials [chunks, d, E] of whichever form runs (fp32 or bf16 x)
+  const size_t nc = (size_t)std::max(cdiv(T, xtg_chunk(T, d, E)), cdiv(T, xtg_mfma_chunk(T, d, E)));
   return align_up(nc * (size_t)d * E * sizeof(float), 256);
+}
+
+template <int NB>
+void launch_xtg_mfma(const bf16_t* x, const float* G, int T, int d, int E, float* dW, float* part,
+                     hipStream_t s) {
+  const int tc = xtg_mfma_chunk(T, d, E);
+  const int nc = cdiv(T, tc);
+  hipLaunchKernelGGL((xtg_mfma_kernel<NB>), dim3(cdiv(d, XM_COLS), nc, cdiv(E, 16 * NB)),
+                     dim3(kThreads), 0, s, x, G, T, d, E, tc, part);
+  const size_t n = (size_t)d * E;
+  hipLaunchKernelGGL(sum_chunks_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, part, nc, n, dW);
+}
+
+void launch_linear_bwd_mfma(const void* x, const void* W, const float* G, int T, int d, int E,
+                            float* dW, float* dx, void* ws, hipStream_t s) {
+  const bf16_t* xb = static_cast<const bf16_t*>(x);
+  float* part = static_cast<float*>(ws);
+  if (dW) {
+    const int nb = xtg_mfma_nb(E);
+    if (nb == 1) launch_xtg_mfma<1>(xb, G, T, d, E, dW, part, s);
+    else if (nb == 2) launch_xtg_mfma<2>(xb, G, T, d, E, dW, part, s);
+    else launch_xtg_mfma<4>(xb, G, T, d, E, dW, part, s);
+  }
+  if (dx) {
+    const dim3 grid(cdiv(d, DM_C), cdiv(T, DM_T));
+    const bf16_t* Wb = static_cast<const bf16_t*>(W);
+    if (E <= 32)
+      hipLaunchKernelGGL((dx_mfma_kernel<1>), grid, dim3(kThreads), 0, s, G, Wb, T, d, E, dx);
+    else
+      hipLaunchKernelGGL((dx_mfma_kernel<2>), grid, dim3(kThreads), 0, s, G, Wb, T, d, E, dx);
+  }
 }
 
 template <typename XT, int EB>
@@ -532,7 +750,7 @@ hipError_t launch_linear_backward(const void* x, const void* W, const float* G, 
                                   hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (bf16)
-    launch_linear_bwd_e<bf16_t>(x, W, G, T, d, E, dW, dx, ws, s);
+    launch_linear_bwd_mfma(x, W, G, T, d, E, dW, dx, ws, s);
   else
     launch_linear_bwd_e<float>(x, W, G, T, d, E, dW, dx, ws, s);
   if (db) hipLaunchKernelGGL(colsum_kernel, dim3(E), dim3(kThreads), 0, s, G, T, E, db);

@@ -360,7 +360,8 @@ def test_linear_backward_any_expert_count(L, E):
     for name, (got, ref) in refs.items():
         nrm, _, c = errors(got.cpu().double().numpy(), ref)
         log(f"  linear backward E={E} {name}: normwise {nrm:.2e}, c {c:.2e}")
-        # fp32 sums of at most T bf16 x fp32 products: far inside 1e-5
+        # fp32 sums of at most T products of bf16 x or W with G (G split
+        # exactly into bf16 hi + lo, residual <= 2^-18 |G|): far inside 1e-5
         assert nrm <= 1e-5 and c <= 1e-4, (name, nrm, c)
 
 

@@ -309,7 +309,12 @@ int moe_topk_weights_backward(const float* logits, const int32_t* topk_idx, cons
  *   dx += G W^T       (if dx != NULL; fp32, added to).
  * Arguments: x [T, d] (dtype), W [d, E] (dtype), G [T, E] fp32, dW [d, E]
  *   fp32 out or NULL, db [E] fp32 out or NULL, dx [T, d] fp32 in/out or NULL;
- *   workspace of moe_linear_backward_workspace_size(T, d, E) bytes (when dW).
+ *   workspace of moe_linear_backward_workspace_size(T, d, E) bytes, 16-byte
+ *   aligned (when dW, and always for bf16; MOE_ERR_WORKSPACE if missing or
+ *   smaller).
+ * bf16: both products run on the matrix cores with G entering as hi + lo,
+ *   hi = bf16(G), lo = bf16(G - hi) (|G - hi - lo| <= 2^-18 |G|; each
+ *   product is exact in the fp32 accumulators); fp32: plain fp32 FMA.
  * Requirements: 1 <= E <= 256; d a multiple of 8 and x, dx 16-byte aligned
  * (MOE_ERR_UNSUPPORTED otherwise: x rows and dx rows move as 16-byte vectors).
  * Every sum runs in a fixed order: the results are deterministic.

@@ -438,11 +438,37 @@ __global__ __launch_bounds__(kThreads) void dx_linear_kernel(const float* __rest
 // |G - hi - lo| <= 2^-18 |G|, and every product with a bf16 x or W value is
 // exact in the fp32 accumulator: the result is an fp32 sum as above, in a
 // different but fixed order.
+//
+// G is split once, into hi and lo arrays [T, EP] whose rows are padded with
+// zeros to EP = E rounded up to 64.  The operand loads then carry no guards:
+// a lane whose row or column lies outside an operand reads an in-bounds
+// element instead (its results are never stored), and experts past E meet
+// the zeros of the G side whatever the W side reads.  A guarded load (a
+// branch, or a select on the loaded value) makes the compiler wait for it
+// where it is guarded, one memory round trip at a time.
 typedef __attribute__((address_space(3))) bf16x4 lds_b16x4;
+
+__host__ __device__ __forceinline__ int split_ep(int E) { return (E + 63) / 64 * 64; }
 
 __device__ __forceinline__ void split_bf16(float g, bf16_t& hi, bf16_t& lo) {
   hi = f32_to_bf16(g);
   lo = f32_to_bf16(g - bf16_to_f32(hi));
+}
+
+// gh, gl [T, EP]: the split of G, zeros past E
+__global__ __launch_bounds__(kThreads) void split_g_kernel(const float* __restrict__ G, int T,
+                                                           int E, int EP, bf16_t* __restrict__ gh,
+                                                           bf16_t* __restrict__ gl) {
+  const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (size_t)T * EP) return;
+  const int t = (int)(i / EP), e = (int)(i - (size_t)t * EP);
+  split_bf16(e < E ? G[(size_t)t * E + e] : 0.f, gh[i], gl[i]);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
 }
 
 // 8 consecutive K values of one column for an MFMA operand, from a K-outer
@@ -458,45 +484,67 @@ __device__ __forceinline__ bf16x8 tr_frag(const bf16_t* tile, int ld, int kr, in
 // dW partials: part[c][i][e] = sum over the tokens t of chunk c of
 // x[t, i] G[t, e].  A workgroup takes 128 columns of x, NB * 16 experts
 // (blockIdx.z selects the group) and one token chunk, 32 tokens a step:
-// x and G (as hi, lo) are staged K-outer in LDS (rows 32 bytes longer than
-// the data, against bank conflicts) and both operands are read with the
+// x and G (hi, lo) are staged K-outer in LDS (rows 32 bytes longer than the
+// data, against bank conflicts) and both operands are read with the
 // transpose read; wave w owns columns 32 w .. 32 w + 31 (2 x NB blocks).
+// The next step's global loads are issued before this step's MFMAs; G rows
+// past the chunk are zeroed when staged (the x side may hold anything there).
 constexpr int XM_COLS = 128, XM_K = 32, XM_LD = XM_COLS + 16;
 template <int NB>
 __global__ __launch_bounds__(kThreads) void xtg_mfma_kernel(const bf16_t* __restrict__ x,
-                                                            const float* __restrict__ G, int T,
-                                                            int d, int E, int tc_len,
+                                                            const bf16_t* __restrict__ Gh,
+                                                            const bf16_t* __restrict__ Gl, int T,
+                                                            int d, int E, int EP, int tc_len,
                                                             float* __restrict__ part) {
-  constexpr int EP = 16 * NB, GL = EP + 16;
+  constexpr int EB = 16 * NB, GL = EB + 16;
+  constexpr int GCH = XM_K * (EB / 8);  // 16-byte chunks of a G tile
   __shared__ __attribute__((aligned(16))) bf16_t xs[XM_K * XM_LD];
   __shared__ __attribute__((aligned(16))) bf16_t gh[XM_K * GL];
   __shared__ __attribute__((aligned(16))) bf16_t gl[XM_K * GL];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int c0 = blockIdx.x * XM_COLS, e0 = blockIdx.z * EP;
+  const int c0 = blockIdx.x * XM_COLS, e0 = blockIdx.z * EB;
   const int t0 = blockIdx.y * tc_len, t1 = min(T, t0 + tc_len);
   const int kr = (lane >> 4) * 8 + ((lane & 15) >> 2), cq = (lane & 3) * 4;
+  // this thread's staging chunks: x rows q / 16, columns 8 (q % 16), for
+  // q = tid and tid + 256; G row tid / (EB / 8), experts 8 (tid % (EB / 8))
+  const int gr = threadIdx.x / (EB / 8), gc = (threadIdx.x % (EB / 8)) * 8;
+  const bool gload = threadIdx.x < GCH;
+  u32x4 xr[2], hr = {0u, 0u, 0u, 0u}, lr = {0u, 0u, 0u, 0u};
+  bool gin = false;
+  auto load = [&](int tb) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int q = threadIdx.x + k * kThreads, r = q >> 4, cc = (q & 15) * 8;
+      const bool in = tb + r < T && c0 + cc < d;
+      xr[k] = *reinterpret_cast<const u32x4*>(x + (in ? (size_t)(tb + r) * d + c0 + cc : 0));
+    }
+    if (gload) {
+      gin = tb + gr < t1;
+      const size_t off = gin ? (size_t)(tb + gr) * EP + e0 + gc : 0;
+      hr = *reinterpret_cast<const u32x4*>(Gh + off);
+      lr = *reinterpret_cast<const u32x4*>(Gl + off);
+    }
+  };
   f32x4 acc[2][NB];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (t0 < t1) load(t0);
   for (int tb = t0; tb < t1; tb += XM_K) {
-    const int nt = min(XM_K, t1 - tb);
-    __syncthreads();
-    // x: 32 rows x 16 chunks of 8 columns (d is a multiple of 8: a chunk is
-    // whole or past the end); zeros past the chunk's tokens
-    for (int q = threadIdx.x; q < XM_K * 16; q += kThreads) {
-      const int r = q >> 4, cc = (q & 15) * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (r < nt && c0 + cc < d) v = *reinterpret_cast<const u32x4*>(x + (size_t)(tb + r) * d + c0 + cc);
-      *reinterpret_cast<u32x4*>(xs + r * XM_LD + cc) = v;
+    __syncthreads();  // the previous step's fragment reads are done
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int q = threadIdx.x + k * kThreads;
+      *reinterpret_cast<u32x4*>(xs + (q >> 4) * XM_LD + (q & 15) * 8) = xr[k];
     }
-    for (int q = threadIdx.x; q < XM_K * EP; q += kThreads) {
-      const int r = q / EP, e = q % EP;
-      const float v = r < nt && e0 + e < E ? G[(size_t)(tb + r) * E + e0 + e] : 0.f;
-      split_bf16(v, gh[r * GL + e], gl[r * GL + e]);
+    if (gload) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(gh + gr * GL + gc) = gin ? hr : z;
+      *reinterpret_cast<u32x4*>(gl + gr * GL + gc) = gin ? lr : z;
     }
     __syncthreads();
+    if (tb + XM_K < t1) load(tb + XM_K);
     bf16x8 a[2], bh[NB], bl[NB];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) a[mb] = tr_frag(xs, XM_LD, kr, 32 * w + 16 * mb + cq);
@@ -528,83 +576,92 @@ __global__ __launch_bounds__(kThreads) void xtg_mfma_kernel(const bf16_t* __rest
 }
 
 // dx[t, i] += sum_e G[t, e] W[i, e], as C^T = W G^T: A = W (rows i, K = e),
-// B = G^T (K = e, columns t), both K-contiguous, so the fragments are
-// 16-byte LDS reads.  A workgroup takes 64 tokens x 256 columns, experts in
-// stages of 32 KS; wave w owns columns 64 w .. 64 w + 63 of all 64 tokens
-// (4 x 4 blocks).  The accumulators start from dx (lane l: token l % 16 of a
-// block, 4 consecutive columns), so dx is read and written once, 16 bytes
-// per lane, and the sum order is fixed.
-constexpr int DM_T = 64, DM_C = 256;
-template <int KS>
-__global__ __launch_bounds__(kThreads) void dx_mfma_kernel(const float* __restrict__ G,
+// B = G^T (K = e, columns t).  Both are K-contiguous in memory (W [d, E],
+// the split G [T, EP] row-major), so each lane loads its fragments directly:
+// 8 experts of one W row (kept in registers across the tokens when E <= 32
+// KS) and 8 experts of one G row; no LDS.  Wave w of a workgroup owns
+// columns 64 w .. 64 w + 63 of the block's 256 and walks its tokens 64 at a
+// time (4 x 4 blocks of 16 x 16).  The accumulators start from dx (lane l:
+// token l % 16 of a block, 4 consecutive columns), so dx is read and written
+// once, 16 bytes per lane, and the sum order is fixed: experts in order, hi
+// before lo.  VEC: W rows 16-byte aligned (E a multiple of 8, W aligned).
+#ifndef MOE_DX_TOKENS
+#define MOE_DX_TOKENS 128
+#endif
+constexpr int DM_T = MOE_DX_TOKENS, DM_C = 256;
+template <int KS, bool VEC>
+__global__ __launch_bounds__(kThreads) void dx_mfma_kernel(const bf16_t* __restrict__ Gh,
+                                                           const bf16_t* __restrict__ Gl,
                                                            const bf16_t* __restrict__ W, int T,
-                                                           int d, int E, float* __restrict__ dx) {
-  constexpr int EK = 32 * KS, LD = EK + 8;  // experts per stage; LDS row stride (+16 bytes)
-  __shared__ __attribute__((aligned(16))) bf16_t ws[DM_C * LD];
-  __shared__ __attribute__((aligned(16))) bf16_t gh[DM_T * LD];
-  __shared__ __attribute__((aligned(16))) bf16_t gl[DM_T * LD];
+                                                           int d, int E, int EP,
+                                                           float* __restrict__ dx) {
+  constexpr int EK = 32 * KS;  // experts per pass
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, l15 = lane & 15;
-  const int t0 = blockIdx.y * DM_T, c0 = blockIdx.x * DM_C;
-  const bool wvec = (E % 8) == 0 && ((uintptr_t)W & 15) == 0;
-  f32x4 acc[4][4];
+  const int c0 = blockIdx.x * DM_C + 64 * w;  // the wave's first column
+  const int tb = blockIdx.y * DM_T;
+  const int npass = cdiv(E, EK);
+  bf16x8 a[4][KS];
+  auto load_a = [&](int e0) {
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int t = t0 + 16 * nb + l15, col = c0 + 64 * w + 16 * mb + 4 * g;
-      acc[mb][nb] = t < T && col < d ? *reinterpret_cast<const f32x4*>(dx + (size_t)t * d + col)
-                                     : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  for (int e0 = 0; e0 < E; e0 += EK) {
-    __syncthreads();
-    // W rows c0 .. c0 + 255, experts e0 .. e0 + EK - 1 (zeros past d and E)
-    for (int q = threadIdx.x; q < DM_C * (EK / 8); q += kThreads) {
-      const int r = q / (EK / 8), ec = (q % (EK / 8)) * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (c0 + r < d) {
-        const bf16_t* src = W + (size_t)(c0 + r) * E + e0 + ec;
-        if (wvec) {
-          if (e0 + ec < E) v = *reinterpret_cast<const u32x4*>(src);
+      for (int ks = 0; ks < KS; ++ks) {
+        const int i = c0 + 16 * mb + l15, e = e0 + 32 * ks + 8 * g;
+        if (VEC) {
+          const size_t off = i < d && e < E ? (size_t)i * E + e : 0;
+          a[mb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(W + off));
         } else {
           bf16_t b[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) b[j] = e0 + ec + j < E ? src[j] : bf16_t(0);
-          __builtin_memcpy(&v, b, 16);
+          for (int j = 0; j < 8; ++j) b[j] = W[i < d && e + j < E ? (size_t)i * E + e + j : 0];
+          __builtin_memcpy(&a[mb][ks], b, 16);
         }
       }
-      *reinterpret_cast<u32x4*>(ws + r * LD + ec) = v;
-    }
-    for (int q = threadIdx.x; q < DM_T * EK; q += kThreads) {
-      const int r = q / EK, e = q % EK;
-      const float v = t0 + r < T && e0 + e < E ? G[(size_t)(t0 + r) * E + e0 + e] : 0.f;
-      split_bf16(v, gh[r * LD + e], gl[r * LD + e]);
-    }
-    __syncthreads();
+  };
+  if (npass == 1) load_a(0);
+  for (int sb = 0; sb < DM_T / 64; ++sb) {
+    const int t0 = tb + 64 * sb;
+    if (t0 >= T) break;
+    f32x4 acc[4][4];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 a[4], bh[4], bl[4];
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        a[j] = *reinterpret_cast<const bf16x8*>(ws + (64 * w + 16 * j + l15) * LD + 32 * ks + 8 * g);
-        bh[j] = *reinterpret_cast<const bf16x8*>(gh + (16 * j + l15) * LD + 32 * ks + 8 * g);
-        bl[j] = *reinterpret_cast<const bf16x8*>(gl + (16 * j + l15) * LD + 32 * ks + 8 * g);
+      for (int nb = 0; nb < 4; ++nb) {
+        const int t = t0 + 16 * nb + l15, col = c0 + 16 * mb + 4 * g;
+        const size_t off = t < T && col < d ? (size_t)t * d + col : 0;
+        acc[mb][nb] = *reinterpret_cast<const f32x4*>(dx + off);
       }
+    for (int ps = 0; ps < npass; ++ps) {
+      const int e0 = ps * EK;
+      if (npass > 1) load_a(e0);
+      bf16x8 bh[4][KS], bl[4][KS];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], bh[nb], acc[mb][nb], 0, 0, 0);
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb], bl[nb], acc[mb][nb], 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) {
+          const int t = t0 + 16 * nb + l15;
+          const size_t off = (size_t)(t < T ? t : 0) * EP + e0 + 32 * ks + 8 * g;
+          bh[nb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(Gh + off));
+          bl[nb][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(Gl + off));
         }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb][ks], bh[nb][ks], acc[mb][nb], 0, 0, 0);
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mb][ks], bl[nb][ks], acc[mb][nb], 0, 0, 0);
+          }
     }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int t = t0 + 16 * nb + l15, col = c0 + 16 * mb + 4 * g;
+        if (t < T && col < d) *reinterpret_cast<f32x4*>(dx + (size_t)t * d + col) = acc[mb][nb];
+      }
   }
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int t = t0 + 16 * nb + l15, col = c0 + 64 * w + 16 * mb + 4 * g;
-      if (t < T && col < d) *reinterpret_cast<f32x4*>(dx + (size_t)t * d + col) = acc[mb][nb];
-    }
 }
 
 template <int KS>
@@ -679,41 +736,63 @@ int xtg_mfma_chunk(int T, int d, int E) {
   return (int)std::min<long long>(1024, std::max<long long>(XM_K, (want + XM_K - 1) / XM_K * XM_K));
 }
 
-size_t linear_backward_workspace_bytes(int T, int d, int E) {
-  // partials [chunks, d, E] of whichever form runs (fp32 or bf16 x)
+// workspace: partials [chunks, d, E] fp32 of whichever form runs (fp32 or
+// bf16 x), then the split G (hi, lo: [T, EP] bf16 each) of the bf16 form
+size_t linear_partials_bytes(int T, int d, int E) {
   const size_t nc = (size_t)std::max(cdiv(T, xtg_chunk(T, d, E)), cdiv(T, xtg_mfma_chunk(T, d, E)));
   return align_up(nc * (size_t)d * E * sizeof(float), 256);
 }
+size_t split_g_bytes(int T, int E) {
+  return align_up((size_t)T * split_ep(E) * sizeof(bf16_t), 256);
+}
+size_t linear_backward_workspace_bytes(int T, int d, int E) {
+  return linear_partials_bytes(T, d, E) + 2 * split_g_bytes(T, E);
+}
 
 template <int NB>
-void launch_xtg_mfma(const bf16_t* x, const float* G, int T, int d, int E, float* dW, float* part,
-                     hipStream_t s) {
+void launch_xtg_mfma(const bf16_t* x, const bf16_t* gh, const bf16_t* gl, int T, int d, int E,
+                     float* dW, float* part, hipStream_t s) {
   const int tc = xtg_mfma_chunk(T, d, E);
   const int nc = cdiv(T, tc);
   hipLaunchKernelGGL((xtg_mfma_kernel<NB>), dim3(cdiv(d, XM_COLS), nc, cdiv(E, 16 * NB)),
-                     dim3(kThreads), 0, s, x, G, T, d, E, tc, part);
+                     dim3(kThreads), 0, s, x, gh, gl, T, d, E, split_ep(E), tc, part);
   const size_t n = (size_t)d * E;
   hipLaunchKernelGGL(sum_chunks_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, s, part, nc, n, dW);
 }
 
+template <int KS>
+void launch_dx_mfma(const bf16_t* gh, const bf16_t* gl, const bf16_t* W, int T, int d, int E,
+                    float* dx, hipStream_t s) {
+  const dim3 grid(cdiv(d, DM_C), cdiv(T, DM_T));
+  const int EP = split_ep(E);
+  if (E % 8 == 0 && ((uintptr_t)W & 15) == 0)
+    hipLaunchKernelGGL((dx_mfma_kernel<KS, true>), grid, dim3(kThreads), 0, s, gh, gl, W, T, d, E,
+                       EP, dx);
+  else
+    hipLaunchKernelGGL((dx_mfma_kernel<KS, false>), grid, dim3(kThreads), 0, s, gh, gl, W, T, d,
+                       E, EP, dx);
+}
+
 void launch_linear_bwd_mfma(const void* x, const void* W, const float* G, int T, int d, int E,
                             float* dW, float* dx, void* ws, hipStream_t s) {
-  const bf16_t* xb = static_cast<const bf16_t*>(x);
   float* part = static_cast<float*>(ws);
+  bf16_t* gh = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + linear_partials_bytes(T, d, E));
+  bf16_t* gl = reinterpret_cast<bf16_t*>(reinterpret_cast<char*>(gh) + split_g_bytes(T, E));
+  const size_t n = (size_t)T * split_ep(E);
+  hipLaunchKernelGGL(split_g_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, G, T, E, split_ep(E), gh, gl);
   if (dW) {
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
     const int nb = xtg_mfma_nb(E);
-    if (nb == 1) launch_xtg_mfma<1>(xb, G, T, d, E, dW, part, s);
-    else if (nb == 2) launch_xtg_mfma<2>(xb, G, T, d, E, dW, part, s);
-    else launch_xtg_mfma<4>(xb, G, T, d, E, dW, part, s);
+    if (nb == 1) launch_xtg_mfma<1>(xb, gh, gl, T, d, E, dW, part, s);
+    else if (nb == 2) launch_xtg_mfma<2>(xb, gh, gl, T, d, E, dW, part, s);
+    else launch_xtg_mfma<4>(xb, gh, gl, T, d, E, dW, part, s);
   }
   if (dx) {
-    const dim3 grid(cdiv(d, DM_C), cdiv(T, DM_T));
     const bf16_t* Wb = static_cast<const bf16_t*>(W);
-    if (E <= 32)
-      hipLaunchKernelGGL((dx_mfma_kernel<1>), grid, dim3(kThreads), 0, s, G, Wb, T, d, E, dx);
-    else
-      hipLaunchKernelGGL((dx_mfma_kernel<2>), grid, dim3(kThreads), 0, s, G, Wb, T, d, E, dx);
+    if (E <= 32) launch_dx_mfma<1>(gh, gl, Wb, T, d, E, dx, s);
+    else launch_dx_mfma<2>(gh, gl, Wb, T, d, E, dx, s);
   }
 }
 

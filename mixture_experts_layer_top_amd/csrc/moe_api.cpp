@@ -311,9 +311,10 @@ int moe_linear_backward(const void* x, const void* W, const float* G, int T, int
   if (!G || (dW && !x) || (dx && !W)) return MOE_ERR_INVALID;
   if (!dims_ok(d)) return MOE_ERR_UNSUPPORTED;
   if ((dW && !aligned16(x)) || (dx && !aligned16(dx))) return MOE_ERR_UNSUPPORTED;
-  if (dW) {
+  if (dW || dtype == MOE_BF16) {  // dW partials; bf16: G split into hi, lo
     const size_t need = moe::linear_backward_workspace_bytes(T, d, E);
     if (!workspace || ws_bytes < need) return MOE_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MOE_ERR_UNSUPPORTED;
   }
   return hip_status(moe::launch_linear_backward(x, W, G, T, d, E, dtype == MOE_BF16, dW, db, dx,
                                                 workspace, stream));

@@ -193,6 +193,9 @@ def test_backward_validation(lib):
     assert lin_bwd(x=MIS) == L.MOE_ERR_UNSUPPORTED
     assert lin_bwd(dx=MIS) == L.MOE_ERR_UNSUPPORTED
     assert lin_bwd(ws_bytes=16) == L.MOE_ERR_WORKSPACE
+    # bf16 splits G into the workspace even without dW
+    assert lin_bwd(dW=None, workspace=None, ws_bytes=0) == L.MOE_ERR_WORKSPACE
+    assert lin_bwd(workspace=MIS) == L.MOE_ERR_UNSUPPORTED
     assert lin_bwd(T=0) == L.MOE_OK
     assert L.moe_linear_backward_workspace_size(16, 64, 8) > 0
 

@@ -116,36 +116,80 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(const f32x4* __rest
   }
 }
 
-// dL [T, E] from the fp32 logits, the selection and dw; one thread per token
+// dL [T, E] from the fp32 logits, the selection and dw.  LPT lanes per token
+// (a power of two >= E, at most 64): lane li takes experts li, li + LPT, ...
+// (at most 4, E <= 256), so a token's logits are read and dL written
+// contiguously; its max and sums are xor-shuffle reductions over its lanes
+// (a fixed order).  Renormalised: w_j = softmax over the k selected logits,
+// dL[e_j] = w_j (dw_j - s), s = sum_j w_j dw_j, 0 elsewhere; otherwise
+// p = softmax over all E, dL[e] = p_e ([e = e_j] dw_j - s), s = sum_j p_{e_j} dw_j.
+template <int LPT>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int off = LPT / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+template <int LPT>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = LPT / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+template <int LPT>
 __global__ __launch_bounds__(kThreads) void topk_weights_backward_kernel(
     const float* __restrict__ L, const int32_t* __restrict__ idx, const float* __restrict__ dw,
     int T, int E, int k, int renorm, float* __restrict__ dL) {
-  const int t = blockIdx.x * kThreads + threadIdx.x;
-  if (t >= T) return;
-  const float* Lt = L + (size_t)t * E;
-  const int32_t* it = idx + (size_t)t * k;
-  const float* dwt = dw + (size_t)t * k;
-  float* out = dL + (size_t)t * E;
-  if (renorm) {
-    // softmax over the k selected logits
-    float m = -INFINITY;
-    for (int j = 0; j < k; ++j) m = fmaxf(m, Lt[it[j]]);
-    float z = 0.f;
-    for (int j = 0; j < k; ++j) z += __expf(Lt[it[j]] - m);
-    float s = 0.f;
-    for (int j = 0; j < k; ++j) s += __expf(Lt[it[j]] - m) / z * dwt[j];
-    for (int e = 0; e < E; ++e) out[e] = 0.f;
-    for (int j = 0; j < k; ++j) out[it[j]] = __expf(Lt[it[j]] - m) / z * (dwt[j] - s);
-  } else {
-    float m = -INFINITY;
-    for (int e = 0; e < E; ++e) m = fmaxf(m, Lt[e]);
-    float z = 0.f;
-    for (int e = 0; e < E; ++e) z += __expf(Lt[e] - m);
-    float s = 0.f;
-    for (int j = 0; j < k; ++j) s += __expf(Lt[it[j]] - m) / z * dwt[j];
-    for (int e = 0; e < E; ++e) out[e] = -__expf(Lt[e] - m) / z * s;
-    for (int j = 0; j < k; ++j) out[it[j]] += __expf(Lt[it[j]] - m) / z * dwt[j];
+  constexpr int NE = 4;
+  const int gid = blockIdx.x * kThreads + threadIdx.x;
+  const int t = gid / LPT, li = gid % LPT;
+  const bool live = t < T;
+  const int tt = live ? t : 0;  // every lane takes part in the shuffles
+  const float* Lt = L + (size_t)tt * E;
+  float lv[NE], dsel[NE];
+  bool sel[NE], in[NE];
+#pragma unroll
+  for (int r = 0; r < NE; ++r) {
+    const int e = li + LPT * r;
+    in[r] = e < E;
+    lv[r] = in[r] ? Lt[e] : 0.f;
+    sel[r] = false;
+    dsel[r] = 0.f;
   }
+  for (int j = 0; j < k; ++j) {
+    const int ej = idx[(size_t)tt * k + j];
+    const float dj = dw[(size_t)tt * k + j];
+#pragma unroll
+    for (int r = 0; r < NE; ++r)
+      if (li + LPT * r == ej) {
+        sel[r] = true;
+        dsel[r] = dj;
+      }
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < NE; ++r)
+    if (in[r] && (!renorm || sel[r])) m = fmaxf(m, lv[r]);
+  m = group_max<LPT>(m);
+  float q[NE], z = 0.f;
+#pragma unroll
+  for (int r = 0; r < NE; ++r) {
+    q[r] = in[r] && (!renorm || sel[r]) ? __expf(lv[r] - m) : 0.f;
+    z += q[r];
+  }
+  z = group_sum<LPT>(z);
+  float sp = 0.f;
+#pragma unroll
+  for (int r = 0; r < NE; ++r)
+    if (sel[r]) sp += q[r] / z * dsel[r];
+  sp = group_sum<LPT>(sp);
+  if (!live) return;
+  float* out = dL + (size_t)t * E;
+#pragma unroll
+  for (int r = 0; r < NE; ++r)
+    if (in[r]) {
+      const float pe = q[r] / z;
+      out[li + LPT * r] = renorm ? (sel[r] ? pe * (dsel[r] - sp) : 0.f) : pe * (dsel[r] - sp);
+    }
 }
 
 template <typename XT>
@@ -721,8 +765,17 @@ hipError_t launch_topk_weights_backward(const float* logits, const int32_t* idx,
                                         int T, int E, int k, bool renorm, float* dL,
                                         hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_weights_backward_kernel, dim3(cdiv(T, kThreads)), dim3(kThreads), 0, s,
-                     logits, idx, dw, T, E, k, renorm ? 1 : 0, dL);
+  const int lpt = E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : 64;
+  const dim3 grid((unsigned)(((size_t)T * lpt + kThreads - 1) / kThreads));
+  const int rn = renorm ? 1 : 0;
+  if (lpt == 8)
+    hipLaunchKernelGGL(topk_weights_backward_kernel<8>, grid, dim3(kThreads), 0, s, logits, idx, dw, T, E, k, rn, dL);
+  else if (lpt == 16)
+    hipLaunchKernelGGL(topk_weights_backward_kernel<16>, grid, dim3(kThreads), 0, s, logits, idx, dw, T, E, k, rn, dL);
+  else if (lpt == 32)
+    hipLaunchKernelGGL(topk_weights_backward_kernel<32>, grid, dim3(kThreads), 0, s, logits, idx, dw, T, E, k, rn, dL);
+  else
+    hipLaunchKernelGGL(topk_weights_backward_kernel<64>, grid, dim3(kThreads), 0, s, logits, idx, dw, T, E, k, rn, dL);
   return hipGetLastError();
 }
 

@@ -230,19 +230,29 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
   for (int j = kKR; j < k; ++j) place(j, it[j]);
 }
 
-// x_perm[r, :] = x[perm_token[r], :]; rows of `vecs` 16-byte vectors.
+// x_perm[r, :] = x[perm_token[r], :]; rows of `vecs` 16-byte vectors.  A
+// block copies 8 rows; a thread takes columns c, c + 256, ... of all 8 and
+// issues the 8 loads of a column before its stores (rows past R re-read the
+// block's first source row and are not stored), so 8 loads are in flight
+// per thread instead of one load-store round trip at a time.
 constexpr int kGatherRows = 8;
 __global__ __launch_bounds__(kThreads) void gather_kernel(const u32x4* __restrict__ x,
                                                           const int32_t* __restrict__ perm_token,
                                                           int R, int vecs,
                                                           u32x4* __restrict__ x_perm) {
   const int r0 = blockIdx.x * kGatherRows;
-  const int n = min(kGatherRows, R - r0) * vecs;
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    const int rr = i / vecs, c = i - rr * vecs;
-    const int r = r0 + rr;
-    const int t = perm_token[r];
-    x_perm[(size_t)r * vecs + c] = x[(size_t)t * vecs + c];
+  const int nr = min(kGatherRows, R - r0);
+  size_t src[kGatherRows];
+#pragma unroll
+  for (int j = 0; j < kGatherRows; ++j)
+    src[j] = (size_t)perm_token[r0 + (j < nr ? j : 0)] * vecs;
+  for (int c = threadIdx.x; c < vecs; c += kThreads) {
+    u32x4 v[kGatherRows];
+#pragma unroll
+    for (int j = 0; j < kGatherRows; ++j) v[j] = x[src[j] + c];
+#pragma unroll
+    for (int j = 0; j < kGatherRows; ++j)
+      if (j < nr) x_perm[(size_t)(r0 + j) * vecs + c] = v[j];
   }
 }
 

@@ -123,6 +123,22 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, const void* x, int
 size_t moe_ffn_workspace_size(int E, int rows, int d, int f);
 
 /*
+ * moe_workspace_size -- one workspace size that serves every forward call of
+ * a layer with T tokens, model dim d, expert FFN dim f, E experts and top-k
+ * (moe_route, moe_permute, moe_expert_up / moe_expert_down / moe_ffn_forward
+ * with rows = T*k): the calls of one forward run in order on one stream, so
+ * they can share one buffer of this many bytes (16-byte aligned).  It is at
+ * least each of moe_route_workspace_size(d, E, dtype),
+ * moe_permute_workspace_size(T, E, k) and moe_ffn_workspace_size(E, T*k, d, f);
+ * the FFN part does not depend on the shapes, so the same buffer also serves
+ * a shared-expert FFN (E = 1, rows = T, any f).  Returns 0 for T = 0 (every
+ * call is then a no-op that reads no workspace) and for arguments any call
+ * would reject.  The buffer must not be shared by calls running at the same
+ * time.
+ */
+size_t moe_workspace_size(int T, int d, int f, int E, int k, int dtype);
+
+/*
  * moe_expert_up -- grouped GEMM "layer 0" with fused SwiGLU (COMET page,
  * "COMET's Technical Principles": the expert's first GEMM, over the token
  * dimension M; its tiles are walked M-first for each weight panel).

@@ -26,7 +26,7 @@ EXPORTS = (
     "moe_combine", "moe_expert_up_save",
     "moe_combine_backward", "moe_expert_down_backward", "moe_expert_up_backward",
     "moe_unpermute", "moe_topk_weights_backward", "moe_linear_backward_workspace_size",
-    "moe_linear_backward", "moe_ffn_backward_workspace_size",
+    "moe_linear_backward", "moe_ffn_backward_workspace_size", "moe_workspace_size",
 )
 
 _lib = None
@@ -56,6 +56,7 @@ def load():
         "moe_permute": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                               sz, vp]),
         "moe_ffn_workspace_size": (sz, [i32, i32, i32, i32]),
+        "moe_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
         "moe_expert_up": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
         "moe_expert_down": (i32, [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz,
                                   vp]),
@@ -145,6 +146,10 @@ def moe_permute(topk_idx, topk_w, x, T, d, E, k, dtype, counts, offsets, perm_to
 
 def moe_ffn_workspace_size(E, rows, d, f):
     return load().moe_ffn_workspace_size(E, rows, d, f)
+
+
+def moe_workspace_size(T, d, f, E, k, dtype):
+    return load().moe_workspace_size(T, d, f, E, k, dtype)
 
 
 def moe_expert_up(x, gather_idx, offsets, E, rows, d, f, dtype, W_gate, W_up, a_out, workspace,

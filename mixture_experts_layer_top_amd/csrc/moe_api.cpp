@@ -5,6 +5,8 @@
 
 #include "moe_internal.h"
 
+#include <algorithm>
+
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -87,6 +89,18 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, const void* x, int
 
 size_t moe_ffn_workspace_size(int E, int rows, int d, int f) {
   return moe::ffn_workspace_bytes(E, rows, d, f);
+}
+
+size_t moe_workspace_size(int T, int d, int f, int E, int k, int dtype) {
+  if (T < 0 || d <= 0 || f <= 0 || E < 1 || E > 256 || k < 1 || k > E || !dtype_ok(dtype))
+    return 0;
+  if ((long long)T * k >= (1ll << 31)) return 0;
+  if (T == 0) return 0;  // every call is a no-op
+  const bool bf = dtype == MOE_BF16;
+  size_t need = moe::route_workspace_bytes(d, E, bf);
+  need = std::max(need, moe::permute_workspace_bytes(T, E, k));
+  need = std::max(need, moe::ffn_workspace_bytes(E, T * k, d, f));
+  return need;
 }
 
 static int check_ffn_common(const int32_t* offsets, int E, int rows, int d, int f, int dtype,

@@ -326,8 +326,11 @@ def brute_force(layer: dict, k: int, renorm: bool) -> dict:
 
 def selection_margin(L: np.ndarray, k: int) -> np.ndarray:
     """Smallest gap between adjacent values among the k+1 largest logits of
-    each row (inf when k == E): below it, a perturbation of the logits can
-    change the selection or its order."""
+    each row (all E when k == E, since the rank order of the k picks is part
+    of the selection; inf only for a single expert): a perturbation of every
+    logit by less than half of it changes neither the selection nor its
+    order, while moving the two logits at that gap by a little more than half
+    of it swaps them."""
     T, E = L.shape
     s = -np.sort(-L, axis=1)
     top = s[:, :min(k + 1, E)]

@@ -213,3 +213,26 @@ def test_product_path_does_not_import_oracle():
                 src = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in src and "from oracle" not in src, fn
                 assert "moe_oracle" not in src, fn
+
+
+@pytest.mark.parametrize("T,d,f,E,k,dt", [
+    (4096, 4096, 14336, 8, 2, 1), (8192, 3584, 2560, 64, 8, 1), (32768, 2048, 1408, 64, 6, 1),
+    (100000, 64, 48, 256, 8, 1), (128, 64, 128, 4, 2, 0), (1, 8, 8, 1, 1, 1)])
+def test_one_workspace_serves_every_forward_call(lib, T, d, f, E, k, dt):
+    ws = L.moe_workspace_size(T, d, f, E, k, dt)
+    assert ws % 16 == 0
+    assert ws >= L.moe_route_workspace_size(d, E, dt)
+    assert ws >= L.moe_permute_workspace_size(T, E, k)
+    assert ws >= L.moe_ffn_workspace_size(E, T * k, d, f)
+    # the FFN part is shape independent: the same buffer serves a shared-expert FFN
+    assert ws >= L.moe_ffn_workspace_size(1, T, d, 20480)
+
+
+def test_workspace_size_edge_cases(lib):
+    assert L.moe_workspace_size(0, 4096, 14336, 8, 2, 1) == 0    # T = 0: every call is a no-op
+    assert L.moe_workspace_size(-1, 64, 64, 8, 2, 1) == 0        # rejected arguments
+    assert L.moe_workspace_size(16, 64, 64, 8, 9, 1) == 0        # k > E
+    assert L.moe_workspace_size(16, 64, 64, 257, 2, 1) == 0      # E > 256
+    assert L.moe_workspace_size(16, 64, 64, 8, 2, 7) == 0        # unknown dtype
+    # with T = 0 the calls need no workspace and accept none
+    assert route(T=0, workspace=None, ws_bytes=0) == L.MOE_OK

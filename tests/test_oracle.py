@@ -379,3 +379,132 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     monkeypatch.setattr(O, attr, fn)
     with pytest.raises(AssertionError):
         _run_pins(name)
+
+
+# ---------------------------------------------------------------- comparison helpers
+#
+# Two oracle helpers decide how the GPU's fp32 routing is compared with the
+# fp64 oracle: selection_margin (how far a row's logits are from changing
+# its top-k order) and fp32_logit_error_bound (how far fp32 logits may be
+# from fp64 ones).  Their pins: hand rows, a brute-force perturbation search,
+# an adversarial sum on which sequential fp32 summation attains the bound,
+# and a bias-dominated sum.
+
+
+def _python_topk(row, k):
+    """Top-k order by a plain Python sort on (-value, index)."""
+    return sorted(range(len(row)), key=lambda e: (-row[e], e))[:k]
+
+
+def margin_pins(margin_fn):
+    # hand rows
+    assert margin_fn(np.array([[3.0, 3.0, 1.0, 0.0]]), 1)[0] == 0.0          # tie at the cut
+    assert margin_fn(np.array([[10.0, 7.0, 6.5, 0.0]]), 2)[0] == 0.5          # (k+1)-th gap
+    assert margin_fn(np.array([[10.0, 7.0, 6.5, 0.0]]), 1)[0] == 3.0          # first gap
+    assert margin_fn(np.array([[0.0, 4.0, 9.0, 1.0]]), 2)[0] == 3.0           # unsorted input
+    assert margin_fn(np.array([[1.0, 2.5, 3.0]]), 3)[0] == 0.5               # k = E: the order
+    assert np.isinf(margin_fn(np.array([[1.0], [2.0]]), 1)).all()            # one expert
+    # brute force: perturbations below half the margin never change the
+    # top-k order; moving the two logits at the smallest gap by a little
+    # more than half of it always does
+    rng = np.random.default_rng(17)
+    for _ in range(200):
+        E = int(rng.integers(2, 9))
+        k = int(rng.integers(1, E + 1))
+        row = rng.normal(size=E)
+        m = margin_fn(row[None, :], k)[0]
+        ref = _python_topk(row, k)
+        for _ in range(20):
+            delta = rng.uniform(-0.49, 0.49, size=E) * m
+            assert _python_topk(row + delta, k) == ref
+        order = sorted(range(E), key=lambda e: (-row[e], e))[:k + 1]
+        gaps = [row[order[i]] - row[order[i + 1]] for i in range(len(order) - 1)]
+        i = int(np.argmin(gaps))
+        bumped = row.copy()
+        bumped[order[i]] -= 0.51 * m
+        bumped[order[i + 1]] += 0.51 * m
+        assert _python_topk(bumped, k) != ref
+
+
+def test_selection_margin_pins():
+    margin_pins(O.selection_margin)
+
+
+def _seq_fp32_logits(x, W, b=None):
+    """fp32 logits by plain sequential float32 summation of the (exact)
+    products, in index order, then the bias add in float32."""
+    prod = (np.asarray(x, np.float64)[:, :, None] * np.asarray(W, np.float64)[None]).astype(np.float32)
+    s = np.cumsum(prod, axis=1, dtype=np.float32)[:, -1, :]
+    if b is not None:
+        s = (s + np.asarray(b, np.float32)[None, :]).astype(np.float32)
+    return s.astype(np.float64)
+
+
+def bound_pins(bound_fn):
+    u = 2.0 ** -24
+    # (1) tightness: terms [1, u, u, ...] -- each add of u to 1 is an exact
+    # tie that rounds back to 1 (round to nearest even), so sequential fp32
+    # summation loses (d - 1) u in total, which is the classical bound's
+    # leading term: the bound must hold, and not be more than 2x too loose
+    for d in (8, 64, 4096):
+        x = np.full((1, d), u)
+        x[0, 0] = 1.0
+        W = np.ones((d, 2))
+        err = np.max(np.abs(_seq_fp32_logits(x, W) - O.router_logits(x, W)))
+        bd = bound_fn(x, W, None, safety=1.0)[0]
+        assert err <= bd and err >= 0.5 * bd, (d, err, bd)
+    # (2) a bias-dominated logit: a tiny dot product added to a large bias
+    # rounds by ~u |b|, which only the bias term of the bound covers
+    x = np.zeros((1, 16))
+    x[0, 0] = 2.0 ** -30
+    W = np.ones((16, 2))
+    b = np.array([1000.0 + 1.0 / 3.0, 0.0], np.float32).astype(np.float64)
+    err = np.max(np.abs(_seq_fp32_logits(x, W, b) - O.router_logits(x, W, b)))
+    assert err > 0 and err <= bound_fn(x, W, b, safety=1.0)[0]
+    # (3) the skewed workload's router at full d, with its bias: fp32 logits
+    # by sequential summation and by torch's float32 matmul stay inside the
+    # bound on every token
+    cfg = CONFIGS["mixtral_skew"]
+    lay = make_layer(cfg, seed=0, T=256, parts=ROUTER_PARTS)
+    h = to_f64(lay)
+    bd = bound_fn(h["x"], h["W_r"], h["b"], safety=1.0)
+    L64 = O.router_logits(h["x"], h["W_r"], h["b"])
+    L_seq = _seq_fp32_logits(h["x"][:32], h["W_r"], h["b"])
+    assert np.all(np.abs(L_seq - L64[:32]) <= bd[:32, None])
+    L_mm = ((lay["x"].float() @ lay["W_r"].float()) + lay["b"].float()).double().numpy()
+    assert np.all(np.abs(L_mm - L64) <= bd[:, None])
+
+
+def test_fp32_logit_error_bound_pins():
+    bound_pins(O.fp32_logit_error_bound)
+
+
+def _margin_top_k_only(L, k):
+    s = -np.sort(-np.asarray(L, np.float64), axis=1)[:, :k]
+    if s.shape[1] < 2:
+        return np.full(L.shape[0], np.inf)
+    return np.min(s[:, :-1] - s[:, 1:], axis=1)
+
+
+def _bound_without_bias(x, W_r, b=None, safety=2.0, _f=O.fp32_logit_error_bound):
+    return _f(x, W_r, None, safety)
+
+
+def _bound_half_precision_u(x, W_r, b=None, safety=2.0):
+    d = x.shape[1]
+    u = 2.0 ** -16
+    n = d + 1
+    s = np.abs(np.asarray(x, np.float64)) @ np.abs(np.asarray(W_r, np.float64)).max(axis=1)
+    if b is not None:
+        s = s + float(np.abs(np.asarray(b, np.float64)).max())
+    return safety * n * u / (1 - n * u) * s
+
+
+@pytest.mark.parametrize("mistake,pins", [
+    (_margin_top_k_only, margin_pins),
+    (_bound_without_bias, bound_pins),
+    (_bound_half_precision_u, bound_pins),
+])
+def test_planted_helper_mistake_is_caught(mistake, pins):
+    with pytest.raises(AssertionError):
+        pins(mistake)

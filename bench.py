@@ -41,6 +41,10 @@ def parse():
                          "atomic: combine fused into layer 1 with atomic adds; "
                          "reference: permuted copy of x and separate combine")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--protocol-steps", type=int, default=20,
+                    help="steps of the cache-flushed per-step timing (median, p10, p90)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured peaks (MFMA-only loop, 1 GiB device copy)")
     ap.add_argument("--cpu-target-s", type=float, default=10.0,
                     help="approximate seconds of oracle work for the CPU baseline sample")
     ap.add_argument("--sweep", choices=["tokens", "skew"], default=None,
@@ -69,13 +73,100 @@ def copy_calibration(nbytes):
 
 
 def stage_bytes(cfg):
-    """Algorithmic HBM bytes of the memory-bound stages (fused path)."""
+    """Algorithmic HBM bytes of the memory-bound stages of the fused path:
+    route = x once, W_r once, the top-k indices and weights out; permute =
+    the indices and weights in, perm_token, inv and perm_w out (the gather
+    is fused into layer 0); combine = the k fp32 expert rows of every token
+    in, y out, the indices and weights in, plus the shared-expert output
+    (and its gate logit) when the layer has shared experts."""
     s = 2 if cfg.dtype == "bf16" else 4
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
     R = T * k
+    comb = R * d * 4 + T * d * 4 + T * k * 8
+    if cfg.n_shared:
+        comb += T * d * 4 + (T * 4 if cfg.shared_gated else 0)
     return {
         "route": T * d * s + d * E * s + T * k * 8,
-        "permute": T * k * 4 + R * 16,
+        "permute": R * 4 + R * 4 + 3 * R * 4,
+        "combine": comb,
+    }
+
+
+def pct(v, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(v), q))
+
+
+def protocol_times(m, steps, flush_bytes):
+    """Per-step HIP-event times of `steps` layer steps, each preceded by a
+    write of `flush_bytes` bytes (outside the events) that evicts the 256 MB
+    last-level cache, so no stage finds its inputs cached from the previous
+    step.  Returns {stage: [ms per step]} and the whole steps' ms."""
+    import torch
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda:0")
+    stages = m.STAGES
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(steps)]
+    for s in range(steps):
+        flush.fill_(s & 0xFF)
+        ev[s][0].record(stream)
+        pos = [1]
+
+        def mark(_name, s=s, pos=pos):
+            ev[s][pos[0]].record(stream)
+            pos[0] += 1
+
+        m.forward(marks=mark)
+    torch.cuda.synchronize()
+    per = {name: [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]
+           for i, name in enumerate(stages)}
+    step = [ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)]
+    del flush
+    return per, step
+
+
+def measured_peaks(copy_bytes=1 << 30, probe_iters=20000):
+    """Peaks measured on this machine: the bf16 MFMA rate and shader clock of an
+    all-compute-unit MFMA-only loop (two 4-wave blocks per compute unit),
+    and a device copy of `copy_bytes` bytes (read + write bytes / time)."""
+    import torch
+    from mixture_experts_layer_top_amd import _lib
+    dev = torch.device("cuda:0")
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = 2 * n_cu
+    ticks = torch.zeros(3 * blocks, dtype=torch.int64, device=dev)
+    _lib.moe_probe_mfma(blocks, 100, ticks)  # warm-up
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    _lib.moe_probe_mfma(blocks, probe_iters, ticks)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    flops = blocks * 4 * probe_iters * 16 * 16384
+    t = ticks.view(blocks, 3).cpu().double()
+    sclk = float((t[:, 0] / (t[:, 1] / 100e6)).median()) / 1e9
+    src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(5):
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del src, dst
+    cms = sorted(times)[len(times) // 2]
+    return {
+        "mfma_bf16_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+        "sclk_GHz_under_mfma_load": round(sclk, 3),
+        "mfma_probe": f"{blocks} blocks x 4 waves x {probe_iters} x 16 MFMA 16x16x32 bf16, "
+                      f"{ms:.2f} ms",
+        "hbm_copy_GBs": round(2 * copy_bytes / (cms * 1e-3) / 1e9, 1),
+        "copy": f"device copy of {copy_bytes >> 20} MiB, median of 5",
     }
 
 
@@ -141,6 +232,14 @@ def cpu_baseline(cfg, layer, target_s):
     sub_cfg = cfg.shrink(T=n, d=cfg.d, f=cfg.f, f_shared=cfg.f_shared)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     del host
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {
         "value": sub_cfg.flops() / dt / 1e12,
         "unit": "TFLOP/s",
@@ -149,6 +248,7 @@ def cpu_baseline(cfg, layer, target_s):
         "sample": f"first {n} of {cfg.T} tokens, full expert weights, fp64 numpy; "
                   f"{reps} forward(s), {dt:.2f} s each; bf16->fp64 input conversion excluded",
         "host_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": model,
     }
 
 
@@ -367,7 +467,8 @@ def main():
         "stage_rates": {
             "expert_up_TFLOPs": round(g0, 1),
             "expert_down_TFLOPs": round(g1, 1),
-            "route_GBs": round(by["route"] / (stage_ms["route"] * 1e-3) / 1e9, 1),
+            **{f"{st}_GBs": round(by[st] / (stage_ms[st] * 1e-3) / 1e9, 1)
+               for st in ("route", "permute", "combine")},
         },
         "roofline": {
             "kernel": gemm_kernel_name(cfg, up=True) + " (layer 0 + SwiGLU; main pass and "
@@ -380,6 +481,32 @@ def main():
             "traffic": measured_traffic(cfg),
         },
     }
+    if args.protocol_steps > 0:
+        # every step after a 1 GiB write that evicts the last-level cache:
+        # median, p10 and p90 of the per-step event times, and the
+        # memory-bound stages' HBM rates (fraction of 8 TB/s) at the medians
+        per, step = protocol_times(m, args.protocol_steps, 1 << 30)
+        med = {st: pct(v, 50) for st, v in per.items()}
+        out["protocol"] = {
+            "what": f"{args.protocol_steps} steps, each after a 1 GiB device write outside the "
+                    "events (last-level cache flushed); HIP events on the launch stream",
+            "step_ms": {"median": round(pct(step, 50), 4), "p10": round(pct(step, 10), 4),
+                        "p90": round(pct(step, 90), 4)},
+            "layer_TFLOPs_at_median": round(flops / (pct(step, 50) * 1e-3) / 1e12, 1),
+            "stages_ms_median": {st: round(v, 4) for st, v in med.items()},
+            "stages_ms_p10": {st: round(pct(v, 10), 4) for st, v in per.items()},
+            "stages_ms_p90": {st: round(pct(v, 90), 4) for st, v in per.items()},
+            "hbm_stages": {st: {"bytes": by[st],
+                                "GBs": round(by[st] / (med[st] * 1e-3) / 1e9, 1),
+                                "frac_of_8TBs": round(by[st] / (med[st] * 1e-3) / 1e9 /
+                                                      PEAK_HBM_GBS, 3)}
+                           for st in ("route", "permute", "combine")},
+            "expert_up_TFLOPs_at_median": round(g0_flops / (med["expert_up"] * 1e-3) / 1e12, 1),
+            "expert_down_TFLOPs_at_median": round(g1_flops / (med["expert_down"] * 1e-3) / 1e12,
+                                                  1),
+        }
+    if not args.no_peaks:
+        out["measured_peaks"] = measured_peaks()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, layer, args.cpu_target_s)
     print(json.dumps(out), flush=True)

@@ -72,15 +72,16 @@ const char* moe_status_string(int status);
  * Arguments:
  *   x [T, d] (dtype), W_r [d, E] (dtype), bias [E] fp32 or NULL;
  *   topk_idx [T, k] int32 out; topk_w [T, k] fp32 out;
- *   logits_out [T, E] fp32 out or NULL: the exact logits the selection used;
- *   workspace of at least moe_route_workspace_size(d, E, dtype) bytes (the
- *   bf16 path keeps a transposed copy of W_r there during the call).
- * The logits are summed in a fixed order: the call is deterministic.
+ *   logits_out [T, E] fp32 out or NULL: the exact logits the selection used.
+ * The logits are summed in a fixed order: the call is deterministic.  It
+ * needs no workspace: W_r is read in the layout given.  Every token gets k
+ * distinct experts in [0, E) whatever its logits (a NaN logit ranks below
+ * -inf and counts as -inf in the weights; a token whose logits are all NaN
+ * gets NaN weights).
  */
-size_t moe_route_workspace_size(int d, int E, int dtype);
 int moe_route(const void* x, const void* W_r, const float* bias, int T, int d, int E, int k,
               int score, int dtype, int32_t* topk_idx, float* topk_w, float* logits_out,
-              void* workspace, size_t ws_bytes, hipStream_t stream);
+              hipStream_t stream);
 
 /* Workspace bytes moe_permute needs for T tokens, E experts, top-k. */
 size_t moe_permute_workspace_size(int T, int E, int k);
@@ -101,7 +102,8 @@ size_t moe_permute_workspace_size(int T, int E, int k);
  *   undefined behaviour) and the k experts of a token distinct, as
  *   moe_route produces them (an expert repeated in one token's list is
  *   counted once: both slots get the same row, offsets[E] < T*k, and every
- *   row below offsets[E] is still written); topk_w [T, k] fp32 or NULL (then perm_w must be
+ *   row below offsets[E] is still written, rows offsets[E] .. T*k-1 of
+ *   perm_token, perm_w and x_perm are left untouched); topk_w [T, k] fp32 or NULL (then perm_w must be
  *   NULL); x [T, d] (dtype) required only with x_perm; counts [E],
  *   offsets [E+1], perm_token [T*k], inv [T, k] int32 out; perm_w [T*k]
  *   fp32 out or NULL; x_perm [T*k, d] (dtype) out or NULL.
@@ -125,10 +127,10 @@ size_t moe_ffn_workspace_size(int E, int rows, int d, int f);
 /*
  * moe_workspace_size -- one workspace size that serves every forward call of
  * a layer with T tokens, model dim d, expert FFN dim f, E experts and top-k
- * (moe_route, moe_permute, moe_expert_up / moe_expert_down / moe_ffn_forward
- * with rows = T*k): the calls of one forward run in order on one stream, so
- * they can share one buffer of this many bytes (16-byte aligned).  It is at
- * least each of moe_route_workspace_size(d, E, dtype),
+ * (moe_permute, moe_expert_up / moe_expert_down / moe_ffn_forward with
+ * rows = T*k; moe_route and moe_combine need none): the calls of one forward
+ * run in order on one stream, so they can share one buffer of this many
+ * bytes (16-byte aligned).  It is at least each of
  * moe_permute_workspace_size(T, E, k) and moe_ffn_workspace_size(E, T*k, d, f);
  * the FFN part does not depend on the shapes, so the same buffer also serves
  * a shared-expert FFN (E = 1, rows = T, any f).  Returns 0 for T = 0 (every
@@ -339,6 +341,25 @@ size_t moe_linear_backward_workspace_size(int T, int d, int E);
 int moe_linear_backward(const void* x, const void* W, const float* G, int T, int d, int E,
                         int dtype, float* dW, float* db, float* dx, void* workspace,
                         size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement.  Kernel rates are reported as fractions of the chip's peaks
+ * (the pages compare layer times across token lengths and expert loads:
+ * COMET page, "COMET's Performance"); this call measures the bf16 matrix
+ * peak the chip sustains, and its shader clock, under an all-compute-unit
+ * load, to set beside the datasheet figure.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * moe_probe_mfma -- `blocks` workgroups of 4 wave64s each run `iters` rounds
+ * of 16 independent bf16 MFMAs of 16 x 16 x 32 (16384 flops each) on
+ * register operands, so the launch performs blocks * 4 * iters * 16 * 16384
+ * flops (time it with events on the stream).  ticks [3 * blocks] uint64
+ * device out: per block, the shader-clock ticks and the 100 MHz real-time
+ * ticks its wave 0 spent in the loop, and a word that is always 0.
+ * MOE_ERR_INVALID for blocks outside [1, 2^20], iters < 1 or a NULL ticks.
+ */
+int moe_probe_mfma(int blocks, int iters, uint64_t* ticks, hipStream_t stream);
 
 #ifdef __cplusplus
 }

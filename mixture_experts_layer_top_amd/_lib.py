@@ -20,13 +20,14 @@ MOE_SOFTMAX_TOPK_RENORM, MOE_SOFTMAX_TOPK = 0, 1
 
 # every symbol include/moe.h declares
 EXPORTS = (
-    "moe_status_string", "moe_route_workspace_size", "moe_route", "moe_permute_workspace_size",
+    "moe_status_string", "moe_route", "moe_permute_workspace_size",
     "moe_permute",
     "moe_ffn_workspace_size", "moe_expert_up", "moe_expert_down", "moe_ffn_forward",
     "moe_combine", "moe_expert_up_save",
     "moe_combine_backward", "moe_expert_down_backward", "moe_expert_up_backward",
     "moe_unpermute", "moe_topk_weights_backward", "moe_linear_backward_workspace_size",
     "moe_linear_backward", "moe_ffn_backward_workspace_size", "moe_workspace_size",
+    "moe_probe_mfma",
 )
 
 _lib = None
@@ -50,13 +51,13 @@ def load():
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     sig = {
         "moe_status_string": (ctypes.c_char_p, [i32]),
-        "moe_route_workspace_size": (sz, [i32, i32, i32]),
-        "moe_route": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
+        "moe_route": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
         "moe_permute_workspace_size": (sz, [i32, i32, i32]),
         "moe_permute": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                               sz, vp]),
         "moe_ffn_workspace_size": (sz, [i32, i32, i32, i32]),
         "moe_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
+        "moe_probe_mfma": (i32, [i32, i32, vp, vp]),
         "moe_expert_up": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
         "moe_expert_down": (i32, [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz,
                                   vp]),
@@ -117,14 +118,10 @@ def status_string(st: int) -> str:
 moe_status_string = status_string
 
 
-def moe_route_workspace_size(d, E, dtype):
-    return load().moe_route_workspace_size(d, E, dtype)
-
-
-def moe_route(x, W_r, bias, T, d, E, k, score, dtype, topk_idx, topk_w, logits_out, workspace,
-              ws_bytes, stream=None, check=True):
+def moe_route(x, W_r, bias, T, d, E, k, score, dtype, topk_idx, topk_w, logits_out,
+              stream=None, check=True):
     st = load().moe_route(_p(x), _p(W_r), _p(bias), T, d, E, k, score, dtype, _p(topk_idx),
-                          _p(topk_w), _p(logits_out), _p(workspace), ws_bytes, _stream(stream))
+                          _p(topk_w), _p(logits_out), _stream(stream))
     if check:
         _check("moe_route", st)
     return st
@@ -266,4 +263,14 @@ def moe_linear_backward(x, W, G, T, d, E, dtype, dW, db, dx, workspace, ws_bytes
                                     _p(workspace), ws_bytes, _stream(stream))
     if check:
         _check("moe_linear_backward", st)
+    return st
+
+
+# ---------------------------------------------------------------- measurement
+
+
+def moe_probe_mfma(blocks, iters, ticks, stream=None, check=True):
+    st = load().moe_probe_mfma(blocks, iters, _p(ticks), _stream(stream))
+    if check:
+        _check("moe_probe_mfma", st)
     return st

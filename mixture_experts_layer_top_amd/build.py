@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libmoe.so")
 ARCH = "gfx950"
 
 SOURCES = ["moe_api.cpp", "route.hip", "permute.hip", "gemm.hip", "combine.hip",
-           "gemm_bwd.hip", "backward.hip"]
+           "gemm_bwd.hip", "backward.hip", "probe.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -42,19 +42,25 @@ def hipcc() -> str:
     return h
 
 
-def scratch_kernels(remarks: str) -> list[tuple[str, int]]:
-    """Kernels with a scratch (private) segment, from hipcc's
-    kernel-resource-usage remarks: (mangled name, bytes per lane)."""
-    out, name = [], None
+def kernel_scratch(remarks: str) -> dict[str, int]:
+    """Scratch (private) segment bytes per lane of every kernel, from hipcc's
+    kernel-resource-usage remarks: {mangled name: bytes}."""
+    out, name = {}, None
     for line in remarks.splitlines():
         m = re.search(r"Function Name: (\S+)", line)
         if m:
             name = m.group(1)
             continue
         m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
-        if m and name is not None and int(m.group(1)) > 0:
-            out.append((name, int(m.group(1))))
+        if m and name is not None:
+            out[name] = int(m.group(1))
+            name = None
     return out
+
+
+def scratch_kernels(remarks: str) -> list[tuple[str, int]]:
+    """Kernels with a scratch segment: (mangled name, bytes per lane)."""
+    return [(n, b) for n, b in kernel_scratch(remarks).items() if b > 0]
 
 
 def _compile(src: str) -> str:
@@ -65,7 +71,12 @@ def _compile(src: str) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     # every kernel keeps its state in registers and LDS: a kernel that spills
-    # (accumulators demoted to scratch run several times slower) is a build error
+    # (accumulators demoted to scratch run several times slower) is a build
+    # error.  A kernel source whose remarks name no kernel would pass this
+    # check without checking anything, so that is an error too.
+    if src.endswith(".hip") and not kernel_scratch(r.stderr):
+        raise RuntimeError(f"{src}: hipcc printed no kernel-resource-usage remarks; "
+                           "the scratch check cannot run")
     spilled = scratch_kernels(r.stderr)
     if spilled:
         raise RuntimeError(f"{src}: kernels with scratch memory: {spilled}")

@@ -31,14 +31,9 @@ const char* moe_status_string(int status) {
   }
 }
 
-size_t moe_route_workspace_size(int d, int E, int dtype) {
-  if (d <= 0 || E < 1 || E > 256 || !dtype_ok(dtype)) return 0;
-  return moe::route_workspace_bytes(d, E, dtype == MOE_BF16);
-}
-
 int moe_route(const void* x, const void* W_r, const float* bias, int T, int d, int E, int k,
               int score, int dtype, int32_t* topk_idx, float* topk_w, float* logits_out,
-              void* workspace, size_t ws_bytes, hipStream_t stream) {
+              hipStream_t stream) {
   if (T < 0 || E < 1 || E > 256 || k < 1 || k > E || d <= 0) return MOE_ERR_INVALID;
   if ((long long)T * k >= (1ll << 31) || (long long)T * E >= (1ll << 31)) return MOE_ERR_INVALID;
   if (!dtype_ok(dtype) || (score != MOE_SOFTMAX_TOPK_RENORM && score != MOE_SOFTMAX_TOPK))
@@ -46,15 +41,11 @@ int moe_route(const void* x, const void* W_r, const float* bias, int T, int d, i
   if (T == 0) return MOE_OK;
   if (!x || !W_r || !topk_idx || !topk_w) return MOE_ERR_INVALID;
   if (d % 8) return MOE_ERR_UNSUPPORTED;
-  const size_t need = moe::route_workspace_bytes(d, E, dtype == MOE_BF16);
-  if (need > 0 && (!workspace || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(W_r) || !aligned16(topk_idx) || !aligned16(topk_w) ||
-      (bias && !aligned16(bias)) || (logits_out && !aligned16(logits_out)) ||
-      (workspace && !aligned16(workspace)))
+      (bias && !aligned16(bias)) || (logits_out && !aligned16(logits_out)))
     return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_route(x, W_r, bias, T, d, E, k, score == MOE_SOFTMAX_TOPK_RENORM,
-                                      dtype == MOE_BF16, topk_idx, topk_w, logits_out, workspace,
-                                      stream));
+                                      dtype == MOE_BF16, topk_idx, topk_w, logits_out, stream));
 }
 
 size_t moe_permute_workspace_size(int T, int E, int k) {
@@ -96,9 +87,7 @@ size_t moe_workspace_size(int T, int d, int f, int E, int k, int dtype) {
     return 0;
   if ((long long)T * k >= (1ll << 31)) return 0;
   if (T == 0) return 0;  // every call is a no-op
-  const bool bf = dtype == MOE_BF16;
-  size_t need = moe::route_workspace_bytes(d, E, bf);
-  need = std::max(need, moe::permute_workspace_bytes(T, E, k));
+  size_t need = moe::permute_workspace_bytes(T, E, k);
   need = std::max(need, moe::ffn_workspace_bytes(E, T * k, d, f));
   return need;
 }
@@ -332,6 +321,15 @@ int moe_linear_backward(const void* x, const void* W, const float* G, int T, int
   }
   return hip_status(moe::launch_linear_backward(x, W, G, T, d, E, dtype == MOE_BF16, dW, db, dx,
                                                 workspace, stream));
+}
+
+// ---------------------------------------------------------------- measurement
+
+int moe_probe_mfma(int blocks, int iters, uint64_t* ticks, hipStream_t stream) {
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1) return MOE_ERR_INVALID;
+  if (!ticks) return MOE_ERR_INVALID;
+  if (!aligned16(ticks)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_probe_mfma(blocks, iters, ticks, stream));
 }
 
 }  // extern "C"

@@ -47,10 +47,9 @@ __host__ __device__ __forceinline__ size_t align_up(size_t a, size_t b) { return
 
 int device_cu_count();  // compute units of the current device
 
-size_t route_workspace_bytes(int d, int E, bool bf16);
 hipError_t launch_route(const void* x, const void* W_r, const float* bias, int T, int d, int E,
                         int k, bool renorm, bool bf16, int32_t* idx, float* w, float* logits_out,
-                        void* ws, hipStream_t s);
+                        hipStream_t s);
 
 size_t permute_workspace_bytes(int T, int E, int k);
 hipError_t launch_permute(const int32_t* idx, const float* topk_w, const void* x, int T, int d,
@@ -71,6 +70,8 @@ hipError_t launch_expert_down(const void* a, const int32_t* offsets, int E, int 
 hipError_t launch_combine(const float* y_perm, const int32_t* inv, const float* topk_w, int T,
                           int d, int k, const float* y_shared, const float* gate_logit,
                           bool accumulate, float* y, hipStream_t s);
+
+hipError_t launch_probe_mfma(int blocks, int iters, uint64_t* ticks, hipStream_t s);
 
 // backward
 hipError_t launch_combine_backward(const float* dy, const float* y_perm, const int32_t* inv,

@@ -230,17 +230,22 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
   for (int j = kKR; j < k; ++j) place(j, it[j]);
 }
 
-// x_perm[r, :] = x[perm_token[r], :]; rows of `vecs` 16-byte vectors.  A
-// block copies 8 rows; a thread takes columns c, c + 256, ... of all 8 and
-// issues the 8 loads of a column before its stores (rows past R re-read the
-// block's first source row and are not stored), so 8 loads are in flight
-// per thread instead of one load-store round trip at a time.
+// x_perm[r, :] = x[perm_token[r], :] for the rows r < offsets[E] the rank
+// kernel wrote (all T k of them unless a token listed an expert twice);
+// rows of `vecs` 16-byte vectors.  A block copies 8 rows; a thread takes
+// columns c, c + 256, ... of all 8 and issues the 8 loads of a column
+// before its stores (rows past the end re-read the block's first source row
+// and are not stored), so 8 loads are in flight per thread instead of one
+// load-store round trip at a time.
 constexpr int kGatherRows = 8;
 __global__ __launch_bounds__(kThreads) void gather_kernel(const u32x4* __restrict__ x,
                                                           const int32_t* __restrict__ perm_token,
-                                                          int R, int vecs,
+                                                          const int32_t* __restrict__ offsets,
+                                                          int E, int vecs,
                                                           u32x4* __restrict__ x_perm) {
+  const int R = offsets[E];
   const int r0 = blockIdx.x * kGatherRows;
+  if (r0 >= R) return;
   const int nr = min(kGatherRows, R - r0);
   size_t src[kGatherRows];
 #pragma unroll
@@ -295,7 +300,7 @@ hipError_t launch_permute(const int32_t* idx, const float* topk_w, const void* x
   if (x_perm && R > 0) {
     const int vecs = d * (bf16 ? 2 : 4) / 16;
     hipLaunchKernelGGL(gather_kernel, dim3(cdiv(R, kGatherRows)), dim3(kThreads), 0, s,
-                       static_cast<const u32x4*>(x), perm_token, R, vecs,
+                       static_cast<const u32x4*>(x), perm_token, offsets, E, vecs,
                        static_cast<u32x4*>(x_perm));
   }
   return hipGetLastError();

@@ -1,25 +1,30 @@
-// Router: logits, softmax top-k selection and weights, one pass over x.
+// Router: logits, softmax top-k selection and weights, one launch, one pass
+// over x.
 //
 // Top-k expert choice per token: DisagMoE technical summary, "2.2 AF-Pipe".
 //
 // bf16 path.  The logits L = x W_r are a skinny contraction (E <= 256
-// columns) bound by reading x from HBM once:
-//   1. a small pre-pass writes W_r transposed (K contiguous, [E_pad, d], zero
-//      rows past E) into the caller's workspace; it is at most d * 256 * 2
-//      bytes and stays in L2 for the main pass;
-//   2. a workgroup of 4 wave64s takes 16 * MB tokens; the 4 waves split K
-//      four ways, and each wave streams its token rows (A operand, 16
-//      contiguous K-bytes per lane) and the transposed W_r rows (B operand,
-//      likewise) straight from memory into v_mfma_f32_16x16x32_bf16 -- no LDS
-//      staging, no barrier in the loop.  bf16 products are exact in fp32;
-//      sums are fp32;
-//   3. the four partial logits are added in wave order (deterministic), the
-//      bias added, and the result kept in LDS for the selection.
+// columns), bound by reading x from HBM once:
+//   * a workgroup of NWV wave64s takes 16 MB tokens; the waves split K into
+//     NWV ranges, and each wave walks its range in chunks of 32 ST;
+//   * x rows (the A operand: 16 contiguous K-bytes per lane) go straight
+//     from memory into registers; the next chunk's loads are issued before
+//     this chunk's MFMAs, so a wave always has one chunk in flight;
+//   * W_r is read in the caller's [d, E] layout: the chunk's rows are one
+//     contiguous block, which each wave loads (16 bytes per lane), writes to
+//     its own LDS tile, and reads back with the gfx950 LDS transpose read
+//     (8 consecutive K values of one expert per lane, the B operand of
+//     v_mfma_f32_16x16x32_bf16); lanes whose columns lie past E read a zero
+//     patch, so E need not be a multiple of 16 (it must be a multiple of 8;
+//     other E gather their B operand straight from memory);
+//   * bf16 products are exact in fp32; sums are fp32; the NWV partial
+//     logits are added in wave order (deterministic), then the bias.
 //
-// Selection and weights: 4 lanes serve one token and each scans every 4th
-// expert.  The j-th pick is the best (value desc, index asc) among experts
-// strictly below the (j-1)-th pick in that order, so no pick is ever marked;
-// exactly equal logits go to the lower index.
+// Selection and weights: 16 lanes per token, each holding every 16th
+// logit.  The j-th pick is the best (value desc, index asc) strictly below
+// the (j-1)-th pick in that order, so no pick is ever marked; exactly equal
+// logits go to the lower index.  A NaN logit ranks below -inf, so every
+// token gets k distinct experts in [0, E) whatever its logits.
 #include "moe_internal.h"
 
 namespace moe {
@@ -42,9 +47,9 @@ struct RouteArgs {
 // lane q; padded experts hold -inf).  Waves take groups of 4 tokens in turn.
 // The j-th pick is the best (value desc, index asc) strictly below the
 // (j-1)-th pick in that order, found by a per-lane scan and a 16-lane
-// reduction, so no pick is ever marked and exactly equal logits go to the
-// lower index.  With renormalisation the unnormalised weights are written
-// first and divided by their sum afterwards (by the same lane).
+// reduction.  NaN logits are taken as -inf for the order and the weights.
+// With renormalisation the unnormalised weights are written first and
+// divided by their sum afterwards (by the same lane).
 template <int NV>
 __device__ __forceinline__ void select_and_weigh(const float* ll, int lstride, const RouteArgs& a,
                                                  int t_base, int ntok) {
@@ -61,7 +66,8 @@ __device__ __forceinline__ void select_and_weigh(const float* ll, int lstride, c
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int e = q + 16 * u;
-      v[u] = (e < E) ? row[e] : -INFINITY;
+      const float l = (e < E) ? row[e] : -INFINITY;
+      v[u] = (l == l) ? l : -INFINITY;  // NaN ranks with -inf
     }
     // softmax denominator relative to the row max
     float m = -INFINITY;
@@ -125,56 +131,99 @@ __device__ __forceinline__ void write_logits(const float* ll, int lstride, const
   }
 }
 
-// W_t[e, k] = W_r[k, e] for e < E, 0 for E <= e < Ep (d % 8 == 0).  Thread
-// (kc, e) gathers rows 8 kc .. 8 kc + 7 of column e and writes them as one
-// 16-byte vector; consecutive threads take consecutive experts, so each row
-// read of a wave is contiguous.
-__global__ __launch_bounds__(kThreads) void transpose_router_kernel(const bf16_t* __restrict__ W,
-                                                                   int d, int E, int Ep,
-                                                                   bf16_t* __restrict__ Wt) {
-  const int i = blockIdx.x * kThreads + threadIdx.x;
-  if (i >= (d / 8) * Ep) return;
-  const int e = i % Ep, kc = i / Ep;
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (e < E) {
-    const bf16_t* src = W + (size_t)kc * 8 * E + e;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) v[r >> 1] |= (uint32_t)src[(size_t)r * E] << (16 * (r & 1));
-  }
-  *reinterpret_cast<u32x4*>(Wt + (size_t)e * d + (size_t)kc * 8) = v;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
 
+// One direct-to-LDS load: 64 lanes x 16 bytes from their global addresses
+// to the 1 KiB of LDS starting at lds_addr (wave-uniform).  Inline assembly:
+// the compiler does not model it, so its completion is waited for
+// explicitly (wait_vmcnt_route) before the LDS bytes are read.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gptr), "s"(lds_addr)
+      : "m0", "memory");  // keeps the chunk's x loads after it (waits count in issue order)
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding);
+// a compiler memory barrier, so no LDS read moves above it
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_route() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+// LDS bytes of the route kernel: the waves' W_r tiles (KC rows x E columns
+// each, plus a 16-byte zero patch), then reused for the partial logits
+// [NWV][TW][Ep] and the logits [TW][Ep + 1].
+template <int NB, int MB, int NWV, int ST>
+struct RouteCfg {
+  static constexpr int Ep = NB * 16, TW = MB * 16, KC = 32 * ST;
+  static constexpr int WTILE = KC * Ep * 2;                 // bytes, E <= Ep
+  static constexpr int ZERO = NWV * WTILE;                  // offset of the zero patch
+  static constexpr int W_BYTES = ZERO + 16;
+  static constexpr int P_BYTES = NWV * TW * Ep * 4;
+  static constexpr int L_BYTES = TW * (Ep + 1) * 4;
+  static constexpr int LDS = W_BYTES > P_BYTES ? (W_BYTES > L_BYTES ? W_BYTES : L_BYTES)
+                                               : (P_BYTES > L_BYTES ? P_BYTES : L_BYTES);
+  static constexpr int WL = ST * NB;  // 16-byte pieces of a W_r chunk per lane (at most)
+};
+
 // NB = ceil(E / 16) column blocks of 16 experts; MB = token blocks of 16 per
-// workgroup; NWV waves split K (more waves = more loads in flight per CU: the
-// kernel is bound by streaming x once from HBM).
-template <int NB, int MB, int NWV>
-__global__ __launch_bounds__(NWV * 64) void route_bf16_kernel(RouteArgs a, const bf16_t* __restrict__ Wt) {
+// workgroup; NWV waves split K; ST MFMA K-steps (of 32) per chunk.
+// WTR: E % 8 == 0, W_r staged through LDS; otherwise the B operand is
+// gathered from memory one element at a time (small E only: the gate of a
+// shared expert has E = 1, whose column is contiguous).
+template <int NB, int MB, int NWV, int ST, bool WTR>
+__global__ __launch_bounds__(NWV * 64) void route_bf16_kernel(RouteArgs a) {
+  using C = RouteCfg<NB, MB, NWV, ST>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int Ep = NB * 16;
-  constexpr int TW = MB * 16;   // tokens per workgroup
-  constexpr int ls = Ep + 1;    // LDS row stride of the logits, in floats
+  constexpr int Ep = C::Ep, TW = C::TW, KC = C::KC, WL = C::WL;
   constexpr int NT = NWV * 64;
-  float* part = reinterpret_cast<float*>(smem);  // [NWV][TW][Ep] partial logits
-  float* ll = part;                               // [TW][ls] logits (reuses part)
+  constexpr int ls = Ep + 1;  // LDS row stride of the logits, in floats
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: K bounds in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t_base = blockIdx.x * TW;
   const int d = a.d, E = a.E;
-  const int kq = cdiv(cdiv(d, NWV), 32) * 32;  // K per wave, a multiple of 32
-  const int kb = wave * kq, ke = min(d, kb + kq);
+  const int kq = cdiv(cdiv(d, NWV), KC) * KC;  // K per wave, whole chunks
+  const int kb = min(d, wave * kq), ke = min(d, kb + kq);
+  const int nch = cdiv(ke - kb, KC);
 
+  const bf16_t* X = static_cast<const bf16_t*>(a.x);
+  const bf16_t* W = static_cast<const bf16_t*>(a.W);
   const bf16_t* xr[MB];
-  bool t_ok[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int t = t_base + mb * 16 + (lane & 15);
-    t_ok[mb] = t < a.T;
-    xr[mb] = static_cast<const bf16_t*>(a.x) + (size_t)(t_ok[mb] ? t : 0) * d;
+    xr[mb] = X + (size_t)(t < a.T ? t : 0) * d + (lane >> 4) * 8;  // rows past T read token 0
   }
-  const bf16_t* wr[NB];
+
+  // W_r tile of this wave: the chunk's KC rows x E columns as in memory
+  char* wt = smem + wave * C::WTILE;
+  if (WTR && tid < 4) reinterpret_cast<uint32_t*>(smem + C::ZERO)[tid] = 0u;
+  // transpose-read offsets: lane l takes column 16 nb + l % 16 of rows
+  // kr .. kr + 3 (and + 4); lanes whose 4 columns lie past E read zeros
+  const int kr = (lane >> 4) * 8 + ((lane & 15) >> 2), cq = (lane & 3) * 4;
+  const uint32_t zrel = (uint32_t)(C::ZERO - wave * C::WTILE);  // the zero patch, from wt
+  uint32_t tr_lo[NB];
+  bool tr_in[NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) wr[nb] = Wt + (size_t)(nb * 16 + (lane & 15)) * d;
+  for (int nb = 0; nb < NB; ++nb) {
+    const int col = nb * 16 + cq;
+    tr_in[nb] = col < E;
+    tr_lo[nb] = (uint32_t)((kr * E + col) * 2);
+  }
 
   f32x4 acc[MB][NB];
 #pragma unroll
@@ -182,48 +231,104 @@ __global__ __launch_bounds__(NWV * 64) void route_bf16_kernel(RouteArgs a, const
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // K in chunks of ST steps of 32: all loads of a chunk are issued before its
-  // MFMAs, so each wave keeps ST (MB + NB) 1 KiB loads in flight
-  constexpr int ST = (MB + NB) <= 2 ? 8 : (MB + NB) <= 8 ? 4 : 2;
+  // One chunk: ST K-steps of 32.  Its W_r rows (KC x E bf16, one contiguous
+  // block) go straight to the wave's LDS tile with direct-to-LDS loads,
+  // issued first; then its x fragments are loaded into registers.  Loads
+  // complete in issue order, so the first wait for an x fragment (inserted
+  // by the compiler) also covers the W_r rows; an explicit wait for them
+  // precedes the transpose reads.  Rows past the wave's range load a valid
+  // W_r row and meet zero x fragments.
+  const int cbytes = KC * E * 2;                 // bytes of a full W_r chunk
+  const int nwl = WTR ? cdiv(cbytes, 1024) : 0;  // 1 KiB loads per chunk
+  const uint32_t wt_lds = lds_addr_of(wt);
+  const char* Wb = reinterpret_cast<const char*>(W);
+  const long long wlast = (long long)d * E * 2 - 16;  // last 16 bytes of W_r
   const bf16x8 zero8 = {};
-  // rows of tokens past T read token 0 (xr); their logits are never stored
-  for (int k0 = kb; k0 < ke; k0 += 32 * ST) {
-    bf16x8 av[ST][MB], bv[ST][NB];
-    if (k0 + 32 * ST <= ke) {
-      // the whole chunk lies inside K: no predicates
-#pragma unroll
-      for (int st = 0; st < ST; ++st) {
-        const int kk = k0 + st * 32 + (lane >> 4) * 8;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) av[st][mb] = *reinterpret_cast<const bf16x8*>(xr[mb] + kk);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) bv[st][nb] = *reinterpret_cast<const bf16x8*>(wr[nb] + kk);
-      }
-    } else {
-#pragma unroll
-      for (int st = 0; st < ST; ++st) {
-        const int kk = k0 + st * 32 + (lane >> 4) * 8;
-        const bool kin = kk < ke;  // d % 8 == 0: a lane's 8 values are all in or all out
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          av[st][mb] = kin ? *reinterpret_cast<const bf16x8*>(xr[mb] + kk) : zero8;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          bv[st][nb] = kin ? *reinterpret_cast<const bf16x8*>(wr[nb] + kk) : zero8;
+  if (WTR) __syncthreads();  // the zero patch is written
+  for (int c = 0; c < nch; ++c) {
+    const int k0 = kb + c * KC;
+    if (WTR) {
+      // the wave's earlier transpose reads of its tile have completed
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const long long base = (long long)k0 * E * 2;
+      for (int j = 0; j < nwl; ++j) {
+        long long off = base + j * 1024 + lane * 16;
+        if (off > wlast) off = wlast;
+        dma16(Wb + off, wt_lds + (uint32_t)(j * 1024));
       }
     }
+    bf16x8 xv[ST][MB];
+    if (k0 + KC <= ke) {
 #pragma unroll
-    for (int st = 0; st < ST; ++st)
+      for (int st = 0; st < ST; ++st)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          xv[st][mb] = *reinterpret_cast<const bf16x8*>(xr[mb] + k0 + st * 32);
+    } else {
+      // ragged last chunk: K past the wave's range contributes zeros
+#pragma unroll
+      for (int st = 0; st < ST; ++st) {
+        const int kk = k0 + st * 32 + (lane >> 4) * 8;  // d % 8 == 0: 8 values all in or all out
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          xv[st][mb] = kk < ke ? *reinterpret_cast<const bf16x8*>(xr[mb] + k0 + st * 32) : zero8;
+      }
+    }
+    if (WTR) {
+      // the W_r rows have landed once at most the x loads are outstanding
+      if (ST * MB == 1) wait_vmcnt_route<1>();
+      else if (ST * MB == 2) wait_vmcnt_route<2>();
+      else if (ST * MB == 4) wait_vmcnt_route<4>();
+      else if (ST * MB == 8) wait_vmcnt_route<8>();
+      else wait_vmcnt_route<16>();
+    }
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+      bf16x8 bv[NB];
+      if (WTR) {
+        const uint32_t base = (uint32_t)(st * 32 * E * 2);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint32_t lo_off = tr_in[nb] ? tr_lo[nb] + base : zrel;
+          const uint32_t hi_off = tr_in[nb] ? tr_lo[nb] + base + (uint32_t)(4 * E * 2) : zrel;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wt + lo_off));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wt + hi_off));
+          bv[nb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      } else {
+        // gather: lane l takes expert 16 nb + l % 16, K rows kk .. kk + 7
+        const int kk = k0 + st * 32 + (lane >> 4) * 8;
+        if (E == 1) {
+          // one contiguous column: lane l % 16 == 0 loads its 8 K values at once
+          bv[0] = ((lane & 15) == 0 && kk < ke) ? *reinterpret_cast<const bf16x8*>(W + kk) : zero8;
+#pragma unroll
+          for (int nb = 1; nb < NB; ++nb) bv[nb] = zero8;
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const int e = nb * 16 + (lane & 15);
+            bf16_t tmp[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              tmp[i] = (e < E && kk < ke) ? W[(size_t)(kk + i) * E + e] : (bf16_t)0;
+            u32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (uint32_t)tmp[2 * i] | ((uint32_t)tmp[2 * i + 1] << 16);
+            bv[nb] = as_bf16x8(v);
+          }
+        }
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          acc[mb][nb] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[st][mb], bv[st][nb], acc[mb][nb], 0, 0, 0);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xv[st][mb], bv[nb], acc[mb][nb], 0, 0, 0);
+    }
   }
-
-  // accumulator lane layout of a 16x16 block: column lane % 16, rows
-  // 4 * (lane / 16) + i
+  // partial logits of each wave; the accumulator layout of a 16 x 16 block
+  // is column lane % 16, rows 4 (lane / 16) + i
+  __syncthreads();  // every wave is done with its W_r tile
+  float* part = reinterpret_cast<float*>(smem);  // [NWV][TW][Ep]
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -250,6 +355,7 @@ __global__ __launch_bounds__(NWV * 64) void route_bf16_kernel(RouteArgs a, const
     lv[u] = v;
   }
   __syncthreads();
+  float* ll = part;  // [TW][ls] logits
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int i = tid + u * NT;
@@ -286,50 +392,50 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(RouteArgs a) {
   select_and_weigh<NV>(ll, ls, a, t_base, kTok);
 }
 
-template <int NB, int MB, int NWV>
-hipError_t launch_nb_mb(const RouteArgs& a, const bf16_t* Wt, hipStream_t s) {
-  constexpr int Ep = NB * 16, TW = MB * 16;
-  const size_t lds = (size_t)NWV * TW * Ep * 4;  // >= TW * (Ep + 1) * 4, the logits reuse it
-  static_assert((size_t)NWV * TW * Ep * 4 <= 65536, "partial logits fit 64 KiB");
-  hipLaunchKernelGGL((route_bf16_kernel<NB, MB, NWV>), dim3(cdiv(a.T, TW)), dim3(NWV * 64), lds, s,
-                     a, Wt);
+template <int NB, int MB, int NWV, bool WTR>
+hipError_t launch_cfg(const RouteArgs& a, hipStream_t s) {
+  // K-steps per chunk: a chunk's x loads (16 KiB a wave at most, 64
+  // registers) are all in flight before its first MFMA, and the waves' W_r
+  // tiles take at most 64 KiB of LDS
+  constexpr int ST_X = 16 / MB < 8 ? 16 / MB : 8;
+  constexpr int ST_W = 1024 / (NB * 16 * NWV) > 0 ? 1024 / (NB * 16 * NWV) : 1;
+  constexpr int ST = ST_X < ST_W ? ST_X : ST_W;
+  using C = RouteCfg<NB, MB, NWV, ST>;
+  static_assert(C::LDS <= 160 * 1024, "LDS");
+  auto kern = route_bf16_kernel<NB, MB, NWV, ST, WTR>;
+  if (C::LDS > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(cdiv(a.T, C::TW)), dim3(NWV * 64), C::LDS, s, a);
   return hipGetLastError();
 }
 
-// Token blocks per workgroup (MB) and K-splitting waves (NWV): the kernel
-// streams x once, so it wants many loads in flight -- about 16 waves per
-// CU -- while the partial logits [NWV][16 MB][Ep] stay within 64 KiB and
-// each workgroup reads the transposed W_r (from L2) once per 16 MB tokens.
+// Tokens per workgroup (16 MB) and K-splitting waves (NWV): the kernel
+// streams x once, so it wants many loads in flight on every compute unit,
+// while W_r is re-read (from L2) once per workgroup -- more tokens per
+// workgroup means fewer W_r reads per token but fewer workgroups.  E not a
+// multiple of 8 (small gates) takes one shape.
 template <int NB>
-hipError_t launch_nb(const RouteArgs& a, const bf16_t* Wt, hipStream_t s) {
-  constexpr int Ep = NB * 16;
-  constexpr int NW16 = (16 * 16 * Ep * 4 <= 65536) ? 16 : (8 * 16 * Ep * 4 <= 65536) ? 8 : 4;
-  constexpr int NW32 = (16 * 32 * Ep * 4 <= 65536) ? 16 : (8 * 32 * Ep * 4 <= 65536) ? 8 : 4;
-  if constexpr (4 * 64 * Ep * 4 <= 65536) {
-    // 4 token blocks for long batches: a quarter of the W_r reads per token
-    if (a.T >= 256 * 64) return launch_nb_mb<NB, 4, 4>(a, Wt, s);
+hipError_t launch_nb(const RouteArgs& a, hipStream_t s) {
+  // more than 128 experts: 4-wave workgroups (one per SIMD, the whole
+  // register file) keep the 16 accumulator blocks and two chunks in registers
+  constexpr int NWS = NB >= 8 ? 4 : 8;
+  if (a.E % 8 != 0) return launch_cfg<NB, 1, NWS, false>(a, s);
+  if constexpr (NB <= 4) {
+    if (a.T >= 256 * 64) return launch_cfg<NB, 4, 4, true>(a, s);
+    if (a.T >= 256 * 32) return launch_cfg<NB, 2, 4, true>(a, s);
   }
-  if constexpr (4 * 32 * Ep * 4 <= 65536) {
-    if (a.T >= 256 * 32) {
-      // 2 token blocks: fewer reads of W_r per token
-      if (a.T >= 256 * 32 * 4) return launch_nb_mb<NB, 2, (NW32 > 4 ? 4 : NW32)>(a, Wt, s);
-      return launch_nb_mb<NB, 2, (NW32 > 8 ? 8 : NW32)>(a, Wt, s);
-    }
-  }
-  if (a.T >= 256 * 16 * 2) return launch_nb_mb<NB, 1, (NW16 > 8 ? 8 : NW16)>(a, Wt, s);
-  return launch_nb_mb<NB, 1, NW16>(a, Wt, s);
+  if (a.T >= 256 * 16 * 2) return launch_cfg<NB, 1, 4, true>(a, s);
+  return launch_cfg<NB, 1, NWS, true>(a, s);
 }
 
 }  // namespace
 
-size_t route_workspace_bytes(int d, int E, bool bf16) {
-  if (!bf16) return 0;
-  return align_up((size_t)cdiv(E, 16) * 16 * d * sizeof(bf16_t), 256);
-}
-
 hipError_t launch_route(const void* x, const void* W_r, const float* bias, int T, int d, int E,
                         int k, bool renorm, bool bf16, int32_t* idx, float* w, float* logits_out,
-                        void* ws, hipStream_t s) {
+                        hipStream_t s) {
   RouteArgs a{x, W_r, bias, T, d, E, k, renorm ? 1 : 0, idx, w, logits_out};
   if (!bf16) {
     const size_t lds = (size_t)64 * (E + 1) * 4;  // <= 64 * 257 * 4 = 65792 bytes
@@ -348,28 +454,14 @@ hipError_t launch_route(const void* x, const void* W_r, const float* bias, int T
     if (E <= 64) return launch(route_f32_kernel<4>);
     return launch(route_f32_kernel<16>);
   }
-  const int Ep = cdiv(E, 16) * 16;
-  bf16_t* Wt = static_cast<bf16_t*>(ws);
-  hipLaunchKernelGGL(transpose_router_kernel, dim3(cdiv((d / 8) * Ep, kThreads)), dim3(kThreads),
-                     0, s, static_cast<const bf16_t*>(W_r), d, E, Ep, Wt);
-  switch (Ep / 16) {
-    case 1: return launch_nb<1>(a, Wt, s);
-    case 2: return launch_nb<2>(a, Wt, s);
-    case 3: return launch_nb<3>(a, Wt, s);
-    case 4: return launch_nb<4>(a, Wt, s);
-    case 5: return launch_nb<5>(a, Wt, s);
-    case 6: return launch_nb<6>(a, Wt, s);
-    case 7: return launch_nb<7>(a, Wt, s);
-    case 8: return launch_nb<8>(a, Wt, s);
-    case 9: return launch_nb<9>(a, Wt, s);
-    case 10: return launch_nb<10>(a, Wt, s);
-    case 11: return launch_nb<11>(a, Wt, s);
-    case 12: return launch_nb<12>(a, Wt, s);
-    case 13: return launch_nb<13>(a, Wt, s);
-    case 14: return launch_nb<14>(a, Wt, s);
-    case 15: return launch_nb<15>(a, Wt, s);
-    default: return launch_nb<16>(a, Wt, s);
-  }
+  // column blocks of 16 experts, rounded up to one of a few widths (the
+  // columns past E read zeros and are never selected)
+  const int nb = cdiv(E, 16);
+  if (nb <= 1) return launch_nb<1>(a, s);
+  if (nb <= 2) return launch_nb<2>(a, s);
+  if (nb <= 4) return launch_nb<4>(a, s);
+  if (nb <= 8) return launch_nb<8>(a, s);
+  return launch_nb<16>(a, s);
 }
 
 }  // namespace moe

@@ -87,8 +87,6 @@ class MoeLayer:
         self.a = e(R, f, dt=act)
         self.y_perm = e(R, d) if self.comb == "separate" else None
         self.y = e(T, d)
-        self.ws_route_bytes = L.moe_route_workspace_size(d, E, self.dtype)
-        self.ws_route = e(max(self.ws_route_bytes, 16), dt=torch.uint8)
         self.ws_perm_bytes = L.moe_permute_workspace_size(T, E, k)
         self.ws_perm = e(max(self.ws_perm_bytes, 16), dt=torch.uint8)
         self.ws_ffn_bytes = L.moe_ffn_workspace_size(E, R, d, f)
@@ -114,16 +112,13 @@ class MoeLayer:
                 self.g_w = e(T, 1)
                 self.g_logit = e(T, 1)
                 self.w_s_col = layer["w_s"].reshape(d, 1).contiguous()
-                self.g_ws_bytes = L.moe_route_workspace_size(d, 1, self.dtype)
-                self.g_ws = e(max(self.g_ws_bytes, 16), dt=torch.uint8)
 
     # -- stages ------------------------------------------------------------
     def route(self, stream=None):
         c, t = self.cfg, self.t
         score = L.MOE_SOFTMAX_TOPK_RENORM if c.renorm else L.MOE_SOFTMAX_TOPK
         L.moe_route(t["x"], t["W_r"], t.get("b"), c.T, c.d, c.E, c.k, score, self.dtype,
-                    self.idx, self.w, self.logits, self.ws_route, self.ws_route_bytes,
-                    stream=stream)
+                    self.idx, self.w, self.logits, stream=stream)
 
     def permute(self, stream=None):
         c, t = self.cfg, self.t
@@ -144,8 +139,7 @@ class MoeLayer:
         if c.shared_gated:
             # gate logit x . w_s (a one-column router)
             L.moe_route(t["x"], self.w_s_col, None, T, d, 1, 1, L.MOE_SOFTMAX_TOPK, self.dtype,
-                        self.g_idx, self.g_w, self.g_logit, self.g_ws, self.g_ws_bytes,
-                        stream=stream)
+                        self.g_idx, self.g_w, self.g_logit, stream=stream)
         if self.train:
             L.moe_expert_up_save(t["x"], None, self.s_offsets, 1, T, d, fs, self.dtype,
                                  t["Ws_gate"], t["Ws_up"], self.s_a, self.s_h, self.s_u, self.s_ws,

@@ -371,9 +371,99 @@ def check_full_sampled(cfg, n_sample=24):
     return counts
 
 
-@pytest.mark.parametrize("name", ["mixtral", "qwen2moe", "mixtral_skew", "deepseek"])
-def test_full_size_sampled(L, name):
-    check_full_sampled(CONFIGS[name])
+def check_full(cfg):
+    """The layer at full size in the launch configuration the benchmark times
+    (the "fast" path): routing and dispatch on every token, and y compared
+    on all T x d elements with the oracle at the GPU's selection (experts
+    converted to float64 one at a time)."""
+    log(f"[full] {cfg.name} T={cfg.T} d={cfg.d} f={cfg.f} E={cfg.E} k={cfg.k} (every token)")
+    layer = make_layer(cfg, seed=0, device="cuda")
+    m = run_layer(cfg, layer, "fast")
+    h = host_layer(layer, lazy=True)
+    idx_g, w_g, near = check_routing(cfg, m, h)
+    log(f"  routing ok ({len(near)} certified near-ties)")
+    check_dispatch(cfg, m, idx_g, w_g)
+    log("  dispatch ok")
+    y = m.y.cpu().double().numpy()
+    del m, layer
+    torch.cuda.empty_cache()
+    ref = O.forward(h, cfg.k, cfg.renorm, idx=idx_g)["y"]
+    check_y(cfg, y, ref, "all tokens")
+
+
+@pytest.mark.parametrize("name", ["tiny", "mixtral", "qwen2moe", "mixtral_skew", "deepseek"])
+def test_full_size_every_token(L, name):
+    check_full(CONFIGS[name])
+
+
+def test_permute_large_histogram_path(L):
+    """256 experts and more than 32768 / 256 blocks of 256 tokens: the
+    permute takes its separate-scan path (block histograms with atomic
+    totals, one scan workgroup, then the ranks from the scanned bases).
+    f = 512: with a very narrow FFN (f = 48) the bf16 rounding of the
+    layer-0 output alone moves some of the 2.1M outputs by 2.7e-2 rms (CPU
+    emulation), past the bar that the workloads' widths keep well inside."""
+    cfg = small_cfg(E=256, k=8, T=33001, d=64, f=512)
+    log(f"[edge] permute scan path T={cfg.T} E={cfg.E} k={cfg.k}")
+    layer = make_layer(cfg, seed=8, device="cuda")
+    for path in ("fast", "reference"):
+        m = run_layer(cfg, layer, path)
+        h = host_layer(layer)
+        idx_g, w_g, _ = check_routing(cfg, m, h)
+        perm_token = check_dispatch(cfg, m, idx_g, w_g)
+        if path == "reference":
+            assert torch.equal(m.x_perm.cpu(), layer["x"].cpu()[torch.from_numpy(perm_token)])
+        check_y(cfg, m.y.cpu().double().numpy(),
+                O.forward(h, cfg.k, cfg.renorm, idx=idx_g)["y"], path)
+
+
+@pytest.mark.parametrize("path", ["fast", "reference"])
+def test_combine_more_than_eight_slots(L, path):
+    """k = 10 of 16 experts: the combine's run-time slot loop."""
+    cfg = small_cfg(E=16, k=10, T=600, d=72, f=40)
+    log(f"[edge] combine k={cfg.k} path={path}")
+    layer = make_layer(cfg, seed=10, device="cuda")
+    m = run_layer(cfg, layer, path)
+    h = host_layer(layer)
+    idx_g, w_g, _ = check_routing(cfg, m, h)
+    check_dispatch(cfg, m, idx_g, w_g)
+    check_y(cfg, m.y.cpu().double().numpy(), O.forward(h, cfg.k, cfg.renorm, idx=idx_g)["y"], path)
+
+
+def test_nan_token_gets_valid_distinct_experts(L):
+    """A token whose x row holds a NaN has NaN logits for every expert; the
+    selection must still give k distinct experts in [0, E), so the dispatch
+    and the gather stay in bounds, and every other token is unaffected."""
+    cfg = small_cfg(E=8, k=3, T=300)
+    log("[edge] NaN token")
+    layer = make_layer(cfg, seed=12, device="cuda")
+    layer["x"][7, 5] = float("nan")
+    m = run_layer(cfg, layer, "reference")
+    idx = m.idx.cpu().numpy()
+    assert np.all((idx >= 0) & (idx < cfg.E))
+    assert all(len(set(r)) == cfg.k for r in idx.tolist())
+    assert idx[7].tolist() == [0, 1, 2]  # all logits NaN: they rank as equal, lower index first
+    counts = m.counts.cpu().numpy()
+    assert counts.sum() == cfg.T * cfg.k
+    h = host_layer(layer)
+    ok = np.arange(cfg.T) != 7
+    L32 = m.logits.to("cpu", torch.float64).numpy()
+    assert np.array_equal(O.select_topk(L32[ok], cfg.k), idx[ok].astype(np.int64))
+    idx_g = idx.astype(np.int64)
+    w_g = m.w.cpu().numpy().astype(np.float64)  # token 7's weights are NaN
+    counts, offsets, perm_token, inv, perm_w = O.dispatch(idx_g, w_g, cfg.E)
+    assert np.array_equal(m.counts.cpu().numpy(), counts)
+    assert np.array_equal(m.offsets.cpu().numpy(), offsets)
+    assert np.array_equal(m.perm_token.cpu().numpy(), perm_token)
+    assert np.array_equal(m.inv.cpu().numpy(), inv)
+    assert np.array_equal(m.perm_w.cpu().numpy().astype(np.float64), perm_w, equal_nan=True)
+    x_ref = layer["x"].cpu()[torch.from_numpy(perm_token)]
+    assert torch.equal(torch.nan_to_num(m.x_perm.cpu(), nan=7.0), torch.nan_to_num(x_ref, nan=7.0))
+    y = m.y.cpu().double().numpy()
+    assert np.all(np.isfinite(np.delete(y, 7, axis=0)))
+    sub = dict(h, x=h["x"][ok])
+    ref = O.forward(sub, cfg.k, cfg.renorm, idx=idx_g[ok])["y"]
+    check_y(cfg, y[ok], ref, "tokens without NaN")
 
 
 # ---------------------------------------------------------------- sweeps

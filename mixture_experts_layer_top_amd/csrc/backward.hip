@@ -629,10 +629,7 @@ __global__ __launch_bounds__(kThreads) void xtg_mfma_kernel(const bf16_t* __rest
 // token l % 16 of a block, 4 consecutive columns), so dx is read and written
 // once, 16 bytes per lane, and the sum order is fixed: experts in order, hi
 // before lo.  VEC: W rows 16-byte aligned (E a multiple of 8, W aligned).
-#ifndef MOE_DX_TOKENS
-#define MOE_DX_TOKENS 128
-#endif
-constexpr int DM_T = MOE_DX_TOKENS, DM_C = 256;
+constexpr int DM_T = 128, DM_C = 256;
 template <int KS, bool VEC>
 __global__ __launch_bounds__(kThreads) void dx_mfma_kernel(const bf16_t* __restrict__ Gh,
                                                            const bf16_t* __restrict__ Gl,

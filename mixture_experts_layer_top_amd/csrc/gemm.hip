@@ -45,24 +45,15 @@ namespace moe {
 namespace {
 
 constexpr int BM = 256;        // rows per tile
-#ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 64
-#endif
-constexpr int BK = MOE_GEMM_BK;  // K per pipeline stage (32 or 64)
+constexpr int BK = 64;         // K per pipeline stage
 constexpr int A_CPR = BK / 8;    // 16-byte chunks per A row in a stage
 constexpr int A_RPL = 1024 / (BK * 2);  // A rows per 1 KiB load
 constexpr int A_LOADS = BM * BK * 2 / 1024;
-#ifndef MOE_GEMM_NST
-#define MOE_GEMM_NST (BK == 32 ? 4 : 2)
-#endif
-// MOE_GEMM_BRING3: with BK = 64, give the weight operand (B) three LDS
-// stage buffers and the token operand (A) two (64 + 96 = 160 KiB): weight
-// loads are issued two stages ahead, token rows one stage ahead.
-#ifndef MOE_GEMM_BRING3
-#define MOE_GEMM_BRING3 1
-#endif
-constexpr int NST = MOE_GEMM_NST;  // LDS stages (NST - 1 in flight while one computes)
-constexpr int A_BYTES = BM * BK * 2;  // 16 KiB per stage
+// LDS stage buffers: two for the token operand (A), three for the weight
+// operand (B), 2 x 32 + 3 x 32 = 160 KiB: weight loads are issued two
+// stages ahead, token rows one stage ahead
+constexpr int A_SLOTS = 2, B_SLOTS = 3;
+constexpr int A_BYTES = BM * BK * 2;  // 32 KiB per stage
 
 // Per tile-width constants.  BNA = accumulator columns per tile.
 template <int BNA>
@@ -73,7 +64,6 @@ struct TileCfg {
   static constexpr int ROWS_PER_LOAD = 1024 / (BNA * 2);  // B rows per 1 KiB load
   static constexpr int B_LOADS = B_BYTES / 1024;
 };
-static_assert(BK == 32 || BK == 64, "stage depth");
 
 struct GemmArgs {
   const bf16_t* A;          // [n_a, K] rows (x for layer 0, activations for layer 1)
@@ -89,9 +79,7 @@ struct GemmArgs {
   const int32_t* scatter;   // layer 1 fused combine target row, or NULL (identity)
   const float* row_w;       // layer 1 fused combine weight, or NULL (1)
   float* y;                 // layer 1 fused combine target, or NULL
-  int tiles_n;              // column tiles per expert, times ksplit
-  int ksplit;               // K ranges per output tile (layer 1 with fused combine only)
-  int k_per_split;          // K per range, a multiple of BK
+  int tiles_n;              // column tiles per expert
   int grid_per_xcd;         // padded grid / 8
   int m_group;              // ping-pong kernel: most M tiles walked per pass over the N panels
   int m_group_min;          // experts with at most this many M tiles are walked in one pass
@@ -103,7 +91,7 @@ struct GemmArgs {
 };
 
 struct TileInfo {
-  int e, row0, row_end, n_t, m_t, ks;
+  int e, row0, row_end, n_t, m_t;
   int nb;  // ping-pong kernel: 16-row blocks in the tile (<= BM / 16)
   bool ok;
 };
@@ -164,9 +152,6 @@ __device__ __forceinline__ TileInfo locate_tile(const GemmArgs& p, int tile) {
     ti.m_t = local / p.tiles_n;
     ti.n_t = local - ti.m_t * p.tiles_n;
   }
-  // the column index runs over (n-tile, K range) pairs, K range innermost
-  ti.ks = ti.n_t % p.ksplit;
-  ti.n_t = ti.n_t / p.ksplit;
   ti.row0 = toff + ti.m_t * BM;
   ti.row_end = min(ti.row0 + BM, p.offsets[ti.e + 1]);
   return ti;
@@ -175,17 +160,13 @@ __device__ __forceinline__ TileInfo locate_tile(const GemmArgs& p, int tile) {
 // Byte offsets inside one stage.
 // A: [BM rows][BK] bf16, 2 BK bytes per row.  A fragment read touches 16
 // consecutive rows at one 16-byte chunk.  The chunk index is XOR-ed with
-// ((row >> 1) ^ (row >> 3)) & 3 (BK = 32) or (row >> 1) & 7 (BK = 64); the
-// latter measured free of bank conflicts on gfx950.
+// (row >> 1) & 7, measured free of bank conflicts on gfx950.
 // B: [BK rows][BNA] bf16.  One transpose read touches 4 rows x 32 bytes per
 // 16 lanes (rows 8 apart for the next 16 lanes).  The chunk index is XOR-ed
 // with 2 * (row % 8) + (row & 8): even values keep the 32-byte pairs whole,
 // the low part spreads 4 rows over a 128-byte window and bit 3 moves rows
 // 8..15 to the other half of a 256-byte window.
-__device__ __forceinline__ int a_swz(int row) {
-  // BK = 32: 4 chunks per row; BK = 64: 8 chunks per row
-  return BK == 32 ? (((row >> 1) ^ (row >> 3)) & 3) : ((row >> 1) & 7);
-}
+__device__ __forceinline__ int a_swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int a_off(int row, int chunk) {
   return row * (BK * 2) + ((chunk ^ a_swz(row)) << 4);
 }
@@ -205,10 +186,6 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 // K tail of the last stage arrives as zeros (no clearing pass needed).
 __device__ __attribute__((aligned(16))) const bf16_t kZeroChunk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 
-#ifndef MOE_GEMM_PP
-#define MOE_GEMM_PP 0
-#endif
-
 // One direct-to-LDS load: 64 lanes x 16 bytes from their global addresses to
 // the 1 KiB of LDS starting at lds_addr (wave-uniform).  Written as inline
 // assembly so that the compiler's wait-count pass does not model it: these
@@ -227,24 +204,6 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_addr) {
       : "m0");
 }
 
-// One 4-byte-per-lane direct-to-LDS load, used only to pull lines into L2
-// ahead of their real load (the LDS bytes it writes are never read).
-__device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dword %0, off"
-      :
-      : "v"(gptr), "s"(lds_addr)
-      : "m0");
-}
-
-#ifndef MOE_GEMM_L2PF
-#define MOE_GEMM_L2PF 0
-#endif
-#ifndef MOE_GEMM_SPREAD
-#define MOE_GEMM_SPREAD 1
-#endif
-
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
@@ -255,37 +214,20 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-// Wait until a stage's loads have landed, given that after them were issued
-// TAIL more loads of the same issue group and `later` groups of LPS loads.
-template <int LPS, int TAIL = 0>
-__device__ __forceinline__ void wait_stages(int later) {
-  if (later >= 3) wait_vmcnt<3 * LPS + TAIL>();
-  else if (later == 2) wait_vmcnt<2 * LPS + TAIL>();
-  else if (later == 1) wait_vmcnt<LPS + TAIL>();
-  else wait_vmcnt<TAIL>();
-}
-
 // WM x WN waves; each owns (BM / WM) x (BNA / WN) accumulators.
 template <bool UP, int WM, int WN, int BNA>
 __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(GemmArgs p) {
   using C = TileCfg<BNA>;
   constexpr int NW = WM * WN;
-  constexpr int NT = 64 * NW;
   constexpr int MI = BM / WM / 16;     // 16-row blocks per wave
   constexpr int NJ = BNA / WN / 16;    // 16-column blocks per wave
   constexpr int A_LD = A_LOADS / NW;   // A loads per wave per stage
   constexpr int B_LD = C::B_LOADS / NW;
-  // L2 warm-up loads per wave per stage (issued right after each stage's loads)
-  constexpr int PF = (MOE_GEMM_L2PF > 0 && NW == 8 && !MOE_GEMM_PP) ? 1 : 0;
-  constexpr int LPS = A_LD + B_LD + PF;
   static_assert(A_LD >= 1 && B_LD >= 1 && A_LOADS % NW == 0 && C::B_LOADS % NW == 0,
                 "loader split");
   static_assert(!UP || NJ % 2 == 0, "gate/up pairs");
-  constexpr bool RING3 = MOE_GEMM_BRING3 && BK == 64 && !MOE_GEMM_PP;
-  constexpr int A_SLOTS = RING3 ? 2 : NST;
-  constexpr int B_SLOTS = RING3 ? 3 : NST;
   constexpr int LDS_OPS = A_SLOTS * A_BYTES + B_SLOTS * C::B_BYTES;
-  __shared__ __attribute__((aligned(1024))) char lds[LDS_OPS + (MOE_GEMM_L2PF ? 256 : 0)];
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_OPS];
   // operand buffers: A slots first, then B slots
   auto a_base = [&](int kt) { return (kt % A_SLOTS) * A_BYTES; };
   auto b_base = [&](int kt) { return A_SLOTS * A_BYTES + (kt % B_SLOTS) * C::B_BYTES; };
@@ -305,9 +247,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
   const int K = p.K, N = p.N;
   const int n0 = ti.n_t * (UP ? BNA / 2 : BNA);
   const uint32_t lds0 = lds_addr_of(lds);
-  const int k_begin = ti.ks * p.k_per_split;
-  const int k_end = min(K, k_begin + p.k_per_split);
-  const int nk_ = cdiv(k_end - k_begin, BK);  // K stages of this tile
+  const int nk = cdiv(K, BK);  // K stages (the last one zero-filled past K)
 
   // ---- direct-to-LDS loader.  One load moves 64 lanes x 16 B = 1 KiB into
   // consecutive LDS bytes, so each layout's swizzle is applied on the global
@@ -348,59 +288,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
   // the last are skipped
   auto issue_load2 = [&](int kt_a, int kt_b, int i) {
     if (i < A_LD) {
-      if (kt_a >= nk_) return;
-      const int kk = k_begin + kt_a * BK + a_k[i];
-      const bf16_t* src = kk < k_end ? a_src[i] + kk : kZeroChunk;  // K tail -> zeros
+      if (kt_a >= nk) return;
+      const int kk = kt_a * BK + a_k[i];
+      const bf16_t* src = kk < K ? a_src[i] + kk : kZeroChunk;  // K tail -> zeros
       lds_dma16(src, lds0 + (uint32_t)(a_base(kt_a) + (wave * A_LD + i) * 1024));
     } else {
-      if (kt_b >= nk_) return;
+      if (kt_b >= nk) return;
       const int q = i - A_LD;
-      const int kr = min(k_begin + kt_b * BK + b_krow[q], K - 1);
+      const int kr = min(kt_b * BK + b_krow[q], K - 1);
       lds_dma16(b_src[q] + (size_t)kr * N,
                 lds0 + (uint32_t)(b_base(kt_b) + (wave * B_LD + q) * 1024));
     }
-  };
-  auto issue_load = [&](int kt, int i) { issue_load2(kt, kt, i); };
-  auto issue_stage = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < A_LD + B_LD; ++i) issue_load(kt, i);
-  };
-
-  // ---- L2 warm-up of a later stage: one lane per 128-byte line.  Waves 0-3
-  // cover the 256 A rows (one line each when BK = 64), waves 4-7 the B rows
-  // (4 lines per K row of 256 columns).
-  const bf16_t* pf_src = nullptr;
-  int pf_kstride = 0;  // elements per K step of the line this lane warms
-  if (PF) {
-    if (wave < 4) {
-      int r = ti.row0 + wave * 64 + lane;
-      if (r >= ti.row_end) r = ti.row0;
-      pf_src = p.A + (size_t)(p.gather ? p.gather[r] : r) * K;
-      pf_kstride = 1;
-    } else {
-      const int krow = (wave - 4) * 16 + (lane >> 2);
-      const int line = lane & 3;
-      const bf16_t* mat;
-      int col;
-      if (UP) {
-        mat = line < 2 ? p.B0 : p.B1;
-        col = n0 + (line & 1) * 64;
-      } else {
-        mat = p.B0;
-        col = n0 + line * 64;
-      }
-      if (col >= N) col = N - 8;
-      pf_src = mat + (size_t)ti.e * K * N + (size_t)krow * N + col;
-      pf_kstride = N;
-    }
-  }
-  const uint32_t pf_lds = lds0 + (uint32_t)LDS_OPS;
-  auto prefetch_stage = [&](int kt) {
-    const int k0 = k_begin + kt * BK;
-    int koff = k0;
-    if (wave >= 4) koff = min(k0 + (wave - 4) * 16 + (lane >> 2), K - 1) - ((wave - 4) * 16 + (lane >> 2));
-    else koff = min(k0, K - 8);
-    lds_dma4(pf_src + (size_t)koff * pf_kstride, pf_lds);
   };
 
   // ---- per-lane LDS read offsets (within a stage)
@@ -435,7 +333,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj) acc[mi][nj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = nk_;
   auto read_frags = [&](int kt, int ks, bf16x8 (&af)[MI], bf16x8 (&bfr)[NJ]) {
     const char* As = lds + a_base(kt);
     const char* Bs = lds + b_base(kt);
@@ -455,7 +352,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
       for (int nj = 0; nj < NJ; ++nj)
         acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr[nj], acc[mi][nj], 0, 0, 0);
   };
-  // the same MFMAs with the loads of stage `ld_kt` (if < nk) spread between
+  // the same MFMAs with the loads of A(ld_a) and B(ld_b) spread between
   // their rows, so that no wave stalls on a burst of load issues while its
   // matrix core idles
   auto mfmas_with_loads = [&](const bf16x8 (&af)[MI], const bf16x8 (&bfr)[NJ], int ld_a,
@@ -473,103 +370,30 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
     }
   };
 
-  // every stage's loads are followed by the warm-up of stage + MOE_GEMM_L2PF
-  // (clamped to the last stage, so each issue group has LPS loads)
-  auto issue_group = [&](int kt) {
-    issue_stage(kt);
-    if (PF) prefetch_stage(min(kt + MOE_GEMM_L2PF, nk - 1));
-  };
-  if (RING3) {
-    // B(0), then the steady-state group [A(0), B(1)]
+  // prologue: B(0), then the steady-state group [A(0), B(1)]
 #pragma unroll
-    for (int i = A_LD; i < A_LD + B_LD; ++i) issue_load2(0, 0, i);
+  for (int i = A_LD; i < A_LD + B_LD; ++i) issue_load2(0, 0, i);
 #pragma unroll
-    for (int i = 0; i < A_LD + B_LD; ++i) issue_load2(0, 1, i);
-  } else {
-#pragma unroll
-    for (int s = 0; s < NST - 1; ++s)
-      if (s < nk) issue_group(s);
-  }
-#ifdef MOE_GEMM_WAVE_SKIP
-  const bool wave_active = wrow0 < ti.row_end - ti.row0;
-#else
-  // measured: letting a tail tile's empty waves skip their MFMAs makes that
-  // tile finish early and breaks the lockstep of the tiles that share its
-  // operand panels in L2 (layer-0 L2 hit rate 59% with the skip, 79% without)
-  constexpr bool wave_active = true;
-#endif
-
-#if MOE_GEMM_PP
-  // Ping-pong: the two halves of the waves (one wave of each per SIMD) run
-  // one barrier apart, so while one half reads its fragments from LDS the
-  // other half keeps the SIMD's matrix core busy.  Per stage kt each wave
-  // runs a memory phase (refill the buffer of stage kt - 1, read stage kt's
-  // fragments) and a compute phase, each closed by a barrier.  Visibility:
-  // before the barrier that precedes any read of stage kt + 1, every wave
-  // has waited for its own loads of that stage (half 1 at the end of its
-  // memory phase, half 0 at the end of its compute phase).  Reuse: a buffer
-  // is refilled only after the barrier that closes the last memory phase
-  // reading it, and every wave drains its LDS reads before that barrier.
-  static_assert(NW == 8 && WM == 2 && KS == 1, "ping-pong pairs the two row halves");
-  const int half = wm;
-  wait_stages<LPS>(min(NST - 2, nk - 1));
-  __builtin_amdgcn_s_barrier();
-  if (half == 1) __builtin_amdgcn_s_barrier();
+  for (int i = 0; i < A_LD + B_LD; ++i) issue_load2(0, 1, i);
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + NST - 1 < nk) issue_stage(kt + NST - 1);
+    // A(kt) and B(kt) have landed once at most B(kt + 1) is outstanding;
+    // then every wave's share is visible after the barrier, and every wave
+    // is done with the buffers of stage kt - 1
+    if (kt + 1 < nk) wait_vmcnt<B_LD>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
     bf16x8 af[MI], bfr[NJ];
     read_frags(kt, 0, af, bfr);
-    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
-    if (half == 1 && kt + 1 < nk) wait_stages<LPS>(min(NST - 2, nk - 2 - kt));
-    __builtin_amdgcn_s_barrier();
-    mfmas(af, bfr);
-    if (half == 0 && kt + 1 < nk) wait_stages<LPS>(min(NST - 2, nk - 2 - kt));
-    __builtin_amdgcn_s_barrier();
-  }
-  if (half == 0) __builtin_amdgcn_s_barrier();
-  wait_vmcnt<0>();
-#else
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed once at most the loads of the later stages issued
-    // so far are outstanding; then every wave's share is visible after the
-    // barrier, and every wave is done with the buffer of stage kt - 1
-    if (RING3) {
-      // A(kt) and B(kt) have landed once at most B(kt + 1) is outstanding
-      if (kt + 1 < nk) wait_vmcnt<B_LD>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_stages<LPS, PF>(min(NST - 2, nk - 1 - kt));
-    }
-    __builtin_amdgcn_s_barrier();
-    bf16x8 af[MI], bfr[NJ];
-    if (wave_active) read_frags(kt, 0, af, bfr);
-    // refill the buffer of stage kt - 1 (issued after this stage's first
-    // reads so that no read waits for the new loads)
-#if MOE_GEMM_SPREAD
-    if (RING3) {
-      // A(kt + 1) into the A slot of stage kt - 1, B(kt + 2) into the B slot
-      // of stage kt - 1: both were last read before this stage's barrier
-      mfmas_with_loads(af, bfr, kt + 1, kt + 2);
-    } else if (wave_active) {
-      mfmas_with_loads(af, bfr, kt + NST - 1, kt + NST - 1);
-    } else if (kt + NST - 1 < nk) {
-      issue_stage(kt + NST - 1);
-    }
-    if (PF && kt + NST - 1 < nk) prefetch_stage(min(kt + NST - 1 + MOE_GEMM_L2PF, nk - 1));
-#else
-    if (kt + NST - 1 < nk) issue_group(kt + NST - 1);
-    if (wave_active) mfmas(af, bfr);
-#endif
+    // A(kt + 1) into the A slot of stage kt - 1, B(kt + 2) into the B slot
+    // of stage kt - 1: both were last read before this stage's barrier
+    mfmas_with_loads(af, bfr, kt + 1, kt + 2);
 #pragma unroll
     for (int ks = 1; ks < KS; ++ks) {
-      if (wave_active) {
-        read_frags(kt, ks, af, bfr);
-        mfmas(af, bfr);
-      }
+      read_frags(kt, ks, af, bfr);
+      mfmas(af, bfr);
     }
   }
   wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
-#endif
 
   // ---- epilogue.  Accumulator layout of a 16 x 16 block: column lane % 16,
   // rows 4 * (lane / 16) + i.  Outputs go through a per-wave LDS staging
@@ -685,9 +509,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
 // wave waits for its part of stage s + 1 at the end of phase 2s + 1, and
 // the barrier after it makes the stage visible to all.
 //
-// Stage depth PBK = 64 (two MFMA K steps per stage; rings 2 + 3) or 32 (one
-// K step; rings 5 + 5): the same 160 KiB of LDS, but with 32-deep stages
-// every load is issued 3 stages (6 phases) ahead instead of 1 (A) or 2 (B).
+// Stage depth PBK = 64: two MFMA K steps per stage; rings of 2 (A) and 3
+// (B) stages fill the 160 KiB of LDS (32-deep stages with rings of 5 + 5,
+// which issue every load 3 stages ahead, measured slower: twice the
+// barriers per K).
 //
 // B stage layout: two halves of PBK K rows x 128 columns (256 B per row),
 // each 1 KiB load filling 4 rows of one half.  Layer 0: half 0 = W_gate,
@@ -699,9 +524,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
 // advance the scalar base.  K must be a multiple of PBK and the A operand
 // smaller than 4 GiB; other shapes take the kernel above.
 // ------------------------------------------------------------------------
-#ifndef MOE_PP_PRIO
-#define MOE_PP_PRIO 1
-#endif
 namespace pp {
 constexpr int NW = 8, MI = 8, NJ = 4;
 
@@ -709,8 +531,9 @@ template <int PBK>
 struct Cfg {
   static constexpr int SLOT = BM * PBK * 2;            // one operand stage (A or B)
   static constexpr int HALF = PBK * 128 * 2;           // one B half
-  static constexpr int RA = PBK == 64 ? 2 : 5;         // A ring
-  static constexpr int RB = PBK == 64 ? 3 : 5;         // B ring
+  static_assert(PBK == 64, "stage depth");
+  static constexpr int RA = 2;                         // A ring
+  static constexpr int RB = 3;                         // B ring
   static constexpr int LDS_BYTES = (RA + RB) * SLOT;
   static constexpr int KS = PBK / 32;                  // MFMA K steps per stage
   static constexpr int LD = SLOT / 1024 / 4;           // 1 KiB loads per wave per stage
@@ -771,9 +594,7 @@ __device__ __forceinline__ void wait_groups(int n) {
 //   fixup pass, block b < tail * FIXQ: tail tile F + b / FIXQ, 16-row
 //     block b % FIXQ of each wave (the partials are read by FIXQ times more
 //     workgroups than there are tail tiles).
-#ifndef MOE_PP_SPLIT_MAX_ROUNDS
-#define MOE_PP_SPLIT_MAX_ROUNDS 64
-#endif
+constexpr int kSplitMaxRounds = 64;  // no tail split for launches of more rounds
 constexpr int FIXQ = 8;  // fixup workgroups per tail tile (one 16-row block of each wave)
 struct Work {
   int tile, ks, S, item;  // item: index of the split item (-1: a whole tile)
@@ -815,10 +636,10 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   const int nk_all = p.K / pbk;
   int S = 1, kps = p.K;
   // split only where the last round is mostly idle (at most half full) and
-  // the launch has at most MOE_PP_SPLIT_MAX_ROUNDS rounds; otherwise the
+  // the launch has at most kSplitMaxRounds rounds; otherwise the
   // fixup pass costs more than the idle compute units
   if (p.part != nullptr && tail > 0 && 2 * tail <= C &&
-      n_tiles <= MOE_PP_SPLIT_MAX_ROUNDS * C && nk_all >= 2) {
+      n_tiles <= kSplitMaxRounds * C && nk_all >= 2) {
     S = min(C / tail, nk_all);
     kps = cdiv(nk_all, S) * pbk;
     S = cdiv(p.K, kps);  // parts that are not empty
@@ -899,7 +720,6 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   const int r = local - m0 * tn;
   ti.n_t = r / mq;
   ti.m_t = m0 + (r - ti.n_t * mq);
-  ti.ks = 0;
   // Balanced M tiles: the expert's c rows form nbe = ceil(c / 16) blocks of
   // 16, dealt to its tmt = ceil(c / BM) tiles as evenly as possible (the
   // first nbe % tmt tiles take one block more; every tile takes between 1
@@ -1067,7 +887,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
   };
   auto compute = [&]() {
-    if (MOE_PP_PRIO) __builtin_amdgcn_s_setprio(MOE_PP_PRIO);
+    __builtin_amdgcn_s_setprio(1);
     // blocks in (16-row block, K step) order: one test per block of a
     // partial tile
 #pragma unroll
@@ -1080,7 +900,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
           acc[mi][nj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ks][mi], fb[ks][nj],
                                                                acc[mi][nj], 0, 0, 0);
     }
-    if (MOE_PP_PRIO) __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // The two groups run separate loops with the same barrier count: one
@@ -1307,31 +1127,12 @@ int max_tiles_m(int rows, int E) {
   return (int)(((long long)rows + (long long)E * (BM - 1)) / BM);
 }
 
-#ifndef MOE_UP_WN
-#define MOE_UP_WN 4
-#endif
-#ifndef MOE_UP_BNA
-#define MOE_UP_BNA 256
-#endif
-#ifndef MOE_DN_WN
-#define MOE_DN_WN 4
-#endif
-#ifndef MOE_DN_BNA
-#define MOE_DN_BNA 256
-#endif
-#ifndef MOE_GEMM_PPK
-#define MOE_GEMM_PPK 1
-#endif
-#ifndef MOE_PP_BK
-#define MOE_PP_BK 64  // stage depth of the ping-pong kernel (64 or 32)
-#endif
-#ifndef MOE_PP_MGROUP_MB
-#define MOE_PP_MGROUP_MB 32
-#endif
-#ifndef MOE_PP_MGROUP_MIN_MB
-#define MOE_PP_MGROUP_MIN_MB 64
-#endif
-constexpr int UP_WN = MOE_UP_WN, UP_BNA = MOE_UP_BNA, DN_WN = MOE_DN_WN, DN_BNA = MOE_DN_BNA;
+// the general kernel's wave grid (2 x 4 waves) and accumulator columns per tile
+constexpr int UP_WN = 4, UP_BNA = 256, DN_WN = 4, DN_BNA = 256;
+// An expert whose A rows exceed kMGroupMinMB is walked in passes of at most
+// kMGroupMB of A rows, each pass covering all N panels (its rows are then
+// re-read from the last-level cache, not HBM)
+constexpr long long kMGroupMB = 32, kMGroupMinMB = 64;
 
 int num_cus() {
   static int cached[64] = {0};
@@ -1346,63 +1147,27 @@ int num_cus() {
   return cached[dev];
 }
 
-// K ranges per layer-1 tile.  Only with the fused combine (its atomic adds
-// take partial sums for free): pick the smallest split that fills the last
-// round of tiles on the CUs to >= 90%, else the best of 1..4.
-int choose_ksplit(long long tiles, int K, int cus) {
-  int best = 1;
-  double best_eff = 0.0;
-  for (int sp = 1; sp <= 4; ++sp) {
-    if ((long long)sp * BK > K) break;
-    const double work = (double)tiles * sp / cus;
-    const double eff = work / (double)((long long)((tiles * sp + cus - 1) / cus));
-    if (eff >= 0.9) return sp;
-    if (eff > best_eff + 1e-9) {
-      best_eff = eff;
-      best = sp;
-    }
-  }
-  return best;
-}
-
-// a_rows_bytes: size of the A matrix the kernel may read (rows that can be
-// addressed times K times 2 bytes)
 // Workspace of the ping-pong kernel's tail split: one 256 x 256 fp32
 // partial tile per split item, at most one item per compute unit.
 size_t pp_part_bytes(int n_cu) { return (size_t)n_cu * BM * 256 * sizeof(float); }
 
-// p.part: the caller's workspace (ws_bytes); used when large enough
+// a_rows_bytes: size of the A matrix the kernel may read (rows that can be
+// addressed times K times 2 bytes); p.part: the caller's workspace
+// (ws_bytes bytes), used when large enough
 template <bool UP, int WM, int WN, int BNA>
 hipError_t launch_gemm(GemmArgs& p, int rows, int E, int ncols, unsigned long long a_rows_bytes,
                        size_t ws_bytes, hipStream_t s) {
-  const int tiles_n = cdiv(ncols, UP ? BNA / 2 : BNA);
-  const long long tiles_mn = (long long)max_tiles_m(rows, E) * tiles_n;
-  int ksplit = 1;
-  (void)tiles_mn;
-#ifdef MOE_GEMM_KSPLIT
-  // measured slower on the Mixtral-shape layer (the extra atomic traffic
-  // outweighs the fuller last round of tiles), so off unless asked for
-  if (!UP && p.y != nullptr && p.y_perm == nullptr) ksplit = choose_ksplit(tiles_mn, p.K, num_cus());
-#endif
-  p.k_per_split = cdiv(cdiv(p.K, ksplit), BK) * BK;
-  p.ksplit = cdiv(p.K, p.k_per_split);
-  p.tiles_n = tiles_n * p.ksplit;
-  // M tiles per pass over an expert's N panels: experts whose A rows exceed
-  // MOE_PP_MGROUP_MIN_MB are walked in passes of at most MOE_PP_MGROUP_MB of
-  // A rows (0: every expert in one pass)
+  static_assert(BNA == 256, "ping-pong kernel tile width");
+  p.tiles_n = cdiv(ncols, UP ? BNA / 2 : BNA);
   {
     const long long a_tile = (long long)BM * p.K * 2;
-    const long long lim = (long long)MOE_PP_MGROUP_MB << 20;
-    p.m_group = lim > 0 ? (int)std::max(1LL, lim / a_tile) : (1 << 30);
-    p.m_group_min = lim > 0 ? (int)std::max(1LL, ((long long)MOE_PP_MGROUP_MIN_MB << 20) / a_tile)
-                            : (1 << 30);
+    p.m_group = (int)std::max(1LL, (kMGroupMB << 20) / a_tile);
+    p.m_group_min = (int)std::max(1LL, (kMGroupMinMB << 20) / a_tile);
   }
   const long long tiles = (long long)max_tiles_m(rows, E) * p.tiles_n;
   const long long grid = (tiles + 7) / 8 * 8;
   p.grid_per_xcd = (int)(grid / 8);
-#if MOE_GEMM_PPK
-  static_assert(BNA == 256, "ping-pong kernel tile width");
-  if (ksplit == 1 && p.K % MOE_PP_BK == 0 && a_rows_bytes < (1ull << 32)) {
+  if (p.K % 64 == 0 && a_rows_bytes < (1ull << 32)) {
     // main pass: the whole tiles plus at most n_cu split items; then the
     // fixup pass over at most n_cu / 2 tail tiles (both derive the split
     // from the device offsets; without a workspace there is none)
@@ -1414,16 +1179,15 @@ hipError_t launch_gemm(GemmArgs& p, int rows, int E, int ncols, unsigned long lo
     p.nt_y = p.y_perm && (unsigned long long)rows * ncols * 4 > (256ull << 20);
     if (ws_bytes < pp_part_bytes(p.n_cu)) p.part = nullptr;
     const long long grid_pp = grid + (p.part ? p.n_cu : 0);
-    hipLaunchKernelGGL((grouped_gemm_bf16_pp_kernel<UP, MOE_PP_BK, false>),
+    hipLaunchKernelGGL((grouped_gemm_bf16_pp_kernel<UP, 64, false>),
                        dim3((unsigned)grid_pp), dim3(64 * pp::NW), 0, s, p);
     if (p.part) {
       p.fixup = 1;
-      hipLaunchKernelGGL((grouped_gemm_bf16_pp_kernel<UP, MOE_PP_BK, true>),
+      hipLaunchKernelGGL((grouped_gemm_bf16_pp_kernel<UP, 64, true>),
                          dim3((unsigned)(p.n_cu / 2 * FIXQ)), dim3(64 * pp::NW), 0, s, p);
     }
     return hipGetLastError();
   }
-#endif
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<UP, WM, WN, BNA>), dim3((unsigned)grid),
                      dim3(64 * WM * WN), 0, s, p);
   return hipGetLastError();

@@ -1071,29 +1071,18 @@ __global__ void wgrad_sum_kernel(const float* __restrict__ part, int E, int S, i
   __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(dst));
 }
 
-#ifndef MOE_BWD_PP
-#define MOE_BWD_PP 1
-#endif
-
 int pad8(long long g) { return (int)((g + 7) / 8 * 8); }
 
 // DGRAD / WGRAD launches of the ping-pong kernel (tile 256 x 256)
 // the ping-pong DGRAD keeps 32-bit element offsets of a tile's rows
 bool dgrad256_ok(const BwdArgs& p) {
-  return MOE_BWD_PP && 256ll * (p.lda > p.K0 ? p.lda : p.K0) < (1ll << 31) &&
+  return 256ll * (p.lda > p.K0 ? p.lda : p.K0) < (1ll << 31) &&
          (p.B1 == nullptr || p.K1 == p.K0);
 }
 
-#ifndef MOE_BWD_FASTK
-#define MOE_BWD_FASTK 1
-#endif
-
-#ifndef MOE_BWD_PAIR
-#define MOE_BWD_PAIR 1
-#endif
-#ifndef MOE_BWD_PAIR_ROUNDS
-#define MOE_BWD_PAIR_ROUNDS 12
-#endif
+// one launch for a layer's DGRAD and WGRAD only while the data gradient has
+// at most this many rounds of tiles on the compute units (more measured slower)
+constexpr int kPairMaxRounds = 12;
 
 // grids of the 256 x 256 kernel (padded to a multiple of 8); they set the
 // tile counts in the arguments
@@ -1108,10 +1097,10 @@ int wgrad256_grid(BwdArgs& q) {
   q.tiles_n = cdiv(q.N, 256);
   return pad8((long long)q.E * q.ksplit * q.tiles_m * q.tiles_n);
 }
-bool dgrad_fast(const BwdArgs& p) { return MOE_BWD_FASTK && p.K % 64 == 0 && p.K0 % 64 == 0; }
+bool dgrad_fast(const BwdArgs& p) { return p.K % 64 == 0 && p.K0 % 64 == 0; }
 // the scalar-base form keeps 32-bit offsets within 32 rows of A and B
 bool wgrad_fast(const BwdArgs& q) {
-  return MOE_BWD_FASTK && 32ll * (q.lda > q.ldb ? q.lda : q.ldb) * 2 < (1ll << 32);
+  return 32ll * (q.lda > q.ldb ? q.lda : q.ldb) * 2 < (1ll << 32);
 }
 
 // K chunks per expert for the weight gradients: when the launch has fewer
@@ -1174,8 +1163,7 @@ void launch_wgrad256(BwdArgs q, hipStream_t s) {
 // 256 x 256 kernel; returns false (nothing launched) otherwise
 template <int EPI>
 bool launch_pair256(BwdArgs p, BwdArgs q, int rows, hipStream_t s) {
-  if (!MOE_BWD_PAIR || rows <= 0 || !dgrad256_ok(p) || !dgrad_fast(p) || q.a_gather != nullptr ||
-      !MOE_BWD_PP || !wgrad_fast(q))
+  if (rows <= 0 || !dgrad256_ok(p) || !dgrad_fast(p) || q.a_gather != nullptr || !wgrad_fast(q))
     return false;
   const int gd = dgrad256_grid(p, rows);
   // only where the data gradient has few rounds of tiles, so that its last,
@@ -1183,7 +1171,7 @@ bool launch_pair256(BwdArgs p, BwdArgs q, int rows, hipStream_t s) {
   // Measured: a 2.4-round layer gains 8%, 8.3 rounds 1.4%; at 16 and 25
   // rounds the pair was 1-4% slower than two launches.
   const long long typ = ((long long)rows / 256 + p.E / 2) * p.tiles_n;
-  if (typ > (long long)MOE_BWD_PAIR_ROUNDS * device_cu_count()) return false;
+  if (typ > (long long)kPairMaxRounds * device_cu_count()) return false;
   const int gw = wgrad256_grid(q);
   hipLaunchKernelGGL((grouped_gemm_bwd256_pair_kernel<EPI>), dim3(gd + gw), dim3(512), 0, s, p,
                      wgrad_kernel_args(q), gd);
@@ -1255,7 +1243,7 @@ hipError_t launch_expert_down_backward(const void* dy_perm, const int32_t* offse
   q.tiles_n = cdiv(d, BN);
   q.w0 = dW_down;
   q.n_split = d;
-  q.ksplit = MOE_BWD_PP ? wgrad_chunks(E, rows, f, d, ws_bytes) : 1;
+  q.ksplit = wgrad_chunks(E, rows, f, d, ws_bytes);
   q.part = static_cast<float*>(ws);
   if (launch_pair256<EPI_SWIGLU_BWD>(p, q, rows, s)) return hipGetLastError();
   if (rows > 0) {
@@ -1268,11 +1256,7 @@ hipError_t launch_expert_down_backward(const void* dy_perm, const int32_t* offse
                            0, s, p);
     }
   }
-  if (MOE_BWD_PP)
-    launch_wgrad256(q, s);
-  else
-    hipLaunchKernelGGL((grouped_gemm_bwd_kernel<WGRAD, EPI_WGRAD>),
-                       dim3((unsigned)(E * q.tiles_m * q.tiles_n)), dim3(NT), 0, s, q);
+  launch_wgrad256(q, s);
   return hipGetLastError();
 }
 
@@ -1327,7 +1311,7 @@ hipError_t launch_expert_up_backward(const void* x, const int32_t* gather_idx,
   q.w1 = dW_up;
   q.n_split = f;
   // the K split needs the 256 x 256 kernel (rows in order, no gather)
-  q.ksplit = (MOE_BWD_PP && gather_idx == nullptr) ? wgrad_chunks(E, rows, d, 2 * f, ws_bytes) : 1;
+  q.ksplit = gather_idx == nullptr ? wgrad_chunks(E, rows, d, 2 * f, ws_bytes) : 1;
   q.part = static_cast<float*>(ws);
   const bool add = accumulate != 0;
   if (add ? launch_pair256<EPI_F32_ADD>(p, q, rows, s) : launch_pair256<EPI_F32>(p, q, rows, s))
@@ -1345,7 +1329,7 @@ hipError_t launch_expert_up_backward(const void* x, const int32_t* gather_idx,
                            p);
     }
   }
-  if (MOE_BWD_PP && gather_idx == nullptr)  // the ping-pong WGRAD reads A rows in order
+  if (gather_idx == nullptr)  // the ping-pong WGRAD reads A rows in order
     launch_wgrad256(q, s);
   else
     hipLaunchKernelGGL((grouped_gemm_bwd_kernel<WGRAD, EPI_WGRAD>),

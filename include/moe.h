@@ -115,6 +115,24 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, const void* x, int
                 hipStream_t stream);
 
 /*
+ * moe_permute_noalloc -- moe_permute without a workspace argument, for
+ * callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The same
+ * arguments, results and status codes as moe_permute; its block tables live
+ * in a static device array of 1 MiB per GPU instead (held until the process
+ * ends), so it calls no allocator.  Limit: 2 * ceil(T / 256) * E int32 (each
+ * table rounded up to 256 bytes) must fit 1 MiB -- e.g. T <= 131072 at
+ * E = 256, T <= 1048576 at E = 32 -- else MOE_ERR_WORKSPACE and nothing is
+ * launched.  Every byte the kernels read from the array is written earlier in
+ * the same call.  Calls that overlap on one GPU (other streams, other host
+ * threads) share the array and race: serialise them.
+ */
+int moe_permute_noalloc(const int32_t* topk_idx, const float* topk_w, const void* x, int T, int d,
+                        int E, int k, int dtype, int32_t* counts, int32_t* offsets,
+                        int32_t* perm_token, int32_t* inv, float* perm_w, void* x_perm,
+                        hipStream_t stream);
+
+/*
  * Workspace bytes that let moe_expert_up / moe_expert_down / moe_ffn_forward
  * split the K loop of the tiles of a mostly idle last round of tiles (the
  * partial sums of the split tiles are kept there and added in a fixed

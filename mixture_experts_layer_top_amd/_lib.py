@@ -27,7 +27,7 @@ EXPORTS = (
     "moe_combine_backward", "moe_expert_down_backward", "moe_expert_up_backward",
     "moe_unpermute", "moe_topk_weights_backward", "moe_linear_backward_workspace_size",
     "moe_linear_backward", "moe_ffn_backward_workspace_size", "moe_workspace_size",
-    "moe_probe_mfma",
+    "moe_probe_mfma", "moe_permute_noalloc",
 )
 
 _lib = None
@@ -58,6 +58,8 @@ def load():
         "moe_ffn_workspace_size": (sz, [i32, i32, i32, i32]),
         "moe_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
         "moe_probe_mfma": (i32, [i32, i32, vp, vp]),
+        "moe_permute_noalloc": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                      vp]),
         "moe_expert_up": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
         "moe_expert_down": (i32, [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz,
                                   vp]),
@@ -138,6 +140,16 @@ def moe_permute(topk_idx, topk_w, x, T, d, E, k, dtype, counts, offsets, perm_to
                             _p(workspace), ws_bytes, _stream(stream))
     if check:
         _check("moe_permute", st)
+    return st
+
+
+def moe_permute_noalloc(topk_idx, topk_w, x, T, d, E, k, dtype, counts, offsets, perm_token, inv,
+                        perm_w, x_perm, stream=None, check=True):
+    st = load().moe_permute_noalloc(_p(topk_idx), _p(topk_w), _p(x), T, d, E, k, dtype, _p(counts),
+                                    _p(offsets), _p(perm_token), _p(inv), _p(perm_w), _p(x_perm),
+                                    _stream(stream))
+    if check:
+        _check("moe_permute_noalloc", st)
     return st
 
 

@@ -78,6 +78,31 @@ int moe_permute(const int32_t* topk_idx, const float* topk_w, const void* x, int
                                         stream));
 }
 
+int moe_permute_noalloc(const int32_t* topk_idx, const float* topk_w, const void* x, int T, int d,
+                        int E, int k, int dtype, int32_t* counts, int32_t* offsets,
+                        int32_t* perm_token, int32_t* inv, float* perm_w, void* x_perm,
+                        hipStream_t stream) {
+  if (T < 0 || E < 1 || E > 256 || k < 1 || k > E) return MOE_ERR_INVALID;
+  if ((long long)T * k >= (1ll << 31)) return MOE_ERR_INVALID;
+  if (!dtype_ok(dtype)) return MOE_ERR_UNSUPPORTED;
+  if (!counts || !offsets) return MOE_ERR_INVALID;
+  if (T > 0 && (!topk_idx || !perm_token || !inv)) return MOE_ERR_INVALID;
+  if (perm_w && !topk_w) return MOE_ERR_INVALID;
+  if (x_perm) {
+    if (!x) return MOE_ERR_INVALID;
+    if (!dims_ok(d)) return d <= 0 ? MOE_ERR_INVALID : MOE_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_UNSUPPORTED;
+  }
+  if (moe::permute_workspace_bytes(T, E, k) > moe::kNoAllocScratchBytes) return MOE_ERR_WORKSPACE;
+  if (!aligned16(counts) || !aligned16(offsets) || !aligned16(perm_token) || !aligned16(inv) ||
+      (perm_w && !aligned16(perm_w)))
+    return MOE_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (moe::noalloc_scratch(&ws) != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_permute(topk_idx, topk_w, x, T, d, E, k, dtype == MOE_BF16, counts,
+                                        offsets, perm_token, inv, perm_w, x_perm, ws, stream));
+}
+
 size_t moe_ffn_workspace_size(int E, int rows, int d, int f) {
   return moe::ffn_workspace_bytes(E, rows, d, f);
 }

@@ -52,6 +52,10 @@ hipError_t launch_route(const void* x, const void* W_r, const float* bias, int T
                         hipStream_t s);
 
 size_t permute_workspace_bytes(int T, int E, int k);
+// allocation-free permute: the static device scratch of this many bytes and
+// its address on the current device (looked up once per device)
+constexpr size_t kNoAllocScratchBytes = 1u << 20;
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_permute(const int32_t* idx, const float* topk_w, const void* x, int T, int d,
                           int E, int k, bool bf16, int32_t* counts, int32_t* offsets,
                           int32_t* perm_token, int32_t* inv, float* perm_w, void* x_perm,

@@ -19,6 +19,8 @@
 // rank block does the scan itself (its own column prefixes, and the
 // totals): two launches, hist and scan+rank.  Otherwise hist also adds into
 // the global counts (integer adds commute) and one workgroup scans.
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -262,6 +264,33 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const u32x4* __restric
 }
 
 }  // namespace
+
+// Static scratch of the allocation-free permute: each device holds its own
+// copy of this array (until the process ends).  Host code never uses its
+// name as an address: the device address comes from hipGetSymbolAddress,
+// once per device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};  // per device
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t permute_workspace_bytes(int T, int E, int k) {
   (void)k;

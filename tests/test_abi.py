@@ -240,3 +240,24 @@ def test_probe_validation(lib):
     assert L.moe_probe_mfma(4, 0, A, stream=0, check=False) == L.MOE_ERR_INVALID
     assert L.moe_probe_mfma(4, 10, None, stream=0, check=False) == L.MOE_ERR_INVALID
     assert L.moe_probe_mfma(4, 10, MIS, stream=0, check=False) == L.MOE_ERR_UNSUPPORTED
+
+
+def permute_noalloc(**kw):
+    args = dict(topk_idx=A, topk_w=A, x=None, T=64, d=64, E=8, k=2, dtype=1, counts=A,
+                offsets=A, perm_token=A, inv=A, perm_w=A, x_perm=None)
+    args.update(kw)
+    return L.moe_permute_noalloc(**args, stream=0, check=False)
+
+
+def test_permute_noalloc_validation(lib):
+    # the static scratch holds 1 MiB: 2 * ceil(T / 256) * E int32 tables
+    assert permute_noalloc(T=131073, E=256, k=8) == L.MOE_ERR_WORKSPACE
+    assert L.moe_permute_workspace_size(131072, 256, 8) <= 1 << 20
+    assert L.moe_permute_workspace_size(131073, 256, 8) > 1 << 20
+    assert permute_noalloc(k=9) == L.MOE_ERR_INVALID
+    assert permute_noalloc(counts=None) == L.MOE_ERR_INVALID
+    assert permute_noalloc(topk_w=None) == L.MOE_ERR_INVALID
+    assert permute_noalloc(x_perm=A) == L.MOE_ERR_INVALID
+    assert permute_noalloc(x_perm=A, x=A, d=12) == L.MOE_ERR_UNSUPPORTED
+    assert permute_noalloc(perm_token=MIS) == L.MOE_ERR_UNSUPPORTED
+    assert permute_noalloc(dtype=5) == L.MOE_ERR_UNSUPPORTED

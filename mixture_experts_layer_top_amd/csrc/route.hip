@@ -4,21 +4,26 @@
 // Top-k expert choice per token: DisagMoE technical summary, "2.2 AF-Pipe".
 //
 // bf16 path.  The logits L = x W_r are a skinny contraction (E <= 256
-// columns), bound by reading x from HBM once:
-//   * a workgroup of NWV wave64s takes 16 MB tokens; the waves split K into
-//     NWV ranges, and each wave walks its range in chunks of 32 ST;
-//   * x rows (the A operand: 16 contiguous K-bytes per lane) go straight
-//     from memory into registers; the next chunk's loads are issued before
-//     this chunk's MFMAs, so a wave always has one chunk in flight;
-//   * W_r is read in the caller's [d, E] layout: the chunk's rows are one
-//     contiguous block, which each wave loads (16 bytes per lane), writes to
-//     its own LDS tile, and reads back with the gfx950 LDS transpose read
-//     (8 consecutive K values of one expert per lane, the B operand of
-//     v_mfma_f32_16x16x32_bf16); lanes whose columns lie past E read a zero
-//     patch, so E need not be a multiple of 16 (it must be a multiple of 8;
-//     other E gather their B operand straight from memory);
-//   * bf16 products are exact in fp32; sums are fp32; the NWV partial
-//     logits are added in wave order (deterministic), then the bias.
+// columns), bound by reading x from HBM once.  W_r is read in the caller's
+// [d, E] layout: a K chunk of its rows is one contiguous block, moved to LDS
+// with direct-to-LDS loads and read back with the gfx950 LDS transpose read
+// (8 consecutive K values of one expert per lane, the B operand of
+// v_mfma_f32_16x16x32_bf16); lanes whose columns lie past E read a zero
+// patch, so E must only be a multiple of 8 (other E gather their B operand
+// from memory one element at a time: small gates, E = 1 in one load).
+// bf16 products are exact in fp32; sums are fp32 in a fixed order.
+//
+//   route_bf16_kernel: a workgroup of NWV wave64s takes 16 MB tokens and
+//     the waves split K into NWV ranges.  Each wave walks its range in
+//     chunks of 32 ST K values: the chunk's W_r rows go to the wave's own
+//     LDS tile, then all its x fragments (16 token rows x 16 contiguous
+//     bytes per lane) are loaded into registers before its first MFMA; the
+//     partial logits of the waves are added in wave order, then the bias.
+//   route_bf16_sw_kernel (long batches, E <= 16): the waves split tokens
+//     instead, so each W_r chunk is loaded once per workgroup; x tiles and
+//     W_r chunks stream through an LDS ring with one barrier per stage, and
+//     each wave holds its tokens' complete logits.
+//   Both walk their K chunks in an order rotated by the workgroup index.
 //
 // Selection and weights: 16 lanes per token, each holding every 16th
 // logit.  The j-th pick is the best (value desc, index asc) strictly below
@@ -245,7 +250,11 @@ __global__ __launch_bounds__(NWV * 64) void route_bf16_kernel(RouteArgs a) {
   const long long wlast = (long long)d * E * 2 - 16;  // last 16 bytes of W_r
   const bf16x8 zero8 = {};
   if (WTR) __syncthreads();  // the zero patch is written
-  for (int c = 0; c < nch; ++c) {
+  // chunk order rotated per workgroup (as in the shared-W_r kernel below):
+  // concurrent workgroups then read different offsets of their rows
+  const int rot = nch > 0 ? (int)(blockIdx.x % (unsigned)nch) : 0;
+  for (int c0 = 0; c0 < nch; ++c0) {
+    const int c = c0 + rot < nch ? c0 + rot : c0 + rot - nch;
     const int k0 = kb + c * KC;
     if (WTR) {
       // the wave's earlier transpose reads of its tile have completed
@@ -392,6 +401,181 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(RouteArgs a) {
   select_and_weigh<NV>(ll, ls, a, t_base, kTok);
 }
 
+// ------------------------------------------------------------------------
+// Long token batches: a workgroup of NWV waves takes 16 NWV tokens (16 per
+// wave, each wave the full K), so every K chunk of W_r is loaded once per
+// workgroup and shared by all its waves.  Both operands move HBM -> LDS
+// with direct-to-LDS loads through a ring of RING stages of KC K values:
+// the x tile [16 NWV rows][KC] (one 1 KiB load covers whole 128-byte lines
+// of 1024 / (2 KC) token rows, the 16-byte chunk index XOR-ed with (row / 2)
+// mod 8 as in the grouped GEMM's A layout), and the W_r rows of the chunk
+// [KC][E] as one contiguous block.  Loads are dealt round-robin over the
+// waves (a wave re-issues a load already in its list, same bytes to the same
+// place, when the count does not divide evenly), each wave waits for its own
+// loads of a stage, and a barrier makes the stage visible: one barrier per
+// stage.  Each wave then holds its tokens' complete logits: no reduction
+// across waves.  Requires d % KC == 0 and E % 8 == 0.
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 63] (larger n waits for 63)
+__device__ __forceinline__ void wait_vmcnt_rt(int n) {
+  switch (n) {
+#define MOE_W4(b) case b: wait_vmcnt_route<b>(); break; case b + 1: wait_vmcnt_route<b + 1>(); break; \
+                  case b + 2: wait_vmcnt_route<b + 2>(); break; case b + 3: wait_vmcnt_route<b + 3>(); break;
+    MOE_W4(0) MOE_W4(4) MOE_W4(8) MOE_W4(12) MOE_W4(16) MOE_W4(20) MOE_W4(24) MOE_W4(28)
+    MOE_W4(32) MOE_W4(36) MOE_W4(40) MOE_W4(44) MOE_W4(48) MOE_W4(52) MOE_W4(56) MOE_W4(60)
+#undef MOE_W4
+    default: wait_vmcnt_route<63>(); break;
+  }
+}
+
+template <int NB, int NWV, int KC, int RING>
+struct SwCfg {
+  static constexpr int Ep = NB * 16, TB = 16 * NWV;
+  static constexpr int X_BYTES = TB * KC * 2;
+  static constexpr int W_BYTES = KC * Ep * 2;         // E <= Ep
+  static constexpr int STAGE = X_BYTES + W_BYTES;
+  static constexpr int ZERO = RING * STAGE;           // 16-byte zero patch
+  static constexpr int LDS_RING = ZERO + 16;
+  static constexpr int L_BYTES = TB * (Ep + 1) * 4;
+  static constexpr int LDS = LDS_RING > L_BYTES ? LDS_RING : L_BYTES;
+  static constexpr int XL = X_BYTES / 1024;           // x loads per stage
+  static constexpr int CPR = KC / 8;                  // 16-byte chunks per x row
+  static constexpr int RPL = 1024 / (KC * 2);         // x rows per load
+  static_assert(KC == 64 || KC == 128 || KC == 256 || KC == 512, "chunk");
+  static_assert(X_BYTES % 1024 == 0, "x loads");
+};
+
+template <int NB, int NWV, int KC, int RING>
+__global__ __launch_bounds__(NWV * 64) void route_bf16_sw_kernel(RouteArgs a) {
+  using C = SwCfg<NB, NWV, KC, RING>;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  constexpr int Ep = C::Ep, TB = C::TB, KS = KC / 32;
+  constexpr int ls = Ep + 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t_base = blockIdx.x * TB;
+  const int d = a.d, E = a.E;
+  const int ns = d / KC;                               // stages
+  const int wl = (KC * E * 2 + 1023) / 1024;           // W_r loads per stage
+  const int nl = C::XL + wl;                           // loads per stage
+  const int lpw = (nl + NWV - 1) / NWV;                // loads per wave per stage
+  const char* X = static_cast<const char*>(a.x);
+  const char* W = static_cast<const char*>(a.W);
+  const long long w_last = (long long)d * E * 2 - 16;  // last 16 bytes of W_r
+  const uint32_t lds0 = lds_addr_of(smem);
+  if (tid < 4) reinterpret_cast<uint32_t*>(smem + C::ZERO)[tid] = 0u;
+
+  // load j of a stage (j < nl): x load j < XL fills x rows RPL j .. + RPL - 1
+  // of the tile; W_r load j - XL fills bytes 1024 (j - XL) .. of the chunk.
+  // This lane's global byte offset at stage 0 and LDS byte offset in a stage.
+  // stage st covers K chunk (st + rot) mod ns: workgroups start at
+  // different chunks, so the rows they read at one moment (d * 2 bytes
+  // apart) do not all sit at the same offset in their rows, which measured
+  // as a strong slowdown of the whole stream (same-offset requests of every
+  // compute unit collide in the memory channels)
+  const int rot = (int)(blockIdx.x % (unsigned)ns);
+  auto issue_stage = [&](int st) {
+    const uint32_t slot = lds0 + (uint32_t)((st % RING) * C::STAGE);
+    int kc = st + rot;
+    if (kc >= ns) kc -= ns;
+    for (int i = 0; i < lpw; ++i) {
+      int j = wave + i * NWV;
+      if (j >= nl) j = j % nl;  // a repeat: same bytes to the same place
+      if (j < C::XL) {
+        const int row = j * C::RPL + lane / C::CPR;
+        const int chunk = (lane % C::CPR) ^ ((row >> 1) & (C::CPR - 1));
+        int t = t_base + row;
+        if (t >= a.T) t = 0;  // rows past T read token 0; their logits are never stored
+        const long long off = ((long long)t * d + (long long)kc * KC + chunk * 8) * 2;
+        dma16(X + off, slot + (uint32_t)(j * 1024));
+      } else {
+        long long off = (long long)kc * KC * E * 2 + (long long)(j - C::XL) * 1024 + lane * 16;
+        if (off > w_last) off = w_last;  // past the chunk (last load of a small E): unused bytes
+        dma16(W + off, slot + (uint32_t)(C::X_BYTES + (j - C::XL) * 1024));
+      }
+    }
+  };
+
+  // fragment read offsets inside a stage: A = this wave's 16 token rows,
+  // K step ks chunk 4 ks + lane / 16 (swizzled); B = W_r rows kr .. kr + 3
+  // and + 4, column 16 nb + 4 (lane % 4) (lanes past E read the zero patch)
+  const int l15 = lane & 15;
+  const int arow = wave * 16 + l15;
+  int a_rd[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    a_rd[ks] = arow * KC * 2 + (((ks * 4 + (lane >> 4)) ^ ((arow >> 1) & (C::CPR - 1))) << 4);
+  const int kr = (lane >> 4) * 8 + (l15 >> 2), cq = (lane & 3) * 4;
+  uint32_t b_rd[NB];
+  bool b_in[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    b_in[nb] = nb * 16 + cq < E;
+    b_rd[nb] = (uint32_t)(C::X_BYTES + (kr * E + nb * 16 + cq) * 2);
+  }
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  __syncthreads();  // the zero patch is written
+  for (int st = 0; st < RING - 1 && st < ns; ++st) issue_stage(st);
+  for (int st = 0; st < ns; ++st) {
+    // this wave's loads of stage st have landed once at most those of the
+    // later stages already issued are outstanding
+    wait_vmcnt_rt(lpw * min(RING - 2, ns - 1 - st));
+    // every wave's part of stage st is visible, and every wave is done
+    // reading stage st - 1 (its reads drained before the barrier)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (st + RING - 1 < ns) issue_stage(st + RING - 1);  // into the slot of stage st - 1
+    const char* sl = smem + (st % RING) * C::STAGE;
+    const uint32_t zrel = (uint32_t)(C::ZERO - (st % RING) * C::STAGE);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(sl + a_rd[ks]);
+      const uint32_t kb_off = (uint32_t)(ks * 32 * E * 2);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint32_t lo = b_in[nb] ? b_rd[nb] + kb_off : zrel;
+        const uint32_t hi = b_in[nb] ? b_rd[nb] + kb_off + (uint32_t)(4 * E * 2) : zrel;
+        const bf16x4 blo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(sl + lo));
+        const bf16x4 bhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(sl + hi));
+        const bf16x8 bv = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[nb], 0, 0, 0);
+      }
+    }
+  }
+  wait_vmcnt_route<0>();
+  __syncthreads();  // every wave is done with the ring
+  // logits of this wave's 16 tokens, plus the bias (column lane % 16, rows
+  // 4 (lane / 16) + i of each accumulator block)
+  float* ll = reinterpret_cast<float*>(smem);  // [TB][ls]
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tt = wave * 16 + (lane >> 4) * 4 + i;
+      const int e = nb * 16 + l15;
+      ll[tt * ls + e] = acc[nb][i] + ((a.bias && e < E) ? a.bias[e] : 0.f);
+    }
+  __syncthreads();
+  write_logits(ll, ls, a, t_base, TB);
+  select_and_weigh<NB>(ll, ls, a, t_base, TB);
+}
+
+template <int NB, int NWV, int KC, int RING>
+hipError_t launch_sw(const RouteArgs& a, hipStream_t s) {
+  using C = SwCfg<NB, NWV, KC, RING>;
+  static_assert(C::LDS <= 160 * 1024, "LDS");
+  auto kern = route_bf16_sw_kernel<NB, NWV, KC, RING>;
+  if (C::LDS > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(cdiv(a.T, C::TB)), dim3(NWV * 64), C::LDS, s, a);
+  return hipGetLastError();
+}
+
 template <int NB, int MB, int NWV, bool WTR>
 hipError_t launch_cfg(const RouteArgs& a, hipStream_t s) {
   // K-steps per chunk: a chunk's x loads (16 KiB a wave at most, 64
@@ -423,6 +607,12 @@ hipError_t launch_nb(const RouteArgs& a, hipStream_t s) {
   // register file) keep the 16 accumulator blocks and two chunks in registers
   constexpr int NWS = NB >= 8 ? 4 : 8;
   if (a.E % 8 != 0) return launch_cfg<NB, 1, NWS, false>(a, s);
+  // long batches with at most 16 experts: the shared-W_r kernel, once it
+  // has a workgroup per compute unit (same box, 134 MB of x: 52 -> 49 us at
+  // 8 experts; at 64 experts it measured 66 us against this kernel's 64)
+  if constexpr (NB == 1) {
+    if (a.d % 256 == 0 && cdiv(a.T, 64) >= device_cu_count()) return launch_sw<1, 4, 256, 3>(a, s);
+  }
   if constexpr (NB <= 4) {
     if (a.T >= 256 * 64) return launch_cfg<NB, 4, 4, true>(a, s);
     if (a.T >= 256 * 32) return launch_cfg<NB, 2, 4, true>(a, s);

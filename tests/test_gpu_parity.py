@@ -430,6 +430,22 @@ def test_combine_more_than_eight_slots(L, path):
     check_y(cfg, m.y.cpu().double().numpy(), O.forward(h, cfg.k, cfg.renorm, idx=idx_g)["y"], path)
 
 
+@pytest.mark.parametrize("E,k,T,d", [(8, 2, 16400, 256), (16, 4, 16390, 512), (24, 3, 32770, 128),
+                                     (40, 5, 32768, 192), (64, 6, 33000, 64)])
+def test_route_long_batches(L, E, k, T, d):
+    """Batches long enough for the router's shared-W_r kernel (a workgroup
+    of 16 tokens per wave on every compute unit): routing exact on the
+    GPU's logits and within the fp32 bound of the fp64 logits, dispatch
+    bit-exact; ragged last workgroups (T not a multiple of its tokens)."""
+    cfg = small_cfg(E=E, k=k, T=T, d=d, f=64)
+    log(f"[edge] long-batch route T={T} d={d} E={E} k={k}")
+    layer = make_layer(cfg, seed=30 + E, device="cuda")
+    m = run_layer(cfg, layer, "fast")
+    h = host_layer(layer)
+    idx_g, w_g, _ = check_routing(cfg, m, h)
+    check_dispatch(cfg, m, idx_g, w_g)
+
+
 def test_nan_token_gets_valid_distinct_experts(L):
     """A token whose x row holds a NaN has NaN logits for every expert; the
     selection must still give k distinct experts in [0, E), so the dispatch

@@ -171,9 +171,12 @@ def measured_peaks(copy_bytes=1 << 30, probe_iters=20000):
 
 
 def gemm_kernel_name(cfg, up):
-    """The bf16 grouped-GEMM kernel the library launches for this layer: the
-    ping-pong kernel (main pass) when K is a multiple of its 64-deep stages
-    and the A operand is below 4 GiB, else the general kernel."""
+    """The grouped-GEMM kernel the library launches for this layer: for bf16
+    the ping-pong kernel (main pass) when K is a multiple of its 64-deep
+    stages and the A operand is below 4 GiB, else the general kernel; for
+    fp32 the plain FMA kernels."""
+    if cfg.dtype != "bf16":
+        return "up_f32_kernel" if up else "down_f32_kernel"
     K = cfg.d if up else cfg.f
     a_bytes = cfg.T * cfg.k * K * 2
     u = "true" if up else "false"
@@ -471,9 +474,12 @@ def main():
                for st in ("route", "permute", "combine")},
         },
         "roofline": {
-            "kernel": gemm_kernel_name(cfg, up=True) + " (layer 0 + SwiGLU; main pass and "
-                      "tail-split fixup, the launches the expert_up events bracket)",
-            "bound": "mfma",
+            "kernel": gemm_kernel_name(cfg, up=True) + (
+                " (layer 0 + SwiGLU; main pass and tail-split fixup, the launches the expert_up "
+                "events bracket)" if cfg.dtype == "bf16" else
+                " (layer 0 + SwiGLU, one fp32 FMA chain per output; the small fp32 layer is not "
+                "sized to fill the chip)"),
+            "bound": "mfma" if cfg.dtype == "bf16" else "alu",
             "achieved": round(g0, 2),
             "peak": peak,
             "unit": "TFLOP/s",

@@ -28,7 +28,7 @@
 // Selection and weights: 16 lanes per token, each holding every 16th
 // logit.  The j-th pick is the best (value desc, index asc) strictly below
 // the (j-1)-th pick in that order, so no pick is ever marked; exactly equal
-// logits go to the lower index.  A NaN logit ranks below -inf, so every
+// logits go to the lower index.  A NaN logit is taken as -inf, so every
 // token gets k distinct experts in [0, E) whatever its logits.
 #include "moe_internal.h"
 

@@ -126,6 +126,30 @@ def protocol_times(m, steps, flush_bytes):
     return per, step
 
 
+def flushed_read_ms(nbytes, reps=5, flush_bytes=1 << 30):
+    """Median HIP-event time of a pure streaming read (moe_probe_read) of
+    `nbytes` bytes, each rep after a write of `flush_bytes` bytes that evicts
+    the last-level cache (outside the events)."""
+    import torch
+    from mixture_experts_layer_top_amd import _lib
+    nbytes = (nbytes + 15) // 16 * 16
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda:0")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    _lib.moe_probe_read(src, nbytes, sink)  # warm-up
+    times = []
+    for r in range(reps):
+        flush.fill_(r & 0xFF)
+        a.record()
+        _lib.moe_probe_read(src, nbytes, sink)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del src, flush
+    return sorted(times)[reps // 2]
+
+
 def measured_peaks(copy_bytes=1 << 30, probe_iters=20000):
     """Peaks measured on this machine: the bf16 MFMA rate and shader clock of an
     all-compute-unit MFMA-only loop (two 4-wave blocks per compute unit),
@@ -167,6 +191,9 @@ def measured_peaks(copy_bytes=1 << 30, probe_iters=20000):
                       f"{ms:.2f} ms",
         "hbm_copy_GBs": round(2 * copy_bytes / (cms * 1e-3) / 1e9, 1),
         "copy": f"device copy of {copy_bytes >> 20} MiB, median of 5",
+        "hbm_read_GBs": round(copy_bytes / (flushed_read_ms(copy_bytes) * 1e-3) / 1e9, 1),
+        "read": f"streaming read (moe_probe_read) of {copy_bytes >> 20} MiB after a 1 GiB "
+                "flush, median of 5",
     }
 
 
@@ -493,6 +520,7 @@ def main():
         # memory-bound stages' HBM rates (fraction of 8 TB/s) at the medians
         per, step = protocol_times(m, args.protocol_steps, 1 << 30)
         med = {st: pct(v, 50) for st, v in per.items()}
+        rd = {st: flushed_read_ms(by[st]) for st in ("route", "permute", "combine")}
         out["protocol"] = {
             "what": f"{args.protocol_steps} steps, each after a 1 GiB device write outside the "
                     "events (last-level cache flushed); HIP events on the launch stream",
@@ -505,7 +533,12 @@ def main():
             "hbm_stages": {st: {"bytes": by[st],
                                 "GBs": round(by[st] / (med[st] * 1e-3) / 1e9, 1),
                                 "frac_of_8TBs": round(by[st] / (med[st] * 1e-3) / 1e9 /
-                                                      PEAK_HBM_GBS, 3)}
+                                                      PEAK_HBM_GBS, 3),
+                                # a pure streaming read of the same byte count,
+                                # also after a flush: what ramp-up and launch
+                                # leave of the bandwidth at this size
+                                "pure_read_GBs": round(by[st] / (rd[st] * 1e-3) / 1e9, 1),
+                                "frac_of_pure_read": round(rd[st] / med[st], 3)}
                            for st in ("route", "permute", "combine")},
             "expert_up_TFLOPs_at_median": round(g0_flops / (med["expert_up"] * 1e-3) / 1e12, 1),
             "expert_down_TFLOPs_at_median": round(g1_flops / (med["expert_down"] * 1e-3) / 1e12,

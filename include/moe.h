@@ -363,9 +363,10 @@ int moe_linear_backward(const void* x, const void* W, const float* G, int T, int
 /* ------------------------------------------------------------------------
  * Measurement.  Kernel rates are reported as fractions of the chip's peaks
  * (the pages compare layer times across token lengths and expert loads:
- * COMET page, "COMET's Performance"); this call measures the bf16 matrix
+ * COMET page, "COMET's Performance"); these calls measure the bf16 matrix
  * peak the chip sustains, and its shader clock, under an all-compute-unit
- * load, to set beside the datasheet figure.
+ * load, and the rate of a pure streaming read of a given size, to set
+ * beside the datasheet figures.
  * ------------------------------------------------------------------------ */
 
 /*
@@ -378,6 +379,18 @@ int moe_linear_backward(const void* x, const void* W, const float* G, int T, int
  * MOE_ERR_INVALID for blocks outside [1, 2^20], iters < 1 or a NULL ticks.
  */
 int moe_probe_mfma(int blocks, int iters, uint64_t* ticks, hipStream_t stream);
+
+/*
+ * moe_probe_read -- reads `bytes` bytes of device memory at src once, in
+ * 16-byte non-temporal loads at a grid stride (at most 2048 workgroups of
+ * 256 threads, four loads in flight per thread), and writes nothing but, in practice
+ * never, one word at sink.  Time it with events on the stream: bytes / time
+ * is the rate a pure streaming read reaches at that size, the reference for
+ * a memory-bound stage of the same byte count.  src and sink device, 16-byte
+ * aligned; bytes a multiple of 16 (MOE_ERR_UNSUPPORTED otherwise); bytes = 0
+ * is a no-op; MOE_ERR_INVALID for a NULL src or sink.
+ */
+int moe_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ EXPORTS = (
     "moe_combine_backward", "moe_expert_down_backward", "moe_expert_up_backward",
     "moe_unpermute", "moe_topk_weights_backward", "moe_linear_backward_workspace_size",
     "moe_linear_backward", "moe_ffn_backward_workspace_size", "moe_workspace_size",
-    "moe_probe_mfma", "moe_permute_noalloc",
+    "moe_probe_mfma", "moe_permute_noalloc", "moe_probe_read",
 )
 
 _lib = None
@@ -58,6 +58,7 @@ def load():
         "moe_ffn_workspace_size": (sz, [i32, i32, i32, i32]),
         "moe_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
         "moe_probe_mfma": (i32, [i32, i32, vp, vp]),
+        "moe_probe_read": (i32, [vp, sz, vp, vp]),
         "moe_permute_noalloc": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                       vp]),
         "moe_expert_up": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
@@ -285,4 +286,11 @@ def moe_probe_mfma(blocks, iters, ticks, stream=None, check=True):
     st = load().moe_probe_mfma(blocks, iters, _p(ticks), _stream(stream))
     if check:
         _check("moe_probe_mfma", st)
+    return st
+
+
+def moe_probe_read(src, nbytes, sink, stream=None, check=True):
+    st = load().moe_probe_read(_p(src), nbytes, _p(sink), _stream(stream))
+    if check:
+        _check("moe_probe_read", st)
     return st

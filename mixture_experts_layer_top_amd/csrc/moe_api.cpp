@@ -357,4 +357,11 @@ int moe_probe_mfma(int blocks, int iters, uint64_t* ticks, hipStream_t stream) {
   return hip_status(moe::launch_probe_mfma(blocks, iters, ticks, stream));
 }
 
+int moe_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (bytes == 0) return MOE_OK;
+  if (!src || !sink) return MOE_ERR_INVALID;
+  if (bytes % 16 != 0 || !aligned16(src) || !aligned16(sink)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_probe_read(src, bytes, sink, stream));
+}
+
 }  // extern "C"

@@ -76,6 +76,7 @@ hipError_t launch_combine(const float* y_perm, const int32_t* inv, const float* 
                           bool accumulate, float* y, hipStream_t s);
 
 hipError_t launch_probe_mfma(int blocks, int iters, uint64_t* ticks, hipStream_t s);
+hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 
 // backward
 hipError_t launch_combine_backward(const float* dy, const float* y_perm, const int32_t* inv,

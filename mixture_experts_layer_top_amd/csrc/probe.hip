@@ -1,5 +1,7 @@
 // Measured peaks: an MFMA-only loop that reports the bf16 matrix-core rate
-// and the shader clock the chip holds while every compute unit runs it.
+// and the shader clock the chip holds while every compute unit runs it, and
+// a streaming read of a buffer of any size (the rate a pure read reaches at
+// the byte count of a memory-bound stage).
 //
 // The pages compare systems by layer time across token lengths and loads
 // (COMET page, "COMET's Performance"); the fraction of the chip's peak that
@@ -12,6 +14,8 @@
 // every block records the shader-clock counter (s_memtime) and the 100 MHz
 // real-time counter (s_memrealtime) around its loop, so their ratio is the
 // shader clock under this load.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -51,7 +55,44 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, uint64_t* __r
   }
 }
 
+// Streaming read: every thread loads 16-byte words at a grid stride, four
+// in flight, non-temporal (the faster form on a cache holding dirty lines),
+// and folds them with XOR; sink is written only if the fold
+// equals a value no realistic buffer produces (so the loads are kept and
+// nothing else is written).
+constexpr int kReadThreads = 256, kReadUnroll = 4;
+
+__global__ __launch_bounds__(kReadThreads) void read_stream_kernel(const u32x4* __restrict__ src,
+                                                                   size_t n16,
+                                                                   uint32_t* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * kReadThreads;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (size_t i = (size_t)blockIdx.x * kReadThreads + threadIdx.x; i < n16;
+       i += stride * kReadUnroll) {
+    u32x4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) {
+      const size_t j = i + u * stride;
+      v[u] = j < n16 ? __builtin_nontemporal_load(src + j) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u];
+  }
+  const uint32_t f = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  if (f == 0x9e3779b9u) sink[0] = f;
+}
+
 }  // namespace
+
+hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const size_t per_block = (size_t)kReadThreads * kReadUnroll;
+  const int blocks = (int)std::min<size_t>((n16 + per_block - 1) / per_block, 8 * 256);
+  hipLaunchKernelGGL(read_stream_kernel, dim3(blocks), dim3(kReadThreads), 0, s,
+                     static_cast<const u32x4*>(src), n16, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_probe_mfma(int blocks, int iters, uint64_t* ticks, hipStream_t s) {
   hipLaunchKernelGGL(mfma_peak_kernel, dim3(blocks), dim3(256), 0, s, iters, ticks);

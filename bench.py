@@ -284,8 +284,9 @@ def cpu_baseline(cfg, layer, target_s):
 
 def time_layer(cfg, args):
     """Draw the layer on the GPU, run the warmup steps, then time exactly
-    args.steps steps (host sync on both sides), with HIP events recorded on
-    the launch stream between stages.  Returns the layer, the MoeLayer, the
+    args.steps steps (host sync on both sides; one event pair around them on
+    the launch stream), then run args.steps more with HIP events between
+    stages for the per-stage times.  Returns the layer, the MoeLayer, the
     wall-clock ms per step, the event ms per step and the per-stage ms."""
     import torch
     from mixture_experts_layer_top_amd.inputs import make_layer
@@ -300,11 +301,25 @@ def time_layer(cfg, args):
         m.forward()
     torch.cuda.synchronize()
 
+    # the timed steps: nothing but the layer between the two syncs (one
+    # event pair around all of them gives the GPU-side time per step)
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e_start.record(stream)
+    for s in range(args.steps):
+        m.forward()
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = e_start.elapsed_time(e_end) / args.steps
+
+    # per-stage times from as many further steps, with an event on the
+    # stream after every stage (each event record costs a few microseconds
+    # of GPU time, so these steps are not the timed ones)
     stages = MoeLayer.STAGES
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for s in range(args.steps):
         ev[s][0].record(stream)
         pos = [1]
@@ -315,9 +330,6 @@ def time_layer(cfg, args):
 
         m.forward(marks=mark)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    step_ms = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps)) / args.steps
     stage_ms = {}
     for i, name in enumerate(stages):
         stage_ms[name] = sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps

@@ -56,14 +56,60 @@ struct RouteArgs {
   float* logits_out;
 };
 
-// Softmax top-k over `ntok` logits rows in LDS: 16 lanes per token, each
-// holding NV = Ep / 16 of the row's logits in registers (expert q + 16 u for
-// lane q; padded experts hold -inf).  Waves take groups of 4 tokens in turn.
-// The j-th pick is the best (value desc, index asc) strictly below the
-// (j-1)-th pick in that order, found by a per-lane scan and a 16-lane
-// reduction.  NaN logits are taken as -inf for the order and the weights.
-// With renormalisation the unnormalised weights are written first and
-// divided by their sum afterwards (by the same lane).
+// Reductions over one DPP row (16 lanes): xor 1 and xor 2 inside each quad,
+// then the half-row mirror (lane i <-> 7 - i in each 8-lane half) pairs the
+// two quads of a half and the row mirror (i <-> 15 - i) the two halves.
+// Every step combines two lanes' values with a commutative operation, so all
+// 16 lanes end with the bitwise-same result.  DPP moves run on the vector
+// ALU; the shuffles they replace went through the LDS permute unit.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, x)));
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<kDppXor1>(x));
+  x = fmaxf(x, dpp_f<kDppXor2>(x));
+  x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+  return fmaxf(x, dpp_f<kDppMirror>(x));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<kDppXor1>(x);
+  x += dpp_f<kDppXor2>(x);
+  x += dpp_f<kDppHalfMirror>(x);
+  return x + dpp_f<kDppMirror>(x);
+}
+// the best (value desc, index asc) of the row's (value, index) pairs
+template <int CTRL>
+__device__ __forceinline__ void best_step(float& bv, int& be) {
+  const float ov = dpp_f<CTRL>(bv);
+  const int oe = dpp_i<CTRL>(be);
+  if (ov > bv || (ov == bv && oe < be)) {
+    bv = ov;
+    be = oe;
+  }
+}
+__device__ __forceinline__ void row16_best(float& bv, int& be) {
+  best_step<kDppXor1>(bv, be);
+  best_step<kDppXor2>(bv, be);
+  best_step<kDppHalfMirror>(bv, be);
+  best_step<kDppMirror>(bv, be);
+}
+
+// Softmax top-k over `ntok` logits rows in LDS: 16 lanes (one DPP row) per
+// token, each holding NV = Ep / 16 of the row's logits in registers (expert
+// q + 16 u for lane q; padded experts hold -inf).  Waves take groups of 4
+// tokens in turn.  The j-th pick is the best (value desc, index asc)
+// strictly below the (j-1)-th pick in that order, found by a per-lane scan
+// and a row reduction.  NaN logits are taken as -inf for the order and the
+// weights.  For k <= 16, lane j keeps pick j and the k picks are written
+// together at the end (divided by their sum with renormalisation); larger k
+// writes each pick as it is found and divides afterwards.
 template <int NV>
 __device__ __forceinline__ void select_and_weigh(const float* ll, int lstride, const RouteArgs& a,
                                                  int t_base, int ntok) {
@@ -74,8 +120,8 @@ __device__ __forceinline__ void select_and_weigh(const float* ll, int lstride, c
   for (int g0 = (threadIdx.x >> 6) * 4; g0 < ntok; g0 += nwaves * 4) {
     const int tt = g0 + (lane >> 4);
     const int t = t_base + tt;
-    const bool live = tt < ntok;
-    const float* row = ll + (live ? tt : 0) * lstride;
+    const bool live = tt < ntok && t < a.T;
+    const float* row = ll + (tt < ntok ? tt : 0) * lstride;
     float v[NV];
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
@@ -87,16 +133,16 @@ __device__ __forceinline__ void select_and_weigh(const float* ll, int lstride, c
     float m = -INFINITY;
 #pragma unroll
     for (int u = 0; u < NV; ++u) m = fmaxf(m, v[u]);
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+    m = row16_max(m);
     float sum = 0.f;
 #pragma unroll
     for (int u = 0; u < NV; ++u) sum += (q + 16 * u < E) ? __expf(v[u] - m) : 0.f;
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off);
+    sum = row16_sum(sum);
 
     float pv = INFINITY, sel = 0.f;
     int pe = -1;
+    int my_e = 0;
+    float my_ex = 0.f;
     for (int j = 0; j < k; ++j) {
       float bv = -INFINITY;
       int be = 0x7fffffff;
@@ -110,25 +156,27 @@ __device__ __forceinline__ void select_and_weigh(const float* ll, int lstride, c
           be = e;
         }
       }
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oe = __shfl_xor(be, off);
-        if (ov > bv || (ov == bv && oe < be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
+      row16_best(bv, be);
       pv = bv;
       pe = be;
       const float ex = __expf(bv - m);
       sel += ex;
-      if (q == 0 && live && t < a.T) {
+      if (k <= 16) {
+        if (q == j) {
+          my_e = be;
+          my_ex = ex;
+        }
+      } else if (q == 0 && live) {
         a.idx[(size_t)t * k + j] = be;
         a.w[(size_t)t * k + j] = a.renorm ? ex : ex / sum;
       }
     }
-    if (a.renorm && q == 0 && live && t < a.T) {
+    if (k <= 16) {
+      if (q < k && live) {
+        a.idx[(size_t)t * k + q] = my_e;
+        a.w[(size_t)t * k + q] = a.renorm ? my_ex / sel : my_ex / sum;
+      }
+    } else if (a.renorm && q == 0 && live) {
       for (int j = 0; j < k; ++j) a.w[(size_t)t * k + j] = a.w[(size_t)t * k + j] / sel;
     }
   }

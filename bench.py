@@ -36,8 +36,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral")
-    ap.add_argument("--path", default="fast", choices=["fast", "atomic", "reference"],
-                    help="fast: gather fused into layer 0, separate deterministic combine; "
+    ap.add_argument("--path", default="fast", choices=["fast", "fast32", "atomic", "reference"],
+                    help="fast: gather fused into layer 0, separate deterministic combine over "
+                         "compact rows (fp16 + a power-of-two factor per 32 columns); "
+                         "fast32: the same over fp32 rows; "
                          "atomic: combine fused into layer 1 with atomic adds; "
                          "reference: permuted copy of x and separate combine")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -72,19 +74,21 @@ def copy_calibration(nbytes):
     print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 3}), flush=True)
 
 
-def stage_bytes(cfg):
+def stage_bytes(cfg, compact=False):
     """Algorithmic HBM bytes of the memory-bound stages of the fused path:
     route = x once, W_r once, the top-k indices and weights out; permute =
     the indices and weights in, perm_token, inv and perm_w out (the gather
-    is fused into layer 0); combine = the k fp32 expert rows of every token
-    in, y out, the indices and weights in, plus the shared-expert output
+    is fused into layer 0); combine = the k expert rows of every token in
+    (fp32, or compact: fp16 plus one fp32 factor per 32 columns), y out, the
+    indices and weights in, plus the shared-expert output in the same form
     (and its gate logit) when the layer has shared experts."""
     s = 2 if cfg.dtype == "bf16" else 4
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
     R = T * k
-    comb = R * d * 4 + T * d * 4 + T * k * 8
+    row = d * 2 + d // 32 * 4 if compact else d * 4  # one expert row as the combine reads it
+    comb = R * row + T * d * 4 + T * k * 8
     if cfg.n_shared:
-        comb += T * d * 4 + (T * 4 if cfg.shared_gated else 0)
+        comb += T * row + (T * 4 if cfg.shared_gated else 0)
     return {
         "route": T * d * s + d * E * s + T * k * 8,
         "permute": R * 4 + R * 4 + 3 * R * 4,
@@ -481,7 +485,7 @@ def main():
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     g0 = g0_flops / (stage_ms["expert_up"] * 1e-3) / 1e12
     g1 = g1_flops / (stage_ms["expert_down"] * 1e-3) / 1e12
-    by = stage_bytes(cfg)
+    by = stage_bytes(cfg, m.comb == "separate16")
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -499,7 +503,10 @@ def main():
                                f"top-{k}" + (f" + {cfg.n_shared} shared f={cfg.f_shared}"
                                              if cfg.n_shared else ""),
                    "T": T, "d": d, "f": f, "E": cfg.E, "k": k,
-                   "path": {"fast": "gather fused into layer 0, separate combine",
+                   "path": {"fast": "gather fused into layer 0, separate combine" + (
+                                " over compact rows (fp16 + power-of-two factor per 32 columns)"
+                                if m.comb == "separate16" else ""),
+                            "fast32": "gather fused into layer 0, separate combine",
                             "atomic": "gather fused into layer 0, combine fused into layer 1",
                             "reference": "permuted copy of x, separate combine"}[args.path]},
         "pct_of_bf16_peak": round(100 * tflops / peak, 2),

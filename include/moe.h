@@ -239,6 +239,46 @@ int moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w, in
                 const float* y_shared, const float* shared_gate_logit, int accumulate, float* y,
                 hipStream_t stream);
 
+/*
+ * Compact layer-1 rows.  The same expert outputs as moe_expert_down's
+ * y_perm, stored in half the bytes for the combine that reads them back:
+ *   y_perm[r, c] = y_h[r, c] * y_s[r, c / 32],
+ * y_h IEEE fp16 (round to nearest even), y_s one power of two per 32-column
+ * row segment, chosen so that the segment's largest finite magnitude lands
+ * in [2^14, 2^15): no value overflows fp16 and each keeps 11 significant
+ * bits at its segment's scale (error at most 2^-11 of the segment's largest
+ * magnitude; inf and NaN are kept).  The pages fix no storage precision for
+ * this intermediate (DisagMoE technical summary, "2.2 AF-Pipe": the expert
+ * outputs go back to be combined); the fp32 calls above stay the exact form.
+ *
+ * moe_expert_down_f16 -- moe_expert_down with this output (no fused combine):
+ *   out[r, :] = a[r, :] W_down[e] for rows r of expert e, stored as above.
+ * Arguments: a [rows, f] bf16; offsets, E, rows, f, workspace as in
+ *   moe_expert_down; W_down [E, f, d] bf16; y_h [rows, d] (fp16 bits) out;
+ *   y_s [rows, d / 32] fp32 out.  bf16 only and d a multiple of 32, else
+ *   MOE_ERR_UNSUPPORTED.
+ */
+int moe_expert_down_f16(const void* a, const int32_t* offsets, int E, int rows, int f, int d,
+                        const void* W_down, uint16_t* y_h, float* y_s, void* workspace,
+                        size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_combine_f16 -- moe_combine over compact rows: the same v and y, with
+ *   y_perm[r, :] read as y_h[r, :] * y_s[r, : / 32] and y_shared[t, :] as
+ *   ys_h[t, :] * ys_s[t, : / 32] (e.g. the shared experts' moe_expert_down_f16
+ *   over T rows).  Each term is the product moe_combine forms from the
+ *   restored value, in the same slot order: given the same rows, both calls
+ *   write the same bits.
+ * Arguments: y_h [T*k, d] fp16 bits and y_s [T*k, d / 32] fp32, inv [T, k]
+ *   and topk_w [T, k] as in moe_combine (all four given or inv NULL);
+ *   ys_h [T, d] and ys_s [T, d / 32], both or neither; shared_gate_logit [T]
+ *   or NULL (needs ys_h); accumulate 0 or 1; y [T, d] fp32 out.  d a multiple
+ *   of 32, else MOE_ERR_UNSUPPORTED.
+ */
+int moe_combine_f16(const uint16_t* y_h, const float* y_s, const int32_t* inv, const float* topk_w,
+                    int T, int d, int k, const uint16_t* ys_h, const float* ys_s,
+                    const float* shared_gate_logit, int accumulate, float* y, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Backward pass (training).  The pages train MoE models (COMET page, "What
  * Is COMET"; DisagMoE technical summary, "2.2 AF-Pipe", whose pipeline has

@@ -28,6 +28,7 @@ EXPORTS = (
     "moe_unpermute", "moe_topk_weights_backward", "moe_linear_backward_workspace_size",
     "moe_linear_backward", "moe_ffn_backward_workspace_size", "moe_workspace_size",
     "moe_probe_mfma", "moe_permute_noalloc", "moe_probe_read",
+    "moe_expert_down_f16", "moe_combine_f16",
 )
 
 _lib = None
@@ -67,6 +68,8 @@ def load():
         "moe_ffn_forward": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                   vp, vp, vp, sz, vp]),
         "moe_combine": (i32, [vp, vp, vp, i32, i32, i32, vp, vp, i32, vp, vp]),
+        "moe_expert_down_f16": (i32, [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
+        "moe_combine_f16": (i32, [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, i32, vp, vp]),
         "moe_expert_up_save": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                      vp, sz, vp]),
         "moe_combine_backward": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
@@ -199,6 +202,25 @@ def moe_combine(y_perm, inv, topk_w, T, d, k, y_shared, shared_gate_logit, accum
                             _p(shared_gate_logit), accumulate, _p(y), _stream(stream))
     if check:
         _check("moe_combine", st)
+    return st
+
+
+def moe_expert_down_f16(a, offsets, E, rows, f, d, W_down, y_h, y_s, workspace, ws_bytes,
+                        stream=None, check=True):
+    st = load().moe_expert_down_f16(_p(a), _p(offsets), E, rows, f, d, _p(W_down), _p(y_h),
+                                    _p(y_s), _p(workspace), ws_bytes, _stream(stream))
+    if check:
+        _check("moe_expert_down_f16", st)
+    return st
+
+
+def moe_combine_f16(y_h, y_s, inv, topk_w, T, d, k, ys_h, ys_s, shared_gate_logit, accumulate, y,
+                    stream=None, check=True):
+    st = load().moe_combine_f16(_p(y_h), _p(y_s), _p(inv), _p(topk_w), T, d, k, _p(ys_h),
+                                _p(ys_s), _p(shared_gate_logit), accumulate, _p(y),
+                                _stream(stream))
+    if check:
+        _check("moe_combine_f16", st)
     return st
 
 

@@ -76,6 +76,8 @@ struct GemmArgs {
   bf16_t* h_out;            // layer 0: x W_gate [rows, N] saved for the backward, or NULL
   bf16_t* u_out;            // layer 0: x W_up [rows, N] (given with h_out)
   float* y_perm;            // layer 1 output [rows, N] or NULL
+  uint16_t* y_h;            // layer 1 compact output [rows, N] fp16, or NULL (see store_seg_f16)
+  float* y_s;               // its restoring factors [rows, N / 32] (with y_h)
   const int32_t* scatter;   // layer 1 fused combine target row, or NULL (identity)
   const float* row_w;       // layer 1 fused combine weight, or NULL (1)
   float* y;                 // layer 1 fused combine target, or NULL
@@ -87,8 +89,58 @@ struct GemmArgs {
   float* part;              // partial accumulators of split tiles, or NULL (no split)
   int n_cu;                 // compute units the tiles are spread over
   int fixup;                // 0: main pass; 1: sum the split tiles' partials
-  int nt_y;                 // y_perm stores non-temporal (y_perm larger than the last-level cache)
+  int nt_y;                 // layer-1 output stores non-temporal (larger than the last-level cache)
 };
+
+// Compact layer-1 output: IEEE fp16 with one power-of-two factor per
+// 32-column row segment.  The segment's largest finite magnitude m is scaled
+// into [2^14, 2^15), well inside the fp16 range, so nothing overflows and
+// every value keeps fp16's 11 significant bits at the segment's scale
+// (round to nearest even; relative error at most 2^-11 of the segment's
+// largest value); y_s holds the factor that restores it, 1 / scale, exact
+// since both are powers of two.  Inf and NaN do not set the scale and stay
+// inf and NaN.  Four consecutive lanes hold one segment, 8 columns each:
+// src (LDS, 8 floats), dst (8 columns of y_h), fdst (the segment's factor,
+// written by the first lane of the four); valid: the lane's row and columns
+// exist.  Every lane of the wave must take part (quad reduction by DPP).
+template <bool NT>
+__device__ __forceinline__ void store_seg_f16(const float* src, uint16_t* dst, float* fdst,
+                                              bool valid, bool leader) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+  const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  uint32_t m = 0;  // largest finite magnitude, as bits (ordered like the values)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t u = __float_as_uint(v[i]) & 0x7fffffffu;
+    m = max(m, u < 0x7f800000u ? u : 0u);
+  }
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));  // lane ^ 1
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));  // lane ^ 2
+  // m lies in [2^(eb - 127), 2^(eb - 126)); the scale 2^(141 - eb) takes it
+  // into [2^14, 2^15).  eb is raised to at least 15 so that scale and factor
+  // are normal floats (segments below 2^-112 are stored as they are scaled).
+  const int eb = max((int)(m >> 23), 15);
+  const float scale = __uint_as_float((uint32_t)(268 - eb) << 23);
+  const float back = __uint_as_float((uint32_t)(eb - 14) << 23);
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const _Float16 lo = static_cast<_Float16>(v[2 * i] * scale);
+    const _Float16 hi = static_cast<_Float16>(v[2 * i + 1] * scale);
+    o[i] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+  }
+  if (valid) {
+    if (NT) {
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst));
+      if (leader) __builtin_nontemporal_store(back, fdst);
+    } else {
+      *reinterpret_cast<u32x4*>(dst) = o;
+      if (leader) *fdst = back;
+    }
+  }
+}
 
 struct TileInfo {
   int e, row0, row_end, n_t, m_t;
@@ -442,7 +494,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
       }
     }
   } else {
-    if (p.y_perm) {
+    if (p.y_perm || p.y_h) {
       constexpr int OC = NJ * 16;   // output columns per wave, contiguous
       constexpr int SS = OC + 4;    // staging stride in floats (16-byte aligned, padded)
       float* sf = reinterpret_cast<float*>(stg);
@@ -453,6 +505,24 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void grouped_gemm_bf16_kernel(Gemm
         for (int nj = 0; nj < NJ; ++nj)
 #pragma unroll
           for (int i = 0; i < 4; ++i) sf[(row_l + i) * SS + nj * 16 + col_l] = acc[mi][nj][i];
+        if (p.y_h) {
+          // 16 rows x OC / 8 chunks of 8 columns; OC is a multiple of 32 and
+          // the wave's columns start at a multiple of 32 (N too): whole segments
+          static_assert(OC % 32 == 0 && (16 * OC / 8) % 64 == 0, "compact output segments");
+          constexpr int CH = OC / 8;
+          const int segs = N >> 5;
+#pragma unroll
+          for (int q = 0; q < 16 * CH / 64; ++q) {
+            const int idx = q * 64 + lane;
+            const int r = idx / CH, c = idx % CH;
+            const int row = ti.row0 + wrow0 + mi * 16 + r;
+            const int col = ocol0 + c * 8;
+            store_seg_f16<false>(sf + r * SS + c * 8, p.y_h + (size_t)row * N + col,
+                                 p.y_s + (size_t)row * segs + (col >> 5),
+                                 row < ti.row_end && col < N, (c & 3) == 0);
+          }
+          continue;
+        }
         constexpr int CH = OC / 4;  // 16-byte chunks per row
 #pragma unroll
         for (int q = 0; q < (16 * CH + 63) / 64; ++q) {
@@ -609,18 +679,20 @@ struct Work {
 // expert's first tile), the split, this block's work item and its tile.
 __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   const int lane = threadIdx.x & 63;
-  int cnt_tiles[4], mt[4], offe[4];
+  int cnt_tiles[4], mt[4], offe[4], rows_e[4];
   int lane_sum = 0;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int e = lane * 4 + u;
-    int m = 0, o = 0;
+    int m = 0, o = 0, c = 0;
     if (e < p.E) {
       o = p.offsets[e];
-      m = cdiv(p.offsets[e + 1] - o, BM);
+      c = p.offsets[e + 1] - o;
+      m = cdiv(c, BM);
     }
     mt[u] = m;
     offe[u] = o;
+    rows_e[u] = c;
     cnt_tiles[u] = m * p.tiles_n;
     lane_sum += cnt_tiles[u];
   }
@@ -678,7 +750,7 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   if (w.tile < 0) return w;
   // the expert holding tile w.tile, from the same prefix sums
   int start = incl - lane_sum;
-  int hit_e = -1, hit_start = 0, hit_mt = 0, hit_off = 0;
+  int hit_e = -1, hit_start = 0, hit_mt = 0, hit_off = 0, hit_rows = 0;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     if (w.tile >= start && w.tile < start + cnt_tiles[u]) {
@@ -686,6 +758,7 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
       hit_start = start;
       hit_mt = mt[u];
       hit_off = offe[u];
+      hit_rows = rows_e[u];
     }
     start += cnt_tiles[u];
   }
@@ -697,6 +770,9 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   const int tstart = __shfl(hit_start, src);
   const int tmt = __shfl(hit_mt, src);
   const int toff = __shfl(hit_off, src);
+  // the expert's row count comes from the lane that holds it, not from a
+  // second, dependent read of the offsets (a memory round trip per tile)
+  const int c_e = __shfl(hit_rows, src);
   const int local = w.tile - tstart;
   // A large expert's M tiles are walked in ng balanced groups of at most
   // m_group tiles (the first tmt % ng groups hold one tile more); a group
@@ -726,7 +802,6 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   // and BM / 16).  Against full tiles plus one ragged last tile, this
   // removes all padding but the last block's, and the tiles of an (expert,
   // N panel), which run side by side and share the panel, take equal time.
-  const int c_e = p.offsets[ti.e + 1] - toff;
   const int nbe = cdiv(c_e, 16);
   const int b_lo = nbe / tmt, b_rem = nbe - b_lo * tmt;
   const int b0 = ti.m_t * b_lo + min(ti.m_t, b_rem);
@@ -1008,7 +1083,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
     }
   } else {
     // the wave's columns: n0 + h * 128 + wg * 32 + [0, 32) for halves h = 0, 1
-    if (p.y_perm) {
+    if (p.y_perm || p.y_h) {
       constexpr int SS = 64 + 4;  // staging stride in floats
       float* sf = reinterpret_cast<float*>(lds + wave * 16 * SS * 4);
 #pragma unroll
@@ -1018,6 +1093,27 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
         for (int nj = 0; nj < NJ; ++nj)
 #pragma unroll
           for (int i = 0; i < 4; ++i) sf[(row_l + i) * SS + nj * 16 + col_l] = acc[mi][nj][i];
+        if (p.y_h) {
+          // 16 rows x 8 chunks of 8 columns; chunks 4h .. 4h + 3 are the
+          // wave's 32-column segment of half h (N is a multiple of 32)
+          const int segs = N >> 5;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int idx = q * 64 + lane;
+            const int r = idx >> 3, c = idx & 7;
+            const int row = t_row0 + grow0 + (mi + mi_off) * 16 + r;
+            const int col = n0 + (c >> 2) * 128 + wg * 32 + (c & 3) * 8;
+            const float* src = sf + r * SS + c * 8;
+            uint16_t* dst = p.y_h + (size_t)row * N + col;
+            float* fdst = p.y_s + (size_t)row * segs + (col >> 5);
+            const bool ok = row < grow_end && col < N;
+            if (p.nt_y)
+              store_seg_f16<true>(src, dst, fdst, ok, (c & 3) == 0);
+            else
+              store_seg_f16<false>(src, dst, fdst, ok, (c & 3) == 0);
+          }
+          continue;
+        }
         // 16 rows x 16 chunks of 16 B; two separate loops, so that the
         // compiler keeps the non-temporal hint (merging the two stores drops it)
         if (p.nt_y) {
@@ -1176,7 +1272,8 @@ hipError_t launch_gemm(GemmArgs& p, int rows, int E, int ncols, unsigned long lo
     // a y_perm beyond the 256 MB last-level cache is streamed past it (the
     // combine re-reads it from HBM either way); a smaller one stays cached
     // for the combine (DeepSeek shape, 1.6 GB: +2%; Mixtral, 134 MB: cached)
-    p.nt_y = p.y_perm && (unsigned long long)rows * ncols * 4 > (256ull << 20);
+    p.nt_y = (p.y_perm && (unsigned long long)rows * ncols * 4 > (256ull << 20)) ||
+             (p.y_h && (unsigned long long)rows * ncols * 2 > (256ull << 20));
     if (ws_bytes < pp_part_bytes(p.n_cu)) p.part = nullptr;
     const long long grid_pp = grid + (p.part ? p.n_cu : 0);
     hipLaunchKernelGGL((grouped_gemm_bf16_pp_kernel<UP, 64, false>),
@@ -1253,6 +1350,22 @@ hipError_t launch_expert_down(const void* a, const int32_t* offsets, int E, int 
   p.scatter = scatter_idx;
   p.row_w = row_w;
   p.y = y;
+  p.part = static_cast<float*>(ws);
+  return launch_gemm<false, 2, DN_WN, DN_BNA>(p, rows, E, d, (unsigned long long)rows * f * 2,
+                                              ws ? ws_bytes : 0, s);
+}
+
+hipError_t launch_expert_down_f16(const void* a, const int32_t* offsets, int E, int rows, int f,
+                                  int d, const void* W_down, uint16_t* y_h, float* y_s, void* ws,
+                                  size_t ws_bytes, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  GemmArgs p{};
+  p.A = static_cast<const bf16_t*>(a);
+  p.offsets = offsets;
+  p.E = E; p.rows = rows; p.K = f; p.N = d;
+  p.B0 = static_cast<const bf16_t*>(W_down);
+  p.y_h = y_h;
+  p.y_s = y_s;
   p.part = static_cast<float*>(ws);
   return launch_gemm<false, 2, DN_WN, DN_BNA>(p, rows, E, d, (unsigned long long)rows * f * 2,
                                               ws ? ws_bytes : 0, s);

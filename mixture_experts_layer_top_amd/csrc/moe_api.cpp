@@ -219,6 +219,41 @@ int moe_combine(const float* y_perm, const int32_t* inv, const float* topk_w, in
                                         accumulate == 1, y, stream));
 }
 
+int moe_expert_down_f16(const void* a, const int32_t* offsets, int E, int rows, int f, int d,
+                        const void* W_down, uint16_t* y_h, float* y_s, void* workspace,
+                        size_t ws_bytes, hipStream_t stream) {
+  int st = check_ffn_common(offsets, E, rows, d, f, MOE_BF16, workspace, ws_bytes);
+  if (st != MOE_OK) return st;
+  if (d % 32) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!a || !W_down || !y_h || !y_s) return MOE_ERR_INVALID;
+  if (!aligned16(a) || !aligned16(W_down) || !aligned16(offsets) || !aligned16(y_h) ||
+      !aligned16(y_s))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_expert_down_f16(a, offsets, E, rows, f, d, W_down, y_h, y_s,
+                                                workspace, ws_bytes, stream));
+}
+
+int moe_combine_f16(const uint16_t* y_h, const float* y_s, const int32_t* inv, const float* topk_w,
+                    int T, int d, int k, const uint16_t* ys_h, const float* ys_s,
+                    const float* shared_gate_logit, int accumulate, float* y,
+                    hipStream_t stream) {
+  if (T < 0 || k < 1 || k > 256 || d <= 0) return MOE_ERR_INVALID;
+  if ((long long)T * k >= (1ll << 31)) return MOE_ERR_INVALID;
+  if (accumulate != 0 && accumulate != 1) return MOE_ERR_INVALID;
+  if (T == 0) return MOE_OK;
+  if (!y) return MOE_ERR_INVALID;
+  if (inv && (!y_h || !y_s || !topk_w)) return MOE_ERR_INVALID;
+  if (!ys_h != !ys_s) return MOE_ERR_INVALID;
+  if (shared_gate_logit && !ys_h) return MOE_ERR_INVALID;
+  if (d % 32) return MOE_ERR_UNSUPPORTED;
+  if ((inv && (!aligned16(y_h) || !aligned16(y_s) || !aligned16(inv) || !aligned16(topk_w))) ||
+      !aligned16(y) || (ys_h && (!aligned16(ys_h) || !aligned16(ys_s))))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_combine_f16(y_h, y_s, inv, topk_w, T, d, k, ys_h, ys_s,
+                                            shared_gate_logit, accumulate == 1, y, stream));
+}
+
 // ---------------------------------------------------------------- backward
 
 int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* inv,

@@ -70,10 +70,21 @@ hipError_t launch_expert_down(const void* a, const int32_t* offsets, int E, int 
                               int d, bool bf16, const void* W_down, float* y_perm,
                               const int32_t* scatter_idx, const float* row_w, float* y, void* ws,
                               size_t ws_bytes, hipStream_t s);
+// layer 1 (bf16) with the compact output: fp16 y_h [rows, d] and one
+// restoring factor per 32-column row segment, y_s [rows, d / 32] (d % 32 == 0)
+hipError_t launch_expert_down_f16(const void* a, const int32_t* offsets, int E, int rows, int f,
+                                  int d, const void* W_down, uint16_t* y_h, float* y_s, void* ws,
+                                  size_t ws_bytes, hipStream_t s);
 
 hipError_t launch_combine(const float* y_perm, const int32_t* inv, const float* topk_w, int T,
                           int d, int k, const float* y_shared, const float* gate_logit,
                           bool accumulate, float* y, hipStream_t s);
+// the combine over compact rows (y_h, y_s as written by launch_expert_down_f16;
+// the shared term in the same form, ys_h [T, d], ys_s [T, d / 32], or NULL)
+hipError_t launch_combine_f16(const uint16_t* y_h, const float* y_s, const int32_t* inv,
+                              const float* topk_w, int T, int d, int k, const uint16_t* ys_h,
+                              const float* ys_s, const float* gate_logit, bool accumulate,
+                              float* y, hipStream_t s);
 
 hipError_t launch_probe_mfma(int blocks, int iters, uint64_t* ticks, hipStream_t s);
 hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);

@@ -12,12 +12,18 @@ Two independent choices shape the path:
   permutation (no permuted copy of x); "copy" -- moe_permute writes x_perm.
 * combine: "separate" -- the layer-1 GEMM writes y_perm (fp32) and
   moe_combine sums each token's k rows in slot order (deterministic);
-  "atomic" -- the layer-1 epilogue adds w * out straight into y with fp32
-  atomic adds (no y_perm; the order of a token's k adds is not fixed).
+  "separate16" -- the same with y_perm in its compact form (fp16 and one
+  power-of-two factor per 32-column row segment: moe_expert_down_f16,
+  moe_combine_f16; half the bytes of the round trip, the shared experts'
+  output likewise); "atomic" -- the layer-1 epilogue adds w * out straight
+  into y with fp32 atomic adds (no y_perm; the order of a token's k adds is
+  not fixed).
 
-Paths: "fast" = fused gather + separate combine (the benchmarked default,
-deterministic); "atomic" = fused gather + atomic combine; "reference" =
-copy gather + separate combine.
+Paths: "fast" = fused gather + separate16 combine (the benchmarked default,
+deterministic; bf16 layers with d a multiple of 32, the fp32 y_perm
+otherwise and in training); "fast32" = fused gather + separate combine;
+"atomic" = fused gather + atomic combine; "reference" = copy gather +
+separate combine.
 
 Training (``train=True``): the forward also keeps the layer-0 projections
 h = x W_gate and u = x W_up (routed and shared) and the router logits, and
@@ -50,8 +56,8 @@ import torch
 from . import _lib as L
 from .inputs import LayerConfig
 
-PATHS = {"fast": ("fused", "separate"), "atomic": ("fused", "atomic"),
-         "reference": ("copy", "separate")}
+PATHS = {"fast": ("fused", "separate16"), "fast32": ("fused", "separate"),
+         "atomic": ("fused", "atomic"), "reference": ("copy", "separate")}
 
 
 class MoeLayer:
@@ -62,6 +68,10 @@ class MoeLayer:
         self.path = path
         self.gather, self.comb = PATHS[path]
         self.train = train
+        # the compact rows: bf16 layers whose d splits into 32-column segments;
+        # training keeps the fp32 y_perm that moe_combine_backward reads
+        if self.comb == "separate16" and (train or cfg.dtype != "bf16" or cfg.d % 32):
+            self.comb = "separate"
         if train:
             if self.comb != "separate":
                 raise ValueError("training needs the separate combine")
@@ -86,6 +96,9 @@ class MoeLayer:
         self.x_perm = e(R, d, dt=act) if (self.gather == "copy" or train) else None
         self.a = e(R, f, dt=act)
         self.y_perm = e(R, d) if self.comb == "separate" else None
+        if self.comb == "separate16":
+            self.y_h = e(R, d, dt=torch.float16)
+            self.y_s = e(R, d // 32)
         self.y = e(T, d)
         self.ws_perm_bytes = L.moe_permute_workspace_size(T, E, k)
         self.ws_perm = e(max(self.ws_perm_bytes, 16), dt=torch.uint8)
@@ -105,7 +118,10 @@ class MoeLayer:
             if train:
                 self.s_h = e(T, self.fs_all, dt=act)
                 self.s_u = e(T, self.fs_all, dt=act)
-            if not (self.comb == "atomic" and not cfg.shared_gated):
+            if self.comb == "separate16":   # shared-expert output, compact
+                self.ys_h = e(T, d, dt=torch.float16)
+                self.ys_s = e(T, d // 32)
+            elif not (self.comb == "atomic" and not cfg.shared_gated):
                 self.ys = e(T, d)   # shared-expert output
             if cfg.shared_gated:
                 self.g_idx = e(T, 1, dt=i32)
@@ -147,6 +163,10 @@ class MoeLayer:
         else:
             L.moe_expert_up(t["x"], None, self.s_offsets, 1, T, d, fs, self.dtype, t["Ws_gate"],
                             t["Ws_up"], self.s_a, self.s_ws, self.s_ws_bytes, stream=stream)
+        if self.comb == "separate16":
+            L.moe_expert_down_f16(self.s_a, self.s_offsets, 1, T, fs, d, t["Ws_down"], self.ys_h,
+                                  self.ys_s, self.s_ws, self.s_ws_bytes, stream=stream)
+            return
         # ungated with the atomic combine: the output initialises y directly
         out = self.y if (self.comb == "atomic" and not c.shared_gated) else self.ys
         L.moe_expert_down(self.s_a, self.s_offsets, 1, T, fs, d, self.dtype, t["Ws_down"],
@@ -177,6 +197,9 @@ class MoeLayer:
             L.moe_expert_down(self.a, self.offsets, c.E, R, c.f, c.d, self.dtype, t["W_down"],
                               None, self.perm_token, self.perm_w, self.y, self.ws_ffn,
                               self.ws_ffn_bytes, stream=stream)
+        elif self.comb == "separate16":
+            L.moe_expert_down_f16(self.a, self.offsets, c.E, R, c.f, c.d, t["W_down"], self.y_h,
+                                  self.y_s, self.ws_ffn, self.ws_ffn_bytes, stream=stream)
         else:
             L.moe_expert_down(self.a, self.offsets, c.E, R, c.f, c.d, self.dtype, t["W_down"],
                               self.y_perm, None, None, None, self.ws_ffn, self.ws_ffn_bytes,
@@ -187,8 +210,13 @@ class MoeLayer:
             return
         c = self.cfg
         T = c.T
-        ys = self.ys if self.ns else None
         gl = self.g_logit if (self.ns and c.shared_gated) else None
+        if self.comb == "separate16":
+            ys_h, ys_s = (self.ys_h, self.ys_s) if self.ns else (None, None)
+            L.moe_combine_f16(self.y_h, self.y_s, self.inv, self.w, T, c.d, c.k, ys_h, ys_s, gl,
+                              0, self.y, stream=stream)
+            return
+        ys = self.ys if self.ns else None
         L.moe_combine(self.y_perm, self.inv, self.w, T, c.d, c.k, ys, gl, 0, self.y,
                       stream=stream)
 

@@ -131,6 +131,37 @@ def test_combine_validation(lib):
     assert c(T=0) == L.MOE_OK
 
 
+def test_compact_rows_validation(lib):
+    dn = lambda **kw: L.moe_expert_down_f16(**dict(dict(  # noqa
+        a=A, offsets=A, E=8, rows=128, f=128, d=64, W_down=A, y_h=A, y_s=A, workspace=A,
+        ws_bytes=1 << 20), **kw), stream=0, check=False)
+    assert dn(y_h=None) == L.MOE_ERR_INVALID
+    assert dn(y_s=None) == L.MOE_ERR_INVALID
+    assert dn(W_down=None) == L.MOE_ERR_INVALID
+    assert dn(offsets=None) == L.MOE_ERR_INVALID
+    assert dn(E=0) == L.MOE_ERR_INVALID
+    assert dn(d=72) == L.MOE_ERR_UNSUPPORTED   # not whole 32-column segments
+    assert dn(f=100) == L.MOE_ERR_UNSUPPORTED  # bf16 rows of 16-byte vectors
+    assert dn(y_s=MIS) == L.MOE_ERR_UNSUPPORTED
+    assert dn(y_h=MIS) == L.MOE_ERR_UNSUPPORTED
+    assert dn(rows=0) == L.MOE_OK
+    assert dn(rows=0, d=72) == L.MOE_ERR_UNSUPPORTED
+    c = lambda **kw: L.moe_combine_f16(**dict(dict(  # noqa
+        y_h=A, y_s=A, inv=A, topk_w=A, T=16, d=64, k=2, ys_h=None, ys_s=None,
+        shared_gate_logit=None, accumulate=0, y=A), **kw), stream=0, check=False)
+    assert c(y=None) == L.MOE_ERR_INVALID
+    assert c(y_s=None) == L.MOE_ERR_INVALID
+    assert c(topk_w=None) == L.MOE_ERR_INVALID
+    assert c(ys_h=A) == L.MOE_ERR_INVALID               # shared rows without their factors
+    assert c(ys_s=A) == L.MOE_ERR_INVALID
+    assert c(shared_gate_logit=A) == L.MOE_ERR_INVALID  # gate without a shared term
+    assert c(accumulate=2) == L.MOE_ERR_INVALID
+    assert c(k=0) == L.MOE_ERR_INVALID
+    assert c(d=72) == L.MOE_ERR_UNSUPPORTED
+    assert c(ys_h=A, ys_s=MIS) == L.MOE_ERR_UNSUPPORTED
+    assert c(T=0) == L.MOE_OK
+
+
 def test_backward_validation(lib):
     """The training entry points reject bad arguments on the host."""
     cb = dict(dy=A, y_perm=A, inv=A, topk_w=A, T=16, d=64, k=2, dtype=L.MOE_BF16, y_shared=None,

@@ -137,7 +137,7 @@ def check_y(cfg, y_g, y_ref, what=""):
 # ---------------------------------------------------------------- mid sizes
 
 
-PATH_IDS = ["fast", "atomic", "reference"]
+PATH_IDS = ["fast", "fast32", "atomic", "reference"]
 
 
 @pytest.mark.parametrize("path", PATH_IDS)
@@ -168,15 +168,92 @@ def test_deterministic_paths_are_bitwise_repeatable(L, name, path):
     assert torch.equal(m2.y, y1)
 
 
-def test_paths_agree(L):
-    cfg = MID["qwen2moe"]
+@pytest.mark.parametrize("name", ["qwen2moe", "qwen2moe_k64"])
+def test_paths_agree(L, name):
+    """fp32 rows: the same products whichever path; only the order of the fp32
+    adds may differ (atomic), and fast32 and reference add in the same order.
+    Compact rows (the fast path where d is a multiple of 32, else fast32's):
+    each term moves by at most 2^-11 of its segment's largest magnitude, so
+    |y_fast - y_ref| <= 2^-11 (max |y_perm| sum_j w_j + g max |y_shared|)."""
+    cfg = MID[name]
     layer = make_layer(cfg, seed=5, device="cuda")
-    ys = {p: run_layer(cfg, layer, p).y.cpu().double().numpy() for p in PATH_IDS}
+    ms = {p: run_layer(cfg, layer, p) for p in PATH_IDS}
+    ys = {p: m.y.cpu().double().numpy() for p, m in ms.items()}
     b = ys["reference"]
-    for p in ("fast", "atomic"):
-        # same products; only the order of the fp32 adds may differ
+    for p in ("fast32", "atomic"):
         assert np.max(np.abs(ys[p] - b)) <= 1e-5 * rms(b), p
-    assert np.array_equal(ys["fast"], ys["reference"])  # identical sums in identical order
+    assert np.array_equal(ys["fast32"], ys["reference"])  # identical sums in identical order
+    m32 = ms["fast32"]
+    wsum = m32.w.sum(dim=1).max().item()
+    bound = float(m32.y_perm.abs().max()) * wsum
+    if cfg.n_shared:
+        bound += float(m32.ys.abs().max())  # the gate is at most 1
+    assert ms["fast"].comb == ("separate16" if cfg.d % 32 == 0 else "separate")
+    assert np.max(np.abs(ys["fast"] - b)) <= 2.0 ** -11 * bound * (1 + 1e-6) + 1e-5 * rms(b)
+
+
+def restore(y_h, y_s):
+    """Values of compact rows: y_h[r, c] * y_s[r, c / 32] (exact in fp32)."""
+    return y_h.float() * y_s.repeat_interleave(32, dim=1)
+
+
+@pytest.mark.parametrize("name", ["deepseek", "qwen2moe_k64", "mixtral_skew", "mixtral_k64"])
+def test_compact_rows_encode_the_fp32_rows(L, name):
+    """The compact layer-1 rows against the fp32 rows of the same GEMM (same
+    tiles, same accumulation order, so the same fp32 values), routed and
+    shared: every factor is a power of two that puts the segment's largest
+    magnitude in [2^14, 2^15) (2^-126 for segments below 2^-112), every fp16
+    value is the fp32 value over the factor rounded to nearest even, bit for
+    bit; and the combine over the compact rows writes the bits moe_combine
+    writes over the restored rows."""
+    cfg = MID[name]
+    log(f"[compact] encode {name} T={cfg.T} d={cfg.d} f={cfg.f}")
+    layer = make_layer(cfg, seed=21, device="cuda")
+    m32 = run_layer(cfg, layer, "fast32")
+    m16 = run_layer(cfg, layer, "fast")
+    assert m16.comb == "separate16" and m32.comb == "separate"
+    pairs = [(m32.y_perm, m16.y_h, m16.y_s)]
+    if cfg.n_shared:
+        pairs.append((m32.ys, m16.ys_h, m16.ys_s))
+    for y32, yh, ysc in pairs:
+        R, d = y32.shape
+        seg = y32.view(R, d // 32, 32)
+        mx = seg.abs().amax(dim=2)
+        mant, _ = torch.frexp(ysc)
+        assert torch.all(mant == 0.5)
+        big = mx >= 2.0 ** -112
+        scaled = mx[big] / ysc[big]
+        assert torch.all((scaled >= 2.0 ** 14) & (scaled < 2.0 ** 15))
+        assert torch.all(ysc[~big] == 2.0 ** -126)
+        want = (seg / ysc.unsqueeze(2)).to(torch.float16).view(R, d)
+        assert torch.equal(yh.view(torch.int16), want.view(torch.int16))
+    T, d, k = cfg.T, cfg.d, cfg.k
+    ys = restore(m16.ys_h, m16.ys_s).contiguous() if cfg.n_shared else None
+    gl = m16.g_logit if (cfg.n_shared and cfg.shared_gated) else None
+    y = torch.empty_like(m16.y)
+    L.moe_combine(restore(m16.y_h, m16.y_s).contiguous(), m16.inv, m16.w, T, d, k, ys, gl, 0, y)
+    torch.cuda.synchronize()
+    assert torch.equal(y, m16.y)
+
+
+@pytest.mark.parametrize("scale_log2", [24, -30])
+def test_compact_rows_far_outside_fp16_range(L, scale_log2):
+    """W_down and the shared experts' W_down scaled by 2^24 and by 2^-30 (exact
+    in bf16): layer-1 outputs far above fp16's largest value, or below its
+    smallest, are kept by the segment factors, and y stays within the bar of
+    the oracle on the scaled layer."""
+    cfg = MID["deepseek"]
+    log(f"[compact] range 2^{scale_log2}")
+    layer = make_layer(cfg, seed=23, device="cuda")
+    s = 2.0 ** scale_log2
+    layer["W_down"] = (layer["W_down"] * s).contiguous()
+    layer["Ws_down"] = (layer["Ws_down"] * s).contiguous()
+    m = run_layer(cfg, layer, "fast")
+    assert m.comb == "separate16"
+    h = host_layer(layer)
+    idx_g, w_g, _ = check_routing(cfg, m, h)
+    check_y(cfg, m.y.cpu().double().numpy(), O.forward(h, cfg.k, cfg.renorm, idx=idx_g)["y"],
+            f"compact 2^{scale_log2}")
 
 
 # ---------------------------------------------------------------- edge cases
@@ -186,6 +263,22 @@ def small_cfg(**kw):
     base = dict(name="edge", cfg_id=9, T=130, d=72, f=40, E=8, k=2, renorm=True, dtype="bf16")
     base.update(kw)
     return CONFIGS["mixtral"].__class__(**base)
+
+
+@pytest.mark.parametrize("T,f", [(1, 40), (65, 40), (257, 64), (130, 64), (63, 128)])
+def test_compact_rows_ragged(L, T, f):
+    """d = 96 (three 32-column segments, a partial column tile) on the fast
+    path: compact rows from the general kernel (f = 40, K not a multiple of
+    64) and from the ping-pong kernel (f = 64, 128), ragged token counts."""
+    cfg = small_cfg(T=T, d=96, f=f)
+    log(f"[compact] ragged T={T} d=96 f={f}")
+    layer = make_layer(cfg, seed=40 + T, device="cuda")
+    m = run_layer(cfg, layer, "fast")
+    assert m.comb == "separate16"
+    h = host_layer(layer)
+    idx_g, w_g, _ = check_routing(cfg, m, h)
+    check_dispatch(cfg, m, idx_g, w_g)
+    check_y(cfg, m.y.cpu().double().numpy(), O.forward(h, cfg.k, cfg.renorm, idx=idx_g)["y"])
 
 
 @pytest.mark.parametrize("T", [1, 63, 65, 257])
@@ -417,11 +510,13 @@ def test_permute_large_histogram_path(L):
                 O.forward(h, cfg.k, cfg.renorm, idx=idx_g)["y"], path)
 
 
+@pytest.mark.parametrize("d", [72, 96])
 @pytest.mark.parametrize("path", ["fast", "reference"])
-def test_combine_more_than_eight_slots(L, path):
-    """k = 10 of 16 experts: the combine's run-time slot loop."""
-    cfg = small_cfg(E=16, k=10, T=600, d=72, f=40)
-    log(f"[edge] combine k={cfg.k} path={path}")
+def test_combine_more_than_eight_slots(L, path, d):
+    """k = 10 of 16 experts: the combine's run-time slot loop (d = 96: over
+    compact rows on the fast path)."""
+    cfg = small_cfg(E=16, k=10, T=600, d=d, f=40)
+    log(f"[edge] combine k={cfg.k} d={d} path={path}")
     layer = make_layer(cfg, seed=10, device="cuda")
     m = run_layer(cfg, layer, path)
     h = host_layer(layer)

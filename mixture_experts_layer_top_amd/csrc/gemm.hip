@@ -142,6 +142,24 @@ __device__ __forceinline__ void store_seg_f16(const float* src, uint16_t* dst, f
   }
 }
 
+// Inclusive prefix sum over the wave's 64 lanes (every lane active): a
+// Hillis-Steele scan inside each row of 16 lanes by DPP row shifts (lanes
+// shifted in from outside the row read 0), then the totals of the rows
+// below, read from lanes 15, 31 and 47, added to each row.  The shuffles
+// this replaces each took a round trip through the LDS permute unit, in a
+// dependent chain at the head of every tile.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15);
+  const int r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
 struct TileInfo {
   int e, row0, row_end, n_t, m_t;
   int nb;  // ping-pong kernel: 16-row blocks in the tile (<= BM / 16)
@@ -169,12 +187,7 @@ __device__ __forceinline__ TileInfo locate_tile(const GemmArgs& p, int tile) {
     lane_sum += cnt_tiles[u];
   }
   // inclusive wave prefix of lane_sum
-  int incl = lane_sum;
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const int v = __shfl_up(incl, s);
-    if (lane >= s) incl += v;
-  }
+  const int incl = wave_incl_sum(lane_sum);
   int start = incl - lane_sum;
   int hit_e = -1, hit_start = 0, hit_mt = 0, hit_off = 0;
 #pragma unroll
@@ -191,11 +204,11 @@ __device__ __forceinline__ TileInfo locate_tile(const GemmArgs& p, int tile) {
   TileInfo ti;
   ti.ok = hit != 0;
   if (!ti.ok) return ti;
-  const int src = __ffsll((unsigned long long)hit) - 1;
-  ti.e = __shfl(hit_e, src);
-  const int tstart = __shfl(hit_start, src);
-  const int tmt = __shfl(hit_mt, src);
-  const int toff = __shfl(hit_off, src);
+  const int src = __ffsll((unsigned long long)hit) - 1;  // uniform: read from that lane
+  ti.e = __builtin_amdgcn_readlane(hit_e, src);
+  const int tstart = __builtin_amdgcn_readlane(hit_start, src);
+  const int tmt = __builtin_amdgcn_readlane(hit_mt, src);
+  const int toff = __builtin_amdgcn_readlane(hit_off, src);
   const int local = tile - tstart;
   if (M_ORDERED) {
     ti.n_t = local / tmt;
@@ -696,13 +709,8 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
     cnt_tiles[u] = m * p.tiles_n;
     lane_sum += cnt_tiles[u];
   }
-  int incl = lane_sum;
-#pragma unroll
-  for (int sft = 1; sft < 64; sft <<= 1) {
-    const int v = __shfl_up(incl, sft);
-    if (lane >= sft) incl += v;
-  }
-  const int n_tiles = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+  const int incl = wave_incl_sum(lane_sum);
+  const int n_tiles = __builtin_amdgcn_readlane(incl, 63);
   const int C = p.n_cu;
   int tail = n_tiles % C;
   const int nk_all = p.K / pbk;
@@ -764,15 +772,15 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   }
   const uint64_t hit = __ballot(hit_e >= 0);
   if (hit == 0) return w;
-  const int src = __ffsll((unsigned long long)hit) - 1;
+  const int src = __ffsll((unsigned long long)hit) - 1;  // uniform: read from that lane
   TileInfo& ti = w.ti;
-  ti.e = __shfl(hit_e, src);
-  const int tstart = __shfl(hit_start, src);
-  const int tmt = __shfl(hit_mt, src);
-  const int toff = __shfl(hit_off, src);
+  ti.e = __builtin_amdgcn_readlane(hit_e, src);
+  const int tstart = __builtin_amdgcn_readlane(hit_start, src);
+  const int tmt = __builtin_amdgcn_readlane(hit_mt, src);
+  const int toff = __builtin_amdgcn_readlane(hit_off, src);
   // the expert's row count comes from the lane that holds it, not from a
-  // second, dependent read of the offsets (a memory round trip per tile)
-  const int c_e = __shfl(hit_rows, src);
+  // second, dependent read of the offsets
+  const int c_e = __builtin_amdgcn_readlane(hit_rows, src);
   const int local = w.tile - tstart;
   // A large expert's M tiles are walked in ng balanced groups of at most
   // m_group tiles (the first tmt % ng groups hold one tile more); a group

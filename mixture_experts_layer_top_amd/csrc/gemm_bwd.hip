@@ -125,12 +125,7 @@ __device__ __forceinline__ Loc locate_dgrad(const BwdArgs& p, int tile) {
     cnt[q] = m * p.tiles_n;
     lane_sum += cnt[q];
   }
-  int incl = lane_sum;
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const int v = __shfl_up(incl, s);
-    if (lane >= s) incl += v;
-  }
+  const int incl = wave_incl_sum(lane_sum);
   int start = incl - lane_sum;
   int he = -1, hs = 0, hm = 0, ho = 0;
 #pragma unroll
@@ -147,13 +142,13 @@ __device__ __forceinline__ Loc locate_dgrad(const BwdArgs& p, int tile) {
   Loc L{};
   L.ok = hit != 0;
   if (!L.ok) return L;
-  const int src = __ffsll((unsigned long long)hit) - 1;
-  L.e = __shfl(he, src);
-  const int local = tile - __shfl(hs, src);
-  const int tmt = __shfl(hm, src);
+  const int src = __ffsll((unsigned long long)hit) - 1;  // uniform: read from that lane
+  L.e = __builtin_amdgcn_readlane(he, src);
+  const int local = tile - __builtin_amdgcn_readlane(hs, src);
+  const int tmt = __builtin_amdgcn_readlane(hm, src);
   L.n_t = local / tmt;
   const int m_t = local - L.n_t * tmt;
-  L.row0 = __shfl(ho, src) + m_t * BM;
+  L.row0 = __builtin_amdgcn_readlane(ho, src) + m_t * BM;
   L.row_end = min(L.row0 + BM, p.offsets[L.e + 1]);
   return L;
 }
@@ -465,12 +460,7 @@ __device__ __forceinline__ PTile locate_dgrad256(const BwdArgs& p, int tile) {
     cnt[q] = m * p.tiles_n;
     lane_sum += cnt[q];
   }
-  int incl = lane_sum;
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const int v = __shfl_up(incl, s);
-    if (lane >= s) incl += v;
-  }
+  const int incl = wave_incl_sum(lane_sum);
   int start = incl - lane_sum;
   int he = -1, hs = 0, hm = 0, ho = 0;
 #pragma unroll
@@ -487,11 +477,11 @@ __device__ __forceinline__ PTile locate_dgrad256(const BwdArgs& p, int tile) {
   PTile L{};
   L.ok = hit != 0;
   if (!L.ok) return L;
-  const int src = __ffsll((unsigned long long)hit) - 1;
-  L.e = __shfl(he, src);
-  const int local = tile - __shfl(hs, src);
-  const int tmt = __shfl(hm, src);
-  const int toff = __shfl(ho, src);
+  const int src = __ffsll((unsigned long long)hit) - 1;  // uniform: read from that lane
+  L.e = __builtin_amdgcn_readlane(he, src);
+  const int local = tile - __builtin_amdgcn_readlane(hs, src);
+  const int tmt = __builtin_amdgcn_readlane(hm, src);
+  const int toff = __builtin_amdgcn_readlane(ho, src);
   L.n_t = local / tmt;
   const int m_t = local - L.n_t * tmt;
   const int c_e = p.offsets[L.e + 1] - toff;

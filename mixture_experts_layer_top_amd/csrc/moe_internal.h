@@ -37,6 +37,24 @@ __device__ __forceinline__ float silu(float h) {
   return h * __builtin_amdgcn_rcpf(1.0f + __expf(-h));
 }
 
+// Inclusive prefix sum over the wave's 64 lanes (every lane active): a
+// Hillis-Steele scan inside each row of 16 lanes by DPP row shifts (lanes
+// shifted in from outside the row read 0), then the totals of the rows
+// below, read from lanes 15, 31 and 47, added to each row.  The shuffles
+// this replaces each took a round trip through the LDS permute unit, in a
+// dependent chain (at the head of every GEMM tile, for one).
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15);
+  const int r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
 // Round up a / b.
 __host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ __forceinline__ size_t align_up(size_t a, size_t b) { return (a + b - 1) / b * b; }

@@ -151,12 +151,7 @@ __device__ __forceinline__ void block_bases(const int32_t* __restrict__ blk_cnt,
     }
   }
   // exclusive scan of the totals over experts: wave prefix, then wave sums
-  int incl = tot;
-#pragma unroll
-  for (int sft = 1; sft < 64; sft <<= 1) {
-    const int v = __shfl_up(incl, sft);
-    if (lane >= sft) incl += v;
-  }
+  int incl = wave_incl_sum(tot);
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   for (int w2 = 0; w2 < wave; ++w2) incl += wsum[w2];

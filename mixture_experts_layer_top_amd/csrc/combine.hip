@@ -7,7 +7,9 @@
 //
 // One workgroup per token.  The token's k rows and weights are read once
 // (scalar loads); k is a template parameter so each thread keeps all k
-// row loads of two 16-byte chunks in flight before it adds them.
+// row loads of two 16-byte chunks in flight before it adds them.  The rows
+// come as fp32 (combine_kernel) or in the compact fp16 form layer 1 writes
+// on the default path (combine_f16_kernel, half the bytes).
 #include "moe_internal.h"
 
 namespace moe {

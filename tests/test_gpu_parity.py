@@ -602,3 +602,64 @@ def test_skew_sweep_sampled(L, scale):
         assert np.all(np.abs(share - 0.125) <= 0.02), share
     else:
         assert 0.48 <= share[0] <= 0.5 and share[7] < 0.01, share
+
+
+@pytest.mark.parametrize("k", [2, 6, 10])
+def test_compact_combine_every_term_combination(L, k):
+    """moe_combine_f16 through the C ABI on seeded compact rows (fp16 values,
+    power-of-two factors), for every combination of its terms: routed only,
+    shared only (gated or not), both, neither (y cleared), with accumulate 0
+    and 1; each against moe_combine over the restored rows, bit for bit."""
+    T, d, E = 333, 96, 16
+    R = T * k
+    log(f"[compact] combine terms k={k}")
+    g = torch.Generator(device="cpu").manual_seed(50 + k)
+    y_h = torch.randn(R, d, generator=g).to(torch.float16).cuda()
+    y_s = torch.ldexp(torch.ones(R, d // 32), torch.randint(-30, 30, (R, d // 32), generator=g)).cuda()
+    inv = torch.stack([torch.randperm(R, generator=g)[:T] for _ in range(k)], dim=1).to(torch.int32).cuda()
+    w = torch.rand(T, k, generator=g).cuda()
+    ys_h = torch.randn(T, d, generator=g).to(torch.float16).cuda()
+    ys_s = torch.ldexp(torch.ones(T, d // 32), torch.randint(-8, 8, (T, d // 32), generator=g)).cuda()
+    gl = torch.randn(T, generator=g).cuda()
+    y0 = torch.randn(T, d, generator=g).cuda()
+    rows, shared = restore(y_h, y_s).contiguous(), restore(ys_h, ys_s).contiguous()
+    for routed in (True, False):
+        for sh in ("none", "plain", "gated"):
+            for acc in (0, 1):
+                y16, y32 = y0.clone(), y0.clone()
+                L.moe_combine_f16(y_h if routed else None, y_s if routed else None,
+                                  inv if routed else None, w if routed else None, T, d, k,
+                                  None if sh == "none" else ys_h, None if sh == "none" else ys_s,
+                                  gl if sh == "gated" else None, acc, y16)
+                L.moe_combine(rows if routed else None, inv if routed else None,
+                              w if routed else None, T, d, k, None if sh == "none" else shared,
+                              gl if sh == "gated" else None, acc, y32)
+                torch.cuda.synchronize()
+                assert torch.equal(y16, y32), (routed, sh, acc)
+
+
+def test_compact_rows_keep_nan_without_losing_their_segment(L):
+    """Column 5 of every W_down set to +inf (bf16 holds it): each expert row's
+    column 5 sums infinite terms of both signs, so it is NaN on both paths.
+    The compact rows keep the NaN, and the NaN does not set its segment's
+    scale: y has the same NaN entries on both paths, and every other entry,
+    including columns 0..31 beside it, agrees to the compact rows' bound."""
+    cfg = MID["mixtral_k64"]
+    log("[compact] NaN column")
+    layer = make_layer(cfg, seed=31, device="cuda")
+    layer["W_down"][:, :, 5] = float("inf")
+    m32 = run_layer(cfg, layer, "fast32")
+    m16 = run_layer(cfg, layer, "fast")
+    assert m16.comb == "separate16"
+    y32, y16 = m32.y, m16.y
+    nan32, nan16 = torch.isnan(y32), torch.isnan(y16)
+    assert nan32[:, 5].all() and torch.equal(nan32, nan16)
+    ok = ~nan32
+    assert torch.isfinite(y32[ok]).all() and torch.isfinite(y16[ok]).all()
+    yp = m32.y_perm
+    fmax = float(torch.where(torch.isfinite(yp), yp.abs(), torch.zeros_like(yp)).amax())
+    err = (y16[ok] - y32[ok]).abs()
+    assert float(err.max()) <= 2.0 ** -11 * fmax * 1.000001
+    # the segment holding the NaN column is as precise as its neighbours
+    near = (y16[:, :32] - y32[:, :32]).abs()[ok[:, :32]]
+    assert float(near.max()) <= 2.0 ** -11 * fmax * 1.000001

@@ -464,6 +464,18 @@ def check_full_sampled(cfg, n_sample=24):
     return counts
 
 
+def test_layer1_operand_above_4GiB(L):
+    """Layer 1's A operand beyond 4 GiB (T = 133120 tokens, f = 8192: 266240
+    x 8192 bf16 = 4.36e9 bytes), past the ping-pong kernel's 32-bit operand
+    offsets: layer 1 runs on the general kernel (64-bit addressing), layer 0
+    on the ping-pong kernel (x is 1.1 GB). Routing and dispatch on every
+    token, y on sampled tokens, through the benchmark's launch path."""
+    cfg = dataclasses.replace(CONFIGS["mixtral"], name="mixtral_bigA", T=133120, f=8192)
+    assert cfg.T * cfg.k * cfg.f * 2 > 2 ** 32 > cfg.T * cfg.d * 2
+    check_full_sampled(cfg, n_sample=16)
+    torch.cuda.empty_cache()
+
+
 def check_full(cfg):
     """The layer at full size in the launch configuration the benchmark times
     (the "fast" path): routing and dispatch on every token, and y compared

@@ -192,13 +192,6 @@ __global__ __launch_bounds__(kThreads) void topk_weights_backward_kernel(
     }
 }
 
-template <typename XT>
-__device__ __forceinline__ float ldx(const XT* p, size_t i);
-template <>
-__device__ __forceinline__ float ldx<bf16_t>(const bf16_t* p, size_t i) { return bf16_to_f32(p[i]); }
-template <>
-__device__ __forceinline__ float ldx<float>(const float* p, size_t i) { return p[i]; }
-
 // dW partials (register-blocked fp32): a block takes EB experts, XCB
 // columns (512, or 256 for EB = 64) and token chunk tc of tc_len tokens.
 // Thread (token slice ts, expert group eg, column group cg) accumulates an

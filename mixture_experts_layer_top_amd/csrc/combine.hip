@@ -22,7 +22,7 @@ constexpr int kUnroll = 2;  // 16-byte chunks per thread in flight
 template <int KS>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const f32x4* __restrict__ y_perm, const int32_t* __restrict__ inv,
-    const float* __restrict__ topk_w, int T, int vecs, const f32x4* __restrict__ y_shared,
+    const float* __restrict__ topk_w, int vecs, const f32x4* __restrict__ y_shared,
     const float* __restrict__ gate_logit, int accumulate, f32x4* __restrict__ y) {
   const int t = blockIdx.x;
   float g = 1.f;
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 // any k (the C ABI allows up to 256): slot loop at run time
 __global__ __launch_bounds__(kThreads) void combine_any_kernel(
     const f32x4* __restrict__ y_perm, const int32_t* __restrict__ inv,
-    const float* __restrict__ topk_w, int T, int vecs, int k, const f32x4* __restrict__ y_shared,
+    const float* __restrict__ topk_w, int vecs, int k, const f32x4* __restrict__ y_shared,
     const float* __restrict__ gate_logit, int accumulate, f32x4* __restrict__ y) {
   const int t = blockIdx.x;
   float g = 1.f;
@@ -85,7 +85,7 @@ void launch_k(const float* y_perm, const int32_t* inv, const float* topk_w, int 
               const float* y_shared, const float* gate_logit, bool accumulate, float* y,
               hipStream_t s) {
   hipLaunchKernelGGL((combine_kernel<KS>), dim3(T), dim3(kThreads), 0, s,
-                     reinterpret_cast<const f32x4*>(y_perm), inv, topk_w, T, d / 4,
+                     reinterpret_cast<const f32x4*>(y_perm), inv, topk_w, d / 4,
                      reinterpret_cast<const f32x4*>(y_shared), gate_logit, accumulate ? 1 : 0,
                      reinterpret_cast<f32x4*>(y));
 }
@@ -111,7 +111,7 @@ __device__ __forceinline__ void add_f16_chunk(f32x4& lo, f32x4& hi, float c, u32
 template <int KS>
 __global__ __launch_bounds__(kThreads) void combine_f16_kernel(
     const u32x4* __restrict__ y_h, const float* __restrict__ y_s, const int32_t* __restrict__ inv,
-    const float* __restrict__ topk_w, int T, int chunks, const u32x4* __restrict__ ys_h,
+    const float* __restrict__ topk_w, int chunks, const u32x4* __restrict__ ys_h,
     const float* __restrict__ ys_s, const float* __restrict__ gate_logit, int accumulate,
     f32x4* __restrict__ y) {
   const int t = blockIdx.x;
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void combine_f16_kernel(
 // any k: slot loop at run time
 __global__ __launch_bounds__(kThreads) void combine_f16_any_kernel(
     const u32x4* __restrict__ y_h, const float* __restrict__ y_s, const int32_t* __restrict__ inv,
-    const float* __restrict__ topk_w, int T, int chunks, int k, const u32x4* __restrict__ ys_h,
+    const float* __restrict__ topk_w, int chunks, int k, const u32x4* __restrict__ ys_h,
     const float* __restrict__ ys_s, const float* __restrict__ gate_logit, int accumulate,
     f32x4* __restrict__ y) {
   const int t = blockIdx.x;
@@ -190,7 +190,7 @@ void launch_f16_k(const uint16_t* y_h, const float* y_s, const int32_t* inv, con
                   int T, int d, const uint16_t* ys_h, const float* ys_s, const float* gate_logit,
                   bool accumulate, float* y, hipStream_t s) {
   hipLaunchKernelGGL((combine_f16_kernel<KS>), dim3(T), dim3(kThreads), 0, s,
-                     reinterpret_cast<const u32x4*>(y_h), y_s, inv, topk_w, T, d / 8,
+                     reinterpret_cast<const u32x4*>(y_h), y_s, inv, topk_w, d / 8,
                      reinterpret_cast<const u32x4*>(ys_h), ys_s, gate_logit, accumulate ? 1 : 0,
                      reinterpret_cast<f32x4*>(y));
 }
@@ -216,7 +216,7 @@ hipError_t launch_combine_f16(const uint16_t* y_h, const float* y_s, const int32
     case 8: MOE_F16_K(8); break;
     default:
       hipLaunchKernelGGL(combine_f16_any_kernel, dim3(T), dim3(kThreads), 0, s,
-                         reinterpret_cast<const u32x4*>(y_h), y_s, inv, topk_w, T, d / 8, k,
+                         reinterpret_cast<const u32x4*>(y_h), y_s, inv, topk_w, d / 8, k,
                          reinterpret_cast<const u32x4*>(ys_h), ys_s, gate_logit,
                          accumulate ? 1 : 0, reinterpret_cast<f32x4*>(y));
   }
@@ -240,7 +240,7 @@ hipError_t launch_combine(const float* y_perm, const int32_t* inv, const float* 
     case 8: launch_k<8>(y_perm, inv, topk_w, T, d, y_shared, gate_logit, accumulate, y, s); break;
     default:
       hipLaunchKernelGGL(combine_any_kernel, dim3(T), dim3(kThreads), 0, s,
-                         reinterpret_cast<const f32x4*>(y_perm), inv, topk_w, T, d / 4, k,
+                         reinterpret_cast<const f32x4*>(y_perm), inv, topk_w, d / 4, k,
                          reinterpret_cast<const f32x4*>(y_shared), gate_logit, accumulate ? 1 : 0,
                          reinterpret_cast<f32x4*>(y));
   }

@@ -260,7 +260,7 @@ template <int NB, int MB, int NWV, int ST, bool WTR>
 __global__ __launch_bounds__(NWV * 64) void route_bf16_kernel(RouteArgs a) {
   using C = RouteCfg<NB, MB, NWV, ST>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int Ep = C::Ep, TW = C::TW, KC = C::KC, WL = C::WL;
+  constexpr int Ep = C::Ep, TW = C::TW, KC = C::KC;
   constexpr int NT = NWV * 64;
   constexpr int ls = Ep + 1;  // LDS row stride of the logits, in floats
 

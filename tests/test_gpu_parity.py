@@ -293,8 +293,14 @@ def test_ragged_token_counts(L, T):
     check_y(cfg, m.y.cpu().double().numpy(), O.forward(h, cfg.k, cfg.renorm, idx=idx_g)["y"])
 
 
-@pytest.mark.parametrize("E,k", [(1, 1), (4, 4), (256, 8), (3, 2)])
+@pytest.mark.parametrize("E,k", [(1, 1), (4, 4), (256, 8), (3, 2), (8, 1), (64, 1), (16, 16),
+                                 (64, 20), (256, 256)])
 def test_expert_count_extremes(L, E, k):
+    """Expert and slot counts at the ends of the accepted range: one expert,
+    top-1 over 8 and 64 (renormalised weights exactly 1), k = E = 16 (the
+    last k whose picks stay one per lane of the router's 16-lane row),
+    k = 20 > 16 (picks written one by one), k = E = 256 (every token on every
+    expert; the combine's run-time slot loop)."""
     cfg = small_cfg(E=E, k=k, T=300, d=64, f=48)
     log(f"[edge] E={E} k={k}")
     layer = make_layer(cfg, seed=E, device="cuda")

@@ -306,7 +306,8 @@ int moe_combine_f16(const uint16_t* y_h, const float* y_s, const int32_t* inv, c
  *   forward) or NULL; shared_gate_logit [T] or NULL; dy_perm [T*k, d] out in
  *   dtype (the storage dtype of the layer); dw [T, k] fp32 out; dy_shared
  *   [T, d] out in dtype or NULL; dgate_logit [T] fp32 out (required with the
- *   logit) or NULL.  1 <= k <= 8.
+ *   logit) or NULL.  1 <= k <= 256 (above 8 the slots are taken one after
+ *   another, with the same summation order).
  */
 int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* inv,
                          const float* topk_w, int T, int d, int k, int dtype,
@@ -359,7 +360,7 @@ int moe_expert_up_backward(const void* x, const int32_t* gather_idx, const int32
  * moe_unpermute -- gradient of the dispatch (DisagMoE technical summary,
  * "2.2 AF-Pipe", dispatch): dx[t, :] (+)= sum_j dx_perm[inv[t, j], :] in slot
  * order.  dx_perm [T*k, d] fp32, inv [T, k], dx [T, d] fp32 out (added to
- * when accumulate = 1); 1 <= k <= 8.
+ * when accumulate = 1); 1 <= k <= 256.
  */
 int moe_unpermute(const float* dx_perm, const int32_t* inv, int T, int d, int k, int accumulate,
                   float* dx, hipStream_t stream);

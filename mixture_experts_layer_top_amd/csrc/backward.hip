@@ -97,6 +97,63 @@ __global__ __launch_bounds__(kThreads) void combine_backward_kernel(
   }
 }
 
+// Any k (the forward takes up to 256 slots): the slots one after another,
+// each slot's dot product reduced over the workgroup before the next; the
+// same per-thread, per-wave and cross-wave order as the kernel above.
+template <typename OT>
+__global__ __launch_bounds__(kThreads) void combine_backward_any_kernel(
+    const f32x4* __restrict__ dy, const f32x4* __restrict__ y_perm, const int32_t* __restrict__ inv,
+    const float* __restrict__ topk_w, int vecs, int k, const f32x4* __restrict__ y_shared,
+    const float* __restrict__ gate_logit, OT* __restrict__ dy_perm, float* __restrict__ dw,
+    OT* __restrict__ dy_shared, float* __restrict__ dgate) {
+  __shared__ float red[kThreads / 64];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float g = 1.f;
+  if (gate_logit) g = 1.f / (1.f + __expf(-gate_logit[t]));
+  for (int j = 0; j < k; ++j) {
+    const int r = inv[(size_t)t * k + j];
+    const float w = topk_w[(size_t)t * k + j];
+    float dot = 0.f;
+    for (int c = threadIdx.x; c < vecs; c += kThreads) {
+      const f32x4 v = dy[(size_t)t * vecs + c];
+      const f32x4 yp = y_perm[(size_t)r * vecs + c];
+      dot += v[0] * yp[0] + v[1] * yp[1] + v[2] * yp[2] + v[3] * yp[3];
+      store4(dy_perm, (size_t)r * vecs + c, w * v);
+    }
+    const float sw = wave_sum(dot);
+    if (lane == 0) red[wave] = sw;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float tot = 0.f;
+      for (int w2 = 0; w2 < kThreads / 64; ++w2) tot += red[w2];
+      dw[(size_t)t * k + j] = tot;
+    }
+    __syncthreads();  // red is reused by the next slot
+  }
+  if (dy_shared) {
+    float dot_s = 0.f;
+    for (int c = threadIdx.x; c < vecs; c += kThreads) {
+      const f32x4 v = dy[(size_t)t * vecs + c];
+      store4(dy_shared, (size_t)t * vecs + c, g * v);
+      if (dgate) {
+        const f32x4 ys = y_shared[(size_t)t * vecs + c];
+        dot_s += v[0] * ys[0] + v[1] * ys[1] + v[2] * ys[2] + v[3] * ys[3];
+      }
+    }
+    if (dgate) {
+      const float sw = wave_sum(dot_s);
+      if (lane == 0) red[wave] = sw;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        float tot = 0.f;
+        for (int w2 = 0; w2 < kThreads / 64; ++w2) tot += red[w2];
+        dgate[t] = tot * g * (1.f - g);
+      }
+    }
+  }
+}
+
 // dx[t] (+)= sum_j dx_perm[inv[t, j]] (slot order); one workgroup per token
 template <int KS>
 __global__ __launch_bounds__(kThreads) void unpermute_kernel(const f32x4* __restrict__ dx_perm,
@@ -112,6 +169,20 @@ __global__ __launch_bounds__(kThreads) void unpermute_kernel(const f32x4* __rest
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < KS; ++j) s += dx_perm[(size_t)r[j] * vecs + c];
+    dx[(size_t)t * vecs + c] = v + s;
+  }
+}
+
+// any k: the same sum with the slot loop at run time
+__global__ __launch_bounds__(kThreads) void unpermute_any_kernel(const f32x4* __restrict__ dx_perm,
+                                                                 const int32_t* __restrict__ inv,
+                                                                 int vecs, int k, int accumulate,
+                                                                 f32x4* __restrict__ dx) {
+  const int t = blockIdx.x;
+  for (int c = threadIdx.x; c < vecs; c += kThreads) {
+    f32x4 v = accumulate ? dx[(size_t)t * vecs + c] : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) s += dx_perm[(size_t)inv[(size_t)t * k + j] * vecs + c];
     dx[(size_t)t * vecs + c] = v + s;
   }
 }
@@ -734,7 +805,20 @@ hipError_t launch_combine_backward(const float* dy, const float* y_perm, const i
 #define MOE_CB(K) case K: launch_cb<K>(dy, y_perm, inv, topk_w, T, d, bf16, y_shared, gate_logit, dy_perm, dw, dy_shared, dgate, s); break;
     MOE_CB(1) MOE_CB(2) MOE_CB(3) MOE_CB(4) MOE_CB(5) MOE_CB(6) MOE_CB(7) MOE_CB(8)
 #undef MOE_CB
-    default: return hipErrorInvalidValue;
+    default: {
+      const f32x4* dyv = reinterpret_cast<const f32x4*>(dy);
+      const f32x4* ypv = reinterpret_cast<const f32x4*>(y_perm);
+      const f32x4* ysv = reinterpret_cast<const f32x4*>(y_shared);
+      if (bf16)
+        hipLaunchKernelGGL((combine_backward_any_kernel<bf16_t>), dim3(T), dim3(kThreads), 0, s,
+                           dyv, ypv, inv, topk_w, d / 4, k, ysv, gate_logit,
+                           static_cast<bf16_t*>(dy_perm), dw, static_cast<bf16_t*>(dy_shared),
+                           dgate);
+      else
+        hipLaunchKernelGGL((combine_backward_any_kernel<float>), dim3(T), dim3(kThreads), 0, s,
+                           dyv, ypv, inv, topk_w, d / 4, k, ysv, gate_logit,
+                           static_cast<float*>(dy_perm), dw, static_cast<float*>(dy_shared), dgate);
+    }
   }
   return hipGetLastError();
 }
@@ -746,7 +830,10 @@ hipError_t launch_unpermute(const float* dx_perm, const int32_t* inv, int T, int
 #define MOE_UP(K) case K: launch_up<K>(dx_perm, inv, T, d, accumulate, dx, s); break;
     MOE_UP(1) MOE_UP(2) MOE_UP(3) MOE_UP(4) MOE_UP(5) MOE_UP(6) MOE_UP(7) MOE_UP(8)
 #undef MOE_UP
-    default: return hipErrorInvalidValue;
+    default:
+      hipLaunchKernelGGL(unpermute_any_kernel, dim3(T), dim3(kThreads), 0, s,
+                         reinterpret_cast<const f32x4*>(dx_perm), inv, d / 4, k,
+                         accumulate ? 1 : 0, reinterpret_cast<f32x4*>(dx));
   }
   return hipGetLastError();
 }

@@ -260,8 +260,8 @@ int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* in
                          const float* topk_w, int T, int d, int k, int dtype,
                          const float* y_shared, const float* shared_gate_logit, void* dy_perm,
                          float* dw, void* dy_shared, float* dgate_logit, hipStream_t stream) {
-  if (T < 0 || k < 1 || d <= 0) return MOE_ERR_INVALID;
-  if (k > 8 || !dtype_ok(dtype)) return MOE_ERR_UNSUPPORTED;
+  if (T < 0 || k < 1 || k > 256 || d <= 0) return MOE_ERR_INVALID;
+  if (!dtype_ok(dtype)) return MOE_ERR_UNSUPPORTED;
   if ((long long)T * k >= (1ll << 31)) return MOE_ERR_INVALID;
   if (T == 0) return MOE_OK;
   if (!dy || !y_perm || !inv || !topk_w || !dy_perm || !dw) return MOE_ERR_INVALID;
@@ -336,8 +336,7 @@ int moe_expert_up_backward(const void* x, const int32_t* gather_idx, const int32
 
 int moe_unpermute(const float* dx_perm, const int32_t* inv, int T, int d, int k, int accumulate,
                   float* dx, hipStream_t stream) {
-  if (T < 0 || k < 1 || d <= 0) return MOE_ERR_INVALID;
-  if (k > 8) return MOE_ERR_UNSUPPORTED;
+  if (T < 0 || k < 1 || k > 256 || d <= 0) return MOE_ERR_INVALID;
   if ((long long)T * k >= (1ll << 31)) return MOE_ERR_INVALID;
   if (accumulate != 0 && accumulate != 1) return MOE_ERR_INVALID;
   if (T == 0) return MOE_OK;

@@ -168,7 +168,8 @@ def test_backward_validation(lib):
               shared_gate_logit=None, dy_perm=A, dw=A, dy_shared=None, dgate_logit=None)
     def combine_bwd(**kw):
         return L.moe_combine_backward(**{**cb, **kw}, stream=0, check=False)
-    assert combine_bwd(k=9) == L.MOE_ERR_UNSUPPORTED
+    assert combine_bwd(k=257) == L.MOE_ERR_INVALID
+    assert combine_bwd(k=9, T=0) == L.MOE_OK  # any k up to 256
     assert combine_bwd(k=0) == L.MOE_ERR_INVALID
     assert combine_bwd(dy=None) == L.MOE_ERR_INVALID
     assert combine_bwd(d=60) == L.MOE_ERR_UNSUPPORTED
@@ -199,7 +200,8 @@ def test_backward_validation(lib):
     unp = dict(dx_perm=A, inv=A, T=16, d=64, k=2, accumulate=0, dx=A)
     def unpermute(**kw):
         return L.moe_unpermute(**{**unp, **kw}, stream=0, check=False)
-    assert unpermute(k=9) == L.MOE_ERR_UNSUPPORTED
+    assert unpermute(k=257) == L.MOE_ERR_INVALID
+    assert unpermute(k=9, T=0) == L.MOE_OK
     assert unpermute(inv=None) == L.MOE_ERR_INVALID
     assert unpermute(d=20) == L.MOE_ERR_UNSUPPORTED
     assert unpermute(T=0) == L.MOE_OK

@@ -201,6 +201,18 @@ def test_backward_expert_and_token_extremes(L, E, k, T):
     _edge_run(_edge_cfg(E=E, k=k, T=T, d=64, f=48), seed=100 + E + T)
 
 
+@pytest.mark.parametrize("E,k,shared", [(16, 10, False), (64, 20, True), (32, 32, False)])
+def test_backward_more_than_eight_slots(L, E, k, shared):
+    """k above 8: the combine backward and the unpermute take the slots one
+    after another (k = 10, 20 and k = E = 32); with a gated shared expert,
+    the shared gate's gradient through the same kernel."""
+    log(f"[bwd edge] E={E} k={k} shared={shared}")
+    kw = dict(E=E, k=k, T=200, d=64, f=48)
+    if shared:
+        kw.update(n_shared=1, f_shared=64, shared_gated=True)
+    _edge_run(_edge_cfg(**kw), seed=300 + E + k)
+
+
 @pytest.mark.parametrize("nk", [1, 2, 3, 5])
 def test_backward_stage_counts(L, nk):
     """d = f = 64 nk: the scalar-base backward GEMMs with 1, 2, 3 and 5 K

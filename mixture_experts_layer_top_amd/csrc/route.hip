@@ -629,14 +629,30 @@ __global__ __launch_bounds__(NWV * 64) void route_bf16_sw_kernel(RouteArgs a) {
   select_and_weigh<NB>(ll, ls, a, t_base, TB);
 }
 
+// Raise kernel KERN's dynamic LDS limit to `bytes`, once per device: a
+// function attribute, not a stream operation, so that later launches (also
+// under graph capture) make no host call besides the launch.
+constexpr int kMaxDevices = 64;
+template <auto KERN>
+hipError_t allow_lds(int bytes) {
+  static bool done[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool known = dev >= 0 && dev < kMaxDevices;
+  if (known && done[dev]) return hipSuccess;
+  e = hipFuncSetAttribute((const void*)KERN, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && known) done[dev] = true;
+  return e;
+}
+
 template <int NB, int NWV, int KC, int RING>
 hipError_t launch_sw(const RouteArgs& a, hipStream_t s) {
   using C = SwCfg<NB, NWV, KC, RING>;
   static_assert(C::LDS <= 160 * 1024, "LDS");
   auto kern = route_bf16_sw_kernel<NB, NWV, KC, RING>;
   if (C::LDS > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    hipError_t e = allow_lds<route_bf16_sw_kernel<NB, NWV, KC, RING>>(C::LDS);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, dim3(cdiv(a.T, C::TB)), dim3(NWV * 64), C::LDS, s, a);
@@ -655,8 +671,7 @@ hipError_t launch_cfg(const RouteArgs& a, hipStream_t s) {
   static_assert(C::LDS <= 160 * 1024, "LDS");
   auto kern = route_bf16_kernel<NB, MB, NWV, ST, WTR>;
   if (C::LDS > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    hipError_t e = allow_lds<route_bf16_kernel<NB, MB, NWV, ST, WTR>>(C::LDS);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, dim3(cdiv(a.T, C::TW)), dim3(NWV * 64), C::LDS, s, a);
@@ -697,18 +712,18 @@ hipError_t launch_route(const void* x, const void* W_r, const float* bias, int T
   if (!bf16) {
     const size_t lds = (size_t)64 * (E + 1) * 4;  // <= 64 * 257 * 4 = 65792 bytes
     auto launch = [&](auto kern) -> hipError_t {
-      if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-      }
       hipLaunchKernelGGL(kern, dim3(cdiv(T, 64)), dim3(kThreads), lds, s, a);
       return hipGetLastError();
     };
-    // logits per lane in the selection: E / 16 rounded up
+    // logits per lane in the selection: E / 16 rounded up (only the widest
+    // form can need more than 64 KiB of LDS: E = 256)
     if (E <= 16) return launch(route_f32_kernel<1>);
     if (E <= 32) return launch(route_f32_kernel<2>);
     if (E <= 64) return launch(route_f32_kernel<4>);
+    if (lds > 65536) {
+      hipError_t e = allow_lds<route_f32_kernel<16>>(64 * 257 * 4);
+      if (e != hipSuccess) return e;
+    }
     return launch(route_f32_kernel<16>);
   }
   // column blocks of 16 experts, rounded up to one of a few widths (the

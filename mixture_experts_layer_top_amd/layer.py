@@ -231,6 +231,26 @@ class MoeLayer:
                 marks(name)
         return self.y
 
+    def capture_graph(self):
+        """Record one forward pass into a HIP graph (a torch.cuda.CUDAGraph)
+        over this layer's buffers and inputs, after one eager pass on a side
+        stream (default priority); ``graph.replay()`` then reruns the whole
+        path on whatever the input buffers hold, writing the same buffers.
+        Every C-ABI call of the path is asynchronous on the calling stream,
+        allocates nothing and synchronises nothing, which is what lets the
+        capture record it; no call records a memset."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.forward()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            self.forward()
+        torch.cuda.synchronize()
+        return g
+
     # -- backward ----------------------------------------------------------
     BSTAGES = ("combine_bwd", "expert_down_bwd", "expert_up_bwd", "unpermute", "router_bwd",
                "shared_bwd")

@@ -9,34 +9,36 @@
 // layers walk M fastest inside an (expert, weight panel), so the tiles that
 // run together share the panel.
 //
-// bf16 kernel (gfx950):
-//   * workgroup = 8 wave64s (two per SIMD, 2 x 4), macro tile 256 rows x
-//     256 accumulator columns; each wave owns 128 x 64 = 8 x 4 blocks of
-//     16 x 16 computed with v_mfma_f32_16x16x32_bf16 (fp32 accumulation,
-//     128 accumulator registers per lane);
-//   * layer 0: the 256 columns are 128 columns of W_gate and the same 128
-//     columns of W_up, so SiLU(h) * u is formed in registers (the two
-//     accumulators of an output element sit in the same lane);
-//   * K stages of 64 (every gathered token row is one full 128-byte line
-//     per stage), two LDS buffers of 64 KiB: one stage loads while the other
-//     computes; one barrier per stage;
+// bf16 kernels (gfx950), both with 256-row x 256-accumulator-column tiles,
+// K stages of 64, v_mfma_f32_16x16x32_bf16 with fp32 accumulation:
+//   * grouped_gemm_bf16_pp_kernel (K a multiple of 64, the token operand
+//     below 4 GiB): 8 waves in two groups of 4, X (rows 0-127) and Y (rows
+//     128-255), taking turns on the matrix cores ("ping-pong"): while one
+//     group runs its MFMAs at raised priority, the other reads its fragments
+//     of the next stage from LDS and issues its share of the operand loads
+//     (X all A loads, Y all B loads), with a workgroup barrier between
+//     phases.  LDS holds an A ring of 2 stages and a B ring of 3 (5 x 32 KiB);
+//   * grouped_gemm_bf16_kernel (any K a multiple of 8, any operand size):
+//     8 waves that all load and all compute, the K tail zero-filled on load;
+//   * layer 0: the 256 columns are 128 columns of W_gate and the same 128 of
+//     W_up, so SiLU(h) * u is formed in registers; its rows are gathered on
+//     load through the permutation, so no permuted copy of x exists;
+//   * layer 1 writes fp32 rows, or compact rows (fp16 with a power-of-two
+//     factor per 32-column segment, store_seg_f16), or adds w * out into y
+//     with atomics (the fused combine);
 //   * operands move HBM -> LDS with global_load_lds_dwordx4 (no register
-//     staging), their issues spread between the MFMA rows; one load fills
-//     1 KiB of consecutive LDS, so each layout's swizzle is applied to the
-//     global addresses instead;
-//   * A (tokens, K contiguous) is stored row-major with the 16-byte chunk
-//     index XOR-swizzled by the row, read with ds_read_b128;
-//   * B (weights [K, N], N contiguous) is stored as is, swizzled by 32-byte
-//     pairs, and read with ds_read_b64_tr_b16, the gfx950 LDS transpose
-//     read, which gives each lane 4 consecutive K values of one column --
-//     no repacking of the caller's weights;
-//   * rows of layer 0 are gathered on load through the permutation
-//     (gather_idx), so the permuted copy of x need not exist;
-//   * tiles never straddle experts; each workgroup derives its (expert,
-//     tile) from the device-side offsets with a wave prefix sum, so the
-//     host never reads the per-expert counts; the workgroup id is remapped
-//     so that consecutive tiles land on the same XCD (and its L2), where
-//     they run in near lockstep and share their panels' lines.
+//     staging); one load fills 1 KiB of consecutive LDS, so each layout's
+//     swizzle is applied to the global addresses; A (K contiguous) is read
+//     with ds_read_b128, B (the caller's [K, N] weights, N contiguous) with
+//     ds_read_b64_tr_b16, the gfx950 LDS transpose read: no repacked copy;
+//   * tiles never straddle experts; each workgroup derives its tile from the
+//     device offsets (a wave prefix sum by DPP), so the host never reads the
+//     routing; tiles go M fastest inside an (expert, weight panel), large
+//     experts in groups of M tiles whose rows stay in the last-level cache,
+//     and consecutive tiles land on one XCD (its L2); an expert's rows are
+//     dealt to its M tiles in balanced 16-row blocks; the last round's tiles
+//     are split along K when it is mostly idle, and a second launch adds the
+//     parts in order (deterministic).
 #include <algorithm>
 
 #include "moe_internal.h"

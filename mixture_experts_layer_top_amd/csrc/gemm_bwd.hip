@@ -17,18 +17,26 @@
 //     layer 0: [dW_gate[e] | dW_up[e]] = x_perm^T [dH | dU] (M = d, N = 2f,
 //              rows of x gathered through the permutation).
 //
-// Kernel: 4 wave64s (2 x 2) per 128 x 128 tile, each wave 64 x 64 = 4 x 4
-// blocks of v_mfma_f32_16x16x32_bf16; K stages of 32; operands move HBM ->
-// LDS with direct-to-LDS loads (global_load_lds_dwordx4, no register
-// staging) into a ring of 4 stages, issued 3 stages ahead; one barrier per
-// stage.
-//   K-contiguous operands (DGRAD): LDS [128 rows][32 K], the 16-byte chunk
-//     index XOR-ed with (row / 4) % 4 so that a fragment read (16 rows at one
-//     chunk per 16 lanes) touches every bank once; read with ds_read_b128.
-//   K-outer operands (WGRAD): LDS [32 K rows][128 columns], 32-byte pairs
-//     swizzled by the K row, read with ds_read_b64_tr_b16 (the gfx950 LDS
-//     transpose read: each lane receives 4 consecutive K values of one column).
-// Out-of-range rows, columns and K are loaded as zeros and never stored.
+// Kernels:
+//   * grouped_gemm_bwd256_kernel (and the _pair form that runs a layer's
+//     DGRAD and WGRAD tiles in one launch): the forward's ping-pong design,
+//     256 x 256 tiles, 8 waves in two groups taking turns between fragment
+//     reads + loads and 64 MFMAs per K stage of 64, A ring 2 / B ring 3 in
+//     160 KiB of LDS, direct-to-LDS loads (global_load_lds_dwordx4) with the
+//     swizzle applied on the global side, epilogues staged through LDS so
+//     every global access is 16 bytes per lane;
+//   * grouped_gemm_bwd_kernel: 4 wave64s (2 x 2) per 128 x 128 tile, K stages
+//     of 32 in a ring of 4; it serves the layer-0 weight gradient when the
+//     rows of x are gathered through the permutation.
+// LDS layouts:
+//   K-contiguous operands (DGRAD): [rows][K], the 16-byte chunk index XOR-ed
+//     by the row so that a fragment read touches every bank once; read with
+//     ds_read_b128.
+//   K-outer operands (WGRAD): [K rows][columns], 32-byte pairs swizzled by
+//     the K row, read with ds_read_b64_tr_b16 (the gfx950 LDS transpose read:
+//     each lane receives 4 consecutive K values of one column).
+// Rows and columns past an operand read zeros or a valid row, and their
+// results are never stored; K past the operand is zero-filled.
 // Every sum runs in a fixed order: the results are deterministic.
 #include "moe_internal.h"
 

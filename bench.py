@@ -397,7 +397,9 @@ def run_backward(args):
     cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     layer = make_layer(cfg, seed=0, device=dev)
-    m = MoeLayer(cfg, layer, path="fast", train=True)
+    if args.path not in ("fast", "fast32", "reference"):
+        raise SystemExit(f"--backward trains a separate combine: --path {args.path} has none")
+    m = MoeLayer(cfg, layer, path=args.path, train=True)
     dy = torch.randn(cfg.T, cfg.d, generator=torch.Generator(device=dev).manual_seed(1),
                      device=dev, dtype=torch.float32)
     stream = torch.cuda.current_stream()
@@ -431,6 +433,7 @@ def run_backward(args):
     out = {
         "metric": "MoE layer bwd TFLOP/s + training-step tokens/s, 1xMI355X",
         "workload": cfg.name, "T": T, "d": d, "f": f, "E": cfg.E, "k": k,
+        "path": args.path, "combine": m.comb,
         "value": round(backward_flops(cfg) / (bwd_ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "steps": args.steps, "warmup": args.warmup,

@@ -316,6 +316,25 @@ int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* in
                          void* dy_shared, float* dgate_logit, hipStream_t stream);
 
 /*
+ * moe_combine_backward_f16 -- moe_combine_backward over compact rows (the
+ *   output of moe_expert_down_f16): the same gradients, with y_perm[r, :]
+ *   read as y_h[r, :] * y_s[r, : / 32] and y_shared[t, :] as
+ *   ys_h[t, :] * ys_s[t, : / 32].  dy_perm and dy_shared are the same values
+ *   as moe_combine_backward's; dw and dgate_logit may differ from them in
+ *   rounding order only (8 columns per step instead of 4).
+ * Arguments: dy [T, d] fp32; y_h [T*k, d] fp16 bits, y_s [T*k, d / 32] fp32;
+ *   inv, topk_w [T, k]; ys_h [T, d] and ys_s [T, d / 32], both or neither
+ *   (the ungated shared output; needed with the logit); shared_gate_logit,
+ *   dy_perm, dw, dy_shared, dgate_logit as in moe_combine_backward.
+ *   1 <= k <= 256; d a multiple of 32, else MOE_ERR_UNSUPPORTED.
+ */
+int moe_combine_backward_f16(const float* dy, const uint16_t* y_h, const float* y_s,
+                             const int32_t* inv, const float* topk_w, int T, int d, int k,
+                             int dtype, const uint16_t* ys_h, const float* ys_s,
+                             const float* shared_gate_logit, void* dy_perm, float* dw,
+                             void* dy_shared, float* dgate_logit, hipStream_t stream);
+
+/*
  * moe_expert_down_backward -- gradients of moe_expert_down (layer 1) and of
  * the SwiGLU of moe_expert_up, per expert e and row r of e:
  *   dA = dy_perm[r] W_down[e]^T,  s = sigmoid(h[r]),

@@ -28,7 +28,7 @@ EXPORTS = (
     "moe_unpermute", "moe_topk_weights_backward", "moe_linear_backward_workspace_size",
     "moe_linear_backward", "moe_ffn_backward_workspace_size", "moe_workspace_size",
     "moe_probe_mfma", "moe_permute_noalloc", "moe_probe_read",
-    "moe_expert_down_f16", "moe_combine_f16",
+    "moe_expert_down_f16", "moe_combine_f16", "moe_combine_backward_f16",
 )
 
 _lib = None
@@ -74,6 +74,8 @@ def load():
                                      vp, sz, vp]),
         "moe_combine_backward": (i32, [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                        vp, vp]),
+        "moe_combine_backward_f16": (i32, [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp,
+                                           vp, vp, vp, vp, vp]),
         "moe_expert_down_backward": (i32, [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                            vp, vp, sz, vp]),
         "moe_expert_up_backward": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp,
@@ -244,6 +246,18 @@ def moe_combine_backward(dy, y_perm, inv, topk_w, T, d, k, dtype, y_shared, shar
                                      _p(dy_shared), _p(dgate_logit), _stream(stream))
     if check:
         _check("moe_combine_backward", st)
+    return st
+
+
+def moe_combine_backward_f16(dy, y_h, y_s, inv, topk_w, T, d, k, dtype, ys_h, ys_s,
+                             shared_gate_logit, dy_perm, dw, dy_shared, dgate_logit, stream=None,
+                             check=True):
+    st = load().moe_combine_backward_f16(_p(dy), _p(y_h), _p(y_s), _p(inv), _p(topk_w), T, d, k,
+                                         dtype, _p(ys_h), _p(ys_s), _p(shared_gate_logit),
+                                         _p(dy_perm), _p(dw), _p(dy_shared), _p(dgate_logit),
+                                         _stream(stream))
+    if check:
+        _check("moe_combine_backward_f16", st)
     return st
 
 

@@ -154,6 +154,103 @@ __global__ __launch_bounds__(kThreads) void combine_backward_any_kernel(
   }
 }
 
+// The combine backward over compact rows (layer 1's fp16 output with one
+// power-of-two factor per 32-column segment): the same gradients. The factor
+// is a power of two, so <dy, h * f> = f <dy, h> exactly (no overflow at these
+// magnitudes): each 8-column dot is taken on the fp16 values and scaled once.
+// 8 columns per step: two 16-byte vectors of dy, one of a row.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float dot8(const f32x4 a, const f32x4 b, const u32x4 raw, float fac) {
+  const f16x8 h = __builtin_bit_cast(f16x8, raw);
+  float s = a[0] * static_cast<float>(h[0]) + a[1] * static_cast<float>(h[1]) +
+            a[2] * static_cast<float>(h[2]) + a[3] * static_cast<float>(h[3]);
+  s += b[0] * static_cast<float>(h[4]) + b[1] * static_cast<float>(h[5]) +
+       b[2] * static_cast<float>(h[6]) + b[3] * static_cast<float>(h[7]);
+  return s * fac;
+}
+
+// one workgroup per token; KS = k (1..8): one pass over dy for every slot and
+// the shared term; KS = 0: any k, the slots one after another (each slot's
+// dot reduced over the workgroup before the next), then the shared term
+template <int KS, typename OT>
+__global__ __launch_bounds__(kThreads) void combine_backward_f16_kernel(
+    const f32x4* __restrict__ dy, const u32x4* __restrict__ y_h, const float* __restrict__ y_s,
+    const int32_t* __restrict__ inv, const float* __restrict__ topk_w, int chunks, int k,
+    const u32x4* __restrict__ ys_h, const float* __restrict__ ys_s,
+    const float* __restrict__ gate_logit, OT* __restrict__ dy_perm, float* __restrict__ dw,
+    OT* __restrict__ dy_shared, float* __restrict__ dgate) {
+  constexpr bool kOne = KS > 0;     // every slot in one pass
+  constexpr int NS = kOne ? KS : 1;  // slots per pass
+  __shared__ float red[kThreads / 64][NS + 1];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int segs = chunks >> 2;
+  const int kk = kOne ? KS : k;
+  const f32x4* dyt = dy + (size_t)t * chunks * 2;
+  float g = 1.f;
+  if (gate_logit) g = 1.f / (1.f + __expf(-gate_logit[t]));
+  float dot_s = 0.f;
+  for (int j0 = 0; j0 < kk; j0 += NS) {
+    int r[NS];
+    float w[NS], dot[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      r[j] = inv[(size_t)t * kk + j0 + j];
+      w[j] = topk_w[(size_t)t * kk + j0 + j];
+      dot[j] = 0.f;
+    }
+    for (int c = threadIdx.x; c < chunks; c += kThreads) {
+      const f32x4 v0 = dyt[2 * c], v1 = dyt[2 * c + 1];
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        dot[j] += dot8(v0, v1, y_h[(size_t)r[j] * chunks + c], y_s[(size_t)r[j] * segs + (c >> 2)]);
+        store4(dy_perm, (size_t)r[j] * chunks * 2 + 2 * c, w[j] * v0);
+        store4(dy_perm, (size_t)r[j] * chunks * 2 + 2 * c + 1, w[j] * v1);
+      }
+      if (kOne && dy_shared) {
+        store4(dy_shared, (size_t)t * chunks * 2 + 2 * c, g * v0);
+        store4(dy_shared, (size_t)t * chunks * 2 + 2 * c + 1, g * v1);
+        if (dgate)
+          dot_s += dot8(v0, v1, ys_h[(size_t)t * chunks + c], ys_s[(size_t)t * segs + (c >> 2)]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const float sw = wave_sum(dot[j]);
+      if (lane == 0) red[wave][j] = sw;
+    }
+    __syncthreads();
+    if (threadIdx.x < NS) {
+      float s = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kThreads / 64; ++w2) s += red[w2][threadIdx.x];
+      dw[(size_t)t * kk + j0 + threadIdx.x] = s;
+    }
+    __syncthreads();  // red is reused below
+  }
+  if (!kOne && dy_shared) {
+    for (int c = threadIdx.x; c < chunks; c += kThreads) {
+      const f32x4 v0 = dyt[2 * c], v1 = dyt[2 * c + 1];
+      store4(dy_shared, (size_t)t * chunks * 2 + 2 * c, g * v0);
+      store4(dy_shared, (size_t)t * chunks * 2 + 2 * c + 1, g * v1);
+      if (dgate)
+        dot_s += dot8(v0, v1, ys_h[(size_t)t * chunks + c], ys_s[(size_t)t * segs + (c >> 2)]);
+    }
+  }
+  if (dgate) {
+    const float sw = wave_sum(dot_s);
+    if (lane == 0) red[wave][0] = sw;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float s = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kThreads / 64; ++w2) s += red[w2][0];
+      dgate[t] = s * g * (1.f - g);
+    }
+  }
+}
+
 // dx[t] (+)= sum_j dx_perm[inv[t, j]] (slot order); one workgroup per token
 template <int KS>
 __global__ __launch_bounds__(kThreads) void unpermute_kernel(const f32x4* __restrict__ dx_perm,
@@ -820,6 +917,45 @@ hipError_t launch_combine_backward(const float* dy, const float* y_perm, const i
                            static_cast<float*>(dy_perm), dw, static_cast<float*>(dy_shared), dgate);
     }
   }
+  return hipGetLastError();
+}
+
+template <int KS, typename OT>
+void launch_cbh(const float* dy, const uint16_t* y_h, const float* y_s, const int32_t* inv,
+                const float* topk_w, int T, int d, int k, const uint16_t* ys_h, const float* ys_s,
+                const float* gate_logit, void* dy_perm, float* dw, void* dy_shared, float* dgate,
+                hipStream_t s) {
+  hipLaunchKernelGGL((combine_backward_f16_kernel<KS, OT>), dim3(T), dim3(kThreads), 0, s,
+                     reinterpret_cast<const f32x4*>(dy), reinterpret_cast<const u32x4*>(y_h), y_s,
+                     inv, topk_w, d / 8, k, reinterpret_cast<const u32x4*>(ys_h), ys_s, gate_logit,
+                     static_cast<OT*>(dy_perm), dw, static_cast<OT*>(dy_shared), dgate);
+}
+
+hipError_t launch_combine_backward_f16(const float* dy, const uint16_t* y_h, const float* y_s,
+                                       const int32_t* inv, const float* topk_w, int T, int d,
+                                       int k, bool bf16, const uint16_t* ys_h, const float* ys_s,
+                                       const float* gate_logit, void* dy_perm, float* dw,
+                                       void* dy_shared, float* dgate, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+#define MOE_CBH(K)                                                                              \
+  if (bf16)                                                                                     \
+    launch_cbh<K, bf16_t>(dy, y_h, y_s, inv, topk_w, T, d, k, ys_h, ys_s, gate_logit, dy_perm,   \
+                          dw, dy_shared, dgate, s);                                             \
+  else                                                                                          \
+    launch_cbh<K, float>(dy, y_h, y_s, inv, topk_w, T, d, k, ys_h, ys_s, gate_logit, dy_perm, dw, \
+                         dy_shared, dgate, s);
+  switch (k) {
+    case 1: MOE_CBH(1) break;
+    case 2: MOE_CBH(2) break;
+    case 3: MOE_CBH(3) break;
+    case 4: MOE_CBH(4) break;
+    case 5: MOE_CBH(5) break;
+    case 6: MOE_CBH(6) break;
+    case 7: MOE_CBH(7) break;
+    case 8: MOE_CBH(8) break;
+    default: MOE_CBH(0)
+  }
+#undef MOE_CBH
   return hipGetLastError();
 }
 

@@ -277,6 +277,29 @@ int moe_combine_backward(const float* dy, const float* y_perm, const int32_t* in
                                                  dy_perm, dw, dy_shared, dgate_logit, stream));
 }
 
+int moe_combine_backward_f16(const float* dy, const uint16_t* y_h, const float* y_s,
+                             const int32_t* inv, const float* topk_w, int T, int d, int k,
+                             int dtype, const uint16_t* ys_h, const float* ys_s,
+                             const float* shared_gate_logit, void* dy_perm, float* dw,
+                             void* dy_shared, float* dgate_logit, hipStream_t stream) {
+  if (T < 0 || k < 1 || k > 256 || d <= 0) return MOE_ERR_INVALID;
+  if (!dtype_ok(dtype)) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * k >= (1ll << 31)) return MOE_ERR_INVALID;
+  if (T == 0) return MOE_OK;
+  if (!dy || !y_h || !y_s || !inv || !topk_w || !dy_perm || !dw) return MOE_ERR_INVALID;
+  if (!ys_h != !ys_s) return MOE_ERR_INVALID;
+  if (shared_gate_logit && (!dy_shared || !ys_h || !dgate_logit)) return MOE_ERR_INVALID;
+  if (dgate_logit && !shared_gate_logit) return MOE_ERR_INVALID;
+  if (d % 32) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(dy) || !aligned16(y_h) || !aligned16(y_s) || !aligned16(inv) ||
+      !aligned16(topk_w) || !aligned16(dy_perm) || !aligned16(dw) ||
+      (ys_h && (!aligned16(ys_h) || !aligned16(ys_s))) || (dy_shared && !aligned16(dy_shared)))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_combine_backward_f16(
+      dy, y_h, y_s, inv, topk_w, T, d, k, dtype == MOE_BF16, ys_h, ys_s, shared_gate_logit,
+      dy_perm, dw, dy_shared, dgate_logit, stream));
+}
+
 static int check_bwd_common(const int32_t* offsets, int E, int rows, int d, int f, int dtype) {
   if (E < 1 || E > 256 || rows < 0 || d <= 0 || f <= 0) return MOE_ERR_INVALID;
   if ((long long)rows * 2 * (d > f ? d : f) >= (1ll << 40)) return MOE_ERR_INVALID;

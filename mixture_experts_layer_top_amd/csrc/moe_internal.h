@@ -109,6 +109,13 @@ hipError_t launch_probe_mfma(int blocks, int iters, uint64_t* ticks, hipStream_t
 hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 
 // backward
+// the same over compact rows (y_h, y_s and the shared ys_h, ys_s as written
+// by launch_expert_down_f16)
+hipError_t launch_combine_backward_f16(const float* dy, const uint16_t* y_h, const float* y_s,
+                                       const int32_t* inv, const float* topk_w, int T, int d,
+                                       int k, bool bf16, const uint16_t* ys_h, const float* ys_s,
+                                       const float* gate_logit, void* dy_perm, float* dw,
+                                       void* dy_shared, float* dgate, hipStream_t s);
 hipError_t launch_combine_backward(const float* dy, const float* y_perm, const int32_t* inv,
                                    const float* topk_w, int T, int d, int k, bool bf16,
                                    const float* y_shared, const float* gate_logit, void* dy_perm,

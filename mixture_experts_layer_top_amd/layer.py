@@ -21,7 +21,7 @@ Two independent choices shape the path:
 
 Paths: "fast" = fused gather + separate16 combine (the benchmarked default,
 deterministic; bf16 layers with d a multiple of 32, the fp32 y_perm
-otherwise and in training); "fast32" = fused gather + separate combine;
+otherwise); "fast32" = fused gather + separate combine;
 "atomic" = fused gather + atomic combine; "reference" = copy gather +
 separate combine.
 
@@ -29,13 +29,14 @@ Training (``train=True``): the forward also keeps the layer-0 projections
 h = x W_gate and u = x W_up (routed and shared) and the router logits, and
 ``backward(dy)`` issues the backward C-ABI calls in reverse order:
 
-    moe_combine_backward -> moe_expert_down_backward -> moe_expert_up_backward
+    moe_combine_backward[_f16] -> moe_expert_down_backward -> moe_expert_up_backward
     -> moe_unpermute -> moe_topk_weights_backward -> moe_linear_backward
     [-> shared experts: moe_expert_down_backward, moe_expert_up_backward,
         moe_linear_backward for the gate]
 
 leaving the gradients in ``self.grads`` (fp32 device tensors).  Training
-needs the deterministic separate combine (y_perm), keeps the backward's
+needs a deterministic separate combine (the combine backward reads the
+forward's rows: y_perm, or its compact form on the "fast" path), keeps the backward's
 intermediates in the layer's storage dtype (bf16 or fp32), and
 always has moe_permute write x_perm: the layer-0 weight gradient reads the
 expert's token rows in order from it (the forward GEMMs still read x
@@ -68,12 +69,11 @@ class MoeLayer:
         self.path = path
         self.gather, self.comb = PATHS[path]
         self.train = train
-        # the compact rows: bf16 layers whose d splits into 32-column segments;
-        # training keeps the fp32 y_perm that moe_combine_backward reads
-        if self.comb == "separate16" and (train or cfg.dtype != "bf16" or cfg.d % 32):
+        # the compact rows: bf16 layers whose d splits into 32-column segments
+        if self.comb == "separate16" and (cfg.dtype != "bf16" or cfg.d % 32):
             self.comb = "separate"
         if train:
-            if self.comb != "separate":
+            if self.comb not in ("separate", "separate16"):
                 raise ValueError("training needs the separate combine")
             keep_logits = True
         self.cfg = cfg
@@ -305,10 +305,17 @@ class MoeLayer:
         R = T * k
         mk = (lambda n: marks(n)) if marks is not None else (lambda n: None)
         gated = bool(self.ns and c.shared_gated)
-        L.moe_combine_backward(dy, self.y_perm, self.inv, self.w, T, d, k, self.dtype,
-                               self.ys if gated else None, self.g_logit if gated else None,
-                               self.dy_perm, self.dw, self.dys if self.ns else None,
-                               self.dgl if gated else None, stream=stream)
+        if self.comb == "separate16":
+            ys_h, ys_s = (self.ys_h, self.ys_s) if gated else (None, None)
+            L.moe_combine_backward_f16(dy, self.y_h, self.y_s, self.inv, self.w, T, d, k,
+                                       self.dtype, ys_h, ys_s, self.g_logit if gated else None,
+                                       self.dy_perm, self.dw, self.dys if self.ns else None,
+                                       self.dgl if gated else None, stream=stream)
+        else:
+            L.moe_combine_backward(dy, self.y_perm, self.inv, self.w, T, d, k, self.dtype,
+                                   self.ys if gated else None, self.g_logit if gated else None,
+                                   self.dy_perm, self.dw, self.dys if self.ns else None,
+                                   self.dgl if gated else None, stream=stream)
         mk("combine_bwd")
         L.moe_expert_down_backward(self.dy_perm, self.offsets, E, R, f, d, self.dtype,
                                    t["W_down"], self.h, self.u, self.a, self.dhu, g["dW_down"],

@@ -177,6 +177,23 @@ def test_backward_validation(lib):
     assert combine_bwd(shared_gate_logit=A) == L.MOE_ERR_INVALID  # gate without its outputs
     assert combine_bwd(dtype=7) == L.MOE_ERR_UNSUPPORTED
     assert combine_bwd(T=0) == L.MOE_OK
+    ch = dict(dy=A, y_h=A, y_s=A, inv=A, topk_w=A, T=16, d=64, k=2, dtype=L.MOE_BF16,
+              ys_h=None, ys_s=None, shared_gate_logit=None, dy_perm=A, dw=A, dy_shared=None,
+              dgate_logit=None)
+    def combine_bwd16(**kw):
+        return L.moe_combine_backward_f16(**{**ch, **kw}, stream=0, check=False)
+    assert combine_bwd16(k=257) == L.MOE_ERR_INVALID
+    assert combine_bwd16(k=20, T=0) == L.MOE_OK
+    assert combine_bwd16(k=0) == L.MOE_ERR_INVALID
+    assert combine_bwd16(y_h=None) == L.MOE_ERR_INVALID
+    assert combine_bwd16(y_s=None) == L.MOE_ERR_INVALID
+    assert combine_bwd16(ys_h=A) == L.MOE_ERR_INVALID        # shared rows without factors
+    assert combine_bwd16(shared_gate_logit=A, dy_shared=A, dgate_logit=A) == L.MOE_ERR_INVALID
+    assert combine_bwd16(dgate_logit=A) == L.MOE_ERR_INVALID  # gradient without a gate
+    assert combine_bwd16(d=72) == L.MOE_ERR_UNSUPPORTED       # not whole 32-column segments
+    assert combine_bwd16(y_s=MIS) == L.MOE_ERR_UNSUPPORTED
+    assert combine_bwd16(dtype=7) == L.MOE_ERR_UNSUPPORTED
+    assert combine_bwd16(T=0, d=72) == L.MOE_OK
     db = dict(dy_perm=A, offsets=A, E=8, rows=32, f=64, d=64, dtype=L.MOE_BF16, W_down=A, h=A,
               u=A, act=A, dhu=A, dW_down=A, workspace=None, ws_bytes=0)
     def down_bwd(**kw):

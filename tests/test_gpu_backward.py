@@ -492,3 +492,72 @@ def test_backward_full_size_sampled(L, name):
         if nrm > 1e-5 or c > 1e-4:
             fails.append(f"dw_s: {nrm:.3e} {c:.3e}")
     assert not fails, fails
+
+
+@pytest.mark.parametrize("T,d,k,shared,dt", [
+    (77, 96, 1, "none", "bf16"), (77, 96, 2, "gated", "bf16"), (130, 2048, 6, "plain", "bf16"),
+    (130, 4128, 8, "gated", "bf16"), (50, 512, 10, "gated", "bf16"), (33, 160, 20, "plain", "f32"),
+    (64, 64, 8, "gated", "f32")])
+def test_combine_backward_compact_rows(L, T, d, k, shared, dt):
+    """moe_combine_backward_f16 against moe_combine_backward over the
+    restored rows (y_h * factor): dy_perm and dy_shared are the same products
+    w dy and g dy, bit for bit; dw and the gate gradient are dot products of
+    the same exact values in another summation order, so both lie within fp32
+    summation error of their fp64 definition.  k of 1..8 (one pass) and
+    above 8 (slot by slot); d of one thread's chunk, of exactly one chunk per
+    thread (2048) and of a ragged second pass (4128)."""
+    log(f"[bwd compact] T={T} d={d} k={k} shared={shared} {dt}")
+    gen = torch.Generator(device="cuda").manual_seed(T * 31 + d + k)
+    R, S = T * k, d // 32
+    dtype = L.MOE_BF16 if dt == "bf16" else L.MOE_F32
+    act = torch.bfloat16 if dt == "bf16" else torch.float32
+    dy = torch.randn(T, d, generator=gen, device="cuda")
+    # compact rows: fp16 values and power-of-two factors 2^-20 .. 2^-6
+    y_h = (torch.rand(R, d, generator=gen, device="cuda") * 6e4 - 3e4).to(torch.float16)
+    y_s = torch.exp2(torch.randint(-20, -5, (R, S), generator=gen, device="cuda").float())
+    y_perm = y_h.float() * y_s.repeat_interleave(32, dim=1)
+    inv = torch.randperm(R, generator=gen, device="cuda").to(torch.int32).reshape(T, k)
+    w = torch.rand(T, k, generator=gen, device="cuda")
+    ys_h = ys_s = ys = gl = None
+    if shared == "gated":
+        ys_h = (torch.rand(T, d, generator=gen, device="cuda") * 6e4 - 3e4).to(torch.float16)
+        ys_s = torch.exp2(torch.randint(-20, -5, (T, S), generator=gen, device="cuda").float())
+        ys = ys_h.float() * ys_s.repeat_interleave(32, dim=1)
+        gl = torch.randn(T, 1, generator=gen, device="cuda")
+    out = {}
+    for name in ("f16", "f32"):
+        o = dict(dy_perm=torch.full((R, d), float("nan"), device="cuda").to(act),
+                 dw=torch.full((T, k), float("nan"), device="cuda"),
+                 dys=torch.full((T, d), float("nan"), device="cuda").to(act)
+                 if shared != "none" else None,
+                 dgl=torch.full((T, 1), float("nan"), device="cuda") if gl is not None else None)
+        if name == "f16":
+            L.moe_combine_backward_f16(dy, y_h, y_s, inv, w, T, d, k, dtype, ys_h, ys_s, gl,
+                                       o["dy_perm"], o["dw"], o["dys"], o["dgl"])
+        else:
+            L.moe_combine_backward(dy, y_perm, inv, w, T, d, k, dtype, ys, gl, o["dy_perm"],
+                                   o["dw"], o["dys"], o["dgl"])
+        torch.cuda.synchronize()
+        out[name] = o
+    assert torch.equal(out["f16"]["dy_perm"], out["f32"]["dy_perm"])
+    if shared != "none":
+        assert torch.equal(out["f16"]["dys"], out["f32"]["dys"])
+    # fp64 definitions and their fp32 summation bound: d 2^-24 sum |terms|
+    dyh, yph, invh = dy.cpu().double(), y_perm.cpu().double(), inv.cpu().long()
+    rows = yph[invh]                                    # [T, k, d]
+    ref = (rows * dyh[:, None, :]).sum(-1)
+    bound = 2 * d * 2.0 ** -24 * (rows * dyh[:, None, :]).abs().sum(-1) + 1e-30
+    for name in ("f16", "f32"):
+        err = float(((out[name]["dw"].cpu().double() - ref).abs() / bound).max())
+        log(f"  dw {name}: max err / bound {err:.3f}")
+        assert err <= 1.0, (name, err)
+    if gl is not None:
+        g = torch.sigmoid(gl.cpu().double())[:, 0]
+        prod = ys.cpu().double() * dyh
+        ref_g = prod.sum(-1) * g * (1 - g)
+        bound_g = (2 * d * 2.0 ** -24 * prod.abs().sum(-1) + 2e-5 * prod.sum(-1).abs()) \
+            * g * (1 - g) + 1e-30
+        for name in ("f16", "f32"):
+            err = float(((out[name]["dgl"].cpu().double()[:, 0] - ref_g).abs() / bound_g).max())
+            log(f"  dgate {name}: max err / bound {err:.3f}")
+            assert err <= 1.0, (name, err)

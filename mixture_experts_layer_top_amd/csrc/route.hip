@@ -25,11 +25,12 @@
 //     each wave holds its tokens' complete logits.
 //   Both walk their K chunks in an order rotated by the workgroup index.
 //
-// Selection and weights: 16 lanes per token, each holding every 16th
-// logit.  The j-th pick is the best (value desc, index asc) strictly below
-// the (j-1)-th pick in that order, so no pick is ever marked; exactly equal
-// logits go to the lower index.  A NaN logit is taken as -inf, so every
-// token gets k distinct experts in [0, E) whatever its logits.
+// Selection and weights: LPT lanes per token (2 to 16, as many as the
+// workgroup's lanes allow), each holding every LPT-th logit.  The j-th pick
+// is the best (value desc, index asc) strictly below the (j-1)-th pick in
+// that order, so no pick is ever marked; exactly equal logits go to the
+// lower index.  A NaN logit is taken as -inf, so every token gets k
+// distinct experts in [0, E) whatever its logits.
 #include "moe_internal.h"
 
 namespace moe {
@@ -56,12 +57,13 @@ struct RouteArgs {
   float* logits_out;
 };
 
-// Reductions over one DPP row (16 lanes): xor 1 and xor 2 inside each quad,
-// then the half-row mirror (lane i <-> 7 - i in each 8-lane half) pairs the
-// two quads of a half and the row mirror (i <-> 15 - i) the two halves.
-// Every step combines two lanes' values with a commutative operation, so all
-// 16 lanes end with the bitwise-same result.  DPP moves run on the vector
-// ALU; the shuffles they replace went through the LDS permute unit.
+// Reductions over a part of a DPP row (2, 4, 8 or all 16 lanes): xor 1
+// and xor 2 inside each quad, then the half-row mirror (lane i <-> 7 - i in
+// each 8-lane half) pairs the two quads of a half and the row mirror
+// (i <-> 15 - i) the two halves.  Every step combines two lanes' values with
+// a commutative operation, so all lanes of the part end with the
+// bitwise-same result.  DPP moves run on the vector ALU; the shuffles they
+// replace went through the LDS permute unit.
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 
 template <int CTRL>
@@ -72,114 +74,155 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
   return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, x)));
 }
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_f<kDppXor1>(x));
-  x = fmaxf(x, dpp_f<kDppXor2>(x));
-  x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
-  return fmaxf(x, dpp_f<kDppMirror>(x));
+
+// Ordered keys of the selection: (value desc, index asc) as one unsigned
+// 64-bit integer, larger = better.  The value's bits map monotonically to
+// an unsigned 32-bit integer (negative values: all bits flipped; others:
+// sign bit set), the index goes below it as 255 - e (E <= 256).  Every
+// valid key is above 0, the key of the padded experts.
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_f<kDppXor1>(x);
-  x += dpp_f<kDppXor2>(x);
-  x += dpp_f<kDppHalfMirror>(x);
-  return x + dpp_f<kDppMirror>(x);
-}
-// the best (value desc, index asc) of the row's (value, index) pairs
-template <int CTRL>
-__device__ __forceinline__ void best_step(float& bv, int& be) {
-  const float ov = dpp_f<CTRL>(bv);
-  const int oe = dpp_i<CTRL>(be);
-  if (ov > bv || (ov == bv && oe < be)) {
-    bv = ov;
-    be = oe;
-  }
-}
-__device__ __forceinline__ void row16_best(float& bv, int& be) {
-  best_step<kDppXor1>(bv, be);
-  best_step<kDppXor2>(bv, be);
-  best_step<kDppHalfMirror>(bv, be);
-  best_step<kDppMirror>(bv, be);
+__device__ __forceinline__ float from_ordered(uint32_t h) {
+  return __builtin_bit_cast(float, (h & 0x80000000u) ? (h & 0x7fffffffu) : ~h);
 }
 
-// Softmax top-k over `ntok` logits rows in LDS: 16 lanes (one DPP row) per
-// token, each holding NV = Ep / 16 of the row's logits in registers (expert
-// q + 16 u for lane q; padded experts hold -inf).  Waves take groups of 4
-// tokens in turn.  The j-th pick is the best (value desc, index asc)
-// strictly below the (j-1)-th pick in that order, found by a per-lane scan
-// and a row reduction.  NaN logits are taken as -inf for the order and the
-// weights.  For k <= 16, lane j keeps pick j and the k picks are written
-// together at the end (divided by their sum with renormalisation); larger k
-// writes each pick as it is found and divides afterwards.
-template <int NV>
+// Reductions over LPT consecutive lanes (LPT a power of two up to 16: the
+// steps above taken as far as needed)
+template <int LPT>
+__device__ __forceinline__ float part_max(float x) {
+  if (LPT >= 2) x = fmaxf(x, dpp_f<kDppXor1>(x));
+  if (LPT >= 4) x = fmaxf(x, dpp_f<kDppXor2>(x));
+  if (LPT >= 8) x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+  if (LPT >= 16) x = fmaxf(x, dpp_f<kDppMirror>(x));
+  return x;
+}
+template <int LPT>
+__device__ __forceinline__ float part_sum(float x) {
+  if (LPT >= 2) x += dpp_f<kDppXor1>(x);
+  if (LPT >= 4) x += dpp_f<kDppXor2>(x);
+  if (LPT >= 8) x += dpp_f<kDppHalfMirror>(x);
+  if (LPT >= 16) x += dpp_f<kDppMirror>(x);
+  return x;
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t key_max_step(uint64_t x) {
+  const uint32_t lo = (uint32_t)dpp_i<CTRL>((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)dpp_i<CTRL>((int)(uint32_t)(x >> 32));
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > x ? o : x;
+}
+template <int LPT>
+__device__ __forceinline__ uint64_t part_max_key(uint64_t x) {
+  if (LPT >= 2) x = key_max_step<kDppXor1>(x);
+  if (LPT >= 4) x = key_max_step<kDppXor2>(x);
+  if (LPT >= 8) x = key_max_step<kDppHalfMirror>(x);
+  if (LPT >= 16) x = key_max_step<kDppMirror>(x);
+  return x;
+}
+
+// Softmax top-k over `ntok` logits rows in LDS: LPT lanes per token, each
+// holding NV = Ep / LPT of the row's logits in registers (expert q + LPT u
+// for lane q); waves take groups of 64 / LPT tokens in turn.  The j-th pick
+// is the largest key strictly below the (j-1)-th pick's: a per-lane scan of
+// NV keys and a reduction over the token's lanes.  NaN logits are taken as
+// -inf for the order and the weights.  For k <= 16, lane q keeps the picks
+// j = q, q + LPT, ... and the k picks are written together at the end
+// (divided by their sum with renormalisation); larger k writes each pick as
+// it is found and divides afterwards.  Callers choose LPT so that the
+// workgroup's lanes cover its tokens: fewer lanes per token means fewer
+// reduction steps per pick and more tokens at once.
+template <int NV, int LPT>
 __device__ __forceinline__ void select_and_weigh(const float* ll, int lstride, const RouteArgs& a,
                                                  int t_base, int ntok) {
+  static_assert(LPT == 1 || LPT == 2 || LPT == 4 || LPT == 8 || LPT == 16, "lanes per token");
+  constexpr int TPW = 64 / LPT;              // tokens per wave and pass
+  constexpr int KPL = (16 + LPT - 1) / LPT;  // picks a lane keeps (k <= 16)
   const int lane = threadIdx.x & 63;
   const int nwaves = blockDim.x >> 6;
-  const int q = lane & 15;
+  const int q = lane & (LPT - 1);
   const int E = a.E, k = a.k;
-  for (int g0 = (threadIdx.x >> 6) * 4; g0 < ntok; g0 += nwaves * 4) {
-    const int tt = g0 + (lane >> 4);
+  for (int g0 = (threadIdx.x >> 6) * TPW; g0 < ntok; g0 += nwaves * TPW) {
+    const int tt = g0 + lane / LPT;
     const int t = t_base + tt;
     const bool live = tt < ntok && t < a.T;
     const float* row = ll + (tt < ntok ? tt : 0) * lstride;
     float v[NV];
+    uint64_t key[NV];
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
-      const int e = q + 16 * u;
+      const int e = q + LPT * u;
       const float l = (e < E) ? row[e] : -INFINITY;
       v[u] = (l == l) ? l : -INFINITY;  // NaN ranks with -inf
+      key[u] = (e < E) ? ((uint64_t)ordered_bits(v[u]) << 32) | (uint32_t)(255 - e) : 0ull;
     }
     // softmax denominator relative to the row max
     float m = -INFINITY;
 #pragma unroll
     for (int u = 0; u < NV; ++u) m = fmaxf(m, v[u]);
-    m = row16_max(m);
+    m = part_max<LPT>(m);
     float sum = 0.f;
 #pragma unroll
-    for (int u = 0; u < NV; ++u) sum += (q + 16 * u < E) ? __expf(v[u] - m) : 0.f;
-    sum = row16_sum(sum);
+    for (int u = 0; u < NV; ++u) sum += (q + LPT * u < E) ? __expf(v[u] - m) : 0.f;
+    sum = part_sum<LPT>(sum);
 
-    float pv = INFINITY, sel = 0.f;
-    int pe = -1;
-    int my_e = 0;
-    float my_ex = 0.f;
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
+    uint64_t prev = ~0ull;
+    float sel = 0.f;
+    int my_e[KPL];
+    float my_ex[KPL];
 #pragma unroll
-      for (int u = 0; u < NV; ++u) {
-        const int e = q + 16 * u;
-        const bool below = (v[u] < pv) || (v[u] == pv && e > pe);
-        const bool better = (v[u] > bv) || (v[u] == bv && e < be);
-        if (e < E && below && better) {
-          bv = v[u];
-          be = e;
-        }
-      }
-      row16_best(bv, be);
-      pv = bv;
-      pe = be;
-      const float ex = __expf(bv - m);
+    for (int s = 0; s < KPL; ++s) {
+      my_e[s] = 0;
+      my_ex[s] = 0.f;
+    }
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int u = 0; u < NV; ++u)
+        if (key[u] < prev && key[u] > best) best = key[u];
+      best = part_max_key<LPT>(best);
+      prev = best;
+      const int be = 255 - (int)(uint32_t)best;
+      const float ex = __expf(from_ordered((uint32_t)(best >> 32)) - m);
       sel += ex;
       if (k <= 16) {
-        if (q == j) {
-          my_e = be;
-          my_ex = ex;
-        }
+#pragma unroll
+        for (int s = 0; s < KPL; ++s)
+          if (j == q + LPT * s) {
+            my_e[s] = be;
+            my_ex[s] = ex;
+          }
       } else if (q == 0 && live) {
         a.idx[(size_t)t * k + j] = be;
         a.w[(size_t)t * k + j] = a.renorm ? ex : ex / sum;
       }
     }
     if (k <= 16) {
-      if (q < k && live) {
-        a.idx[(size_t)t * k + q] = my_e;
-        a.w[(size_t)t * k + q] = a.renorm ? my_ex / sel : my_ex / sum;
+      if (live) {
+#pragma unroll
+        for (int s = 0; s < KPL; ++s) {
+          const int j = q + LPT * s;
+          if (j < k) {
+            a.idx[(size_t)t * k + j] = my_e[s];
+            a.w[(size_t)t * k + j] = a.renorm ? my_ex[s] / sel : my_ex[s] / sum;
+          }
+        }
       }
     } else if (a.renorm && q == 0 && live) {
       for (int j = 0; j < k; ++j) a.w[(size_t)t * k + j] = a.w[(size_t)t * k + j] / sel;
     }
   }
+}
+
+// Lanes per token for a workgroup of `threads` lanes routing `tokens` tokens
+// over Ep (padded) experts: every lane busy where the tokens allow, at most
+// 16 (one DPP row) and at most 32 keys per lane.
+constexpr int lanes_per_token(int threads, int tokens, int Ep) {
+  int l = threads / tokens;
+  l = l < 1 ? 1 : (l > 16 ? 16 : l);
+  while (Ep / l > 32) l *= 2;  // at most 32 keys per lane
+  return l > 16 ? 16 : l;
 }
 
 __device__ __forceinline__ void write_logits(const float* ll, int lstride, const RouteArgs& a,
@@ -439,7 +482,8 @@ __global__ __launch_bounds__(NWV * 64) void route_bf16_kernel(RouteArgs a) {
   }
   __syncthreads();
   write_logits(ll, ls, a, t_base, TW);
-  select_and_weigh<NB>(ll, ls, a, t_base, TW);
+  constexpr int LPT = lanes_per_token(NT, TW, Ep);
+  select_and_weigh<Ep / LPT, LPT>(ll, ls, a, t_base, TW);
 }
 
 // fp32 path (small layers): plain sequential FMA dot products, 64 tokens
@@ -465,7 +509,8 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(RouteArgs a) {
   }
   __syncthreads();
   write_logits(ll, ls, a, t_base, kTok);
-  select_and_weigh<NV>(ll, ls, a, t_base, kTok);
+  constexpr int LPT = lanes_per_token(kThreads, kTok, NV * 16);
+  select_and_weigh<NV * 16 / LPT, LPT>(ll, ls, a, t_base, kTok);
 }
 
 // ------------------------------------------------------------------------
@@ -626,7 +671,8 @@ __global__ __launch_bounds__(NWV * 64) void route_bf16_sw_kernel(RouteArgs a) {
     }
   __syncthreads();
   write_logits(ll, ls, a, t_base, TB);
-  select_and_weigh<NB>(ll, ls, a, t_base, TB);
+  constexpr int LPT = lanes_per_token(NWV * 64, TB, Ep);
+  select_and_weigh<Ep / LPT, LPT>(ll, ls, a, t_base, TB);
 }
 
 // Raise kernel KERN's dynamic LDS limit to `bytes`, once per device: a

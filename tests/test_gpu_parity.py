@@ -544,12 +544,15 @@ def test_combine_more_than_eight_slots(L, path, d):
 
 
 @pytest.mark.parametrize("E,k,T,d", [(8, 2, 16400, 256), (16, 4, 16390, 512), (24, 3, 32770, 128),
-                                     (40, 5, 32768, 192), (64, 6, 33000, 64)])
+                                     (40, 5, 32768, 192), (64, 6, 33000, 64), (64, 4, 32800, 1024),
+                                     (64, 8, 9000, 256), (56, 4, 8200, 384)])
 def test_route_long_batches(L, E, k, T, d):
     """Batches long enough for the router's shared-W_r kernel (a workgroup
-    of 16 tokens per wave on every compute unit): routing exact on the
-    GPU's logits and within the fp32 bound of the fp64 logits, dispatch
-    bit-exact; ragged last workgroups (T not a multiple of its tokens)."""
+    of 16 tokens per wave on every compute unit) and, at 56 and 64 experts,
+    for the 64- and 32-token workgroups of the K-splitting kernel (selection
+    with 4 and 8 lanes per token): routing exact on the GPU's logits and
+    within the fp32 bound of the fp64 logits, dispatch bit-exact; ragged last
+    workgroups (T not a multiple of its tokens)."""
     cfg = small_cfg(E=E, k=k, T=T, d=d, f=64)
     log(f"[edge] long-batch route T={T} d={d} E={E} k={k}")
     layer = make_layer(cfg, seed=30 + E, device="cuda")

@@ -38,8 +38,15 @@
 //     and consecutive tiles land on one XCD (its L2); an expert's rows are
 //     dealt to its M tiles in balanced 16-row blocks; the last round's tiles
 //     are split along K when it is mostly idle, and a second launch adds the
-//     parts in order (deterministic).
+//     parts in order (deterministic);
+//   * wide items (K of 2048 and more): an expert whose last rows fill at most
+//     half a tile takes whole 256-row tiles for the rest, and those last rows
+//     as one item per pair of N panels, both groups on the same rows, X on
+//     one panel and Y on the next (rings of 2, 16 + 64 KiB a stage): a
+//     nearly empty tile per panel becomes half an item.  Every output
+//     element sees the same K order either way (same bits).
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -92,6 +99,7 @@ struct GemmArgs {
   int n_cu;                 // compute units the tiles are spread over
   int fixup;                // 0: main pass; 1: sum the split tiles' partials
   int nt_y;                 // layer-1 output stores non-temporal (larger than the last-level cache)
+  int wide_rem;             // 1: an expert's last rows, when at most BM / 2, form wide items
 };
 
 // Compact layer-1 output: IEEE fp16 with one power-of-two factor per
@@ -146,7 +154,8 @@ __device__ __forceinline__ void store_seg_f16(const float* src, uint16_t* dst, f
 
 struct TileInfo {
   int e, row0, row_end, n_t, m_t;
-  int nb;  // ping-pong kernel: 16-row blocks in the tile (<= BM / 16)
+  int nb;     // ping-pong kernel: 16-row blocks in the tile (<= BM / 16)
+  bool wide;  // ping-pong kernel: at most BM / 2 rows over N panels n_t and n_t + 1
   bool ok;
 };
 
@@ -674,9 +683,13 @@ struct Work {
 // One pass over the offsets (4 experts per lane, as in locate_tile): the
 // per-expert tile counts, their wave prefix sum (the total and each
 // expert's first tile), the split, this block's work item and its tile.
+// WIDE_OK: the enumeration may form wide items (when p.wide_rem is set);
+// without it their code is left out (it runs in every tile's prologue).
+template <bool WIDE_OK>
 __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   const int lane = threadIdx.x & 63;
   int cnt_tiles[4], mt[4], offe[4], rows_e[4];
+  bool wide_e[4];
   int lane_sum = 0;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -690,7 +703,12 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
     mt[u] = m;
     offe[u] = o;
     rows_e[u] = c;
-    cnt_tiles[u] = m * p.tiles_n;
+    // an expert walked in one pass whose last rows fill at most half a tile:
+    // floor(c / BM) full tiles per N panel, and its last rows as one wide
+    // item per pair of panels (ceil(tn / 2) of them)
+    const int rem = c - (c / BM) * BM;
+    wide_e[u] = WIDE_OK && p.wide_rem && rem > 0 && 2 * rem <= BM && m <= p.m_group_min;
+    cnt_tiles[u] = wide_e[u] ? (c / BM) * p.tiles_n + (p.tiles_n + 1) / 2 : m * p.tiles_n;
     lane_sum += cnt_tiles[u];
   }
   const int incl = wave_incl_sum(lane_sum);
@@ -742,7 +760,7 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   if (w.tile < 0) return w;
   // the expert holding tile w.tile, from the same prefix sums
   int start = incl - lane_sum;
-  int hit_e = -1, hit_start = 0, hit_mt = 0, hit_off = 0, hit_rows = 0;
+  int hit_e = -1, hit_start = 0, hit_mt = 0, hit_off = 0, hit_rows = 0, hit_wide = 0;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     if (w.tile >= start && w.tile < start + cnt_tiles[u]) {
@@ -751,6 +769,7 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
       hit_mt = mt[u];
       hit_off = offe[u];
       hit_rows = rows_e[u];
+      hit_wide = wide_e[u] ? 1 : 0;
     }
     start += cnt_tiles[u];
   }
@@ -766,6 +785,33 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   // second, dependent read of the offsets
   const int c_e = __builtin_amdgcn_readlane(hit_rows, src);
   const int local = w.tile - tstart;
+  ti.wide = false;
+  if (WIDE_OK && __builtin_amdgcn_readlane(hit_wide, src)) {
+    // items per pair of N panels (2j, 2j + 1): the mf full M tiles of panel
+    // 2j, those of panel 2j + 1, then the wide item of the last rows (a last
+    // odd panel: its mf tiles, then a wide item with no second panel)
+    const int mf = c_e / BM;
+    const int per = 2 * mf + 1;
+    const int j = local / per, r = local - j * per;
+    if (r < mf || (r < 2 * mf && 2 * j + 1 < p.tiles_n)) {
+      const int second = r >= mf ? 1 : 0;
+      ti.n_t = 2 * j + second;
+      ti.m_t = r - second * mf;
+      ti.nb = BM / 16;
+      ti.row0 = toff + BM * ti.m_t;
+      ti.row_end = ti.row0 + BM;
+    } else {
+      ti.wide = true;
+      ti.n_t = 2 * j;
+      ti.m_t = mf;
+      ti.row0 = toff + BM * mf;
+      ti.row_end = toff + c_e;
+      ti.nb = cdiv(ti.row_end - ti.row0, 16);
+    }
+    ti.ok = true;
+    w.ok = true;
+    return w;
+  }
   // A large expert's M tiles are walked in ng balanced groups of at most
   // m_group tiles (the first tmt % ng groups hold one tile more); a group
   // covers all N panels, M fastest inside each panel, before the next, so
@@ -806,22 +852,27 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   return w;
 }
 
-// FIX = false: the main pass; FIX = true: the fixup pass of the tail split
-// (no K loop: the accumulators are the sum of the split items' partials).
-template <bool UP, int PBK, bool FIX>
-__global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p) {
+// One work item of the ping-pong kernel.  FIX = false: the main pass; FIX =
+// true: the fixup pass of the tail split (no K loop: the accumulators are the
+// sum of the split items' partials).  WIDE = false: a tile of up to 256 rows
+// x one N panel, group X on its first ceil(nb / 2) 16-row blocks, group Y on
+// the rest.  WIDE = true: a wide item, up to 128 rows x two N panels, both
+// groups on the same rows, X on panel n_t and Y on panel n_t + 1; its stage
+// is an A slot of 128 rows (16 KiB) and a B slot of both panels (64 KiB),
+// rings of 2 (160 KiB); X issues the A loads and its panel's B loads, Y its
+// panel's B loads.  A separate instantiation, so that the whole tiles' loop
+// carries no test for it.
+template <bool UP, int PBK, bool FIX, bool WIDE>
+__device__ __forceinline__ void pp_tile(const GemmArgs p, const Work wk, char* lds) {
   using namespace pp;
   using C = Cfg<PBK>;
-  constexpr int SLOT = C::SLOT, HALF = C::HALF, RA = C::RA, RB = C::RB, KS = C::KS, LD = C::LD;
-  constexpr int B_RING = RA * SLOT;  // B slots start after the A slots
-  // the fixup pass uses LDS only for the epilogue's per-wave staging (at
-  // most 16 rows x 68 floats per wave): sized so that several of its short
-  // workgroups share a compute unit
-  constexpr int FIX_LDS = NW * 16 * 68 * 4;
-  __shared__ __attribute__((aligned(1024))) char lds[FIX ? FIX_LDS : C::LDS_BYTES];
-
-  const Work wk = assign_work(p, blockIdx.x, PBK);
-  if (!wk.ok) return;
+  constexpr int SLOT = C::SLOT, HALF = C::HALF, KS = C::KS, LD = C::LD;
+  constexpr int RA = WIDE ? 2 : C::RA, RB = WIDE ? 2 : C::RB;
+  constexpr int SLOT_A = WIDE ? SLOT / 2 : SLOT;  // A stage: 128 or 256 rows
+  constexpr int SLOT_B = WIDE ? 2 * SLOT : SLOT;  // B stage: two panels or one
+  constexpr int B_RING = RA * SLOT_A;             // B slots start after the A slots
+  static_assert(RA * SLOT_A + RB * SLOT_B <= C::LDS_BYTES, "LDS");
+  constexpr int LDA = WIDE ? LD / 2 : LD;         // A loads per X wave per stage
   const TileInfo& ti0 = wk.ti;
   // the tile is the same for every lane: keep it in scalar registers
   const int t_e = __builtin_amdgcn_readfirstlane(ti0.e);
@@ -837,11 +888,13 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool X = wave < 4;       // leading group: LDS rows 0-127, issues the A loads
   const int wg = wave & 3;       // wave inside its group
-  const int my_nb = X ? t_bx : t_nb - t_bx;    // blocks this wave computes (0..MI)
-  const int grow0 = X ? 0 : 16 * t_bx;         // the group's first row inside the tile
+  const int my_nb = WIDE ? t_nb : (X ? t_bx : t_nb - t_bx);  // blocks this wave computes (0..MI)
+  const int grow0 = WIDE ? 0 : (X ? 0 : 16 * t_bx);          // the group's first row inside the tile
   const int grow_end = min(t_row_end, t_row0 + grow0 + 16 * my_nb);  // its row bound
   const int K = p.K, N = p.N;
-  const int n0 = t_n * (UP ? 128 : 256);
+  // the group's N panel (wide items: Y takes the next one; past the last
+  // panel its loads read valid columns and nothing is stored)
+  const int n0 = (t_n + (WIDE && !X ? 1 : 0)) * (UP ? 128 : 256);
   const uint32_t lds0 = lds_addr_of(lds);
   const int k_begin = __builtin_amdgcn_readfirstlane(wk.k_begin);
   const int k_end = __builtin_amdgcn_readfirstlane(wk.k_end);
@@ -858,23 +911,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
   uint32_t ld_off[LD];  // X: A byte offsets at k_begin; Y: B byte offsets (q < 4)
   const char* ld_base0; // stage-0 scalar base
   const int b_half = wg >> 1;
-  if (X) {
-#pragma unroll
-    for (int q = 0; q < LD; ++q) {
-      const int row = (wg * LD + q) * C::RPL + lane / C::CPR;  // LDS row
-      const int chunk = (lane % C::CPR) ^ a_swz16<PBK>(row);
-      // LDS rows 0-127 hold group X's blocks, 128-255 group Y's
-      const int j = row & 127;
-      const int gnb = row < 128 ? t_bx : t_nb - t_bx;
-      int r = t_row0 + (row < 128 ? 0 : 16 * t_bx) + j;
-      // rows past the group's blocks or the expert's rows read a valid row;
-      // their results are never stored
-      if (j >= 16 * gnb || r >= t_row_end) r = t_row0;
-      const int src_row = p.gather ? p.gather[r] : r;
-      ld_off[q] = ((uint32_t)src_row * (uint32_t)K + (uint32_t)(k_begin + chunk * 8)) * 2u;
-    }
-    ld_base0 = uniform_ptr(p.A);
-  } else {
+  // B offsets of the group's panel (whole tiles: group Y's loads)
+  auto b_offsets = [&]() {
     const bf16_t* b_mat = UP ? (b_half ? p.B1 : p.B0) : p.B0;
     const int n0h = UP ? n0 : n0 + b_half * 128;
 #pragma unroll
@@ -887,20 +925,56 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
     }
     ld_base0 = uniform_ptr(b_mat + (size_t)t_e * K * N +
                            (size_t)(k_begin + (PBK / 2) * (wg & 1)) * N);
+  };
+  // A offsets (X): load j = LDA wg + q fills LDS rows RPL j .. RPL (j + 1) - 1
+  auto a_offset = [&](int q) {
+    const int row = (wg * LDA + q) * C::RPL + lane / C::CPR;  // LDS row
+    const int chunk = (lane % C::CPR) ^ a_swz16<PBK>(row);
+    // LDS rows 0-127 hold group X's blocks, 128-255 group Y's (wide items:
+    // rows 0-127 only, the blocks of both)
+    const int j = row & 127;
+    const int gnb = WIDE ? t_nb : (row < 128 ? t_bx : t_nb - t_bx);
+    int r = t_row0 + ((WIDE || row < 128) ? 0 : 16 * t_bx) + j;
+    // rows past the group's blocks or the expert's rows read a valid row;
+    // their results are never stored
+    if (j >= 16 * gnb || r >= t_row_end) r = t_row0;
+    const int src_row = p.gather ? p.gather[r] : r;
+    return ((uint32_t)src_row * (uint32_t)K + (uint32_t)(k_begin + chunk * 8)) * 2u;
+  };
+  uint32_t a_off[LDA];  // wide items: X's A byte offsets (its ld_off are B's)
+  const char* a_base0 = nullptr;
+  if constexpr (!WIDE) {
+    if (X) {
+#pragma unroll
+      for (int q = 0; q < LD; ++q) ld_off[q] = a_offset(q);
+      ld_base0 = uniform_ptr(p.A);
+    } else {
+      b_offsets();
+    }
+  } else {
+    if (X) {
+#pragma unroll
+      for (int q = 0; q < LDA; ++q) a_off[q] = a_offset(q);
+      a_base0 = uniform_ptr(p.A);
+    }
+    b_offsets();
   }
   auto issue_a = [&](int kt, int slot, int q) {
-    const uint32_t dst = lds0 + (uint32_t)(slot * SLOT + (wg * LD + q) * 1024);
-    lds_dma16_s(ld_off[q], ld_base0 + (size_t)kt * PBK * 2, dst);
+    const uint32_t dst = lds0 + (uint32_t)(slot * SLOT_A + (wg * LDA + q) * 1024);
+    if constexpr (WIDE) lds_dma16_s(a_off[q], a_base0 + (size_t)kt * PBK * 2, dst);
+    else lds_dma16_s(ld_off[q], ld_base0 + (size_t)kt * PBK * 2, dst);
   };
+  // wide items: the group's panel is the first or the second half of the B slot
+  const int b_panel = (WIDE && !X) ? SLOT : 0;
   auto issue_b = [&](int kt, int slot, int q) {
-    const uint32_t dst = lds0 + (uint32_t)(B_RING + slot * SLOT + (wg * LD + q) * 1024);
+    const uint32_t dst = lds0 + (uint32_t)(B_RING + slot * SLOT_B + b_panel + (wg * LD + q) * 1024);
     const char* base = ld_base0 + ((size_t)kt * PBK + (size_t)(16 * (q >> 2))) * N * 2;
     lds_dma16_s(ld_off[q], uniform_ptr(base), dst);
   };
 
   // ---- fragment read offsets (bytes inside a stage slot)
   const int l15 = lane & 15, g = lane >> 4;
-  const int wrow0 = X ? 0 : 128;
+  const int wrow0 = (WIDE || X) ? 0 : 128;
   const int a_s = a_swz16<PBK>(l15);
   const int a_rd0 = (wrow0 + l15) * (PBK * 2) + ((g ^ a_s) << 4);        // K step 0
   const int a_rd1 = (wrow0 + l15) * (PBK * 2) + (((g + 4) ^ a_s) << 4);  // K step 1 (PBK = 64)
@@ -924,8 +998,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
   // memory phase: read the stage's fragments (A slot sa, B slot sb), issue
   // this wave's loads of stage ld_kt into slot ld_slot, wait for the reads
   auto memory = [&](int sa, int sb, int ld_kt, int ld_slot) {
-    const char* As = lds + sa * SLOT;
-    const char* Bs = lds + B_RING + sb * SLOT;
+    const char* As = lds + sa * SLOT_A;
+    const char* Bs = lds + B_RING + sb * SLOT_B + b_panel;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
@@ -944,10 +1018,19 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
       // the loads after the reads of each K step (half of them each when
       // there are two)
       if (ld_kt < nk) {
+        if constexpr (WIDE) {
+          if (X) {
 #pragma unroll
-        for (int q = ks * (LD / KS); q < (ks + 1) * (LD / KS); ++q) {
-          if (X) issue_a(ld_kt, ld_slot, q);
-          else issue_b(ld_kt, ld_slot, q);
+            for (int q = ks * (LDA / KS); q < (ks + 1) * (LDA / KS); ++q) issue_a(ld_kt, ld_slot, q);
+          }
+#pragma unroll
+          for (int q = ks * (LD / KS); q < (ks + 1) * (LD / KS); ++q) issue_b(ld_kt, ld_slot, q);
+        } else {
+#pragma unroll
+          for (int q = ks * (LD / KS); q < (ks + 1) * (LD / KS); ++q) {
+            if (X) issue_a(ld_kt, ld_slot, q);
+            else issue_b(ld_kt, ld_slot, q);
+          }
         }
       }
     }
@@ -976,11 +1059,17 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
   if (FIX) {
     // no K loop
   } else if (X) {
-    // prologue: A(0) .. A(RA - 2); wait for A(0)
-    for (int s = 0; s < RA - 1 && s < nk; ++s)
+    // prologue: A(0) .. A(RA - 2) (wide items: with the panel's B); wait for A(0)
+    for (int s = 0; s < RA - 1 && s < nk; ++s) {
 #pragma unroll
-      for (int q = 0; q < LD; ++q) issue_a(s, s, q);
-    wait_groups<LD>(min(RA - 2, nk - 1));
+      for (int q = 0; q < LDA; ++q) issue_a(s, s, q);
+      if (WIDE) {
+#pragma unroll
+        for (int q = 0; q < LD; ++q) issue_b(s, s, q);
+      }
+    }
+    if (WIDE) wait_vmcnt<0>();  // rings of 2: stage 0 is everything issued
+    else wait_groups<LD>(min(RA - 2, nk - 1));
     __builtin_amdgcn_s_barrier();
     int sa = 0, sb = 0;
     for (int s = 0; s < nk; ++s) {
@@ -989,7 +1078,9 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
       __builtin_amdgcn_s_barrier();
       compute();                                  // phase 2s + 1
       // A(s + 1) has landed once the later stages' loads are all that remain
-      wait_groups<LD>(min(RA - 2, nk - 2 - s));
+      // (wide items: with the panel's B(s + 1), everything outstanding)
+      if (WIDE) wait_vmcnt<0>();
+      else wait_groups<LD>(min(RA - 2, nk - 2 - s));
       __builtin_amdgcn_s_barrier();
       sa = sa == RA - 1 ? 0 : sa + 1;
       sb = sb == RB - 1 ? 0 : sb + 1;
@@ -999,17 +1090,24 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
     for (int s = 0; s < RB - 1 && s < nk; ++s)
 #pragma unroll
       for (int q = 0; q < LD; ++q) issue_b(s, s, q);
-    wait_groups<LD>(min(RB - 2, nk - 1));
+    if (WIDE) wait_vmcnt<0>();
+    else wait_groups<LD>(min(RB - 2, nk - 1));
     __builtin_amdgcn_s_barrier();
     int sa = 0, sb = 0;
     for (int s = 0; s < nk; ++s) {
-      if (s > 0) compute();  // phase 2s: stage s - 1
+      if (s > 0) {
+        compute();  // phase 2s: stage s - 1
+        // wide items: only this group reads its panel, and it reads B(s) in
+        // phase 2s + 1: its loads (issued in phase 2s - 1) are awaited here
+        if (WIDE) wait_vmcnt<0>();
+      }
       __builtin_amdgcn_s_barrier();
       // phase 2s + 1: read stage s, load B(s + RB - 1) into the slot of stage
-      // s - 1; then B(s + 1) must have landed
+      // s - 1; then (whole tiles: X reads B(s + 1) next phase) B(s + 1) must
+      // have landed
       const int lb = sb == 0 ? RB - 1 : sb - 1;
       memory(sa, sb, s + RB - 1, lb);
-      wait_groups<LD>(min(RB - 2, nk - 2 - s));
+      if (!WIDE) wait_groups<LD>(min(RB - 2, nk - 2 - s));
       __builtin_amdgcn_s_barrier();
       sa = sa == RA - 1 ? 0 : sa + 1;
       sb = sb == RB - 1 ? 0 : sb + 1;
@@ -1154,6 +1252,29 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p
   }
 }
 
+// FIX = false: the main pass; FIX = true: the fixup pass of the tail split.
+// WIDE_OK: the launch may hold wide items (p.wide_rem = 1); without them the
+// kernel holds no wide-item code at all (its presence alone changes the
+// register assignment of the whole tiles' code: 0.5-0.8% on a short K loop).
+template <bool UP, int PBK, bool FIX, bool WIDE_OK>
+__global__ __launch_bounds__(512, 1) void grouped_gemm_bf16_pp_kernel(GemmArgs p) {
+  using C = pp::Cfg<PBK>;
+  // the fixup pass uses LDS only for the epilogue's per-wave staging (at
+  // most 16 rows x 68 floats per wave): sized so that several of its short
+  // workgroups share a compute unit
+  constexpr int FIX_LDS = pp::NW * 16 * 68 * 4;
+  __shared__ __attribute__((aligned(1024))) char lds[FIX ? FIX_LDS : C::LDS_BYTES];
+  const Work wk = assign_work<WIDE_OK>(p, blockIdx.x, PBK);
+  if (!wk.ok) return;
+  if constexpr (WIDE_OK) {
+    if (wk.ti.wide) {
+      pp_tile<UP, PBK, FIX, true>(p, wk, lds);
+      return;
+    }
+  }
+  pp_tile<UP, PBK, FIX, false>(p, wk, lds);
+}
+
 // ------------------------------------------------------------------------
 // fp32 path (small layers): one thread per output element, sequential FMA.
 // ------------------------------------------------------------------------
@@ -1221,6 +1342,8 @@ constexpr int UP_WN = 4, UP_BNA = 256, DN_WN = 4, DN_BNA = 256;
 // kMGroupMB of A rows, each pass covering all N panels (its rows are then
 // re-read from the last-level cache, not HBM)
 constexpr long long kMGroupMB = 32, kMGroupMinMB = 64;
+// Wide items (see assign_work) from this K on
+constexpr int kWideMinK = 2048;
 
 int num_cus() {
   static int cached[64] = {0};
@@ -1261,6 +1384,9 @@ hipError_t launch_gemm(GemmArgs& p, int rows, int E, int ncols, unsigned long lo
     // from the device offsets; without a workspace there is none)
     p.n_cu = num_cus();
     p.fixup = 0;
+    // wide items where the K loop is long enough to carry their rings of
+    // two (measured: with K = 1408, 22 stages, they cost 2.4%)
+    p.wide_rem = p.K >= kWideMinK ? 1 : 0;
     // a y_perm beyond the 256 MB last-level cache is streamed past it (the
     // combine re-reads it from HBM either way); a smaller one stays cached
     // for the combine (DeepSeek shape, 1.6 GB: +2%; Mixtral, 134 MB: cached)
@@ -1268,13 +1394,19 @@ hipError_t launch_gemm(GemmArgs& p, int rows, int E, int ncols, unsigned long lo
              (p.y_h && (unsigned long long)rows * ncols * 2 > (256ull << 20));
     if (ws_bytes < pp_part_bytes(p.n_cu)) p.part = nullptr;
     const long long grid_pp = grid + (p.part ? p.n_cu : 0);
-    hipLaunchKernelGGL((grouped_gemm_bf16_pp_kernel<UP, 64, false>),
-                       dim3((unsigned)grid_pp), dim3(64 * pp::NW), 0, s, p);
-    if (p.part) {
-      p.fixup = 1;
-      hipLaunchKernelGGL((grouped_gemm_bf16_pp_kernel<UP, 64, true>),
-                         dim3((unsigned)(p.n_cu / 2 * FIXQ)), dim3(64 * pp::NW), 0, s, p);
-    }
+    // both passes derive the same items, so they take the same instantiation
+    auto launch = [&](auto wide_ok) {
+      constexpr bool W = decltype(wide_ok)::value;
+      hipLaunchKernelGGL((grouped_gemm_bf16_pp_kernel<UP, 64, false, W>),
+                         dim3((unsigned)grid_pp), dim3(64 * pp::NW), 0, s, p);
+      if (p.part) {
+        p.fixup = 1;
+        hipLaunchKernelGGL((grouped_gemm_bf16_pp_kernel<UP, 64, true, W>),
+                           dim3((unsigned)(p.n_cu / 2 * FIXQ)), dim3(64 * pp::NW), 0, s, p);
+      }
+    };
+    if (p.wide_rem) launch(std::true_type{});
+    else launch(std::false_type{});
     return hipGetLastError();
   }
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<UP, WM, WN, BNA>), dim3((unsigned)grid),

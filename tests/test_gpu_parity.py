@@ -684,3 +684,105 @@ def test_compact_rows_keep_nan_without_losing_their_segment(L):
     # the segment holding the NaN column is as precise as its neighbours
     near = (y16[:, :32] - y32[:, :32]).abs()[ok[:, :32]]
     assert float(near.max()) <= 2.0 ** -11 * fmax * 1.000001
+
+
+def _wide_pads(counts):
+    """Rows to add to each expert so that its last rows exceed half a tile
+    (200 of 256): every row of the expert then sits in a whole tile."""
+    pads = []
+    for c in counts:
+        rem = c % 256
+        pads.append(200 - rem if 0 < rem <= 128 else 0)
+    return pads
+
+
+@pytest.mark.parametrize("counts,d,f", [
+    ([300, 44, 0, 128, 129, 256, 700, 1], 2112, 2176),
+    ([1057, 986, 1030, 1010], 2048, 2048),
+    ([17, 5, 96], 2048, 2176)])
+def test_gemm_wide_items_match_whole_tiles(L, counts, d, f):
+    """An expert whose last rows fill at most half a 256-row tile runs them
+    as wide items (those rows over two N panels, one per wave group). Every
+    output element takes the same K order as in a whole tile, so the same
+    rows give the same bits when the expert is padded (200 rows past its
+    last whole tile) so that they fall in whole tiles instead: layer 0 (bf16
+    SwiGLU output, rows gathered from x) and layer 1 (fp32 rows and compact
+    rows), K of at least 2048 (wide items are used from there), with odd and
+    partial panel counts (17 and 9 panels: a wide item with no second
+    panel). With the workspace (every item split along K, the fixup pass
+    finishing the wide items too) the results stay within fp32 summation
+    error of the unsplit ones."""
+    log(f"[edge] wide items counts={counts} d={d} f={f}")
+    E = len(counts)
+    dev = "cuda"
+    gen = torch.Generator(device=dev).manual_seed(sum(counts) + d + f)
+    bf = torch.bfloat16
+    T = 3000
+    x = torch.randn(T, d, generator=gen, device=dev).to(bf)
+    Wg = (torch.randn(E, d, f, generator=gen, device=dev) * d ** -0.5).to(bf)
+    Wu = (torch.randn(E, d, f, generator=gen, device=dev) * d ** -0.5).to(bf)
+    Wd = (torch.randn(E, f, d, generator=gen, device=dev) * f ** -0.5).to(bf)
+    pads = _wide_pads(counts)
+
+    def layout(cnts):
+        off = np.concatenate([[0], np.cumsum(cnts)]).astype(np.int32)
+        return off, torch.tensor(off, dtype=torch.int32, device=dev)
+
+    off1, off1_d = layout(counts)
+    off2, off2_d = layout([c + p for c, p in zip(counts, pads)])
+    R1, R2 = int(off1[-1]), int(off2[-1])
+    # gather entries lie below min(T, rows), as moe_expert_up requires
+    gather1 = torch.randint(0, min(T, R1), (R1,), generator=gen, device=dev, dtype=torch.int32)
+    # the padded layout: each expert's rows first, then its pad rows
+    where = np.concatenate([np.arange(off2[e], off2[e] + counts[e]) for e in range(E)]).astype(np.int64)
+    where_d = torch.from_numpy(where).to(dev)
+    gather2 = torch.randint(0, min(T, R2), (R2,), generator=gen, device=dev, dtype=torch.int32)
+    gather2[where_d] = gather1
+
+    def run(off_d, R, gather, ws, a_in=None):
+        # layer 1 reads a_in when given (the same input for split and unsplit)
+        wsb = L.moe_ffn_workspace_size(E, R, d, f) if ws else 0
+        w = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        a = torch.empty(R, f, dtype=bf, device=dev)
+        L.moe_expert_up(x, gather, off_d, E, R, d, f, L.MOE_BF16, Wg, Wu, a, w if ws else None, wsb)
+        if a_in is not None:
+            a = a_in
+        yp = torch.empty(R, d, device=dev)
+        L.moe_expert_down(a, off_d, E, R, f, d, L.MOE_BF16, Wd, yp, None, None, None,
+                          w if ws else None, wsb)
+        yh = torch.empty(R, d, dtype=torch.float16, device=dev)
+        ys = torch.empty(R, d // 32, device=dev)
+        L.moe_expert_down_f16(a, off_d, E, R, f, d, Wd, yh, ys, w if ws else None, wsb)
+        torch.cuda.synchronize()
+        return a, yp, yh, ys
+
+    a1, y1, h1, s1 = run(off1_d, R1, gather1, False)
+    a2, y2, h2, s2 = run(off2_d, R2, gather2, False)
+    assert torch.equal(a1, a2[where_d])
+    assert torch.equal(y1, y2[where_d])
+    assert torch.equal(h1, h2[where_d]) and torch.equal(s1, s2[where_d])
+    # with the workspace: the tail split (every item here) against the unsplit run
+    a3, _, _, _ = run(off1_d, R1, gather1, True)
+    _, y3, _, _ = run(off1_d, R1, gather1, True, a_in=a1)
+    # another fp32 grouping of h and u: one bf16 ulp of a, plus fp32 summation
+    # error (about 1e-5 of the scale) where SiLU(h) u lies near zero
+    a_rms = float(a1.float().pow(2).mean().sqrt())
+    excess = ((a3.float() - a1.float()).abs() - a1.float().abs() * 2.0 ** -7) / a_rms
+    log(f"  split vs unsplit: a beyond one ulp by at most {float(excess.max()):.2e} of rms")
+    assert float(excess.max()) <= 1e-4
+    scale = float(y1.abs().max()) if R1 else 1.0
+    assert float((y3 - y1).abs().max()) <= 1e-5 * scale
+    # and against the definition, fp64 on the same bf16 operands
+    for e in range(E):
+        r0, r1 = int(off1[e]), int(off1[e + 1])
+        if r0 == r1:
+            continue
+        z = x[gather1[r0:r1].long()].double()
+        h = z @ Wg[e].double()
+        u = z @ Wu[e].double()
+        a_ref = h * torch.sigmoid(h) * u
+        err = float((a1[r0:r1].double() - a_ref).abs().max() / a_ref.abs().max())
+        assert err <= 2e-2, (e, err)
+        y_ref = a1[r0:r1].double() @ Wd[e].double()
+        err = float((y1[r0:r1].double() - y_ref).abs().max() / y_ref.abs().max())
+        assert err <= 1e-4, (e, err)

@@ -154,27 +154,41 @@ def flushed_read_ms(nbytes, reps=5, flush_bytes=1 << 30):
     return sorted(times)[reps // 2]
 
 
-def measured_peaks(copy_bytes=1 << 30, probe_iters=20000):
+def measured_peaks(copy_bytes=1 << 30, probe_iters=2500, probe_launches=20):
     """Peaks measured on this machine: the bf16 MFMA rate and shader clock of an
-    all-compute-unit MFMA-only loop (two 4-wave blocks per compute unit),
-    and a device copy of `copy_bytes` bytes (read + write bytes / time)."""
+    all-compute-unit MFMA-only loop (two 4-wave blocks per compute unit), with
+    operands that change from one MFMA to the next (random bf16 values, as in
+    a GEMM) and with fixed operands, each timed over `probe_launches` launches
+    after as many warm-up launches (the clock settles over tens of
+    milliseconds of load); and a device copy of `copy_bytes` bytes (read +
+    write bytes / time)."""
     import torch
     from mixture_experts_layer_top_amd import _lib
     dev = torch.device("cuda:0")
     n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
     blocks = 2 * n_cu
     ticks = torch.zeros(3 * blocks, dtype=torch.int64, device=dev)
-    _lib.moe_probe_mfma(blocks, 100, ticks)  # warm-up
-    torch.cuda.synchronize()
+    g = torch.Generator(device=dev).manual_seed(0)
+    ops = torch.randn(blocks * 16 * 256 * 8, generator=g, device=dev).to(torch.bfloat16)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    _lib.moe_probe_mfma(blocks, probe_iters, ticks)
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b)
-    flops = blocks * 4 * probe_iters * 16 * 16384
-    t = ticks.view(blocks, 3).cpu().double()
-    sclk = float((t[:, 0] / (t[:, 1] / 100e6)).median()) / 1e9
+
+    def mfma_rate(operands):
+        for _ in range(probe_launches):  # warm-up
+            _lib.moe_probe_mfma(blocks, probe_iters, operands, ticks)
+        a.record()
+        for _ in range(probe_launches):
+            _lib.moe_probe_mfma(blocks, probe_iters, operands, ticks)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        flops = probe_launches * blocks * 4 * probe_iters * 32 * 16384
+        t = ticks.view(blocks, 3).cpu().double()  # the last launch
+        sclk = float((t[:, 0] / (t[:, 1] / 100e6)).median()) / 1e9
+        return flops / (ms * 1e-3) / 1e12, sclk, ms
+
+    rnd_tf, rnd_clk, rnd_ms = mfma_rate(ops)
+    fix_tf, fix_clk, _ = mfma_rate(None)
+    del ops
     src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -189,10 +203,14 @@ def measured_peaks(copy_bytes=1 << 30, probe_iters=20000):
     del src, dst
     cms = sorted(times)[len(times) // 2]
     return {
-        "mfma_bf16_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
-        "sclk_GHz_under_mfma_load": round(sclk, 3),
-        "mfma_probe": f"{blocks} blocks x 4 waves x {probe_iters} x 16 MFMA 16x16x32 bf16, "
-                      f"{ms:.2f} ms",
+        "mfma_bf16_TFLOPs": round(rnd_tf, 1),
+        "sclk_GHz_under_mfma_load": round(rnd_clk, 3),
+        "mfma_bf16_TFLOPs_fixed_operands": round(fix_tf, 1),
+        "sclk_GHz_fixed_operands": round(fix_clk, 3),
+        "mfma_probe": f"{probe_launches} launches of {blocks} blocks x 4 waves x {probe_iters} x 32 "
+                      f"MFMA 16x16x32 bf16 after {probe_launches} warm-up launches, random bf16 "
+                      f"operands changing every MFMA ({rnd_ms:.1f} ms); the same with fixed "
+                      "operands",
         "hbm_copy_GBs": round(2 * copy_bytes / (cms * 1e-3) / 1e9, 1),
         "copy": f"device copy of {copy_bytes >> 20} MiB, median of 5",
         "hbm_read_GBs": round(copy_bytes / (flushed_read_ms(copy_bytes) * 1e-3) / 1e9, 1),

@@ -431,14 +431,21 @@ int moe_linear_backward(const void* x, const void* W, const float* G, int T, int
 
 /*
  * moe_probe_mfma -- `blocks` workgroups of 4 wave64s each run `iters` rounds
- * of 16 independent bf16 MFMAs of 16 x 16 x 32 (16384 flops each) on
- * register operands, so the launch performs blocks * 4 * iters * 16 * 16384
- * flops (time it with events on the stream).  ticks [3 * blocks] uint64
- * device out: per block, the shader-clock ticks and the 100 MHz real-time
- * ticks its wave 0 spent in the loop, and a word that is always 0.
- * MOE_ERR_INVALID for blocks outside [1, 2^20], iters < 1 or a NULL ticks.
+ * of 32 bf16 MFMAs of 16 x 16 x 32 (16384 flops each) on register operands
+ * into 16 accumulators, so the launch performs blocks * 4 * iters * 32 *
+ * 16384 flops (time it with events on the stream).  operands: NULL, or
+ * device bf16 values, blocks * 16 * 256 vectors of 8 (blocks * 65536 bytes,
+ * 16-byte aligned): every thread loads 8 A and 8 B vectors once and the
+ * MFMAs cycle through them, so consecutive MFMAs multiply different bits (the
+ * switching of a real GEMM's operands; NULL: fixed per-lane values).  The
+ * values never reach memory and only need to be finite.  ticks [3 * blocks]
+ * uint64 device out: per block, the shader-clock ticks and the 100 MHz
+ * real-time ticks its wave 0 spent in the loop, and a word that is always 0.
+ * MOE_ERR_INVALID for blocks outside [1, 2^20], iters < 1 or a NULL ticks;
+ * MOE_ERR_UNSUPPORTED for a misaligned ticks or operands.
  */
-int moe_probe_mfma(int blocks, int iters, uint64_t* ticks, hipStream_t stream);
+int moe_probe_mfma(int blocks, int iters, const void* operands, uint64_t* ticks,
+                   hipStream_t stream);
 
 /*
  * moe_probe_read -- reads `bytes` bytes of device memory at src once, in

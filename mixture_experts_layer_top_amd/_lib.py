@@ -58,7 +58,7 @@ def load():
                               sz, vp]),
         "moe_ffn_workspace_size": (sz, [i32, i32, i32, i32]),
         "moe_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
-        "moe_probe_mfma": (i32, [i32, i32, vp, vp]),
+        "moe_probe_mfma": (i32, [i32, i32, vp, vp, vp]),
         "moe_probe_read": (i32, [vp, sz, vp, vp]),
         "moe_permute_noalloc": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                       vp]),
@@ -318,8 +318,8 @@ def moe_linear_backward(x, W, G, T, d, E, dtype, dW, db, dx, workspace, ws_bytes
 # ---------------------------------------------------------------- measurement
 
 
-def moe_probe_mfma(blocks, iters, ticks, stream=None, check=True):
-    st = load().moe_probe_mfma(blocks, iters, _p(ticks), _stream(stream))
+def moe_probe_mfma(blocks, iters, operands, ticks, stream=None, check=True):
+    st = load().moe_probe_mfma(blocks, iters, _p(operands), _p(ticks), _stream(stream))
     if check:
         _check("moe_probe_mfma", st)
     return st

@@ -407,11 +407,12 @@ int moe_linear_backward(const void* x, const void* W, const float* G, int T, int
 
 // ---------------------------------------------------------------- measurement
 
-int moe_probe_mfma(int blocks, int iters, uint64_t* ticks, hipStream_t stream) {
+int moe_probe_mfma(int blocks, int iters, const void* operands, uint64_t* ticks,
+                   hipStream_t stream) {
   if (blocks < 1 || blocks > (1 << 20) || iters < 1) return MOE_ERR_INVALID;
   if (!ticks) return MOE_ERR_INVALID;
-  if (!aligned16(ticks)) return MOE_ERR_UNSUPPORTED;
-  return hip_status(moe::launch_probe_mfma(blocks, iters, ticks, stream));
+  if (!aligned16(ticks) || (operands && !aligned16(operands))) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_probe_mfma(blocks, iters, operands, ticks, stream));
 }
 
 int moe_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {

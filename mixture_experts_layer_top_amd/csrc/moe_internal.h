@@ -105,7 +105,8 @@ hipError_t launch_combine_f16(const uint16_t* y_h, const float* y_s, const int32
                               const float* ys_s, const float* gate_logit, bool accumulate,
                               float* y, hipStream_t s);
 
-hipError_t launch_probe_mfma(int blocks, int iters, uint64_t* ticks, hipStream_t s);
+hipError_t launch_probe_mfma(int blocks, int iters, const void* ops, uint64_t* ticks,
+                             hipStream_t s);
 hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 
 // backward

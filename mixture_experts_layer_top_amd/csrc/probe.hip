@@ -8,12 +8,16 @@
 // a kernel reaches needs the peak the chip actually sustains, which under
 // its power limit is below the datasheet figure.
 //
-// Each wave issues `iters` rounds of 16 independent
-// v_mfma_f32_16x16x32_bf16 on register operands (16 accumulators: enough
-// to keep a SIMD's matrix pipe busy with one wave); lane 0 of wave 0 of
-// every block records the shader-clock counter (s_memtime) and the 100 MHz
-// real-time counter (s_memrealtime) around its loop, so their ratio is the
-// shader clock under this load.
+// Each wave issues `iters` rounds of 32 v_mfma_f32_16x16x32_bf16 on register
+// operands into 16 accumulators (enough to keep a SIMD's matrix pipe busy
+// with one wave); lane 0 of wave 0 of every block records the shader-clock
+// counter (s_memtime) and the 100 MHz real-time counter (s_memrealtime)
+// around its loop, so their ratio is the shader clock under this load.  The
+// operands are either fixed per lane (the same A and B bits in every MFMA)
+// or 16 fragments of caller-supplied values, loaded once and rotated so that
+// consecutive MFMAs multiply different A and B: a GEMM's operand bits change
+// from one MFMA to the next, and the switching costs power, so the chip
+// holds a lower clock under that load than under fixed operands.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -23,24 +27,43 @@ namespace {
 
 constexpr int kProbeAcc = 16;
 
-__global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, uint64_t* __restrict__ ticks) {
+template <bool OPS>
+__global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, const bf16x8* __restrict__ ops,
+                                                        uint64_t* __restrict__ ticks) {
   f32x4 acc[kProbeAcc];
 #pragma unroll
   for (int i = 0; i < kProbeAcc; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 a[4], b[4];
+  // 8 A and 8 B fragments: caller values (block b, fragment j at
+  // ops[(16 b + j) * 256 + thread]) or fixed per lane
+  bf16x8 a[8], b[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 8; ++j) {
+    if constexpr (OPS) {
+      a[j] = ops[((size_t)blockIdx.x * 16 + j) * 256 + threadIdx.x];
+      b[j] = ops[((size_t)blockIdx.x * 16 + 8 + j) * 256 + threadIdx.x];
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      a[j][i] = (__bf16)((threadIdx.x & 7) * 0.125f + j);
-      b[j][i] = (__bf16)(i * 0.0625f - j);
+      for (int i = 0; i < 8; ++i) {
+        a[j][i] = (__bf16)((threadIdx.x & 7) * 0.125f + (j & 3));
+        b[j][i] = (__bf16)(i * 0.0625f - (j & 3));
+      }
     }
+  }
   const uint64_t t0 = __builtin_amdgcn_s_memtime();
   const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
   for (int it = 0; it < iters; ++it) {
+    // two passes over the 16 accumulators in the order of a GEMM's block
+    // loop (row block m, K step q, column block n): accumulator 4 m + n takes
+    // A fragment (2 m + q + n) % 8 and B fragment (2 n + q + m) % 8, so
+    // consecutive MFMAs differ in both operands
 #pragma unroll
-    for (int i = 0; i < kProbeAcc; ++i)
-      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i & 3], b[(i >> 2) & 3], acc[i], 0, 0, 0);
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          acc[4 * m + n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              a[(2 * m + q + n) & 7], b[(2 * n + q + m) & 7], acc[4 * m + n], 0, 0, 0);
   }
   const uint64_t t1 = __builtin_amdgcn_s_memtime();
   const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
@@ -94,8 +117,14 @@ hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_probe_mfma(int blocks, int iters, uint64_t* ticks, hipStream_t s) {
-  hipLaunchKernelGGL(mfma_peak_kernel, dim3(blocks), dim3(256), 0, s, iters, ticks);
+hipError_t launch_probe_mfma(int blocks, int iters, const void* ops, uint64_t* ticks,
+                             hipStream_t s) {
+  if (ops)
+    hipLaunchKernelGGL(mfma_peak_kernel<true>, dim3(blocks), dim3(256), 0, s, iters,
+                       static_cast<const bf16x8*>(ops), ticks);
+  else
+    hipLaunchKernelGGL(mfma_peak_kernel<false>, dim3(blocks), dim3(256), 0, s, iters,
+                       static_cast<const bf16x8*>(nullptr), ticks);
   return hipGetLastError();
 }
 

@@ -286,10 +286,11 @@ def test_workspace_size_edge_cases(lib):
 
 
 def test_probe_validation(lib):
-    assert L.moe_probe_mfma(0, 10, A, stream=0, check=False) == L.MOE_ERR_INVALID
-    assert L.moe_probe_mfma(4, 0, A, stream=0, check=False) == L.MOE_ERR_INVALID
-    assert L.moe_probe_mfma(4, 10, None, stream=0, check=False) == L.MOE_ERR_INVALID
-    assert L.moe_probe_mfma(4, 10, MIS, stream=0, check=False) == L.MOE_ERR_UNSUPPORTED
+    assert L.moe_probe_mfma(0, 10, None, A, stream=0, check=False) == L.MOE_ERR_INVALID
+    assert L.moe_probe_mfma(4, 0, A, A, stream=0, check=False) == L.MOE_ERR_INVALID
+    assert L.moe_probe_mfma(4, 10, A, None, stream=0, check=False) == L.MOE_ERR_INVALID
+    assert L.moe_probe_mfma(4, 10, None, MIS, stream=0, check=False) == L.MOE_ERR_UNSUPPORTED
+    assert L.moe_probe_mfma(4, 10, MIS, A, stream=0, check=False) == L.MOE_ERR_UNSUPPORTED
     # the streaming-read probe: validation before any launch (bytes = 0 is a no-op)
     assert L.moe_probe_read(A, 0, A, stream=0, check=False) == L.MOE_OK
     assert L.moe_probe_read(None, 64, A, stream=0, check=False) == L.MOE_ERR_INVALID

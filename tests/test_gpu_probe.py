@@ -19,9 +19,16 @@ def test_probe_read_sizes():
         assert sink.tolist() == [-7, -7, -7, -7]
 
 
-def test_probe_mfma_ticks():
-    ticks = torch.full((3 * 8,), -1, dtype=torch.int64, device="cuda:0")
-    _lib.moe_probe_mfma(8, 50, ticks)
+@pytest.mark.parametrize("with_operands", [False, True])
+def test_probe_mfma_ticks(with_operands):
+    print(f"[probe_mfma] operands={with_operands}", flush=True)
+    blocks = 8
+    ops = None
+    if with_operands:
+        g = torch.Generator(device="cuda:0").manual_seed(0)
+        ops = torch.randn(blocks * 16 * 256 * 8, generator=g, device="cuda:0").to(torch.bfloat16)
+    ticks = torch.full((3 * blocks,), -1, dtype=torch.int64, device="cuda:0")
+    _lib.moe_probe_mfma(blocks, 50, ops, ticks)
     torch.cuda.synchronize()
-    t = ticks.view(8, 3).cpu()
+    t = ticks.view(blocks, 3).cpu()
     assert bool((t[:, 0] > 0).all()) and bool((t[:, 1] > 0).all()) and bool((t[:, 2] == 0).all())

@@ -15,10 +15,15 @@
 //   3. rank:  each block marks its tokens in per-expert bit columns (LDS
 //             OR) and ranks each pair by popcounts of the bits below it;
 //   4. gather (optional): x_perm[r] = x[perm_token[r]], 16-byte vectors.
-// When the block histograms are small (blocks x experts <= 32768), every
-// rank block does the scan itself (its own column prefixes, and the
-// totals): two launches, hist and scan+rank.  Otherwise hist also adds into
-// the global counts (integer adds commute) and one workgroup scans.
+// A batch of at most 4096 tokens and 8192 (token, expert) pairs is permuted
+// in one launch: all of its bit columns fit in every workgroup's LDS, and
+// every workgroup builds them (measured: the two-launch path's 10.9 µs
+// become 6.7 µs at T = 128, and about 12 µs stay about 12 µs at T = 4096,
+// E = 8, k = 2).  Otherwise, when the block histograms
+// are small (blocks x experts <= 32768), every rank block does the scan
+// itself (its own column prefixes, and the totals): two launches, hist and
+// scan+rank.  Otherwise hist also adds into the global counts (integer adds
+// commute) and one workgroup scans.
 #include <mutex>
 
 #include "moe_internal.h"
@@ -227,6 +232,120 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
   for (int j = kKR; j < k; ++j) place(j, it[j]);
 }
 
+// The whole permutation of a short batch in one launch (T <= kSmallT,
+// T k <= 2 kSmallT, E * ceil(T / 64) <= kSmallWords): every workgroup
+// builds the bit columns of all T tokens in LDS (the same bits as hist and
+// rank: a few kilobytes of picks, read from L2), scans them, and places the
+// pairs of its own 256 tokens; workgroup 0 also writes counts and offsets.  One launch replaces
+// two, and the scattered row writes stay spread over as many compute units
+// as before.  Thread i builds from tokens i, i + 1024, ...; each expert's
+// column prefix (over its 64-token words) is a wave scan, and the expert
+// offsets a scan over the column totals.  Counts, offsets and ranks are
+// those of the two-launch path (the same popcounts of the same bits).
+constexpr int kSmallT = 4096;
+constexpr int kSmallWords = 8192;
+constexpr int kSmallThreads = 1024;
+__global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
+    const int32_t* __restrict__ idx, const float* __restrict__ topk_w, int T, int E, int k,
+    int32_t* __restrict__ perm_token, int32_t* __restrict__ inv, float* __restrict__ perm_w,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  __shared__ unsigned long long bits[kSmallWords];  // [E][NW]
+  __shared__ int wbase[kSmallWords];                // [E][NW]: rows of e in earlier words
+  __shared__ int ebase[257];                        // offsets
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NWV = kSmallThreads / 64;
+  const int NW = cdiv(T, 64);
+  for (int i = tid; i < E * NW; i += kSmallThreads) bits[i] = 0ull;
+  __syncthreads();
+  constexpr int TPT = kSmallT / kSmallThreads;  // tokens per thread
+  int er[TPT][kKR];
+  // the first min(k, kKR) picks of each of the thread's tokens, all loads
+  // issued before any is used (k is uniform: the tests are scalar branches)
+#pragma unroll
+  for (int q = 0; q < TPT; ++q) {
+    const int t = q * kSmallThreads + tid;
+    if (t < T) {
+#pragma unroll
+      for (int j = 0; j < kKR; ++j)
+        if (j < k) er[q][j] = idx[(size_t)t * k + j];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < TPT; ++q) {
+    const int t = q * kSmallThreads + tid;
+    if (t >= T) continue;
+    const int w = t >> 6;
+    const unsigned long long me = 1ull << (t & 63);
+#pragma unroll
+    for (int j = 0; j < kKR; ++j)
+      if (j < k) atomicOr(&bits[er[q][j] * NW + w], me);
+    for (int j = kKR; j < k; ++j) atomicOr(&bits[idx[(size_t)t * k + j] * NW + w], me);
+  }
+  __syncthreads();
+  // column prefixes: wave v scans experts v, v + NWV, ... (lane = word, NW <= 64)
+  for (int e = wave; e < E; e += NWV) {
+    const int c = lane < NW ? __popcll(bits[e * NW + lane]) : 0;
+    const int incl = wave_incl_sum(c);
+    if (lane < NW) wbase[e * NW + lane] = incl - c;
+    if (lane == 63) ebase[e] = incl;  // the column total, for now
+  }
+  __syncthreads();
+  // offsets: exclusive scan of the totals over experts (wave 0, 4 per lane)
+  if (wave == 0) {
+    int tot[4], s4 = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = lane * 4 + u;
+      tot[u] = e < E ? ebase[e] : 0;
+      s4 += tot[u];
+    }
+    const int incl = wave_incl_sum(s4);
+    int run = incl - s4;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = lane * 4 + u;
+      if (e < E) {
+        if (blockIdx.x == 0) {
+          counts[e] = tot[u];
+          offsets[e] = run;
+        }
+        ebase[e] = run;
+      }
+      run += tot[u];
+    }
+    if (lane == 63 && blockIdx.x == 0) offsets[E] = incl;
+  }
+  __syncthreads();
+  // this workgroup's 256 tokens t0 .. t0 + 255 were built by threads
+  // t0 % 1024 .. + 255 from their register slot q = t0 / 1024; those threads
+  // place the tokens' pairs
+  const int t0 = blockIdx.x * kPT;
+  const int q_own = t0 / kSmallThreads;
+  const int t = q_own * kSmallThreads + tid;
+  if (tid - t0 % kSmallThreads < 0 || tid - t0 % kSmallThreads >= kPT || t >= T) return;
+  const int w = t >> 6;
+  const unsigned long long below = (1ull << (t & 63)) - 1ull;
+  auto place = [&](int j, int e) {
+    const int r = ebase[e] + wbase[e * NW + w] + __popcll(bits[e * NW + w] & below);
+    const size_t pg = (size_t)t * k + j;
+    perm_token[r] = t;
+    inv[pg] = r;
+    if (perm_w) perm_w[r] = topk_w[pg];
+  };
+#pragma unroll
+  for (int j = 0; j < kKR; ++j) {
+    if (j < k) {
+      // er[q_own][j] without a run-time register index
+      int e = er[0][j];
+#pragma unroll
+      for (int q = 1; q < TPT; ++q)
+        if (q == q_own) e = er[q][j];
+      place(j, e);
+    }
+  }
+  for (int j = kKR; j < k; ++j) place(j, idx[(size_t)t * k + j]);
+}
+
 // x_perm[r, :] = x[perm_token[r], :] for the rows r < offsets[E] the rank
 // kernel wrote (all T k of them unless a token listed an expert twice);
 // rows of `vecs` 16-byte vectors.  A block copies 8 rows; a thread takes
@@ -301,7 +420,12 @@ hipError_t launch_permute(const int32_t* idx, const float* topk_w, const void* x
   int32_t* blk_cnt = static_cast<int32_t*>(ws);
   int32_t* blk_base = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
                                                  align_up((size_t)nb * E * sizeof(int32_t), 256));
-  if (nb > 0 && (long long)nb * E <= 32768) {
+  if (T <= kSmallT && (long long)T * k <= kSmallT * 2 && E * cdiv(T, 64) <= kSmallWords) {
+    // one launch: every workgroup builds and scans the whole batch's bit
+    // columns and places its own tokens
+    hipLaunchKernelGGL(permute_small_kernel, dim3(max(nb, 1)), dim3(kSmallThreads), 0, s, idx,
+                       topk_w, T, E, k, perm_token, inv, perm_w, counts, offsets);
+  } else if (nb > 0 && (long long)nb * E <= 32768) {
     // two launches: block histograms, then scan + rank in every block
     hipLaunchKernelGGL(hist_kernel, dim3(nb), dim3(kThreads), 0, s, idx, T, E, k, blk_cnt,
                        (int32_t*)nullptr);

@@ -222,15 +222,17 @@ def measured_peaks(copy_bytes=1 << 30, probe_iters=2500, probe_launches=20):
 def gemm_kernel_name(cfg, up):
     """The grouped-GEMM kernel the library launches for this layer: for bf16
     the ping-pong kernel (main pass) when K is a multiple of its 64-deep
-    stages and the A operand is below 4 GiB, else the general kernel; for
-    fp32 the plain FMA kernels."""
+    stages and the A operand is below 4 GiB, in the instantiation that may
+    hold wide items (an expert's last rows over two N panels) when K >= 2048,
+    else the general kernel; for fp32 the plain FMA kernels."""
     if cfg.dtype != "bf16":
         return "up_f32_kernel" if up else "down_f32_kernel"
     K = cfg.d if up else cfg.f
     a_bytes = cfg.T * cfg.k * K * 2
     u = "true" if up else "false"
     if K % 64 == 0 and a_bytes < (1 << 32):
-        return f"grouped_gemm_bf16_pp_kernel<{u}, 64, false>"
+        wide = "true" if K >= 2048 else "false"
+        return f"grouped_gemm_bf16_pp_kernel<{u}, 64, false, {wide}>"
     return f"grouped_gemm_bf16_kernel<{u}, 2, 4, 256>"
 
 

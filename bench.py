@@ -255,6 +255,51 @@ def measured_traffic(cfg):
     return rec["traffic_bytes"]
 
 
+def route_alone(m, reps=20, flush_bytes=1 << 30):
+    """The router call on its own: `reps` calls back to back (one event pair
+    around them), and `reps` single calls each after a 1 GiB write that
+    evicts the last-level cache (median of the per-call event times)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m.route()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        m.route()
+    b.record(stream)
+    torch.cuda.synchronize()
+    b2b = a.elapsed_time(b) / reps
+    flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda:0")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i in range(reps):
+        flush.fill_(i & 0xFF)
+        ev[i][0].record(stream)
+        m.route()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    del flush
+    return b2b, pct([x.elapsed_time(y) for x, y in ev], 50)
+
+
+def cpu_routing(cfg, layer, target_s=3.0):
+    """The oracle's routing and dispatch alone (logits, top-k, weights,
+    counts, offsets, stable permutation) on all T tokens, fp64 numpy: the
+    CPU counterpart of the route and permute calls.  Seconds per call
+    (median of the repetitions that fit in about target_s seconds)."""
+    import oracle.moe_oracle as O
+    from mixture_experts_layer_top_amd.inputs import to_f64
+    host = to_f64({kk: layer[kk] for kk in ("x", "W_r", "b") if layer.get(kk) is not None})
+    times = []
+    while sum(times) < target_s and len(times) < 20:
+        t0 = time.perf_counter()
+        _, idx, w = O.route(host, cfg.k, cfg.renorm)
+        O.dispatch(idx, w, cfg.E)
+        times.append(time.perf_counter() - t0)
+    return sorted(times)[len(times) // 2], len(times)
+
+
 def cpu_baseline(cfg, layer, target_s):
     """The fp64 oracle, as it stands, on a bounded sample of the workload's
     tokens with the full expert weights (the same tensors the GPU ran on;
@@ -586,10 +631,32 @@ def main():
             "expert_down_TFLOPs_at_median": round(g1_flops / (med["expert_down"] * 1e-3) / 1e12,
                                                   1),
         }
+    if args.protocol_steps > 0:
+        b2b, alone = route_alone(m)
+        out["route_alone"] = {
+            "what": "moe_route by itself: 20 calls back to back, and 20 single calls each after a "
+                    "1 GiB cache flush (median)",
+            "back_to_back_us": round(b2b * 1e3, 2),
+            "flushed_us": round(alone * 1e3, 2),
+            "flushed_GBs": round(by["route"] / (alone * 1e-3) / 1e9, 1),
+            "flushed_frac_of_8TBs": round(by["route"] / (alone * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+        }
     if not args.no_peaks:
         out["measured_peaks"] = measured_peaks()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, layer, args.cpu_target_s)
+        rt, n_rt = cpu_routing(cfg, layer)
+        gpu_rt = stage_ms["route"] + stage_ms["permute"]
+        out["cpu_baseline"]["routing"] = {
+            "what": "routing and dispatch alone (logits, top-k, weights, counts, offsets, stable "
+                    f"permutation) on all {T} tokens: the oracle against the GPU's route + permute "
+                    "calls inside the layer",
+            "oracle_s": round(rt, 4),
+            "oracle_tokens_per_s": round(T / rt, 1),
+            "repetitions": n_rt,
+            "gpu_route_permute_ms": round(gpu_rt, 4),
+            "gpu_tokens_per_s": round(T / (gpu_rt * 1e-3), 1),
+        }
     print(json.dumps(out), flush=True)
 
 

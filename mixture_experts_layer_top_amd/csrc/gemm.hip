@@ -114,10 +114,8 @@ struct GemmArgs {
 // written by the first lane of the four); valid: the lane's row and columns
 // exist.  Every lane of the wave must take part (quad reduction by DPP).
 template <bool NT>
-__device__ __forceinline__ void store_seg_f16(const float* src, uint16_t* dst, float* fdst,
-                                              bool valid, bool leader) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+__device__ __forceinline__ void store_seg_f16v(const f32x4 a, const f32x4 b, uint16_t* dst,
+                                               float* fdst, bool valid, bool leader) {
   const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   uint32_t m = 0;  // largest finite magnitude, as bits (ordered like the values)
 #pragma unroll
@@ -150,6 +148,12 @@ __device__ __forceinline__ void store_seg_f16(const float* src, uint16_t* dst, f
       if (leader) *fdst = back;
     }
   }
+}
+template <bool NT>
+__device__ __forceinline__ void store_seg_f16(const float* src, uint16_t* dst, float* fdst,
+                                              bool valid, bool leader) {
+  store_seg_f16v<NT>(*reinterpret_cast<const f32x4*>(src), *reinterpret_cast<const f32x4*>(src + 4),
+                     dst, fdst, valid, leader);
 }
 
 struct TileInfo {
@@ -1173,7 +1177,45 @@ __device__ __forceinline__ void pp_tile(const GemmArgs p, const Work wk, char* l
     }
   } else {
     // the wave's columns: n0 + h * 128 + wg * 32 + [0, 32) for halves h = 0, 1
-    if (p.y_perm || p.y_h) {
+    if (p.y_h) {
+      // compact rows: each 16-row block is staged, then every lane reads the
+      // 8 columns of its two row segments (4 LDS reads, one wait), scales,
+      // converts and stores them; the non-temporal choice is made once
+      auto compact = [&](auto nt_tag) {
+        constexpr bool NT = decltype(nt_tag)::value;
+        constexpr int SS = 64 + 4;  // staging stride in floats
+        float* sf = reinterpret_cast<float*>(lds + wave * 16 * SS * 4);
+        const int segs = N >> 5;
+#pragma unroll
+        for (int mi = 0; mi < EMI; ++mi) {
+          if (mi + mi_off >= my_nb) break;
+#pragma unroll
+          for (int nj = 0; nj < NJ; ++nj)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sf[(row_l + i) * SS + nj * 16 + col_l] = acc[mi][nj][i];
+          f32x4 va[2], vb[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int idx = q * 64 + lane;
+            const float* src = sf + (idx >> 3) * SS + (idx & 7) * 8;
+            va[q] = *reinterpret_cast<const f32x4*>(src);
+            vb[q] = *reinterpret_cast<const f32x4*>(src + 4);
+          }
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int idx = q * 64 + lane;
+            const int r = idx >> 3, c = idx & 7;
+            const int row = t_row0 + grow0 + (mi + mi_off) * 16 + r;
+            const int col = n0 + (c >> 2) * 128 + wg * 32 + (c & 3) * 8;
+            store_seg_f16v<NT>(va[q], vb[q], p.y_h + (size_t)row * N + col,
+                               p.y_s + (size_t)row * segs + (col >> 5),
+                               row < grow_end && col < N, (c & 3) == 0);
+          }
+        }
+      };
+      if (p.nt_y) compact(std::true_type{});
+      else compact(std::false_type{});
+    } else if (p.y_perm) {
       constexpr int SS = 64 + 4;  // staging stride in floats
       float* sf = reinterpret_cast<float*>(lds + wave * 16 * SS * 4);
 #pragma unroll
@@ -1183,27 +1225,6 @@ __device__ __forceinline__ void pp_tile(const GemmArgs p, const Work wk, char* l
         for (int nj = 0; nj < NJ; ++nj)
 #pragma unroll
           for (int i = 0; i < 4; ++i) sf[(row_l + i) * SS + nj * 16 + col_l] = acc[mi][nj][i];
-        if (p.y_h) {
-          // 16 rows x 8 chunks of 8 columns; chunks 4h .. 4h + 3 are the
-          // wave's 32-column segment of half h (N is a multiple of 32)
-          const int segs = N >> 5;
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int idx = q * 64 + lane;
-            const int r = idx >> 3, c = idx & 7;
-            const int row = t_row0 + grow0 + (mi + mi_off) * 16 + r;
-            const int col = n0 + (c >> 2) * 128 + wg * 32 + (c & 3) * 8;
-            const float* src = sf + r * SS + c * 8;
-            uint16_t* dst = p.y_h + (size_t)row * N + col;
-            float* fdst = p.y_s + (size_t)row * segs + (col >> 5);
-            const bool ok = row < grow_end && col < N;
-            if (p.nt_y)
-              store_seg_f16<true>(src, dst, fdst, ok, (c & 3) == 0);
-            else
-              store_seg_f16<false>(src, dst, fdst, ok, (c & 3) == 0);
-          }
-          continue;
-        }
         // 16 rows x 16 chunks of 16 B; two separate loops, so that the
         // compiler keeps the non-temporal hint (merging the two stores drops it)
         if (p.nt_y) {

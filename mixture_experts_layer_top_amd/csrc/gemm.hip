@@ -720,20 +720,23 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   const int C = p.n_cu;
   int tail = n_tiles % C;
   const int nk_all = p.K / pbk;
-  int S = 1, kps = p.K;
   // split only where the last round is mostly idle (at most half full) and
   // the launch has at most kSplitMaxRounds rounds; otherwise the
-  // fixup pass costs more than the idle compute units
-  if (p.part != nullptr && tail > 0 && 2 * tail <= C &&
-      n_tiles <= kSplitMaxRounds * C && nk_all >= 2) {
+  // fixup pass costs more than the idle compute units.  A split then has
+  // S >= 2 parts (C / tail >= 2 and nk_all >= 2), so the tail stays.
+  const bool split = p.part != nullptr && tail > 0 && 2 * tail <= C &&
+                     n_tiles <= kSplitMaxRounds * C && nk_all >= 2;
+  if (!split) tail = 0;
+  const int F = n_tiles - tail;
+  // the split's part count and K per part; only the split items and the
+  // fixup pass use them, so whole tiles skip these divisions
+  auto split_parts = [&](int& S, int& kps) {
     S = min(C / tail, nk_all);
     kps = cdiv(nk_all, S) * pbk;
     S = cdiv(p.K, kps);  // parts that are not empty
-  }
-  if (S == 1) tail = 0;
-  const int F = n_tiles - tail;
+  };
   Work w{};
-  w.S = S;
+  w.S = 1;
   w.ok = false;
   w.item = -1;
   w.ks = 0;
@@ -743,6 +746,9 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   w.fix_mi = 0;
   if (p.fixup) {
     if (b < tail * FIXQ) {
+      int S, kps;
+      split_parts(S, kps);
+      w.S = S;
       w.tile = F + b / FIXQ;
       w.item = (b / FIXQ) * S;
       w.fix_mi = b % FIXQ;
@@ -752,13 +758,18 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
     if (b < G) {
       const int t = (b & 7) * (G / 8) + (b >> 3);
       if (t < F) w.tile = t;
-    } else if (b - G < tail * S) {
-      const int j = b - G;
-      w.tile = F + j / S;
-      w.ks = j % S;
-      w.item = j;
-      w.k_begin = w.ks * kps;
-      w.k_end = min(p.K, w.k_begin + kps);
+    } else if (tail > 0) {
+      int S, kps;
+      split_parts(S, kps);
+      if (b - G < tail * S) {
+        const int j = b - G;
+        w.S = S;
+        w.tile = F + j / S;
+        w.ks = j % S;
+        w.item = j;
+        w.k_begin = w.ks * kps;
+        w.k_end = min(p.K, w.k_begin + kps);
+      }
     }
   }
   if (w.tile < 0) return w;
@@ -821,23 +832,29 @@ __device__ __forceinline__ Work assign_work(const GemmArgs& p, int b, int pbk) {
   // covers all N panels, M fastest inside each panel, before the next, so
   // its token rows (the A operand) are reused by every panel while they
   // still sit in the last-level cache.  A small expert is one group.
-  const int ng = tmt <= p.m_group_min ? 1 : cdiv(tmt, p.m_group);
   const int tn = p.tiles_n;
-  const int g_lo = tmt / ng, g_rem = tmt - g_lo * ng;  // group sizes g_lo + 1 (g_rem of them), g_lo
-  const int big = g_rem * (g_lo + 1) * tn;            // tiles in the larger groups
-  int q, m0, mq;
-  if (local < big) {
-    q = local / ((g_lo + 1) * tn);
-    m0 = q * (g_lo + 1);
-    mq = g_lo + 1;
+  if (tmt <= p.m_group_min) {
+    // one group (every expert of moderate size): M fastest inside each panel
+    ti.n_t = local / tmt;
+    ti.m_t = local - ti.n_t * tmt;
   } else {
-    q = g_rem + (local - big) / (g_lo * tn);
-    m0 = g_rem * (g_lo + 1) + (q - g_rem) * g_lo;
-    mq = g_lo;
+    const int ng = cdiv(tmt, p.m_group);
+    const int g_lo = tmt / ng, g_rem = tmt - g_lo * ng;  // group sizes g_lo + 1 (g_rem of them), g_lo
+    const int big = g_rem * (g_lo + 1) * tn;            // tiles in the larger groups
+    int q, m0, mq;
+    if (local < big) {
+      q = local / ((g_lo + 1) * tn);
+      m0 = q * (g_lo + 1);
+      mq = g_lo + 1;
+    } else {
+      q = g_rem + (local - big) / (g_lo * tn);
+      m0 = g_rem * (g_lo + 1) + (q - g_rem) * g_lo;
+      mq = g_lo;
+    }
+    const int r = local - m0 * tn;
+    ti.n_t = r / mq;
+    ti.m_t = m0 + (r - ti.n_t * mq);
   }
-  const int r = local - m0 * tn;
-  ti.n_t = r / mq;
-  ti.m_t = m0 + (r - ti.n_t * mq);
   // Balanced M tiles: the expert's c rows form nbe = ceil(c / 16) blocks of
   // 16, dealt to its tmt = ceil(c / BM) tiles as evenly as possible (the
   // first nbe % tmt tiles take one block more; every tile takes between 1

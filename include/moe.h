@@ -103,8 +103,9 @@ size_t moe_permute_workspace_size(int T, int E, int k);
  *   moe_route produces them (an expert repeated in one token's list is
  *   counted once: both slots get the same row, offsets[E] < T*k, and every
  *   row below offsets[E] is still written, rows offsets[E] .. T*k-1 of
- *   perm_token, perm_w and x_perm are left untouched); topk_w [T, k] fp32 or NULL (then perm_w must be
- *   NULL); x [T, d] (dtype) required only with x_perm; counts [E],
+ *   perm_token, perm_w and x_perm are left untouched); topk_w [T, k] fp32
+ *   or NULL (then perm_w must be NULL); x [T, d] (dtype) required only with
+ *   x_perm; counts [E],
  *   offsets [E+1], perm_token [T*k], inv [T, k] int32 out; perm_w [T*k]
  *   fp32 out or NULL; x_perm [T*k, d] (dtype) out or NULL.
  * The result is deterministic (no atomics decide any order).
